@@ -1,0 +1,381 @@
+"""CPU oracle for the MoE variable-size grouped GEMM.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module: only the tests, the smoke check and the benchmark's CPU-baseline leg
+use it.  It shares no code with the HIP library.
+
+It is the plain, slow, obviously correct definition of every result the HIP
+path computes, written from three pages:
+
+  [GG]   "Grouped GEMM for MoE, in depth" (aicassindra.com engineering article)
+  [CARD] "grouped-gemm-moe" (model card of a published grouped GEMM kernel)
+  [NOTE] "Grouped GEMM" (scholia-log study notes on MoE variable-length matmul)
+
+Conventions:
+  * an assignment is one (token, slot) pair of expert_ids [T, k]; it is numbered
+    s = t*k + j (row-major flatten), as the card's usage example builds the ids;
+  * expert weights are stored (E, N, K) like nn.Linear ([GG] "Data layout,
+    offsets and alignment"), so the forward multiplies a row by W[e] transposed;
+  * offsets are int32 END offsets: offs[e] = end of group e ([GG] "Data layout,
+    offsets and alignment": counts [3,0,5] give offsets [3,3,8]);
+  * floating point is evaluated in float64 by default (``acc``).  [GG]'s loop
+    reference casts to fp32; ``acc=np.float32`` follows it literally.  The
+    float64 default makes a parity tolerance measure the GPU's rounding alone.
+
+Parity pins: every function here is checked in tests/ against something other
+than itself (page examples, closed forms, brute force, finite differences,
+identities).  Exact low-order bits of GPU float results under atomics and the
+order of tiles inside one expert are not pinned (they are not part of the
+result).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+def _cdiv(a, b):
+    return -(-np.asarray(a, dtype=np.int64) // b)
+
+
+# ----------------------------------------------------------------------------
+# Routing schedule
+# ----------------------------------------------------------------------------
+@dataclass
+class Schedule:
+    E: int
+    k: int
+    counts: np.ndarray        # [E] int64: rows per expert (m_e)
+    offsets: np.ndarray       # [E] int32 end offsets
+    starts: np.ndarray        # [E] int64 start offsets
+    perm: np.ndarray          # [R] int64 assignment id s of row r
+    row_to_token: np.ndarray  # [R] int64
+    row_weight: np.ndarray    # [R] routing weight of the row (dtype of the input weights)
+    n_invalid: int            # assignments whose id is outside [0, E)
+
+
+def routing_schedule(expert_ids: np.ndarray, topk_weights: Optional[np.ndarray], E: int) -> Schedule:
+    """Sort the assignments by expert and derive the row maps.
+
+    [GG] "Data layout, offsets and alignment": a stable argsort of the per-copy
+    expert index groups the rows by expert; bincount gives the per-expert
+    counts and an int32 cumulative sum gives the end offsets.
+    [CARD] "How it works": the sorted order gives a row -> token map, a per-row
+    routing weight and the per-expert group sizes.
+    Ids outside [0, E) belong to no expert: they are excluded and counted.
+    """
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.reshape(-1).astype(np.int64)
+    valid = (ids >= 0) & (ids < E)
+    s_valid = np.nonzero(valid)[0]
+    order = np.argsort(ids[s_valid], kind="stable")
+    perm = s_valid[order]
+    counts = np.bincount(ids[valid], minlength=E).astype(np.int64)
+    offsets = np.cumsum(counts).astype(np.int32)
+    starts = offsets.astype(np.int64) - counts
+    if topk_weights is None:
+        row_weight = np.ones(perm.shape[0], dtype=np.float32)
+    else:
+        row_weight = np.asarray(topk_weights).reshape(-1)[perm]
+    return Schedule(E, k, counts, offsets, starts, perm, perm // k, row_weight,
+                    int((~valid).sum()))
+
+
+def group_rows(offsets: np.ndarray) -> list:
+    """Row ranges of each group from END offsets ([GG] "Data layout, offsets and
+    alignment"): group e owns rows [offs[e-1], offs[e]), with offs[-1] := 0."""
+    offs = np.asarray(offsets, dtype=np.int64)
+    prev = np.concatenate([[0], offs[:-1]])
+    return [range(int(a), int(b)) for a, b in zip(prev, offs)]
+
+
+# ----------------------------------------------------------------------------
+# Tile space ([GG] "Problem descriptors and the tile scheduler")
+# ----------------------------------------------------------------------------
+@dataclass
+class TileSpace:
+    BM: int
+    BN: int
+    tiles_n: int
+    tiles: np.ndarray       # [E] int64
+    tile_start: np.ndarray  # [E] int64, exclusive prefix
+    total: int
+
+
+def tile_space(counts: np.ndarray, N: int, BM: int, BN: int) -> TileSpace:
+    """Group g contributes ceil(M_g/BM) * ceil(N/BN) output tiles; an exclusive
+    prefix sum gives each group's first tile; the total is one flat space."""
+    tiles_n = int(_cdiv(N, BN))
+    tiles = _cdiv(counts, BM) * tiles_n
+    tile_start = np.concatenate([[0], np.cumsum(tiles)[:-1]]).astype(np.int64)
+    total = int(tile_start[-1] + tiles[-1]) if len(tiles) else 0
+    return TileSpace(BM, BN, tiles_n, tiles.astype(np.int64), tile_start, total)
+
+
+def tile_owner(ts: TileSpace, tau) -> np.ndarray:
+    """Owning group of tile index tau: the upper bound of tau in the start
+    prefix, minus one.  With empty groups several starts are equal; the upper
+    bound picks the last of them, the only one that owns tiles there."""
+    return np.searchsorted(ts.tile_start, np.asarray(tau), side="right") - 1
+
+
+def tile_coords(ts: TileSpace, counts: np.ndarray, offsets: np.ndarray, tau: int):
+    """(group, row block, column block, first row, rows) of tile tau.
+
+    Inside a group the walk is column-block-major: consecutive tile indices
+    share one column block of the group's weights and step over row blocks
+    ([GG] "Problem descriptors and the tile scheduler", on reusing B_g from
+    L2).  The last row block of a group is ragged; its rows past the group end
+    are masked.
+    """
+    g = int(tile_owner(ts, tau))
+    local = int(tau) - int(ts.tile_start[g])
+    mblocks = int(_cdiv(counts[g], ts.BM))
+    nb, mb = divmod(local, mblocks)
+    start = 0 if g == 0 else int(offsets[g - 1])
+    row0 = start + mb * ts.BM
+    rows = min(ts.BM, int(counts[g]) - mb * ts.BM)
+    return g, mb, nb, row0, rows
+
+
+# ----------------------------------------------------------------------------
+# Masked fixed-capacity layout ([NOTE] section 5, "Masked" decode layout)
+# ----------------------------------------------------------------------------
+@dataclass
+class MaskedSchedule:
+    E: int
+    capacity: int
+    masked_m: np.ndarray     # [E] valid rows per expert = min(m_e, capacity)
+    slot_assign: np.ndarray  # [E, capacity] assignment id or -1
+    slot_token: np.ndarray   # [E, capacity] token or -1
+    slot_weight: np.ndarray  # [E, capacity] routing weight, 0 for empty slots
+    n_invalid: int
+    n_dropped: int
+
+
+def masked_schedule(expert_ids, topk_weights, E: int, capacity: int) -> MaskedSchedule:
+    """Each expert reserves ``capacity`` row slots; its assignments fill them in
+    ascending assignment order and the valid rows are the prefix
+    0 .. min(m_e, capacity)-1.  Assignments beyond the capacity are dropped (the
+    fixed-capacity approach drops tokens, [NOTE] section 2) and counted."""
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.reshape(-1).astype(np.int64)
+    w = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    slot_assign = np.full((E, capacity), -1, dtype=np.int64)
+    fill = np.zeros(E, dtype=np.int64)
+    n_invalid = n_dropped = 0
+    for s in range(ids.shape[0]):
+        e = ids[s]
+        if e < 0 or e >= E:
+            n_invalid += 1
+            continue
+        if fill[e] < capacity:
+            slot_assign[e, fill[e]] = s
+        else:
+            n_dropped += 1
+        fill[e] += 1
+    valid = slot_assign >= 0
+    slot_token = np.where(valid, slot_assign // k, -1)
+    slot_weight = np.zeros((E, capacity), dtype=np.float64 if w is None else w.dtype)
+    if w is None:
+        slot_weight[valid] = 1.0
+    else:
+        slot_weight[valid] = w[slot_assign[valid]]
+    return MaskedSchedule(E, capacity, np.minimum(fill, capacity), slot_assign, slot_token,
+                          slot_weight, n_invalid, n_dropped)
+
+
+# ----------------------------------------------------------------------------
+# Products
+# ----------------------------------------------------------------------------
+def grouped_gemm(A: np.ndarray, W: np.ndarray, offsets: np.ndarray, *, acc=np.float64,
+                 out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Bare grouped GEMM: rows already grouped by expert; for every group e,
+    C[rows of e] = A[rows of e] @ W[e]^T ([GG] loop reference in "Data layout,
+    offsets and alignment"; [CARD] "How it works", the kernel with the maps
+    omitted).  Rows at or past offs[E-1] are not written (``out`` keeps them)."""
+    A = np.asarray(A)
+    M = A.shape[0]
+    N = W.shape[1]
+    C = np.zeros((M, N), dtype=acc) if out is None else np.array(out, dtype=acc, copy=True)
+    for e, rows in enumerate(group_rows(offsets)):
+        if len(rows) == 0:
+            continue
+        C[rows.start:rows.stop] = A[rows.start:rows.stop].astype(acc) @ W[e].astype(acc).T
+    return C
+
+
+def moe_forward_explicit(x, W, expert_ids, topk_weights, E: int, *, acc=np.float64) -> np.ndarray:
+    """The unfused path: gather the token copies in expert order, run the bare
+    grouped GEMM, then un-permute and combine by routing weight ([GG] "Data
+    layout, offsets and alignment"; [NOTE] 4.1 permute, 4.3 un-permute with
+    gating weights; [CARD] "Correctness", the explicit gather -> grouped GEMM ->
+    scatter path).  The weight scales the fp32/fp64 product, not the input.
+    Contributions are added to y in ascending sorted-row order."""
+    sch = routing_schedule(expert_ids, topk_weights, E)
+    T = x.shape[0]
+    N = W.shape[1]
+    xs = np.asarray(x)[sch.row_to_token]                 # [S, K] permuted copies
+    ys = grouped_gemm(xs, W, sch.offsets, acc=acc)       # [S, N]
+    y = np.zeros((T, N), dtype=acc)
+    np.add.at(y, sch.row_to_token, sch.row_weight.astype(acc)[:, None] * ys)
+    return y
+
+
+def moe_forward(x, W, expert_ids, topk_weights, E: int, *, acc=np.float64) -> np.ndarray:
+    """The fused form ([CARD] intro and "How it works"): for each expert, gather
+    its token rows, multiply by its weights, scale by the routing weight and add
+    into the token's output row; nothing of shape [S, K] or [S, N] is built.
+
+    y[t, n] = sum_j w[t, j] * sum_k x[t, k] * W[ids[t, j], n, k].
+    Experts are visited in ascending order and each expert's assignments in
+    ascending s, which is the explicit path's order, so the two agree bit for
+    bit in any precision ([CARD] "Correctness": the fusion is exact)."""
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.reshape(-1)
+    wflat = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    N = W.shape[1]
+    y = np.zeros((T, N), dtype=acc)
+    for e in range(E):
+        s_e = np.nonzero(ids == e)[0]
+        if s_e.size == 0:
+            continue
+        tok = s_e // k
+        z = np.asarray(x)[tok].astype(acc) @ W[e].astype(acc).T
+        we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
+        np.add.at(y, tok, we[:, None] * z)
+    return y
+
+
+def moe_backward(dY, x, W, expert_ids, topk_weights, E: int, *, acc=np.float64):
+    """Gradients of L = sum(dY * y) for the fused layer.
+
+    [GG] "The backward pass": with Y_g = X_g W_g, the input gradient is
+    dY_g W_g^T (the forward pattern with the weights read transposed) and the
+    weight gradient is X_g^T dY_g, a reduction over the group's rows; an
+    expert with no rows gets an exact zero gradient.  In (E, N, K) storage the
+    weight gradient of expert e is sum over its rows of (w * dY[t])^T x[t].
+    [CARD] "How it works": the token gradient is scattered with the routing
+    weight like the forward; the routing-weight gradient is the inner product
+    of the incoming gradient with the unweighted per-assignment product.
+
+    Returns dX [T, K], dW [E, N, K], d_w [T, k].
+    """
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.reshape(-1)
+    wflat = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    K = x.shape[1]
+    N = W.shape[1]
+    dX = np.zeros((T, K), dtype=acc)
+    dW = np.zeros((E, N, K), dtype=acc)
+    d_w = np.zeros(T * k, dtype=acc)
+    xa = np.asarray(x)
+    dYa = np.asarray(dY)
+    for e in range(E):
+        s_e = np.nonzero(ids == e)[0]
+        if s_e.size == 0:
+            continue                      # dW[e] stays exactly zero
+        tok = s_e // k
+        We = W[e].astype(acc)            # [N, K]
+        we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
+        g_rows = dYa[tok].astype(acc)    # [m_e, N]
+        x_rows = xa[tok].astype(acc)     # [m_e, K]
+        G = g_rows @ We                  # unweighted input gradient per assignment
+        np.add.at(dX, tok, we[:, None] * G)
+        dW[e] = (we[:, None] * g_rows).T @ x_rows
+        Z = x_rows @ We.T                # unweighted forward product per assignment
+        d_w[s_e] = np.sum(g_rows * Z, axis=1)
+    return dX, dW, d_w.reshape(T, k)
+
+
+def grouped_weight_grad(X, dY, offsets, E: int, *, acc=np.float64) -> np.ndarray:
+    """Weight gradient of the bare grouped GEMM with rows already grouped:
+    dW[e] = (dY[rows of e])^T X[rows of e], stored (E, N, K); zero for an empty
+    group ([GG] "The backward pass", the variable-K grouped GEMM)."""
+    K = X.shape[1]
+    N = dY.shape[1]
+    dW = np.zeros((E, N, K), dtype=acc)
+    for e, rows in enumerate(group_rows(offsets)):
+        if len(rows) == 0:
+            continue
+        dW[e] = np.asarray(dY[rows.start:rows.stop]).astype(acc).T @ np.asarray(X[rows.start:rows.stop]).astype(acc)
+    return dW
+
+
+def masked_forward(x, W, ms: MaskedSchedule, T: int, *, acc=np.float64) -> np.ndarray:
+    """Decode forward on the masked layout: for every expert, only the valid row
+    prefix of its slots contributes; each valid slot adds its routing-weighted
+    product to its token's output row ([NOTE] section 5, masked layout)."""
+    N = W.shape[1]
+    y = np.zeros((T, N), dtype=acc)
+    for e in range(ms.E):
+        m = int(ms.masked_m[e])
+        if m == 0:
+            continue
+        tok = ms.slot_token[e, :m]
+        z = np.asarray(x)[tok].astype(acc) @ W[e].astype(acc).T
+        np.add.at(y, tok, ms.slot_weight[e, :m].astype(acc)[:, None] * z)
+    return y
+
+
+# ----------------------------------------------------------------------------
+# Sampled evaluation for full-size parity checks
+# ----------------------------------------------------------------------------
+def moe_forward_rows(x, W, expert_ids, topk_weights, tokens, *, acc=np.float64) -> np.ndarray:
+    """y[t, :] for the listed tokens only, straight from the definition
+    y[t] = sum_j w[t, j] * (x[t] @ W[ids[t, j]]^T)."""
+    expert_ids = np.asarray(expert_ids)
+    out = np.zeros((len(tokens), W.shape[1]), dtype=acc)
+    for i, t in enumerate(tokens):
+        xt = np.asarray(x)[t].astype(acc)
+        for j in range(expert_ids.shape[1]):
+            e = int(expert_ids[t, j])
+            w = 1.0 if topk_weights is None else float(topk_weights[t, j])
+            out[i] += acc(w) * (W[e].astype(acc) @ xt)
+    return out
+
+
+def moe_backward_rows(dY, x, W, expert_ids, topk_weights, tokens, *, acc=np.float64):
+    """dX[t, :] and d_w[t, :] for the listed tokens only, from the definitions
+    dX[t] = sum_j w[t, j] * dY[t] @ W[e_tj],  d_w[t, j] = dY[t] . (W[e_tj] @ x[t])."""
+    expert_ids = np.asarray(expert_ids)
+    k = expert_ids.shape[1]
+    dX = np.zeros((len(tokens), W.shape[2]), dtype=acc)
+    dw = np.zeros((len(tokens), k), dtype=acc)
+    for i, t in enumerate(tokens):
+        g = np.asarray(dY)[t].astype(acc)
+        xt = np.asarray(x)[t].astype(acc)
+        for j in range(k):
+            e = int(expert_ids[t, j])
+            We = W[e].astype(acc)
+            w = 1.0 if topk_weights is None else float(topk_weights[t, j])
+            dX[i] += acc(w) * (g @ We)
+            dw[i, j] = g @ (We @ xt)
+    return dX, dw
+
+
+def weight_grad_entries(dY, x, expert_ids, topk_weights, E: int, entries, *, acc=np.float64) -> np.ndarray:
+    """dW[e, n, k] for listed (e, n, k) triples, from the definition
+    sum over assignments s routed to e of w_s * dY[t_s, n] * x[t_s, k]."""
+    expert_ids = np.asarray(expert_ids)
+    kk = expert_ids.shape[1]
+    ids = expert_ids.reshape(-1)
+    wflat = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    members = {}
+    out = np.zeros(len(entries), dtype=acc)
+    for i, (e, n, kc) in enumerate(entries):
+        if e not in members:
+            members[e] = np.nonzero(ids == e)[0]
+        s_e = members[e]
+        if s_e.size == 0:
+            continue
+        tok = s_e // kk
+        we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
+        out[i] = np.sum(we * np.asarray(dY)[tok, n].astype(acc) * np.asarray(x)[tok, kc].astype(acc))
+    return out

@@ -1,0 +1,122 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by its pins.
+
+Each case swaps one oracle function for a copy with a plausible bug -- start
+offsets passed as end offsets, a lower bound instead of an upper bound, a
+dropped routing weight, a transposed operand -- and checks that at least one
+pin of tests/test_oracle_pins.py then fails.  This shows the pins constrain
+the oracle rather than restate it.
+"""
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+import tests.test_oracle_pins as P
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _mut_start_offsets(orig):
+    def f(expert_ids, topk_weights, E):
+        s = orig(expert_ids, topk_weights, E)
+        s.offsets = s.starts.astype(np.int32)        # wrong convention
+        return s
+    return f
+
+
+def _mut_unstable(orig):
+    def f(expert_ids, topk_weights, E):
+        s = orig(expert_ids, topk_weights, E)
+        ids = np.asarray(expert_ids).reshape(-1)
+        order = np.argsort(-np.arange(ids.size), kind="stable")
+        perm = order[np.argsort(ids[order], kind="stable")]   # ties in descending s
+        s.perm = perm
+        s.row_to_token = perm // np.asarray(expert_ids).shape[1]
+        if topk_weights is not None:
+            s.row_weight = np.asarray(topk_weights).reshape(-1)[perm]
+        return s
+    return f
+
+
+def _lower_bound(ts, tau):
+    return np.searchsorted(ts.tile_start, np.asarray(tau), side="left") - 1
+
+
+def _row_block_major(orig):
+    def f(ts, counts, offsets, tau):
+        g = int(O.tile_owner(ts, tau))
+        local = int(tau) - int(ts.tile_start[g])
+        mb, nb = divmod(local, ts.tiles_n)
+        start = 0 if g == 0 else int(offsets[g - 1])
+        return g, mb, nb, start + mb * ts.BM, min(ts.BM, int(counts[g]) - mb * ts.BM)
+    return f
+
+
+def _fwd_no_weight(x, W, expert_ids, topk_weights, E, *, acc=np.float64):
+    return _ORIG["moe_forward"](x, W, expert_ids, None, E, acc=acc)
+
+
+def _fwd_untransposed(x, W, expert_ids, topk_weights, E, *, acc=np.float64):
+    Wt = np.swapaxes(np.asarray(W), 1, 2)      # multiplies by W[e] instead of W[e]^T
+    return _ORIG["moe_forward"](x, Wt, expert_ids, topk_weights, E, acc=acc)
+
+
+def _gg_untransposed(A, W, offsets, *, acc=np.float64, out=None):
+    return _ORIG["grouped_gemm"](A, np.swapaxes(np.asarray(W), 1, 2), offsets, acc=acc, out=out)
+
+
+def _bwd_weighted_dw(dY, x, W, expert_ids, topk_weights, E, *, acc=np.float64):
+    dX, dW, d_w = _ORIG["moe_backward"](dY, x, W, expert_ids, topk_weights, E, acc=acc)
+    return dX, dW, d_w * np.asarray(topk_weights)  # uses the weighted product
+
+
+def _bwd_unweighted_dx(dY, x, W, expert_ids, topk_weights, E, *, acc=np.float64):
+    _, dW, d_w = _ORIG["moe_backward"](dY, x, W, expert_ids, topk_weights, E, acc=acc)
+    dX, _, _ = _ORIG["moe_backward"](dY, x, W, expert_ids, None, E, acc=acc)
+    return dX, dW, d_w
+
+
+def _bwd_dw_transposed_sum(dY, x, W, expert_ids, topk_weights, E, *, acc=np.float64):
+    dX, dW, d_w = _ORIG["moe_backward"](dY, x, W, expert_ids, None, E, acc=acc)
+    dX2, _, d_w2 = _ORIG["moe_backward"](dY, x, W, expert_ids, topk_weights, E, acc=acc)
+    return dX2, dW, d_w2                       # dW without the routing weight
+
+
+_ORIG = {n: getattr(O, n) for n in ["routing_schedule", "tile_owner", "tile_coords", "moe_forward",
+                                     "grouped_gemm", "moe_backward"]}
+
+CASES = [
+    ("end offsets replaced by start offsets", "routing_schedule", lambda: _mut_start_offsets(_ORIG["routing_schedule"]),
+     [P.test_offsets_page_examples]),
+    ("unstable sort", "routing_schedule", lambda: _mut_unstable(_ORIG["routing_schedule"]),
+     [P.test_sorted_rows_brute_force]),
+    ("lower bound owner lookup", "tile_owner", lambda: _lower_bound,
+     [lambda: P.test_tile_owner_brute_force.hypothesis.inner_test([2, 0, 0, 5], 7, 16, 16)]),
+    ("row-block-major walk", "tile_coords", lambda: _row_block_major(_ORIG["tile_coords"]),
+     [P.test_column_block_major_walk]),
+    ("routing weight dropped", "moe_forward", lambda: _fwd_no_weight,
+     [lambda: P.test_moe_forward_brute_force(0), P.test_rank_one_closed_form]),
+    ("weights not transposed", "moe_forward", lambda: _fwd_untransposed,
+     [P.test_rank_one_closed_form]),
+    ("grouped GEMM weights not transposed", "grouped_gemm", lambda: _gg_untransposed,
+     [P.test_single_expert_is_plain_matmul]),
+    ("routing-weight gradient from the weighted product", "moe_backward", lambda: _bwd_weighted_dw,
+     [P.test_backward_finite_differences, P.test_backward_euler_identities]),
+    ("token gradient without the routing weight", "moe_backward", lambda: _bwd_unweighted_dx,
+     [P.test_backward_finite_differences, P.test_backward_euler_identities]),
+    ("weight gradient without the routing weight", "moe_backward", lambda: _bwd_dw_transposed_sum,
+     [P.test_backward_finite_differences, P.test_backward_euler_identities]),
+]
+
+
+@pytest.mark.parametrize("name,attr,make,checks", CASES, ids=[c[0] for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, attr, make, checks):
+    for chk in checks:
+        assert not _fails(chk), f"pin fails on the unmodified oracle: {chk}"
+    monkeypatch.setattr(O, attr, make())
+    assert all(_fails(chk) for chk in checks), f"planted mistake not caught: {name}"

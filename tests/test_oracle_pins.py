@@ -1,0 +1,440 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these tests re-types the oracle's own formula: each compares it with a
+value printed on a page, a brute-force evaluation in plain Python, a closed
+form, a finite difference or an identity the definitions imply.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _ids_from_counts(counts, k=1, seed=0):
+    """Assignments whose per-expert counts are ``counts``, shuffled, as [T, k]."""
+    rng = np.random.default_rng(seed)
+    ids = np.repeat(np.arange(len(counts)), counts)
+    rng.shuffle(ids)
+    return ids.reshape(-1, k).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# Offsets and schedule
+# ----------------------------------------------------------------------------
+def test_offsets_page_examples():
+    g = _load("offsets_examples.json")
+    c0 = g["cases"][0]
+    sch = O.routing_schedule(_ids_from_counts(c0["counts"]), None, len(c0["counts"]))
+    assert sch.offsets.dtype == np.int32
+    assert sch.offsets.tolist() == c0["end_offsets"]
+    assert [list(r) for r in O.group_rows(sch.offsets)] == c0["group_rows"]
+    c1 = g["cases"][1]
+    sch = O.routing_schedule(_ids_from_counts(c1["counts"]), None, len(c1["counts"]))
+    assert int(sch.offsets[-1]) == c1["total_rows"]
+    assert sch.counts.tolist() == c1["counts"]
+
+
+def test_sorted_rows_brute_force():
+    """Rows are grouped by expert and, within an expert, in ascending assignment
+    order (a stable sort); row -> token is s div k; row weight is w[s]."""
+    rng = np.random.default_rng(3)
+    T, k, E = 37, 3, 6
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    sch = O.routing_schedule(ids, w, E)
+    expect = []
+    for e in range(E):
+        for t in range(T):
+            for j in range(k):
+                if ids[t, j] == e:
+                    expect.append((t * k + j, t, w[t, j]))
+    assert sch.perm.tolist() == [a for a, _, _ in expect]
+    assert sch.row_to_token.tolist() == [b for _, b, _ in expect]
+    assert sch.row_weight.tolist() == [c for _, _, c in expect]
+    for e, rows in enumerate(O.group_rows(sch.offsets)):
+        assert all(ids.reshape(-1)[sch.perm[r]] == e for r in rows)
+
+
+@settings(max_examples=60, deadline=None)
+@given(st.lists(st.integers(min_value=0, max_value=9), min_size=1, max_size=12),
+       st.integers(min_value=1, max_value=4))
+def test_sum_of_group_sizes(counts, k):
+    """Sum over experts of m_e equals tokens * top_k when no assignment is lost
+    (study notes, section 1)."""
+    total = sum(counts)
+    pad = (-total) % k
+    counts = list(counts)
+    counts[0] += pad
+    ids = _ids_from_counts(counts, k=k, seed=total)
+    sch = O.routing_schedule(ids, None, len(counts))
+    assert int(sch.counts.sum()) == ids.shape[0] * k
+    assert sch.counts.tolist() == counts
+
+
+def test_out_of_range_ids_are_excluded():
+    ids = np.array([[0, 5], [-1, 1], [1, 0]], dtype=np.int32)
+    sch = O.routing_schedule(ids, None, 2)
+    assert sch.n_invalid == 2
+    assert sch.counts.tolist() == [2, 2]
+    assert sch.perm.tolist() == [0, 5, 3, 4]
+
+
+# ----------------------------------------------------------------------------
+# Tile space: the page's worked example
+# ----------------------------------------------------------------------------
+def test_worked_example_balanced():
+    g = _load("worked_example.json")
+    b = g["balanced"]
+    counts = np.full(g["experts"], b["rows_per_expert"])
+    ts = O.tile_space(counts, g["N"], g["BM"], g["BN"])
+    assert ts.tiles_n == b["col_blocks"]
+    assert (ts.tiles == b["tiles_per_expert"]).all()
+    assert ts.total == b["total_tiles"]
+    assert ts.total / g["gpu_sms"] == pytest.approx(b["waves_exact"], abs=0.05)
+    assert math.ceil(ts.total / g["gpu_sms"]) == b["waves"]
+    S = g["tokens"] * g["top_k"]
+    assert int(counts.sum()) == S
+    assert 2 * S * g["K"] * g["N"] / 1e9 == pytest.approx(g["useful_gflop_approx"], rel=0.01)
+
+
+@pytest.mark.parametrize("key", ["skewed", "skewed_bm64"])
+def test_worked_example_skewed(key):
+    g = _load("worked_example.json")
+    case = g[key]
+    BM = case.get("BM", g["BM"])
+    counts = np.concatenate([np.full(n, rows) for n, rows in g["skewed"]["groups"]])
+    assert int(counts.sum()) == g["tokens"] * g["top_k"]
+    ts = O.tile_space(counts, g["N"], BM, g["BN"])
+    row_blocks = ts.tiles // ts.tiles_n
+    per_group = []
+    i = 0
+    for n, _ in g["skewed"]["groups"]:
+        per_group.append(int(row_blocks[i]))
+        i += n
+    assert per_group == case["row_blocks_per_group"]
+    assert int(row_blocks.sum()) == case["row_blocks"]
+    computed = int(row_blocks.sum()) * BM
+    assert computed == case["computed_rows"]
+    useful = 100.0 * counts.sum() / computed
+    assert round(useful) == case["useful_percent"]
+    if key == "skewed":
+        assert ts.total == case["total_tiles"]
+        assert math.ceil(ts.total / g["gpu_sms"]) == case["waves"]
+        bal = O.tile_space(np.full(64, 256), g["N"], BM, g["BN"])
+        assert ts.total / bal.total == pytest.approx(case["cost_ratio_approx"], abs=0.01)
+
+
+@settings(max_examples=80, deadline=None)
+@given(st.lists(st.sampled_from([0, 0, 0, 1, 2, 5, 31, 32, 33, 64, 100]), min_size=1, max_size=10),
+       st.sampled_from([1, 7, 32, 130]), st.sampled_from([16, 32, 64]), st.sampled_from([16, 64]))
+def test_tile_owner_brute_force(counts, N, BM, BN):
+    """Owner of every tile = the unique group whose tile range contains it; the
+    coordinates enumerate every (row block, column block) of every group once."""
+    counts = np.array(counts)
+    offsets = np.cumsum(counts).astype(np.int32)
+    ts = O.tile_space(counts, N, BM, BN)
+    seen = set()
+    for tau in range(ts.total):
+        owners = [e for e in range(len(counts)) if ts.tile_start[e] <= tau < ts.tile_start[e] + ts.tiles[e]]
+        assert len(owners) == 1
+        assert int(O.tile_owner(ts, tau)) == owners[0]
+        g, mb, nb, row0, rows = O.tile_coords(ts, counts, offsets, tau)
+        assert 1 <= rows <= BM
+        assert row0 >= (0 if g == 0 else offsets[g - 1]) and row0 + rows <= offsets[g]
+        assert 0 <= nb < ts.tiles_n
+        seen.add((g, mb, nb))
+    expect = {(e, mb, nb) for e in range(len(counts)) for mb in range(-(-counts[e] // BM))
+              for nb in range(ts.tiles_n)}
+    assert seen == expect
+
+
+def test_column_block_major_walk():
+    """Consecutive tiles of one group share a column block and step over row blocks."""
+    counts = np.array([300, 0, 130])
+    offsets = np.cumsum(counts).astype(np.int32)
+    ts = O.tile_space(counts, 256, 128, 128)
+    coords = [O.tile_coords(ts, counts, offsets, t)[:3] for t in range(ts.total)]
+    assert coords[:6] == [(0, 0, 0), (0, 1, 0), (0, 2, 0), (0, 0, 1), (0, 1, 1), (0, 2, 1)]
+    assert coords[6:] == [(2, 0, 0), (2, 1, 0), (2, 0, 1), (2, 1, 1)]
+
+
+# ----------------------------------------------------------------------------
+# Products: brute force, closed forms, textbook reductions
+# ----------------------------------------------------------------------------
+def _brute_grouped(A, W, offsets):
+    M = len(A)
+    N = len(W[0])
+    K = len(A[0])
+    C = [[0.0] * N for _ in range(M)]
+    prev = 0
+    for e, end in enumerate(offsets):
+        for r in range(prev, end):
+            for n in range(N):
+                s = 0.0
+                for kk in range(K):
+                    s += float(A[r][kk]) * float(W[e][n][kk])
+                C[r][n] = s
+        prev = end
+    return np.array(C)
+
+
+def _dot_bound(a, b):
+    return len(a) * 2.0 ** -52 * np.sum(np.abs(a * b))
+
+
+@pytest.mark.parametrize("counts", [[3, 0, 5], [0, 1, 4], [2, 2, 0], [0, 0, 6], [1]])
+def test_grouped_gemm_brute_force(counts):
+    rng = np.random.default_rng(sum(counts))
+    M, K, N = sum(counts), 7, 5
+    A = rng.standard_normal((M + 2, K))
+    W = rng.standard_normal((len(counts), N, K))
+    offsets = np.cumsum(counts).astype(np.int32)
+    out = np.full((M + 2, N), -7.0)
+    C = O.grouped_gemm(A, W, offsets, out=out)
+    B = _brute_grouped(A.tolist(), W.tolist(), offsets.tolist())
+    assert np.allclose(C[:M], B[:M], rtol=0, atol=1e-12)
+    assert (C[M:] == -7.0).all()
+
+
+def _brute_moe(x, W, ids, w):
+    T, k = ids.shape
+    N, K = W.shape[1], W.shape[2]
+    y = np.zeros((T, N))
+    for t in range(T):
+        for n in range(N):
+            tot = 0.0
+            for j in range(k):
+                e = ids[t, j]
+                s = 0.0
+                for kk in range(K):
+                    s += float(x[t, kk]) * float(W[e, n, kk])
+                tot += float(w[t, j]) * s
+            y[t, n] = tot
+    return y
+
+
+def _tiny_routed(seed, T=5, k=2, E=3, K=7, N=5, empty=1):
+    rng = np.random.default_rng(seed)
+    live = [e for e in range(E) if e != empty]
+    ids = np.array([rng.choice(live, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    W = rng.standard_normal((E, N, K)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    return x, W, ids, w
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_moe_forward_brute_force(seed):
+    x, W, ids, w = _tiny_routed(seed)
+    y = O.moe_forward(x, W, ids, w, 3)
+    y_explicit = O.moe_forward_explicit(x, W, ids, w, 3)
+    ref = _brute_moe(x, W, ids, w)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    assert np.abs(y_explicit - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_single_expert_is_plain_matmul():
+    """E=1, k=1, weight 1: the layer is x @ W[0]^T."""
+    rng = np.random.default_rng(11)
+    T, K, N = 19, 13, 9
+    x = rng.standard_normal((T, K))
+    W = rng.standard_normal((1, N, K))
+    ids = np.zeros((T, 1), dtype=np.int32)
+    y = O.moe_forward(x, W, ids, None, 1)
+    assert np.allclose(y, np.matmul(x, W[0].T), rtol=1e-13, atol=1e-13)
+    C = O.grouped_gemm(x, W, np.array([T], dtype=np.int32))
+    assert np.allclose(C, np.matmul(x, W[0].T), rtol=1e-13, atol=1e-13)
+
+
+def test_rank_one_closed_form():
+    """W[e] = u_e v_e^T in (E, N, K) storage with K != N gives
+    y[t] = sum_j w[t,j] * (v_{e} . x[t]) * u_{e}: a transposed operand or a
+    dropped weight cannot produce it."""
+    rng = np.random.default_rng(5)
+    T, K, N, E, k = 11, 6, 4, 3, 2
+    u = rng.standard_normal((E, N))
+    v = rng.standard_normal((E, K))
+    W = np.einsum("en,ek->enk", u, v)
+    x = rng.standard_normal((T, K))
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    w = rng.random((T, k))
+    y = O.moe_forward(x, W, ids, w, E)
+    expect = np.zeros((T, N))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            expect[t] += w[t, j] * float(v[e] @ x[t]) * u[e]
+    assert np.allclose(y, expect, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("acc", [np.float32, np.float64])
+def test_fused_equals_explicit_bitwise(acc):
+    """The card's 'Correctness' section: the fused forward equals the explicit
+    gather -> grouped GEMM -> scatter path bit for bit in fp32."""
+    rng = np.random.default_rng(21)
+    T, K, N, E, k = 64, 24, 16, 5, 2
+    ids = np.array([rng.choice([0, 1, 3, 4], size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    W = rng.standard_normal((E, N, K)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    a = O.moe_forward(x, W, ids, w, E, acc=acc)
+    b = O.moe_forward_explicit(x, W, ids, w, E, acc=acc)
+    assert a.dtype == acc and np.array_equal(a, b)
+
+
+def test_empty_and_single_row_experts():
+    """'What to do next', step 2: an empty expert and a single-row expert."""
+    rng = np.random.default_rng(8)
+    T, K, N, E = 9, 5, 3, 4
+    ids = np.array([[0], [0], [2], [0], [0], [3], [3], [0], [3]], dtype=np.int32)   # expert 1 empty, 2 single
+    x = rng.standard_normal((T, K))
+    W = rng.standard_normal((E, N, K))
+    y = O.moe_forward(x, W, ids, None, E)
+    assert np.allclose(y[2], W[2] @ x[2], rtol=1e-13, atol=1e-13)
+    W2 = W.copy()
+    W2[1] = np.nan                      # an empty expert's weights are never read
+    y2 = O.moe_forward(x, W2, ids, None, E)
+    assert np.array_equal(y, y2)
+
+
+# ----------------------------------------------------------------------------
+# Backward: finite differences, identities, exact zeros
+# ----------------------------------------------------------------------------
+def _loss(dY, x, W, ids, w, E):
+    return float(np.sum(dY * O.moe_forward(x, W, ids, w, E)))
+
+
+def test_backward_finite_differences():
+    """y is linear in each of x, W and w separately, so a central difference in
+    float64 has no truncation error and must match the analytic gradients up to
+    rounding (the card: the backward agrees with finite differences)."""
+    rng = np.random.default_rng(13)
+    T, K, N, E, k = 6, 5, 4, 3, 2
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    W = rng.standard_normal((E, N, K))
+    w = rng.random((T, k))
+    dY = rng.standard_normal((T, N))
+    dX, dW, d_w = O.moe_backward(dY, x, W, ids, w, E)
+    h = 0.5
+
+    def fd(arr, idx, f):
+        a = arr.copy(); a[idx] += h
+        b = arr.copy(); b[idx] -= h
+        return (f(a) - f(b)) / (2 * h)
+
+    for idx in np.ndindex(x.shape):
+        assert fd(x, idx, lambda a: _loss(dY, a, W, ids, w, E)) == pytest.approx(dX[idx], abs=1e-12)
+    for idx in np.ndindex(W.shape):
+        assert fd(W, idx, lambda a: _loss(dY, x, a, ids, w, E)) == pytest.approx(dW[idx], abs=1e-12)
+    for idx in np.ndindex(w.shape):
+        assert fd(w, idx, lambda a: _loss(dY, x, W, ids, a, E)) == pytest.approx(d_w[idx], abs=1e-12)
+
+
+def test_backward_euler_identities():
+    """L = <dY, y> is linear in x, in W and in w, so
+    <dX, x> = <dW, W> = sum(w * d_w) = L."""
+    rng = np.random.default_rng(17)
+    T, K, N, E, k = 40, 12, 9, 6, 3
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    W = rng.standard_normal((E, N, K))
+    w = rng.random((T, k))
+    dY = rng.standard_normal((T, N))
+    L = float(np.sum(dY * O.moe_forward(x, W, ids, w, E)))
+    dX, dW, d_w = O.moe_backward(dY, x, W, ids, w, E)
+    assert float(np.sum(dX * x)) == pytest.approx(L, rel=1e-12)
+    assert float(np.sum(dW * W)) == pytest.approx(L, rel=1e-12)
+    assert float(np.sum(d_w * w)) == pytest.approx(L, rel=1e-12)
+
+
+def test_weight_grad_of_empty_expert_is_exact_zero():
+    """'The backward pass' and 'What to do next', step 6."""
+    x, W, ids, w = _tiny_routed(4, T=8, E=4, empty=2)
+    dY = np.random.default_rng(4).standard_normal((8, W.shape[1]))
+    _, dW, _ = O.moe_backward(dY, x, W, ids, w, 4)
+    assert np.all(dW[2] == 0.0) and not np.signbit(dW[2]).any()
+    assert np.abs(dW[[0, 1, 3]]).max() > 0
+
+
+def test_backward_brute_force_entries():
+    """Sampled-entry evaluators agree with plain Python loops over the definition."""
+    x, W, ids, w = _tiny_routed(9, T=6, k=2, E=3, K=4, N=3, empty=1)
+    dY = np.random.default_rng(9).standard_normal((6, 3))
+    dX, dW, d_w = O.moe_backward(dY, x, W, ids, w, 3)
+    T, k = ids.shape
+    bx = np.zeros_like(dX)
+    bw = np.zeros_like(dW)
+    bd = np.zeros_like(d_w)
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            for kk in range(x.shape[1]):
+                bx[t, kk] += w[t, j] * sum(dY[t, n] * W[e, n, kk] for n in range(3))
+            for n in range(3):
+                for kk in range(x.shape[1]):
+                    bw[e, n, kk] += w[t, j] * dY[t, n] * x[t, kk]
+            bd[t, j] = sum(dY[t, n] * sum(x[t, kk] * W[e, n, kk] for kk in range(x.shape[1])) for n in range(3))
+    assert np.allclose(dX, bx, atol=1e-12) and np.allclose(dW, bw, atol=1e-12) and np.allclose(d_w, bd, atol=1e-12)
+    toks = [0, 3, 5]
+    rx, rd = O.moe_backward_rows(dY, x, W, ids, w, toks)
+    assert np.allclose(rx, bx[toks], atol=1e-12) and np.allclose(rd, bd[toks], atol=1e-12)
+    ent = [(0, 1, 2), (1, 0, 0), (2, 2, 3)]
+    assert np.allclose(O.weight_grad_entries(dY, x, ids, w, 3, ent), [bw[e] [n][kk] for e, n, kk in ent], atol=1e-12)
+    ry = O.moe_forward_rows(x, W, ids, w, toks)
+    assert np.allclose(ry, _brute_moe(x, W, ids, w)[toks], atol=1e-12)
+
+
+def test_grouped_weight_grad_brute_force():
+    rng = np.random.default_rng(31)
+    counts = [3, 0, 1, 4]
+    M, K, N = sum(counts), 5, 3
+    X = rng.standard_normal((M, K))
+    dY = rng.standard_normal((M, N))
+    offsets = np.cumsum(counts).astype(np.int32)
+    dW = O.grouped_weight_grad(X, dY, offsets, 4)
+    prev = 0
+    for e, end in enumerate(offsets):
+        for n in range(N):
+            for kk in range(K):
+                s = sum(dY[r, n] * X[r, kk] for r in range(prev, end))
+                assert dW[e, n, kk] == pytest.approx(s, abs=1e-12)
+        prev = end
+    assert np.all(dW[1] == 0)
+
+
+# ----------------------------------------------------------------------------
+# Masked layout
+# ----------------------------------------------------------------------------
+def test_masked_equals_contiguous_without_overflow():
+    rng = np.random.default_rng(41)
+    T, K, N, E, k = 30, 8, 6, 7, 3
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    W = rng.standard_normal((E, N, K))
+    w = rng.random((T, k))
+    ms = O.masked_schedule(ids, w, E, capacity=T)
+    assert ms.n_dropped == 0
+    assert np.allclose(O.masked_forward(x, W, ms, T), O.moe_forward(x, W, ids, w, E), rtol=1e-13, atol=1e-13)
+
+
+def test_masked_overflow_drops_latest_assignments():
+    ids = np.array([[0, 1], [0, 2], [0, 1], [1, 0]], dtype=np.int32)
+    ms = O.masked_schedule(ids, None, 3, capacity=2)
+    assert ms.masked_m.tolist() == [2, 2, 1]
+    assert ms.slot_assign.tolist() == [[0, 2], [1, 5], [3, -1]]
+    assert ms.n_dropped == 3       # s=4, 7 (expert 0) and s=6 (expert 1)
+    assert ms.slot_token.tolist() == [[0, 1], [0, 2], [1, -1]]
+    assert ms.slot_weight.tolist() == [[1, 1], [1, 1], [1, 0]]

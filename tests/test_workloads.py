@@ -1,0 +1,73 @@
+"""The seeded input generators: deterministic, and the stated properties hold."""
+import hashlib
+
+import numpy as np
+import pytest
+
+from moe_variable_size_amd import workloads as W
+
+
+def _h(*arrays):
+    m = hashlib.sha256()
+    for a in arrays:
+        m.update(np.ascontiguousarray(a).tobytes())
+    return m.hexdigest()
+
+
+def test_bf16_rounding_is_nearest_even():
+    vals = np.array([1.0, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -9, -2.5], dtype=np.float32)
+    bits, out = W.round_to_bf16(vals)
+    # ties go to even: 1+2^-8 -> 1.0, 1+3*2^-8 -> 1+2^-6 ... (bf16 has 7 fraction bits)
+    assert out.tolist() == [1.0, 1.0, 1.0 + 2.0 ** -6, 1.0, -2.5]
+    assert bits.dtype == np.uint16 and bits[0] == 0x3F80
+
+
+def test_generators_are_deterministic():
+    a = W.routed("t", 33, 24, 40, 5, 2, seed=7)
+    b = W.routed("t", 33, 24, 40, 5, 2, seed=7)
+    assert _h(a.x.bits, a.W.bits, a.expert_ids, a.topk_weights, a.dY.bits) == \
+        _h(b.x.bits, b.W.bits, b.expert_ids, b.topk_weights, b.dY.bits)
+    c = W.routed("t", 33, 24, 40, 5, 2, seed=8)
+    assert _h(a.x.bits) != _h(c.x.bits)
+    r = W.routed("t", 33, 24, 40, 5, 2, seed=7, dense=False)
+    assert np.array_equal(r.expert_ids, a.expert_ids) and np.array_equal(r.topk_weights, a.topk_weights)
+
+
+def test_config1_shapes():
+    g = W.config1()
+    assert g.group_sizes.tolist() == [40, 0, 88, 128]
+    assert g.A.shape == (256, 128) and g.W.shape == (4, 128, 128) and g.A.bits is None
+
+
+def test_config2_routing():
+    r = W.config2(dense=False)
+    assert r.expert_ids.shape == (4096, 2)
+    assert (r.expert_ids[:, 0] != r.expert_ids[:, 1]).all()
+    assert r.topk_weights.dtype == np.float32 and (0 <= r.topk_weights).all() and (r.topk_weights < 1).all()
+    c = np.bincount(r.expert_ids.reshape(-1), minlength=8)
+    assert c.sum() == 8192 and c.min() > 900
+
+
+def test_config3_routing_is_skewed_with_empties():
+    r = W.config3(dense=False)
+    ids = r.expert_ids
+    assert ids.shape == (8192, 4)
+    assert all(len(set(row)) == 4 for row in ids[:500].tolist())
+    c = np.bincount(ids.reshape(-1), minlength=64)
+    assert (c == 0).sum() == 4 and sorted(np.nonzero(c == 0)[0].tolist()) == r.notes["zero_experts"]
+    assert c.max() > 10 * np.median(c[c > 0])
+    assert np.allclose(r.topk_weights.sum(axis=1), 1.0, atol=1e-6)
+
+
+def test_config4_seed_rule():
+    g = W.config4(dense=False)
+    assert g.group_sizes.sum() == 65536 and len(g.group_sizes) == 128
+    assert (g.group_sizes == 0).sum() >= 1 and (g.group_sizes > 4096).sum() >= 2
+    assert g.seed >= W.BASE_SEED + 4
+
+
+def test_config5_fits_capacity():
+    r = W.config5(dense=False)
+    c = np.bincount(r.expert_ids.reshape(-1), minlength=64)
+    assert r.capacity == 64 and c.max() <= 64 and c.min() > 0
+    assert all(len(set(row)) == 8 for row in r.expert_ids.tolist())
