@@ -1,0 +1,164 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE grouped GEMM layer on one MI355X.
+
+One step = the whole hot path on one batch: build the routing schedule on the
+device, the fused forward (gather on load, weighted atomic scatter-combine),
+and the fused backward (dX with the routing-weight gradient, and dW).
+
+Workload (seeded, synthetic, resident in HBM before timing): T=4096 tokens,
+K=N=2048, E=8 experts, top-2 routing drawn uniformly, routing weights U[0,1),
+x, dY ~ N(0,1), W ~ N(0,1/K), bf16 storage with fp32 accumulation.
+
+Metric: useful TFLOP/s = (2SKN forward + 4SKN backward + 2SN routing-weight
+gradient) / step time, S = T*top_k; padding is never counted.
+
+Prints ONE JSON line.  --gpus above 1 is not supported (one GPU per process,
+single-GPU machine) and exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("useful TFLOP/s (2·S·K·N) + % bf16 MFMA peak, fused MoE fwd/bwd; "
+          "decode HBM GB/s")
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(r, flops_step: float) -> dict:
+    """The CPU oracle, untuned, on the host cores: one full step (forward and
+    backward) of the same workload."""
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((d.get("num_threads", 1) for d in info), default=1)
+        blas = ",".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in info}))
+    except Exception:  # pragma: no cover
+        threads, blas = os.cpu_count() or 1, "unknown"
+    t0 = time.perf_counter()
+    O.moe_forward(r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+    O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops_step / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "one full step (forward + backward, float64) of the same workload",
+            "seconds": round(dt, 3), "host_cpu": platform.processor() or platform.machine(),
+            "blas": blas}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported by this build "
+              "(single-GPU path; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_variable_size_amd import api
+    from moe_variable_size_amd import workloads as WL
+
+    r = WL.config2()
+    T, K, N, E, k = r.T, r.K, r.N, r.E, r.k
+    S = T * k
+    dev = torch.device("cuda:0")
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, W, dY = to_dev(r.x), to_dev(r.W), to_dev(r.dY)
+    ids = torch.from_numpy(r.expert_ids).to(dev)
+    w = torch.from_numpy(r.topk_weights).to(dev)
+    ws = torch.empty(api.moe_schedule_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dX = torch.empty((T, K), dtype=torch.float32, device=dev)
+    dW = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    dT = torch.empty((T, k), dtype=torch.float32, device=dev)
+
+    def step():
+        sch = api.moe_build_schedule(ids, w, E, workspace=ws)
+        api.moe_fused_fwd(x, W, sch, y=y)
+        api.moe_fused_bwd(dY, x, W, sch, out_dX=dX, out_dW=dW, out_dtopk=dT)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, synchronised on both sides
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
+
+    # per-kernel durations: HIP events recorded by the library on each launch's
+    # own stream, over a second run of the same steps
+    api.moe_timing_enable(True)
+    for _ in range(a.steps):
+        step()
+    torch.cuda.synchronize()
+    api.moe_timing_enable(False)
+    fams = ["build_schedule", "fill_zero", "fused_fwd", "bwd_dx", "bwd_dw"]
+    kt = {}
+    for f in fams:
+        tot, n = api.moe_timing_read(f)
+        kt[f] = {"avg_us": round(tot * 1e3 / max(n, 1), 3), "launches": n}
+
+    gemm = 2.0 * S * K * N
+    flops_step = 3 * gemm + 2.0 * S * N
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    # dominant kernel = the grouped GEMM family with the largest time per launch
+    dom = max(["fused_fwd", "bwd_dx", "bwd_dw"], key=lambda f: kt[f]["avg_us"])
+    dom_flops = gemm + (2.0 * S * N if dom == "bwd_dx" else 0.0)
+    achieved = dom_flops / (kt[dom]["avg_us"] * 1e-6) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded numpy PCG64; bf16 storage, fp32 accumulation)",
+        "config": {"workload": f"{r.name} fwd+bwd step (schedule + fused fwd + dX/d_topk + dW)",
+                   "T": T, "K": K, "N": N, "E": E, "top_k": k, "S": S,
+                   "routing": "2 distinct experts per token, uniform; weights U[0,1)"},
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "kernels_us": kt,
+        "fwd_tflops": round(gemm / (kt["fused_fwd"]["avg_us"] * 1e-6) / 1e12, 2),
+        "bwd_tflops": round((2 * gemm + 2.0 * S * N)
+                            / ((kt["bwd_dx"]["avg_us"] + kt["bwd_dw"]["avg_us"]) * 1e-6) / 1e12, 2),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(r, flops_step)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

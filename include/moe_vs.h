@@ -1,0 +1,241 @@
+/*
+ * moe_vs.h -- C ABI of the MI355X (gfx950) MoE variable-size grouped GEMM.
+ *
+ * One launch computes Y_e = X_e W_e for every expert e, where K and N are shared
+ * and the row count m_e of each expert is data-dependent, may be zero, and sums
+ * to T*k.  Pages the operations follow:
+ *   [GG]   "Grouped GEMM for MoE, in depth" (aicassindra.com)
+ *   [CARD] "grouped-gemm-moe" (model card of a published grouped GEMM kernel)
+ *   [NOTE] "Grouped GEMM" (scholia-log study notes)
+ *
+ * Conventions shared by every call:
+ *   - Every array argument is a DEVICE pointer unless stated otherwise; arrays
+ *     are dense, row-major, with unit last stride.  The caller owns every
+ *     buffer; no pointer is retained after a call returns.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  No call synchronises with the device, reads device data back to
+ *     the host, or allocates/frees device memory, so the whole layer can be
+ *     captured in a HIP graph ([GG] "Problem descriptors and the tile
+ *     scheduler": the schedule is computed on the device; "Failure modes": no
+ *     host sync per layer).
+ *   - Argument errors that the host can see (NULL pointers, sizes, dtypes,
+ *     alignment, workspace size) return a nonzero MOE_ERR_* code BEFORE anything
+ *     is launched.  A failed launch returns MOE_ERR_HIP.  Errors that depend on
+ *     device data are never trapped: they are counted in the schedule's status
+ *     words (see moe_schedule).
+ *   - An assignment is one (token t, slot j) entry of expert_ids [T, k]; it is
+ *     numbered s = t*k + j.
+ *   - Expert weights are stored (E, N, K) like nn.Linear ([GG] "Data layout,
+ *     offsets and alignment"): the forward product of a row x is x W[e]^T.
+ *   - Offsets are int32 END offsets: offsets[e] = one past the last row of
+ *     group e, so counts [3,0,5] give offsets [3,3,8] ([GG] "Data layout,
+ *     offsets and alignment").  Empty groups are legal.
+ *   - dtype codes: MOE_F32 (float) or MOE_BF16 (bfloat16 bit patterns).  The
+ *     bf16 path multiplies on the matrix cores with fp32 accumulation; the fp32
+ *     path is exact fp32 (no reduced-precision products) ([CARD] "How it works").
+ *   - Sizes: every tensor handed to a call must be smaller than 2^31 bytes
+ *     (x, dY and each expert's weight slice are addressed with 32-bit offsets);
+ *     E <= 1024; 1 <= k <= 64.
+ */
+#ifndef MOE_VS_H
+#define MOE_VS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define MOE_OK 0
+#define MOE_ERR_NULL 1      /* a required pointer is NULL                          */
+#define MOE_ERR_SHAPE 2     /* a size is out of range or sizes are inconsistent    */
+#define MOE_ERR_DTYPE 3     /* unsupported dtype or dtype combination              */
+#define MOE_ERR_ALIGN 4     /* a pointer is not aligned as the call requires       */
+#define MOE_ERR_WORKSPACE 5 /* workspace NULL or smaller than the query returned   */
+#define MOE_ERR_HIP 6       /* the HIP runtime reported an error at launch         */
+#define MOE_ERR_LIMIT 7     /* a size exceeds a documented library limit          */
+
+/* ---- dtype and layout codes --------------------------------------------- */
+#define MOE_F32 0
+#define MOE_BF16 1
+#define MOE_LAYOUT_CONTIGUOUS 0 /* rows of all experts concatenated (training / prefill) */
+#define MOE_LAYOUT_MASKED 1     /* fixed capacity slots per expert (decode)               */
+
+/* Row-block prefixes are kept for these tile heights (index i -> 32 << i). */
+#define MOE_NUM_BM 4
+
+/*
+ * Routing schedule: a host-side descriptor filled by moe_build_schedule.  All
+ * array members point into the caller's device workspace.  The descriptor is
+ * plain data: copy it freely; it stays valid as long as the workspace does.
+ *
+ * Contiguous layout ([GG] "Data layout, offsets and alignment"; [CARD] "How it
+ * works"): the assignments are sorted stably by expert, so row r (0 <= r <
+ * offsets[E-1]) of the virtual sorted matrix is assignment row_to_assign[r];
+ * rows of expert e are [offsets[e]-counts[e], offsets[e]) and come in ascending
+ * assignment order.  Rows at or past offsets[E-1] (only when some ids are out
+ * of range) hold -1 / weight 0.
+ *
+ * Masked layout ([NOTE] section 5): expert e owns the `capacity` rows
+ * [e*capacity, (e+1)*capacity); its j-th assignment (ascending s) sits in row
+ * e*capacity + j when j < capacity and is dropped otherwise; counts[e] =
+ * min(m_e, capacity) valid rows form a prefix; empty slots hold -1 / weight 0.
+ */
+typedef struct moe_schedule {
+  int64_t T;        /* tokens                                                */
+  int64_t S;        /* assignments T*k                                       */
+  int64_t R;        /* rows of the row maps: S (contiguous) or E*capacity    */
+  int32_t k;        /* experts per token                                     */
+  int32_t E;        /* experts                                               */
+  int32_t layout;   /* MOE_LAYOUT_*                                          */
+  int32_t capacity; /* masked: slots per expert; contiguous: 0               */
+  int32_t *counts;        /* [E]  rows per expert (masked: min(m_e, capacity))  */
+  int32_t *offsets;       /* [E]  END offsets = inclusive prefix sum of counts  */
+  int32_t *block_start;   /* [MOE_NUM_BM][E+1] exclusive prefix of
+                             ceil(counts[e] / BM) for BM = 32, 64, 128, 256;
+                             entry E is the total number of row blocks          */
+  int32_t *expert_order;  /* [E]  experts by descending count (ties: lower id)  */
+  int32_t *row_to_assign; /* [R]  assignment s of each row, or -1               */
+  int32_t *row_to_token;  /* [R]  token s / k of each row, or -1                */
+  float *row_weight;      /* [R]  routing weight of each row (1 when no weights
+                             were given), 0 for an empty row                    */
+  int32_t *status;        /* [2]  {#assignments with expert id outside [0, E),
+                                   #assignments dropped over capacity}          */
+} moe_schedule;
+
+/* Bytes of device workspace moe_build_schedule needs (256-byte aligned
+ * internally).  Returns 0 for invalid sizes. */
+size_t moe_schedule_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t layout,
+                                    int32_t capacity);
+
+/*
+ * Build the routing schedule on the device: per-expert counts (bincount), END
+ * offsets (int32 inclusive scan), the row-block/tile prefix, a stable counting
+ * sort by expert giving row -> assignment, row -> token and the per-row
+ * routing weight, and (masked layout) the fixed-capacity slots.
+ * [GG] "Data layout, offsets and alignment" (argsort(stable), bincount, int32
+ * cumsum); [GG] "Problem descriptors and the tile scheduler" (tiles per group,
+ * prefix, total, on the device); [CARD] "How it works" (row -> token map,
+ * per-row weight, tile layout); [NOTE] 4.1 permute and section 5 masked layout.
+ *
+ *   expert_ids   [T, k] int32 device; ids outside [0, E) are excluded from every
+ *                group and counted in status[0].
+ *   topk_weights [T, k] float device, or NULL for weight 1.
+ *   layout       MOE_LAYOUT_CONTIGUOUS (capacity ignored) or MOE_LAYOUT_MASKED
+ *                (1 <= capacity <= 65536; E*capacity < 2^31).
+ *   workspace    device buffer of at least moe_schedule_workspace_bytes(...)
+ *                bytes, 256-byte aligned; owned by the caller; holds every
+ *                array of the schedule.
+ *   sched        HOST pointer; filled on return (before the device work ends).
+ * Requires T >= 1, 1 <= k <= 64, 1 <= E <= 1024, T*k < 2^31.
+ */
+int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T,
+                       int32_t k, int32_t E, int32_t layout, int32_t capacity,
+                       void *workspace, size_t workspace_bytes, moe_schedule *sched,
+                       void *stream);
+
+/*
+ * Bare variable-size grouped GEMM, rows already grouped by expert ([GG] "Problem
+ * descriptors and the tile scheduler"; [CARD] "How it works", the kernel with
+ * the permutation maps omitted):
+ *     C[r, n] = sum_k A[r, k] * W[e(r), n, k]   for r < offsets[E-1],
+ * where e(r) is the group whose row range holds r.  Rows r >= offsets[E-1] of C
+ * are not written.  One persistent launch covers every group; the tile space is
+ * derived on the device from `offsets`.
+ *   A [M, K], W [E, N, K] in `dtype`; offsets [E] int32 END offsets,
+ *   non-decreasing, offsets[E-1] <= M; C [M, N] in `out_dtype`.
+ *   dtype MOE_F32 -> out_dtype MOE_F32; dtype MOE_BF16 -> MOE_BF16 or MOE_F32.
+ *   M may be 0 (nothing is launched).  Any K, N >= 1 (tails are guarded).
+ */
+int grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int64_t M,
+                 int64_t K, int64_t N, int32_t E, int32_t dtype, int32_t out_dtype,
+                 void *stream);
+
+/*
+ * Fused MoE forward ([CARD] intro and "How it works"): activation rows are
+ * gathered through row -> token as they are loaded, each tile multiplies by its
+ * expert's weights, and each result is scaled by its routing weight and added
+ * atomically into the token's output row, so neither the [S, K] permuted input
+ * nor the [S, N] expanded output is stored:
+ *     y[t, n] = sum_j w[t, j] * sum_k x[t, k] * W[ids[t, j], n, k].
+ * Works on both layouts (masked = the decode path; tiles with no valid rows
+ * skip their weights).
+ *   x [T, K] and W [E, N, K] in `dtype`; sched from moe_build_schedule;
+ *   y [T, N] float, OVERWRITTEN (zeroed by the call, then accumulated).
+ * With dtype MOE_F32 and k <= 2 the result is bitwise reproducible.
+ */
+int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float *y,
+                  int64_t K, int64_t N, int32_t dtype, void *stream);
+
+/* Bytes of device workspace moe_fused_bwd needs for these sizes (may be 0). */
+size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64_t N,
+                                     int32_t dtype);
+
+/*
+ * Fused MoE backward for L = sum(dY * y) ([GG] "The backward pass"; [CARD]
+ * "How it works"):
+ *   dX[t, k]     = sum_j w[t,j] * sum_n dY[t, n] * W[ids[t,j], n, k]
+ *                  (the fused forward run on dY with each expert's weights
+ *                  transposed; gather on load, weighted atomic scatter);
+ *   dW[e, n, k]  = sum over assignments s routed to e of
+ *                  w_s * dY[t_s, n] * x[t_s, k]   (a per-expert A^T B reduction
+ *                  whose reduction length m_e varies; written for EVERY expert,
+ *                  exactly 0 for an expert with no rows);
+ *   d_topk[t, j] = sum_n dY[t, n] * Z[s, n], Z[s] = x[t] W[ids[t,j]]^T, the
+ *                  unweighted per-assignment product.
+ *   dY [T, N], x [T, K], W [E, N, K] in `dtype`.
+ *   dX [T, K] float or NULL (skip); OVERWRITTEN.
+ *   dW [E, N, K] in `dtype` or NULL (skip); OVERWRITTEN.
+ *   d_topk [T, k] float or NULL (skip); OVERWRITTEN.  Rows of empty masked
+ *   slots contribute nothing; dropped assignments get 0.
+ *   W may be NULL only when dX and d_topk are both NULL.
+ *   workspace: device buffer of moe_fused_bwd_workspace_bytes(...) bytes (may
+ *   be NULL when that is 0).
+ */
+int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedule *sched,
+                  float *dX, void *dW, float *d_topk, int64_t K, int64_t N, int32_t dtype,
+                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Export the flat tile space the grouped kernels walk for an output of N
+ * columns with tiles of BM x BN ([GG] "Problem descriptors and the tile
+ * scheduler"): tiles[e] = ceil(counts[e]/BM) * ceil(N/BN) (masked layout:
+ * ceil(capacity/BM) * ceil(N/BN)), tile_start = exclusive prefix, total, and
+ * the owner of every tile, found with the same device code the kernels use
+ * (upper bound of the tile index in tile_start, minus one).
+ *   BM in {32, 64, 128, 256}; BN >= 1.
+ *   tile_start [E] int32, total [1] int32, owner [owner_capacity] int32 (device);
+ *   owners of tiles >= owner_capacity are not written.
+ */
+int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
+                 int32_t *tile_start, int32_t *total, int32_t *owner, int64_t owner_capacity,
+                 void *stream);
+
+/*
+ * Kernel timing for benchmarks.  While enabled, the library brackets every
+ * kernel it launches with a pair of HIP events recorded on that launch's own
+ * stream and keeps them per kernel family.  Families: "build_schedule",
+ * "fill_zero", "grouped_gemm", "fused_fwd", "bwd_dx", "bwd_dw", "tile_map".
+ *   moe_timing_enable(1) clears earlier records and starts recording;
+ *   moe_timing_enable(0) stops recording (records are kept).
+ *   moe_timing_read waits for the recorded events of `family` and returns the
+ *   summed duration in milliseconds and the number of launches.  Returns
+ *   MOE_ERR_SHAPE for an unknown family, MOE_ERR_HIP on an event failure.
+ * Recording creates HIP events (host-side objects); it is meant for benchmark
+ * runs, not for graph capture.
+ */
+int moe_timing_enable(int enable);
+int moe_timing_read(const char *family, double *total_ms, int64_t *launches);
+
+/* Human-readable text of a status code (static storage). */
+const char *moe_status_string(int status);
+
+/* Library version string (static storage). */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_VS_H */

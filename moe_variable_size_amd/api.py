@@ -1,0 +1,275 @@
+"""Python binding of the C ABI (include/moe_vs.h), same names as the C calls.
+
+PyTorch supplies device memory and the current stream; every computation runs
+in the HIP library (libmoe_vs.so).  Nothing here falls back to another
+implementation: a missing library or a device-side failure raises.
+
+Pages the operations follow:
+  [GG]   "Grouped GEMM for MoE, in depth" (aicassindra.com)
+  [CARD] "grouped-gemm-moe" (model card of a published grouped GEMM kernel)
+  [NOTE] "Grouped GEMM" (scholia-log study notes)
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_BF16, MOE_F32, MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_MASKED, BM_VALUES
+
+_DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, ndim=None, contiguous=True) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+@dataclass
+class Schedule:
+    """A routing schedule built on the device (``moe_build_schedule``).
+
+    ``workspace`` owns every array; ``c`` is the C descriptor that points into
+    it.  Views of the arrays are exposed as tensors for inspection.
+    """
+
+    c: _lib.MoeSchedule
+    workspace: torch.Tensor
+
+    def _view(self, ptr: int, n: int, dtype) -> torch.Tensor:
+        base = self.workspace.data_ptr()
+        off = ptr - base
+        esz = torch.tensor([], dtype=dtype).element_size()
+        return self.workspace[off:off + n * esz].view(dtype)
+
+    @property
+    def E(self) -> int:
+        return self.c.E
+
+    @property
+    def counts(self) -> torch.Tensor:
+        return self._view(self.c.counts, self.c.E, torch.int32)
+
+    @property
+    def offsets(self) -> torch.Tensor:
+        return self._view(self.c.offsets, self.c.E, torch.int32)
+
+    def block_start(self, BM: int) -> torch.Tensor:
+        i = BM_VALUES.index(BM)
+        E = self.c.E
+        return self._view(self.c.block_start, 4 * (E + 1), torch.int32)[i * (E + 1):(i + 1) * (E + 1)]
+
+    @property
+    def expert_order(self) -> torch.Tensor:
+        return self._view(self.c.expert_order, self.c.E, torch.int32)
+
+    @property
+    def row_to_assign(self) -> torch.Tensor:
+        return self._view(self.c.row_to_assign, self.c.R, torch.int32)
+
+    @property
+    def row_to_token(self) -> torch.Tensor:
+        return self._view(self.c.row_to_token, self.c.R, torch.int32)
+
+    @property
+    def row_weight(self) -> torch.Tensor:
+        return self._view(self.c.row_weight, self.c.R, torch.float32)
+
+    @property
+    def status(self) -> torch.Tensor:
+        return self._view(self.c.status, 2, torch.int32)
+
+
+def moe_schedule_workspace_bytes(T: int, k: int, E: int, layout: int = MOE_LAYOUT_CONTIGUOUS,
+                                 capacity: int = 0) -> int:
+    return int(_lib.load().moe_schedule_workspace_bytes(T, k, E, layout, capacity))
+
+
+def moe_build_schedule(expert_ids: torch.Tensor, topk_weights: Optional[torch.Tensor], E: int, *,
+                       layout: int = MOE_LAYOUT_CONTIGUOUS, capacity: int = 0,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> Schedule:
+    """Counts, END offsets, tile prefixes and the stable sort by expert, on the
+    device ([GG] "Data layout, offsets and alignment"; [CARD] "How it works")."""
+    lib = _lib.load()
+    _require(expert_ids, "expert_ids", torch.int32, 2)
+    T, k = expert_ids.shape
+    if topk_weights is not None:
+        _require(topk_weights, "topk_weights", torch.float32, 2)
+        if tuple(topk_weights.shape) != (T, k):
+            raise ValueError("topk_weights must have the shape of expert_ids")
+    nbytes = lib.moe_schedule_workspace_bytes(T, k, E, layout, capacity)
+    if nbytes == 0:
+        raise ValueError(f"invalid schedule sizes T={T} k={k} E={E} layout={layout} capacity={capacity}")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=expert_ids.device)
+    c = _lib.MoeSchedule()
+    st = lib.moe_build_schedule(_ptr(expert_ids), _ptr(topk_weights), T, k, E, layout, capacity,
+                                _ptr(workspace), workspace.numel(), ctypes.byref(c), _stream(stream))
+    _lib.check("moe_build_schedule", st)
+    return Schedule(c, workspace)
+
+
+def grouped_gemm(A: torch.Tensor, W: torch.Tensor, offsets: torch.Tensor, *,
+                 out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Bare grouped GEMM: C[r] = A[r] @ W[e(r)]^T for rows grouped by END offsets
+    ([GG] "Problem descriptors and the tile scheduler")."""
+    lib = _lib.load()
+    _require(A, "A", None, 2)
+    _require(W, "W", A.dtype, 3)
+    _require(offsets, "offsets", torch.int32, 1)
+    M, K = A.shape
+    E, N, K2 = W.shape
+    if K2 != K or offsets.numel() != E:
+        raise ValueError("shape mismatch: A [M,K], W [E,N,K], offsets [E]")
+    if out_dtype is None:
+        out_dtype = A.dtype
+    if out is None:
+        out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    _require(out, "out", out_dtype, 2)
+    st = lib.grouped_gemm(_ptr(A), _ptr(W), _ptr(offsets), _ptr(out), M, K, N, E, _dtype_code(A),
+                          _DTYPES[out_dtype], _stream(stream))
+    _lib.check("grouped_gemm", st)
+    return out
+
+
+def moe_fused_fwd(x: torch.Tensor, W: torch.Tensor, sched: Schedule, *,
+                  y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Fused MoE forward: gather on load, weighted atomic scatter-combine on
+    store; y [T, N] float32 ([CARD] intro, "How it works")."""
+    lib = _lib.load()
+    _require(x, "x", None, 2)
+    _require(W, "W", x.dtype, 3)
+    T, K = x.shape
+    E, N, K2 = W.shape
+    if K2 != K or T != sched.c.T or E != sched.c.E:
+        raise ValueError("shape mismatch between x [T,K], W [E,N,K] and the schedule")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _require(y, "y", torch.float32, 2)
+    st = lib.moe_fused_fwd(_ptr(x), _ptr(W), ctypes.byref(sched.c), _ptr(y), K, N, _dtype_code(x),
+                           _stream(stream))
+    _lib.check("moe_fused_fwd", st)
+    return y
+
+
+def moe_fused_bwd_workspace_bytes(sched: Schedule, K: int, N: int, dtype) -> int:
+    return int(_lib.load().moe_fused_bwd_workspace_bytes(ctypes.byref(sched.c), K, N, _DTYPES[dtype]))
+
+
+def moe_fused_bwd(dY: torch.Tensor, x: torch.Tensor, W: Optional[torch.Tensor], sched: Schedule, *,
+                  dx: bool = True, dw: bool = True, dtopk: bool = True, N: Optional[int] = None,
+                  out_dX=None, out_dW=None, out_dtopk=None, stream=None):
+    """Fused MoE backward ([GG] "The backward pass"; [CARD] "How it works").
+    Returns (dX [T,K] fp32 | None, dW [E,N,K] in x's dtype | None, d_topk [T,k] fp32 | None)."""
+    lib = _lib.load()
+    _require(dY, "dY", None, 2)
+    _require(x, "x", dY.dtype, 2)
+    T, K = x.shape
+    N = dY.shape[1] if N is None else N
+    E = sched.c.E
+    if W is not None:
+        _require(W, "W", x.dtype, 3)
+        if tuple(W.shape) != (E, N, K):
+            raise ValueError("W must be [E, N, K]")
+    if dY.shape[0] != T or T != sched.c.T:
+        raise ValueError("dY, x and the schedule disagree on T")
+    dev = x.device
+    dX = (out_dX if out_dX is not None else torch.empty((T, K), dtype=torch.float32, device=dev)) if dx else None
+    dW = (out_dW if out_dW is not None else torch.empty((E, N, K), dtype=x.dtype, device=dev)) if dw else None
+    dT = (out_dtopk if out_dtopk is not None else torch.empty((T, sched.c.k), dtype=torch.float32, device=dev)) if dtopk else None
+    code = _dtype_code(x)
+    ws_bytes = int(lib.moe_fused_bwd_workspace_bytes(ctypes.byref(sched.c), K, N, code))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = lib.moe_fused_bwd(_ptr(dY), _ptr(x), _ptr(W), ctypes.byref(sched.c), _ptr(dX), _ptr(dW),
+                           _ptr(dT), K, N, code, _ptr(ws), ws_bytes, _stream(stream))
+    _lib.check("moe_fused_bwd", st)
+    return dX, dW, dT
+
+
+def moe_tile_map(sched: Schedule, N: int, BM: int, BN: int, owner_capacity: Optional[int] = None,
+                 stream=None):
+    """Flat tile space of an N-column output with BM x BN tiles: (tile_start [E],
+    total [1], owner [owner_capacity]) ([GG] "Problem descriptors and the tile
+    scheduler")."""
+    lib = _lib.load()
+    E = sched.c.E
+    tiles_n = -(-N // BN)
+    if owner_capacity is None:
+        owner_capacity = (sched.c.R // BM + E) * tiles_n + 1
+    dev = sched.workspace.device
+    tile_start = torch.empty(E, dtype=torch.int32, device=dev)
+    total = torch.empty(1, dtype=torch.int32, device=dev)
+    owner = torch.full((owner_capacity,), -1, dtype=torch.int32, device=dev)
+    st = lib.moe_tile_map(ctypes.byref(sched.c), N, BM, BN, _ptr(tile_start), _ptr(total), _ptr(owner),
+                          owner_capacity, _stream(stream))
+    _lib.check("moe_tile_map", st)
+    return tile_start, total, owner
+
+
+def moe_timing_enable(enable: bool = True) -> None:
+    """Start (clearing earlier records) or stop per-kernel event timing."""
+    _lib.check("moe_timing_enable", _lib.load().moe_timing_enable(1 if enable else 0))
+
+
+def moe_timing_read(family: str):
+    """(total milliseconds, launches) recorded for a kernel family."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _lib.check("moe_timing_read", _lib.load().moe_timing_read(family.encode(), ctypes.byref(ms),
+                                                              ctypes.byref(n)))
+    return ms.value, n.value
+
+
+class MoEFunction(torch.autograd.Function):
+    """Differentiable fused MoE layer y = moe(x, W, expert_ids, topk_weights)
+    over the C ABI (the card's "Usage": gradients reach the tokens, the expert
+    weights and the routing weights)."""
+
+    @staticmethod
+    def forward(ctx, x, W, expert_ids, topk_weights):
+        sched = moe_build_schedule(expert_ids, topk_weights.detach().float().contiguous(), W.shape[0])
+        y = moe_fused_fwd(x.detach().contiguous(), W.detach().contiguous(), sched)
+        ctx.save_for_backward(x, W)
+        ctx.sched = sched
+        ctx.w_dtype = topk_weights.dtype
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, W = ctx.saved_tensors
+        dY = gy.to(x.dtype).contiguous()
+        dX, dW, dT = moe_fused_bwd(dY, x.detach().contiguous(), W.detach().contiguous(), ctx.sched,
+                                   dx=ctx.needs_input_grad[0], dw=ctx.needs_input_grad[1],
+                                   dtopk=ctx.needs_input_grad[3])
+        return (dX.to(x.dtype) if dX is not None else None, dW, None,
+                dT.to(ctx.w_dtype) if dT is not None else None)
+
+
+def moe(x, W, expert_ids, topk_weights):
+    return MoEFunction.apply(x, W, expert_ids, topk_weights)

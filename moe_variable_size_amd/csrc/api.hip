@@ -1,0 +1,345 @@
+// C ABI of the MoE grouped GEMM library: host-side validation and dispatch.
+//
+// Every entry point checks its arguments completely before it launches
+// anything, so a nonzero return means nothing was enqueued.  Nothing here
+// synchronises, reads device memory back or allocates: the whole layer can be
+// captured in a HIP graph ([GG] "Failure modes": no host sync per layer;
+// [GG] = "Grouped GEMM for MoE, in depth").
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "common.hpp"
+
+namespace moe {
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+constexpr int64_t kMax32 = (int64_t)1 << 31;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+struct WsLayout {
+  size_t counts, offsets, bstart, order, status, r2a, r2t, rw, total;
+};
+
+WsLayout ws_layout(int64_t R, int E) {
+  WsLayout l;
+  size_t o = 0;
+  l.counts = o;  o = align256(o + sizeof(int32_t) * E);
+  l.offsets = o; o = align256(o + sizeof(int32_t) * E);
+  l.bstart = o;  o = align256(o + sizeof(int32_t) * MOE_NUM_BM * (E + 1));
+  l.order = o;   o = align256(o + sizeof(int32_t) * E);
+  l.status = o;  o = align256(o + sizeof(int32_t) * 2);
+  l.r2a = o;     o = align256(o + sizeof(int32_t) * R);
+  l.r2t = o;     o = align256(o + sizeof(int32_t) * R);
+  l.rw = o;      o = align256(o + sizeof(float) * R);
+  l.total = o;
+  return l;
+}
+
+int check_sizes(int64_t T, int32_t k, int32_t E, int32_t layout, int32_t capacity, int64_t *R) {
+  if (T < 1 || k < 1 || k > 64 || E < 1) return MOE_ERR_SHAPE;
+  if (E > kMaxExperts) return MOE_ERR_LIMIT;
+  if (T * k >= kMax32) return MOE_ERR_LIMIT;
+  if (layout == MOE_LAYOUT_CONTIGUOUS) {
+    *R = T * k;
+  } else if (layout == MOE_LAYOUT_MASKED) {
+    if (capacity < 1 || capacity > 65536) return MOE_ERR_SHAPE;
+    if ((int64_t)E * capacity >= kMax32) return MOE_ERR_LIMIT;
+    *R = (int64_t)E * capacity;
+  } else {
+    return MOE_ERR_SHAPE;
+  }
+  return MOE_OK;
+}
+
+int check_sched(const moe_schedule *s) {
+  if (!s || !s->counts || !s->offsets || !s->block_start || !s->expert_order ||
+      !s->row_to_assign || !s->row_to_token || !s->row_weight || !s->status)
+    return MOE_ERR_NULL;
+  int64_t R = 0;
+  int rc = check_sizes(s->T, s->k, s->E, s->layout, s->capacity, &R);
+  if (rc) return rc;
+  if (R != s->R || s->S != s->T * s->k) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+int check_dtype_dims(int32_t dtype, int64_t K, int64_t N) {
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (K < 1 || N < 1) return MOE_ERR_SHAPE;
+  if (K >= kMax32 || N >= kMax32) return MOE_ERR_LIMIT;
+  return MOE_OK;
+}
+
+size_t esize(int32_t dtype) { return dtype == MOE_F32 ? 4 : 2; }
+
+// byte size of an [rows, cols] tensor must stay below 2^31 (32-bit offsets)
+bool fits(int64_t rows, int64_t cols, int32_t dtype) {
+  return (double)rows * (double)cols * (double)esize(dtype) < (double)kMax32;
+}
+
+// ---- kernel timing (benchmarks only) ---------------------------------------
+const char *const kFamilies[] = {"build_schedule", "fill_zero", "grouped_gemm", "fused_fwd",
+                                 "bwd_dx", "bwd_dw", "tile_map"};
+constexpr int kNumFamilies = sizeof(kFamilies) / sizeof(kFamilies[0]);
+
+struct Timing {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[kNumFamilies];
+};
+Timing &timing() {
+  static Timing t;
+  return t;
+}
+
+int family_index(const char *name) {
+  for (int i = 0; i < kNumFamilies; ++i)
+    if (strcmp(name, kFamilies[i]) == 0) return i;
+  return -1;
+}
+
+// Launch `f` (returning hipError_t) bracketed by events when timing is on.
+template <typename F>
+hipError_t timed(int fam, hipStream_t st, F &&f) {
+  Timing &t = timing();
+  if (!t.on) return f();
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return f();
+  hipEventRecord(a, st);
+  hipError_t e = f();
+  hipEventRecord(b, st);
+  std::lock_guard<std::mutex> g(t.mu);
+  t.ev[fam].emplace_back(a, b);
+  return e;
+}
+
+enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP };
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char *moe_version(void) { return "moe_vs 0.1.0 gfx950"; }
+
+const char *moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case MOE_ERR_DTYPE: return "unsupported dtype";
+    case MOE_ERR_ALIGN: return "a pointer is not aligned as required";
+    case MOE_ERR_WORKSPACE: return "workspace NULL or too small";
+    case MOE_ERR_HIP: return "HIP runtime error at launch";
+    case MOE_ERR_LIMIT: return "a size exceeds a library limit";
+    default: return "unknown status";
+  }
+}
+
+size_t moe_schedule_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t layout,
+                                    int32_t capacity) {
+  int64_t R = 0;
+  if (check_sizes(T, k, E, layout, capacity, &R)) return 0;
+  return ws_layout(R, E).total;
+}
+
+int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T, int32_t k,
+                       int32_t E, int32_t layout, int32_t capacity, void *workspace,
+                       size_t workspace_bytes, moe_schedule *sched, void *stream) {
+  if (!expert_ids || !sched) return MOE_ERR_NULL;
+  int64_t R = 0;
+  int rc = check_sizes(T, k, E, layout, capacity, &R);
+  if (rc) return rc;
+  if (!aligned(expert_ids, 4) || (topk_weights && !aligned(topk_weights, 4))) return MOE_ERR_ALIGN;
+  const WsLayout l = ws_layout(R, E);
+  if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
+  char *w = (char *)workspace;
+  moe_schedule s;
+  memset(&s, 0, sizeof(s));
+  s.T = T;
+  s.S = T * k;
+  s.R = R;
+  s.k = k;
+  s.E = E;
+  s.layout = layout;
+  s.capacity = layout == MOE_LAYOUT_MASKED ? capacity : 0;
+  s.counts = (int32_t *)(w + l.counts);
+  s.offsets = (int32_t *)(w + l.offsets);
+  s.block_start = (int32_t *)(w + l.bstart);
+  s.expert_order = (int32_t *)(w + l.order);
+  s.status = (int32_t *)(w + l.status);
+  s.row_to_assign = (int32_t *)(w + l.r2a);
+  s.row_to_token = (int32_t *)(w + l.r2t);
+  s.row_weight = (float *)(w + l.rw);
+  *sched = s;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(
+      timed(F_SCHED, st, [&] { return launch_build_schedule(expert_ids, topk_weights, s, st); }));
+}
+
+int grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int64_t M,
+                 int64_t K, int64_t N, int32_t E, int32_t dtype, int32_t out_dtype,
+                 void *stream) {
+  int rc = check_dtype_dims(dtype, K, N);
+  if (rc) return rc;
+  if (M < 0 || E < 1) return MOE_ERR_SHAPE;
+  if (E > kMaxExperts) return MOE_ERR_LIMIT;
+  if (dtype == MOE_F32 && out_dtype != MOE_F32) return MOE_ERR_DTYPE;
+  if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (M == 0) return MOE_OK;
+  if (!A || !W || !offsets || !C) return MOE_ERR_NULL;
+  if (!fits(M, K, dtype) || !fits(N, K, dtype) || !fits(M, N, out_dtype)) return MOE_ERR_LIMIT;
+  const size_t al = dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(A, al) || !aligned(W, al) || !aligned(offsets, 4) || !aligned(C, esize(out_dtype)))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(timed(F_BARE, st, [&] {
+    if (dtype == MOE_BF16 && mfma_supported((int)K, (int)N))
+      return mfma_grouped_gemm(A, W, offsets, C, (int)M, (int)K, (int)N, E, out_dtype, st);
+    return simt_grouped_gemm(A, W, offsets, C, (int)M, (int)K, (int)N, E, dtype, out_dtype, st);
+  }));
+}
+
+int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float *y, int64_t K,
+                  int64_t N, int32_t dtype, void *stream) {
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  rc = check_dtype_dims(dtype, K, N);
+  if (rc) return rc;
+  if (!x || !W || !y) return MOE_ERR_NULL;
+  const moe_schedule &s = *sched;
+  if (!fits(s.T, K, dtype) || !fits(N, K, dtype) || !fits(s.T, N, MOE_F32)) return MOE_ERR_LIMIT;
+  const size_t al = dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(x, al) || !aligned(W, al) || !aligned(y, 4)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e =
+      timed(F_FILL, st, [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), st); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(F_FWD, st, [&] {
+    if (dtype == MOE_BF16 && mfma_supported((int)K, (int)N))
+      return mfma_fused_fwd(x, W, s, y, (int)K, (int)N, st);
+    return simt_fused_fwd(x, W, s, y, (int)K, (int)N, dtype, st);
+  }));
+}
+
+size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64_t N,
+                                     int32_t dtype) {
+  (void)sched;
+  (void)K;
+  (void)N;
+  (void)dtype;
+  return 0;
+}
+
+int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedule *sched,
+                  float *dX, void *dW, float *d_topk, int64_t K, int64_t N, int32_t dtype,
+                  void *workspace, size_t workspace_bytes, void *stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  rc = check_dtype_dims(dtype, K, N);
+  if (rc) return rc;
+  if (!dY || !x) return MOE_ERR_NULL;
+  if ((dX || d_topk) && !W) return MOE_ERR_NULL;
+  const moe_schedule &s = *sched;
+  if (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(N, K, dtype) || !fits(s.T, K, MOE_F32))
+    return MOE_ERR_LIMIT;
+  const size_t al = dtype == MOE_BF16 ? 16 : 4;
+  if (!aligned(dY, al) || !aligned(x, al) || (W && !aligned(W, al)) || (dX && !aligned(dX, 4)) ||
+      (dW && !aligned(dW, esize(dtype))) || (d_topk && !aligned(d_topk, 4)))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const bool mfma = dtype == MOE_BF16 && mfma_supported((int)K, (int)N);
+  hipError_t e = hipSuccess;
+  if (dX)
+    e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, (size_t)s.T * K * sizeof(float), st); });
+  if (e == hipSuccess && d_topk)
+    e = timed(F_FILL, st,
+              [&] { return launch_fill_zero(d_topk, (size_t)s.S * sizeof(float), st); });
+  if (e == hipSuccess && (dX || d_topk))
+    e = timed(F_DX, st, [&] {
+      return mfma ? mfma_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, st)
+                  : simt_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, dtype, st);
+    });
+  if (e == hipSuccess && dW)
+    e = timed(F_DW, st, [&] {
+      return mfma ? mfma_bwd_dw(dY, x, s, dW, (int)K, (int)N, st)
+                  : simt_bwd_dw(dY, x, s, dW, (int)K, (int)N, dtype, st);
+    });
+  return hip_status(e);
+}
+
+int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN, int32_t *tile_start,
+                 int32_t *total, int32_t *owner, int64_t owner_capacity, void *stream) {
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  if (bm_index(BM) < 0 || BN < 1 || N < 1 || N >= kMax32 || owner_capacity < 0) return MOE_ERR_SHAPE;
+  if (!tile_start || !total || (owner_capacity > 0 && !owner)) return MOE_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(timed(F_TILEMAP, st, [&] {
+    return launch_tile_map(*sched, (int)N, BM, BN, tile_start, total, owner, owner_capacity, st);
+  }));
+}
+
+int moe_timing_enable(int enable) {
+  Timing &t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  if (enable) {
+    for (auto &v : t.ev) {
+      for (auto &pr : v) {
+        hipEventDestroy(pr.first);
+        hipEventDestroy(pr.second);
+      }
+      v.clear();
+    }
+  }
+  t.on = enable != 0;
+  return MOE_OK;
+}
+
+int moe_timing_read(const char *family, double *total_ms, int64_t *launches) {
+  if (!family || !total_ms || !launches) return MOE_ERR_NULL;
+  const int f = family_index(family);
+  if (f < 0) return MOE_ERR_SHAPE;
+  Timing &t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  double sum = 0.0;
+  for (auto &pr : t.ev[f]) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return MOE_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return MOE_ERR_HIP;
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int64_t)t.ev[f].size();
+  return MOE_OK;
+}
+
+}  // extern "C"
