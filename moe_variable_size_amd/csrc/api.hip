@@ -52,9 +52,11 @@ WsLayout ws_layout(int64_t R, int E) {
   l.bstart = o;  o = align256(o + sizeof(int32_t) * MOE_NUM_BM * (E + 1));
   l.order = o;   o = align256(o + sizeof(int32_t) * E);
   l.status = o;  o = align256(o + sizeof(int32_t) * 2);
-  l.r2a = o;     o = align256(o + sizeof(int32_t) * R);
-  l.r2t = o;     o = align256(o + sizeof(int32_t) * R);
-  l.rw = o;      o = align256(o + sizeof(float) * R);
+  // row arrays carry kRowPad spare entries: kernels read row data a stage
+  // (32 rows) at a time and may read past the last row (values ignored)
+  l.r2a = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
+  l.r2t = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
+  l.rw = o;      o = align256(o + sizeof(float) * (R + kRowPad));
   l.total = o;
   return l;
 }

@@ -14,6 +14,7 @@ typedef uint16_t bf16_t;  // raw bfloat16 bit pattern
 
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxExperts = 1024;    // E limit (LDS-resident per-expert tables)
+constexpr int kRowPad = 64;          // spare entries after each schedule row array
 constexpr int kBmValues[MOE_NUM_BM] = {32, 64, 128, 256};
 
 MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }

@@ -4,63 +4,140 @@
 // [CARD] = "grouped-gemm-moe" model card
 // [NOTE] = "Grouped GEMM" study notes (scholia-log)
 //
-// All kernels share one tile core:
-//   * a workgroup of 4 waves (WGM x WGN) owns a BM x BN output tile made of
-//     32 x 32 blocks, each block one v_mfma_f32_32x32x16_bf16 accumulator (16
-//     fp32 per lane); wave (wm, wn) owns row blocks wm, wm + WGM, ... and column
-//     blocks wn, wn + WGN, ... (interleaved, so that a wave's LDS addresses differ
-//     by constants and fit in instruction offsets);
-//   * the reduction advances 64 elements per stage; both operands sit in LDS as
-//     [operand row][64 reduction elements] (128 bytes per row), with the eight
-//     16-byte chunks of a row XOR-swizzled by the row index so that the 16-byte
-//     MFMA operand reads and the 16-byte stores both spread over all banks;
-//   * two LDS stages: while the waves multiply stage i, the global loads of stage
-//     i+1 are in flight into registers and are stored to the other stage after the
-//     multiply ([GG] "Problem descriptors and the tile scheduler": the per-tile K
-//     loop; [CARD] "How it works": the next chunk streams while the current one
-//     computes);
-//   * global loads are raw buffer loads: an out-of-range offset returns zeros, so
-//     rows past a group's end, columns past N and reduction chunks past K are
-//     masked without branches and without touching memory ([GG] "Problem
-//     descriptors and the tile scheduler": ragged rows masked on load and store).
-//
-// Operands whose reduction index is the contiguous one ("K-major": token rows,
-// weight rows in the forward) are stored to LDS as loaded.  Operands whose
-// reduction index is strided (the weights in the input gradient, both operands
-// of the weight gradient) are loaded as 8 x 8 element blocks and transposed in
-// registers before the store.
-//
-// The persistent grid has one workgroup per compute unit.  Workgroup ids are
-// remapped so that the 8 XCDs (each with its own L2) each take one contiguous
-// slice of the flat tile space; inside a group tiles are walked
-// column-block-major, so the workgroups of one XCD share the same weight column
-// blocks ([GG] "Problem descriptors and the tile scheduler", reuse of B_g from
-// L2).
+// All kernels share one tile core.
+//  * A workgroup of 4 waves (WGM x WGN) owns a BM x BN output tile made of
+//    32 x 32 blocks, each one v_mfma_f32_32x32x16_bf16 accumulator (16 fp32 per
+//    lane).  Wave (wm, wn) owns row blocks wm, wm + WGM, ... and column blocks
+//    wn, wn + WGN, ... (interleaved so a wave's LDS addresses differ by
+//    constants).
+//  * The reduction advances 32 elements per stage.  An operand tile sits in LDS
+//    in one of two layouts:
+//      K-major : [tile row][32 reduction elements], 64 B per row -- token rows
+//                and weight rows whose reduction index is contiguous in memory
+//                (both operands of the forward, dY in the input gradient);
+//      MN-major: [32 reduction rows][256 tile columns], 512 B per row -- operands
+//                whose reduction index is strided in memory (the weights in the
+//                input gradient, both operands of the weight gradient).
+//    16-byte chunks are XOR-swizzled by the row so that the operand reads and
+//    the DMA writes are free of bank conflicts.
+//  * Tiles are loaded by direct global->LDS DMA (buffer_load ... lds, 16 bytes
+//    per lane, any global address per lane): gathered token rows land in LDS
+//    without passing through registers ([CARD] "How it works": rows gathered
+//    on load).  Out-of-range offsets of a raw buffer load return zeros, which
+//    masks rows past a group's end, columns past N and chunks past K
+//    ([GG] "Problem descriptors and the tile scheduler").
+//  * MFMA operands come from K-major tiles with one 16-byte read per lane and
+//    from MN-major tiles with two ds_read_b64_tr_b16 (4 x 16 transposing reads).
+//  * Four LDS stages: while stage i multiplies, stages i+1 .. i+3 are in
+//    flight ([CARD] "How it works": the next K chunk streams while the current
+//    one computes).  Each stage is two 16-deep MFMA steps; the fragments of
+//    step 1 are read while step 0 multiplies; then the waves meet at one
+//    barrier, the DMA of stage i+4 goes into the buffer just released, and the
+//    first fragments of stage i+1 are read while step 1 multiplies.  The DMA is
+//    issued from inline assembly with explicit vmcnt accounting, so the
+//    compiler's conservative waits on LDS DMA do not serialise the pipeline.
+//  * One persistent workgroup per compute unit.  Workgroup ids are remapped so
+//    that each of the 8 XCDs (one L2 each) takes a contiguous slice of the
+//    flat tile space; inside a group tiles are walked column-block-major, so the
+//    workgroups of one XCD share weight column blocks in L2 ([GG] "Problem
+//    descriptors and the tile scheduler").  Whole tiles go out in waves of one
+//    tile per workgroup (all workgroups advance through K together, which keeps
+//    the shared blocks in L2); only the last partial wave is split along K over
+//    all workgroups (stream-K), which evens out the tail.
 #include "common.hpp"
 
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr int NT = 256;        // 4 waves
-constexpr int BK = 64;         // reduction elements per stage
-constexpr int ROWB = BK * 2;   // bytes per LDS operand row
+constexpr int BK = 32;         // reduction elements per stage
+constexpr int KROW = BK * 2;   // bytes per K-major LDS row
+constexpr int MNROW = 256 * 2; // bytes per MN-major LDS row (256 columns)
+constexpr int NSTAGE = 4;      // LDS stages
+constexpr int OPND = 256 * KROW;                  // 16 KB: one 256-wide operand tile
+constexpr int STAGE = 2 * OPND;                   // A then B
+constexpr int WREGION = NSTAGE * STAGE;           // per-stage routing weights (weight gradient)
+constexpr int WBYTES = 4 * 256;                   // per stage: 4 waves x 64 floats
+constexpr int TOKREGION = WREGION + NSTAGE * WBYTES;  // token ring (weight gradient)
+constexpr int TOKSLOT = 4 * 256;                  // per ring slot: 4 waves x 64 ints
 
-// Byte offset of 16-byte chunk `chunk` (0..7) of LDS operand row `row`.
-MOE_DEV int lds_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+// ---- LDS layouts --------------------------------------------------------------
+// The LDS serves 256 bytes per clock (64 banks x 4 B), i.e. sixteen 16-byte
+// lane accesses.  The swizzles make 16 consecutive lanes of an operand read hit
+// 16 different 16-byte bank groups.
+// K-major: chunk c (0..3) of row r at r*64 + ((c ^ ((r >> 2) & 3)) << 4): the 16
+// rows read together fall 4 per 256-byte line, each at a different chunk.
+MOE_DEV int kmaj_off(int row, int chunk) { return row * KROW + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// MN-major: chunk c (0..31) of reduction row r at r*512 + ((c ^ ((r & 3) << 2)) << 4):
+// a transposing read touches 4 rows x 2 chunks per 16 lanes (4 chunks per 32).
+MOE_DEV int mnmaj_off(int row, int chunk) { return row * MNROW + ((chunk ^ ((row & 3) << 2)) << 4); }
+
+// ---- DMA and waits ---------------------------------------------------------------
+// 16 (dma16) or 4 (dma4) bytes per lane from global (rsrc + voff) to LDS byte
+// address lds + size * lane.  `lds` is taken from the first lane.  Nothing else
+// in these kernels uses m0, so setting it here disturbs no compiler-held value.
+MOE_DEV void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+MOE_DEV void dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+template <int N>
+MOE_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// wait until at most `stages` stages of D operations each are outstanding
+template <int D>
+MOE_DEV void wait_stages(int stages) {
+  if (stages >= 3)
+    wait_vmcnt<3 * D>();
+  else if (stages >= 2)
+    wait_vmcnt<2 * D>();
+  else if (stages == 1)
+    wait_vmcnt<D>();
+  else
+    wait_vmcnt<0>();
+}
+MOE_DEV void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+MOE_DEV void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-MOE_DEV u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+// Buffer resource built from wave-uniform values (scalar registers), as the
+// DMA instructions require.
+MOE_DEV __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, uint32_t num_records) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const void *q = (const void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return make_rsrc(q, __builtin_amdgcn_readfirstlane(num_records));
 }
 
-MOE_DEV void lds_store(char *lds, int off, u32x4 v) { *(u32x4 *)(lds + off) = v; }
+MOE_DEV uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const LDS_AS void *)p);
+}
 
 // Logical workgroup id: consecutive ids land on one XCD (the hardware deals
 // workgroup ids to the 8 XCDs round robin).
@@ -69,61 +146,214 @@ MOE_DEV int logical_block() {
   return (G & 7) ? b : (b & 7) * (G >> 3) + (b >> 3);
 }
 
-// One stage of the tile multiply: 4 steps of 16 reduction elements.  The
-// operand fragments of step s+1 are read from LDS while step s multiplies.
-// A rows of the wave: a_row0 + mi * a_str + (0..31); B rows: b_row0 + ni * b_str.
-// SKIP: row blocks at or past `live_mi` (no valid row) skip their MFMAs.
-template <int MI, int NI, bool SKIP>
-MOE_DEV void mma_stage(const char *As, const char *Bs, int a_row0, int a_str, int b_row0,
-                       int b_str, int lane, int live_mi, f32x16 (&acc)[MI][NI]) {
-  bf16x8_t a[2][MI], b[2][NI];
-  auto frag = [&](int s, int buf) __attribute__((always_inline)) {
-    const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      a[buf][mi] = *(const bf16x8_t *)(As + lds_off(a_row0 + mi * a_str + (lane & 31), ch));
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-      b[buf][ni] = *(const bf16x8_t *)(Bs + lds_off(b_row0 + ni * b_str + (lane & 31), ch));
-  };
-  frag(0, 0);
-#pragma unroll
-  for (int s = 0; s < BK / 16; ++s) {
-    if (s + 1 < BK / 16) frag(s + 1, (s + 1) & 1);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (SKIP && mi >= live_mi) continue;  // wave-uniform
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[s & 1][mi], b[s & 1][ni],
-                                                              acc[mi][ni], 0, 0, 0);
+// Work split of `total` tiles of KI stages over G workgroups: whole tiles in
+// waves of G, the remaining tiles' stages split evenly.  Workgroup Lb walks
+// [it, it_end) of the flat (tile, stage) space, jumping by whole tiles in the
+// first phase.
+struct WorkSplit {
+  int64_t it, it_end, tail0, tot;
+  int KI, G;
+  MOE_DEV void init(int total, int KI_, int G_, int Lb, bool sk) {
+    KI = KI_;
+    G = G_;
+    tot = (int64_t)total * KI;
+    const int full = sk ? (total / G) * G : total;
+    tail0 = (int64_t)full * KI;
+    if (Lb < full) {
+      it = (int64_t)Lb * KI;
+      it_end = it + KI;
+    } else {
+      it = tail0 + (tot - tail0) * Lb / G;
+      it_end = tail0 + (tot - tail0) * (Lb + 1) / G;
     }
   }
+  // next piece (tile, kb, ke); false when done
+  MOE_DEV bool next(int &tau, int &kb, int &ke, int Lb) {
+    while (it >= it_end) {
+      if (it_end <= tail0 && it_end + (int64_t)(G - 1) * KI < tail0) {
+        it = it_end + (int64_t)(G - 1) * KI;  // next whole tile of this workgroup
+        it_end = it + KI;
+      } else if (it_end <= tail0) {
+        it = tail0 + (tot - tail0) * Lb / G;  // whole tiles done: tail slice
+        it_end = tail0 + (tot - tail0) * (Lb + 1) / G;
+        if (it >= it_end) return false;
+      } else {
+        return false;
+      }
+    }
+    tau = (int)(it / KI);
+    kb = (int)(it - (int64_t)tau * KI);
+    ke = (int)min((int64_t)KI, kb + (it_end - it));
+    it += ke - kb;
+    return true;
+  }
+};
+
+// ---- MFMA operand fragments ----------------------------------------------------
+// Lane l of a 32x32x16 MFMA holds, for operand row/column (l & 31), the 8
+// reduction elements 8*(l >> 5) .. +7 of the 16-element step.
+
+// K-major: one 16-byte read.
+MOE_DEV bf16x8_t frag_kmaj(const char *tile, int row, int step, int lane) {
+  return *(const bf16x8_t *)(tile + kmaj_off(row, 2 * step + (lane >> 5)));
 }
 
-// 8 x 8 transpose of bf16 straight into LDS: in[r] holds row r (8 elements,
-// element 2d in the low half of dword d); column c (rows 0..7) is stored as one
-// 16-byte chunk at LDS operand row row0 + c, chunk `chunk`.
-MOE_DEV void transpose8x8_store(const u32x4 (&in)[8], char *lds, int row0, int chunk) {
+// MN-major: two transposing reads.  In each 16-lane group, lane j supplies the
+// address of 4 consecutive columns of reduction row (j >> 2) and receives the
+// 4 rows of column (j & 15) of the 4 x 16 block.
+MOE_DEV bf16x8_t frag_mnmaj(const char *tile, int col0, int step, int lane) {
+  const int j = lane & 15;
+  const int col = col0 + ((lane >> 4) & 1) * 16 + 4 * (j & 3);
+  const int r = step * 16 + 8 * (lane >> 5) + (j >> 2);
+  const int inchunk = (col & 7) * 2;
+  LDS_AS i16x4 *p0 = (LDS_AS i16x4 *)(LDS_AS char *)(tile + mnmaj_off(r, col >> 3) + inchunk);
+  LDS_AS i16x4 *p1 = (LDS_AS i16x4 *)(LDS_AS char *)(tile + mnmaj_off(r + 4, col >> 3) + inchunk);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Multiply the 8 elements of a fragment by 8 fp32 factors, rounding to bf16.
+MOE_DEV bf16x8_t scale_frag(bf16x8_t f, const float (&w)[8]) {
+  bf16x8_t o;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-    u32x4 o;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)  // low half: row 2p, high half: row 2p+1, column c
-      o[p] = __builtin_amdgcn_perm(in[2 * p + 1][c >> 1], in[2 * p][c >> 1], sel);
-    lds_store(lds, lds_off(row0 + c, chunk), o);
-  }
+  for (int i = 0; i < 8; ++i) o[i] = (__bf16)((float)f[i] * w[i]);
+  return o;
 }
 
 // Row r of a 32x32 MFMA accumulator held in register i of lane `lane`.
 MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 2) + (i & 3); }
 
+// ---- the pipelined tile multiply --------------------------------------------
+// Op supplies:
+//   static constexpr bool A_KMAJ, B_KMAJ, A_SCALED;  operand layouts; A_SCALED:
+//       A fragments are multiplied by per-reduction-row factors read with
+//       row_scale(buf, step, lane, w)
+//   static constexpr int DMA_PER_STAGE;   DMA operations per thread per stage
+//   void issue(int kt, int buf);           start loading stage kt into buffer buf
+// Buffer b: A at lds + b * STAGE, B at + OPND.
+template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op>
+MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
+                           int live_mi, f32x16 (&acc)[MI][NI]) {
+  constexpr int D = Op::DMA_PER_STAGE;
+  bf16x8_t fa[2][MI], fb[2][NI];
+  auto frags = [&](int buf, int step, int slot) __attribute__((always_inline)) {
+    const char *As = lds + buf * STAGE;
+    const char *Bs = As + OPND;
+    float w[8];
+    if (Op::A_SCALED) op.row_scale(buf, step, lane, w);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (Op::A_KMAJ)
+        fa[slot][mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
+      else
+        fa[slot][mi] = frag_mnmaj(As, wm * 32 + mi * 32 * WGM, step, lane);
+      if (Op::A_SCALED) fa[slot][mi] = scale_frag(fa[slot][mi], w);
+    }
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+      if (Op::B_KMAJ)
+        fb[slot][ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
+      else
+        fb[slot][ni] = frag_mnmaj(Bs, wn * 32 + ni * 32 * WGN, step, lane);
+    }
+  };
+  auto mma = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      if (SKIP && mi >= live_mi) continue;  // wave-uniform: rows past the group end
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
+                                                              acc[mi][ni], 0, 0, 0);
+    }
+  };
+  constexpr int NREAD = (Op::A_KMAJ ? MI : 2 * MI) + (Op::B_KMAJ ? NI : 2 * NI);
+  constexpr int NMFMA = MI * NI;
+  auto interleave = [&]() __attribute__((always_inline)) {
+    // one LDS read after each MFMA until the reads run out
+#pragma unroll
+    for (int i = 0; i < (NREAD < NMFMA ? NREAD : NMFMA); ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    if (NMFMA > NREAD) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
+    if (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);
+  };
+
+  // prologue: up to NSTAGE stages in flight; wait for the first
+  const int n = ke - kb;
+  const int pre = n < NSTAGE ? n : NSTAGE;
+  for (int s = 0; s < pre; ++s) op.issue(kb + s, s);
+  wait_stages<D>(pre - 1 > 2 ? 3 : pre - 1);
+  wait_lgkm0();
+  barrier();
+  frags(0, 0, 0);
+  for (int kt = kb; kt < ke; ++kt) {
+    const int buf = (kt - kb) & (NSTAGE - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    frags(buf, 1, 1);
+    mma(0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < ke) {
+      // issued and not yet waited: stages kt+1 .. min(kt+3, ke-1); keep the
+      // later ones in flight, wait for kt+1
+      const int later = min(2, ke - kt - 2);
+      wait_stages<D>(later);
+      wait_lgkm0();
+      barrier();
+      if (kt + NSTAGE < ke) op.issue(kt + NSTAGE, buf);  // buffer of stage kt is free
+      frags((buf + 1) & (NSTAGE - 1), 0, 0);  // first fragments of the next stage
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    mma(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// K-major DMA of a tile of R rows x 32 reduction elements: thread (wave w, lane
+// p), instruction i loads row (w * R/64 + i) * 16 + p/4, physical chunk p % 4.
+template <int R>
+struct KmajDma {
+  static constexpr int PER_WAVE = R / 64;
+  uint32_t base[PER_WAVE];  // per-lane global byte offset of the row chunk, stage 0
+  int chunk[PER_WAVE];      // logical chunk (reduction elements 8*chunk .. +7)
+  MOE_DEV void setup(int wid, int lane, const int *rowoff /* byte offset of tile row or -1 */) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int row = (wid * PER_WAVE + i) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      chunk[i] = c;
+      const int ro = rowoff[row];
+      base[i] = ro >= 0 ? (uint32_t)ro + (uint32_t)c * 16u : kOobOffset;
+    }
+  }
+  MOE_DEV void issue(__amdgpu_buffer_rsrc_t rs, int kt, int kred, uint32_t lds_tile, int wid) {
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const bool in = kt * BK + chunk[i] * 8 < kred;
+      const uint32_t off = in ? base[i] + (uint32_t)kt * KROW : kOobOffset;
+      dma16(rs, off, lds_tile + (uint32_t)((wid * PER_WAVE + i) * 1024));
+    }
+  }
+};
+
+// MN-major DMA of a 32 x 256 tile: thread (wave w, lane p), instruction i loads
+// reduction row 2 * (w * 4 + i) + p/32, physical chunk p % 32.
+struct MnmajMap {
+  MOE_DEV static int row_of(int wid, int i, int lane) { return 2 * (wid * 4 + i) + (lane >> 5); }
+  MOE_DEV static int chunk_of(int wid, int i, int lane) {
+    return (lane & 31) ^ ((row_of(wid, i, lane) & 3) << 2);
+  }
+};
+
 // ============================================================================
 // Forward-shaped kernel: out[r, n] = sum_k A[src(r), k] * W[g, n, k].
 //   FUSED: src(r) = row_to_token[r], y[src(r), n] += row_weight[r] * acc
-//          (atomic; rows of both layouts) -- [CARD] gather on load,
-//          scatter-combine on store.
+//          (atomic; both layouts) -- [CARD] gather on load, scatter-combine on
+//          store, so neither [S, K] nor [S, N] is stored.
 //   bare : src(r) = r, C[r, n] = acc (plain store, fp32 or bf16).
 // ============================================================================
 struct FwdArgs {
@@ -137,20 +367,36 @@ struct FwdArgs {
   const float *row_weight;
   int E, layout, capacity, K, N;
   uint32_t a_bytes;  // bytes of A (x or the bare A)
-  int stream_k;      // 1: split the (tile, stage) space evenly over workgroups
+  int stream_k;      // 1: split the last partial wave of tiles along K
   int M;             // bare: rows of A and C (rows at or past M are never touched)
+};
+
+template <int BM, int BN>
+struct FwdOp {
+  static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false;
+  static constexpr int DMA_PER_STAGE = BM / 64 + BN / 64;
+  KmajDma<BM> da;
+  KmajDma<BN> db;
+  __amdgpu_buffer_rsrc_t rsA, rsW;
+  uint32_t lds0;
+  int K, wid;
+  MOE_DEV void issue(int kt, int buf) {
+    const uint32_t t = lds0 + (uint32_t)buf * STAGE;
+    da.issue(rsA, kt, K, t, wid);
+    db.issue(rsW, kt, K, t + OPND, wid);
+  }
+  MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
 };
 
 template <int BM, int BN, int WGM, int WGN, bool FUSED, typename Tout>
 __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int MI = WTM / 32, NI = WTN / 32;
-  constexpr int CA = BM / 32, CB = BN / 32;  // 16-byte chunks per thread per stage
+  constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   static_assert(WGM * WGN == 4, "4 waves");
-  extern __shared__ __attribute__((aligned(16))) char lds[];  // 2 stages x (BM + BN) rows
+  extern __shared__ __attribute__((aligned(16))) char lds[];  // NSTAGE x (A, B)
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
   __shared__ __attribute__((aligned(16))) int tok[BM];
   __shared__ __attribute__((aligned(16))) float wgt[BM];
+  __shared__ int rowoff_a[BM], rowoff_b[BN];
   __shared__ int scratch[NT / kWave + 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -165,26 +411,18 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
   const int tiles_n = (N + BN - 1) / BN;
   const int KI = (K + BK - 1) / BK;
   const int total = bs[E] * tiles_n;
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.A, p.a_bytes);
+  FwdOp<BM, BN> op;
+  op.rsA = uniform_rsrc(p.A, p.a_bytes);
+  op.lds0 = lds_addr(lds);
+  op.K = K;
+  op.wid = wid;
   const uint32_t wbytes = (uint32_t)N * K * 2;
-  const int ch = tid & 7, rsub = tid >> 3;
 
-  const int G = gridDim.x, Lb = logical_block();
-  const bool sk = p.stream_k != 0;
-  const int64_t tot_it = (int64_t)total * KI;
-  int64_t it = sk ? tot_it * Lb / G : (int64_t)Lb * KI;
-  int64_t it_end = sk ? tot_it * (Lb + 1) / G : min(tot_it, it + KI);
-  // stream-K: one contiguous slice of the (tile, stage) space per workgroup;
-  // otherwise whole tiles Lb, Lb + G, ...
-  for (; it < it_end;) {
-    const int tau = (int)(it / KI);
-    const int kb = (int)(it - (int64_t)tau * KI);
-    const int ke = (int)min((int64_t)KI, kb + (it_end - it));
-    it += ke - kb;
-    if (!sk && it >= it_end) {
-      it += (int64_t)(G - 1) * KI;
-      it_end = min(tot_it, it + KI);
-    }
+  const int Lb = logical_block();
+  WorkSplit ws;
+  ws.init(total, KI, gridDim.x, Lb, p.stream_k != 0);
+  int tau, kb, ke;
+  while (ws.next(tau, kb, ke, Lb)) {
     const TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
     if (c.rows <= 0) continue;
     const int n0 = c.nb * BN;
@@ -192,22 +430,16 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
     if (tid < BM) {
       const bool ok = tid < c.rows;
       const int r = c.row0 + tid;
-      tok[tid] = ok ? (FUSED ? p.row_to_token[r] : (r < p.M ? r : -1)) : -1;
+      const int t = ok ? (FUSED ? p.row_to_token[r] : (r < p.M ? r : -1)) : -1;
+      tok[tid] = t;
       wgt[tid] = (FUSED && ok) ? p.row_weight[r] : 0.f;
+      rowoff_a[tid] = t >= 0 ? t * K * 2 : -1;
     }
+    for (int j = tid; j < BN; j += NT) rowoff_b[j] = n0 + j < N ? (n0 + j) * K * 2 : -1;
     __syncthreads();
-    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(p.W + (size_t)c.g * N * K, wbytes);
-    uint32_t ao[CA], bo[CB];
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int t = tok[rsub + 32 * i];
-      ao[i] = t >= 0 ? (uint32_t)t * (uint32_t)K * 2u + ch * 16 : kOobOffset;
-    }
-#pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int n = n0 + rsub + 32 * i;
-      bo[i] = n < N ? (uint32_t)n * (uint32_t)K * 2u + ch * 16 : kOobOffset;
-    }
+    op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
+    op.da.setup(wid, lane, rowoff_a);
+    op.db.setup(wid, lane, rowoff_b);
     const int live_mi = min(MI, max(0, (c.rows - wm * 32 + 32 * WGM - 1) / (32 * WGM)));
     f32x16 acc[MI][NI];
 #pragma unroll
@@ -215,36 +447,8 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
 
-    u32x4 ra[CA], rb[CB];
-    auto gload = [&](int kt) {
-      const bool kin = kt * BK + ch * 8 < K;
-      const uint32_t dk = (uint32_t)kt * ROWB;
-#pragma unroll
-      for (int i = 0; i < CA; ++i) ra[i] = bload(rsA, kin ? ao[i] + dk : kOobOffset);
-#pragma unroll
-      for (int i = 0; i < CB; ++i) rb[i] = bload(rsW, kin ? bo[i] + dk : kOobOffset);
-    };
-    auto sstore = [&](int stage) {
-      char *As = lds + stage * (BM + BN) * ROWB;
-      char *Bs = As + BM * ROWB;
-#pragma unroll
-      for (int i = 0; i < CA; ++i) lds_store(As, lds_off(rsub + 32 * i, ch), ra[i]);
-#pragma unroll
-      for (int i = 0; i < CB; ++i) lds_store(Bs, lds_off(rsub + 32 * i, ch), rb[i]);
-    };
-    gload(kb);
-    sstore(0);
-    __syncthreads();
-    for (int kt = kb; kt < ke; ++kt) {
-      const int cur = (kt - kb) & 1;
-      const bool more = kt + 1 < ke;
-      if (more) gload(kt + 1);
-      const char *As = lds + cur * (BM + BN) * ROWB;
-      mma_stage<MI, NI, (BM <= 64)>(As, As + BM * ROWB, wm * 32, 32 * WGM, wn * 32, 32 * WGN,
-                                    lane, live_mi, acc);
-      if (more) sstore(cur ^ 1);
-      __syncthreads();
-    }
+    tile_multiply<MI, NI, WGM, WGN, (BM <= 64)>(op, lds, kb, ke, wm, wn, lane, live_mi, acc);
+
     // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
     // row tables; each row's base address is formed once for all column blocks
 #pragma unroll
@@ -259,18 +463,18 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
         for (int q = 0; q < 4; ++q) {
           const int t = t4[q];
           if (t < 0) continue;
-          const size_t rowoff = (size_t)t * N;
+          const size_t rowo = (size_t)t * N;
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni) {
             const int col = n0 + wn * 32 + ni * 32 * WGN + (lane & 31);
             if (col >= N) continue;
             const float v = acc[mi][ni][4 * j + q];
             if (FUSED) {
-              unsafeAtomicAdd((float *)p.C + rowoff + col, w4[q] * v);
+              unsafeAtomicAdd((float *)p.C + rowo + col, w4[q] * v);
             } else if (sizeof(Tout) == 4) {
-              ((float *)p.C)[rowoff + col] = v;
+              ((float *)p.C)[rowo + col] = v;
             } else {
-              ((bf16_t *)p.C)[rowoff + col] = f32_to_bf16(v);
+              ((__bf16 *)p.C)[rowo + col] = (__bf16)v;
             }
           }
         }
@@ -285,10 +489,11 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
 //   G[r, kc] = sum_n dY[tok(r), n] * W[g, n, kc]           (MFMA, fp32 acc)
 //   dX[tok(r), kc] += w_r * G[r, kc]                       (atomic)
 //   d_w[assign(r)] += sum_{kc in tile} G[r, kc] * x[tok(r), kc]   (atomic)
-// [GG] "The backward pass": the forward pattern with the weights transposed;
+// [GG] "The backward pass": the forward pattern with the weights read
+// transposed (here an MN-major weight tile read with transposing LDS reads);
 // [CARD] "How it works": the same gather / scatter-combine as the forward, and
 // the routing-weight gradient as the inner product of dY with the unweighted
-// product, here taken through the identity <dY W_e, x> = <dY, x W_e^T>.
+// product, taken through the identity <dY W_e, x> = <dY, x W_e^T>.
 // ============================================================================
 struct DxArgs {
   const bf16_t *dY;
@@ -303,21 +508,48 @@ struct DxArgs {
   const int32_t *row_to_token;
   const float *row_weight;
   int E, layout, capacity, K, N;
-  uint32_t dy_bytes;
+  uint32_t dy_bytes, x_bytes;
   int stream_k;
 };
 
-template <int BM, int BN, int WGM, int WGN>
+struct DxOp {
+  static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false;
+  static constexpr int DMA_PER_STAGE = 4 + 4;
+  KmajDma<256> da;
+  uint32_t bcol[4];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
+  __amdgpu_buffer_rsrc_t rsA, rsW;
+  uint32_t lds0, rowbytes_w;
+  int N, wid, lane;
+  MOE_DEV void setup_b(int kc0, int K) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = kc0 + 8 * MnmajMap::chunk_of(wid, i, lane);
+      bcol[i] = col < K ? (uint32_t)col * 2u : kOobOffset;
+    }
+  }
+  MOE_DEV void issue(int kt, int buf) {
+    const uint32_t t = lds0 + (uint32_t)buf * STAGE;
+    da.issue(rsA, kt, N, t, wid);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = kt * BK + MnmajMap::row_of(wid, i, lane);
+      const uint32_t off = (n < N && bcol[i] != kOobOffset) ? (uint32_t)n * rowbytes_w + bcol[i]
+                                                            : kOobOffset;
+      dma16(rsW, off, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
+    }
+  }
+  MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
+};
+
 __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int MI = WTM / 32, NI = WTN / 32;
-  constexpr int CA = BM / 32;
-  static_assert(BN == 256, "transposing loader covers 256 output columns");
+  constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2;
+  constexpr int MI = 4, NI = 4;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
   __shared__ __attribute__((aligned(16))) int tok[BM];
   __shared__ __attribute__((aligned(16))) float wgt[BM];
   __shared__ __attribute__((aligned(16))) int asg[BM];
+  __shared__ int rowoff_a[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
@@ -327,27 +559,21 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
   const int tiles_n = (K + BN - 1) / BN;  // output columns run over K
   const int KI = (N + BK - 1) / BK;       // reduction runs over N
   const int total = bs[E] * tiles_n;
-  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.dY, p.dy_bytes);
+  DxOp op;
+  op.rsA = uniform_rsrc(p.dY, p.dy_bytes);
+  op.lds0 = lds_addr(lds);
+  op.rowbytes_w = (uint32_t)K * 2u;
+  op.N = N;
+  op.wid = wid;
+  op.lane = lane;
   const uint32_t wbytes = (uint32_t)N * K * 2;
-  const int ch = tid & 7, rsub = tid >> 3;
-  const int cb = tid & 31, nb = tid >> 5;  // transposing loader: 8 cols x 8 rows block
+  const __amdgpu_buffer_rsrc_t rsX = uniform_rsrc(p.x, p.x_bytes);
 
-  const int G = gridDim.x, Lb = logical_block();
-  const bool sk = p.stream_k != 0;
-  const int64_t tot_it = (int64_t)total * KI;
-  int64_t it = sk ? tot_it * Lb / G : (int64_t)Lb * KI;
-  int64_t it_end = sk ? tot_it * (Lb + 1) / G : min(tot_it, it + KI);
-  // stream-K: one contiguous slice of the (tile, stage) space per workgroup;
-  // otherwise whole tiles Lb, Lb + G, ...
-  for (; it < it_end;) {
-    const int tau = (int)(it / KI);
-    const int kb = (int)(it - (int64_t)tau * KI);
-    const int ke = (int)min((int64_t)KI, kb + (it_end - it));
-    it += ke - kb;
-    if (!sk && it >= it_end) {
-      it += (int64_t)(G - 1) * KI;
-      it_end = min(tot_it, it + KI);
-    }
+  const int Lb = logical_block();
+  WorkSplit ws;
+  ws.init(total, KI, gridDim.x, Lb, p.stream_k != 0);
+  int tau, kb, ke;
+  while (ws.next(tau, kb, ke, Lb)) {
     const TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
     if (c.rows <= 0) continue;
     const int kc0 = c.nb * BN;
@@ -355,65 +581,49 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
     if (tid < BM) {
       const bool ok = tid < c.rows;
       const int r = c.row0 + tid;
-      tok[tid] = ok ? p.row_to_token[r] : -1;
+      const int t = ok ? p.row_to_token[r] : -1;
+      tok[tid] = t;
       wgt[tid] = ok ? p.row_weight[r] : 0.f;
       asg[tid] = ok ? p.row_to_assign[r] : -1;
+      rowoff_a[tid] = t >= 0 ? t * N * 2 : -1;
     }
     __syncthreads();
-    const __amdgpu_buffer_rsrc_t rsW = make_rsrc(p.W + (size_t)c.g * N * K, wbytes);
-    uint32_t ao[CA];
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int t = tok[rsub + 32 * i];
-      ao[i] = t >= 0 ? (uint32_t)t * (uint32_t)N * 2u + ch * 16 : kOobOffset;
-    }
-    const int kcol = kc0 + cb * 8;
-    const bool col_ok = kcol < K;
-    const int live_mi = min(MI, max(0, (c.rows - wm * 32 + 32 * WGM - 1) / (32 * WGM)));
+    op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
+    op.da.setup(wid, lane, rowoff_a);
+    op.setup_b(kc0, K);
     f32x16 acc[MI][NI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
 
-    u32x4 ra[CA], rb[8];
-    auto gload = [&](int kt) {
-      const bool kin = kt * BK + ch * 8 < N;
-      const uint32_t dk = (uint32_t)kt * ROWB;
+    tile_multiply<MI, NI, WGM, WGN, false>(op, lds, kb, ke, wm, wn, lane, MI, acc);
+
+    // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: eight
+    // 32-column K-major sub-tiles into the (now idle) LDS stages
+    if (p.d_w) {
+      barrier();
+      const uint32_t l0 = lds_addr(lds);
 #pragma unroll
-      for (int i = 0; i < CA; ++i) ra[i] = bload(rsA, kin ? ao[i] + dk : kOobOffset);
+      for (int q = 0; q < 8; ++q) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int n = kt * BK + nb * 8 + j;
-        rb[j] = bload(rsW, (col_ok && n < N) ? (uint32_t)n * (uint32_t)K * 2u + (uint32_t)kcol * 2u
-                                              : kOobOffset);
+        for (int i = 0; i < 4; ++i) {
+          const int row = (wid * 4 + i) * 16 + (lane >> 2);
+          const int cch = (lane & 3) ^ ((row >> 2) & 3);
+          const int t = tok[row];
+          const int col = kc0 + q * 32 + cch * 8;
+          const uint32_t off =
+              (t >= 0 && col < K) ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u : kOobOffset;
+          dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * 4 + i) * 1024));
+        }
       }
-    };
-    auto sstore = [&](int stage) {
-      char *As = lds + stage * (BM + BN) * ROWB;
-      char *Bs = As + BM * ROWB;
-#pragma unroll
-      for (int i = 0; i < CA; ++i) lds_store(As, lds_off(rsub + 32 * i, ch), ra[i]);
-      transpose8x8_store(rb, Bs, cb * 8, nb);
-    };
-    gload(kb);
-    sstore(0);
-    __syncthreads();
-    for (int kt = kb; kt < ke; ++kt) {
-      const int cur = (kt - kb) & 1;
-      const bool more = kt + 1 < ke;
-      if (more) gload(kt + 1);
-      const char *As = lds + cur * (BM + BN) * ROWB;
-      mma_stage<MI, NI, (BM <= 64)>(As, As + BM * ROWB, wm * 32, 32 * WGM, wn * 32, 32 * WGN,
-                                    lane, live_mi, acc);
-      if (more) sstore(cur ^ 1);
-      __syncthreads();
+      wait_vmcnt<0>();
+      barrier();
     }
     // epilogue: weighted atomic scatter of G into dX and, per row, the partial
     // inner product of G with x over this tile's columns into d_w
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      if (BM <= 64 && mi >= live_mi) continue;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
@@ -423,16 +633,22 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int t = t4[q];
+          const int rl = rq + q;
           float part = 0.f;
           if (t >= 0) {
-            const size_t rowoff = (size_t)t * K;
+            const size_t rowo = (size_t)t * K;
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
-              const int col = kc0 + wn * 32 + ni * 32 * WGN + (lane & 31);
+              const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
+              const int col = kc0 + cl;
               if (col >= K) continue;
               const float g = acc[mi][ni][4 * j + q];
-              if (p.dX) unsafeAtomicAdd(p.dX + rowoff + col, w4[q] * g);
-              if (p.d_w) part = fmaf(g, bf16_to_f32(p.x[rowoff + col]), part);
+              if (p.dX) unsafeAtomicAdd(p.dX + rowo + col, w4[q] * g);
+              if (p.d_w) {
+                const __bf16 xv = *(const __bf16 *)(lds + (cl >> 5) * OPND +
+                                                    kmaj_off(rl, (cl >> 3) & 3) + (cl & 7) * 2);
+                part = fmaf(g, (float)xv, part);
+              }
             }
           }
           if (p.d_w) {
@@ -456,8 +672,12 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
 // dealt to workgroups in a snake order, so the longest reductions start first
 // and the per-workgroup sums even out ([NOTE] 4.2: hot experts get more work
 // units and the persistent workgroups absorb the imbalance).
-// The routing weight is applied to dY in fp32 and rounded to bf16 before the
-// multiply (one bf16 rounding per product).
+// Both operands are MN-major tiles of 32 gathered token rows, loaded by DMA.
+// The routing weights of a stage are DMA'd next to it; each dY fragment is
+// multiplied by its rows' weights in fp32 and rounded to bf16 before the MFMA
+// (one bf16 rounding per product).  The tokens that address a stage's rows are
+// themselves DMA'd into a small LDS ring four stages ahead, so issuing a stage
+// never waits on a global load outside the DMA accounting.
 // ============================================================================
 struct DwArgs {
   const bf16_t *dY;
@@ -469,15 +689,84 @@ struct DwArgs {
   const int32_t *row_to_token;
   const float *row_weight;
   int E, layout, capacity, K, N;
-  uint32_t dy_bytes, x_bytes;
+  uint32_t dy_bytes, x_bytes, rw_bytes;
   int weighted;
+};
+
+struct DwOp {
+  static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true;
+  // per stage: 4 dY + 4 x chunks, the stage's routing weights, the tokens of
+  // the stage NSTAGE ahead
+  static constexpr int DMA_PER_STAGE = 4 + 4 + 1 + 1;
+  __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
+  uint32_t lds0;
+  const char *lds;
+  int r0, m, wid, lane, K, N, weighted;
+  uint32_t ncol[4], kcol[4];  // byte offsets of this lane's column chunk (dY / x), or OOB
+
+  MOE_DEV void setup(int n0, int kc0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = MnmajMap::chunk_of(wid, i, lane);
+      ncol[i] = n0 + 8 * ch < N ? (uint32_t)(n0 + 8 * ch) * 2u : kOobOffset;
+      kcol[i] = kc0 + 8 * ch < K ? (uint32_t)(kc0 + 8 * ch) * 2u : kOobOffset;
+    }
+  }
+  MOE_DEV int ring_off(int kt) const { return TOKREGION + (kt & 7) * TOKSLOT + wid * 256; }
+  // Tokens of stages kt0 .. kt0+n-1 into the ring, synchronously (no DMA in flight).
+  MOE_DEV void fill_ring(const int32_t *r2t, int kt0, int n) {
+    for (int s = 0; s < n; ++s) {
+      const int q = (kt0 + s) * BK + lane;
+      if (lane < 32) *(int *)(lds + ring_off(kt0 + s) + lane * 4) = q < m ? r2t[r0 + q] : -1;
+    }
+  }
+  MOE_DEV void issue(int kt, int buf) {
+    // tokens of this wave's rows 8*wid .. +7 of stage kt (ring copy of this wave)
+    const i32x4 ta = *(const i32x4 *)(lds + ring_off(kt) + wid * 32);
+    const i32x4 tb = *(const i32x4 *)(lds + ring_off(kt) + wid * 32 + 16);
+    const uint32_t t = lds0 + (uint32_t)buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rl = 2 * i + (lane >> 5);  // row within the wave's 8
+      const int q = kt * BK + 8 * wid + rl;
+      int tok = i < 2 ? ta[rl & 3] : tb[rl & 3];
+      if (q >= m) tok = -1;
+      const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
+                                ? (uint32_t)tok * (uint32_t)N * 2u + ncol[i]
+                                : kOobOffset;
+      dma16(rsY, offy, t + (uint32_t)((wid * 4 + i) * 1024));
+      const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
+                                ? (uint32_t)tok * (uint32_t)K * 2u + kcol[i]
+                                : kOobOffset;
+      dma16(rsX, offx, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
+    }
+    // routing weights of the stage's 32 rows into this wave's strip
+    const int qw = kt * BK + lane;
+    const uint32_t offw = (lane < 32 && qw < m) ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
+    dma4(rsW, offw, lds0 + (uint32_t)(WREGION + buf * WBYTES + wid * 256));
+    // tokens of stage kt + NSTAGE into the ring (consumed by its issue, after the
+    // barrier that waits for this stage)
+    const int qt = (kt + NSTAGE) * BK + lane;
+    const uint32_t offt = (lane < 32 && qt < m) ? (uint32_t)(r0 + qt) * 4u : kOobOffset;
+    dma4(rsT, offt, lds0 + (uint32_t)ring_off(kt + NSTAGE));
+  }
+  // factors of the 8 reduction rows this lane holds in step `step`
+  MOE_DEV void row_scale(int buf, int step, int ln, float (&w)[8]) {
+    const float *src = (const float *)(lds + WREGION + buf * WBYTES + wid * 256) + step * 16 +
+                       8 * (ln >> 5);
+    const f32x4 a = *(const f32x4 *)src, b = *(const f32x4 *)(src + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w[i] = weighted ? a[i] : 1.f;
+      w[4 + i] = weighted ? b[i] : 1.f;
+    }
+  }
 };
 
 template <typename Tout>
 __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2;
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int MI = WTM / 32, NI = WTN / 32;
+  constexpr int MI = 4, NI = 4;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / WGN, wn = wid % WGN;
@@ -486,9 +775,18 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   const int per_e = tn * tk;
   const int units = E * per_e;
   const int G = gridDim.x, L = logical_block();
-  const __amdgpu_buffer_rsrc_t rsY = make_rsrc(p.dY, p.dy_bytes);
-  const __amdgpu_buffer_rsrc_t rsX = make_rsrc(p.x, p.x_bytes);
-  const int cb = tid & 31, rb = tid >> 5;
+  DwOp op;
+  op.rsY = uniform_rsrc(p.dY, p.dy_bytes);
+  op.rsX = uniform_rsrc(p.x, p.x_bytes);
+  op.rsW = uniform_rsrc(p.row_weight, p.rw_bytes);
+  op.rsT = uniform_rsrc(p.row_to_token, p.rw_bytes);
+  op.lds0 = lds_addr(lds);
+  op.lds = lds;
+  op.wid = wid;
+  op.lane = lane;
+  op.K = K;
+  op.N = N;
+  op.weighted = p.weighted;
 
   for (int round = 0;; ++round) {
     const int base = round * G;
@@ -499,9 +797,9 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
     const int t = u - (u / per_e) * per_e;
     const int n0 = (t / tk) * BM, kc0 = (t % tk) * BN;
     const int m = p.counts[e];
-    const int r0 = p.layout == MOE_LAYOUT_MASKED ? e * p.capacity : p.offsets[e] - m;
-    const int ncol = n0 + cb * 8, kcol = kc0 + cb * 8;
-    const bool n_ok = ncol < N, k_ok = kcol < K;
+    op.r0 = p.layout == MOE_LAYOUT_MASKED ? e * p.capacity : p.offsets[e] - m;
+    op.m = m;
+    op.setup(n0, kc0);
     const int KI = (m + BK - 1) / BK;
 
     f32x16 acc[MI][NI];
@@ -509,54 +807,10 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
-
-    u32x4 ra[8], rbx[8];
-    float wr[8];
-    auto gload = [&](int kt) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int q = kt * BK + rb * 8 + j;
-        const bool ok = q < m;
-        const int tk_ = ok ? p.row_to_token[r0 + q] : 0;
-        wr[j] = ok ? (p.weighted ? p.row_weight[r0 + q] : 1.f) : 0.f;
-        ra[j] = bload(rsY, (ok && n_ok) ? (uint32_t)tk_ * (uint32_t)N * 2u + (uint32_t)ncol * 2u
-                                        : kOobOffset);
-        rbx[j] = bload(rsX, (ok && k_ok) ? (uint32_t)tk_ * (uint32_t)K * 2u + (uint32_t)kcol * 2u
-                                         : kOobOffset);
-      }
-    };
-    auto sstore = [&](int stage) {
-      char *As = lds + stage * (BM + BN) * ROWB;
-      char *Bs = As + BM * ROWB;
-      if (p.weighted) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-            const uint32_t v = ra[j][d];
-            const bf16_t lo = f32_to_bf16(wr[j] * __uint_as_float(v << 16));
-            const bf16_t hi = f32_to_bf16(wr[j] * __uint_as_float(v & 0xFFFF0000u));
-            ra[j][d] = (uint32_t)lo | ((uint32_t)hi << 16);
-          }
-      }
-      transpose8x8_store(ra, As, cb * 8, rb);
-      transpose8x8_store(rbx, Bs, cb * 8, rb);
-    };
     if (KI > 0) {
       __syncthreads();  // previous unit done with LDS
-      gload(0);
-      sstore(0);
-      __syncthreads();
-      for (int kt = 0; kt < KI; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < KI;
-        if (more) gload(kt + 1);
-        const char *As = lds + cur * (BM + BN) * ROWB;
-        mma_stage<MI, NI, false>(As, As + BM * ROWB, wm * 32, 32 * WGM, wn * 32, 32 * WGN, lane,
-                                 MI, acc);
-        if (more) sstore(cur ^ 1);
-        __syncthreads();
-      }
+      op.fill_ring(p.row_to_token, 0, KI < NSTAGE ? KI : NSTAGE);
+      tile_multiply<MI, NI, WGM, WGN, false>(op, lds, 0, KI, wm, wn, lane, MI, acc);
     }
     // store (exact zeros for an empty expert)
     Tout *out = (Tout *)p.dW + (size_t)e * N * K;
@@ -573,7 +827,7 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
           if (sizeof(Tout) == 4)
             ((float *)out)[(size_t)n * K + col] = acc[mi][ni][i];
           else
-            ((bf16_t *)out)[(size_t)n * K + col] = f32_to_bf16(acc[mi][ni][i]);
+            ((__bf16 *)out)[(size_t)n * K + col] = (__bf16)acc[mi][ni][i];
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -581,11 +835,9 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   }
 }
 
-// dynamic LDS: the two operand stages (the row tables are static LDS)
-template <int BM, int BN>
-constexpr size_t gemm_smem() {
-  return (size_t)2 * (BM + BN) * ROWB;
-}
+// dynamic LDS: NSTAGE stages of (A 16 KB, B 16 KB), the weight strips and the
+// 8-slot token ring
+constexpr size_t kStageLds = (size_t)TOKREGION + 8 * (size_t)TOKSLOT;
 
 template <typename K>
 hipError_t set_smem(K kernel, size_t bytes) {
@@ -607,18 +859,17 @@ hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offset
   FwdArgs a{(const bf16_t *)A, (const bf16_t *)W, C, offsets, nullptr, nullptr, nullptr, nullptr,
             E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), 0, M};
   constexpr int BM = 256, BN = 256;
-  const size_t smem = gemm_smem<BM, BN>();
   const dim3 grid(device_cu_count()), block(NT);
   if (out_dtype == MOE_F32) {
     auto k = mfma_fwd_kernel<BM, BN, 2, 2, false, float>;
-    hipError_t e = set_smem(k, smem);
+    hipError_t e = set_smem(k, kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, smem, st, a);
+    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   } else {
     auto k = mfma_fwd_kernel<BM, BN, 2, 2, false, bf16_t>;
-    hipError_t e = set_smem(k, smem);
+    hipError_t e = set_smem(k, kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, smem, st, a);
+    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   }
   return hipGetLastError();
 }
@@ -633,34 +884,31 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
     constexpr int BM = 64, BN = 256;
     a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
     auto k = mfma_fwd_kernel<BM, BN, 1, 4, true, float>;
-    const size_t smem = gemm_smem<BM, BN>();
-    hipError_t e = set_smem(k, smem);
+    hipError_t e = set_smem(k, kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, smem, st, a);
+    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   } else {
     constexpr int BM = 256, BN = 256;
     a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
     auto k = mfma_fwd_kernel<BM, BN, 2, 2, true, float>;
-    const size_t smem = gemm_smem<BM, BN>();
-    hipError_t e = set_smem(k, smem);
+    hipError_t e = set_smem(k, kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, smem, st, a);
+    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   }
   return hipGetLastError();
 }
 
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, hipStream_t st) {
-  constexpr int BM = 256, BN = 256;
+  constexpr int BM = 256;
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
            s.counts, s.block_start + bm_index(BM) * (s.E + 1), s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
-           env_int("MOE_VS_STREAM_K", 1)};
-  auto k = mfma_dx_kernel<BM, BN, 2, 2>;
-  const size_t smem = gemm_smem<BM, BN>();
-  hipError_t e = set_smem(k, smem);
+           (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 1)};
+  auto k = mfma_dx_kernel;
+  hipError_t e = set_smem(k, kStageLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), smem, st, a);
+  hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), kStageLds, st, a);
   return hipGetLastError();
 }
 
@@ -668,12 +916,12 @@ hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, voi
                        int N, hipStream_t st) {
   DwArgs a{(const bf16_t *)dY, (const bf16_t *)x, dW, s.offsets, s.counts, s.expert_order,
            s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-           (uint32_t)((size_t)s.T * N * 2), (uint32_t)((size_t)s.T * K * 2), 1};
+           (uint32_t)((size_t)s.T * N * 2), (uint32_t)((size_t)s.T * K * 2),
+           (uint32_t)((size_t)s.R * 4), 1};
   auto k = mfma_dw_kernel<bf16_t>;
-  const size_t smem = (size_t)2 * 512 * ROWB;
-  hipError_t e = set_smem(k, smem);
+  hipError_t e = set_smem(k, kStageLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), smem, st, a);
+  hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), kStageLds, st, a);
   return hipGetLastError();
 }
 
