@@ -39,13 +39,19 @@ PEAK_HBM_GBS = 8000.0
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=400,
+                   help="untimed steps first (also brings the GPU clocks to their loaded state)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum host time spent on the oracle sample")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
     return p.parse_args()
 
 
-def cpu_baseline(r, flops_step: float) -> dict:
+def cpu_baseline(r, flops_step: float, min_seconds: float) -> dict:
     """The CPU oracle, untuned, on the host cores: one full step (forward and
     backward) of the same workload."""
     from oracle import moe_oracle as O
@@ -56,15 +62,97 @@ def cpu_baseline(r, flops_step: float) -> dict:
         blas = ",".join(sorted({f"{d.get('internal_api')} {d.get('version')}" for d in info}))
     except Exception:  # pragma: no cover
         threads, blas = os.cpu_count() or 1, "unknown"
+    reps = 0
     t0 = time.perf_counter()
-    O.moe_forward(r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
-    O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
-    dt = time.perf_counter() - t0
-    return {"value": round(flops_step / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": "one full step (forward + backward, float64) of the same workload",
+    while True:
+        O.moe_forward(r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+        O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds:
+            break
+    return {"value": round(reps * flops_step / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} full steps (forward + backward, float64) of the same workload",
             "seconds": round(dt, 3), "host_cpu": platform.processor() or platform.machine(),
             "blas": blas}
+
+
+KERNEL_SOURCES = ("moe_variable_size_amd/csrc/mfma.hip", "moe_variable_size_amd/csrc/common.hpp",
+                  "moe_variable_size_amd/csrc/api.hip")
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources: counter figures are used only while it
+    still matches the one they were taken with."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _traffic(kernel_family: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy's reading),
+    or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel_family)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def decode_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
+    """Masked fixed-capacity decode (E=64, capacity 64, T=128 top-8, K=7168,
+    N=2048): the forward streams every active expert's weights once.  Reported
+    as HBM GB/s of the algorithmic bytes (weights of active experts + x + y)."""
+    r = WL.config5()
+    T, K, N, E, k, cap = r.T, r.K, r.N, r.E, r.k, r.capacity
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, W = to_dev(r.x), to_dev(r.W)
+    ids = torch.from_numpy(r.expert_ids).to(dev)
+    w = torch.from_numpy(r.topk_weights).to(dev)
+    lay = api.MOE_LAYOUT_MASKED
+    ws = torch.empty(api.moe_schedule_workspace_bytes(T, k, E, lay, cap), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+
+    def step():
+        sch = api.moe_build_schedule(ids, w, E, layout=lay, capacity=cap, workspace=ws)
+        api.moe_fused_fwd(x, W, sch, y=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    api.moe_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    api.moe_timing_enable(False)
+    tot, n = api.moe_timing_read("fused_fwd")
+    fwd_us = tot * 1e3 / max(n, 1)
+    active = int(np.count_nonzero(np.bincount(r.expert_ids.ravel(), minlength=E)))
+    nbytes = active * N * K * 2 + T * K * 2 + T * N * 4
+    gbs = nbytes / (fwd_us * 1e-6) / 1e9
+    return {"workload": f"{r.name} forward (masked layout)", "active_experts": active,
+            "bytes_per_launch": nbytes, "fwd_us": round(fwd_us, 3),
+            "hbm_GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "step_ms": round(ms_step, 4),
+            "step_GBps": round(nbytes / (ms_step * 1e-3) / 1e9, 1)}
 
 
 def main():
@@ -123,6 +211,15 @@ def main():
         tot, n = api.moe_timing_read(f)
         kt[f] = {"avg_us": round(tot * 1e3 / max(n, 1), 3), "launches": n}
 
+    if a.calib_copy:
+        # a plain copy of known size for the HBM byte counters
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     gemm = 2.0 * S * K * N
     flops_step = 3 * gemm + 2.0 * S * N
     value = flops_step / (ms_step * 1e-3) / 1e12
@@ -151,12 +248,19 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
         "kernels_us": kt,
+        "pct_bf16_peak_fwd": round(100.0 * gemm / (kt["fused_fwd"]["avg_us"] * 1e-6) / 1e12
+                                   / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(gemm / (kt["fused_fwd"]["avg_us"] * 1e-6) / 1e12, 2),
         "bwd_tflops": round((2 * gemm + 2.0 * S * N)
                             / ((kt["bwd_dx"]["avg_us"] + kt["bwd_dw"]["avg_us"]) * 1e-6) / 1e12, 2),
     }
+    tr = _traffic(dom)
+    if tr is not None:
+        out["roofline"]["traffic"] = tr
+    if not a.no_decode:
+        out["decode"] = decode_line(torch, api, WL, dev, a.steps, a.warmup)
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(r, flops_step)
+        out["cpu_baseline"] = cpu_baseline(r, flops_step, a.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 
