@@ -46,6 +46,8 @@
 //    all workgroups (stream-K), which evens out the tail.
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -227,89 +229,155 @@ MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 
 
 // ---- the pipelined tile multiply --------------------------------------------
 // Op supplies:
-//   static constexpr bool A_KMAJ, B_KMAJ, A_SCALED;  operand layouts; A_SCALED:
-//       A fragments are multiplied by per-reduction-row factors read with
-//       row_scale(buf, step, lane, w)
-//   static constexpr int DMA_PER_STAGE;   DMA operations per thread per stage
-//   void issue(int kt, int buf);           start loading stage kt into buffer buf
+//   static constexpr bool A_KMAJ, B_KMAJ  operand layouts
+//   static constexpr bool A_SCALED        A fragments are multiplied by per-
+//       reduction-row factors read with row_scale(buf, step, lane, w)
+//   static constexpr bool PREFETCH        prefetch(kt) must run (LDS reads)
+//       before the parts of stage kt are issued
+//   static constexpr int DMA_PER_STAGE    DMA instructions per thread per stage
+//   void issue_part(int kt, int buf, int j)  j-th DMA instruction of stage kt
 // Buffer b: A at lds + b * STAGE, B at + OPND.
+//
+// Per stage (two 16-deep MFMA steps, operand slots 0 and 1):
+//   phase A: MFMAs of step 0 (slot 0), with the reads of step 1 into slot 1
+//            placed between them;
+//   phase B: wait for the next stage's DMA and this wave's reads; barrier
+//            (all waves are done with this stage's buffer);
+//   phase C: MFMAs of step 1 (slot 1), with the reads of the next stage's
+//            step 0 into slot 0 and the DMA of stage +NSTAGE into the freed
+//            buffer placed between them.
+// The MFMA pipe is idle only across the barrier.  The order inside a phase is
+// pinned with scheduling fences.
+#define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
 template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op>
 MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
                            int live_mi, f32x16 (&acc)[MI][NI]) {
   constexpr int D = Op::DMA_PER_STAGE;
+  constexpr int NM = MI * NI;                         // MFMAs per step
+  constexpr int NR = MI + NI + (Op::A_SCALED ? 1 : 0);  // read items per step
+  constexpr int NS = Op::A_SCALED ? MI : 0;           // scale items per step
+  constexpr int NP = Op::PREFETCH ? 1 : 0;
+  constexpr int SLOTS = NM - NS;                      // slots for reads / DMA
+  static_assert(SLOTS > 0, "tile too small");
   bf16x8_t fa[2][MI], fb[2][NI];
-  auto frags = [&](int buf, int step, int slot) __attribute__((always_inline)) {
+  float sc[2][8];
+
+  auto read_item = [&](int buf, int step, int slot, int f) __attribute__((always_inline)) {
     const char *As = lds + buf * STAGE;
     const char *Bs = As + OPND;
-    float w[8];
-    if (Op::A_SCALED) op.row_scale(buf, step, lane, w);
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
+    if (Op::A_SCALED && f == 0) {
+      op.row_scale(buf, step, lane, sc[slot]);
+      return;
+    }
+    const int g = f - (Op::A_SCALED ? 1 : 0);
+    if (g < MI) {
+      const int mi = g;
       if (Op::A_KMAJ)
         fa[slot][mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
       else
         fa[slot][mi] = frag_mnmaj(As, wm * 32 + mi * 32 * WGM, step, lane);
-      if (Op::A_SCALED) fa[slot][mi] = scale_frag(fa[slot][mi], w);
-    }
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
+    } else {
+      const int ni = g - MI;
       if (Op::B_KMAJ)
         fb[slot][ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
       else
         fb[slot][ni] = frag_mnmaj(Bs, wn * 32 + ni * 32 * WGN, step, lane);
     }
   };
-  auto mma = [&](int slot) __attribute__((always_inline)) {
+  auto mfma = [&](int slot, int i) __attribute__((always_inline)) {
+    const int mi = i / NI, ni = i % NI;
+    if (SKIP && mi >= live_mi) return;  // wave-uniform: rows past the group end
+    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
+                                                          acc[mi][ni], 0, 0, 0);
+  };
+  // phase A of the stage in buffer `buf`; with PF: prefetch for stage pf
+  auto phase_a = [&](int buf, int pf, auto PF) __attribute__((always_inline)) {
+    constexpr int NIT = NR + NP;
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (SKIP && mi >= live_mi) continue;  // wave-uniform: rows past the group end
+    for (int i = 0; i < NM; ++i) {
+      mfma(0, i);
+      MOE_FENCE();
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
-                                                              acc[mi][ni], 0, 0, 0);
+      for (int j = 0; j < NIT; ++j) {
+        if (j * SLOTS / NIT != i) continue;
+        if (j < NR)
+          read_item(buf, 1, 1, j);
+        else if (decltype(PF)::value)
+          op.prefetch(pf);
+      }
+      if (NS > 0 && i >= NM - NS) fa[1][i - (NM - NS)] = scale_frag(fa[1][i - (NM - NS)], sc[1]);
+      MOE_FENCE();
     }
   };
-  constexpr int NREAD = (Op::A_KMAJ ? MI : 2 * MI) + (Op::B_KMAJ ? NI : 2 * NI);
-  constexpr int NMFMA = MI * NI;
-  auto interleave = [&]() __attribute__((always_inline)) {
-    // one LDS read after each MFMA until the reads run out
+  // phase C: step 1 of the stage in `buf`, step-0 reads of `nbuf`; with DMA:
+  // issue stage `dma` into `buf`
+  auto phase_c = [&](int buf, int nbuf, int dma, auto DMA) __attribute__((always_inline)) {
+    constexpr int NIT = NR + D;
 #pragma unroll
-    for (int i = 0; i < (NREAD < NMFMA ? NREAD : NMFMA); ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < NM; ++i) {
+      mfma(1, i);
+      MOE_FENCE();
+#pragma unroll
+      for (int j = 0; j < NIT; ++j) {
+        if (j * SLOTS / NIT != i) continue;
+        if (j < NR)
+          read_item(nbuf, 0, 0, j);
+        else if (decltype(DMA)::value)
+          op.issue_part(dma, buf, j - NR);
+      }
+      if (NS > 0 && i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
+      MOE_FENCE();
     }
-    if (NMFMA > NREAD) __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
-    if (NREAD > NMFMA) __builtin_amdgcn_sched_group_barrier(0x100, NREAD - NMFMA, 0);
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    wait_lgkm0();
+    MOE_FENCE();
+    __builtin_amdgcn_s_barrier();
+    MOE_FENCE();
   };
 
   // prologue: up to NSTAGE stages in flight; wait for the first
   const int n = ke - kb;
   const int pre = n < NSTAGE ? n : NSTAGE;
-  for (int s = 0; s < pre; ++s) op.issue(kb + s, s);
+  for (int s = 0; s < pre; ++s) {
+    if (Op::PREFETCH) op.prefetch(kb + s);
+#pragma unroll
+    for (int j = 0; j < D; ++j) op.issue_part(kb + s, s, j);
+  }
   wait_stages<D>(pre - 1 > 2 ? 3 : pre - 1);
-  wait_lgkm0();
-  barrier();
-  frags(0, 0, 0);
-  for (int kt = kb; kt < ke; ++kt) {
+  sync();
+#pragma unroll
+  for (int j = 0; j < NR; ++j) read_item(0, 0, 0, j);
+  if (NS > 0) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) fa[0][mi] = scale_frag(fa[0][mi], sc[0]);
+  }
+  MOE_FENCE();
+
+  int kt = kb;
+  // stages whose buffer is refilled with stage kt + NSTAGE
+  for (; kt + NSTAGE < ke; ++kt) {
     const int buf = (kt - kb) & (NSTAGE - 1);
-    __builtin_amdgcn_sched_barrier(0);
-    frags(buf, 1, 1);
-    mma(0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < ke) {
-      // issued and not yet waited: stages kt+1 .. min(kt+3, ke-1); keep the
-      // later ones in flight, wait for kt+1
-      const int later = min(2, ke - kt - 2);
-      wait_stages<D>(later);
-      wait_lgkm0();
-      barrier();
-      if (kt + NSTAGE < ke) op.issue(kt + NSTAGE, buf);  // buffer of stage kt is free
-      frags((buf + 1) & (NSTAGE - 1), 0, 0);  // first fragments of the next stage
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mma(1);
-    __builtin_amdgcn_sched_barrier(0);
+    phase_a(buf, kt + NSTAGE, std::integral_constant<bool, Op::PREFETCH>());
+    wait_vmcnt<2 * D>();  // stage kt+1 landed (kt+2, kt+3 may be in flight)
+    sync();
+    phase_c(buf, (buf + 1) & (NSTAGE - 1), kt + NSTAGE, std::true_type());
+  }
+  // the last stages: nothing more to issue
+  for (; kt + 1 < ke; ++kt) {
+    const int buf = (kt - kb) & (NSTAGE - 1);
+    phase_a(buf, 0, std::false_type());
+    wait_stages<D>(min(2, ke - kt - 2));
+    sync();
+    phase_c(buf, (buf + 1) & (NSTAGE - 1), 0, std::false_type());
+  }
+  // final stage
+  {
+    const int buf = (kt - kb) & (NSTAGE - 1);
+    phase_a(buf, 0, std::false_type());
+#pragma unroll
+    for (int i = 0; i < NM; ++i) mfma(1, i);
+    MOE_FENCE();
   }
 }
 
@@ -330,13 +398,12 @@ struct KmajDma {
       base[i] = ro >= 0 ? (uint32_t)ro + (uint32_t)c * 16u : kOobOffset;
     }
   }
-  MOE_DEV void issue(__amdgpu_buffer_rsrc_t rs, int kt, int kred, uint32_t lds_tile, int wid) {
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-      const bool in = kt * BK + chunk[i] * 8 < kred;
-      const uint32_t off = in ? base[i] + (uint32_t)kt * KROW : kOobOffset;
-      dma16(rs, off, lds_tile + (uint32_t)((wid * PER_WAVE + i) * 1024));
-    }
+  // instruction i of stage kt
+  MOE_DEV void issue_one(__amdgpu_buffer_rsrc_t rs, int kt, int kred, uint32_t lds_tile, int wid,
+                         int i) {
+    const bool in = kt * BK + chunk[i] * 8 < kred;
+    const uint32_t off = in ? base[i] + (uint32_t)kt * KROW : kOobOffset;
+    dma16(rs, off, lds_tile + (uint32_t)((wid * PER_WAVE + i) * 1024));
   }
 };
 
@@ -373,18 +440,21 @@ struct FwdArgs {
 
 template <int BM, int BN>
 struct FwdOp {
-  static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false;
+  static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false, PREFETCH = false;
   static constexpr int DMA_PER_STAGE = BM / 64 + BN / 64;
   KmajDma<BM> da;
   KmajDma<BN> db;
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0;
   int K, wid;
-  MOE_DEV void issue(int kt, int buf) {
+  MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    da.issue(rsA, kt, K, t, wid);
-    db.issue(rsW, kt, K, t + OPND, wid);
+    if (j < BM / 64)
+      da.issue_one(rsA, kt, K, t, wid, j);
+    else
+      db.issue_one(rsW, kt, K, t + OPND, wid, j - BM / 64);
   }
+  MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
 };
 
@@ -399,7 +469,8 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
   __shared__ int rowoff_a[BM], rowoff_b[BN];
   __shared__ int scratch[NT / kWave + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
   if (FUSED)
@@ -513,7 +584,7 @@ struct DxArgs {
 };
 
 struct DxOp {
-  static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false;
+  static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false, PREFETCH = false;
   static constexpr int DMA_PER_STAGE = 4 + 4;
   KmajDma<256> da;
   uint32_t bcol[4];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
@@ -527,17 +598,19 @@ struct DxOp {
       bcol[i] = col < K ? (uint32_t)col * 2u : kOobOffset;
     }
   }
-  MOE_DEV void issue(int kt, int buf) {
+  MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    da.issue(rsA, kt, N, t, wid);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    if (j < 4) {
+      da.issue_one(rsA, kt, N, t, wid, j);
+    } else {
+      const int i = j - 4;
       const int n = kt * BK + MnmajMap::row_of(wid, i, lane);
       const uint32_t off = (n < N && bcol[i] != kOobOffset) ? (uint32_t)n * rowbytes_w + bcol[i]
                                                             : kOobOffset;
       dma16(rsW, off, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
     }
   }
+  MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
 };
 
@@ -551,7 +624,8 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
   __shared__ __attribute__((aligned(16))) int asg[BM];
   __shared__ int rowoff_a[BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
   group_tables_from_schedule<NT>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
@@ -694,7 +768,7 @@ struct DwArgs {
 };
 
 struct DwOp {
-  static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true;
+  static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
   // per stage: 4 dY + 4 x chunks, the stage's routing weights, the tokens of
   // the stage NSTAGE ahead
   static constexpr int DMA_PER_STAGE = 4 + 4 + 1 + 1;
@@ -720,35 +794,43 @@ struct DwOp {
       if (lane < 32) *(int *)(lds + ring_off(kt0 + s) + lane * 4) = q < m ? r2t[r0 + q] : -1;
     }
   }
-  MOE_DEV void issue(int kt, int buf) {
-    // tokens of this wave's rows 8*wid .. +7 of stage kt (ring copy of this wave)
-    const i32x4 ta = *(const i32x4 *)(lds + ring_off(kt) + wid * 32);
-    const i32x4 tb = *(const i32x4 *)(lds + ring_off(kt) + wid * 32 + 16);
+  i32x4 ta, tb;  // tokens of this wave's 8 rows of the stage being issued
+  // tokens of this wave's rows 8*wid .. +7 of stage kt (ring copy of this wave)
+  MOE_DEV void prefetch(int kt) {
+    ta = *(const i32x4 *)(lds + ring_off(kt) + wid * 32);
+    tb = *(const i32x4 *)(lds + ring_off(kt) + wid * 32 + 16);
+  }
+  MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    if (j < 8) {
+      const int i = j & 3;
       const int rl = 2 * i + (lane >> 5);  // row within the wave's 8
       const int q = kt * BK + 8 * wid + rl;
       int tok = i < 2 ? ta[rl & 3] : tb[rl & 3];
       if (q >= m) tok = -1;
-      const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
-                                ? (uint32_t)tok * (uint32_t)N * 2u + ncol[i]
-                                : kOobOffset;
-      dma16(rsY, offy, t + (uint32_t)((wid * 4 + i) * 1024));
-      const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
-                                ? (uint32_t)tok * (uint32_t)K * 2u + kcol[i]
-                                : kOobOffset;
-      dma16(rsX, offx, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
+      if (j < 4) {
+        const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
+                                  ? (uint32_t)tok * (uint32_t)N * 2u + ncol[i]
+                                  : kOobOffset;
+        dma16(rsY, offy, t + (uint32_t)((wid * 4 + i) * 1024));
+      } else {
+        const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
+                                  ? (uint32_t)tok * (uint32_t)K * 2u + kcol[i]
+                                  : kOobOffset;
+        dma16(rsX, offx, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
+      }
+    } else if (j == 8) {
+      // routing weights of the stage's 32 rows into this wave's strip
+      const int qw = kt * BK + lane;
+      const uint32_t offw = (lane < 32 && qw < m) ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
+      dma4(rsW, offw, lds0 + (uint32_t)(WREGION + buf * WBYTES + wid * 256));
+    } else {
+      // tokens of stage kt + NSTAGE into the ring (read by its prefetch after
+      // this stage has been waited for)
+      const int qt = (kt + NSTAGE) * BK + lane;
+      const uint32_t offt = (lane < 32 && qt < m) ? (uint32_t)(r0 + qt) * 4u : kOobOffset;
+      dma4(rsT, offt, lds0 + (uint32_t)ring_off(kt + NSTAGE));
     }
-    // routing weights of the stage's 32 rows into this wave's strip
-    const int qw = kt * BK + lane;
-    const uint32_t offw = (lane < 32 && qw < m) ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
-    dma4(rsW, offw, lds0 + (uint32_t)(WREGION + buf * WBYTES + wid * 256));
-    // tokens of stage kt + NSTAGE into the ring (consumed by its issue, after the
-    // barrier that waits for this stage)
-    const int qt = (kt + NSTAGE) * BK + lane;
-    const uint32_t offt = (lane < 32 && qt < m) ? (uint32_t)(r0 + qt) * 4u : kOobOffset;
-    dma4(rsT, offt, lds0 + (uint32_t)ring_off(kt + NSTAGE));
   }
   // factors of the 8 reduction rows this lane holds in step `step`
   MOE_DEV void row_scale(int buf, int step, int ln, float (&w)[8]) {
@@ -768,7 +850,8 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2;
   constexpr int MI = 4, NI = 4;
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int K = p.K, N = p.N, E = p.E;
   const int tn = (N + BM - 1) / BM, tk = (K + BN - 1) / BN;
@@ -879,7 +962,7 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
   const dim3 grid(device_cu_count()), block(NT);
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 1), (int)s.T};
+            (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 0), (int)s.T};
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
     a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
@@ -904,7 +987,7 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
            s.counts, s.block_start + bm_index(BM) * (s.E + 1), s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
-           (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 1)};
+           (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 0)};
   auto k = mfma_dx_kernel;
   hipError_t e = set_smem(k, kStageLds);
   if (e != hipSuccess) return e;
