@@ -63,24 +63,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
 
 constexpr int NT = 256;        // 4 waves
-constexpr int BK = 32;         // reduction elements per stage
-constexpr int KROW = BK * 2;   // bytes per K-major LDS row
+constexpr int BK = 64;         // reduction elements per stage
+constexpr int KS = BK / 16;    // 16-deep MFMA steps per stage
+constexpr int KROW = BK * 2;   // bytes per K-major LDS row (one 128-byte line)
 constexpr int MNROW = 256 * 2; // bytes per MN-major LDS row (256 columns)
-constexpr int NSTAGE = 4;      // LDS stages
-constexpr int OPND = 256 * KROW;                  // 16 KB: one 256-wide operand tile
+constexpr int NSTAGE = 2;      // LDS stages
+constexpr int OPND = 256 * KROW;                  // 32 KB: one 256 x 64 operand tile
 constexpr int STAGE = 2 * OPND;                   // A then B
 constexpr int WREGION = NSTAGE * STAGE;           // per-stage routing weights (weight gradient)
 constexpr int WBYTES = 4 * 256;                   // per stage: 4 waves x 64 floats
 constexpr int TOKREGION = WREGION + NSTAGE * WBYTES;  // token ring (weight gradient)
 constexpr int TOKSLOT = 4 * 256;                  // per ring slot: 4 waves x 64 ints
+constexpr int TOKSLOTS = 4;                       // ring slots
+static_assert(OPND == BK * MNROW, "K-major and MN-major operand tiles have one size");
 
 // ---- LDS layouts --------------------------------------------------------------
 // The LDS serves 256 bytes per clock (64 banks x 4 B), i.e. sixteen 16-byte
 // lane accesses.  The swizzles make 16 consecutive lanes of an operand read hit
 // 16 different 16-byte bank groups.
-// K-major: chunk c (0..3) of row r at r*64 + ((c ^ ((r >> 2) & 3)) << 4): the 16
-// rows read together fall 4 per 256-byte line, each at a different chunk.
-MOE_DEV int kmaj_off(int row, int chunk) { return row * KROW + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// K-major: chunk c (0..7) of row r at r*128 + ((c ^ ((r >> 1) & 7)) << 4): of the
+// 16 rows read together, two share each 256-byte line of banks, and within the
+// pair the chunks differ, so the 16 lanes hit 16 different bank groups.
+MOE_DEV int kmaj_off(int row, int chunk) { return row * KROW + ((chunk ^ ((row >> 1) & 7)) << 4); }
 // MN-major: chunk c (0..31) of reduction row r at r*512 + ((c ^ ((r & 3) << 2)) << 4):
 // a transposing read touches 4 rows x 2 chunks per 16 lanes (4 chunks per 32).
 MOE_DEV int mnmaj_off(int row, int chunk) { return row * MNROW + ((chunk ^ ((row & 3) << 2)) << 4); }
@@ -238,30 +242,34 @@ MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 
 //   void issue_part(int kt, int buf, int j)  j-th DMA instruction of stage kt
 // Buffer b: A at lds + b * STAGE, B at + OPND.
 //
-// Per stage (two 16-deep MFMA steps, operand slots 0 and 1):
-//   phase A: MFMAs of step 0 (slot 0), with the reads of step 1 into slot 1
-//            placed between them;
-//   phase B: wait for the next stage's DMA and this wave's reads; barrier
-//            (all waves are done with this stage's buffer);
-//   phase C: MFMAs of step 1 (slot 1), with the reads of the next stage's
-//            step 0 into slot 0 and the DMA of stage +NSTAGE into the freed
-//            buffer placed between them.
-// The MFMA pipe is idle only across the barrier.  The order inside a phase is
-// pinned with scheduling fences.
+// A stage holds 64 reduction elements = four 16-deep MFMA steps; operand
+// fragments alternate between register slots 0 and 1 (step s uses slot s & 1).
+//   steps 0..2: the MFMAs of the step, with the reads of the next step of the
+//               same stage placed between them;
+//   then:       wait for the next stage's DMA and this wave's reads; barrier
+//               (every wave is done with this stage's buffer);
+//   step 3:     the MFMAs, with the DMA of stage +2 into the freed buffer and
+//               the reads of the next stage's step 0 placed between them.
+// So a stage's DMA has one whole stage of MFMAs to land, and the MFMA pipe is
+// idle only across the barrier.  The order inside a step is pinned with
+// scheduling fences.
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
 template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op>
 MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
                            int live_mi, f32x16 (&acc)[MI][NI]) {
   constexpr int D = Op::DMA_PER_STAGE;
-  constexpr int NM = MI * NI;                         // MFMAs per step
+  constexpr int NM = MI * NI;                           // MFMAs per step
   constexpr int NR = MI + NI + (Op::A_SCALED ? 1 : 0);  // read items per step
-  constexpr int NS = Op::A_SCALED ? MI : 0;           // scale items per step
+  constexpr int NS = Op::A_SCALED ? MI : 0;             // scale items per step
   constexpr int NP = Op::PREFETCH ? 1 : 0;
-  constexpr int SLOTS = NM - NS;                      // slots for reads / DMA
+  constexpr int SLOTS = NM - NS;                        // MFMA slots for reads / DMA
   static_assert(SLOTS > 0, "tile too small");
+  static_assert(KS == 4 && NSTAGE == 2, "pipeline written for 4 steps x 2 stages");
   bf16x8_t fa[2][MI], fb[2][NI];
   float sc[2][8];
 
+  // read item f, in order of first use by the next step's MFMAs (mi outer,
+  // ni inner): [scale factors], A0, B0 .. B(NI-1), A1 .. A(MI-1)
   auto read_item = [&](int buf, int step, int slot, int f) __attribute__((always_inline)) {
     const char *As = lds + buf * STAGE;
     const char *Bs = As + OPND;
@@ -270,14 +278,14 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
       return;
     }
     const int g = f - (Op::A_SCALED ? 1 : 0);
-    if (g < MI) {
-      const int mi = g;
+    if (g == 0 || g > NI) {
+      const int mi = g == 0 ? 0 : g - NI;
       if (Op::A_KMAJ)
         fa[slot][mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
       else
         fa[slot][mi] = frag_mnmaj(As, wm * 32 + mi * 32 * WGM, step, lane);
     } else {
-      const int ni = g - MI;
+      const int ni = g - 1;
       if (Op::B_KMAJ)
         fb[slot][ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
       else
@@ -290,41 +298,45 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
                                                           acc[mi][ni], 0, 0, 0);
   };
-  // phase A of the stage in buffer `buf`; with PF: prefetch for stage pf
-  auto phase_a = [&](int buf, int pf, auto PF) __attribute__((always_inline)) {
+  // step `step` (< KS-1) of the stage in `buf`: MFMAs on slot step&1, reads of
+  // step+1 into the other slot; with PF, the prefetch for stage pf
+  auto step_inner = [&](int buf, int step, int pf, auto PF) __attribute__((always_inline)) {
+    const int slot = step & 1, nslot = slot ^ 1;
     constexpr int NIT = NR + NP;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
-      mfma(0, i);
+      mfma(slot, i);
       MOE_FENCE();
+      // reads spread evenly over the step (bunching them saturates the LDS),
+      // in first-use order so each has >= 10 MFMAs to land; then the prefetch
 #pragma unroll
       for (int j = 0; j < NIT; ++j) {
         if (j * SLOTS / NIT != i) continue;
         if (j < NR)
-          read_item(buf, 1, 1, j);
+          read_item(buf, step + 1, nslot, j);
         else if (decltype(PF)::value)
           op.prefetch(pf);
       }
-      if (NS > 0 && i >= NM - NS) fa[1][i - (NM - NS)] = scale_frag(fa[1][i - (NM - NS)], sc[1]);
+      if (NS > 0 && i >= NM - NS)
+        fa[nslot][i - (NM - NS)] = scale_frag(fa[nslot][i - (NM - NS)], sc[nslot]);
       MOE_FENCE();
     }
   };
-  // phase C: step 1 of the stage in `buf`, step-0 reads of `nbuf`; with DMA:
-  // issue stage `dma` into `buf`
-  auto phase_c = [&](int buf, int nbuf, int dma, auto DMA) __attribute__((always_inline)) {
-    constexpr int NIT = NR + D;
+  // last step of the stage in `buf` (slot 1): reads of step 0 of `nbuf` into
+  // slot 0; with DMA, stage `dma` is issued into `buf`
+  auto step_last = [&](int buf, int nbuf, int dma, auto DMA) __attribute__((always_inline)) {
+    constexpr int DD = decltype(DMA)::value ? D : 0;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma(1, i);
       MOE_FENCE();
+      // reads and DMA parts each spread evenly over the step
 #pragma unroll
-      for (int j = 0; j < NIT; ++j) {
-        if (j * SLOTS / NIT != i) continue;
-        if (j < NR)
-          read_item(nbuf, 0, 0, j);
-        else if (decltype(DMA)::value)
-          op.issue_part(dma, buf, j - NR);
-      }
+      for (int j = 0; j < NR; ++j)
+        if (j * SLOTS / NR == i) read_item(nbuf, 0, 0, j);
+#pragma unroll
+      for (int j = 0; j < DD; ++j)
+        if (j * SLOTS / DD == i) op.issue_part(dma, buf, j);
       if (NS > 0 && i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
       MOE_FENCE();
     }
@@ -335,16 +347,21 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
     __builtin_amdgcn_s_barrier();
     MOE_FENCE();
   };
-
-  // prologue: up to NSTAGE stages in flight; wait for the first
-  const int n = ke - kb;
-  const int pre = n < NSTAGE ? n : NSTAGE;
-  for (int s = 0; s < pre; ++s) {
-    if (Op::PREFETCH) op.prefetch(kb + s);
+  auto issue_stage = [&](int kt, int buf) __attribute__((always_inline)) {
+    if (Op::PREFETCH) op.prefetch(kt);
 #pragma unroll
-    for (int j = 0; j < D; ++j) op.issue_part(kb + s, s, j);
+    for (int j = 0; j < D; ++j) op.issue_part(kt, buf, j);
+  };
+
+  // prologue: the first two stages in flight; wait for the first
+  const int n = ke - kb;
+  issue_stage(kb, 0);
+  if (n > 1) {
+    issue_stage(kb + 1, 1);
+    wait_vmcnt<D>();
+  } else {
+    wait_vmcnt<0>();
   }
-  wait_stages<D>(pre - 1 > 2 ? 3 : pre - 1);
   sync();
 #pragma unroll
   for (int j = 0; j < NR; ++j) read_item(0, 0, 0, j);
@@ -355,44 +372,52 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   MOE_FENCE();
 
   int kt = kb;
-  // stages whose buffer is refilled with stage kt + NSTAGE
-  for (; kt + NSTAGE < ke; ++kt) {
-    const int buf = (kt - kb) & (NSTAGE - 1);
-    phase_a(buf, kt + NSTAGE, std::integral_constant<bool, Op::PREFETCH>());
-    wait_vmcnt<2 * D>();  // stage kt+1 landed (kt+2, kt+3 may be in flight)
+  // stages whose buffer is refilled with stage kt + 2
+  for (; kt + 2 < ke; ++kt) {
+    const int buf = (kt - kb) & 1;
+    step_inner(buf, 0, kt + 2, std::integral_constant<bool, Op::PREFETCH>());
+    step_inner(buf, 1, 0, std::false_type());
+    step_inner(buf, 2, 0, std::false_type());
+    wait_vmcnt<0>();  // stage kt+1 landed
     sync();
-    phase_c(buf, (buf + 1) & (NSTAGE - 1), kt + NSTAGE, std::true_type());
+    step_last(buf, buf ^ 1, kt + 2, std::true_type());
   }
-  // the last stages: nothing more to issue
-  for (; kt + 1 < ke; ++kt) {
-    const int buf = (kt - kb) & (NSTAGE - 1);
-    phase_a(buf, 0, std::false_type());
-    wait_stages<D>(min(2, ke - kt - 2));
+  // the stage before the last: nothing more to issue
+  if (kt + 1 < ke) {
+    const int buf = (kt - kb) & 1;
+    step_inner(buf, 0, 0, std::false_type());
+    step_inner(buf, 1, 0, std::false_type());
+    step_inner(buf, 2, 0, std::false_type());
+    wait_vmcnt<0>();
     sync();
-    phase_c(buf, (buf + 1) & (NSTAGE - 1), 0, std::false_type());
+    step_last(buf, buf ^ 1, 0, std::false_type());
+    ++kt;
   }
   // final stage
   {
-    const int buf = (kt - kb) & (NSTAGE - 1);
-    phase_a(buf, 0, std::false_type());
+    const int buf = (kt - kb) & 1;
+    step_inner(buf, 0, 0, std::false_type());
+    step_inner(buf, 1, 0, std::false_type());
+    step_inner(buf, 2, 0, std::false_type());
 #pragma unroll
     for (int i = 0; i < NM; ++i) mfma(1, i);
     MOE_FENCE();
   }
 }
 
-// K-major DMA of a tile of R rows x 32 reduction elements: thread (wave w, lane
-// p), instruction i loads row (w * R/64 + i) * 16 + p/4, physical chunk p % 4.
+// K-major DMA of a tile of R rows x 64 reduction elements (128 bytes per row):
+// one instruction fills 8 rows (1 KB of LDS).  Thread (wave w, lane p),
+// instruction i loads row (w * R/32 + i) * 8 + p/8, physical chunk p % 8.
 template <int R>
 struct KmajDma {
-  static constexpr int PER_WAVE = R / 64;
+  static constexpr int PER_WAVE = R / 32;
   uint32_t base[PER_WAVE];  // per-lane global byte offset of the row chunk, stage 0
   int chunk[PER_WAVE];      // logical chunk (reduction elements 8*chunk .. +7)
   MOE_DEV void setup(int wid, int lane, const int *rowoff /* byte offset of tile row or -1 */) {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
-      const int row = (wid * PER_WAVE + i) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+      const int row = (wid * PER_WAVE + i) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
       chunk[i] = c;
       const int ro = rowoff[row];
       base[i] = ro >= 0 ? (uint32_t)ro + (uint32_t)c * 16u : kOobOffset;
@@ -407,13 +432,16 @@ struct KmajDma {
   }
 };
 
-// MN-major DMA of a 32 x 256 tile: thread (wave w, lane p), instruction i loads
-// reduction row 2 * (w * 4 + i) + p/32, physical chunk p % 32.
+// MN-major DMA of a 64 x 256 tile (512 bytes per reduction row): one instruction
+// fills 2 rows.  Thread (wave w, lane p), instruction i loads reduction row
+// 2 * (w * 8 + i) + p/32, physical chunk p % 32.
 struct MnmajMap {
-  MOE_DEV static int row_of(int wid, int i, int lane) { return 2 * (wid * 4 + i) + (lane >> 5); }
+  static constexpr int PER_WAVE = 8;
+  MOE_DEV static int row_of(int wid, int i, int lane) { return 2 * (wid * PER_WAVE + i) + (lane >> 5); }
   MOE_DEV static int chunk_of(int wid, int i, int lane) {
     return (lane & 31) ^ ((row_of(wid, i, lane) & 3) << 2);
   }
+  MOE_DEV static uint32_t lds_of(int wid, int i) { return (uint32_t)((wid * PER_WAVE + i) * 1024); }
 };
 
 // ============================================================================
@@ -441,7 +469,7 @@ struct FwdArgs {
 template <int BM, int BN>
 struct FwdOp {
   static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false, PREFETCH = false;
-  static constexpr int DMA_PER_STAGE = BM / 64 + BN / 64;
+  static constexpr int DMA_PER_STAGE = BM / 32 + BN / 32;
   KmajDma<BM> da;
   KmajDma<BN> db;
   __amdgpu_buffer_rsrc_t rsA, rsW;
@@ -449,10 +477,10 @@ struct FwdOp {
   int K, wid;
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < BM / 64)
+    if (j < BM / 32)
       da.issue_one(rsA, kt, K, t, wid, j);
     else
-      db.issue_one(rsW, kt, K, t + OPND, wid, j - BM / 64);
+      db.issue_one(rsW, kt, K, t + OPND, wid, j - BM / 32);
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
@@ -585,29 +613,29 @@ struct DxArgs {
 
 struct DxOp {
   static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false, PREFETCH = false;
-  static constexpr int DMA_PER_STAGE = 4 + 4;
+  static constexpr int DMA_PER_STAGE = 8 + 8;
   KmajDma<256> da;
-  uint32_t bcol[4];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
+  uint32_t bcol[8];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0, rowbytes_w;
   int N, wid, lane;
   MOE_DEV void setup_b(int kc0, int K) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int col = kc0 + 8 * MnmajMap::chunk_of(wid, i, lane);
       bcol[i] = col < K ? (uint32_t)col * 2u : kOobOffset;
     }
   }
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < 4) {
+    if (j < 8) {
       da.issue_one(rsA, kt, N, t, wid, j);
     } else {
-      const int i = j - 4;
+      const int i = j - 8;
       const int n = kt * BK + MnmajMap::row_of(wid, i, lane);
       const uint32_t off = (n < N && bcol[i] != kOobOffset) ? (uint32_t)n * rowbytes_w + bcol[i]
                                                             : kOobOffset;
-      dma16(rsW, off, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
+      dma16(rsW, off, t + OPND + MnmajMap::lds_of(wid, i));
     }
   }
   MOE_DEV void prefetch(int) {}
@@ -673,29 +701,33 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
 
     tile_multiply<MI, NI, WGM, WGN, false>(op, lds, kb, ke, wm, wn, lane, MI, acc);
 
-    // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: eight
-    // 32-column K-major sub-tiles into the (now idle) LDS stages
+    // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: four
+    // 64-column K-major sub-tiles into the (now idle) LDS stages
     if (p.d_w) {
       barrier();
       const uint32_t l0 = lds_addr(lds);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = (wid * 4 + i) * 16 + (lane >> 2);
-          const int cch = (lane & 3) ^ ((row >> 2) & 3);
+        for (int i = 0; i < 8; ++i) {
+          const int row = (wid * 8 + i) * 8 + (lane >> 3);
+          const int cch = (lane & 7) ^ ((row >> 1) & 7);
           const int t = tok[row];
-          const int col = kc0 + q * 32 + cch * 8;
+          const int col = kc0 + q * 64 + cch * 8;
           const uint32_t off =
               (t >= 0 && col < K) ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u : kOobOffset;
-          dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * 4 + i) * 1024));
+          dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * 8 + i) * 1024));
         }
       }
       wait_vmcnt<0>();
       barrier();
     }
     // epilogue: weighted atomic scatter of G into dX and, per row, the partial
-    // inner product of G with x over this tile's columns into d_w
+    // inner product of G with x over this tile's columns into d_w.  Register
+    // 4j+q of accumulator (mi, ni) holds row rq + q, column cl(ni) of G, with
+    // rq = wm*32 + mi*64 + 8j + 4*(lane/32); one transposing read of the K-major
+    // x tile gives each lane exactly x at rows rq .. rq+3 of its column.
+    const bool has_dw = p.d_w != nullptr, has_dx = p.dX != nullptr;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
@@ -704,32 +736,45 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
         const i32x4 t4 = *(const i32x4 *)(tok + rq);
         const f32x4 w4 = *(const f32x4 *)(wgt + rq);
         const i32x4 a4 = *(const i32x4 *)(asg + rq);
+        i16x4 xq[NI];
+        if (has_dw) {
+          const int jl = lane & 15;
+          const int row = rq + (jl >> 2);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = t4[q];
-          const int rl = rq + q;
-          float part = 0.f;
-          if (t >= 0) {
-            const size_t rowo = (size_t)t * K;
+          for (int ni = 0; ni < NI; ++ni) {
+            const int cs = wn * 32 + ni * 32 * WGN + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
+            const char *a = lds + (cs >> 6) * OPND + kmaj_off(row, (cs >> 3) & 7) + (cs & 7) * 2;
+            xq[ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS i16x4 *)(LDS_AS char *)a);
+          }
+        }
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-              const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
-              const int col = kc0 + cl;
-              if (col >= K) continue;
-              const float g = acc[mi][ni][4 * j + q];
-              if (p.dX) unsafeAtomicAdd(p.dX + rowo + col, w4[q] * g);
-              if (p.d_w) {
-                const __bf16 xv = *(const __bf16 *)(lds + (cl >> 5) * OPND +
-                                                    kmaj_off(rl, (cl >> 3) & 3) + (cl & 7) * 2);
-                part = fmaf(g, (float)xv, part);
-              }
+        for (int ni = 0; ni < NI; ++ni) {
+          const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
+          const int col = kc0 + cl;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float g = acc[mi][ni][4 * j + q];
+            if (has_dx && t4[q] >= 0 && col < K)
+              unsafeAtomicAdd(p.dX + (size_t)t4[q] * K + col, w4[q] * g);
+            if (has_dw) {
+              const float xv = __builtin_bit_cast(float, (uint32_t)(uint16_t)xq[ni][q] << 16);
+              part[q] = fmaf(g, xv, part[q]);  // masked rows / columns hold zeros
             }
           }
-          if (p.d_w) {
-            // lanes 0-31 hold one row, lanes 32-63 another
+        }
+        if (has_dw) {
+          // sum each row over the 32 lanes of its half-wave
 #pragma unroll
-            for (int d = 16; d >= 1; d >>= 1) part += __shfl_xor(part, d, 32);
-            if ((lane & 31) == 0 && t >= 0) unsafeAtomicAdd(p.d_w + a4[q], part);
+          for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int d = 16; d >= 1; d >>= 1) part[q] += __shfl_xor(part[q], d, 32);
+          }
+          if ((lane & 31) == 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (t4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], part[q]);
           }
         }
       }
@@ -769,67 +814,70 @@ struct DwArgs {
 
 struct DwOp {
   static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
-  // per stage: 4 dY + 4 x chunks, the stage's routing weights, the tokens of
-  // the stage NSTAGE ahead
-  static constexpr int DMA_PER_STAGE = 4 + 4 + 1 + 1;
+  // per stage: 8 dY + 8 x instructions, the stage's routing weights, the
+  // tokens of the stage two ahead
+  static constexpr int DMA_PER_STAGE = 8 + 8 + 1 + 1;
   __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
   uint32_t lds0;
   const char *lds;
   int r0, m, wid, lane, K, N, weighted;
-  uint32_t ncol[4], kcol[4];  // byte offsets of this lane's column chunk (dY / x), or OOB
+  uint32_t ncol[8], kcol[8];  // byte offsets of this lane's column chunk (dY / x), or OOB
+  i32x4 tq[4];                // tokens of this wave's 16 rows of the stage being issued
 
   MOE_DEV void setup(int n0, int kc0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int ch = MnmajMap::chunk_of(wid, i, lane);
       ncol[i] = n0 + 8 * ch < N ? (uint32_t)(n0 + 8 * ch) * 2u : kOobOffset;
       kcol[i] = kc0 + 8 * ch < K ? (uint32_t)(kc0 + 8 * ch) * 2u : kOobOffset;
     }
   }
-  MOE_DEV int ring_off(int kt) const { return TOKREGION + (kt & 7) * TOKSLOT + wid * 256; }
+  MOE_DEV int ring_off(int kt) const {
+    return TOKREGION + (kt & (TOKSLOTS - 1)) * TOKSLOT + wid * 256;
+  }
   // Tokens of stages kt0 .. kt0+n-1 into the ring, synchronously (no DMA in flight).
   MOE_DEV void fill_ring(const int32_t *r2t, int kt0, int n) {
     for (int s = 0; s < n; ++s) {
       const int q = (kt0 + s) * BK + lane;
-      if (lane < 32) *(int *)(lds + ring_off(kt0 + s) + lane * 4) = q < m ? r2t[r0 + q] : -1;
+      *(int *)(lds + ring_off(kt0 + s) + lane * 4) = q < m ? r2t[r0 + q] : -1;
     }
   }
-  i32x4 ta, tb;  // tokens of this wave's 8 rows of the stage being issued
-  // tokens of this wave's rows 8*wid .. +7 of stage kt (ring copy of this wave)
+  // tokens of this wave's rows 16*wid .. +15 of stage kt (ring copy of this wave)
   MOE_DEV void prefetch(int kt) {
-    ta = *(const i32x4 *)(lds + ring_off(kt) + wid * 32);
-    tb = *(const i32x4 *)(lds + ring_off(kt) + wid * 32 + 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tq[i] = *(const i32x4 *)(lds + ring_off(kt) + wid * 64 + 16 * i);
   }
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < 8) {
-      const int i = j & 3;
-      const int rl = 2 * i + (lane >> 5);  // row within the wave's 8
-      const int q = kt * BK + 8 * wid + rl;
-      int tok = i < 2 ? ta[rl & 3] : tb[rl & 3];
+    if (j < 16) {
+      const int i = j & 7;
+      const int rl = 2 * i + (lane >> 5);  // row within the wave's 16
+      const int q = kt * BK + 16 * wid + rl;
+      const int te = tq[i >> 1][(2 * i) & 3], to = tq[i >> 1][(2 * i + 1) & 3];
+      int tok = (lane >> 5) ? to : te;
       if (q >= m) tok = -1;
-      if (j < 4) {
+      if (j < 8) {
         const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
                                   ? (uint32_t)tok * (uint32_t)N * 2u + ncol[i]
                                   : kOobOffset;
-        dma16(rsY, offy, t + (uint32_t)((wid * 4 + i) * 1024));
+        dma16(rsY, offy, t + MnmajMap::lds_of(wid, i));
       } else {
         const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
                                   ? (uint32_t)tok * (uint32_t)K * 2u + kcol[i]
                                   : kOobOffset;
-        dma16(rsX, offx, t + OPND + (uint32_t)((wid * 4 + i) * 1024));
+        dma16(rsX, offx, t + OPND + MnmajMap::lds_of(wid, i));
       }
-    } else if (j == 8) {
-      // routing weights of the stage's 32 rows into this wave's strip
+    } else if (j == 16) {
+      // routing weights of the stage's 64 rows into this wave's strip
       const int qw = kt * BK + lane;
-      const uint32_t offw = (lane < 32 && qw < m) ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
+      const uint32_t offw = qw < m ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
       dma4(rsW, offw, lds0 + (uint32_t)(WREGION + buf * WBYTES + wid * 256));
     } else {
-      // tokens of stage kt + NSTAGE into the ring (read by its prefetch after
-      // this stage has been waited for)
-      const int qt = (kt + NSTAGE) * BK + lane;
-      const uint32_t offt = (lane < 32 && qt < m) ? (uint32_t)(r0 + qt) * 4u : kOobOffset;
-      dma4(rsT, offt, lds0 + (uint32_t)ring_off(kt + NSTAGE));
+      // tokens of stage kt + 2 into the ring (read by its prefetch after this
+      // stage has been waited for)
+      const int qt = (kt + 2) * BK + lane;
+      const uint32_t offt = qt < m ? (uint32_t)(r0 + qt) * 4u : kOobOffset;
+      dma4(rsT, offt, lds0 + (uint32_t)ring_off(kt + 2));
     }
   }
   // factors of the 8 reduction rows this lane holds in step `step`
@@ -892,7 +940,7 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
       for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
     if (KI > 0) {
       __syncthreads();  // previous unit done with LDS
-      op.fill_ring(p.row_to_token, 0, KI < NSTAGE ? KI : NSTAGE);
+      op.fill_ring(p.row_to_token, 0, KI < 2 ? KI : 2);
       tile_multiply<MI, NI, WGM, WGN, false>(op, lds, 0, KI, wm, wn, lane, MI, acc);
     }
     // store (exact zeros for an empty expert)
@@ -918,9 +966,9 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   }
 }
 
-// dynamic LDS: NSTAGE stages of (A 16 KB, B 16 KB), the weight strips and the
-// 8-slot token ring
-constexpr size_t kStageLds = (size_t)TOKREGION + 8 * (size_t)TOKSLOT;
+// dynamic LDS: NSTAGE stages of (A 32 KB, B 32 KB), the weight strips and the
+// token ring
+constexpr size_t kStageLds = (size_t)TOKREGION + TOKSLOTS * (size_t)TOKSLOT;
 
 template <typename K>
 hipError_t set_smem(K kernel, size_t bytes) {
