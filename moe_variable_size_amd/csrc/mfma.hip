@@ -152,20 +152,42 @@ MOE_DEV int logical_block() {
   return (G & 7) ? b : (b & 7) * (G >> 3) + (b >> 3);
 }
 
-// Work split of `total` tiles of KI stages over G workgroups: whole tiles in
-// waves of G, the remaining tiles' stages split evenly.  Workgroup Lb walks
-// [it, it_end) of the flat (tile, stage) space, jumping by whole tiles in the
-// first phase.
+// Work split of `total` tiles of KI stages over G workgroups.  Whole tiles go
+// out in rounds of G (workgroup Lb takes tiles Lb, Lb + G, ...).  The tiles of
+// the last partial round are then either
+//   * cut into S sub-tiles each (S = 2..16, rows and columns split, at most
+//     one sub-tile per workgroup), so no workgroup idles for a whole tile time
+//     and every output element is still produced by exactly one workgroup; or
+//   * (stream_k) split along the reduction over all G workgroups.
 struct WorkSplit {
   int64_t it, it_end, tail0, tot;
-  int KI, G;
-  MOE_DEV void init(int total, int KI_, int G_, int Lb, bool sk) {
+  int KI, G, Lb;
+  bool sk;
+  int next_tile, full, pieces, S;
+  bool piece_done;
+  int s, nS;  // sub-tile of the current piece (0 of 1 for a whole tile)
+  enum { WHOLE = 0, SUBTILE_TAIL = 1, STREAM_K = 2 };
+  MOE_DEV void init(int total, int KI_, int G_, int Lb_, int mode) {
     KI = KI_;
     G = G_;
+    Lb = Lb_;
+    sk = mode == STREAM_K;
+    s = 0;
+    nS = 1;
+    if (!sk) {
+      full = (total / G) * G;
+      const int rem = total - full;
+      S = 1;
+      if (mode == SUBTILE_TAIL && rem > 0) S = rem * 8 <= G ? 8 : (rem * 4 <= G ? 4 : 1);
+      pieces = rem * S;
+      next_tile = Lb;
+      piece_done = false;
+      return;
+    }
     tot = (int64_t)total * KI;
-    const int full = sk ? (total / G) * G : total;
-    tail0 = (int64_t)full * KI;
-    if (Lb < full) {
+    const int fullr = (total / G) * G;
+    tail0 = (int64_t)fullr * KI;
+    if (Lb < fullr) {
       it = (int64_t)Lb * KI;
       it_end = it + KI;
     } else {
@@ -173,8 +195,25 @@ struct WorkSplit {
       it_end = tail0 + (tot - tail0) * (Lb + 1) / G;
     }
   }
-  // next piece (tile, kb, ke); false when done
-  MOE_DEV bool next(int &tau, int &kb, int &ke, int Lb) {
+  // next piece (tile, kb, ke; sub-tile s of nS); false when done
+  MOE_DEV bool next(int &tau, int &kb, int &ke) {
+    if (!sk) {
+      kb = 0;
+      ke = KI;
+      if (next_tile < full) {
+        tau = next_tile;
+        next_tile += G;
+        s = 0;
+        nS = 1;
+        return true;
+      }
+      if (piece_done || Lb >= pieces) return false;
+      piece_done = true;
+      tau = full + Lb / S;
+      s = Lb % S;
+      nS = S;
+      return true;
+    }
     while (it >= it_end) {
       if (it_end <= tail0 && it_end + (int64_t)(G - 1) * KI < tail0) {
         it = it_end + (int64_t)(G - 1) * KI;  // next whole tile of this workgroup
@@ -194,6 +233,15 @@ struct WorkSplit {
     return true;
   }
 };
+
+// Sub-tile s of nS (4: 128 x 128, 8: 64 x 128) of a 256 x 256 tile.
+struct SubTile {
+  int r0, c0, rows, cols;  // offsets inside the tile and extents
+};
+MOE_DEV SubTile sub_tile(int s, int nS) {
+  const int rows = nS == 8 ? 64 : 128, cols = 128;
+  return SubTile{(s >> 1) * rows, (s & 1) * cols, rows, cols};
+}
 
 // ---- MFMA operand fragments ----------------------------------------------------
 // Lane l of a 32x32x16 MFMA holds, for operand row/column (l & 31), the 8
@@ -239,7 +287,8 @@ MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 
 //   static constexpr bool PREFETCH        prefetch(kt) must run (LDS reads)
 //       before the parts of stage kt are issued
 //   static constexpr int DMA_PER_STAGE    DMA instructions per thread per stage
-//   void issue_part(int kt, int buf, int j)  j-th DMA instruction of stage kt
+//   template <bool SKIP> void issue_part(int kt, int buf, int j)
+//       j-th DMA instruction of stage kt (SKIP: may be left out for dead rows)
 // Buffer b: A at lds + b * STAGE, B at + OPND.
 //
 // A stage holds 64 reduction elements = four 16-deep MFMA steps; operand
@@ -254,9 +303,12 @@ MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 
 // idle only across the barrier.  The order inside a step is pinned with
 // scheduling fences.
 #define MOE_FENCE() __builtin_amdgcn_sched_barrier(0)
-template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op>
+// SKIP: wave-uniform live_mi / live_ni bound the row / column blocks this wave
+// multiplies, and the Op may leave out DMA instructions of dead rows.
+// DSKIP: the Op leaves out DMA instructions whose rows are all dead.
+template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op, bool DSKIP = SKIP>
 MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
-                           int live_mi, f32x16 (&acc)[MI][NI]) {
+                           int live_mi, int live_ni, f32x16 (&acc)[MI][NI]) {
   constexpr int D = Op::DMA_PER_STAGE;
   constexpr int NM = MI * NI;                           // MFMAs per step
   constexpr int NR = MI + NI + (Op::A_SCALED ? 1 : 0);  // read items per step
@@ -294,7 +346,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   };
   auto mfma = [&](int slot, int i) __attribute__((always_inline)) {
     const int mi = i / NI, ni = i % NI;
-    if (SKIP && mi >= live_mi) return;  // wave-uniform: rows past the group end
+    if (SKIP && (mi >= live_mi || ni >= live_ni)) return;  // wave-uniform
     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
                                                           acc[mi][ni], 0, 0, 0);
   };
@@ -336,7 +388,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
         if (j * SLOTS / NR == i) read_item(nbuf, 0, 0, j);
 #pragma unroll
       for (int j = 0; j < DD; ++j)
-        if (j * SLOTS / DD == i) op.issue_part(dma, buf, j);
+        if (j * SLOTS / DD == i) op.template issue_part<DSKIP>(dma, buf, j);
       if (NS > 0 && i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
       MOE_FENCE();
     }
@@ -350,7 +402,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   auto issue_stage = [&](int kt, int buf) __attribute__((always_inline)) {
     if (Op::PREFETCH) op.prefetch(kt);
 #pragma unroll
-    for (int j = 0; j < D; ++j) op.issue_part(kt, buf, j);
+    for (int j = 0; j < D; ++j) op.template issue_part<DSKIP>(kt, buf, j);
   };
 
   // prologue: the first two stages in flight; wait for the first
@@ -358,7 +410,10 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   issue_stage(kb, 0);
   if (n > 1) {
     issue_stage(kb + 1, 1);
-    wait_vmcnt<D>();
+    if (DSKIP)
+      wait_vmcnt<0>();  // the instruction count of a stage varies
+    else
+      wait_vmcnt<D>();
   } else {
     wait_vmcnt<0>();
   }
@@ -413,7 +468,10 @@ struct KmajDma {
   static constexpr int PER_WAVE = R / 32;
   uint32_t base[PER_WAVE];  // per-lane global byte offset of the row chunk, stage 0
   int chunk[PER_WAVE];      // logical chunk (reduction elements 8*chunk .. +7)
-  MOE_DEV void setup(int wid, int lane, const int *rowoff /* byte offset of tile row or -1 */) {
+  int live_rows;            // rows at or past this are never read (wave-uniform)
+  MOE_DEV void setup(int wid, int lane, const int *rowoff /* byte offset of tile row or -1 */,
+                     int live = R) {
+    live_rows = live;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int row = (wid * PER_WAVE + i) * 8 + (lane >> 3);
@@ -423,9 +481,12 @@ struct KmajDma {
       base[i] = ro >= 0 ? (uint32_t)ro + (uint32_t)c * 16u : kOobOffset;
     }
   }
-  // instruction i of stage kt
+  // instruction i of stage kt (SKIP: left out when all its rows are dead; the
+  // LDS rows then keep stale values, which only reach dead accumulator rows)
+  template <bool SKIP>
   MOE_DEV void issue_one(__amdgpu_buffer_rsrc_t rs, int kt, int kred, uint32_t lds_tile, int wid,
                          int i) {
+    if (SKIP && (wid * PER_WAVE + i) * 8 >= live_rows) return;
     const bool in = kt * BK + chunk[i] * 8 < kred;
     const uint32_t off = in ? base[i] + (uint32_t)kt * KROW : kOobOffset;
     dma16(rs, off, lds_tile + (uint32_t)((wid * PER_WAVE + i) * 1024));
@@ -475,12 +536,13 @@ struct FwdOp {
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0;
   int K, wid;
+  template <bool SKIP>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < BM / 32)
-      da.issue_one(rsA, kt, K, t, wid, j);
+      da.template issue_one<SKIP>(rsA, kt, K, t, wid, j);
     else
-      db.issue_one(rsW, kt, K, t + OPND, wid, j - BM / 32);
+      db.template issue_one<SKIP>(rsW, kt, K, t + OPND, wid, j - BM / 32);
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
@@ -519,12 +581,20 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
 
   const int Lb = logical_block();
   WorkSplit ws;
-  ws.init(total, KI, gridDim.x, Lb, p.stream_k != 0);
+  ws.init(total, KI, gridDim.x, Lb,
+          p.stream_k ? WorkSplit::STREAM_K : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE));
   int tau, kb, ke;
-  while (ws.next(tau, kb, ke, Lb)) {
-    const TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
-    if (c.rows <= 0) continue;
-    const int n0 = c.nb * BN;
+  while (ws.next(tau, kb, ke)) {
+    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
+    int n0 = c.nb * BN, ncols = min(BN, N - n0);
+    if (ws.nS > 1) {  // a sub-tile of a tile of the last round
+      const SubTile st = sub_tile(ws.s, ws.nS);
+      c.row0 += st.r0;
+      c.rows = min(st.rows, c.rows - st.r0);
+      n0 += st.c0;
+      ncols = min(st.cols, N - n0);
+    }
+    if (c.rows <= 0 || ncols <= 0) continue;
     __syncthreads();  // LDS stages and row tables free
     if (tid < BM) {
       const bool ok = tid < c.rows;
@@ -534,51 +604,76 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
       wgt[tid] = (FUSED && ok) ? p.row_weight[r] : 0.f;
       rowoff_a[tid] = t >= 0 ? t * K * 2 : -1;
     }
-    for (int j = tid; j < BN; j += NT) rowoff_b[j] = n0 + j < N ? (n0 + j) * K * 2 : -1;
+    for (int j = tid; j < BN; j += NT) rowoff_b[j] = j < ncols ? (n0 + j) * K * 2 : -1;
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
-    op.da.setup(wid, lane, rowoff_a);
-    op.db.setup(wid, lane, rowoff_b);
-    const int live_mi = min(MI, max(0, (c.rows - wm * 32 + 32 * WGM - 1) / (32 * WGM)));
-    f32x16 acc[MI][NI];
+    const bool part = BM <= 64 || ws.nS > 1;  // rows / columns partly dead
+    op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
+    op.db.setup(wid, lane, rowoff_b, part ? ncols : BN);
+    // The tile body, instantiated per accumulator shape: MIc x NIc blocks per
+    // wave (a whole tile, or a 128 x 128 / 64 x 128 sub-tile), each with its own
+    // accumulators.  SKM: MFMAs of row blocks past the last live row are left
+    // out (wave-uniform, masked decode); DSK: DMA of dead rows is left out.
+    auto tile = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_) __attribute__((always_inline)) {
+      constexpr int MIc = decltype(MIc_)::value, NIc = decltype(NIc_)::value;
+      constexpr bool SKM = decltype(SKM_)::value, DSK = decltype(DSK_)::value;
+      const int live_mi =
+          SKM ? min(MIc, max(0, (c.rows - wm * 32 + 32 * WGM - 1) / (32 * WGM))) : MIc;
+      f32x16 acc[MIc][NIc];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MIc; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
+        for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
+      tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN>, DSK>(op, lds, kb, ke, wm, wn, lane,
+                                                                 live_mi, NIc, acc);
 
-    tile_multiply<MI, NI, WGM, WGN, (BM <= 64)>(op, lds, kb, ke, wm, wn, lane, live_mi, acc);
-
-    // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
-    // row tables; each row's base address is formed once for all column blocks
+      // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
+      // row tables; each row's base address is formed once for all column blocks
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      if (BM <= 64 && mi >= live_mi) continue;
+      for (int mi = 0; mi < MIc; ++mi) {
+        if (mi >= live_mi) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
-        const i32x4 t4 = *(const i32x4 *)(tok + rq);
-        const f32x4 w4 = *(const f32x4 *)(wgt + rq);
+        for (int j = 0; j < 4; ++j) {
+          const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
+          const i32x4 t4 = *(const i32x4 *)(tok + rq);
+          const f32x4 w4 = *(const f32x4 *)(wgt + rq);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int t = t4[q];
-          if (t < 0) continue;
-          const size_t rowo = (size_t)t * N;
+          for (int q = 0; q < 4; ++q) {
+            const int t = t4[q];
+            if (t < 0) continue;
+            const size_t rowo = (size_t)t * N;
 #pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            const int col = n0 + wn * 32 + ni * 32 * WGN + (lane & 31);
-            if (col >= N) continue;
-            const float v = acc[mi][ni][4 * j + q];
-            if (FUSED) {
-              unsafeAtomicAdd((float *)p.C + rowo + col, w4[q] * v);
-            } else if (sizeof(Tout) == 4) {
-              ((float *)p.C)[rowo + col] = v;
-            } else {
-              ((__bf16 *)p.C)[rowo + col] = (__bf16)v;
+            for (int ni = 0; ni < NIc; ++ni) {
+              const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);
+              if (cl >= ncols) continue;
+              const int col = n0 + cl;
+              const float v = acc[mi][ni][4 * j + q];
+              if (FUSED) {
+                unsafeAtomicAdd((float *)p.C + rowo + col, w4[q] * v);
+              } else if (sizeof(Tout) == 4) {
+                ((float *)p.C)[rowo + col] = v;
+              } else {
+                ((__bf16 *)p.C)[rowo + col] = (__bf16)v;
+              }
             }
           }
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    using std::integral_constant;
+    using std::false_type;
+    using std::true_type;
+    if constexpr (BM <= 64) {
+      tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(), true_type());
+    } else {
+      if (ws.nS == 8)
+        tile(integral_constant<int, 1>(), integral_constant<int, 2>(), false_type(), true_type());
+      else if (ws.nS == 4)
+        tile(integral_constant<int, 2>(), integral_constant<int, 2>(), false_type(), true_type());
+      else
+        tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
+             false_type());
     }
   }
 }
@@ -619,17 +714,19 @@ struct DxOp {
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0, rowbytes_w;
   int N, wid, lane;
-  MOE_DEV void setup_b(int kc0, int K) {
+  // columns kc0 .. kend-1 of W are loaded, the rest read as zeros
+  MOE_DEV void setup_b(int kc0, int kend) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int col = kc0 + 8 * MnmajMap::chunk_of(wid, i, lane);
-      bcol[i] = col < K ? (uint32_t)col * 2u : kOobOffset;
+      bcol[i] = col < kend ? (uint32_t)col * 2u : kOobOffset;
     }
   }
+  template <bool SKIP>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < 8) {
-      da.issue_one(rsA, kt, N, t, wid, j);
+      da.template issue_one<SKIP>(rsA, kt, N, t, wid, j);
     } else {
       const int i = j - 8;
       const int n = kt * BK + MnmajMap::row_of(wid, i, lane);
@@ -673,12 +770,19 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
 
   const int Lb = logical_block();
   WorkSplit ws;
-  ws.init(total, KI, gridDim.x, Lb, p.stream_k != 0);
+  ws.init(total, KI, gridDim.x, Lb, p.stream_k ? WorkSplit::STREAM_K : WorkSplit::SUBTILE_TAIL);
   int tau, kb, ke;
-  while (ws.next(tau, kb, ke, Lb)) {
-    const TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
-    if (c.rows <= 0) continue;
-    const int kc0 = c.nb * BN;
+  while (ws.next(tau, kb, ke)) {
+    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
+    int kc0 = c.nb * BN, ncols = min(BN, K - kc0);
+    if (ws.nS > 1) {  // a sub-tile of a tile of the last round
+      const SubTile st = sub_tile(ws.s, ws.nS);
+      c.row0 += st.r0;
+      c.rows = min(st.rows, c.rows - st.r0);
+      kc0 += st.c0;
+      ncols = min(st.cols, K - kc0);
+    }
+    if (c.rows <= 0 || ncols <= 0) continue;
     __syncthreads();
     if (tid < BM) {
       const bool ok = tid < c.rows;
@@ -691,95 +795,111 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
     }
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
-    op.da.setup(wid, lane, rowoff_a);
-    op.setup_b(kc0, K);
-    f32x16 acc[MI][NI];
+    const bool part = ws.nS > 1;  // rows / columns partly dead
+    op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
+    op.setup_b(kc0, kc0 + ncols);
+    // The tile body, instantiated per accumulator shape: MIc x NIc blocks per
+    // wave (a whole tile, or a 128 x 128 / 64 x 128 sub-tile), each with its own
+    // accumulators; DSK: DMA of dead rows is left out.
+    auto tile = [&](auto MIc_, auto NIc_, auto DSK_) __attribute__((always_inline)) {
+      constexpr int MIc = decltype(MIc_)::value, NIc = decltype(NIc_)::value;
+      constexpr bool DSK = decltype(DSK_)::value;
+      f32x16 acc[MIc][NIc];
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+      for (int mi = 0; mi < MIc; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x16{};
+        for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
+      tile_multiply<MIc, NIc, WGM, WGN, false, DxOp, DSK>(op, lds, kb, ke, wm, wn, lane, MIc, NIc,
+                                                          acc);
 
-    tile_multiply<MI, NI, WGM, WGN, false>(op, lds, kb, ke, wm, wn, lane, MI, acc);
-
-    // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: four
-    // 64-column K-major sub-tiles into the (now idle) LDS stages
-    if (p.d_w) {
-      barrier();
-      const uint32_t l0 = lds_addr(lds);
+      // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: four
+      // 64-column K-major sub-tiles into the (now idle) LDS stages
+      if (p.d_w) {
+        barrier();
+        const uint32_t l0 = lds_addr(lds);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int row = (wid * 8 + i) * 8 + (lane >> 3);
-          const int cch = (lane & 7) ^ ((row >> 1) & 7);
-          const int t = tok[row];
-          const int col = kc0 + q * 64 + cch * 8;
-          const uint32_t off =
-              (t >= 0 && col < K) ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u : kOobOffset;
-          dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * 8 + i) * 1024));
-        }
-      }
-      wait_vmcnt<0>();
-      barrier();
-    }
-    // epilogue: weighted atomic scatter of G into dX and, per row, the partial
-    // inner product of G with x over this tile's columns into d_w.  Register
-    // 4j+q of accumulator (mi, ni) holds row rq + q, column cl(ni) of G, with
-    // rq = wm*32 + mi*64 + 8j + 4*(lane/32); one transposing read of the K-major
-    // x tile gives each lane exactly x at rows rq .. rq+3 of its column.
-    const bool has_dw = p.d_w != nullptr, has_dx = p.dX != nullptr;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
-        const i32x4 t4 = *(const i32x4 *)(tok + rq);
-        const f32x4 w4 = *(const f32x4 *)(wgt + rq);
-        const i32x4 a4 = *(const i32x4 *)(asg + rq);
-        i16x4 xq[NI];
-        if (has_dw) {
-          const int jl = lane & 15;
-          const int row = rq + (jl >> 2);
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni) {
-            const int cs = wn * 32 + ni * 32 * WGN + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
-            const char *a = lds + (cs >> 6) * OPND + kmaj_off(row, (cs >> 3) & 7) + (cs & 7) * 2;
-            xq[ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (LDS_AS i16x4 *)(LDS_AS char *)a);
+          for (int i = 0; i < 8; ++i) {
+            const int row = (wid * 8 + i) * 8 + (lane >> 3);
+            const int cch = (lane & 7) ^ ((row >> 1) & 7);
+            const int t = tok[row];
+            const int col = kc0 + q * 64 + cch * 8;
+            const uint32_t off =
+                (t >= 0 && col < K) ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u : kOobOffset;
+            dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * 8 + i) * 1024));
           }
         }
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        wait_vmcnt<0>();
+        barrier();
+      }
+      // epilogue: weighted atomic scatter of G into dX and, per row, the partial
+      // inner product of G with x over this tile's columns into d_w.  Register
+      // 4j+q of accumulator (mi, ni) holds row rq + q, column cl(ni) of G, with
+      // rq = wm*32 + mi*64 + 8j + 4*(lane/32); one transposing read of the K-major
+      // x tile gives each lane exactly x at rows rq .. rq+3 of its column.
+      const bool has_dw = p.d_w != nullptr, has_dx = p.dX != nullptr;
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
-          const int col = kc0 + cl;
+      for (int mi = 0; mi < MIc; ++mi) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float g = acc[mi][ni][4 * j + q];
-            if (has_dx && t4[q] >= 0 && col < K)
-              unsafeAtomicAdd(p.dX + (size_t)t4[q] * K + col, w4[q] * g);
-            if (has_dw) {
-              const float xv = __builtin_bit_cast(float, (uint32_t)(uint16_t)xq[ni][q] << 16);
-              part[q] = fmaf(g, xv, part[q]);  // masked rows / columns hold zeros
+        for (int j = 0; j < 4; ++j) {
+          const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
+          const i32x4 t4 = *(const i32x4 *)(tok + rq);
+          const f32x4 w4 = *(const f32x4 *)(wgt + rq);
+          const i32x4 a4 = *(const i32x4 *)(asg + rq);
+          i16x4 xq[NIc];
+          if (has_dw) {
+            const int jl = lane & 15;
+            const int row = rq + (jl >> 2);
+#pragma unroll
+            for (int ni = 0; ni < NIc; ++ni) {
+              const int cs = wn * 32 + ni * 32 * WGN + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
+              const char *a = lds + (cs >> 6) * OPND + kmaj_off(row, (cs >> 3) & 7) + (cs & 7) * 2;
+              xq[ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (LDS_AS i16x4 *)(LDS_AS char *)a);
+            }
+          }
+          float dwp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ni = 0; ni < NIc; ++ni) {
+            const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
+            const int col = kc0 + cl;
+            const bool cok = cl < ncols;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float g = cok ? acc[mi][ni][4 * j + q] : 0.f;  // dead columns may hold stale values
+              if (has_dx && t4[q] >= 0 && cok)
+                unsafeAtomicAdd(p.dX + (size_t)t4[q] * K + col, w4[q] * g);
+              if (has_dw) {
+                const float xv = __builtin_bit_cast(float, (uint32_t)(uint16_t)xq[ni][q] << 16);
+                dwp[q] = fmaf(g, xv, dwp[q]);  // masked rows / columns hold zeros
+              }
+            }
+          }
+          if (has_dw) {
+            // sum each row over the 32 lanes of its half-wave
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+              for (int d = 16; d >= 1; d >>= 1) dwp[q] += __shfl_xor(dwp[q], d, 32);
+            }
+            if ((lane & 31) == 0) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                if (t4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], dwp[q]);
             }
           }
         }
-        if (has_dw) {
-          // sum each row over the 32 lanes of its half-wave
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int d = 16; d >= 1; d >>= 1) part[q] += __shfl_xor(part[q], d, 32);
-          }
-          if ((lane & 31) == 0) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (t4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], part[q]);
-          }
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    using std::integral_constant;
+    if (ws.nS == 8)
+      tile(integral_constant<int, 1>(), integral_constant<int, 2>(), std::true_type());
+    else if (ws.nS == 4)
+      tile(integral_constant<int, 2>(), integral_constant<int, 2>(), std::true_type());
+    else
+      tile(integral_constant<int, MI>(), integral_constant<int, NI>(), std::false_type());
   }
 }
 
@@ -847,6 +967,7 @@ struct DwOp {
 #pragma unroll
     for (int i = 0; i < 4; ++i) tq[i] = *(const i32x4 *)(lds + ring_off(kt) + wid * 64 + 16 * i);
   }
+  template <bool SKIP>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < 16) {
@@ -941,7 +1062,7 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
     if (KI > 0) {
       __syncthreads();  // previous unit done with LDS
       op.fill_ring(p.row_to_token, 0, KI < 2 ? KI : 2);
-      tile_multiply<MI, NI, WGM, WGN, false>(op, lds, 0, KI, wm, wn, lane, MI, acc);
+      tile_multiply<MI, NI, WGM, WGN, false>(op, lds, 0, KI, wm, wn, lane, MI, NI, acc);
     }
     // store (exact zeros for an empty expert)
     Tout *out = (Tout *)p.dW + (size_t)e * N * K;
