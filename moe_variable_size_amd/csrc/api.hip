@@ -41,10 +41,10 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 struct WsLayout {
-  size_t counts, offsets, bstart, order, status, r2a, r2t, rw, total;
+  size_t counts, offsets, bstart, order, status, r2a, r2t, rw, scratch, total;
 };
 
-WsLayout ws_layout(int64_t R, int E) {
+WsLayout ws_layout(int64_t S, int64_t R, int E) {
   WsLayout l;
   size_t o = 0;
   l.counts = o;  o = align256(o + sizeof(int32_t) * E);
@@ -57,6 +57,7 @@ WsLayout ws_layout(int64_t R, int E) {
   l.r2a = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
   l.r2t = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
   l.rw = o;      o = align256(o + sizeof(float) * (R + kRowPad));
+  l.scratch = o; o = align256(o + schedule_scratch_bytes(S, E));  // builder's block table
   l.total = o;
   return l;
 }
@@ -167,7 +168,7 @@ size_t moe_schedule_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t lay
                                     int32_t capacity) {
   int64_t R = 0;
   if (check_sizes(T, k, E, layout, capacity, &R)) return 0;
-  return ws_layout(R, E).total;
+  return ws_layout(T * k, R, E).total;
 }
 
 int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T, int32_t k,
@@ -178,7 +179,7 @@ int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int
   int rc = check_sizes(T, k, E, layout, capacity, &R);
   if (rc) return rc;
   if (!aligned(expert_ids, 4) || (topk_weights && !aligned(topk_weights, 4))) return MOE_ERR_ALIGN;
-  const WsLayout l = ws_layout(R, E);
+  const WsLayout l = ws_layout(T * k, R, E);
   if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
   char *w = (char *)workspace;
@@ -202,7 +203,9 @@ int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int
   *sched = s;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(
-      timed(F_SCHED, st, [&] { return launch_build_schedule(expert_ids, topk_weights, s, st); }));
+      timed(F_SCHED, st, [&] {
+        return launch_build_schedule(expert_ids, topk_weights, s, (int32_t *)(w + l.scratch), st);
+      }));
 }
 
 int grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int64_t M,

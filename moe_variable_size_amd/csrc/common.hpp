@@ -67,8 +67,11 @@ struct LaunchCtx {
 };
 int device_cu_count();
 
+// scratch: schedule_scratch_bytes(S, E) bytes of device memory (part of the
+// caller's schedule workspace)
 hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_schedule &s,
-                                 hipStream_t st);
+                                 int32_t *scratch, hipStream_t st);
+size_t schedule_scratch_bytes(int64_t S, int E);
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,
                            int32_t *total, int32_t *owner, int64_t owner_cap, hipStream_t st);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);

@@ -1091,15 +1091,29 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
 // token ring
 constexpr size_t kStageLds = (size_t)TOKREGION + TOKSLOTS * (size_t)TOKSLOT;
 
-template <typename K>
-hipError_t set_smem(K kernel, size_t bytes) {
-  return hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)bytes);
+// Raise a kernel's dynamic LDS limit once per device (the attribute persists).
+template <auto KERNEL>
+hipError_t set_smem(size_t bytes) {
+  static int done[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool slot = dev >= 0 && dev < 64;
+  if (slot && done[dev]) return hipSuccess;
+  e = hipFuncSetAttribute((const void *)KERNEL, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes);
+  if (e == hipSuccess && slot) done[dev] = 1;
+  return e;
 }
 
-int env_int(const char *name, int dflt) {
-  const char *v = getenv(name);
-  return v ? atoi(v) : dflt;
+// MOE_VS_STREAM_K=1: split the last partial round of atomic-output kernels
+// along the reduction instead of into sub-tiles (read once per process)
+int stream_k_mode() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_STREAM_K");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
 }
 
 }  // namespace
@@ -1114,12 +1128,12 @@ hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offset
   const dim3 grid(device_cu_count()), block(NT);
   if (out_dtype == MOE_F32) {
     auto k = mfma_fwd_kernel<BM, BN, 2, 2, false, float>;
-    hipError_t e = set_smem(k, kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 2, 2, false, float>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   } else {
     auto k = mfma_fwd_kernel<BM, BN, 2, 2, false, bf16_t>;
-    hipError_t e = set_smem(k, kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 2, 2, false, bf16_t>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   }
@@ -1131,19 +1145,19 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
   const dim3 grid(device_cu_count()), block(NT);
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 0), (int)s.T};
+            (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), (int)s.T};
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
     a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
     auto k = mfma_fwd_kernel<BM, BN, 1, 4, true, float>;
-    hipError_t e = set_smem(k, kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, true, float>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   } else {
     constexpr int BM = 256, BN = 256;
     a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
     auto k = mfma_fwd_kernel<BM, BN, 2, 2, true, float>;
-    hipError_t e = set_smem(k, kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 2, 2, true, float>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
   }
@@ -1156,9 +1170,9 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
            s.counts, s.block_start + bm_index(BM) * (s.E + 1), s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
-           (uint32_t)((size_t)s.T * K * 2), env_int("MOE_VS_STREAM_K", 0)};
+           (uint32_t)((size_t)s.T * K * 2), stream_k_mode()};
   auto k = mfma_dx_kernel;
-  hipError_t e = set_smem(k, kStageLds);
+  hipError_t e = set_smem<mfma_dx_kernel>(kStageLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), kStageLds, st, a);
   return hipGetLastError();
@@ -1171,7 +1185,7 @@ hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, voi
            (uint32_t)((size_t)s.T * N * 2), (uint32_t)((size_t)s.T * K * 2),
            (uint32_t)((size_t)s.R * 4), 1};
   auto k = mfma_dw_kernel<bf16_t>;
-  hipError_t e = set_smem(k, kStageLds);
+  hipError_t e = set_smem<mfma_dw_kernel<bf16_t>>(kStageLds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), kStageLds, st, a);
   return hipGetLastError();

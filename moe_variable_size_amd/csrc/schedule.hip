@@ -4,21 +4,26 @@
 // [CARD] = "grouped-gemm-moe" model card
 // [NOTE] = "Grouped GEMM" study notes (scholia-log)
 //
-// One workgroup of 1024 threads does the whole build in three phases, with no
-// host readback ([GG] "Problem descriptors and the tile scheduler": group sizes
-// stay on the device; "Failure modes": no host sync):
-//   1. histogram: every wave owns a contiguous range of assignments and counts
-//      its ids per expert (bincount, [GG] "Data layout, offsets and alignment");
-//   2. scans: per-expert counts, int32 END offsets (inclusive prefix), the
-//      row-block prefix for each tile height (tile counts and their exclusive
-//      prefix, [GG] "Problem descriptors and the tile scheduler"), each wave's
-//      first rank inside each expert, and the experts ordered by load;
-//   3. a stable counting sort: every wave walks its range again in order and
-//      places each assignment at (expert base + wave base + rank among equal ids
-//      earlier in the same 64-wide chunk), giving row -> assignment, row ->
-//      token and the per-row routing weight ([CARD] "How it works"; [NOTE] 4.1).
-// Equal ids inside a chunk are matched with one ballot per id bit, so ranks
-// never depend on the order in which hardware executes atomics: the result is
+// Three launches, no host readback ([GG] "Problem descriptors and the tile
+// scheduler": group sizes stay on the device; "Failure modes": no host sync).
+// The assignments s = 0 .. S-1 are cut into nblk blocks of B consecutive ids.
+//   1. hist  (nblk workgroups): per-block count of each expert id
+//      (bincount, [GG] "Data layout, offsets and alignment") and of ids
+//      outside [0, E);
+//   2. scan  (one workgroup): the block x expert table is brought into LDS and
+//      each expert's column turned into exclusive block bases; per-expert
+//      counts, int32 END offsets (inclusive prefix), the row-block prefix for
+//      each tile height (tile counts and their exclusive prefix, [GG] "Problem
+//      descriptors and the tile scheduler"), experts ordered by load, status,
+//      and the rows no assignment fills;
+//   3. place (nblk workgroups): a stable counting sort inside each block: every
+//      wave counts its range per expert, takes its base from the block base
+//      and the waves before it, then walks its range in order and places each
+//      assignment at (base + rank among equal ids earlier in the same 64-wide
+//      chunk), giving row -> assignment, row -> token and the per-row routing
+//      weight ([CARD] "How it works"; [NOTE] 4.1).
+// Equal ids inside a chunk are matched with one ballot per id bit, so ranks do
+// not depend on the order in which hardware executes atomics: the result is
 // deterministic and equals a stable argsort by expert.
 #include "common.hpp"
 
@@ -26,14 +31,17 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kScanThreads = 1024;
+constexpr int kBlkThreads = 256;  // hist / place workgroups: 4 waves
+constexpr int kBlkWaves = kBlkThreads / kWave;
+constexpr int kTableInts = 16384;  // block x expert table held in LDS by the scan
 
 MOE_DEV uint64_t ballot(bool p) { return __ballot(p); }
 
-// Exclusive prefix sum over the block of one int per thread (1024 threads).
-// `scratch` holds kWaves ints.  Returns the prefix; *total gets the sum.
+// Exclusive prefix sum over a 1024-thread block of one int per thread.
+// `scratch` holds kScanThreads/64 + 1 ints.  Returns the prefix; *total gets the sum.
 MOE_DEV int block_exclusive_scan(int v, int *scratch, int *total) {
+  constexpr int kWaves = kScanThreads / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   int inc = v;
@@ -73,132 +81,191 @@ MOE_DEV uint64_t peers(int id, bool valid, int nbits) {
   return m;
 }
 
-__global__ __launch_bounds__(kThreads) void build_schedule_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ w, int S, int k, int E,
+struct BlockRange {
+  int begin, end;  // this wave's assignments [begin, end)
+};
+// Wave w of block b owns a contiguous quarter of the block's B ids (B % 256 == 0).
+MOE_DEV BlockRange wave_range(int b, int B, int S, int w) {
+  const int q = B / kBlkWaves;
+  const int s0 = min(S, b * B + w * q);
+  return BlockRange{s0, min(S, s0 + q)};
+}
+
+// ---- 1. per-block histogram ---------------------------------------------------
+__global__ __launch_bounds__(kBlkThreads) void sched_hist_kernel(
+    const int32_t *__restrict__ ids, int S, int E, int B, int32_t *__restrict__ table,
+    int32_t *__restrict__ invalid_per_block) {
+  extern __shared__ int hist[];  // [E]
+  const int tid = threadIdx.x, b = blockIdx.x;
+  for (int e = tid; e <= E; e += kBlkThreads) hist[e] = 0;
+  __syncthreads();
+  int invalid = 0;
+  const int s0 = b * B, s1 = min(S, s0 + B);
+  for (int s = s0 + tid; s < s1; s += kBlkThreads) {
+    const int id = ids[s];
+    if (id >= 0 && id < E)
+      atomicAdd(&hist[id], 1);
+    else
+      ++invalid;
+  }
+  for (int d = kWave / 2; d >= 1; d >>= 1) invalid += __shfl_xor(invalid, d, kWave);
+  __syncthreads();
+  if ((tid & (kWave - 1)) == 0 && invalid) atomicAdd(&hist[E], invalid);  // hist has E+1 ints
+  __syncthreads();
+  for (int e = tid; e < E; e += kBlkThreads) table[(size_t)b * E + e] = hist[e];
+  if (tid == 0) invalid_per_block[b] = hist[E];
+}
+
+// ---- 2. scan ------------------------------------------------------------------
+__global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(
+    int32_t *__restrict__ table, const int32_t *__restrict__ invalid_per_block, int nblk, int E,
     int layout, int capacity, int R, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
     int32_t *__restrict__ block_start, int32_t *__restrict__ expert_order,
-    int32_t *__restrict__ row_to_assign, int32_t *__restrict__ row_to_token,
-    float *__restrict__ row_weight, int32_t *__restrict__ status) {
+    int32_t *__restrict__ rowbase_out, int32_t *__restrict__ row_to_assign,
+    int32_t *__restrict__ row_to_token, float *__restrict__ row_weight,
+    int32_t *__restrict__ status) {
   extern __shared__ int smem[];
-  int *hist = smem;                      // [kWaves][E]: per-wave counts, then rank bases
-  int *rowbase = hist + kWaves * E;      // [E]: first row of each expert
-  int *cnt = rowbase + E;                // [E]: valid rows per expert
-  int *scratch = cnt + E;                // [kWaves + 1]
-  int *tally = scratch + kWaves + 1;     // [2]: invalid ids, dropped assignments
-
+  int *tab = smem;                      // [nblk * E]
+  int *cnt = tab + nblk * E;            // [E]: valid rows per expert
+  int *scratch = cnt + E;               // [kScanThreads / 64 + 1]
+  int *tally = scratch + kScanThreads / kWave + 1;  // [2]
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-
-  for (int i = tid; i < kWaves * E; i += kThreads) hist[i] = 0;
+  const int n = nblk * E;
+  for (int i = tid; i < n; i += kScanThreads) tab[i] = table[i];
   if (tid < 2) tally[tid] = 0;
   __syncthreads();
+  int inv = 0;
+  for (int i = tid; i < nblk; i += kScanThreads) inv += invalid_per_block[i];
+  if (inv) atomicAdd(&tally[0], inv);
 
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
-  const int per = (((S + kWaves - 1) / kWaves) + kWave - 1) / kWave * kWave;
-  const int s_begin = min(S, wid * per);
-  const int s_end = min(S, s_begin + per);
-
-  // ---- phase 1: per-wave histogram ------------------------------------------
-  int invalid = 0;
-  for (int base = s_begin; base < s_end; base += kWave) {
-    const int s = base + lane;
-    const bool in = s < s_end;
-    const int id = in ? ids[s] : -1;
-    const bool valid = in && id >= 0 && id < E;
-    invalid += (in && !valid) ? 1 : 0;
-    const uint64_t m = peers(id, valid, nbits);
-    if (valid && (m & below) == 0) hist[wid * E + id] += __popcll(m);
-  }
-  if (invalid) atomicAdd(&tally[0], invalid);
-  __syncthreads();
-
-  // ---- phase 2: counts, offsets, tile prefixes, rank bases -------------------
-  const int e = tid;
-  int m_e = 0;
-  if (e < E) {
-    int run = 0;
-    for (int v = 0; v < kWaves; ++v) {  // per-wave exclusive rank base
-      int c = hist[v * E + e];
-      hist[v * E + e] = run;
-      run += c;
-    }
-    m_e = run;
-  }
   const bool masked = layout == MOE_LAYOUT_MASKED;
-  const int valid_rows = (e < E) ? (masked ? min(m_e, capacity) : m_e) : 0;
-  if (masked && e < E && m_e > capacity) atomicAdd(&tally[1], m_e - capacity);
-  int total;
-  const int start = block_exclusive_scan(valid_rows, scratch, &total);
-  if (e < E) {
-    counts[e] = valid_rows;
-    offsets[e] = start + valid_rows;
-    rowbase[e] = masked ? e * capacity : start;
-    cnt[e] = valid_rows;
-  }
+  static_assert(kMaxExperts <= kScanThreads, "one expert per scan thread");
+  {
+    const int e = tid;
+    int m_e = 0;
+    if (e < E) {
+      for (int b = 0; b < nblk; ++b) {  // exclusive block bases inside the expert
+        const int c = tab[b * E + e];
+        tab[b * E + e] = m_e;
+        m_e += c;
+      }
+    }
+    const int valid_rows = (e < E) ? (masked ? min(m_e, capacity) : m_e) : 0;
+    if (masked && e < E && m_e > capacity) atomicAdd(&tally[1], m_e - capacity);
+    int total;
+    const int start = block_exclusive_scan(valid_rows, scratch, &total);
+    if (e < E) {
+      counts[e] = valid_rows;
+      offsets[e] = start + valid_rows;
+      rowbase_out[e] = masked ? e * capacity : start;
+      cnt[e] = valid_rows;
+    }
 #pragma unroll
-  for (int i = 0; i < MOE_NUM_BM; ++i) {
-    const int bm = 32 << i;
-    const int nblk = (e < E) ? (masked ? (capacity + bm - 1) / bm : (valid_rows + bm - 1) / bm) : 0;
-    int tot;
-    const int pre = block_exclusive_scan(nblk, scratch, &tot);
-    if (e < E) block_start[i * (E + 1) + e] = pre;
-    if (tid == 0) block_start[i * (E + 1) + E] = tot;
-  }
-  __syncthreads();  // cnt[] complete
-
-  // experts by descending row count, ties by id
-  if (e < E) {
-    int rank = 0;
-    for (int o = 0; o < E; ++o) {
-      const int c = cnt[o];
-      rank += (c > valid_rows || (c == valid_rows && o < e)) ? 1 : 0;
+    for (int i = 0; i < MOE_NUM_BM; ++i) {
+      const int bm = 32 << i;
+      const int nb = (e < E) ? (masked ? (capacity + bm - 1) / bm : (valid_rows + bm - 1) / bm) : 0;
+      int tot;
+      const int pre = block_exclusive_scan(nb, scratch, &tot);
+      if (e < E) block_start[i * (E + 1) + e] = pre;
+      if (tid == 0) block_start[i * (E + 1) + E] = tot;
     }
-    expert_order[rank] = e;
-  }
-
-  // empty rows: past the last valid row (contiguous) or past each expert's
-  // valid prefix (masked); disjoint from the rows phase 3 writes.
-  if (!masked) {
-    for (int r = total + tid; r < R; r += kThreads) {
-      row_to_assign[r] = -1;
-      row_to_token[r] = -1;
-      row_weight[r] = 0.f;
+    __syncthreads();  // cnt[] and tab[] complete
+    // experts by descending row count, ties by id
+    if (e < E) {
+      int rank = 0;
+      for (int o = 0; o < E; ++o) {
+        const int c = cnt[o];
+        rank += (c > valid_rows || (c == valid_rows && o < e)) ? 1 : 0;
+      }
+      expert_order[rank] = e;
     }
-  } else {
-    for (int r = tid; r < R; r += kThreads) {
-      const int ex = r / capacity;
-      if (r - ex * capacity >= cnt[ex]) {
+    // rows no assignment fills: past the last valid row (contiguous) or past
+    // each expert's valid prefix (masked)
+    if (!masked) {
+      for (int r = total + tid; r < R; r += kScanThreads) {
         row_to_assign[r] = -1;
         row_to_token[r] = -1;
         row_weight[r] = 0.f;
       }
+    } else {
+      for (int r = tid; r < R; r += kScanThreads) {
+        const int ex = r / capacity;
+        if (r - ex * capacity >= cnt[ex]) {
+          row_to_assign[r] = -1;
+          row_to_token[r] = -1;
+          row_weight[r] = 0.f;
+        }
+      }
     }
   }
-
-  // ---- phase 3: stable placement -------------------------------------------
-  for (int base = s_begin; base < s_end; base += kWave) {
-    const int s = base + lane;
-    const bool in = s < s_end;
-    const int id = in ? ids[s] : -1;
-    const bool valid = in && id >= 0 && id < E;
-    const uint64_t m = peers(id, valid, nbits);
-    int rank = 0;
-    if (valid) rank = hist[wid * E + id] + __popcll(m & below);
-    if (valid && (m & below) == 0) hist[wid * E + id] += __popcll(m);
-    if (valid && (!masked || rank < capacity)) {
-      const int r = rowbase[id] + rank;
-      row_to_assign[r] = s;
-      row_to_token[r] = s / k;
-      row_weight[r] = w ? w[s] : 1.f;
-    }
-  }
+  for (int i = tid; i < n; i += kScanThreads) table[i] = tab[i];
   __syncthreads();
   if (tid == 0) {
     status[0] = tally[0];
     status[1] = tally[1];
+  }
+}
+
+// ---- 3. stable placement inside each block -------------------------------------
+__global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ w, int S, int k, int E, int B,
+    int layout, int capacity, const int32_t *__restrict__ table,
+    const int32_t *__restrict__ rowbase, int32_t *__restrict__ row_to_assign,
+    int32_t *__restrict__ row_to_token, float *__restrict__ row_weight) {
+  extern __shared__ int hist[];  // [kBlkWaves][E]: per-wave counts, then running bases
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = tid / kWave;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const bool masked = layout == MOE_LAYOUT_MASKED;
+  for (int i = tid; i < kBlkWaves * E; i += kBlkThreads) hist[i] = 0;
+  __syncthreads();
+  const BlockRange rg = wave_range(b, B, S, wid);
+  for (int s = rg.begin + lane; s < rg.end; s += kWave) {
+    const int id = ids[s];
+    if (id >= 0 && id < E) atomicAdd(&hist[wid * E + id], 1);
+  }
+  __syncthreads();
+  // per-wave base = rank base of this block inside the expert + earlier waves
+  for (int e = tid; e < E; e += kBlkThreads) {
+    int run = table[(size_t)b * E + e];
+    for (int v = 0; v < kBlkWaves; ++v) {
+      const int c = hist[v * E + e];
+      hist[v * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  constexpr int kBatch = 4;
+  for (int b0 = rg.begin; b0 < rg.end; b0 += kBatch * kWave) {
+    int idv[kBatch];
+    float wv[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {  // all loads of the batch before any use
+      const int s = b0 + u * kWave + lane;
+      idv[u] = s < rg.end ? ids[s] : -1;
+      wv[u] = (s < rg.end && w) ? w[s] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (b0 + u * kWave >= rg.end) break;  // wave-uniform
+      const int s = b0 + u * kWave + lane;
+      const int id = idv[u];
+      const bool valid = s < rg.end && id >= 0 && id < E;
+      const uint64_t m = peers(id, valid, nbits);
+      int rank = 0;
+      if (valid) rank = hist[wid * E + id] + __popcll(m & below);
+      if (valid && (m & below) == 0) hist[wid * E + id] += __popcll(m);
+      if (valid && (!masked || rank < capacity)) {
+        const int r = rowbase[id] + rank;
+        row_to_assign[r] = s;
+        row_to_token[r] = s / k;
+        row_weight[r] = wv[u];
+      }
+    }
   }
 }
 
@@ -227,21 +294,47 @@ __global__ void fill_zero_kernel(uint4 *__restrict__ p, size_t n16, uint8_t *__r
 
 }  // namespace
 
-size_t schedule_smem_bytes(int E) { return sizeof(int) * ((size_t)kWaves * E + 2 * E + kWaves + 3); }
+// Block size of the build: a multiple of 256 ids, at least 1024, large enough
+// that the block x expert table fits the scan's LDS.
+int schedule_block(int64_t S, int E) {
+  int64_t B = 1024;
+  while (((S + B - 1) / B) * E > kTableInts) B *= 2;
+  return (int)B;
+}
+int schedule_blocks(int64_t S, int E) {
+  const int B = schedule_block(S, E);
+  return (int)((S + B - 1) / B);
+}
 
 hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_schedule &s,
-                                 hipStream_t st) {
-  const size_t smem = schedule_smem_bytes(s.E);
-  if (smem > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)build_schedule_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+                                 int32_t *scratch, hipStream_t st) {
+  const int S = (int)s.S, E = s.E;
+  const int B = schedule_block(S, E), nblk = schedule_blocks(S, E);
+  int32_t *table = scratch;                          // [nblk * E]
+  int32_t *inv = table + (size_t)nblk * E;           // [nblk]
+  int32_t *rowbase = inv + nblk;                     // [E]
+  hipLaunchKernelGGL(sched_hist_kernel, dim3(nblk), dim3(kBlkThreads), sizeof(int) * (E + 1), st,
+                     ids, S, E, B, table, inv);
+  const size_t scan_smem =
+      sizeof(int) * ((size_t)nblk * E + E + kScanThreads / kWave + 1 + 2);
+  if (scan_smem > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void *)sched_scan_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(build_schedule_kernel, dim3(1), dim3(kThreads), smem, st, ids, w, (int)s.S,
-                     s.k, s.E, s.layout, s.capacity, (int)s.R, s.counts, s.offsets,
-                     s.block_start, s.expert_order, s.row_to_assign, s.row_to_token,
-                     s.row_weight, s.status);
+  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(kScanThreads), scan_smem, st, table, inv,
+                     nblk, E, s.layout, s.capacity, (int)s.R, s.counts, s.offsets, s.block_start,
+                     s.expert_order, rowbase, s.row_to_assign, s.row_to_token, s.row_weight,
+                     s.status);
+  hipLaunchKernelGGL(sched_place_kernel, dim3(nblk), dim3(kBlkThreads),
+                     sizeof(int) * kBlkWaves * E, st, ids, w, S, s.k, E, B, s.layout, s.capacity,
+                     table, rowbase, s.row_to_assign, s.row_to_token, s.row_weight);
   return hipGetLastError();
+}
+
+size_t schedule_scratch_bytes(int64_t S, int E) {
+  const int nblk = schedule_blocks(S, E);
+  return sizeof(int32_t) * ((size_t)nblk * E + nblk + E);
 }
 
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,
