@@ -70,11 +70,7 @@ constexpr int MNROW = 256 * 2; // bytes per MN-major LDS row (256 columns)
 constexpr int NSTAGE = 2;      // LDS stages
 constexpr int OPND = 256 * KROW;                  // 32 KB: one 256 x 64 operand tile
 constexpr int STAGE = 2 * OPND;                   // A then B
-constexpr int WREGION = NSTAGE * STAGE;           // per-stage routing weights (weight gradient)
-constexpr int WBYTES = 4 * 256;                   // per stage: 4 waves x 64 floats
-constexpr int TOKREGION = WREGION + NSTAGE * WBYTES;  // token ring (weight gradient)
-constexpr int TOKSLOT = 4 * 256;                  // per ring slot: 4 waves x 64 ints
-constexpr int TOKSLOTS = 4;                       // ring slots
+constexpr int TOKSLOTS = 4;                       // token ring slots (weight gradient)
 static_assert(OPND == BK * MNROW, "K-major and MN-major operand tiles have one size");
 
 // ---- LDS layouts --------------------------------------------------------------
@@ -493,17 +489,19 @@ struct KmajDma {
   }
 };
 
-// MN-major DMA of a 64 x 256 tile (512 bytes per reduction row): one instruction
-// fills 2 rows.  Thread (wave w, lane p), instruction i loads reduction row
-// 2 * (w * 8 + i) + p/32, physical chunk p % 32.
-struct MnmajMap {
-  static constexpr int PER_WAVE = 8;
+// MN-major DMA of a 64 x 256 tile (512 bytes per reduction row) by NW waves: one
+// instruction fills 2 rows.  Thread (wave w, lane p), instruction i loads
+// reduction row 2 * (w * 32/NW + i) + p/32, physical chunk p % 32.
+template <int NW>
+struct MnmajMapT {
+  static constexpr int PER_WAVE = 32 / NW;
   MOE_DEV static int row_of(int wid, int i, int lane) { return 2 * (wid * PER_WAVE + i) + (lane >> 5); }
   MOE_DEV static int chunk_of(int wid, int i, int lane) {
     return (lane & 31) ^ ((row_of(wid, i, lane) & 3) << 2);
   }
   MOE_DEV static uint32_t lds_of(int wid, int i) { return (uint32_t)((wid * PER_WAVE + i) * 1024); }
 };
+using MnmajMap = MnmajMapT<4>;
 
 // ============================================================================
 // Forward-shaped kernel: out[r, n] = sum_k A[src(r), k] * W[g, n, k].
@@ -932,29 +930,37 @@ struct DwArgs {
   int weighted;
 };
 
+template <int NW>
 struct DwOp {
+  using Map = MnmajMapT<NW>;
+  static constexpr int PW = Map::PER_WAVE;  // dY (and x) instructions per wave per stage
   static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
-  // per stage: 8 dY + 8 x instructions, the stage's routing weights, the
+  // per stage: PW dY + PW x instructions, the stage's routing weights, the
   // tokens of the stage two ahead
-  static constexpr int DMA_PER_STAGE = 8 + 8 + 1 + 1;
+  static constexpr int DMA_PER_STAGE = 2 * PW + 1 + 1;
+  // LDS after the stages: per stage one 64-float weight strip per wave, then a
+  // ring of TOKSLOTS slots holding one 64-token copy per wave
+  static constexpr int WSTRIPS = NSTAGE * STAGE;
+  static constexpr int WB = NW * 256;
+  static constexpr int TOKS = WSTRIPS + NSTAGE * WB;
+  static constexpr int TSLOT = NW * 256;
+  static constexpr size_t LDS_BYTES = (size_t)TOKS + TOKSLOTS * TSLOT;
   __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
   uint32_t lds0;
   const char *lds;
   int r0, m, wid, lane, K, N, weighted;
-  uint32_t ncol[8], kcol[8];  // byte offsets of this lane's column chunk (dY / x), or OOB
-  i32x4 tq[4];                // tokens of this wave's 16 rows of the stage being issued
+  uint32_t ncol[PW], kcol[PW];  // byte offsets of this lane's column chunk (dY / x), or OOB
+  i32x4 tq[PW / 2];             // tokens of this wave's 2*PW rows of the stage being issued
 
   MOE_DEV void setup(int n0, int kc0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int ch = MnmajMap::chunk_of(wid, i, lane);
+    for (int i = 0; i < PW; ++i) {
+      const int ch = Map::chunk_of(wid, i, lane);
       ncol[i] = n0 + 8 * ch < N ? (uint32_t)(n0 + 8 * ch) * 2u : kOobOffset;
       kcol[i] = kc0 + 8 * ch < K ? (uint32_t)(kc0 + 8 * ch) * 2u : kOobOffset;
     }
   }
-  MOE_DEV int ring_off(int kt) const {
-    return TOKREGION + (kt & (TOKSLOTS - 1)) * TOKSLOT + wid * 256;
-  }
+  MOE_DEV int ring_off(int kt) const { return TOKS + (kt & (TOKSLOTS - 1)) * TSLOT + wid * 256; }
   // Tokens of stages kt0 .. kt0+n-1 into the ring, synchronously (no DMA in flight).
   MOE_DEV void fill_ring(const int32_t *r2t, int kt0, int n) {
     for (int s = 0; s < n; ++s) {
@@ -962,37 +968,38 @@ struct DwOp {
       *(int *)(lds + ring_off(kt0 + s) + lane * 4) = q < m ? r2t[r0 + q] : -1;
     }
   }
-  // tokens of this wave's rows 16*wid .. +15 of stage kt (ring copy of this wave)
+  // tokens of this wave's rows 2*PW*wid .. +2*PW-1 of stage kt (ring copy of this wave)
   MOE_DEV void prefetch(int kt) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tq[i] = *(const i32x4 *)(lds + ring_off(kt) + wid * 64 + 16 * i);
+    for (int i = 0; i < PW / 2; ++i)
+      tq[i] = *(const i32x4 *)(lds + ring_off(kt) + wid * (8 * PW) + 16 * i);
   }
   template <bool SKIP>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < 16) {
-      const int i = j & 7;
-      const int rl = 2 * i + (lane >> 5);  // row within the wave's 16
-      const int q = kt * BK + 16 * wid + rl;
+    if (j < 2 * PW) {
+      const int i = j % PW;
+      const int rl = 2 * i + (lane >> 5);  // row within the wave's 2*PW
+      const int q = kt * BK + 2 * PW * wid + rl;
       const int te = tq[i >> 1][(2 * i) & 3], to = tq[i >> 1][(2 * i + 1) & 3];
       int tok = (lane >> 5) ? to : te;
       if (q >= m) tok = -1;
-      if (j < 8) {
+      if (j < PW) {
         const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
                                   ? (uint32_t)tok * (uint32_t)N * 2u + ncol[i]
                                   : kOobOffset;
-        dma16(rsY, offy, t + MnmajMap::lds_of(wid, i));
+        dma16(rsY, offy, t + Map::lds_of(wid, i));
       } else {
         const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
                                   ? (uint32_t)tok * (uint32_t)K * 2u + kcol[i]
                                   : kOobOffset;
-        dma16(rsX, offx, t + OPND + MnmajMap::lds_of(wid, i));
+        dma16(rsX, offx, t + OPND + Map::lds_of(wid, i));
       }
-    } else if (j == 16) {
+    } else if (j == 2 * PW) {
       // routing weights of the stage's 64 rows into this wave's strip
       const int qw = kt * BK + lane;
       const uint32_t offw = qw < m ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
-      dma4(rsW, offw, lds0 + (uint32_t)(WREGION + buf * WBYTES + wid * 256));
+      dma4(rsW, offw, lds0 + (uint32_t)(WSTRIPS + buf * WB + wid * 256));
     } else {
       // tokens of stage kt + 2 into the ring (read by its prefetch after this
       // stage has been waited for)
@@ -1003,7 +1010,7 @@ struct DwOp {
   }
   // factors of the 8 reduction rows this lane holds in step `step`
   MOE_DEV void row_scale(int buf, int step, int ln, float (&w)[8]) {
-    const float *src = (const float *)(lds + WREGION + buf * WBYTES + wid * 256) + step * 16 +
+    const float *src = (const float *)(lds + WSTRIPS + buf * WB + wid * 256) + step * 16 +
                        8 * (ln >> 5);
     const f32x4 a = *(const f32x4 *)src, b = *(const f32x4 *)(src + 4);
 #pragma unroll
@@ -1014,10 +1021,12 @@ struct DwOp {
   }
 };
 
-template <typename Tout>
-__global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
-  constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2;
-  constexpr int MI = 4, NI = 4;
+// NW waves: 4 (2 x 2 grid, 128 x 128 per wave) or 8 (4 x 2, 64 x 128 per wave:
+// two waves per SIMD, half the LDS reads per wave per MFMA step)
+template <typename Tout, int NW>
+__global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
+  constexpr int BM = 256, BN = 256, WGM = NW == 8 ? 4 : 2, WGN = 2;
+  constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -1027,7 +1036,7 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   const int per_e = tn * tk;
   const int units = E * per_e;
   const int G = gridDim.x, L = logical_block();
-  DwOp op;
+  DwOp<NW> op;
   op.rsY = uniform_rsrc(p.dY, p.dy_bytes);
   op.rsX = uniform_rsrc(p.x, p.x_bytes);
   op.rsW = uniform_rsrc(p.row_weight, p.rw_bytes);
@@ -1087,9 +1096,9 @@ __global__ __launch_bounds__(NT) void mfma_dw_kernel(DwArgs p) {
   }
 }
 
-// dynamic LDS: NSTAGE stages of (A 32 KB, B 32 KB), the weight strips and the
-// token ring
-constexpr size_t kStageLds = (size_t)TOKREGION + TOKSLOTS * (size_t)TOKSLOT;
+// dynamic LDS of the forward and input-gradient kernels: NSTAGE stages of
+// (A 32 KB, B 32 KB)
+constexpr size_t kStageLds = (size_t)NSTAGE * STAGE;
 
 // Raise a kernel's dynamic LDS limit once per device (the attribute persists).
 template <auto KERNEL>
@@ -1112,6 +1121,15 @@ int stream_k_mode() {
   static const int v = [] {
     const char *e = getenv("MOE_VS_STREAM_K");
     return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
+// MOE_VS_DW_WAVES=4: weight gradient with 4 waves per workgroup instead of 8
+int dw_waves() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_DW_WAVES");
+    return e && atoi(e) == 4 ? 4 : 8;
   }();
   return v;
 }
@@ -1184,10 +1202,17 @@ hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, voi
            s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
            (uint32_t)((size_t)s.T * N * 2), (uint32_t)((size_t)s.T * K * 2),
            (uint32_t)((size_t)s.R * 4), 1};
-  auto k = mfma_dw_kernel<bf16_t>;
-  hipError_t e = set_smem<mfma_dw_kernel<bf16_t>>(kStageLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), kStageLds, st, a);
+  if (dw_waves() == 4) {
+    constexpr size_t lds = DwOp<4>::LDS_BYTES;
+    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 4>>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 4>), dim3(device_cu_count()), dim3(256), lds, st, a);
+  } else {
+    constexpr size_t lds = DwOp<8>::LDS_BYTES;
+    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8>>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8>), dim3(device_cu_count()), dim3(512), lds, st, a);
+  }
   return hipGetLastError();
 }
 
