@@ -456,12 +456,12 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   }
 }
 
-// K-major DMA of a tile of R rows x 64 reduction elements (128 bytes per row):
-// one instruction fills 8 rows (1 KB of LDS).  Thread (wave w, lane p),
-// instruction i loads row (w * R/32 + i) * 8 + p/8, physical chunk p % 8.
-template <int R>
+// K-major DMA of a tile of R rows x 64 reduction elements (128 bytes per row) by
+// NW waves: one instruction fills 8 rows (1 KB of LDS).  Thread (wave w, lane
+// p), instruction i loads row (w * R/(8 NW) + i) * 8 + p/8, physical chunk p % 8.
+template <int R, int NW = 4>
 struct KmajDma {
-  static constexpr int PER_WAVE = R / 32;
+  static constexpr int PER_WAVE = R / (8 * NW);
   uint32_t base[PER_WAVE];  // per-lane global byte offset of the row chunk, stage 0
   int chunk[PER_WAVE];      // logical chunk (reduction elements 8*chunk .. +7)
   int live_rows;            // rows at or past this are never read (wave-uniform)
@@ -525,52 +525,54 @@ struct FwdArgs {
   int M;             // bare: rows of A and C (rows at or past M are never touched)
 };
 
-template <int BM, int BN>
+template <int BM, int BN, int NW>
 struct FwdOp {
   static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false, PREFETCH = false;
-  static constexpr int DMA_PER_STAGE = BM / 32 + BN / 32;
-  KmajDma<BM> da;
-  KmajDma<BN> db;
+  static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
+  static constexpr int DMA_PER_STAGE = DA + DB;
+  KmajDma<BM, NW> da;
+  KmajDma<BN, NW> db;
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0;
   int K, wid;
   template <bool SKIP>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < BM / 32)
+    if (j < DA)
       da.template issue_one<SKIP>(rsA, kt, K, t, wid, j);
     else
-      db.template issue_one<SKIP>(rsW, kt, K, t + OPND, wid, j - BM / 32);
+      db.template issue_one<SKIP>(rsW, kt, K, t + OPND, wid, j - DA);
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
 };
 
 template <int BM, int BN, int WGM, int WGN, bool FUSED, typename Tout>
-__global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
+__global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
-  static_assert(WGM * WGN == 4, "4 waves");
+  constexpr int NW = WGM * WGN, NTH = NW * 64;
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   extern __shared__ __attribute__((aligned(16))) char lds[];  // NSTAGE x (A, B)
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
   __shared__ __attribute__((aligned(16))) int tok[BM];
   __shared__ __attribute__((aligned(16))) float wgt[BM];
   __shared__ int rowoff_a[BM], rowoff_b[BN];
-  __shared__ int scratch[NT / kWave + 1];
+  __shared__ int scratch[NTH / kWave + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
   if (FUSED)
-    group_tables_from_schedule<NT>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
-                                   rstart, rcnt);
+    group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
+                                    rstart, rcnt);
   else
-    group_tables_from_offsets<NT>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
+    group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
 
   const int tiles_n = (N + BN - 1) / BN;
   const int KI = (K + BK - 1) / BK;
   const int total = bs[E] * tiles_n;
-  FwdOp<BM, BN> op;
+  FwdOp<BM, BN, NW> op;
   op.rsA = uniform_rsrc(p.A, p.a_bytes);
   op.lds0 = lds_addr(lds);
   op.K = K;
@@ -602,7 +604,7 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
       wgt[tid] = (FUSED && ok) ? p.row_weight[r] : 0.f;
       rowoff_a[tid] = t >= 0 ? t * K * 2 : -1;
     }
-    for (int j = tid; j < BN; j += NT) rowoff_b[j] = j < ncols ? (n0 + j) * K * 2 : -1;
+    for (int j = tid; j < BN; j += NTH) rowoff_b[j] = j < ncols ? (n0 + j) * K * 2 : -1;
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
     const bool part = BM <= 64 || ws.nS > 1;  // rows / columns partly dead
@@ -622,8 +624,8 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
       for (int mi = 0; mi < MIc; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
-      tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN>, DSK>(op, lds, kb, ke, wm, wn, lane,
-                                                                 live_mi, NIc, acc);
+      tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW>, DSK>(op, lds, kb, ke, wm, wn, lane,
+                                                                     live_mi, NIc, acc);
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
       // row tables; each row's base address is formed once for all column blocks
@@ -665,10 +667,12 @@ __global__ __launch_bounds__(NT) void mfma_fwd_kernel(FwdArgs p) {
     if constexpr (BM <= 64) {
       tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(), true_type());
     } else {
+      // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
+      constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
       if (ws.nS == 8)
-        tile(integral_constant<int, 1>(), integral_constant<int, 2>(), false_type(), true_type());
+        tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(), true_type());
       else if (ws.nS == 4)
-        tile(integral_constant<int, 2>(), integral_constant<int, 2>(), false_type(), true_type());
+        tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(), true_type());
       else
         tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
              false_type());
@@ -704,42 +708,47 @@ struct DxArgs {
   int stream_k;
 };
 
+template <int NW>
 struct DxOp {
+  using Map = MnmajMapT<NW>;
   static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false, PREFETCH = false;
-  static constexpr int DMA_PER_STAGE = 8 + 8;
-  KmajDma<256> da;
-  uint32_t bcol[8];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
+  static constexpr int DA = 256 / (8 * NW), PW = Map::PER_WAVE;
+  static constexpr int DMA_PER_STAGE = DA + PW;
+  KmajDma<256, NW> da;
+  uint32_t bcol[PW];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0, rowbytes_w;
   int N, wid, lane;
   // columns kc0 .. kend-1 of W are loaded, the rest read as zeros
   MOE_DEV void setup_b(int kc0, int kend) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int col = kc0 + 8 * MnmajMap::chunk_of(wid, i, lane);
+    for (int i = 0; i < PW; ++i) {
+      const int col = kc0 + 8 * Map::chunk_of(wid, i, lane);
       bcol[i] = col < kend ? (uint32_t)col * 2u : kOobOffset;
     }
   }
   template <bool SKIP>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < 8) {
+    if (j < DA) {
       da.template issue_one<SKIP>(rsA, kt, N, t, wid, j);
     } else {
-      const int i = j - 8;
-      const int n = kt * BK + MnmajMap::row_of(wid, i, lane);
+      const int i = j - DA;
+      const int n = kt * BK + Map::row_of(wid, i, lane);
       const uint32_t off = (n < N && bcol[i] != kOobOffset) ? (uint32_t)n * rowbytes_w + bcol[i]
                                                             : kOobOffset;
-      dma16(rsW, off, t + OPND + MnmajMap::lds_of(wid, i));
+      dma16(rsW, off, t + OPND + Map::lds_of(wid, i));
     }
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
 };
 
-__global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
-  constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2;
-  constexpr int MI = 4, NI = 4;
+// NW waves in a 2 x NW/2 grid
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
+  constexpr int BM = 256, BN = 256, WGM = 2, WGN = NW / 2, NTH = NW * 64;
+  constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
   __shared__ __attribute__((aligned(16))) int tok[BM];
@@ -751,12 +760,12 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
-  group_tables_from_schedule<NT>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
-                                 rstart, rcnt);
+  group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
+                                  rstart, rcnt);
   const int tiles_n = (K + BN - 1) / BN;  // output columns run over K
   const int KI = (N + BK - 1) / BK;       // reduction runs over N
   const int total = bs[E] * tiles_n;
-  DxOp op;
+  DxOp<NW> op;
   op.rsA = uniform_rsrc(p.dY, p.dy_bytes);
   op.lds0 = lds_addr(lds);
   op.rowbytes_w = (uint32_t)K * 2u;
@@ -807,25 +816,26 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
       for (int mi = 0; mi < MIc; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
-      tile_multiply<MIc, NIc, WGM, WGN, false, DxOp, DSK>(op, lds, kb, ke, wm, wn, lane, MIc, NIc,
-                                                          acc);
+      tile_multiply<MIc, NIc, WGM, WGN, false, DxOp<NW>, DSK>(op, lds, kb, ke, wm, wn, lane, MIc,
+                                                              NIc, acc);
 
       // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: four
       // 64-column K-major sub-tiles into the (now idle) LDS stages
       if (p.d_w) {
         barrier();
         const uint32_t l0 = lds_addr(lds);
+        constexpr int XPW = 32 / NW;  // instructions per wave per 64-column sub-tile
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int row = (wid * 8 + i) * 8 + (lane >> 3);
+          for (int i = 0; i < XPW; ++i) {
+            const int row = (wid * XPW + i) * 8 + (lane >> 3);
             const int cch = (lane & 7) ^ ((row >> 1) & 7);
             const int t = tok[row];
             const int col = kc0 + q * 64 + cch * 8;
             const uint32_t off =
                 (t >= 0 && col < K) ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u : kOobOffset;
-            dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * 8 + i) * 1024));
+            dma16(rsX, off, l0 + (uint32_t)(q * OPND + (wid * XPW + i) * 1024));
           }
         }
         wait_vmcnt<0>();
@@ -892,10 +902,12 @@ __global__ __launch_bounds__(NT) void mfma_dx_kernel(DxArgs p) {
       }
     };
     using std::integral_constant;
+    // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
+    constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
     if (ws.nS == 8)
-      tile(integral_constant<int, 1>(), integral_constant<int, 2>(), std::true_type());
+      tile(integral_constant<int, R8>(), integral_constant<int, C>(), std::true_type());
     else if (ws.nS == 4)
-      tile(integral_constant<int, 2>(), integral_constant<int, 2>(), std::true_type());
+      tile(integral_constant<int, R4>(), integral_constant<int, C>(), std::true_type());
     else
       tile(integral_constant<int, MI>(), integral_constant<int, NI>(), std::false_type());
   }
@@ -1125,6 +1137,25 @@ int stream_k_mode() {
   return v;
 }
 
+// MOE_VS_DX_WAVES=8: input-gradient kernel with 8 waves per workgroup instead of
+// 4 (its routing-weight epilogue runs short of registers with 8)
+int dx_waves() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_DX_WAVES");
+    return e && atoi(e) == 8 ? 8 : 4;
+  }();
+  return v;
+}
+
+// MOE_VS_GEMM_WAVES=4: forward kernels with 4 waves per workgroup instead of 8
+int gemm_waves() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_GEMM_WAVES");
+    return e && atoi(e) == 4 ? 4 : 8;
+  }();
+  return v;
+}
+
 // MOE_VS_DW_WAVES=4: weight gradient with 4 waves per workgroup instead of 8
 int dw_waves() {
   static const int v = [] {
@@ -1138,29 +1169,36 @@ int dw_waves() {
 
 bool mfma_supported(int K, int N) { return K % 8 == 0 && N % 8 == 0; }
 
+namespace {
+// Launch a 256 x 256 forward-shaped kernel with 4 (2 x 2) or 8 (2 x 4) waves.
+template <bool FUSED, typename Tout>
+hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
+  const dim3 grid(device_cu_count());
+  if (gemm_waves() == 4) {
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, FUSED, Tout>>(kStageLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, FUSED, Tout>), grid, dim3(256), kStageLds,
+                       st, a);
+  } else {
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, FUSED, Tout>>(kStageLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, FUSED, Tout>), grid, dim3(512), kStageLds,
+                       st, a);
+  }
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int M,
                              int K, int N, int E, int out_dtype, hipStream_t st) {
   FwdArgs a{(const bf16_t *)A, (const bf16_t *)W, C, offsets, nullptr, nullptr, nullptr, nullptr,
             E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), 0, M};
-  constexpr int BM = 256, BN = 256;
-  const dim3 grid(device_cu_count()), block(NT);
-  if (out_dtype == MOE_F32) {
-    auto k = mfma_fwd_kernel<BM, BN, 2, 2, false, float>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 2, 2, false, float>>(kStageLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
-  } else {
-    auto k = mfma_fwd_kernel<BM, BN, 2, 2, false, bf16_t>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 2, 2, false, bf16_t>>(kStageLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
-  }
-  return hipGetLastError();
+  if (out_dtype == MOE_F32) return launch_fwd256<false, float>(a, st);
+  return launch_fwd256<false, bf16_t>(a, st);
 }
 
 hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
                           int N, hipStream_t st) {
-  const dim3 grid(device_cu_count()), block(NT);
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
             (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), (int)s.T};
@@ -1170,16 +1208,11 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
     auto k = mfma_fwd_kernel<BM, BN, 1, 4, true, float>;
     hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, true, float>>(kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
-  } else {
-    constexpr int BM = 256, BN = 256;
-    a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
-    auto k = mfma_fwd_kernel<BM, BN, 2, 2, true, float>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 2, 2, true, float>>(kStageLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, grid, block, kStageLds, st, a);
+    hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  a.bstart = s.block_start + bm_index(256) * (s.E + 1);
+  return launch_fwd256<true, float>(a, st);
 }
 
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
@@ -1189,10 +1222,16 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
            s.counts, s.block_start + bm_index(BM) * (s.E + 1), s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
            (uint32_t)((size_t)s.T * K * 2), stream_k_mode()};
-  auto k = mfma_dx_kernel;
-  hipError_t e = set_smem<mfma_dx_kernel>(kStageLds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(NT), kStageLds, st, a);
+  const dim3 grid(device_cu_count());
+  if (dx_waves() == 4) {
+    hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mfma_dx_kernel<4>, grid, dim3(256), kStageLds, st, a);
+  } else {
+    hipError_t e = set_smem<mfma_dx_kernel<8>>(kStageLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mfma_dx_kernel<8>, grid, dim3(512), kStageLds, st, a);
+  }
   return hipGetLastError();
 }
 
