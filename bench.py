@@ -78,21 +78,6 @@ def cpu_baseline(r, flops_step: float, min_seconds: float) -> dict:
             "blas": blas}
 
 
-KERNEL_SOURCES = ("moe_variable_size_amd/csrc/mfma.hip", "moe_variable_size_amd/csrc/common.hpp",
-                  "moe_variable_size_amd/csrc/api.hip")
-
-
-def source_digest() -> str:
-    """sha256 over the kernel sources: counter figures are used only while it
-    still matches the one they were taken with."""
-    import hashlib
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
-
-
 def _traffic(kernel_family: str):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy's reading),
@@ -102,6 +87,7 @@ def _traffic(kernel_family: str):
         return None
     with open(path) as fh:
         rec = json.load(fh)
+    from moe_variable_size_amd.counters import source_digest
     if rec.get("source_sha256") != source_digest():
         return None
     k = rec.get("kernels", {}).get(kernel_family)

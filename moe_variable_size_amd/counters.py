@@ -1,0 +1,116 @@
+"""HBM traffic per kernel launch from rocprofv3 counter runs.
+
+Two runs of the benchmark under ``rocprofv3 --pmc`` (one with FETCH_SIZE, one
+with WRITE_SIZE; both in KiB per dispatch) are reduced to the average per
+launch of each GEMM kernel family.  Each counter is scaled by what it reads for
+a plain device copy of known size (``bench.py --calib-copy`` copies 256 MiB),
+so the figures are bytes, whatever the counter's own unit or coverage.
+
+    python -m moe_variable_size_amd.counters --fetch DIR --write DIR \\
+        --out profiles/traffic_counters.json
+
+DIR is the ``-d`` directory of a run made with ``--output-format csv``.
+The record carries the sha256 of the kernel sources; ``bench.py`` reports the
+traffic only while the sources still match.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ("moe_variable_size_amd/csrc/mfma.hip", "moe_variable_size_amd/csrc/common.hpp",
+                  "moe_variable_size_amd/csrc/api.hip")
+COPY_BYTES = 256 << 20   # bench.py --calib-copy: 64 Mi float32 copied device to device
+
+FAMILIES = (("mfma_fwd_kernel<256", "fused_fwd"), ("mfma_dx_kernel", "bwd_dx"),
+            ("mfma_dw_kernel", "bwd_dw"), ("mfma_fwd_kernel<64", "decode_fwd"))
+
+
+def source_digest() -> str:
+    """sha256 over the kernel sources the counter figures belong to."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _family(name: str):
+    if "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name:
+        return "copy"
+    for key, fam in FAMILIES:
+        if key in name:
+            return fam
+    return None
+
+
+def per_launch_kib(run_dir: str, counter: str) -> dict:
+    """Average counter value per dispatch, per kernel family."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    per_dispatch = defaultdict(float)
+    fam_of = {}
+    for f in files:
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row["Counter_Name"] != counter:
+                    continue
+                fam = _family(row["Kernel_Name"])
+                if fam is None:
+                    continue
+                key = (f, row["Dispatch_Id"])
+                per_dispatch[key] += float(row["Counter_Value"])
+                fam_of[key] = fam
+    sums, counts = defaultdict(float), defaultdict(int)
+    for key, v in per_dispatch.items():
+        sums[fam_of[key]] += v
+        counts[fam_of[key]] += 1
+    return {fam: {"kib": sums[fam] / counts[fam], "dispatches": counts[fam]} for fam in sums}
+
+
+def main(argv=None) -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--fetch", required=True, help="rocprofv3 -d directory of the FETCH_SIZE run")
+    ap.add_argument("--write", required=True, help="rocprofv3 -d directory of the WRITE_SIZE run")
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--command", action="append", default=[],
+                    help="the profiling commands, recorded in the output")
+    a = ap.parse_args(argv)
+    fetch = per_launch_kib(a.fetch, "FETCH_SIZE")
+    write = per_launch_kib(a.write, "WRITE_SIZE")
+    if "copy" not in fetch or "copy" not in write:
+        raise SystemExit("no plain-copy dispatch found: run the bench with --calib-copy")
+    f_scale = COPY_BYTES / (fetch["copy"]["kib"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"]["kib"] * 1024.0)
+    kernels = {}
+    for fam in sorted(set(fetch) & set(write)):
+        if fam == "copy":
+            continue
+        fb = fetch[fam]["kib"] * 1024.0 * f_scale
+        wb = write[fam]["kib"] * 1024.0 * w_scale
+        kernels[fam] = {"fetch_kib_raw": round(fetch[fam]["kib"], 1),
+                        "write_kib_raw": round(write[fam]["kib"], 1),
+                        "fetch_bytes": int(fb), "write_bytes": int(wb),
+                        "hbm_bytes_per_launch": int(fb + wb),
+                        "dispatches": [fetch[fam]["dispatches"], write[fam]["dispatches"]]}
+    rec = {"source_sha256": source_digest(),
+           "calibration": {"copy_bytes": COPY_BYTES,
+                           "fetch_kib_raw": round(fetch["copy"]["kib"], 1),
+                           "write_kib_raw": round(write["copy"]["kib"], 1),
+                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+           "kernels": kernels, "commands": a.command}
+    os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
+    with open(a.out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+if __name__ == "__main__":
+    main()
