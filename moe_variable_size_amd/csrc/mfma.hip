@@ -96,6 +96,17 @@ MOE_DEV void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
                : "s"(m0v), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+// As dma16, with a wave-uniform byte offset `soff` added to the address (the
+// per-stage advance of a tile whose per-lane offsets stay fixed).  Only used
+// where voff + soff stays inside the lane's row; rows masked with an
+// out-of-range voff stay masked.
+MOE_DEV void dma16_so(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
 MOE_DEV void dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
@@ -283,8 +294,12 @@ MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 
 //   static constexpr bool PREFETCH        prefetch(kt) must run (LDS reads)
 //       before the parts of stage kt are issued
 //   static constexpr int DMA_PER_STAGE    DMA instructions per thread per stage
-//   template <bool SKIP> void issue_part(int kt, int buf, int j)
-//       j-th DMA instruction of stage kt (SKIP: may be left out for dead rows)
+//   static constexpr bool CHECKED_TAIL    only the last stage of a range needs
+//       bounds checks (its whole stages take the cheaper unchecked DMA)
+//   template <bool SKIP, bool CHECKED> void issue_part(int kt, int buf, int j)
+//       j-th DMA instruction of stage kt (SKIP: may be left out for dead rows;
+//       CHECKED: the stage may reach past the reduction length, so each lane's
+//       chunk is bounds-checked; otherwise the stage lies wholly inside it)
 // Buffer b: A at lds + b * STAGE, B at + OPND.
 //
 // A stage holds 64 reduction elements = four 16-deep MFMA steps; operand
@@ -372,7 +387,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   };
   // last step of the stage in `buf` (slot 1): reads of step 0 of `nbuf` into
   // slot 0; with DMA, stage `dma` is issued into `buf`
-  auto step_last = [&](int buf, int nbuf, int dma, auto DMA) __attribute__((always_inline)) {
+  auto step_last = [&](int buf, int nbuf, int dma, auto DMA, auto CHK) __attribute__((always_inline)) {
     constexpr int DD = decltype(DMA)::value ? D : 0;
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -384,7 +399,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
         if (j * SLOTS / NR == i) read_item(nbuf, 0, 0, j);
 #pragma unroll
       for (int j = 0; j < DD; ++j)
-        if (j * SLOTS / DD == i) op.template issue_part<DSKIP>(dma, buf, j);
+        if (j * SLOTS / DD == i) op.template issue_part<DSKIP, decltype(CHK)::value>(dma, buf, j);
       if (NS > 0 && i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
       MOE_FENCE();
     }
@@ -398,7 +413,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   auto issue_stage = [&](int kt, int buf) __attribute__((always_inline)) {
     if (Op::PREFETCH) op.prefetch(kt);
 #pragma unroll
-    for (int j = 0; j < D; ++j) op.template issue_part<DSKIP>(kt, buf, j);
+    for (int j = 0; j < D; ++j) op.template issue_part<DSKIP, true>(kt, buf, j);
   };
 
   // prologue: the first two stages in flight; wait for the first
@@ -423,15 +438,29 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   MOE_FENCE();
 
   int kt = kb;
-  // stages whose buffer is refilled with stage kt + 2
-  for (; kt + 2 < ke; ++kt) {
+  // stages whose buffer is refilled with stage kt + 2; every stage but the
+  // last one of the range lies wholly inside the reduction (an Op whose DMA
+  // does not depend on that issues every stage the same way)
+  constexpr int PEEL = Op::CHECKED_TAIL ? 1 : 0;
+  for (; kt + 2 + PEEL < ke; ++kt) {
     const int buf = (kt - kb) & 1;
     step_inner(buf, 0, kt + 2, std::integral_constant<bool, Op::PREFETCH>());
     step_inner(buf, 1, 0, std::false_type());
     step_inner(buf, 2, 0, std::false_type());
     wait_vmcnt<0>();  // stage kt+1 landed
     sync();
-    step_last(buf, buf ^ 1, kt + 2, std::true_type());
+    step_last(buf, buf ^ 1, kt + 2, std::true_type(), std::false_type());
+  }
+  // the last stage of the range is issued with bounds checks
+  if (PEEL && kt + 2 < ke) {
+    const int buf = (kt - kb) & 1;
+    step_inner(buf, 0, kt + 2, std::integral_constant<bool, Op::PREFETCH>());
+    step_inner(buf, 1, 0, std::false_type());
+    step_inner(buf, 2, 0, std::false_type());
+    wait_vmcnt<0>();
+    sync();
+    step_last(buf, buf ^ 1, kt + 2, std::true_type(), std::true_type());
+    ++kt;
   }
   // the stage before the last: nothing more to issue
   if (kt + 1 < ke) {
@@ -441,7 +470,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
     step_inner(buf, 2, 0, std::false_type());
     wait_vmcnt<0>();
     sync();
-    step_last(buf, buf ^ 1, 0, std::false_type());
+    step_last(buf, buf ^ 1, 0, std::false_type(), std::false_type());
     ++kt;
   }
   // final stage
@@ -478,14 +507,20 @@ struct KmajDma {
     }
   }
   // instruction i of stage kt (SKIP: left out when all its rows are dead; the
-  // LDS rows then keep stale values, which only reach dead accumulator rows)
-  template <bool SKIP>
+  // LDS rows then keep stale values, which only reach dead accumulator rows).
+  // CHECKED: chunks at or past the reduction length `kred` read zeros;
+  // otherwise the whole stage lies inside every row.
+  template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_one(__amdgpu_buffer_rsrc_t rs, int kt, int kred, uint32_t lds_tile, int wid,
                          int i) {
     if (SKIP && (wid * PER_WAVE + i) * 8 >= live_rows) return;
-    const bool in = kt * BK + chunk[i] * 8 < kred;
-    const uint32_t off = in ? base[i] + (uint32_t)kt * KROW : kOobOffset;
-    dma16(rs, off, lds_tile + (uint32_t)((wid * PER_WAVE + i) * 1024));
+    const uint32_t lds = lds_tile + (uint32_t)((wid * PER_WAVE + i) * 1024);
+    if (CHECKED) {
+      const bool in = kt * BK + chunk[i] * 8 < kred;
+      dma16(rs, in ? base[i] + (uint32_t)kt * KROW : kOobOffset, lds);
+    } else {
+      dma16_so(rs, base[i], (uint32_t)kt * KROW, lds);
+    }
   }
 };
 
@@ -528,6 +563,7 @@ struct FwdArgs {
 template <int BM, int BN, int NW>
 struct FwdOp {
   static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false, PREFETCH = false;
+  static constexpr bool CHECKED_TAIL = true;
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
   static constexpr int DMA_PER_STAGE = DA + DB;
   KmajDma<BM, NW> da;
@@ -535,13 +571,13 @@ struct FwdOp {
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0;
   int K, wid;
-  template <bool SKIP>
+  template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < DA)
-      da.template issue_one<SKIP>(rsA, kt, K, t, wid, j);
+      da.template issue_one<SKIP, CHECKED>(rsA, kt, K, t, wid, j);
     else
-      db.template issue_one<SKIP>(rsW, kt, K, t + OPND, wid, j - DA);
+      db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + OPND, wid, j - DA);
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
@@ -712,10 +748,12 @@ template <int NW>
 struct DxOp {
   using Map = MnmajMapT<NW>;
   static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false, PREFETCH = false;
+  static constexpr bool CHECKED_TAIL = true;
   static constexpr int DA = 256 / (8 * NW), PW = Map::PER_WAVE;
   static constexpr int DMA_PER_STAGE = DA + PW;
   KmajDma<256, NW> da;
   uint32_t bcol[PW];  // per instruction: byte offset (kc0 + 8 * chunk) * 2, or OOB
+  uint32_t bvo[PW];   // the same plus the lane's reduction row inside a stage, or OOB
   __amdgpu_buffer_rsrc_t rsA, rsW;
   uint32_t lds0, rowbytes_w;
   int N, wid, lane;
@@ -725,19 +763,26 @@ struct DxOp {
     for (int i = 0; i < PW; ++i) {
       const int col = kc0 + 8 * Map::chunk_of(wid, i, lane);
       bcol[i] = col < kend ? (uint32_t)col * 2u : kOobOffset;
+      bvo[i] = col < kend ? (uint32_t)Map::row_of(wid, i, lane) * rowbytes_w + (uint32_t)col * 2u
+                          : kOobOffset;
     }
   }
-  template <bool SKIP>
+  template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < DA) {
-      da.template issue_one<SKIP>(rsA, kt, N, t, wid, j);
+      da.template issue_one<SKIP, CHECKED>(rsA, kt, N, t, wid, j);
     } else {
       const int i = j - DA;
-      const int n = kt * BK + Map::row_of(wid, i, lane);
-      const uint32_t off = (n < N && bcol[i] != kOobOffset) ? (uint32_t)n * rowbytes_w + bcol[i]
-                                                            : kOobOffset;
-      dma16(rsW, off, t + OPND + Map::lds_of(wid, i));
+      if (CHECKED) {
+        const int n = kt * BK + Map::row_of(wid, i, lane);
+        const uint32_t off = (n < N && bcol[i] != kOobOffset)
+                                 ? (uint32_t)n * rowbytes_w + bcol[i]
+                                 : kOobOffset;
+        dma16(rsW, off, t + OPND + Map::lds_of(wid, i));
+      } else {
+        dma16_so(rsW, bvo[i], (uint32_t)(kt * BK) * rowbytes_w, t + OPND + Map::lds_of(wid, i));
+      }
     }
   }
   MOE_DEV void prefetch(int) {}
@@ -947,6 +992,7 @@ struct DwOp {
   using Map = MnmajMapT<NW>;
   static constexpr int PW = Map::PER_WAVE;  // dY (and x) instructions per wave per stage
   static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
+  static constexpr bool CHECKED_TAIL = false;  // offsets are data dependent every stage
   // per stage: PW dY + PW x instructions, the stage's routing weights, the
   // tokens of the stage two ahead
   static constexpr int DMA_PER_STAGE = 2 * PW + 1 + 1;
@@ -986,7 +1032,7 @@ struct DwOp {
     for (int i = 0; i < PW / 2; ++i)
       tq[i] = *(const i32x4 *)(lds + ring_off(kt) + wid * (8 * PW) + 16 * i);
   }
-  template <bool SKIP>
+  template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < 2 * PW) {

@@ -84,6 +84,9 @@ def _fwd(r, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     (257, 512, 264, 9, 3, True, (2, 3, 8)),
     (1030, 2048, 512, 8, 2, True, ()),
     (50, 40, 24, 4, 4, True, ()),
+    (333, 136, 200, 7, 2, True, (3,)),        # three stages, the last one partial
+    (129, 192, 128, 3, 1, True, ()),          # three whole stages
+    (90, 104, 72, 4, 2, True, ()),            # two stages, the last one partial
     (64, 30, 17, 5, 2, True, (1,)),           # vector ALU path for bf16
 ])
 def test_fused_forward_small(T, K, N, E, k, bf16, empty):
@@ -173,6 +176,8 @@ def _bwd(r, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     (700, 256, 512, 5, 2, True, (0,)),
     (257, 512, 264, 9, 3, True, (2, 3, 8)),
     (600, 320, 1024, 4, 1, True, ()),
+    (333, 200, 136, 7, 2, True, (3,)),       # dX reduction: three stages, the last partial
+    (129, 128, 192, 3, 1, True, ()),         # dX reduction: three whole stages
     (64, 30, 17, 5, 2, True, (1,)),          # vector ALU path for bf16
 ])
 def test_backward_small(T, K, N, E, k, bf16, empty):
