@@ -665,6 +665,40 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
       // row tables; each row's base address is formed once for all column blocks
+      if (FUSED) {
+        // weighted scatter-combine: atomics on y with 32-bit byte offsets from
+        // its base; only live rows and columns are touched (the column test is
+        // left out when every column of the accumulator is live)
+        char *const yb = (char *)p.C;
+        const bool all_cols = ncols >= NIc * 32 * WGN;  // wave-uniform
+        uint32_t cb[NIc];
+#pragma unroll
+        for (int ni = 0; ni < NIc; ++ni)
+          cb[ni] = (uint32_t)(n0 + wn * 32 + ni * 32 * WGN + (lane & 31)) * 4u;
+        const int cl0 = wn * 32 + (lane & 31);
+#pragma unroll
+        for (int mi = 0; mi < MIc; ++mi) {
+          if (mi >= live_mi) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
+            const i32x4 t4 = *(const i32x4 *)(tok + rq);
+            const f32x4 w4 = *(const f32x4 *)(wgt + rq);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (t4[q] < 0) continue;
+              const uint32_t ro = (uint32_t)t4[q] * (uint32_t)N * 4u;
+#pragma unroll
+              for (int ni = 0; ni < NIc; ++ni) {
+                if (!all_cols && cl0 + ni * 32 * WGN >= ncols) continue;
+                unsafeAtomicAdd((float *)(yb + (ro + cb[ni])), w4[q] * acc[mi][ni][4 * j + q]);
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
 #pragma unroll
       for (int mi = 0; mi < MIc; ++mi) {
         if (mi >= live_mi) continue;
@@ -672,7 +706,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         for (int j = 0; j < 4; ++j) {
           const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
           const i32x4 t4 = *(const i32x4 *)(tok + rq);
-          const f32x4 w4 = *(const f32x4 *)(wgt + rq);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int t = t4[q];
@@ -684,9 +717,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
               if (cl >= ncols) continue;
               const int col = n0 + cl;
               const float v = acc[mi][ni][4 * j + q];
-              if (FUSED) {
-                unsafeAtomicAdd((float *)p.C + rowo + col, w4[q] * v);
-              } else if (sizeof(Tout) == 4) {
+              if (sizeof(Tout) == 4) {
                 ((float *)p.C)[rowo + col] = v;
               } else {
                 ((__bf16 *)p.C)[rowo + col] = (__bf16)v;
@@ -892,6 +923,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       // rq = wm*32 + mi*64 + 8j + 4*(lane/32); one transposing read of the K-major
       // x tile gives each lane exactly x at rows rq .. rq+3 of its column.
       const bool has_dw = p.d_w != nullptr, has_dx = p.dX != nullptr;
+      // dX scatter: atomics with 32-bit byte offsets from the base of dX, on
+      // live rows and columns only
+      char *const xb = (char *)p.dX;
+      uint32_t cb[NIc];
+#pragma unroll
+      for (int ni = 0; ni < NIc; ++ni)
+        cb[ni] = (uint32_t)(kc0 + wn * 32 + ni * 32 * WGN + (lane & 31)) * 4u;
 #pragma unroll
       for (int mi = 0; mi < MIc; ++mi) {
 #pragma unroll
@@ -913,16 +951,18 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
             }
           }
           float dwp[4] = {0.f, 0.f, 0.f, 0.f};
+          uint32_t ro[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) ro[q] = (uint32_t)t4[q] * (uint32_t)K * 4u;
 #pragma unroll
           for (int ni = 0; ni < NIc; ++ni) {
             const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
-            const int col = kc0 + cl;
             const bool cok = cl < ncols;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float g = cok ? acc[mi][ni][4 * j + q] : 0.f;  // dead columns may hold stale values
               if (has_dx && t4[q] >= 0 && cok)
-                unsafeAtomicAdd(p.dX + (size_t)t4[q] * K + col, w4[q] * g);
+                unsafeAtomicAdd((float *)(xb + (ro[q] + cb[ni])), w4[q] * g);
               if (has_dw) {
                 const float xv = __builtin_bit_cast(float, (uint32_t)(uint16_t)xq[ni][q] << 16);
                 dwp[q] = fmaf(g, xv, dwp[q]);  // masked rows / columns hold zeros
