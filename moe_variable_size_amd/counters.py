@@ -51,12 +51,15 @@ def _family(name: str):
 
 
 def per_launch_kib(run_dir: str, counter: str) -> dict:
-    """Average counter value per dispatch, per kernel family."""
+    """Average counter value per dispatch, per kernel family.  The calibration
+    ("copy") family keeps only the copy dispatches with the largest grid: the
+    256 MiB calibration copy, not the small copies of results to the host."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
     per_dispatch = defaultdict(float)
     fam_of = {}
+    copy_grid = {}
     for f in files:
         with open(f) as fh:
             for row in csv.DictReader(fh):
@@ -68,6 +71,14 @@ def per_launch_kib(run_dir: str, counter: str) -> dict:
                 key = (f, row["Dispatch_Id"])
                 per_dispatch[key] += float(row["Counter_Value"])
                 fam_of[key] = fam
+                if fam == "copy":
+                    copy_grid[key] = int(row["Grid_Size"])
+    if copy_grid:
+        big = max(copy_grid.values())
+        for key, g in copy_grid.items():
+            if g != big:
+                del per_dispatch[key]
+                del fam_of[key]
     sums, counts = defaultdict(float), defaultdict(int)
     for key, v in per_dispatch.items():
         sums[fam_of[key]] += v

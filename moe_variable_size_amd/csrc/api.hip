@@ -244,7 +244,8 @@ int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float
   if (!aligned(x, al) || !aligned(W, al) || !aligned(y, 4)) return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e =
-      timed(F_FILL, st, [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), st); });
+      timed(F_FILL, st,
+            [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st); });
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(timed(F_FWD, st, [&] {
     if (dtype == MOE_BF16 && mfma_supported((int)K, (int)N))
@@ -283,11 +284,11 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
   hipStream_t st = (hipStream_t)stream;
   const bool mfma = dtype == MOE_BF16 && mfma_supported((int)K, (int)N);
   hipError_t e = hipSuccess;
-  if (dX)
-    e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, (size_t)s.T * K * sizeof(float), st); });
-  if (e == hipSuccess && d_topk)
-    e = timed(F_FILL, st,
-              [&] { return launch_fill_zero(d_topk, (size_t)s.S * sizeof(float), st); });
+  if (dX || d_topk)  // both zeroed by one launch
+    e = timed(F_FILL, st, [&] {
+      return launch_fill_zero(dX, dX ? (size_t)s.T * K * sizeof(float) : 0, d_topk,
+                              d_topk ? (size_t)s.S * sizeof(float) : 0, st);
+    });
   if (e == hipSuccess && (dX || d_topk))
     e = timed(F_DX, st, [&] {
       return mfma ? mfma_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, st)

@@ -74,7 +74,10 @@ hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_s
 size_t schedule_scratch_bytes(int64_t S, int E);
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,
                            int32_t *total, int32_t *owner, int64_t owner_cap, hipStream_t st);
-hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st);
+// zero [p, p + bytes) and [p2, p2 + bytes2) in one launch (either pointer may be
+// NULL); 16-byte stores cover whole multiples of 16 bytes from each start (4-byte
+// aligned), byte stores the rest
+hipError_t launch_fill_zero(void *p, size_t bytes, void *p2, size_t bytes2, hipStream_t st);
 
 // fp32 / generic SIMT path
 hipError_t simt_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C,

@@ -284,12 +284,26 @@ __global__ void tile_map_kernel(const int32_t *__restrict__ bstart, int E, int t
   }
 }
 
-__global__ void fill_zero_kernel(uint4 *__restrict__ p, size_t n16, uint8_t *__restrict__ tail,
-                                 int ntail) {
+// Zero up to two byte ranges in one launch: 16-byte nontemporal stores over the
+// aligned part of each, then the bytes of each tail.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+struct FillRange {
+  u32x4_t *p;
+  size_t n16;
+  uint8_t *tail;
+  int ntail;
+};
+__global__ void fill_zero_kernel(FillRange a, FillRange b) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-    p[i] = make_uint4(0, 0, 0, 0);
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n16 + b.n16; i += stride) {
+    if (i < a.n16)
+      __builtin_nontemporal_store(z, a.p + i);
+    else
+      __builtin_nontemporal_store(z, b.p + (i - a.n16));
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < a.ntail) a.tail[threadIdx.x] = 0;
+  if (blockIdx.x == 0 && (int)threadIdx.x < b.ntail) b.tail[threadIdx.x] = 0;
 }
 
 }  // namespace
@@ -349,15 +363,19 @@ hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t
   return hipGetLastError();
 }
 
-hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t st) {
-  if (bytes == 0) return hipSuccess;
-  const size_t n16 = bytes / 16;
-  const int ntail = (int)(bytes - n16 * 16);
-  int blocks = (int)((n16 + 255) / 256);
+hipError_t launch_fill_zero(void *p, size_t bytes, void *p2, size_t bytes2, hipStream_t st) {
+  if (!p) bytes = 0;
+  if (!p2) bytes2 = 0;
+  if (bytes + bytes2 == 0) return hipSuccess;
+  auto range = [](void *q, size_t n) {
+    const size_t n16 = n / 16;
+    return FillRange{(u32x4_t *)q, n16, (uint8_t *)q + n16 * 16, (int)(n - n16 * 16)};
+  };
+  const FillRange a = range(p, bytes), b = range(p2, bytes2);
+  int blocks = (int)((a.n16 + b.n16 + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, (uint4 *)p, n16,
-                     (uint8_t *)p + n16 * 16, ntail);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, st, a, b);
   return hipGetLastError();
 }
 

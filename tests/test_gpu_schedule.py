@@ -75,16 +75,19 @@ def test_schedule_workloads(cfg):
     _check_contiguous(r.expert_ids, r.topk_weights, r.E, r.name)
 
 
-@pytest.mark.parametrize("cap,seed", [(64, None), (3, 1), (1, 2), (200, 3)])
-def test_schedule_masked(cap, seed):
+# (cap, seed, T): random ids with k = 4; T = 9000 spans many builder blocks and
+# overflows the capacity of most experts
+@pytest.mark.parametrize("cap,seed,T", [(64, None, 0), (3, 1, 97), (1, 2, 97), (200, 3, 97),
+                                        (500, 4, 9000)])
+def test_schedule_masked(cap, seed, T):
     if seed is None:
         r = WL.config5(dense=False)
         ids, w, E = r.expert_ids, r.topk_weights, r.E
     else:
         rng = np.random.default_rng(seed)
-        E = 11
-        ids = rng.integers(-1, E, size=(97, 4)).astype(np.int32)
-        w = rng.random((97, 4)).astype(np.float32)
+        E = 11 if T < 1000 else 70
+        ids = rng.integers(-1, E, size=(T, 4)).astype(np.int32)
+        w = rng.random((T, 4)).astype(np.float32)
     log(f"schedule masked: cap={cap} E={E} T={ids.shape[0]}")
     sch = api.moe_build_schedule(dev(ids), dev(w), E, layout=api.MOE_LAYOUT_MASKED, capacity=cap)
     torch.cuda.synchronize()
