@@ -538,6 +538,80 @@ struct MnmajMapT {
 };
 using MnmajMap = MnmajMapT<4>;
 
+// ---- deep pipeline for streaming tiles ----------------------------------------
+// A 64-row masked-decode tile streams its weights through HBM and does few
+// MFMAs per stage: its speed is the number of bytes in flight.  It keeps
+// NSTAGES stages in flight in a compact LDS layout (stage s at s * STAGE_BYTES,
+// B at + A_BYTES) and runs a plain loop per stage: wait for the stage, barrier,
+// refill the buffer just released with the stage NSTAGES-1 ahead, multiply.
+// (Sub-tiles of a last partial round gain nothing from it: their time per
+// stage is the barrier and the read -> MFMA chain, not the DMA.)
+
+// wait until at most n vector-memory operations are outstanding (n >= 16: all)
+MOE_DEV void wait_vmcnt_upto(int n) {
+  switch (n) {
+#define MOE_W(c) \
+  case c:        \
+    wait_vmcnt<c>(); \
+    break;
+    MOE_W(1) MOE_W(2) MOE_W(3) MOE_W(4) MOE_W(5) MOE_W(6) MOE_W(7) MOE_W(8)
+    MOE_W(9) MOE_W(10) MOE_W(11) MOE_W(12) MOE_W(13) MOE_W(14) MOE_W(15)
+#undef MOE_W
+    default:
+      wait_vmcnt<0>();
+  }
+}
+
+// Op supplies STAGE_BYTES, A_BYTES, NSTAGES, DMA_PER_STAGE and
+// issue_part<SKIP, CHECKED>(kt, buf, j) with SKIP always on; `parts` is the
+// number of DMA instructions this wave issues per stage (fixed for the tile,
+// as the rows it skips are).  Only the range's last stage is bounds-checked.
+template <int MI, int NI, int WGM, int WGN, class Op>
+MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
+                                int live_mi, int parts, f32x16 (&acc)[MI][NI]) {
+  constexpr int NS = Op::NSTAGES, D = Op::DMA_PER_STAGE;
+  auto issue = [&](int kt) __attribute__((always_inline)) {
+    const int buf = (kt - kb) % NS;
+    if (kt == ke - 1) {
+#pragma unroll
+      for (int j = 0; j < D; ++j) op.template issue_part<true, true>(kt, buf, j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < D; ++j) op.template issue_part<true, false>(kt, buf, j);
+    }
+  };
+  const int pro = min(NS - 1, ke - kb);
+  for (int s = 0; s < pro; ++s) issue(kb + s);
+  for (int kt = kb; kt < ke; ++kt) {
+    const int buf = (kt - kb) % NS;
+    // stages issued after kt: kt+1 .. min(kt+NS-2, ke-1)
+    wait_vmcnt_upto(min(NS - 2, ke - 1 - kt) * parts);
+    wait_lgkm0();
+    barrier();  // stage kt in LDS for every wave; the buffer of stage kt-1 is free
+    if (kt + NS - 1 < ke) issue(kt + NS - 1);
+    const char *As = lds + buf * Op::STAGE_BYTES;
+    const char *Bs = As + Op::A_BYTES;
+#pragma unroll
+    for (int step = 0; step < KS; ++step) {
+      bf16x8_t fa[MI], fb[NI];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        fa[mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+        fb[ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        if (mi >= live_mi) continue;  // wave-uniform
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // ============================================================================
 // Forward-shaped kernel: out[r, n] = sum_k A[src(r), k] * W[g, n, k].
 //   FUSED: src(r) = row_to_token[r], y[src(r), n] += row_weight[r] * acc
@@ -581,6 +655,39 @@ struct FwdOp {
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
+};
+
+// A (BM rows) and B (BN rows) K-major for the deep pipeline of small tiles.
+template <int BM, int BN, int NW>
+struct FwdDeepOp {
+  static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
+  static_assert(DA >= 1 && DB >= 1, "at least one DMA row group per wave");
+  static constexpr int DMA_PER_STAGE = DA + DB;
+  static constexpr int A_BYTES = BM * KROW, STAGE_BYTES = (BM + BN) * KROW;
+  static constexpr int NSTAGES = NSTAGE * STAGE / STAGE_BYTES > 6 ? 6 : NSTAGE * STAGE / STAGE_BYTES;
+  static_assert(NSTAGES >= 2, "two stages at least");
+  KmajDma<BM, NW> da;
+  KmajDma<BN, NW> db;
+  __amdgpu_buffer_rsrc_t rsA, rsW;
+  uint32_t lds0;
+  int K, wid;
+  template <bool SKIP, bool CHECKED>
+  MOE_DEV void issue_part(int kt, int buf, int j) {
+    const uint32_t t = lds0 + (uint32_t)(buf * STAGE_BYTES);
+    if (j < DA)
+      da.template issue_one<SKIP, CHECKED>(rsA, kt, K, t, wid, j);
+    else
+      db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + A_BYTES, wid, j - DA);
+  }
+  // DMA instructions this wave issues per stage (the others cover dead rows)
+  MOE_DEV int parts() const {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < DA; ++i) n += (wid * DA + i) * 8 < da.live_rows ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < DB; ++i) n += (wid * DB + i) * 8 < db.live_rows ? 1 : 0;
+    return n;
+  }
 };
 
 template <int BM, int BN, int WGM, int WGN, bool FUSED, typename Tout>
@@ -649,8 +756,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     // The tile body, instantiated per accumulator shape: MIc x NIc blocks per
     // wave (a whole tile, or a 128 x 128 / 64 x 128 sub-tile), each with its own
     // accumulators.  SKM: MFMAs of row blocks past the last live row are left
-    // out (wave-uniform, masked decode); DSK: DMA of dead rows is left out.
-    auto tile = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_) __attribute__((always_inline)) {
+    // out (wave-uniform, masked decode); DSK: DMA of dead rows is left out;
+    // DEEP: the streaming pipeline with more stages in flight (masked decode).
+    auto tile = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_, auto DEEP_)
+                    __attribute__((always_inline)) {
       constexpr int MIc = decltype(MIc_)::value, NIc = decltype(NIc_)::value;
       constexpr bool SKM = decltype(SKM_)::value, DSK = decltype(DSK_)::value;
       const int live_mi =
@@ -660,8 +769,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       for (int mi = 0; mi < MIc; ++mi)
 #pragma unroll
         for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
-      tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW>, DSK>(op, lds, kb, ke, wm, wn, lane,
-                                                                     live_mi, NIc, acc);
+      if constexpr (decltype(DEEP_)::value) {
+        constexpr int BMs = MIc * 32 * WGM, BNs = NIc * 32 * WGN;  // rows of A and of B
+        FwdDeepOp<BMs, BNs, NW> dop;
+        dop.rsA = op.rsA;
+        dop.rsW = op.rsW;
+        dop.lds0 = op.lds0;
+        dop.K = K;
+        dop.wid = wid;
+        dop.da.setup(wid, lane, rowoff_a, c.rows);
+        dop.db.setup(wid, lane, rowoff_b, ncols);
+        tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi,
+                                               dop.parts(), acc);
+      } else {
+        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW>, DSK>(op, lds, kb, ke, wm, wn,
+                                                                       lane, live_mi, NIc, acc);
+      }
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
       // row tables; each row's base address is formed once for all column blocks
@@ -732,17 +855,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     using std::false_type;
     using std::true_type;
     if constexpr (BM <= 64) {
-      tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(), true_type());
+      tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(), true_type(),
+           true_type());
     } else {
       // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
       constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
       if (ws.nS == 8)
-        tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(), true_type());
+        tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(), true_type(),
+             false_type());
       else if (ws.nS == 4)
-        tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(), true_type());
+        tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(), true_type(),
+             false_type());
       else
         tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
-             false_type());
+             false_type(), false_type());
     }
   }
 }

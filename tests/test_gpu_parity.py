@@ -87,6 +87,7 @@ def _fwd(r, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     (333, 136, 200, 7, 2, True, (3,)),        # three stages, the last one partial
     (129, 192, 128, 3, 1, True, ()),          # three whole stages
     (90, 104, 72, 4, 2, True, ()),            # two stages, the last one partial
+    (1030, 512, 768, 8, 2, True, ()),         # 48 tiles: 128 x 128 sub-tiles of the last round
     (64, 30, 17, 5, 2, True, (1,)),           # vector ALU path for bf16
 ])
 def test_fused_forward_small(T, K, N, E, k, bf16, empty):
