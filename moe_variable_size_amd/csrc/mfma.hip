@@ -161,10 +161,13 @@ MOE_DEV int logical_block() {
 
 // Work split of `total` tiles of KI stages over G workgroups.  Whole tiles go
 // out in rounds of G (workgroup Lb takes tiles Lb, Lb + G, ...).  The tiles of
-// the last partial round are then either
-//   * cut into S sub-tiles each (S = 2..16, rows and columns split, at most
+// the last partial round are either
+//   * cut into S sub-tiles each (S = 4 or 8, rows and columns split, at most
 //     one sub-tile per workgroup), so no workgroup idles for a whole tile time
-//     and every output element is still produced by exactly one workgroup; or
+//     and every output element is still produced by exactly one workgroup; a
+//     workgroup runs its sub-tile BEFORE its whole tiles, so the sub-tile's
+//     scatter drains while the whole tiles multiply (run after them, it would
+//     wait behind the whole tiles' atomics, which retire in order); or
 //   * (stream_k) split along the reduction over all G workgroups.
 struct WorkSplit {
   int64_t it, it_end, tail0, tot;
@@ -207,6 +210,16 @@ struct WorkSplit {
     if (!sk) {
       kb = 0;
       ke = KI;
+      // a workgroup's piece of the last round comes first: its few atomics
+      // drain while the whole tiles multiply, instead of queueing behind them
+      if (!piece_done && Lb < pieces) {
+        piece_done = true;
+        tau = full + Lb / S;
+        s = Lb % S;
+        nS = S;
+        return true;
+      }
+      piece_done = true;
       if (next_tile < full) {
         tau = next_tile;
         next_tile += G;
@@ -214,12 +227,7 @@ struct WorkSplit {
         nS = 1;
         return true;
       }
-      if (piece_done || Lb >= pieces) return false;
-      piece_done = true;
-      tau = full + Lb / S;
-      s = Lb % S;
-      nS = S;
-      return true;
+      return false;
     }
     while (it >= it_end) {
       if (it_end <= tail0 && it_end + (int64_t)(G - 1) * KI < tail0) {
