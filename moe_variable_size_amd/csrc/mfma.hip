@@ -177,7 +177,7 @@ struct WorkSplit {
   bool piece_done;
   int s, nS;  // sub-tile of the current piece (0 of 1 for a whole tile)
   enum { WHOLE = 0, SUBTILE_TAIL = 1, STREAM_K = 2 };
-  MOE_DEV void init(int total, int KI_, int G_, int Lb_, int mode) {
+  MOE_DEV void init(int total, int KI_, int G_, int Lb_, int mode, int max_split = 8) {
     KI = KI_;
     G = G_;
     Lb = Lb_;
@@ -188,7 +188,10 @@ struct WorkSplit {
       full = (total / G) * G;
       const int rem = total - full;
       S = 1;
-      if (mode == SUBTILE_TAIL && rem > 0) S = rem * 8 <= G ? 8 : (rem * 4 <= G ? 4 : 1);
+      if (mode == SUBTILE_TAIL && rem > 0)
+        S = (max_split >= 8 && rem * 8 <= G) ? 8
+            : (max_split >= 4 && rem * 4 <= G) ? 4
+            : (max_split >= 2 && rem * 2 <= G) ? 2 : 1;
       pieces = rem * S;
       next_tile = Lb;
       piece_done = false;
@@ -249,11 +252,12 @@ struct WorkSplit {
   }
 };
 
-// Sub-tile s of nS (4: 128 x 128, 8: 64 x 128) of a 256 x 256 tile.
+// Sub-tile s of nS (2: 128 x 256, 4: 128 x 128, 8: 64 x 128) of a 256 x 256 tile.
 struct SubTile {
   int r0, c0, rows, cols;  // offsets inside the tile and extents
 };
 MOE_DEV SubTile sub_tile(int s, int nS) {
+  if (nS == 2) return SubTile{s * 128, 0, 128, 256};
   const int rows = nS == 8 ? 64 : 128, cols = 128;
   return SubTile{(s >> 1) * rows, (s & 1) * cols, rows, cols};
 }
@@ -639,6 +643,7 @@ struct FwdArgs {
   int E, layout, capacity, K, N;
   uint32_t a_bytes;  // bytes of A (x or the bare A)
   int stream_k;      // 1: split the last partial wave of tiles along K
+  int tail_split;    // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int M;             // bare: rows of A and C (rows at or past M are never touched)
 };
 
@@ -733,7 +738,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   const int Lb = logical_block();
   WorkSplit ws;
   ws.init(total, KI, gridDim.x, Lb,
-          p.stream_k ? WorkSplit::STREAM_K : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE));
+          p.stream_k ? WorkSplit::STREAM_K : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE), p.tail_split);
   int tau, kb, ke;
   while (ws.next(tau, kb, ke)) {
     TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
@@ -874,6 +879,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       else if (ws.nS == 4)
         tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(), true_type(),
              false_type());
+      else if (ws.nS == 2)
+        tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(), true_type(),
+             false_type());
       else
         tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
              false_type(), false_type());
@@ -907,6 +915,7 @@ struct DxArgs {
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes;
   int stream_k;
+  int tail_split;  // largest split of a tile of the last partial round (8, 4, 2 or 1)
 };
 
 template <int NW>
@@ -987,7 +996,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 
   const int Lb = logical_block();
   WorkSplit ws;
-  ws.init(total, KI, gridDim.x, Lb, p.stream_k ? WorkSplit::STREAM_K : WorkSplit::SUBTILE_TAIL);
+  ws.init(total, KI, gridDim.x, Lb, p.stream_k ? WorkSplit::STREAM_K : WorkSplit::SUBTILE_TAIL,
+          p.tail_split);
   int tau, kb, ke;
   while (ws.next(tau, kb, ke)) {
     TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
@@ -1127,6 +1137,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       tile(integral_constant<int, R8>(), integral_constant<int, C>(), std::true_type());
     else if (ws.nS == 4)
       tile(integral_constant<int, R4>(), integral_constant<int, C>(), std::true_type());
+    else if (ws.nS == 2)
+      tile(integral_constant<int, R4>(), integral_constant<int, NI>(), std::true_type());
     else
       tile(integral_constant<int, MI>(), integral_constant<int, NI>(), std::false_type());
   }
@@ -1357,6 +1369,17 @@ int stream_k_mode() {
   return v;
 }
 
+// MOE_VS_TAIL_SPLIT=n: largest split (8, 4, 2, 1) of a tile of the last
+// partial round of the forward and input-gradient kernels (read once)
+int tail_split() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_TAIL_SPLIT");
+    const int n = e ? atoi(e) : 8;
+    return (n == 1 || n == 2 || n == 4 || n == 8) ? n : 8;
+  }();
+  return v;
+}
+
 // MOE_VS_DX_WAVES=8: input-gradient kernel with 8 waves per workgroup instead of
 // 4 (its routing-weight epilogue runs short of registers with 8)
 int dx_waves() {
@@ -1412,7 +1435,7 @@ hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
 hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int M,
                              int K, int N, int E, int out_dtype, hipStream_t st) {
   FwdArgs a{(const bf16_t *)A, (const bf16_t *)W, C, offsets, nullptr, nullptr, nullptr, nullptr,
-            E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), 0, M};
+            E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), 0, tail_split(), M};
   if (out_dtype == MOE_F32) return launch_fwd256<false, float>(a, st);
   return launch_fwd256<false, bf16_t>(a, st);
 }
@@ -1421,7 +1444,7 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
                           int N, hipStream_t st) {
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), (int)s.T};
+            (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split(), (int)s.T};
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
     a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
@@ -1441,7 +1464,7 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
            s.counts, s.block_start + bm_index(BM) * (s.E + 1), s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
-           (uint32_t)((size_t)s.T * K * 2), stream_k_mode()};
+           (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split()};
   const dim3 grid(device_cu_count());
   if (dx_waves() == 4) {
     hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);

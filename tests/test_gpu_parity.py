@@ -88,6 +88,7 @@ def _fwd(r, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     (129, 192, 128, 3, 1, True, ()),          # three whole stages
     (90, 104, 72, 4, 2, True, ()),            # two stages, the last one partial
     (1030, 512, 768, 8, 2, True, ()),         # 48 tiles: 128 x 128 sub-tiles of the last round
+    (2000, 256, 1536, 8, 2, True, ()),        # 96 tiles: 128 x 256 sub-tiles of the last round
     (64, 30, 17, 5, 2, True, (1,)),           # vector ALU path for bf16
 ])
 def test_fused_forward_small(T, K, N, E, k, bf16, empty):
@@ -179,6 +180,7 @@ def _bwd(r, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     (600, 320, 1024, 4, 1, True, ()),
     (333, 200, 136, 7, 2, True, (3,)),       # dX reduction: three stages, the last partial
     (129, 128, 192, 3, 1, True, ()),         # dX reduction: three whole stages
+    (2000, 1536, 256, 8, 2, True, ()),       # 96 dX tiles: 128 x 256 sub-tiles of the last round
     (64, 30, 17, 5, 2, True, (1,)),          # vector ALU path for bf16
 ])
 def test_backward_small(T, K, N, E, k, bf16, empty):
