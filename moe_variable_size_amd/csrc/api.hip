@@ -284,21 +284,25 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
   hipStream_t st = (hipStream_t)stream;
   const bool mfma = dtype == MOE_BF16 && mfma_supported((int)K, (int)N);
   hipError_t e = hipSuccess;
-  if (dX || d_topk)  // both zeroed by one launch
-    e = timed(F_FILL, st, [&] {
-      return launch_fill_zero(dX, dX ? (size_t)s.T * K * sizeof(float) : 0, d_topk,
-                              d_topk ? (size_t)s.S * sizeof(float) : 0, st);
+  const size_t dx_bytes = dX ? (size_t)s.T * K * sizeof(float) : 0;
+  const size_t dt_bytes = d_topk ? (size_t)s.S * sizeof(float) : 0;
+  // On the matrix-core path the weight gradient runs first and zeroes dX and
+  // d_topk on the side (it reads neither); the kernel boundary orders those
+  // stores before the input-gradient kernel's atomics.  Otherwise one fill.
+  const bool dw_first = mfma && dW != nullptr;
+  if (dw_first)
+    e = timed(F_DW, st, [&] {
+      return mfma_bwd_dw(dY, x, s, dW, (int)K, (int)N, dX, dx_bytes, d_topk, dt_bytes, st);
     });
+  else if (dX || d_topk)
+    e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, dx_bytes, d_topk, dt_bytes, st); });
   if (e == hipSuccess && (dX || d_topk))
     e = timed(F_DX, st, [&] {
       return mfma ? mfma_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, st)
                   : simt_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, dtype, st);
     });
-  if (e == hipSuccess && dW)
-    e = timed(F_DW, st, [&] {
-      return mfma ? mfma_bwd_dw(dY, x, s, dW, (int)K, (int)N, st)
-                  : simt_bwd_dw(dY, x, s, dW, (int)K, (int)N, dtype, st);
-    });
+  if (e == hipSuccess && dW && !dw_first)
+    e = timed(F_DW, st, [&] { return simt_bwd_dw(dY, x, s, dW, (int)K, (int)N, dtype, st); });
   return hip_status(e);
 }
 

@@ -98,8 +98,10 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
                           int N, hipStream_t st);
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, hipStream_t st);
+// zero0 / zero1: byte ranges the kernel zeroes on the side (NULL / 0 when unused)
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
-                       int N, hipStream_t st);
+                       int N, float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
+                       hipStream_t st);
 }  // namespace moe
 
 namespace moe {

@@ -1171,7 +1171,29 @@ struct DwArgs {
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes, rw_bytes;
   int weighted;
+  // zeroed by the kernel on the side (the accumulation targets of the input
+  // gradient kernel that runs after it): byte ranges, NULL / 0 when unused
+  float *zero0;
+  size_t zero0_bytes;
+  float *zero1;
+  size_t zero1_bytes;
 };
+
+// Zero [p, p + bytes) with this workgroup's share of 16-byte nontemporal
+// stores (workgroup Lb of G takes chunks Lb*NTH + tid, stepping G*NTH) and the
+// trailing bytes from workgroup 0.  p is 4-byte aligned (dword stores).
+template <int NTH>
+MOE_DEV void zero_share(float *p, size_t bytes, int Lb, int G) {
+  if (!p || bytes == 0) return;
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const size_t n16 = bytes / 16;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  u32x4_t *q = (u32x4_t *)p;
+  for (size_t i = (size_t)Lb * NTH + threadIdx.x; i < n16; i += (size_t)G * NTH)
+    __builtin_nontemporal_store(z, q + i);
+  const size_t tail = bytes - n16 * 16;  // multiple of 4
+  if (Lb == 0 && threadIdx.x < tail / 4) p[n16 * 4 + threadIdx.x] = 0.f;
+}
 
 template <int NW>
 struct DwOp {
@@ -1280,6 +1302,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   const int per_e = tn * tk;
   const int units = E * per_e;
   const int G = gridDim.x, L = logical_block();
+  // the next kernel's accumulation targets, zeroed while this one runs
+  zero_share<NW * 64>(p.zero0, p.zero0_bytes, L, G);
+  zero_share<NW * 64>(p.zero1, p.zero1_bytes, L, G);
   DwOp<NW> op;
   op.rsY = uniform_rsrc(p.dY, p.dy_bytes);
   op.rsX = uniform_rsrc(p.x, p.x_bytes);
@@ -1479,11 +1504,12 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
 }
 
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
-                       int N, hipStream_t st) {
+                       int N, float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
+                       hipStream_t st) {
   DwArgs a{(const bf16_t *)dY, (const bf16_t *)x, dW, s.offsets, s.counts, s.expert_order,
            s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
            (uint32_t)((size_t)s.T * N * 2), (uint32_t)((size_t)s.T * K * 2),
-           (uint32_t)((size_t)s.R * 4), 1};
+           (uint32_t)((size_t)s.R * 4), 1, zero0, zero0_bytes, zero1, zero1_bytes};
   if (dw_waves() == 4) {
     constexpr size_t lds = DwOp<4>::LDS_BYTES;
     hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 4>>(lds);

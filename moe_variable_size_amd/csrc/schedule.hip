@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
   extern __shared__ int hist[];  // [kBlkWaves][E]: per-wave counts, then running bases
   const int tid = threadIdx.x, b = blockIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wid = tid / kWave;
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const bool masked = layout == MOE_LAYOUT_MASKED;
   for (int i = tid; i < kBlkWaves * E; i += kBlkThreads) hist[i] = 0;
