@@ -325,8 +325,115 @@ def masked_forward(x, W, ms: MaskedSchedule, T: int, *, acc=np.float64) -> np.nd
 
 
 # ----------------------------------------------------------------------------
+# Gated expert FFN ([GG] "Choosing an implementation": the gated FFN's two
+# up-projections, gate and up, form one grouped GEMM with the output width
+# doubled, and the activation belongs in that GEMM's epilogue)
+#
+# Readings (the page names neither the activation nor the weight layout):
+#   * the activation is SiLU on the gate times the up projection,
+#     h = silu(x W_gate^T) * (x W_up^T), silu(z) = z / (1 + exp(-z));
+#   * the doubled weight is W_gu [E, 2F, K]: rows 0 .. F-1 are the gate
+#     projection, rows F .. 2F-1 the up projection;
+#   * the down projection W_down [E, N, F] is the fused forward of the layer
+#     applied to h: y[t] = sum_j w[t, j] * h[s] W_down[e]^T with s = t*k + j.
+# ----------------------------------------------------------------------------
+def silu(z):
+    """SiLU (sigmoid-weighted linear unit): z / (1 + exp(-z)), in float64."""
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def gated_activation(gu, *, acc=np.float64):
+    """h = silu(gate) * up for a row block gu = [gate | up] of width 2F."""
+    F = gu.shape[1] // 2
+    return (silu(gu[:, :F]) * np.asarray(gu[:, F:], dtype=np.float64)).astype(acc)
+
+
+def gated_ffn_forward(x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=np.float64):
+    """Fused gated expert FFN: for each expert, gather its token rows, run the
+    doubled up-projection, apply silu(gate) * up, project down and add the
+    routing-weighted result into each token's output row.  Returns y [T, N]."""
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.reshape(-1)
+    wflat = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    N = W_down.shape[1]
+    y = np.zeros((T, N), dtype=acc)
+    for e in range(E):
+        s_e = np.nonzero(ids == e)[0]
+        if s_e.size == 0:
+            continue
+        tok = s_e // k
+        gu = np.asarray(x)[tok].astype(acc) @ W_gu[e].astype(acc).T
+        z = gated_activation(gu, acc=acc) @ W_down[e].astype(acc).T
+        we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
+        np.add.at(y, tok, we[:, None] * z)
+    return y
+
+
+def gated_intermediate(x, W_gu, expert_ids, E: int, *, acc=np.float64) -> np.ndarray:
+    """The intermediate h [R, F] in the routing schedule's row order (the
+    explicit path: gather the token copies, one grouped GEMM over the doubled
+    weights, then the activation).  Rows past the routed rows stay zero."""
+    sch = routing_schedule(expert_ids, None, E)
+    xs = np.asarray(x)[sch.row_to_token]
+    gu = grouped_gemm(xs, W_gu, sch.offsets, acc=acc)
+    h = np.zeros((np.asarray(expert_ids).size, W_gu.shape[1] // 2), dtype=acc)
+    h[:xs.shape[0]] = gated_activation(gu, acc=acc)
+    return h
+
+
+def gated_ffn_forward_explicit(x, W_gu, W_down, expert_ids, topk_weights, E: int, *,
+                               acc=np.float64) -> np.ndarray:
+    """Unfused gated FFN: h in schedule row order, the bare grouped GEMM with the
+    down weights, then the weighted un-permute ([NOTE] 4.3)."""
+    sch = routing_schedule(expert_ids, topk_weights, E)
+    h = gated_intermediate(x, W_gu, expert_ids, E, acc=acc)[:sch.row_to_token.size]
+    z = grouped_gemm(h, W_down, sch.offsets, acc=acc)
+    y = np.zeros((np.asarray(x).shape[0], W_down.shape[1]), dtype=acc)
+    np.add.at(y, sch.row_to_token, sch.row_weight.astype(acc)[:, None] * z)
+    return y
+
+
+def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.float64):
+    """Gated FFN on the masked layout.  Returns (y [T, N], h [E*capacity, F]);
+    h rows of empty slots are zero (the library leaves them unwritten)."""
+    F = W_gu.shape[1] // 2
+    y = np.zeros((T, W_down.shape[1]), dtype=acc)
+    h = np.zeros((ms.E * ms.capacity, F), dtype=acc)
+    for e in range(ms.E):
+        m = int(ms.masked_m[e])
+        if m == 0:
+            continue
+        tok = ms.slot_token[e, :m]
+        he = gated_activation(np.asarray(x)[tok].astype(acc) @ W_gu[e].astype(acc).T, acc=acc)
+        h[e * ms.capacity:e * ms.capacity + m] = he
+        z = he @ W_down[e].astype(acc).T
+        np.add.at(y, tok, ms.slot_weight[e, :m].astype(acc)[:, None] * z)
+    return y, h
+
+
+# ----------------------------------------------------------------------------
 # Sampled evaluation for full-size parity checks
 # ----------------------------------------------------------------------------
+def gated_ffn_rows(x, W_gu, W_down, expert_ids, topk_weights, tokens, *, acc=np.float64):
+    """y[t, :] of the gated FFN for the listed tokens only, from the definition
+    y[t] = sum_j w[t, j] * W_down[e] (silu(W_gate[e] x[t]) * (W_up[e] x[t]))."""
+    expert_ids = np.asarray(expert_ids)
+    F = W_gu.shape[1] // 2
+    out = np.zeros((len(tokens), W_down.shape[1]), dtype=acc)
+    for i, t in enumerate(tokens):
+        xt = np.asarray(x)[t].astype(acc)
+        for j in range(expert_ids.shape[1]):
+            e = int(expert_ids[t, j])
+            w = 1.0 if topk_weights is None else float(topk_weights[t, j])
+            gu = W_gu[e].astype(acc) @ xt
+            h = (silu(gu[:F]) * gu[F:]).astype(acc)
+            out[i] += acc(w) * (W_down[e].astype(acc) @ h)
+    return out
+
+
 def moe_forward_rows(x, W, expert_ids, topk_weights, tokens, *, acc=np.float64) -> np.ndarray:
     """y[t, :] for the listed tokens only, straight from the definition
     y[t] = sum_j w[t, j] * (x[t] @ W[ids[t, j]]^T)."""

@@ -87,8 +87,31 @@ def _bwd_dw_transposed_sum(dY, x, W, expert_ids, topk_weights, E, *, acc=np.floa
     return dX2, dW, d_w2                       # dW without the routing weight
 
 
+def _gated_swapped(gu, *, acc=np.float64):
+    F = gu.shape[1] // 2
+    return _ORIG["gated_activation"](np.concatenate([gu[:, F:], gu[:, :F]], axis=1), acc=acc)
+
+
+def _gated_sigmoid(gu, *, acc=np.float64):
+    F = gu.shape[1] // 2
+    g = np.asarray(gu[:, :F], dtype=np.float64)
+    return (1.0 / (1.0 + np.exp(-g)) * gu[:, F:]).astype(acc)   # sigmoid instead of silu
+
+
+def _gated_down_untransposed(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+    Wd = np.swapaxes(np.asarray(W_down), 1, 2)
+    if Wd.shape[2] != W_gu.shape[1] // 2:
+        raise ValueError("shape")
+    return _ORIG["gated_ffn_forward"](x, W_gu, Wd, expert_ids, topk_weights, E, acc=acc)
+
+
+def _gated_no_weight(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+    return _ORIG["gated_ffn_forward"](x, W_gu, W_down, expert_ids, None, E, acc=acc)
+
+
 _ORIG = {n: getattr(O, n) for n in ["routing_schedule", "tile_owner", "tile_coords", "moe_forward",
-                                     "grouped_gemm", "moe_backward"]}
+                                     "grouped_gemm", "moe_backward", "gated_activation",
+                                     "gated_ffn_forward"]}
 
 CASES = [
     ("end offsets replaced by start offsets", "routing_schedule", lambda: _mut_start_offsets(_ORIG["routing_schedule"]),
@@ -111,6 +134,14 @@ CASES = [
      [P.test_backward_finite_differences, P.test_backward_euler_identities]),
     ("weight gradient without the routing weight", "moe_backward", lambda: _bwd_dw_transposed_sum,
      [P.test_backward_finite_differences, P.test_backward_euler_identities]),
+    ("gate and up halves swapped", "gated_activation", lambda: _gated_swapped,
+     [P.test_gated_gate_and_up_halves, P.test_gated_ffn_reduces_to_dense_swiglu]),
+    ("sigmoid in place of silu", "gated_activation", lambda: _gated_sigmoid,
+     [P.test_gated_gate_and_up_halves, lambda: P.test_gated_ffn_brute_force(0)]),
+    ("down projection not transposed", "gated_ffn_forward", lambda: _gated_down_untransposed,
+     [P.test_gated_ffn_reduces_to_dense_swiglu, lambda: P.test_gated_ffn_brute_force(1)]),
+    ("gated routing weight dropped", "gated_ffn_forward", lambda: _gated_no_weight,
+     [P.test_gated_gate_and_up_halves, P.test_gated_ffn_homogeneity]),
 ]
 
 

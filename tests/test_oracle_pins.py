@@ -438,3 +438,162 @@ def test_masked_overflow_drops_latest_assignments():
     assert ms.n_dropped == 3       # s=4, 7 (expert 0) and s=6 (expert 1)
     assert ms.slot_token.tolist() == [[0, 1], [0, 2], [1, -1]]
     assert ms.slot_weight.tolist() == [[1, 1], [1, 1], [1, 0]]
+
+
+# ----------------------------------------------------------------------------
+# Gated expert FFN
+# ----------------------------------------------------------------------------
+def test_silu_against_library_and_closed_forms():
+    """silu(z) = z * expit(z) (scipy's logistic function); silu(0) = 0,
+    silu(1) = 1 / (1 + e^-1); it tends to z for large z and to 0 for very
+    negative z."""
+    from scipy.special import expit
+    z = np.linspace(-40.0, 40.0, 2001)
+    assert np.allclose(O.silu(z), z * expit(z), rtol=1e-14, atol=1e-300)
+    assert O.silu(0.0) == 0.0
+    assert abs(float(O.silu(1.0)) - 1.0 / (1.0 + math.exp(-1.0))) <= 1e-16
+    assert float(O.silu(800.0)) == 800.0
+    assert abs(float(O.silu(-800.0))) == 0.0
+
+
+def test_gated_ffn_reduces_to_dense_swiglu():
+    """E = 1, k = 1, weight 1: a dense gated MLP, computed with torch's own
+    SiLU in float64: y = (silu(x Wg^T) * (x Wu^T)) Wd^T."""
+    import torch
+    rng = np.random.default_rng(61)
+    T, K, F, N = 13, 11, 7, 5
+    x = rng.standard_normal((T, K))
+    Wgu = rng.standard_normal((1, 2 * F, K))
+    Wd = rng.standard_normal((1, N, F))
+    ids = np.zeros((T, 1), dtype=np.int32)
+    y = O.gated_ffn_forward(x, Wgu, Wd, ids, None, 1)
+    xt = torch.from_numpy(x)
+    g = xt @ torch.from_numpy(Wgu[0, :F]).T
+    u = xt @ torch.from_numpy(Wgu[0, F:]).T
+    ref = (torch.nn.functional.silu(g) * u) @ torch.from_numpy(Wd[0]).T
+    assert np.allclose(y, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_gated_gate_and_up_halves():
+    """x[:, 0] = 1 and x[:, 1] = v_t; the up rows select column 0 (u = 1), the
+    gate rows give g = a[e, f] * v_t, and W_down is the identity, so
+    y[t, f] = sum_j w[t, j] * silu(a[e_tj, f] * v_t) exactly (scipy's expit).
+    Swapping the gate and up halves gives silu(1) * g instead."""
+    from scipy.special import expit
+    rng = np.random.default_rng(62)
+    T, E, k, F = 17, 4, 2, 6
+    K = 3
+    v = rng.standard_normal(T) * 3
+    x = np.zeros((T, K))
+    x[:, 0] = 1.0
+    x[:, 1] = v
+    x[:, 2] = rng.standard_normal(T)          # never read by a nonzero weight
+    a = rng.standard_normal((E, F))
+    Wgu = np.zeros((E, 2 * F, K))
+    Wgu[:, :F, 1] = a
+    Wgu[:, F:, 0] = 1.0
+    Wd = np.broadcast_to(np.eye(F), (E, F, F)).copy()
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    w = rng.random((T, k))
+    y = O.gated_ffn_forward(x, Wgu, Wd, ids, w, E)
+    expect = np.zeros((T, F))
+    for t in range(T):
+        for j in range(k):
+            z = a[ids[t, j]] * v[t]
+            expect[t] += w[t, j] * z * expit(z)
+    assert np.allclose(y, expect, rtol=1e-13, atol=1e-13)
+
+
+def _brute_gated(x, Wgu, Wd, ids, w):
+    T, k = ids.shape
+    F = Wgu.shape[1] // 2
+    N = Wd.shape[1]
+    K = x.shape[1]
+    y = [[0.0] * N for _ in range(T)]
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            h = []
+            for f in range(F):
+                g = sum(float(x[t, c]) * float(Wgu[e, f, c]) for c in range(K))
+                u = sum(float(x[t, c]) * float(Wgu[e, F + f, c]) for c in range(K))
+                h.append(g / (1.0 + math.exp(-g)) * u)
+            for n in range(N):
+                y[t][n] += float(w[t, j]) * sum(h[f] * float(Wd[e, n, f]) for f in range(F))
+    return np.array(y)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gated_ffn_brute_force(seed):
+    """Plain Python loops on a tiny routed case with an empty expert and
+    F != N != K; the fused and the explicit oracle forms both match."""
+    rng = np.random.default_rng(70 + seed)
+    T, K, F, N, E, k = 5, 7, 3, 4, 3, 2
+    ids = np.array([rng.choice([0, 2], size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    Wgu = rng.standard_normal((E, 2 * F, K))
+    Wd = rng.standard_normal((E, N, F))
+    w = rng.random((T, k))
+    ref = _brute_gated(x, Wgu, Wd, ids, w)
+    for y in (O.gated_ffn_forward(x, Wgu, Wd, ids, w, E),
+              O.gated_ffn_forward_explicit(x, Wgu, Wd, ids, w, E),
+              O.gated_ffn_rows(x, Wgu, Wd, ids, w, range(T))):
+        assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_gated_intermediate_rows_brute_force():
+    """h row r belongs to the r-th assignment in (expert, s) order."""
+    rng = np.random.default_rng(75)
+    T, K, F, E, k = 6, 5, 4, 3, 2
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    Wgu = rng.standard_normal((E, 2 * F, K))
+    h = O.gated_intermediate(x, Wgu, ids, E)
+    order = sorted(range(T * k), key=lambda s: (ids.reshape(-1)[s], s))
+    for r, s in enumerate(order):
+        t, e = s // k, int(ids.reshape(-1)[s])
+        for f in range(F):
+            g = sum(x[t, c] * Wgu[e, f, c] for c in range(K))
+            u = sum(x[t, c] * Wgu[e, F + f, c] for c in range(K))
+            assert abs(h[r, f] - g / (1.0 + math.exp(-g)) * u) <= 1e-12 * max(1.0, abs(h[r, f]))
+
+
+def test_gated_ffn_homogeneity():
+    """y is linear in the up half, in W_down and in the routing weights (exact
+    under power-of-two scaling), but not in the gate half."""
+    rng = np.random.default_rng(77)
+    T, K, F, N, E, k = 9, 6, 5, 4, 3, 2
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    Wgu = rng.standard_normal((E, 2 * F, K))
+    Wd = rng.standard_normal((E, N, F))
+    w = rng.random((T, k))
+    y = O.gated_ffn_forward(x, Wgu, Wd, ids, w, E)
+    up2 = Wgu.copy()
+    up2[:, F:] *= 2
+    assert np.array_equal(O.gated_ffn_forward(x, up2, Wd, ids, w, E), 2 * y)
+    assert np.array_equal(O.gated_ffn_forward(x, Wgu, 4 * Wd, ids, w, E), 4 * y)
+    assert np.array_equal(O.gated_ffn_forward(x, Wgu, Wd, ids, 0.5 * w, E), 0.5 * y)
+    g2 = Wgu.copy()
+    g2[:, :F] *= 2
+    assert not np.allclose(O.gated_ffn_forward(x, g2, Wd, ids, w, E), 2 * y)
+
+
+def test_masked_gated_equals_contiguous_without_overflow():
+    rng = np.random.default_rng(79)
+    T, K, F, N, E, k = 20, 6, 5, 7, 6, 3
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    Wgu = rng.standard_normal((E, 2 * F, K))
+    Wd = rng.standard_normal((E, N, F))
+    w = rng.random((T, k))
+    ms = O.masked_schedule(ids, w, E, capacity=T)
+    y, h = O.masked_gated_ffn(x, Wgu, Wd, ms, T)
+    assert np.allclose(y, _brute_gated(x, Wgu, Wd, ids, w), rtol=1e-12, atol=1e-12)
+    hc = O.gated_intermediate(x, Wgu, ids, E)
+    sch = O.routing_schedule(ids, None, E)
+    for e in range(E):
+        m = int(ms.masked_m[e])
+        start = int(sch.starts[e])
+        assert np.array_equal(h[e * T:e * T + m], hc[start:start + m])
+        assert np.all(h[e * T + m:(e + 1) * T] == 0)
