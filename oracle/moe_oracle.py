@@ -417,6 +417,20 @@ def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.floa
 # ----------------------------------------------------------------------------
 # Sampled evaluation for full-size parity checks
 # ----------------------------------------------------------------------------
+def gated_intermediate_rows(x, W_gu, expert_ids, E: int, rows, *, acc=np.float64) -> np.ndarray:
+    """Rows of h [R, F] for the listed schedule rows only: row r is the r-th
+    assignment s in (expert, s) order, h[r] = silu(W_gate[e] x[t]) * (W_up[e] x[t])."""
+    sch = routing_schedule(expert_ids, None, E)
+    ids = np.asarray(expert_ids).reshape(-1)
+    F = W_gu.shape[1] // 2
+    out = np.zeros((len(rows), F), dtype=acc)
+    for i, r in enumerate(rows):
+        s = int(sch.perm[r])
+        gu = W_gu[int(ids[s])].astype(acc) @ np.asarray(x)[int(sch.row_to_token[r])].astype(acc)
+        out[i] = (silu(gu[:F]) * gu[F:]).astype(acc)
+    return out
+
+
 def gated_ffn_rows(x, W_gu, W_down, expert_ids, topk_weights, tokens, *, acc=np.float64):
     """y[t, :] of the gated FFN for the listed tokens only, from the definition
     y[t] = sum_j w[t, j] * W_down[e] (silu(W_gate[e] x[t]) * (W_up[e] x[t]))."""

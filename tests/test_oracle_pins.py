@@ -556,6 +556,8 @@ def test_gated_intermediate_rows_brute_force():
             g = sum(x[t, c] * Wgu[e, f, c] for c in range(K))
             u = sum(x[t, c] * Wgu[e, F + f, c] for c in range(K))
             assert abs(h[r, f] - g / (1.0 + math.exp(-g)) * u) <= 1e-12 * max(1.0, abs(h[r, f]))
+    sel = [0, 5, 11]
+    assert np.allclose(O.gated_intermediate_rows(x, Wgu, ids, E, sel), h[sel], rtol=1e-12, atol=1e-12)
 
 
 def test_gated_ffn_homogeneity():
