@@ -169,6 +169,32 @@ int grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, 
 int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float *y,
                   int64_t K, int64_t N, int32_t dtype, void *stream);
 
+/*
+ * Gated expert FFN forward ([GG] "Choosing an implementation": the gate and up
+ * projections run as one grouped GEMM over a weight with twice the output
+ * rows, with the activation in that GEMM's epilogue; the down projection is
+ * the fused forward above applied to the activation):
+ *     h[r, f] = silu(g) * u,  g = sum_k x[t_r, k] W_gu[e_r, f, k],
+ *                             u = sum_k x[t_r, k] W_gu[e_r, F + f, k],
+ *     y[t, n] = sum_j w[t, j] * sum_f h[r(t,j), f] * W_down[ids[t, j], n, f],
+ * with silu(z) = z / (1 + exp(-z)), r the schedule row of an assignment, t_r,
+ * e_r its token and expert.
+ *   x [T, K], W_gu [E, 2F, K] (rows 0..F-1 gate, F..2F-1 up) and
+ *   W_down [E, N, F]: bf16 only (MOE_ERR_DTYPE otherwise); K, F and N
+ *   multiples of 8 (MOE_ERR_SHAPE otherwise); x, W_gu, W_down and h 16-byte
+ *   aligned.
+ *   h [sched->R, F] bf16, written for every valid row of the schedule in
+ *   schedule row order (kept for a backward pass); rows of empty masked slots
+ *   and rows at or past offsets[E-1] are left untouched.  h is rounded to bf16
+ *   before the down projection.
+ *   y [T, N] float, OVERWRITTEN (zeroed by the call, then accumulated).
+ * Three launches on `stream`: the gated up-projection, the zeroing of y and
+ * the down projection.
+ */
+int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
+                      const moe_schedule *sched, void *h, float *y, int64_t K, int64_t F,
+                      int64_t N, int32_t dtype, void *stream);
+
 /* Bytes of device workspace moe_fused_bwd needs for these sizes (may be 0). */
 size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64_t N,
                                      int32_t dtype);
@@ -217,7 +243,8 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
  * Kernel timing for benchmarks.  While enabled, the library brackets every
  * kernel it launches with a pair of HIP events recorded on that launch's own
  * stream and keeps them per kernel family.  Families: "build_schedule",
- * "fill_zero", "grouped_gemm", "fused_fwd", "bwd_dx", "bwd_dw", "tile_map".
+ * "fill_zero", "grouped_gemm", "fused_fwd", "bwd_dx", "bwd_dw", "tile_map",
+ * "gated_up", "gated_down".
  *   moe_timing_enable(1) clears earlier records and starts recording;
  *   moe_timing_enable(0) stops recording (records are kept).
  *   moe_timing_read waits for the recorded events of `family` and returns the

@@ -178,6 +178,37 @@ def moe_fused_fwd(x: torch.Tensor, W: torch.Tensor, sched: Schedule, *,
     return y
 
 
+def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor, sched: Schedule, *,
+                      h: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Gated expert FFN forward: h = silu(x W_gate^T) * (x W_up^T) per schedule
+    row from one grouped GEMM over W_gu [E, 2F, K] (gate rows, then up rows),
+    then y = the weighted scatter-combine of h W_down^T, W_down [E, N, F]
+    ([GG] "Choosing an implementation").  Returns (y [T, N] float32,
+    h [R, F] bfloat16)."""
+    lib = _lib.load()
+    _require(x, "x", torch.bfloat16, 2)
+    _require(W_gu, "W_gu", torch.bfloat16, 3)
+    _require(W_down, "W_down", torch.bfloat16, 3)
+    T, K = x.shape
+    E, F2, K2 = W_gu.shape
+    E2, N, F = W_down.shape
+    if K2 != K or F2 != 2 * F or E2 != E or T != sched.c.T or E != sched.c.E:
+        raise ValueError("shape mismatch between x [T,K], W_gu [E,2F,K], W_down [E,N,F] and the schedule")
+    if h is None:
+        h = torch.empty((sched.c.R, F), dtype=torch.bfloat16, device=x.device)
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _require(h, "h", torch.bfloat16, 2)
+    _require(y, "y", torch.float32, 2)
+    if tuple(h.shape) != (sched.c.R, F) or tuple(y.shape) != (T, N):
+        raise ValueError("h must be [R, F] and y [T, N]")
+    st = lib.moe_gated_ffn_fwd(_ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c), _ptr(h),
+                               _ptr(y), K, F, N, MOE_BF16, _stream(stream))
+    _lib.check("moe_gated_ffn_fwd", st)
+    return y, h
+
+
 def moe_fused_bwd_workspace_bytes(sched: Schedule, K: int, N: int, dtype) -> int:
     return int(_lib.load().moe_fused_bwd_workspace_bytes(ctypes.byref(sched.c), K, N, _DTYPES[dtype]))
 

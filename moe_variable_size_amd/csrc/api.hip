@@ -105,7 +105,7 @@ bool fits(int64_t rows, int64_t cols, int32_t dtype) {
 
 // ---- kernel timing (benchmarks only) ---------------------------------------
 const char *const kFamilies[] = {"build_schedule", "fill_zero", "grouped_gemm", "fused_fwd",
-                                 "bwd_dx", "bwd_dw", "tile_map"};
+                                 "bwd_dx", "bwd_dw", "tile_map", "gated_up", "gated_down"};
 constexpr int kNumFamilies = sizeof(kFamilies) / sizeof(kFamilies[0]);
 
 struct Timing {
@@ -139,7 +139,7 @@ hipError_t timed(int fam, hipStream_t st, F &&f) {
   return e;
 }
 
-enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP };
+enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP, F_GATED_UP, F_GATED_DOWN };
 
 }  // namespace
 }  // namespace moe
@@ -249,9 +249,44 @@ int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(timed(F_FWD, st, [&] {
     if (dtype == MOE_BF16 && mfma_supported((int)K, (int)N))
-      return mfma_fused_fwd(x, W, s, y, (int)K, (int)N, st);
+      return mfma_fused_fwd(x, W, s, y, (int)K, (int)N, false, st);
     return simt_fused_fwd(x, W, s, y, (int)K, (int)N, dtype, st);
   }));
+}
+
+int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
+                      const moe_schedule *sched, void *h, float *y, int64_t K, int64_t F,
+                      int64_t N, int32_t dtype, void *stream) {
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  rc = check_dtype_dims(dtype, K, N);
+  if (rc) return rc;
+  if (F < 1) return MOE_ERR_SHAPE;
+  if (F >= kMax32) return MOE_ERR_LIMIT;
+  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!x || !W_gu || !W_down || !h || !y) return MOE_ERR_NULL;
+  const moe_schedule &s = *sched;
+  if (!mfma_supported((int)K, (int)(2 * F)) || !mfma_supported((int)F, (int)N))
+    return MOE_ERR_SHAPE;
+  if (!fits(s.T, K, dtype) || !fits(2 * F, K, dtype) || !fits(N, F, dtype) ||
+      !fits(s.R, F, dtype) || !fits(s.T, N, MOE_F32))
+    return MOE_ERR_LIMIT;
+  if (!aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) || !aligned(h, 16) ||
+      !aligned(y, 4))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = timed(F_GATED_UP, st, [&] {
+    return mfma_gated_up(x, W_gu, s, h, (int)K, (int)F, st);
+  });
+  if (e == hipSuccess)
+    e = timed(F_FILL, st, [&] {
+      return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
+    });
+  if (e == hipSuccess)
+    e = timed(F_GATED_DOWN, st, [&] {
+      return mfma_fused_fwd(h, W_down, s, y, (int)F, (int)N, true, st);
+    });
+  return hip_status(e);
 }
 
 size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64_t N,

@@ -94,8 +94,13 @@ hipError_t simt_bwd_dw(const void *dY, const void *x, const moe_schedule &s, voi
 bool mfma_supported(int K, int N);
 hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C,
                              int M, int K, int N, int E, int out_dtype, hipStream_t st);
+// a_by_row: the A operand is already in schedule row order ([R, K]) instead of
+// being gathered from x [T, K] by token
 hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
-                          int N, hipStream_t st);
+                          int N, bool a_by_row, hipStream_t st);
+// h [R, F] bf16 = silu(x W_gate^T) * (x W_up^T) per schedule row; W_gu [E, 2F, K]
+hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, int K,
+                         int F, hipStream_t st);
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, hipStream_t st);
 // zero0 / zero1: byte ranges the kernel zeroes on the side (NULL / 0 when unused)

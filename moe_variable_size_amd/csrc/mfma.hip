@@ -645,7 +645,18 @@ struct FwdArgs {
   int stream_k;      // 1: split the last partial wave of tiles along K
   int tail_split;    // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int M;             // bare: rows of A and C (rows at or past M are never touched)
+  int a_by_row;      // 1: A row of schedule row r is row r itself (an operand already in
+                     // schedule order, e.g. the gated FFN's intermediate); 0: gather by token
 };
+
+// What a forward-shaped kernel writes:
+//   FWD_BARE    C[r, n] = acc (fp32 or bf16 store; rows grouped by end offsets)
+//   FWD_SCATTER y[token(r), n] += w_r * acc (atomic; routing schedule)
+//   FWD_GATED   h[r, f] = silu(acc_gate) * acc_up in bf16 (routing schedule): the
+//               B tile holds 128 gate rows f0.. and the 128 up rows F + f0.. of a
+//               doubled [2F, K] weight, so each wave's column block ni < NI/2 and
+//               block ni + NI/2 hold the gate and the up value of the same f
+enum { FWD_BARE = 0, FWD_SCATTER = 1, FWD_GATED = 2 };
 
 template <int BM, int BN, int NW>
 struct FwdOp {
@@ -703,9 +714,13 @@ struct FwdDeepOp {
   }
 };
 
-template <int BM, int BN, int WGM, int WGN, bool FUSED, typename Tout>
+template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout>
 __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
+  constexpr bool FUSED = MODE != FWD_BARE;       // rows come from a routing schedule
+  constexpr bool GATED = MODE == FWD_GATED;
+  constexpr int BNO = GATED ? BN / 2 : BN;        // output columns per tile
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
+  static_assert(!GATED || NI % 2 == 0, "gate and up blocks pair up inside a wave");
   constexpr int NW = WGM * WGN, NTH = NW * 64;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   extern __shared__ __attribute__((aligned(16))) char lds[];  // NSTAGE x (A, B)
@@ -725,7 +740,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   else
     group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
 
-  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_n = (N + BNO - 1) / BNO;
   const int KI = (K + BK - 1) / BK;
   const int total = bs[E] * tiles_n;
   FwdOp<BM, BN, NW> op;
@@ -733,22 +748,28 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   op.lds0 = lds_addr(lds);
   op.K = K;
   op.wid = wid;
-  const uint32_t wbytes = (uint32_t)N * K * 2;
+  const int wrows = GATED ? 2 * N : N;  // rows of one expert's weight
+  const uint32_t wbytes = (uint32_t)wrows * K * 2;
 
   const int Lb = logical_block();
   WorkSplit ws;
+  // gated tiles split along rows only (a column split would part gate from up)
   ws.init(total, KI, gridDim.x, Lb,
-          p.stream_k ? WorkSplit::STREAM_K : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE), p.tail_split);
+          p.stream_k && !GATED ? WorkSplit::STREAM_K
+                               : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE),
+          GATED ? min(p.tail_split, 2) : p.tail_split);
   int tau, kb, ke;
   while (ws.next(tau, kb, ke)) {
     TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
-    int n0 = c.nb * BN, ncols = min(BN, N - n0);
+    int n0 = c.nb * BNO, ncols = min(BNO, N - n0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
       const SubTile st = sub_tile(ws.s, ws.nS);
       c.row0 += st.r0;
       c.rows = min(st.rows, c.rows - st.r0);
-      n0 += st.c0;
-      ncols = min(st.cols, N - n0);
+      if (!GATED) {
+        n0 += st.c0;
+        ncols = min(st.cols, N - n0);
+      }
     }
     if (c.rows <= 0 || ncols <= 0) continue;
     __syncthreads();  // LDS stages and row tables free
@@ -758,14 +779,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       const int t = ok ? (FUSED ? p.row_to_token[r] : (r < p.M ? r : -1)) : -1;
       tok[tid] = t;
       wgt[tid] = (FUSED && ok) ? p.row_weight[r] : 0.f;
-      rowoff_a[tid] = t >= 0 ? t * K * 2 : -1;
+      rowoff_a[tid] = t >= 0 ? (p.a_by_row ? r : t) * K * 2 : -1;
     }
-    for (int j = tid; j < BN; j += NTH) rowoff_b[j] = j < ncols ? (n0 + j) * K * 2 : -1;
+    for (int j = tid; j < BN; j += NTH) {
+      const int jj = GATED ? j % BNO : j;  // gated: gate rows, then the up rows
+      rowoff_b[j] = jj < ncols ? (n0 + jj + (GATED && j >= BNO ? N : 0)) * K * 2 : -1;
+    }
     __syncthreads();
-    op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
+    op.rsW = uniform_rsrc(p.W + (size_t)c.g * wrows * K, wbytes);
     const bool part = BM <= 64 || ws.nS > 1;  // rows / columns partly dead
+    // (gated: the live B rows are two runs, not a prefix; nothing is skipped)
+    const int live_b = GATED ? BN : ncols;
     op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
-    op.db.setup(wid, lane, rowoff_b, part ? ncols : BN);
+    op.db.setup(wid, lane, rowoff_b, part ? live_b : BN);
     // The tile body, instantiated per accumulator shape: MIc x NIc blocks per
     // wave (a whole tile, or a 128 x 128 / 64 x 128 sub-tile), each with its own
     // accumulators.  SKM: MFMAs of row blocks past the last live row are left
@@ -791,7 +817,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         dop.K = K;
         dop.wid = wid;
         dop.da.setup(wid, lane, rowoff_a, c.rows);
-        dop.db.setup(wid, lane, rowoff_b, ncols);
+        dop.db.setup(wid, lane, rowoff_b, GATED ? BNs : ncols);
         tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi,
                                                dop.parts(), acc);
       } else {
@@ -801,6 +827,36 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
       // row tables; each row's base address is formed once for all column blocks
+      if constexpr (GATED) {
+        // h[r, f] = silu(g) * u, silu(g) = g / (1 + e^-g), stored bf16 at the
+        // tile's schedule row r for live rows and f < F
+        constexpr int NH = NIc / 2;
+        bf16_t *const hb = (bf16_t *)p.C;
+        const int cl0 = wn * 32 + (lane & 31);
+#pragma unroll
+        for (int mi = 0; mi < MIc; ++mi) {
+          if (mi >= live_mi) continue;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
+            const i32x4 t4 = *(const i32x4 *)(tok + rq);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (t4[q] < 0) continue;
+              bf16_t *const hrow = hb + (size_t)(c.row0 + rq + q) * N + n0;
+#pragma unroll
+              for (int ni = 0; ni < NH; ++ni) {
+                const int cl = cl0 + ni * 32 * WGN;
+                if (cl >= ncols) continue;
+                const float g = acc[mi][ni][4 * j + q], u = acc[mi][ni + NH][4 * j + q];
+                hrow[cl] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        return;
+      }
       if (FUSED) {
         // weighted scatter-combine: atomics on y with 32-bit byte offsets from
         // its base; only live rows and columns are touched (the column test is
@@ -873,18 +929,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     } else {
       // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
       constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
-      if (ws.nS == 8)
-        tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(), true_type(),
-             false_type());
-      else if (ws.nS == 4)
-        tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(), true_type(),
-             false_type());
-      else if (ws.nS == 2)
-        tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(), true_type(),
-             false_type());
-      else
-        tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
-             false_type(), false_type());
+      if constexpr (GATED) {  // whole tiles and 128 x 256 halves only
+        if (ws.nS == 2)
+          tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
+               true_type(), false_type());
+        else
+          tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
+               false_type(), false_type());
+      } else {
+        if (ws.nS == 8)
+          tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
+               true_type(), false_type());
+        else if (ws.nS == 4)
+          tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(),
+               true_type(), false_type());
+        else if (ws.nS == 2)
+          tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
+               true_type(), false_type());
+        else
+          tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
+               false_type(), false_type());
+      }
     }
   }
 }
@@ -1439,21 +1504,38 @@ bool mfma_supported(int K, int N) { return K % 8 == 0 && N % 8 == 0; }
 
 namespace {
 // Launch a 256 x 256 forward-shaped kernel with 4 (2 x 2) or 8 (2 x 4) waves.
-template <bool FUSED, typename Tout>
+template <int MODE, typename Tout>
 hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
   if (gemm_waves() == 4) {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, FUSED, Tout>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout>>(kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, FUSED, Tout>), grid, dim3(256), kStageLds,
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout>), grid, dim3(256), kStageLds,
                        st, a);
   } else {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, FUSED, Tout>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout>>(kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, FUSED, Tout>), grid, dim3(512), kStageLds,
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout>), grid, dim3(512), kStageLds,
                        st, a);
   }
   return hipGetLastError();
+}
+
+// Routed forward-shaped launch: masked schedules of capacity <= 64 take 64-row
+// tiles (one row block per expert), everything else 256 x 256 tiles.
+template <int MODE>
+hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
+  if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
+    constexpr int BM = 64, BN = 256;
+    a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
+    auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float>;
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float>>(kStageLds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
+    return hipGetLastError();
+  }
+  a.bstart = s.block_start + bm_index(256) * (s.E + 1);
+  return launch_fwd256<MODE, float>(a, st);
 }
 }  // namespace
 
@@ -1461,26 +1543,26 @@ hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offset
                              int K, int N, int E, int out_dtype, hipStream_t st) {
   FwdArgs a{(const bf16_t *)A, (const bf16_t *)W, C, offsets, nullptr, nullptr, nullptr, nullptr,
             E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), 0, tail_split(), M};
-  if (out_dtype == MOE_F32) return launch_fwd256<false, float>(a, st);
-  return launch_fwd256<false, bf16_t>(a, st);
+  if (out_dtype == MOE_F32) return launch_fwd256<FWD_BARE, float>(a, st);
+  return launch_fwd256<FWD_BARE, bf16_t>(a, st);
 }
 
 hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
-                          int N, hipStream_t st) {
+                          int N, bool a_by_row, hipStream_t st) {
+  const size_t arows = a_by_row ? (size_t)s.R : (size_t)s.T;
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split(), (int)s.T};
-  if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
-    constexpr int BM = 64, BN = 256;
-    a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
-    auto k = mfma_fwd_kernel<BM, BN, 1, 4, true, float>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, true, float>>(kStageLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
-    return hipGetLastError();
-  }
-  a.bstart = s.block_start + bm_index(256) * (s.E + 1);
-  return launch_fwd256<true, float>(a, st);
+            (uint32_t)(arows * K * 2), stream_k_mode(), tail_split(), (int)s.T,
+            a_by_row ? 1 : 0};
+  return launch_routed<FWD_SCATTER>(a, s, st);
+}
+
+hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, int K,
+                         int F, hipStream_t st) {
+  FwdArgs a{(const bf16_t *)x, (const bf16_t *)W_gu, h, s.offsets, s.counts, nullptr,
+            s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, F,
+            (uint32_t)((size_t)s.T * K * 2), 0, tail_split(), (int)s.T, 0};
+  return launch_routed<FWD_GATED>(a, s, st);
 }
 
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,

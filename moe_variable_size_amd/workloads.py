@@ -151,6 +151,20 @@ def distinct_uniform_ids(rng: np.random.Generator, T: int, E: int, k: int) -> np
     return np.argsort(keys, axis=1, kind="stable")[:, :k].astype(np.int32)
 
 
+def balanced_ids(rng: np.random.Generator, T: int, E: int, k: int) -> np.ndarray:
+    """k distinct experts per token with every expert receiving exactly T*k/E
+    assignments (T*k/E and T/E whole): slot 0 is a shuffled list holding each
+    expert T/E times, slot j is slot 0 mapped through a random permutation of
+    the experts that moves every expert j places along a random cycle."""
+    assert T % E == 0 and k <= E
+    first = rng.permutation(np.repeat(np.arange(E), T // E))
+    cycle = rng.permutation(E)
+    pos = np.empty(E, dtype=np.int64)
+    pos[cycle] = np.arange(E)
+    cols = [cycle[(pos[first] + j) % E] for j in range(k)]
+    return np.stack(cols, axis=1).astype(np.int32)
+
+
 def zipf_gumbel_ids(rng: np.random.Generator, T: int, E: int, k: int, s: float,
                     n_zero: int) -> tuple[np.ndarray, np.ndarray]:
     """k distinct experts per token drawn without replacement with probability
@@ -201,6 +215,8 @@ def routed(name: str, T: int, K: int, N: int, E: int, k: int, *, seed: int, bf16
     notes = {}
     if routing == "uniform":
         ids = distinct_uniform_ids(rng, T, E, k)
+    elif routing == "balanced":
+        ids = balanced_ids(rng, T, E, k)
     elif routing == "zipf":
         ids, order = zipf_gumbel_ids(rng, T, E, k, zipf_s, n_zero)
         notes["zero_experts"] = sorted(int(e) for e in order[E - n_zero:]) if n_zero else []
@@ -271,6 +287,57 @@ def config5(seed: int = BASE_SEED + 5, dense: bool = True) -> Routed:
     return routed("decode_masked_T128_K7168_N2048_E64_top8_cap64", 128, 7168, 2048, 64, 8,
                   seed=seed, routing="uniform", weights="uniform", with_dy=False, capacity=64,
                   dense=dense)
+
+
+@dataclass
+class Gated:
+    """Inputs of the gated expert FFN: the routed layer with a doubled
+    up-projection W_gu [E, 2F, K] (gate rows, then up rows) and a down
+    projection W_down [E, N, F]."""
+
+    name: str
+    T: int
+    K: int
+    F: int
+    N: int
+    E: int
+    k: int
+    x: Optional[Tensor]            # [T, K]
+    W_gu: Optional[Tensor]         # [E, 2F, K]
+    W_down: Optional[Tensor]       # [E, N, F]
+    expert_ids: np.ndarray         # [T, k] int32
+    topk_weights: Optional[np.ndarray]
+    capacity: int = 0
+    seed: int = 0
+
+    @property
+    def S(self) -> int:
+        return self.T * self.k
+
+
+def gated(name: str, T: int, K: int, F: int, N: int, E: int, k: int, *, seed: int,
+          routing: str = "uniform", weights: str = "uniform", capacity: int = 0,
+          dense: bool = True) -> Gated:
+    """Gated FFN workload: routing as in ``routed`` (same draws for the same
+    seed), x ~ N(0, 1), W_gu ~ N(0, 1/K), W_down ~ N(0, 1/F), all bf16."""
+    r = routed(name, T, K, 2 * F, E, k, seed=seed, routing=routing, weights=weights,
+               with_dy=False, capacity=capacity, dense=dense)
+    Wd = None
+    if dense:
+        s_d = np.random.SeedSequence(seed).spawn(5)[4]
+        Wd = _make(_normal_blocks(s_d, E, (N, F), 1.0 / np.sqrt(F)), True)
+    return Gated(name, T, K, F, N, E, k, r.x, r.W, Wd, r.expert_ids, r.topk_weights,
+                 capacity=capacity, seed=seed)
+
+
+def gated_page_example(seed: int = BASE_SEED + 6, dense: bool = True) -> Gated:
+    """The balanced step of "Grouped GEMM for MoE, in depth" ("Worked example:
+    tile counts under skew"): one up-projection with hidden size 4096 and width
+    2048, 8192 tokens, top-2, 64 experts of exactly 256 rows each -- here as a
+    gated FFN: gate and up of width F = 2048 each, down projection back to
+    4096; weights U[0,1)."""
+    return gated("gated_T8192_K4096_F2048_N4096_E64_top2_balanced", 8192, 4096, 2048, 4096, 64,
+                 2, seed=seed, routing="balanced", weights="uniform", dense=dense)
 
 
 def grouped_as_routed(g: Grouped) -> Routed:

@@ -96,3 +96,21 @@ def test_gemm_entry_points_reject_before_launch(lib):
     assert lib.moe_fused_bwd(P, P, None, ctypes.byref(s), P, None, None, 8, 8, 1, None, 0, None) == 1
     assert lib.moe_tile_map(ctypes.byref(s), 8, 48, 16, P, P, P, 4, None) == 2   # BM not in {32..256}
     assert lib.moe_timing_read(b"nope", ctypes.byref(ctypes.c_double()), ctypes.byref(ctypes.c_int64())) == 2
+
+
+def test_gated_ffn_rejects_before_launch(lib):
+    P = FAKE
+    s = _lib.MoeSchedule()
+    s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
+    for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
+              "row_weight", "status"):
+        setattr(s, f, 1 << 20)
+    r = ctypes.byref(s)
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 16, 16, 16, 0, None) == 3      # fp32: bf16 only
+    assert lib.moe_gated_ffn_fwd(P, P, None, r, P, P, 16, 16, 16, 1, None) == 1   # no W_down
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, None, P, 16, 16, 16, 1, None) == 1   # no h
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 16, 0, 16, 1, None) == 2      # F = 0
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 16, 12, 16, 1, None) == 2     # F % 8 != 0
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, ctypes.c_void_p((1 << 20) + 2), P, 16, 16, 16, 1,
+                                 None) == 4                                       # h misaligned
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 1 << 16, 1 << 15, 16, 1, None) == 7  # W_gu > 2^31 B

@@ -71,3 +71,15 @@ def test_config5_fits_capacity():
     c = np.bincount(r.expert_ids.reshape(-1), minlength=64)
     assert r.capacity == 64 and c.max() <= 64 and c.min() > 0
     assert all(len(set(row)) == 8 for row in r.expert_ids.tolist())
+
+
+def test_balanced_routing_and_gated_example():
+    """Every expert gets exactly T*k/E assignments, experts are distinct per
+    token, and the gated example has the shapes of the page's balanced step."""
+    rng = np.random.default_rng(3)
+    ids = W.balanced_ids(rng, 96, 8, 3)
+    assert (np.bincount(ids.ravel(), minlength=8) == 36).all()
+    assert all(len(set(r)) == 3 for r in ids.tolist())
+    g = W.gated_page_example(dense=False)
+    assert (g.T, g.K, g.F, g.N, g.E, g.k) == (8192, 4096, 2048, 4096, 64, 2)
+    assert (np.bincount(g.expert_ids.ravel(), minlength=64) == 256).all()
