@@ -12,6 +12,10 @@ x, dY ~ N(0,1), W ~ N(0,1/K), bf16 storage with fp32 accumulation.
 Metric: useful TFLOP/s = (2SKN forward + 4SKN backward + 2SN routing-weight
 gradient) / step time, S = T*top_k; padding is never counted.
 
+Two more objects ride on the same line: "decode" (masked decode forward,
+HBM GB/s) and "gated_ffn" (gated expert FFN forward on the balanced step of
+the page's worked example, TFLOP/s).
+
 Prints ONE JSON line.  --gpus above 1 is not supported (one GPU per process,
 single-GPU machine) and exits with a message.
 """
@@ -44,6 +48,8 @@ def _args():
                    help="untimed steps first (also brings the GPU clocks to their loaded state)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-gated", action="store_true",
+                   help="skip the gated expert FFN line (its inputs take ~10 s to draw)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="minimum host time spent on the oracle sample")
     p.add_argument("--calib-copy", action="store_true",
@@ -139,6 +145,62 @@ def decode_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
             "hbm_GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "step_ms": round(ms_step, 4),
             "step_GBps": round(nbytes / (ms_step * 1e-3) / 1e9, 1)}
+
+
+def gated_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
+    """Gated expert FFN forward on the balanced step of the page's worked
+    example (T=8192, hidden 4096, F=2048, E=64 with 256 rows each, top-2):
+    gate+up as one grouped GEMM with silu(gate)*up in its epilogue, then the
+    down projection with the weighted scatter-combine.  Useful FLOPs:
+    2*S*K*2F + 2*S*F*N."""
+    g = WL.gated_page_example()
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, Wgu, Wd = to_dev(g.x), to_dev(g.W_gu), to_dev(g.W_down)
+    ids = torch.from_numpy(g.expert_ids).to(dev)
+    w = torch.from_numpy(g.topk_weights).to(dev)
+    S = g.T * g.k
+    ws = torch.empty(api.moe_schedule_workspace_bytes(g.T, g.k, g.E), dtype=torch.uint8, device=dev)
+    h = torch.empty((S, g.F), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((g.T, g.N), dtype=torch.float32, device=dev)
+
+    def step():
+        sch = api.moe_build_schedule(ids, w, g.E, workspace=ws)
+        api.moe_gated_ffn_fwd(x, Wgu, Wd, sch, h=h, y=y)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    api.moe_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    api.moe_timing_enable(False)
+    kt = {}
+    for f in ("build_schedule", "gated_up", "fill_zero", "gated_down"):
+        tot, n = api.moe_timing_read(f)
+        kt[f] = round(tot * 1e3 / max(n, 1), 3)
+    fl_up = 2.0 * S * g.K * 2 * g.F
+    fl_dn = 2.0 * S * g.F * g.N
+    up_tf = fl_up / (kt["gated_up"] * 1e-6) / 1e12
+    del x, Wgu, Wd, h, y
+    return {"workload": f"{g.name} forward (schedule + gated up + zero y + down)",
+            "T": g.T, "K": g.K, "F": g.F, "N": g.N, "E": g.E, "top_k": g.k,
+            "step_ms": round(ms_step, 4),
+            "tflops": round((fl_up + fl_dn) / (ms_step * 1e-3) / 1e12, 2),
+            "kernels_us": kt,
+            "gated_up_tflops": round(up_tf, 2),
+            "gated_down_tflops": round(fl_dn / (kt["gated_down"] * 1e-6) / 1e12, 2),
+            "roofline": {"bound": "mfma", "kernel": "gated_up", "achieved": round(up_tf, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(up_tf / PEAK_BF16_TFLOPS, 4)}}
 
 
 def main():
@@ -245,6 +307,8 @@ def main():
         out["roofline"]["traffic"] = tr
     if not a.no_decode:
         out["decode"] = decode_line(torch, api, WL, dev, a.steps, a.warmup)
+    if not a.no_gated:
+        out["gated_ffn"] = gated_line(torch, api, WL, dev, min(a.steps, 50), min(a.warmup, 20))
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(r, flops_step, a.cpu_seconds)
     print(json.dumps(out), flush=True)
