@@ -262,6 +262,28 @@ MOE_DEV SubTile sub_tile(int s, int nS) {
   return SubTile{(s >> 1) * rows, (s & 1) * cols, rows, cols};
 }
 
+// Rows per tile of a launch over a routing schedule, picked on the device from
+// the row-block totals the schedule already holds (no read-back): 256-row
+// tiles unless 128-row tiles (computed with the 128 x 256 shape) are estimated
+// to finish sooner ([GG] "Worked example: tile counts under skew": small tiles
+// waste fewer rows but reuse each loaded weight tile half as often).  The
+// estimate is rounds of tiles over the G workgroups times the time of one tile;
+// on MI355X a 128 x 256 tile takes 0.64 of a 256 x 256 one.  Every workgroup
+// reads the same totals and takes the same decision.  forced = 128 or 256
+// overrides the estimate.
+MOE_DEV int pick_tile_rows(const int32_t *bstart_all, int E, int tiles_n, int G, int forced) {
+  if (forced == 128 || forced == 256) return forced;
+  const float r256 = (float)bstart_all[bm_index(256) * (E + 1) + E] * tiles_n / G;
+  const float r128 = (float)bstart_all[bm_index(128) * (E + 1) + E] * tiles_n / G;
+  return __builtin_amdgcn_readfirstlane(0.64f * fmaxf(r128, 1.f) < fmaxf(r256, 1.f) ? 128 : 256);
+}
+
+// Sub-tile s of nS (2: 128 x 128, 4: 64 x 128) of a 128 x 256 tile.
+MOE_DEV SubTile sub_tile128(int s, int nS) {
+  if (nS == 2) return SubTile{0, s * 128, 128, 128};
+  return SubTile{(s >> 1) * 64, (s & 1) * 128, 64, 128};
+}
+
 // ---- MFMA operand fragments ----------------------------------------------------
 // Lane l of a 32x32x16 MFMA holds, for operand row/column (l & 31), the 8
 // reduction elements 8*(l >> 5) .. +7 of the 16-element step.
@@ -637,7 +659,7 @@ struct FwdArgs {
   void *C;
   const int32_t *offsets;
   const int32_t *counts;
-  const int32_t *bstart;
+  const int32_t *bstart;  // routed: the schedule's row-block prefixes [MOE_NUM_BM][E+1]
   const int32_t *row_to_token;
   const float *row_weight;
   int E, layout, capacity, K, N;
@@ -647,6 +669,7 @@ struct FwdArgs {
   int M;             // bare: rows of A and C (rows at or past M are never touched)
   int a_by_row;      // 1: A row of schedule row r is row r itself (an operand already in
                      // schedule order, e.g. the gated FFN's intermediate); 0: gather by token
+  int tile_rows;     // routed, BM = 256: 0 = picked on the device, 128 / 256 = forced
 };
 
 // What a forward-shaped kernel writes:
@@ -734,14 +757,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
-  if (FUSED)
-    group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
-                                    rstart, rcnt);
-  else
-    group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
-
   const int tiles_n = (N + BNO - 1) / BNO;
   const int KI = (K + BK - 1) / BK;
+  // rows per tile of this launch (uniform over the grid): BM, or with routed
+  // 256-row kernels possibly 128 (the 128 x 256 shape)
+  const int BMr = (FUSED && BM == 256)
+                      ? pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows)
+                      : BM;
+  if (FUSED)
+    group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * (E + 1), E,
+                                    p.layout, p.capacity, bs, rstart, rcnt);
+  else
+    group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
   const int total = bs[E] * tiles_n;
   FwdOp<BM, BN, NW> op;
   op.rsA = uniform_rsrc(p.A, p.a_bytes);
@@ -753,17 +780,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
 
   const int Lb = logical_block();
   WorkSplit ws;
-  // gated tiles split along rows only (a column split would part gate from up)
+  // gated tiles split along rows only (a column split would part gate from up);
+  // 128-row tiles split at most 4 ways (64 x 128)
   ws.init(total, KI, gridDim.x, Lb,
-          p.stream_k && !GATED ? WorkSplit::STREAM_K
-                               : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE),
-          GATED ? min(p.tail_split, 2) : p.tail_split);
+          p.stream_k && !GATED && BMr == BM
+              ? WorkSplit::STREAM_K
+              : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE),
+          GATED ? (BMr == BM ? min(p.tail_split, 2) : 1)
+                : (BMr == BM ? p.tail_split : min(p.tail_split, 4)));
   int tau, kb, ke;
   while (ws.next(tau, kb, ke)) {
-    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
+    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BMr);
     int n0 = c.nb * BNO, ncols = min(BNO, N - n0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
-      const SubTile st = sub_tile(ws.s, ws.nS);
+      const SubTile st = BMr == 128 ? sub_tile128(ws.s, ws.nS) : sub_tile(ws.s, ws.nS);
       c.row0 += st.r0;
       c.rows = min(st.rows, c.rows - st.r0);
       if (!GATED) {
@@ -787,7 +817,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     }
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * wrows * K, wbytes);
-    const bool part = BM <= 64 || ws.nS > 1;  // rows / columns partly dead
+    const bool part = BM <= 64 || ws.nS > 1 || BMr < BM;  // rows / columns partly dead
     // (gated: the live B rows are two runs, not a prefix; nothing is skipped)
     const int live_b = GATED ? BN : ncols;
     op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
@@ -930,12 +960,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
       constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
       if constexpr (GATED) {  // whole tiles and 128 x 256 halves only
-        if (ws.nS == 2)
+        if (ws.nS == 2 || BMr == 128)
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
         else
           tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
                false_type(), false_type());
+      } else if (BMr == 128) {  // 128 x 256 tiles, split 2 (128 x 128) or 4 (64 x 128)
+        if (ws.nS == 4)
+          tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
+               true_type(), false_type());
+        else if (ws.nS == 2)
+          tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(),
+               true_type(), false_type());
+        else
+          tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
+               true_type(), false_type());
       } else {
         if (ws.nS == 8)
           tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
@@ -981,6 +1021,7 @@ struct DxArgs {
   uint32_t dy_bytes, x_bytes;
   int stream_k;
   int tail_split;  // largest split of a tile of the last partial round (8, 4, 2 or 1)
+  int tile_rows;   // 0 = picked on the device, 128 / 256 = forced
 };
 
 template <int NW>
@@ -1044,10 +1085,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
-  group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart, E, p.layout, p.capacity, bs,
-                                  rstart, rcnt);
   const int tiles_n = (K + BN - 1) / BN;  // output columns run over K
   const int KI = (N + BK - 1) / BK;       // reduction runs over N
+  const int BMr = pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows);
+  group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * (E + 1), E,
+                                  p.layout, p.capacity, bs, rstart, rcnt);
   const int total = bs[E] * tiles_n;
   DxOp<NW> op;
   op.rsA = uniform_rsrc(p.dY, p.dy_bytes);
@@ -1061,14 +1103,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 
   const int Lb = logical_block();
   WorkSplit ws;
-  ws.init(total, KI, gridDim.x, Lb, p.stream_k ? WorkSplit::STREAM_K : WorkSplit::SUBTILE_TAIL,
-          p.tail_split);
+  // 128-row tiles split at most 4 ways (64 x 128)
+  ws.init(total, KI, gridDim.x, Lb,
+          p.stream_k && BMr == BM ? WorkSplit::STREAM_K : WorkSplit::SUBTILE_TAIL,
+          BMr == BM ? p.tail_split : min(p.tail_split, 4));
   int tau, kb, ke;
   while (ws.next(tau, kb, ke)) {
-    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
+    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BMr);
     int kc0 = c.nb * BN, ncols = min(BN, K - kc0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
-      const SubTile st = sub_tile(ws.s, ws.nS);
+      const SubTile st = BMr == 128 ? sub_tile128(ws.s, ws.nS) : sub_tile(ws.s, ws.nS);
       c.row0 += st.r0;
       c.rows = min(st.rows, c.rows - st.r0);
       kc0 += st.c0;
@@ -1087,7 +1131,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
     }
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
-    const bool part = ws.nS > 1;  // rows / columns partly dead
+    const bool part = ws.nS > 1 || BMr < BM;  // rows / columns partly dead
     op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
     op.setup_b(kc0, kc0 + ncols);
     // The tile body, instantiated per accumulator shape: MIc x NIc blocks per
@@ -1198,7 +1242,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
     using std::integral_constant;
     // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
     constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
-    if (ws.nS == 8)
+    if (BMr == 128) {  // 128 x 256 tiles, split 2 (128 x 128) or 4 (64 x 128)
+      if (ws.nS == 4)
+        tile(integral_constant<int, R8>(), integral_constant<int, C>(), std::true_type());
+      else if (ws.nS == 2)
+        tile(integral_constant<int, R4>(), integral_constant<int, C>(), std::true_type());
+      else
+        tile(integral_constant<int, R4>(), integral_constant<int, NI>(), std::true_type());
+    } else if (ws.nS == 8)
       tile(integral_constant<int, R8>(), integral_constant<int, C>(), std::true_type());
     else if (ws.nS == 4)
       tile(integral_constant<int, R4>(), integral_constant<int, C>(), std::true_type());
@@ -1470,6 +1521,17 @@ int tail_split() {
   return v;
 }
 
+// MOE_VS_BM=128 / 256: routed forward and input-gradient kernels with 128- or
+// 256-row tiles instead of the device-side pick (read once)
+int forced_bm() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_BM");
+    const int n = e ? atoi(e) : 0;
+    return n == 128 || n == 256 ? n : 0;
+  }();
+  return v;
+}
+
 // MOE_VS_DX_WAVES=8: input-gradient kernel with 8 waves per workgroup instead of
 // 4 (its routing-weight epilogue runs short of registers with 8)
 int dx_waves() {
@@ -1525,16 +1587,16 @@ hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
 // tiles (one row block per expert), everything else 256 x 256 tiles.
 template <int MODE>
 hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
+  a.bstart = s.block_start;
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
-    a.bstart = s.block_start + bm_index(BM) * (s.E + 1);
     auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float>;
     hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
     return hipGetLastError();
   }
-  a.bstart = s.block_start + bm_index(256) * (s.E + 1);
+  a.tile_rows = forced_bm();
   return launch_fwd256<MODE, float>(a, st);
 }
 }  // namespace
@@ -1567,11 +1629,10 @@ hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s,
 
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, hipStream_t st) {
-  constexpr int BM = 256;
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
-           s.counts, s.block_start + bm_index(BM) * (s.E + 1), s.row_to_assign, s.row_to_token,
+           s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
-           (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split()};
+           (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split(), forced_bm()};
   const dim3 grid(device_cu_count());
   if (dx_waves() == 4) {
     hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);
