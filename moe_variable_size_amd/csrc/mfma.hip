@@ -267,15 +267,17 @@ MOE_DEV SubTile sub_tile(int s, int nS) {
 // tiles unless 128-row tiles (computed with the 128 x 256 shape) are estimated
 // to finish sooner ([GG] "Worked example: tile counts under skew": small tiles
 // waste fewer rows but reuse each loaded weight tile half as often).  The
-// estimate is rounds of tiles over the G workgroups times the time of one tile;
-// on MI355X a 128 x 256 tile takes 0.64 of a 256 x 256 one.  Every workgroup
-// reads the same totals and takes the same decision.  forced = 128 or 256
-// overrides the estimate.
+// estimate is rounds of tiles over the G workgroups (at least one) times the
+// time of one tile, a 128 x 256 tile counted at 0.75 of a 256 x 256 one: whole
+// rounds of 128 x 256 tiles took 0.64 of the time on MI355X, and at estimates
+// closer than 0.75 the 256-row tiles still won (their last round splits
+// better).  Every workgroup reads the same totals and takes the same decision.
+// forced = 128 or 256 overrides the estimate.
 MOE_DEV int pick_tile_rows(const int32_t *bstart_all, int E, int tiles_n, int G, int forced) {
   if (forced == 128 || forced == 256) return forced;
   const float r256 = (float)bstart_all[bm_index(256) * (E + 1) + E] * tiles_n / G;
   const float r128 = (float)bstart_all[bm_index(128) * (E + 1) + E] * tiles_n / G;
-  return __builtin_amdgcn_readfirstlane(0.64f * fmaxf(r128, 1.f) < fmaxf(r256, 1.f) ? 128 : 256);
+  return __builtin_amdgcn_readfirstlane(0.75f * fmaxf(r128, 1.f) < fmaxf(r256, 1.f) ? 128 : 256);
 }
 
 // Sub-tile s of nS (2: 128 x 128, 4: 64 x 128) of a 128 x 256 tile.

@@ -4,7 +4,7 @@ oracle in the forward, the backward and the gated FFN.
 
 The choice is made inside the kernels from the schedule's row-block totals;
 the test states which height the estimate picks for each case (256-row tiles
-estimate rb256 * tiles_n / G rounds, 128-row tiles 0.64 * rb128 * tiles_n / G,
+estimate rb256 * tiles_n / G rounds, 128-row tiles 0.75 * rb128 * tiles_n / G,
 each at least one round) so that the cases cover the 128-row path with whole
 tiles and with its 2- and 4-way splits of a last partial round.
 """
@@ -26,7 +26,7 @@ def _picks_128(counts, ncols):
     tn = -(-ncols // 256)
     rb256 = int((-(-counts // 256)).sum())
     rb128 = int((-(-counts // 128)).sum())
-    return 0.64 * max(rb128 * tn / G, 1.0) < max(rb256 * tn / G, 1.0), rb128 * tn
+    return 0.75 * max(rb128 * tn / G, 1.0) < max(rb256 * tn / G, 1.0), rb128 * tn
 
 
 # (T, K, N, E, k): ~T*k/E rows per expert, all below 128
