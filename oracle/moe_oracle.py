@@ -415,6 +415,65 @@ def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.floa
 
 
 # ----------------------------------------------------------------------------
+# FP8 grouped GEMM with scales that travel with each group ([GG] "Choosing an
+# implementation": FP8 adds per-group or per-block scale factors carried with
+# every group)
+#
+# Readings (the page fixes neither the format nor the scale granularity):
+#   * operands are 8-bit floats in the E4M3 encoding without infinities
+#     (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0
+#     holds subnormals m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; largest
+#     finite value 448);
+#   * a token row t carries one scale sx[t]; expert e carries one scale per
+#     output channel sw[e, n] (per-group scales); the value of an operand is
+#     its decoded 8-bit float times its scale;
+#   * the layer is then the fused forward on the scaled values:
+#     y[t, n] = sum_j w[t, j] * sum_k (sx[t] qx[t, k]) * (sw[e, n] qW[e, n, k]).
+# ----------------------------------------------------------------------------
+def decode_e4m3(bits) -> np.ndarray:
+    """Value of each E4M3 code (uint8) as float64, from the field definition."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    exp = (b >> 3) & 0xF
+    man = b & 0x7
+    val = np.where(exp == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * 2.0 ** (exp - 7))
+    val = np.where((exp == 15) & (man == 7), np.nan, val)
+    return sign * val
+
+
+def moe_forward_fp8(xq, x_scale, Wq, w_scale, expert_ids, topk_weights, E: int, *,
+                    acc=np.float64) -> np.ndarray:
+    """Fused forward of 8-bit operands: decode, apply the per-token and the
+    per-group-per-channel scales, then the fused forward of the layer."""
+    x = decode_e4m3(xq) * np.asarray(x_scale, dtype=np.float64)[:, None]
+    W = decode_e4m3(Wq) * np.asarray(w_scale, dtype=np.float64)[:, :, None]
+    return moe_forward(x, W, expert_ids, topk_weights, E, acc=acc)
+
+
+def masked_forward_fp8(xq, x_scale, Wq, w_scale, ms: MaskedSchedule, T: int, *,
+                       acc=np.float64) -> np.ndarray:
+    """Decode forward of 8-bit operands on the masked layout."""
+    x = decode_e4m3(xq) * np.asarray(x_scale, dtype=np.float64)[:, None]
+    W = decode_e4m3(Wq) * np.asarray(w_scale, dtype=np.float64)[:, :, None]
+    return masked_forward(x, W, ms, T, acc=acc)
+
+
+def moe_forward_fp8_rows(xq, x_scale, Wq, w_scale, expert_ids, topk_weights, tokens, *,
+                         acc=np.float64) -> np.ndarray:
+    """y[t, :] of the 8-bit forward for the listed tokens only."""
+    expert_ids = np.asarray(expert_ids)
+    out = np.zeros((len(tokens), Wq.shape[1]), dtype=acc)
+    for i, t in enumerate(tokens):
+        xt = decode_e4m3(xq[t]) * float(x_scale[t])
+        for j in range(expert_ids.shape[1]):
+            e = int(expert_ids[t, j])
+            w = 1.0 if topk_weights is None else float(topk_weights[t, j])
+            We = decode_e4m3(Wq[e]) * np.asarray(w_scale[e], dtype=np.float64)[:, None]
+            out[i] += acc(w) * (We @ xt)
+    return out
+
+
+# ----------------------------------------------------------------------------
 # Sampled evaluation for full-size parity checks
 # ----------------------------------------------------------------------------
 def gated_intermediate_rows(x, W_gu, expert_ids, E: int, rows, *, acc=np.float64) -> np.ndarray:

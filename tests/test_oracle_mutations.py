@@ -109,9 +109,31 @@ def _gated_no_weight(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.flo
     return _ORIG["gated_ffn_forward"](x, W_gu, W_down, expert_ids, None, E, acc=acc)
 
 
+def _e4m3_bias8(bits):
+    return _ORIG["decode_e4m3"](bits) / 2.0            # exponent bias 8 instead of 7
+
+
+def _e4m3_no_subnormals(bits):
+    v = _ORIG["decode_e4m3"](bits)
+    e = (np.asarray(bits, dtype=np.uint8) >> 3) & 0xF
+    return np.where(e == 0, 0.0, v)                    # subnormals flushed
+
+
+def _fp8_no_token_scale(xq, x_scale, Wq, w_scale, expert_ids, topk_weights, E, *, acc=np.float64):
+    return _ORIG["moe_forward_fp8"](xq, np.ones(len(x_scale)), Wq, w_scale, expert_ids, topk_weights,
+                                    E, acc=acc)
+
+
+def _fp8_channel_scale_on_rows(xq, x_scale, Wq, w_scale, expert_ids, topk_weights, E, *,
+                               acc=np.float64):
+    sw = np.asarray(w_scale)
+    return _ORIG["moe_forward_fp8"](xq, x_scale, Wq, np.broadcast_to(sw[:, :1], sw.shape), expert_ids,
+                                    topk_weights, E, acc=acc)      # one scale per expert only
+
+
 _ORIG = {n: getattr(O, n) for n in ["routing_schedule", "tile_owner", "tile_coords", "moe_forward",
                                      "grouped_gemm", "moe_backward", "gated_activation",
-                                     "gated_ffn_forward"]}
+                                     "gated_ffn_forward", "decode_e4m3", "moe_forward_fp8"]}
 
 CASES = [
     ("end offsets replaced by start offsets", "routing_schedule", lambda: _mut_start_offsets(_ORIG["routing_schedule"]),
@@ -142,6 +164,15 @@ CASES = [
      [P.test_gated_ffn_reduces_to_dense_swiglu, lambda: P.test_gated_ffn_brute_force(1)]),
     ("gated routing weight dropped", "gated_ffn_forward", lambda: _gated_no_weight,
      [P.test_gated_gate_and_up_halves, P.test_gated_ffn_homogeneity]),
+    ("e4m3 exponent bias 8", "decode_e4m3", lambda: _e4m3_bias8,
+     [P.test_e4m3_decode_against_torch]),
+    ("e4m3 subnormals flushed", "decode_e4m3", lambda: _e4m3_no_subnormals,
+     [P.test_e4m3_decode_against_torch]),
+    ("fp8 token scale dropped", "moe_forward_fp8", lambda: _fp8_no_token_scale,
+     [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),
+    ("fp8 channel scale collapsed to one per expert", "moe_forward_fp8",
+     lambda: _fp8_channel_scale_on_rows,
+     [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),
 ]
 
 

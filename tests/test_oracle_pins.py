@@ -599,3 +599,78 @@ def test_masked_gated_equals_contiguous_without_overflow():
         start = int(sch.starts[e])
         assert np.array_equal(h[e * T:e * T + m], hc[start:start + m])
         assert np.all(h[e * T + m:(e + 1) * T] == 0)
+
+
+# ----------------------------------------------------------------------------
+# FP8 operands with per-token and per-group-per-channel scales
+# ----------------------------------------------------------------------------
+def test_e4m3_decode_against_torch():
+    """All 256 codes decode as torch's float8_e4m3fn does (NaN codes too)."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert O.decode_e4m3(0x7E) == 448.0 and O.decode_e4m3(0x01) == 2.0 ** -9
+    assert O.decode_e4m3(0x38) == 1.0 and O.decode_e4m3(0xB8) == -1.0
+
+
+def _tiny_fp8(seed, T=9, K=16, N=6, E=3, k=2):
+    rng = np.random.default_rng(seed)
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    xq = rng.choice(codes, size=(T, K)).astype(np.uint8)
+    Wq = rng.choice(codes, size=(E, N, K)).astype(np.uint8)
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    w = rng.random((T, k))
+    return rng, xq, Wq, ids, w
+
+
+def test_fp8_forward_brute_force():
+    """Plain Python loops over decoded codes (via torch's decoder) and scales."""
+    import torch
+    rng, xq, Wq, ids, w = _tiny_fp8(81)
+    T, K = xq.shape
+    E, N, _ = Wq.shape
+    sx = rng.random(T) + 0.5
+    sw = rng.random((E, N)) + 0.5
+    dec = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xv, Wv = dec(xq), dec(Wq)
+    ref = np.zeros((T, N))
+    for t in range(T):
+        for j in range(ids.shape[1]):
+            e = ids[t, j]
+            for n in range(N):
+                dot = sum(float(xv[t, c]) * float(Wv[e, n, c]) for c in range(K))
+                ref[t, n] += w[t, j] * sx[t] * sw[e, n] * dot
+    y = O.moe_forward_fp8(xq, sx, Wq, sw, ids, w, E)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    rows = O.moe_forward_fp8_rows(xq, sx, Wq, sw, ids, w, range(T))
+    assert np.abs(rows - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_fp8_power_of_two_scales_are_exact():
+    """With sx = 2^a and sw[e, n] = 2^b[n], y equals 2^(a + b[n]) times the
+    unscaled result exactly, column by column: a scale indexed by the
+    reduction dimension (or transposed) breaks this."""
+    rng, xq, Wq, ids, w = _tiny_fp8(82, K=16, N=5)
+    T = xq.shape[0]
+    E, N, _ = Wq.shape
+    y1 = O.moe_forward_fp8(xq, np.ones(T), Wq, np.ones((E, N)), ids, w, E)
+    b = rng.integers(-3, 4, size=N)
+    sw = np.broadcast_to(2.0 ** b, (E, N)).copy()
+    y2 = O.moe_forward_fp8(xq, np.full(T, 4.0), Wq, sw, ids, w, E)
+    assert np.array_equal(y2, y1 * 4.0 * 2.0 ** b[None, :])
+
+
+def test_fp8_masked_equals_contiguous():
+    rng, xq, Wq, ids, w = _tiny_fp8(83, T=20, K=32, N=7, E=5, k=3)
+    T = xq.shape[0]
+    E, N, _ = Wq.shape
+    sx = rng.random(T) + 0.5
+    sw = rng.random((E, N)) + 0.5
+    ms = O.masked_schedule(ids, w, E, capacity=T)
+    a = O.masked_forward_fp8(xq, sx, Wq, sw, ms, T)
+    b = O.moe_forward_fp8(xq, sx, Wq, sw, ids, w, E)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
