@@ -170,6 +170,25 @@ int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float
                   int64_t K, int64_t N, int32_t dtype, void *stream);
 
 /*
+ * Fused MoE forward on 8-bit operands with scales that travel with each group
+ * ([GG] "Choosing an implementation": FP8 brings per-group or per-block scale
+ * factors that must accompany every group):
+ *     y[t, n] = sum_j w[t, j] * x_scale[t] * w_scale[e, n]
+ *               * sum_k q(x_q[t, k]) * q(W_q[e, n, k]),   e = ids[t, j],
+ * where q(.) is the value of an E4M3 code (1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, subnormals, no infinities, 0x7F / 0xFF = NaN, largest
+ * finite 448).  The products run on the matrix cores' 8-bit path with fp32
+ * accumulation; the scales are applied to the fp32 result.
+ *   x_q [T, K] and W_q [E, N, K] uint8 codes, 16-byte aligned; K a multiple
+ *   of 16 (MOE_ERR_SHAPE otherwise); x_scale [T] and w_scale [E, N] float.
+ *   sched from moe_build_schedule (either layout); y [T, N] float,
+ *   OVERWRITTEN (zeroed by the call, then accumulated).
+ */
+int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
+                      const float *w_scale, const moe_schedule *sched, float *y, int64_t K,
+                      int64_t N, void *stream);
+
+/*
  * Gated expert FFN forward ([GG] "Choosing an implementation": the gate and up
  * projections run as one grouped GEMM over a weight with twice the output
  * rows, with the activation in that GEMM's epilogue; the down projection is
@@ -244,7 +263,7 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
  * kernel it launches with a pair of HIP events recorded on that launch's own
  * stream and keeps them per kernel family.  Families: "build_schedule",
  * "fill_zero", "grouped_gemm", "fused_fwd", "bwd_dx", "bwd_dw", "tile_map",
- * "gated_up", "gated_down".
+ * "gated_up", "gated_down", "fused_fwd_fp8".
  *   moe_timing_enable(1) clears earlier records and starts recording;
  *   moe_timing_enable(0) stops recording (records are kept).
  *   moe_timing_read waits for the recorded events of `family` and returns the

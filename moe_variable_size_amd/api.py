@@ -178,6 +178,35 @@ def moe_fused_fwd(x: torch.Tensor, W: torch.Tensor, sched: Schedule, *,
     return y
 
 
+def moe_fused_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, W_q: torch.Tensor,
+                      w_scale: torch.Tensor, sched: Schedule, *, y: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Fused MoE forward on 8-bit E4M3 operands (uint8 codes or float8_e4m3fn
+    tensors) with a per-token scale x_scale [T] and a per-expert output-channel
+    scale w_scale [E, N]; y [T, N] float32 ([GG] "Choosing an implementation")."""
+    lib = _lib.load()
+    f8 = getattr(torch, "float8_e4m3fn", None)
+    for t, name in ((x_q, "x_q"), (W_q, "W_q")):
+        if t.dtype not in (torch.uint8,) + ((f8,) if f8 is not None else ()):
+            raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    _require(x_q, "x_q", None, 2)
+    _require(W_q, "W_q", None, 3)
+    _require(x_scale, "x_scale", torch.float32, 1)
+    _require(w_scale, "w_scale", torch.float32, 2)
+    T, K = x_q.shape
+    E, N, K2 = W_q.shape
+    if K2 != K or T != sched.c.T or E != sched.c.E or tuple(x_scale.shape) != (T,) \
+            or tuple(w_scale.shape) != (E, N):
+        raise ValueError("shape mismatch between x_q [T,K], W_q [E,N,K], the scales and the schedule")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=x_q.device)
+    _require(y, "y", torch.float32, 2)
+    st = lib.moe_fused_fwd_fp8(_ptr(x_q), _ptr(x_scale), _ptr(W_q), _ptr(w_scale),
+                               ctypes.byref(sched.c), _ptr(y), K, N, _stream(stream))
+    _lib.check("moe_fused_fwd_fp8", st)
+    return y
+
+
 def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor, sched: Schedule, *,
                       h: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       stream=None):

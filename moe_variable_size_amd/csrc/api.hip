@@ -105,7 +105,8 @@ bool fits(int64_t rows, int64_t cols, int32_t dtype) {
 
 // ---- kernel timing (benchmarks only) ---------------------------------------
 const char *const kFamilies[] = {"build_schedule", "fill_zero", "grouped_gemm", "fused_fwd",
-                                 "bwd_dx", "bwd_dw", "tile_map", "gated_up", "gated_down"};
+                                 "bwd_dx", "bwd_dw", "tile_map", "gated_up", "gated_down",
+                                 "fused_fwd_fp8"};
 constexpr int kNumFamilies = sizeof(kFamilies) / sizeof(kFamilies[0]);
 
 struct Timing {
@@ -139,7 +140,8 @@ hipError_t timed(int fam, hipStream_t st, F &&f) {
   return e;
 }
 
-enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP, F_GATED_UP, F_GATED_DOWN };
+enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP, F_GATED_UP, F_GATED_DOWN,
+       F_FWD_FP8 };
 
 }  // namespace
 }  // namespace moe
@@ -251,6 +253,31 @@ int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float
     if (dtype == MOE_BF16 && mfma_supported((int)K, (int)N))
       return mfma_fused_fwd(x, W, s, y, (int)K, (int)N, false, st);
     return simt_fused_fwd(x, W, s, y, (int)K, (int)N, dtype, st);
+  }));
+}
+
+int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
+                      const float *w_scale, const moe_schedule *sched, float *y, int64_t K,
+                      int64_t N, void *stream) {
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  if (K < 16 || N < 1 || K % 16 != 0) return MOE_ERR_SHAPE;
+  if (K >= kMax32 || N >= kMax32) return MOE_ERR_LIMIT;
+  if (!x_q || !x_scale || !W_q || !w_scale || !y) return MOE_ERR_NULL;
+  const moe_schedule &s = *sched;
+  if ((double)s.T * K >= (double)kMax32 || (double)N * K >= (double)kMax32 ||
+      !fits(s.T, N, MOE_F32))
+    return MOE_ERR_LIMIT;
+  if (!aligned(x_q, 16) || !aligned(W_q, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
+      !aligned(y, 4))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e =
+      timed(F_FILL, st,
+            [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(F_FWD_FP8, st, [&] {
+    return mfma_fused_fwd_fp8(x_q, x_scale, W_q, w_scale, s, y, (int)K, (int)N, st);
   }));
 }
 

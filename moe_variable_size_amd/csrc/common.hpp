@@ -98,6 +98,11 @@ hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offset
 // being gathered from x [T, K] by token
 hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
                           int N, bool a_by_row, hipStream_t st);
+// 8-bit (E4M3) operands: y[t] += w * x_scale[t] * w_scale[e, n] * (xq[t] . Wq[e, n]);
+// K a multiple of 16 (16-byte rows)
+hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *Wq,
+                              const float *w_scale, const moe_schedule &s, float *y, int K, int N,
+                              hipStream_t st);
 // h [R, F] bf16 = silu(x W_gate^T) * (x W_up^T) per schedule row; W_gu [E, 2F, K]
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, int K,
                          int F, hipStream_t st);

@@ -59,6 +59,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -295,6 +296,24 @@ MOE_DEV bf16x8_t frag_kmaj(const char *tile, int row, int step, int lane) {
   return *(const bf16x8_t *)(tile + kmaj_off(row, 2 * step + (lane >> 5)));
 }
 
+// 8-bit operands: a step is 64 reduction elements (64 bytes of the row); lane
+// half h takes the 32 bytes 32h .. 32h+31 (chunks 4 step + 2h, + 1).  A and B
+// fragments are read with the same pattern, so the products pair the same
+// reduction index whatever order the matrix core assigns inside a lane.
+MOE_DEV i32x8 frag_kmaj8(const char *tile, int row, int step, int lane) {
+  const int c = 4 * step + 2 * (lane >> 5);
+  const i32x4 lo = *(const i32x4 *)(tile + kmaj_off(row, c));
+  const i32x4 hi = *(const i32x4 *)(tile + kmaj_off(row, c + 1));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// 32 x 32 x 64 product of E4M3 operands (format code 0 for A and B), fp32
+// accumulation; the block scales of the instruction are left at 2^0 (E8M0 127).
+MOE_DEV f32x16 mfma_f8(const i32x8 &a, const i32x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0x7f7f7f7f, 0,
+                                                         0x7f7f7f7f);
+}
+
 // MN-major: two transposing reads.  In each 16-lane group, lane j supplies the
 // address of 4 consecutive columns of reduction row (j >> 2) and receives the
 // 4 rows of column (j & 15) of the 4 x 16 block.
@@ -357,14 +376,18 @@ template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op, bool DSKIP = SK
 MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
                            int live_mi, int live_ni, f32x16 (&acc)[MI][NI]) {
   constexpr int D = Op::DMA_PER_STAGE;
+  constexpr bool F8 = Op::F8;                           // 8-bit operands, 64-deep steps
+  constexpr int KSt = F8 ? 2 : KS;                      // steps per stage
   constexpr int NM = MI * NI;                           // MFMAs per step
   constexpr int NR = MI + NI + (Op::A_SCALED ? 1 : 0);  // read items per step
   constexpr int NS = Op::A_SCALED ? MI : 0;             // scale items per step
   constexpr int NP = Op::PREFETCH ? 1 : 0;
   constexpr int SLOTS = NM - NS;                        // MFMA slots for reads / DMA
   static_assert(SLOTS > 0, "tile too small");
-  static_assert(KS == 4 && NSTAGE == 2, "pipeline written for 4 steps x 2 stages");
-  bf16x8_t fa[2][MI], fb[2][NI];
+  static_assert((KSt == 4 || KSt == 2) && NSTAGE == 2, "pipeline written for 2 or 4 steps x 2 stages");
+  static_assert(!F8 || (Op::A_KMAJ && Op::B_KMAJ && !Op::A_SCALED), "8-bit operands are K-major");
+  using frag_t = std::conditional_t<F8, i32x8, bf16x8_t>;
+  frag_t fa[2][MI], fb[2][NI];
   float sc[2][8];
 
   // read item f, in order of first use by the next step's MFMAs (mi outer,
@@ -377,25 +400,39 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
       return;
     }
     const int g = f - (Op::A_SCALED ? 1 : 0);
-    if (g == 0 || g > NI) {
-      const int mi = g == 0 ? 0 : g - NI;
-      if (Op::A_KMAJ)
-        fa[slot][mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
-      else
-        fa[slot][mi] = frag_mnmaj(As, wm * 32 + mi * 32 * WGM, step, lane);
+    if constexpr (F8) {
+      if (g == 0 || g > NI) {
+        const int mi = g == 0 ? 0 : g - NI;
+        fa[slot][mi] = frag_kmaj8(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
+      } else {
+        const int ni = g - 1;
+        fb[slot][ni] = frag_kmaj8(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
+      }
+      return;
     } else {
-      const int ni = g - 1;
-      if (Op::B_KMAJ)
-        fb[slot][ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
-      else
-        fb[slot][ni] = frag_mnmaj(Bs, wn * 32 + ni * 32 * WGN, step, lane);
+      if (g == 0 || g > NI) {
+        const int mi = g == 0 ? 0 : g - NI;
+        if (Op::A_KMAJ)
+          fa[slot][mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
+        else
+          fa[slot][mi] = frag_mnmaj(As, wm * 32 + mi * 32 * WGM, step, lane);
+      } else {
+        const int ni = g - 1;
+        if (Op::B_KMAJ)
+          fb[slot][ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
+        else
+          fb[slot][ni] = frag_mnmaj(Bs, wn * 32 + ni * 32 * WGN, step, lane);
+      }
     }
   };
   auto mfma = [&](int slot, int i) __attribute__((always_inline)) {
     const int mi = i / NI, ni = i % NI;
     if (SKIP && (mi >= live_mi || ni >= live_ni)) return;  // wave-uniform
-    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
-                                                          acc[mi][ni], 0, 0, 0);
+    if constexpr (F8)
+      acc[mi][ni] = mfma_f8(fa[slot][mi], fb[slot][ni], acc[mi][ni]);
+    else
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
+                                                            acc[mi][ni], 0, 0, 0);
   };
   // step `step` (< KS-1) of the stage in `buf`: MFMAs on slot step&1, reads of
   // step+1 into the other slot; with PF, the prefetch for stage pf
@@ -416,8 +453,10 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
         else if (decltype(PF)::value)
           op.prefetch(pf);
       }
-      if (NS > 0 && i >= NM - NS)
-        fa[nslot][i - (NM - NS)] = scale_frag(fa[nslot][i - (NM - NS)], sc[nslot]);
+      if constexpr (NS > 0) {
+        if (i >= NM - NS)
+          fa[nslot][i - (NM - NS)] = scale_frag(fa[nslot][i - (NM - NS)], sc[nslot]);
+      }
       MOE_FENCE();
     }
   };
@@ -436,7 +475,9 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
 #pragma unroll
       for (int j = 0; j < DD; ++j)
         if (j * SLOTS / DD == i) op.template issue_part<DSKIP, decltype(CHK)::value>(dma, buf, j);
-      if (NS > 0 && i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
+      if constexpr (NS > 0) {
+        if (i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
+      }
       MOE_FENCE();
     }
   };
@@ -467,7 +508,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   sync();
 #pragma unroll
   for (int j = 0; j < NR; ++j) read_item(0, 0, 0, j);
-  if (NS > 0) {
+  if constexpr (NS > 0) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) fa[0][mi] = scale_frag(fa[0][mi], sc[0]);
   }
@@ -478,11 +519,15 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   // last one of the range lies wholly inside the reduction (an Op whose DMA
   // does not depend on that issues every stage the same way)
   constexpr int PEEL = Op::CHECKED_TAIL ? 1 : 0;
+  // steps 1 .. KSt-2 of a stage (no prefetch, no DMA)
+  auto middle_steps = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 1; st < KSt - 1; ++st) step_inner(buf, st, 0, std::false_type());
+  };
   for (; kt + 2 + PEEL < ke; ++kt) {
     const int buf = (kt - kb) & 1;
     step_inner(buf, 0, kt + 2, std::integral_constant<bool, Op::PREFETCH>());
-    step_inner(buf, 1, 0, std::false_type());
-    step_inner(buf, 2, 0, std::false_type());
+    middle_steps(buf);
     wait_vmcnt<0>();  // stage kt+1 landed
     sync();
     step_last(buf, buf ^ 1, kt + 2, std::true_type(), std::false_type());
@@ -491,8 +536,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   if (PEEL && kt + 2 < ke) {
     const int buf = (kt - kb) & 1;
     step_inner(buf, 0, kt + 2, std::integral_constant<bool, Op::PREFETCH>());
-    step_inner(buf, 1, 0, std::false_type());
-    step_inner(buf, 2, 0, std::false_type());
+    middle_steps(buf);
     wait_vmcnt<0>();
     sync();
     step_last(buf, buf ^ 1, kt + 2, std::true_type(), std::true_type());
@@ -502,8 +546,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   if (kt + 1 < ke) {
     const int buf = (kt - kb) & 1;
     step_inner(buf, 0, 0, std::false_type());
-    step_inner(buf, 1, 0, std::false_type());
-    step_inner(buf, 2, 0, std::false_type());
+    middle_steps(buf);
     wait_vmcnt<0>();
     sync();
     step_last(buf, buf ^ 1, 0, std::false_type(), std::false_type());
@@ -513,8 +556,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   {
     const int buf = (kt - kb) & 1;
     step_inner(buf, 0, 0, std::false_type());
-    step_inner(buf, 1, 0, std::false_type());
-    step_inner(buf, 2, 0, std::false_type());
+    middle_steps(buf);
 #pragma unroll
     for (int i = 0; i < NM; ++i) mfma(1, i);
     MOE_FENCE();
@@ -627,22 +669,38 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
     if (kt + NS - 1 < ke) issue(kt + NS - 1);
     const char *As = lds + buf * Op::STAGE_BYTES;
     const char *Bs = As + Op::A_BYTES;
+    constexpr bool F8 = Op::F8;
 #pragma unroll
-    for (int step = 0; step < KS; ++step) {
-      bf16x8_t fa[MI], fb[NI];
+    for (int step = 0; step < (F8 ? 2 : KS); ++step) {
+      using frag_t = std::conditional_t<F8, i32x8, bf16x8_t>;
+      frag_t fa[MI], fb[NI];
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        fa[mi] = frag_kmaj(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * 32 + mi * 32 * WGM + (lane & 31);
+        if constexpr (F8)
+          fa[mi] = frag_kmaj8(As, row, step, lane);
+        else
+          fa[mi] = frag_kmaj(As, row, step, lane);
+      }
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        fb[ni] = frag_kmaj(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
+      for (int ni = 0; ni < NI; ++ni) {
+        const int row = wn * 32 + ni * 32 * WGN + (lane & 31);
+        if constexpr (F8)
+          fb[ni] = frag_kmaj8(Bs, row, step, lane);
+        else
+          fb[ni] = frag_kmaj(Bs, row, step, lane);
+      }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         if (mi >= live_mi) continue;  // wave-uniform
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] =
-              __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < NI; ++ni) {
+          if constexpr (F8)
+            acc[mi][ni] = mfma_f8(fa[mi], fb[ni], acc[mi][ni]);
+          else
+            acc[mi][ni] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+        }
       }
     }
   }
@@ -672,6 +730,8 @@ struct FwdArgs {
   int a_by_row;      // 1: A row of schedule row r is row r itself (an operand already in
                      // schedule order, e.g. the gated FFN's intermediate); 0: gather by token
   int tile_rows;     // routed, BM = 256: 0 = picked on the device, 128 / 256 = forced
+  const float *x_scale;  // 8-bit operands: per-token scale [T]
+  const float *w_scale;  // 8-bit operands: per-expert output-channel scale [E, N]
 };
 
 // What a forward-shaped kernel writes:
@@ -683,9 +743,12 @@ struct FwdArgs {
 //               block ni + NI/2 hold the gate and the up value of the same f
 enum { FWD_BARE = 0, FWD_SCATTER = 1, FWD_GATED = 2 };
 
-template <int BM, int BN, int NW>
+// F8: 8-bit operands (a stage is 128 reduction elements; K below is the
+// reduction length in 2-byte units, i.e. row bytes / 2, for the bounds checks)
+template <int BM, int BN, int NW, bool F8_ = false>
 struct FwdOp {
   static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false, PREFETCH = false;
+  static constexpr bool F8 = F8_;
   static constexpr bool CHECKED_TAIL = true;
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
   static constexpr int DMA_PER_STAGE = DA + DB;
@@ -707,8 +770,9 @@ struct FwdOp {
 };
 
 // A (BM rows) and B (BN rows) K-major for the deep pipeline of small tiles.
-template <int BM, int BN, int NW>
+template <int BM, int BN, int NW, bool F8_ = false>
 struct FwdDeepOp {
+  static constexpr bool F8 = F8_;  // as FwdOp
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
   static_assert(DA >= 1 && DB >= 1, "at least one DMA row group per wave");
   static constexpr int DMA_PER_STAGE = DA + DB;
@@ -739,20 +803,23 @@ struct FwdDeepOp {
   }
 };
 
-template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout>
+template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout, bool F8 = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr bool FUSED = MODE != FWD_BARE;       // rows come from a routing schedule
   constexpr bool GATED = MODE == FWD_GATED;
   constexpr int BNO = GATED ? BN / 2 : BN;        // output columns per tile
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   static_assert(!GATED || NI % 2 == 0, "gate and up blocks pair up inside a wave");
+  static_assert(!F8 || MODE == FWD_SCATTER, "8-bit operands: the routed scatter forward");
   constexpr int NW = WGM * WGN, NTH = NW * 64;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  constexpr int ESZ = F8 ? 1 : 2;                 // bytes per operand element
   extern __shared__ __attribute__((aligned(16))) char lds[];  // NSTAGE x (A, B)
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
   __shared__ __attribute__((aligned(16))) int tok[BM];
   __shared__ __attribute__((aligned(16))) float wgt[BM];
   __shared__ int rowoff_a[BM], rowoff_b[BN];
+  __shared__ float cscale[F8 ? BN : 1];           // 8-bit: the tile's output-channel scales
   __shared__ int scratch[NTH / kWave + 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -760,11 +827,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   const int wm = wid / WGN, wn = wid % WGN;
   const int E = p.E, K = p.K, N = p.N;
   const int tiles_n = (N + BNO - 1) / BNO;
-  const int KI = (K + BK - 1) / BK;
+  const int KI = (K * ESZ + KROW - 1) / KROW;     // stages of 128 bytes per row
   // rows per tile of this launch (uniform over the grid): BM, or with routed
-  // 256-row kernels possibly 128 (the 128 x 256 shape)
+  // 256-row kernels possibly 128 (the 128 x 256 shape).  8-bit operands always
+  // take 128-row tiles: a 256 x 256 accumulator with double-buffered 32-byte
+  // fragments does not fit the registers of 8 waves per compute unit.
   const int BMr = (FUSED && BM == 256)
-                      ? pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows)
+                      ? (F8 ? 128 : pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows))
                       : BM;
   if (FUSED)
     group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * (E + 1), E,
@@ -772,13 +841,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   else
     group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
   const int total = bs[E] * tiles_n;
-  FwdOp<BM, BN, NW> op;
+  FwdOp<BM, BN, NW, F8> op;
   op.rsA = uniform_rsrc(p.A, p.a_bytes);
   op.lds0 = lds_addr(lds);
-  op.K = K;
+  op.K = K * ESZ / 2;  // reduction length in 2-byte units (the bounds checks' unit)
   op.wid = wid;
   const int wrows = GATED ? 2 * N : N;  // rows of one expert's weight
-  const uint32_t wbytes = (uint32_t)wrows * K * 2;
+  const uint32_t rowbytes = (uint32_t)K * ESZ;
+  const uint32_t wbytes = (uint32_t)wrows * rowbytes;
 
   const int Lb = logical_block();
   WorkSplit ws;
@@ -810,15 +880,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       const int r = c.row0 + tid;
       const int t = ok ? (FUSED ? p.row_to_token[r] : (r < p.M ? r : -1)) : -1;
       tok[tid] = t;
-      wgt[tid] = (FUSED && ok) ? p.row_weight[r] : 0.f;
-      rowoff_a[tid] = t >= 0 ? (p.a_by_row ? r : t) * K * 2 : -1;
+      // 8-bit: the token's scale rides on its routing weight
+      wgt[tid] = (FUSED && ok) ? p.row_weight[r] * (F8 && t >= 0 ? p.x_scale[t] : 1.f) : 0.f;
+      rowoff_a[tid] = t >= 0 ? (p.a_by_row ? r : t) * (int)rowbytes : -1;
     }
     for (int j = tid; j < BN; j += NTH) {
       const int jj = GATED ? j % BNO : j;  // gated: gate rows, then the up rows
-      rowoff_b[j] = jj < ncols ? (n0 + jj + (GATED && j >= BNO ? N : 0)) * K * 2 : -1;
+      rowoff_b[j] = jj < ncols ? (n0 + jj + (GATED && j >= BNO ? N : 0)) * (int)rowbytes : -1;
+      if (F8) cscale[j] = jj < ncols ? p.w_scale[(size_t)c.g * N + n0 + jj] : 0.f;
     }
     __syncthreads();
-    op.rsW = uniform_rsrc(p.W + (size_t)c.g * wrows * K, wbytes);
+    op.rsW = uniform_rsrc((const char *)p.W + (size_t)c.g * wrows * rowbytes, wbytes);
     const bool part = BM <= 64 || ws.nS > 1 || BMr < BM;  // rows / columns partly dead
     // (gated: the live B rows are two runs, not a prefix; nothing is skipped)
     const int live_b = GATED ? BN : ncols;
@@ -842,19 +914,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
       if constexpr (decltype(DEEP_)::value) {
         constexpr int BMs = MIc * 32 * WGM, BNs = NIc * 32 * WGN;  // rows of A and of B
-        FwdDeepOp<BMs, BNs, NW> dop;
+        FwdDeepOp<BMs, BNs, NW, F8> dop;
         dop.rsA = op.rsA;
         dop.rsW = op.rsW;
         dop.lds0 = op.lds0;
-        dop.K = K;
+        dop.K = K * ESZ / 2;
         dop.wid = wid;
         dop.da.setup(wid, lane, rowoff_a, c.rows);
         dop.db.setup(wid, lane, rowoff_b, GATED ? BNs : ncols);
         tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi,
                                                dop.parts(), acc);
       } else {
-        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW>, DSK>(op, lds, kb, ke, wm, wn,
-                                                                       lane, live_mi, NIc, acc);
+        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8>, DSK>(op, lds, kb, ke, wm, wn,
+                                                                           lane, live_mi, NIc, acc);
       }
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
@@ -900,6 +972,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         for (int ni = 0; ni < NIc; ++ni)
           cb[ni] = (uint32_t)(n0 + wn * 32 + ni * 32 * WGN + (lane & 31)) * 4u;
         const int cl0 = wn * 32 + (lane & 31);
+        float cs[NIc];  // 8-bit: output-channel scale of each column block
+#pragma unroll
+        for (int ni = 0; ni < NIc; ++ni) cs[ni] = F8 ? cscale[cl0 + ni * 32 * WGN] : 1.f;
 #pragma unroll
         for (int mi = 0; mi < MIc; ++mi) {
           if (mi >= live_mi) continue;
@@ -915,7 +990,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
 #pragma unroll
               for (int ni = 0; ni < NIc; ++ni) {
                 if (!all_cols && cl0 + ni * 32 * WGN >= ncols) continue;
-                unsafeAtomicAdd((float *)(yb + (ro + cb[ni])), w4[q] * acc[mi][ni][4 * j + q]);
+                const float v = F8 ? w4[q] * cs[ni] * acc[mi][ni][4 * j + q]
+                                   : w4[q] * acc[mi][ni][4 * j + q];
+                unsafeAtomicAdd((float *)(yb + (ro + cb[ni])), v);
               }
             }
           }
@@ -978,7 +1055,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         else
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
-      } else {
+      } else if constexpr (!F8) {
         if (ws.nS == 8)
           tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
                true_type(), false_type());
@@ -1030,7 +1107,7 @@ template <int NW>
 struct DxOp {
   using Map = MnmajMapT<NW>;
   static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false, PREFETCH = false;
-  static constexpr bool CHECKED_TAIL = true;
+  static constexpr bool CHECKED_TAIL = true, F8 = false;
   static constexpr int DA = 256 / (8 * NW), PW = Map::PER_WAVE;
   static constexpr int DMA_PER_STAGE = DA + PW;
   KmajDma<256, NW> da;
@@ -1319,6 +1396,7 @@ struct DwOp {
   static constexpr int PW = Map::PER_WAVE;  // dY (and x) instructions per wave per stage
   static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
   static constexpr bool CHECKED_TAIL = false;  // offsets are data dependent every stage
+  static constexpr bool F8 = false;
   // per stage: PW dY + PW x instructions, the stage's routing weights, the
   // tokens of the stage two ahead
   static constexpr int DMA_PER_STAGE = 2 * PW + 1 + 1;
@@ -1568,38 +1646,38 @@ bool mfma_supported(int K, int N) { return K % 8 == 0 && N % 8 == 0; }
 
 namespace {
 // Launch a 256 x 256 forward-shaped kernel with 4 (2 x 2) or 8 (2 x 4) waves.
-template <int MODE, typename Tout>
+template <int MODE, typename Tout, bool F8 = false>
 hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
   if (gemm_waves() == 4) {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8>>(kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout>), grid, dim3(256), kStageLds,
-                       st, a);
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8>), grid, dim3(256),
+                       kStageLds, st, a);
   } else {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8>>(kStageLds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout>), grid, dim3(512), kStageLds,
-                       st, a);
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8>), grid, dim3(512),
+                       kStageLds, st, a);
   }
   return hipGetLastError();
 }
 
 // Routed forward-shaped launch: masked schedules of capacity <= 64 take 64-row
 // tiles (one row block per expert), everything else 256 x 256 tiles.
-template <int MODE>
+template <int MODE, bool F8 = false>
 hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
   a.bstart = s.block_start;
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
-    auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float>>(kStageLds);
+    auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8>;
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
     return hipGetLastError();
   }
   a.tile_rows = forced_bm();
-  return launch_fwd256<MODE, float>(a, st);
+  return launch_fwd256<MODE, float, F8>(a, st);
 }
 }  // namespace
 
@@ -1619,6 +1697,17 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
             (uint32_t)(arows * K * 2), stream_k_mode(), tail_split(), (int)s.T,
             a_by_row ? 1 : 0};
   return launch_routed<FWD_SCATTER>(a, s, st);
+}
+
+hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *Wq,
+                              const float *w_scale, const moe_schedule &s, float *y, int K, int N,
+                              hipStream_t st) {
+  FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
+            s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
+            (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T, 0};
+  a.x_scale = x_scale;
+  a.w_scale = w_scale;
+  return launch_routed<FWD_SCATTER, true>(a, s, st);
 }
 
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, int K,

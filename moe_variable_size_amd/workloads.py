@@ -340,6 +340,51 @@ def gated_page_example(seed: int = BASE_SEED + 6, dense: bool = True) -> Gated:
                  2, seed=seed, routing="balanced", weights="uniform", dense=dense)
 
 
+@dataclass
+class Fp8Routed:
+    """Inputs of the 8-bit routed forward: E4M3 codes with a per-token scale
+    for x and a per-expert output-channel scale for W."""
+
+    name: str
+    T: int
+    K: int
+    N: int
+    E: int
+    k: int
+    xq: np.ndarray                 # [T, K] uint8 E4M3 codes
+    x_scale: np.ndarray            # [T] float32
+    Wq: np.ndarray                 # [E, N, K] uint8 E4M3 codes
+    w_scale: np.ndarray            # [E, N] float32
+    expert_ids: np.ndarray
+    topk_weights: Optional[np.ndarray]
+    capacity: int = 0
+
+
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3_rows(a: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Scale each row of ``a`` (last axis) by max|row| / 448 and round to the
+    nearest E4M3 code (torch's float8_e4m3fn conversion).  Returns (codes
+    uint8 with the shape of ``a``, scales float32 with one per row; 1 for an
+    all-zero row)."""
+    import torch
+    a = np.asarray(a, dtype=np.float32)
+    amax = np.abs(a).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = torch.from_numpy(np.ascontiguousarray(a / scale[..., None])).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8).numpy(), scale
+
+
+def fp8_routed(r: Routed) -> Fp8Routed:
+    """8-bit version of a routed workload: x and every expert's weight rows
+    quantized row by row from the workload's own values."""
+    xq, sx = quantize_e4m3_rows(r.x.values)
+    Wq, sw = quantize_e4m3_rows(r.W.values)
+    return Fp8Routed(r.name + "_e4m3", r.T, r.K, r.N, r.E, r.k, xq, sx, Wq, sw, r.expert_ids,
+                     r.topk_weights, capacity=r.capacity)
+
+
 def grouped_as_routed(g: Grouped) -> Routed:
     """The weight-gradient stress case seen as a routed layer with k=1 and rows
     already in expert order (token r belongs to group g(r)), routing weight 1."""

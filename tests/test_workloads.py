@@ -83,3 +83,18 @@ def test_balanced_routing_and_gated_example():
     g = W.gated_page_example(dense=False)
     assert (g.T, g.K, g.F, g.N, g.E, g.k) == (8192, 4096, 2048, 4096, 64, 2)
     assert (np.bincount(g.expert_ids.ravel(), minlength=64) == 256).all()
+
+
+def test_e4m3_quantization_bounds():
+    """Row scales map each row's largest magnitude to 448; every code decodes
+    (torch) to within half an E4M3 step of the scaled value."""
+    import torch
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal((5, 64)).astype(np.float32)
+    a[2] = 0.0
+    q, s = W.quantize_e4m3_rows(a)
+    assert q.dtype == np.uint8 and s.shape == (5,) and s[2] == 1.0
+    v = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy()
+    assert np.allclose(np.abs(v).max(axis=1)[[0, 1, 3, 4]], 448.0)
+    rel = np.abs(v * s[:, None] - a) / np.maximum(np.abs(a), 2.0 ** -6 * s[:, None])
+    assert rel.max() <= 2.0 ** -4 + 1e-6
