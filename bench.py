@@ -12,9 +12,10 @@ x, dY ~ N(0,1), W ~ N(0,1/K), bf16 storage with fp32 accumulation.
 Metric: useful TFLOP/s = (2SKN forward + 4SKN backward + 2SN routing-weight
 gradient) / step time, S = T*top_k; padding is never counted.
 
-Two more objects ride on the same line: "decode" (masked decode forward,
-HBM GB/s) and "gated_ffn" (gated expert FFN forward on the balanced step of
-the page's worked example, TFLOP/s).
+More objects ride on the same line: "decode" (masked decode forward, HBM
+GB/s), "fp8" (the 8-bit forward on the config-2 shape and the masked decode)
+and "gated_ffn" (gated expert FFN forward on the balanced step of the page's
+worked example, TFLOP/s).
 
 Prints ONE JSON line.  --gpus above 1 is not supported (one GPU per process,
 single-GPU machine) and exits with a message.
@@ -38,6 +39,7 @@ METRIC = ("useful TFLOP/s (2·S·K·N) + % bf16 MFMA peak, fused MoE fwd/bwd; "
           "decode HBM GB/s")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA (published)
 
 
 def _args():
@@ -48,6 +50,7 @@ def _args():
                    help="untimed steps first (also brings the GPU clocks to their loaded state)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit forward lines")
     p.add_argument("--no-gated", action="store_true",
                    help="skip the gated expert FFN line (its inputs take ~10 s to draw)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -203,6 +206,63 @@ def gated_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
                          "frac": round(up_tf / PEAK_BF16_TFLOPS, 4)}}
 
 
+def fp8_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
+    """8-bit (E4M3) forward with per-token and per-expert-channel scales on the
+    config-2 shape (useful TFLOP/s against the 8-bit dense peak) and on the
+    config-5 masked decode (HBM GB/s of the algorithmic bytes: 1-byte weights
+    of the active experts + x codes + y)."""
+    out = {}
+    for name, r, lay in (("fwd", WL.config2(with_dy=False), api.MOE_LAYOUT_CONTIGUOUS),
+                         ("decode", WL.config5(), api.MOE_LAYOUT_MASKED)):
+        f = WL.fp8_routed(r)
+
+        def u8(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        xq, sx, Wq, sw = u8(f.xq), u8(f.x_scale), u8(f.Wq), u8(f.w_scale)
+        ids, w = u8(f.expert_ids), u8(f.topk_weights)
+        ws = torch.empty(api.moe_schedule_workspace_bytes(f.T, f.k, f.E, lay, r.capacity),
+                         dtype=torch.uint8, device=dev)
+        y = torch.empty((f.T, f.N), dtype=torch.float32, device=dev)
+
+        def step():
+            sch = api.moe_build_schedule(ids, w, f.E, layout=lay, capacity=r.capacity, workspace=ws)
+            api.moe_fused_fwd_fp8(xq, sx, Wq, sw, sch, y=y)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms_step = (time.perf_counter() - t0) * 1e3 / steps
+        api.moe_timing_enable(True)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        api.moe_timing_enable(False)
+        tot, n = api.moe_timing_read("fused_fwd_fp8")
+        us = tot * 1e3 / max(n, 1)
+        S = f.T * f.k
+        if name == "fwd":
+            tf = 2.0 * S * f.K * f.N / (us * 1e-6) / 1e12
+            out[name] = {"workload": f"{f.name} forward (schedule + zero y + fp8 forward)",
+                         "fwd_us": round(us, 3), "tflops": round(tf, 2),
+                         "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+                         "step_ms": round(ms_step, 4)}
+        else:
+            active = int(np.count_nonzero(np.bincount(f.expert_ids.ravel(), minlength=f.E)))
+            nbytes = active * f.N * f.K + f.T * f.K + f.T * f.N * 4
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[name] = {"workload": f"{f.name} forward (masked layout)",
+                         "bytes_per_launch": nbytes, "fwd_us": round(us, 3),
+                         "hbm_GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+                         "step_ms": round(ms_step, 4)}
+        del xq, Wq, y
+    return out
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -307,6 +367,8 @@ def main():
         out["roofline"]["traffic"] = tr
     if not a.no_decode:
         out["decode"] = decode_line(torch, api, WL, dev, a.steps, a.warmup)
+    if not a.no_fp8:
+        out["fp8"] = fp8_line(torch, api, WL, dev, min(a.steps, 100), min(a.warmup, 50))
     if not a.no_gated:
         out["gated_ffn"] = gated_line(torch, api, WL, dev, min(a.steps, 50), min(a.warmup, 20))
     if not a.no_cpu_baseline:
