@@ -21,6 +21,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -28,8 +29,9 @@ KERNEL_SOURCES = ("moe_variable_size_amd/csrc/mfma.hip", "moe_variable_size_amd/
                   "moe_variable_size_amd/csrc/api.hip")
 COPY_BYTES = 256 << 20   # bench.py --calib-copy: 64 Mi float32 copied device to device
 
-FAMILIES = (("mfma_fwd_kernel<256", "fused_fwd"), ("mfma_dx_kernel", "bwd_dx"),
-            ("mfma_dw_kernel", "bwd_dw"), ("mfma_fwd_kernel<64", "decode_fwd"))
+# forward-shaped kernels: mfma_fwd_kernel<BM, BN, WGM, WGN, MODE, Tout, F8>
+_FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+), (true|false)>")
+FWD_MODES = {0: "grouped_gemm", 1: "fused_fwd", 2: "gated_up", 3: "gated_down"}
 
 
 def source_digest() -> str:
@@ -42,11 +44,22 @@ def source_digest() -> str:
 
 
 def _family(name: str):
+    """Kernel family of a demangled kernel name (None: not counted)."""
     if "copyBuffer" in name or "copy_kernel" in name or "CopyKernel" in name:
         return "copy"
-    for key, fam in FAMILIES:
-        if key in name:
-            return fam
+    m = _FWD.search(name)
+    if m:
+        bm, mode, f8 = int(m.group(1)), int(m.group(5)), m.group(7) == "true"
+        fam = FWD_MODES.get(mode)
+        if fam is None:
+            return None
+        if fam == "fused_fwd" and bm == 64:
+            fam = "decode_fwd"
+        return fam + "_fp8" if f8 else fam
+    if "mfma_dx_kernel" in name:
+        return "bwd_dx"
+    if "mfma_dw_kernel" in name:
+        return "bwd_dw"
     return None
 
 

@@ -727,8 +727,6 @@ struct FwdArgs {
   int stream_k;      // 1: split the last partial wave of tiles along K
   int tail_split;    // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int M;             // bare: rows of A and C (rows at or past M are never touched)
-  int a_by_row;      // 1: A row of schedule row r is row r itself (an operand already in
-                     // schedule order, e.g. the gated FFN's intermediate); 0: gather by token
   int tile_rows;     // routed, BM = 256: 0 = picked on the device, 128 / 256 = forced
   const float *x_scale;  // 8-bit operands: per-token scale [T]
   const float *w_scale;  // 8-bit operands: per-expert output-channel scale [E, N]
@@ -736,12 +734,15 @@ struct FwdArgs {
 
 // What a forward-shaped kernel writes:
 //   FWD_BARE    C[r, n] = acc (fp32 or bf16 store; rows grouped by end offsets)
-//   FWD_SCATTER y[token(r), n] += w_r * acc (atomic; routing schedule)
+//   FWD_SCATTER y[token(r), n] += w_r * acc (atomic; routing schedule), A row of
+//               schedule row r gathered from token(r)
 //   FWD_GATED   h[r, f] = silu(acc_gate) * acc_up in bf16 (routing schedule): the
 //               B tile holds 128 gate rows f0.. and the 128 up rows F + f0.. of a
 //               doubled [2F, K] weight, so each wave's column block ni < NI/2 and
 //               block ni + NI/2 hold the gate and the up value of the same f
-enum { FWD_BARE = 0, FWD_SCATTER = 1, FWD_GATED = 2 };
+//   FWD_SCATTER_ROWS  as FWD_SCATTER with A already in schedule row order (A row
+//               r is row r: the gated FFN's intermediate), nothing gathered
+enum { FWD_BARE = 0, FWD_SCATTER = 1, FWD_GATED = 2, FWD_SCATTER_ROWS = 3 };
 
 // F8: 8-bit operands (a stage is 128 reduction elements; K below is the
 // reduction length in 2-byte units, i.e. row bytes / 2, for the bounds checks)
@@ -807,6 +808,7 @@ template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout, bool F8 = f
 __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr bool FUSED = MODE != FWD_BARE;       // rows come from a routing schedule
   constexpr bool GATED = MODE == FWD_GATED;
+  constexpr bool A_BY_ROW = MODE == FWD_SCATTER_ROWS;
   constexpr int BNO = GATED ? BN / 2 : BN;        // output columns per tile
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   static_assert(!GATED || NI % 2 == 0, "gate and up blocks pair up inside a wave");
@@ -882,7 +884,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       tok[tid] = t;
       // 8-bit: the token's scale rides on its routing weight
       wgt[tid] = (FUSED && ok) ? p.row_weight[r] * (F8 && t >= 0 ? p.x_scale[t] : 1.f) : 0.f;
-      rowoff_a[tid] = t >= 0 ? (p.a_by_row ? r : t) * (int)rowbytes : -1;
+      rowoff_a[tid] = t >= 0 ? (A_BY_ROW ? r : t) * (int)rowbytes : -1;
     }
     for (int j = tid; j < BN; j += NTH) {
       const int jj = GATED ? j % BNO : j;  // gated: gate rows, then the up rows
@@ -1694,8 +1696,8 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
   const size_t arows = a_by_row ? (size_t)s.R : (size_t)s.T;
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)(arows * K * 2), stream_k_mode(), tail_split(), (int)s.T,
-            a_by_row ? 1 : 0};
+            (uint32_t)(arows * K * 2), stream_k_mode(), tail_split(), (int)s.T};
+  if (a_by_row) return launch_routed<FWD_SCATTER_ROWS>(a, s, st);
   return launch_routed<FWD_SCATTER>(a, s, st);
 }
 
@@ -1704,7 +1706,7 @@ hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *
                               hipStream_t st) {
   FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T, 0};
+            (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T};
   a.x_scale = x_scale;
   a.w_scale = w_scale;
   return launch_routed<FWD_SCATTER, true>(a, s, st);
@@ -1714,7 +1716,7 @@ hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s,
                          int F, hipStream_t st) {
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W_gu, h, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, F,
-            (uint32_t)((size_t)s.T * K * 2), 0, tail_split(), (int)s.T, 0};
+            (uint32_t)((size_t)s.T * K * 2), 0, tail_split(), (int)s.T};
   return launch_routed<FWD_GATED>(a, s, st);
 }
 

@@ -1,0 +1,18 @@
+"""Kernel-family attribution of the HBM counter reduction (host logic only)."""
+from moe_variable_size_amd import counters as C
+
+
+def test_families_of_demangled_names():
+    ns = "moe::(anonymous namespace)::"
+    f = lambda t: C._family(ns + t + "(moe::(anonymous namespace)::FwdArgs)")
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, false>") == "fused_fwd"
+    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, false>") == "decode_fwd"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, true>") == "fused_fwd_fp8"
+    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, true>") == "decode_fwd_fp8"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 2, float, false>") == "gated_up"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 3, float, false>") == "gated_down"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 0, unsigned short, false>") == "grouped_gemm"
+    assert C._family(ns + "mfma_dx_kernel<4>(moe::(anonymous namespace)::DxArgs)") == "bwd_dx"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8>(DwArgs)") == "bwd_dw"
+    assert C._family("__amd_rocclr_copyBuffer") == "copy"
+    assert C._family(ns + "sched_hist_kernel(int const*)") is None
