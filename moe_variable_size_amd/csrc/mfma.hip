@@ -831,11 +831,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   const int tiles_n = (N + BNO - 1) / BNO;
   const int KI = (K * ESZ + KROW - 1) / KROW;     // stages of 128 bytes per row
   // rows per tile of this launch (uniform over the grid): BM, or with routed
-  // 256-row kernels possibly 128 (the 128 x 256 shape).  8-bit operands always
-  // take 128-row tiles: a 256 x 256 accumulator with double-buffered 32-byte
-  // fragments does not fit the registers of 8 waves per compute unit.
+  // 256-row kernels possibly 128 (the 128 x 256 shape).  8-bit operands with 8
+  // waves always take 128-row tiles: a 256 x 256 accumulator with
+  // double-buffered 32-byte fragments does not fit the registers of 8 waves
+  // per compute unit (4 waves, one per SIMD, have twice the registers).
+  constexpr bool F8_HALF = F8 && NW == 8;
   const int BMr = (FUSED && BM == 256)
-                      ? (F8 ? 128 : pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows))
+                      ? (F8_HALF ? 128 : pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows))
                       : BM;
   if (FUSED)
     group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * (E + 1), E,
@@ -1057,7 +1059,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         else
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
-      } else if constexpr (!F8) {
+      } else if constexpr (!F8_HALF) {
         if (ws.nS == 8)
           tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
                true_type(), false_type());
@@ -1614,6 +1616,16 @@ int forced_bm() {
   return v;
 }
 
+// MOE_VS_F8_WAVES=4: 8-bit forward with 4 waves (256 x 256 tiles) instead of 8
+// (128 x 256 tiles) (read once)
+int f8_waves() {
+  static const int v = [] {
+    const char *e = getenv("MOE_VS_F8_WAVES");
+    return e && atoi(e) == 4 ? 4 : 8;
+  }();
+  return v;
+}
+
 // MOE_VS_DX_WAVES=8: input-gradient kernel with 8 waves per workgroup instead of
 // 4 (its routing-weight epilogue runs short of registers with 8)
 int dx_waves() {
@@ -1651,7 +1663,7 @@ namespace {
 template <int MODE, typename Tout, bool F8 = false>
 hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
-  if (gemm_waves() == 4) {
+  if ((F8 ? f8_waves() : gemm_waves()) == 4) {
     hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8>), grid, dim3(256),
