@@ -396,6 +396,114 @@ def gated_ffn_forward_explicit(x, W_gu, W_down, expert_ids, topk_weights, E: int
     return y
 
 
+def gated_ffn_backward(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=np.float64):
+    """Gradients of L = sum(dY * y) for the gated FFN, by the chain rule per
+    expert.  With z = h W_down^T, h = silu(g) * u, (g | u) = x W_gu^T:
+      dh = w * dY W_down;  dg = dh * u * silu'(g),  du = dh * silu(g),
+      silu'(g) = s (1 + g (1 - s)) with s = 1 / (1 + exp(-g));
+      dX[t] += (dg | du) W_gu;  dW_gu[e] = sum (dg | du)^T x;
+      dW_down[e] = sum (w dY)^T h;  d_w[s] = dY[t] . z[s] (the unweighted
+      down-projection output).
+    Returns dX [T, K], dW_gu [E, 2F, K], dW_down [E, N, F], d_w [T, k]."""
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.reshape(-1)
+    wflat = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    F = W_gu.shape[1] // 2
+    K = np.asarray(x).shape[1]
+    N = W_down.shape[1]
+    dX = np.zeros((T, K), dtype=acc)
+    dWgu = np.zeros((E, 2 * F, K), dtype=acc)
+    dWd = np.zeros((E, N, F), dtype=acc)
+    d_w = np.zeros(T * k, dtype=acc)
+    for e in range(E):
+        s_e = np.nonzero(ids == e)[0]
+        if s_e.size == 0:
+            continue
+        tok = s_e // k
+        xe = np.asarray(x)[tok].astype(acc)
+        gu = xe @ W_gu[e].astype(acc).T
+        g, u = gu[:, :F].astype(np.float64), gu[:, F:].astype(np.float64)
+        sg = 1.0 / (1.0 + np.exp(-g))
+        h = (g * sg * u).astype(acc)
+        we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
+        dYe = np.asarray(dY)[tok].astype(acc)
+        Wd = W_down[e].astype(acc)
+        d_w[s_e] = np.sum(dYe * (h @ Wd.T), axis=1)
+        dh = we[:, None] * (dYe @ Wd)
+        dg = (dh * u * sg * (1.0 + g * (1.0 - sg))).astype(acc)
+        du = (dh * g * sg).astype(acc)
+        dgu = np.concatenate([dg, du], axis=1)
+        np.add.at(dX, tok, dgu @ W_gu[e].astype(acc))
+        dWgu[e] = dgu.T @ xe
+        dWd[e] = (we[:, None] * dYe).T @ h
+    return dX, dWgu, dWd, d_w.reshape(T, k)
+
+
+def gated_ffn_backward_rows(dY, x, W_gu, W_down, expert_ids, topk_weights, tokens, *,
+                            acc=np.float64):
+    """dX[t] and d_w[t, :] of the gated FFN for the listed tokens only."""
+    expert_ids = np.asarray(expert_ids)
+    k = expert_ids.shape[1]
+    F = W_gu.shape[1] // 2
+    dX = np.zeros((len(tokens), np.asarray(x).shape[1]), dtype=acc)
+    dw = np.zeros((len(tokens), k), dtype=acc)
+    for i, t in enumerate(tokens):
+        xt = np.asarray(x)[t].astype(acc)
+        gy = np.asarray(dY)[t].astype(acc)
+        for j in range(k):
+            e = int(expert_ids[t, j])
+            w = 1.0 if topk_weights is None else float(topk_weights[t, j])
+            gu = W_gu[e].astype(acc) @ xt
+            g, u = gu[:F], gu[F:]
+            sg = 1.0 / (1.0 + np.exp(-g))
+            h = g * sg * u
+            Wd = W_down[e].astype(acc)
+            dw[i, j] = gy @ (Wd @ h)
+            dh = w * (gy @ Wd)
+            dgu = np.concatenate([dh * u * sg * (1.0 + g * (1.0 - sg)), dh * g * sg])
+            dX[i] += dgu @ W_gu[e].astype(acc)
+    return dX, dw
+
+
+def gated_weight_grad_entries(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int,
+                              gu_entries, down_entries, *, acc=np.float64):
+    """Listed entries of dW_gu [(e, j, k)] and dW_down [(e, n, f)], from sums
+    over the expert's assignments."""
+    expert_ids = np.asarray(expert_ids)
+    kk = expert_ids.shape[1]
+    ids = expert_ids.reshape(-1)
+    wflat = None if topk_weights is None else np.asarray(topk_weights).reshape(-1)
+    F = W_gu.shape[1] // 2
+    cache = {}
+
+    def rows(e):
+        if e not in cache:
+            s_e = np.nonzero(ids == e)[0]
+            tok = s_e // kk
+            xe = np.asarray(x)[tok].astype(acc)
+            gu = xe @ W_gu[e].astype(acc).T
+            g, u = gu[:, :F], gu[:, F:]
+            sg = 1.0 / (1.0 + np.exp(-g))
+            h = g * sg * u
+            we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
+            dYe = np.asarray(dY)[tok].astype(acc)
+            dh = we[:, None] * (dYe @ W_down[e].astype(acc))
+            dgu = np.concatenate([dh * u * sg * (1.0 + g * (1.0 - sg)), dh * g * sg], axis=1)
+            cache[e] = (xe, h, we, dYe, dgu)
+        return cache[e]
+
+    out_gu = np.zeros(len(gu_entries), dtype=acc)
+    for i, (e, j, kc) in enumerate(gu_entries):
+        xe, _, _, _, dgu = rows(e)
+        out_gu[i] = np.sum(dgu[:, j] * xe[:, kc])
+    out_d = np.zeros(len(down_entries), dtype=acc)
+    for i, (e, n, f) in enumerate(down_entries):
+        _, h, we, dYe, _ = rows(e)
+        out_d[i] = np.sum(we * dYe[:, n] * h[:, f])
+    return out_gu, out_d
+
+
 def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.float64):
     """Gated FFN on the masked layout.  Returns (y [T, N], h [E*capacity, F]);
     h rows of empty slots are zero (the library leaves them unwritten)."""

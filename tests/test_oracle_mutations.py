@@ -131,9 +131,41 @@ def _fp8_channel_scale_on_rows(xq, x_scale, Wq, w_scale, expert_ids, topk_weight
                                     topk_weights, E, acc=acc)      # one scale per expert only
 
 
+def _gated_bwd_sigmoid_derivative(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+    """silu' taken as the logistic function alone (the g s (1 - s) term dropped)."""
+    saved = np.exp
+    dX, dWgu, dWd, d_w = _ORIG["gated_ffn_backward"](dY, x, W_gu, W_down, expert_ids, topk_weights, E,
+                                                      acc=acc)
+    F = W_gu.shape[1] // 2
+    ids = np.asarray(expert_ids).reshape(-1)
+    k = np.asarray(expert_ids).shape[1]
+    wflat = np.asarray(topk_weights).reshape(-1)
+    dX2 = np.zeros_like(dX)
+    for e in range(E):
+        s_e = np.nonzero(ids == e)[0]
+        if s_e.size == 0:
+            continue
+        tok = s_e // k
+        xe = np.asarray(x)[tok]
+        gu = xe @ W_gu[e].T
+        g, u = gu[:, :F], gu[:, F:]
+        sg = 1.0 / (1.0 + saved(-g))
+        dh = wflat[s_e][:, None] * (np.asarray(dY)[tok] @ W_down[e])
+        dgu = np.concatenate([dh * u * sg, dh * g * sg], axis=1)
+        np.add.at(dX2, tok, dgu @ W_gu[e])
+    return dX2, dWgu, dWd, d_w
+
+
+def _gated_bwd_weighted_dw(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+    dX, dWgu, dWd, d_w = _ORIG["gated_ffn_backward"](dY, x, W_gu, W_down, expert_ids, topk_weights, E,
+                                                      acc=acc)
+    return dX, dWgu, dWd, d_w * np.asarray(topk_weights)
+
+
 _ORIG = {n: getattr(O, n) for n in ["routing_schedule", "tile_owner", "tile_coords", "moe_forward",
                                      "grouped_gemm", "moe_backward", "gated_activation",
-                                     "gated_ffn_forward", "decode_e4m3", "moe_forward_fp8"]}
+                                     "gated_ffn_forward", "decode_e4m3", "moe_forward_fp8",
+                                     "gated_ffn_backward"]}
 
 CASES = [
     ("end offsets replaced by start offsets", "routing_schedule", lambda: _mut_start_offsets(_ORIG["routing_schedule"]),
@@ -170,6 +202,11 @@ CASES = [
      [P.test_e4m3_decode_against_torch]),
     ("fp8 token scale dropped", "moe_forward_fp8", lambda: _fp8_no_token_scale,
      [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),
+    ("silu derivative without its g term", "gated_ffn_backward", lambda: _gated_bwd_sigmoid_derivative,
+     [P.test_gated_backward_finite_differences]),
+    ("gated routing-weight gradient from the weighted product", "gated_ffn_backward",
+     lambda: _gated_bwd_weighted_dw,
+     [P.test_gated_backward_finite_differences, P.test_gated_backward_identities]),
     ("fp8 channel scale collapsed to one per expert", "moe_forward_fp8",
      lambda: _fp8_channel_scale_on_rows,
      [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),

@@ -674,3 +674,69 @@ def test_fp8_masked_equals_contiguous():
     a = O.masked_forward_fp8(xq, sx, Wq, sw, ms, T)
     b = O.moe_forward_fp8(xq, sx, Wq, sw, ids, w, E)
     assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def _gated_case(seed, T=7, K=6, F=4, N=5, E=3, k=2):
+    rng = np.random.default_rng(seed)
+    ids = np.array([rng.choice([0, 2], size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x = rng.standard_normal((T, K))
+    Wgu = rng.standard_normal((E, 2 * F, K))
+    Wd = rng.standard_normal((E, N, F))
+    w = rng.random((T, k))
+    dY = rng.standard_normal((T, N))
+    return x, Wgu, Wd, ids, w, dY
+
+
+def test_gated_backward_finite_differences():
+    """Central differences of L = sum(dY * y) in float64 (h = 1e-6; y is
+    smooth, so the truncation error is O(h^2)) against every gradient."""
+    x, Wgu, Wd, ids, w, dY = _gated_case(91)
+    E = 3
+    L = lambda x_, Wgu_, Wd_, w_: float(np.sum(dY * O.gated_ffn_forward(x_, Wgu_, Wd_, ids, w_, E)))
+    dX, dWgu, dWd, d_w = O.gated_ffn_backward(dY, x, Wgu, Wd, ids, w, E)
+    eps = 1e-6
+
+    def fd(arr, idx, which):
+        p_, m_ = arr.copy(), arr.copy()
+        p_[idx] += eps
+        m_[idx] -= eps
+        args_p = [x, Wgu, Wd, w]
+        args_m = [x, Wgu, Wd, w]
+        args_p[which], args_m[which] = p_, m_
+        return (L(*args_p) - L(*args_m)) / (2 * eps)
+
+    for idx in [(0, 0), (3, 5), (6, 2)]:
+        assert abs(fd(x, idx, 0) - dX[idx]) <= 1e-6 * max(1.0, abs(dX[idx]))
+    for idx in [(0, 0, 0), (2, 1, 3), (2, 6, 5), (0, 7, 1)]:   # gate rows and up rows
+        assert abs(fd(Wgu, idx, 1) - dWgu[idx]) <= 1e-6 * max(1.0, abs(dWgu[idx]))
+    for idx in [(0, 0, 0), (2, 4, 3)]:
+        assert abs(fd(Wd, idx, 2) - dWd[idx]) <= 1e-6 * max(1.0, abs(dWd[idx]))
+    for idx in [(0, 0), (4, 1)]:
+        assert abs(fd(w, idx, 3) - d_w[idx]) <= 1e-6 * max(1.0, abs(d_w[idx]))
+    assert np.all(dWgu[1] == 0) and np.all(dWd[1] == 0)      # expert 1 has no rows
+
+
+def test_gated_backward_identities():
+    """y is linear in W_down, in the up half of W_gu and in w, so
+    <dW_down, W_down> = <dW_up, W_up> = sum w * d_w = <dY, y>."""
+    x, Wgu, Wd, ids, w, dY = _gated_case(92, T=11, K=5, F=3, N=4)
+    E, F = 3, 3
+    y = O.gated_ffn_forward(x, Wgu, Wd, ids, w, E)
+    dX, dWgu, dWd, d_w = O.gated_ffn_backward(dY, x, Wgu, Wd, ids, w, E)
+    Lv = float(np.sum(dY * y))
+    assert abs(float(np.sum(dWd * Wd)) - Lv) <= 1e-12 * max(1.0, abs(Lv))
+    assert abs(float(np.sum(dWgu[:, F:] * Wgu[:, F:])) - Lv) <= 1e-12 * max(1.0, abs(Lv))
+    assert abs(float(np.sum(w * d_w)) - Lv) <= 1e-12 * max(1.0, abs(Lv))
+
+
+def test_gated_backward_sampled_forms_agree():
+    x, Wgu, Wd, ids, w, dY = _gated_case(93)
+    E = 3
+    dX, dWgu, dWd, d_w = O.gated_ffn_backward(dY, x, Wgu, Wd, ids, w, E)
+    rx, rw = O.gated_ffn_backward_rows(dY, x, Wgu, Wd, ids, w, range(x.shape[0]))
+    assert np.allclose(rx, dX, rtol=1e-12, atol=1e-12) and np.allclose(rw, d_w, rtol=1e-12, atol=1e-12)
+    ge = [(0, 0, 0), (2, 7, 5), (2, 3, 1)]
+    de = [(0, 4, 3), (2, 0, 0)]
+    eg, ed = O.gated_weight_grad_entries(dY, x, Wgu, Wd, ids, w, E, ge, de)
+    assert np.allclose(eg, [dWgu[i] for i in ge], rtol=1e-12, atol=1e-12)
+    assert np.allclose(ed, [dWd[i] for i in de], rtol=1e-12, atol=1e-12)
