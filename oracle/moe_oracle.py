@@ -337,6 +337,18 @@ def masked_forward(x, W, ms: MaskedSchedule, T: int, *, acc=np.float64) -> np.nd
 #   * the down projection W_down [E, N, F] is the fused forward of the layer
 #     applied to h: y[t] = sum_j w[t, j] * h[s] W_down[e]^T with s = t*k + j.
 # ----------------------------------------------------------------------------
+def round_bf16(a) -> np.ndarray:
+    """Values rounded to bfloat16 (float64 -> float32 -> the nearest value with
+    an 8-bit significand, ties to even), returned as float64.  The gated FFN's
+    intermediate h is a bf16 tensor of the path; ``round_h=True`` applies this
+    to h where the oracle forms it."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
 def silu(z):
     """SiLU (sigmoid-weighted linear unit): z / (1 + exp(-z)), in float64."""
     z = np.asarray(z, dtype=np.float64)
@@ -344,13 +356,16 @@ def silu(z):
         return z / (1.0 + np.exp(-z))
 
 
-def gated_activation(gu, *, acc=np.float64):
-    """h = silu(gate) * up for a row block gu = [gate | up] of width 2F."""
+def gated_activation(gu, *, acc=np.float64, round_h=False):
+    """h = silu(gate) * up for a row block gu = [gate | up] of width 2F
+    (rounded to bf16 with ``round_h``)."""
     F = gu.shape[1] // 2
-    return (silu(gu[:, :F]) * np.asarray(gu[:, F:], dtype=np.float64)).astype(acc)
+    h = silu(gu[:, :F]) * np.asarray(gu[:, F:], dtype=np.float64)
+    return (round_bf16(h) if round_h else h).astype(acc)
 
 
-def gated_ffn_forward(x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=np.float64):
+def gated_ffn_forward(x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=np.float64,
+                      round_h=False):
     """Fused gated expert FFN: for each expert, gather its token rows, run the
     doubled up-projection, apply silu(gate) * up, project down and add the
     routing-weighted result into each token's output row.  Returns y [T, N]."""
@@ -366,13 +381,13 @@ def gated_ffn_forward(x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=
             continue
         tok = s_e // k
         gu = np.asarray(x)[tok].astype(acc) @ W_gu[e].astype(acc).T
-        z = gated_activation(gu, acc=acc) @ W_down[e].astype(acc).T
+        z = gated_activation(gu, acc=acc, round_h=round_h) @ W_down[e].astype(acc).T
         we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
         np.add.at(y, tok, we[:, None] * z)
     return y
 
 
-def gated_intermediate(x, W_gu, expert_ids, E: int, *, acc=np.float64) -> np.ndarray:
+def gated_intermediate(x, W_gu, expert_ids, E: int, *, acc=np.float64, round_h=False) -> np.ndarray:
     """The intermediate h [R, F] in the routing schedule's row order (the
     explicit path: gather the token copies, one grouped GEMM over the doubled
     weights, then the activation).  Rows past the routed rows stay zero."""
@@ -380,7 +395,7 @@ def gated_intermediate(x, W_gu, expert_ids, E: int, *, acc=np.float64) -> np.nda
     xs = np.asarray(x)[sch.row_to_token]
     gu = grouped_gemm(xs, W_gu, sch.offsets, acc=acc)
     h = np.zeros((np.asarray(expert_ids).size, W_gu.shape[1] // 2), dtype=acc)
-    h[:xs.shape[0]] = gated_activation(gu, acc=acc)
+    h[:xs.shape[0]] = gated_activation(gu, acc=acc, round_h=round_h)
     return h
 
 
@@ -396,7 +411,8 @@ def gated_ffn_forward_explicit(x, W_gu, W_down, expert_ids, topk_weights, E: int
     return y
 
 
-def gated_ffn_backward(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=np.float64):
+def gated_ffn_backward(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int, *, acc=np.float64,
+                       round_h=False):
     """Gradients of L = sum(dY * y) for the gated FFN, by the chain rule per
     expert.  With z = h W_down^T, h = silu(g) * u, (g | u) = x W_gu^T:
       dh = w * dY W_down;  dg = dh * u * silu'(g),  du = dh * silu(g),
@@ -425,7 +441,8 @@ def gated_ffn_backward(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int, *,
         gu = xe @ W_gu[e].astype(acc).T
         g, u = gu[:, :F].astype(np.float64), gu[:, F:].astype(np.float64)
         sg = 1.0 / (1.0 + np.exp(-g))
-        h = (g * sg * u).astype(acc)
+        h = g * sg * u
+        h = (round_bf16(h) if round_h else h).astype(acc)
         we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
         dYe = np.asarray(dY)[tok].astype(acc)
         Wd = W_down[e].astype(acc)
@@ -441,7 +458,7 @@ def gated_ffn_backward(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int, *,
 
 
 def gated_ffn_backward_rows(dY, x, W_gu, W_down, expert_ids, topk_weights, tokens, *,
-                            acc=np.float64):
+                            acc=np.float64, round_h=False):
     """dX[t] and d_w[t, :] of the gated FFN for the listed tokens only."""
     expert_ids = np.asarray(expert_ids)
     k = expert_ids.shape[1]
@@ -457,7 +474,7 @@ def gated_ffn_backward_rows(dY, x, W_gu, W_down, expert_ids, topk_weights, token
             gu = W_gu[e].astype(acc) @ xt
             g, u = gu[:F], gu[F:]
             sg = 1.0 / (1.0 + np.exp(-g))
-            h = g * sg * u
+            h = round_bf16(g * sg * u) if round_h else g * sg * u
             Wd = W_down[e].astype(acc)
             dw[i, j] = gy @ (Wd @ h)
             dh = w * (gy @ Wd)
@@ -467,7 +484,7 @@ def gated_ffn_backward_rows(dY, x, W_gu, W_down, expert_ids, topk_weights, token
 
 
 def gated_weight_grad_entries(dY, x, W_gu, W_down, expert_ids, topk_weights, E: int,
-                              gu_entries, down_entries, *, acc=np.float64):
+                              gu_entries, down_entries, *, acc=np.float64, round_h=False):
     """Listed entries of dW_gu [(e, j, k)] and dW_down [(e, n, f)], from sums
     over the expert's assignments."""
     expert_ids = np.asarray(expert_ids)
@@ -485,7 +502,7 @@ def gated_weight_grad_entries(dY, x, W_gu, W_down, expert_ids, topk_weights, E: 
             gu = xe @ W_gu[e].astype(acc).T
             g, u = gu[:, :F], gu[:, F:]
             sg = 1.0 / (1.0 + np.exp(-g))
-            h = g * sg * u
+            h = round_bf16(g * sg * u) if round_h else g * sg * u
             we = np.ones(s_e.size, dtype=acc) if wflat is None else wflat[s_e].astype(acc)
             dYe = np.asarray(dY)[tok].astype(acc)
             dh = we[:, None] * (dYe @ W_down[e].astype(acc))
@@ -504,7 +521,7 @@ def gated_weight_grad_entries(dY, x, W_gu, W_down, expert_ids, topk_weights, E: 
     return out_gu, out_d
 
 
-def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.float64):
+def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.float64, round_h=False):
     """Gated FFN on the masked layout.  Returns (y [T, N], h [E*capacity, F]);
     h rows of empty slots are zero (the library leaves them unwritten)."""
     F = W_gu.shape[1] // 2
@@ -515,7 +532,8 @@ def masked_gated_ffn(x, W_gu, W_down, ms: MaskedSchedule, T: int, *, acc=np.floa
         if m == 0:
             continue
         tok = ms.slot_token[e, :m]
-        he = gated_activation(np.asarray(x)[tok].astype(acc) @ W_gu[e].astype(acc).T, acc=acc)
+        he = gated_activation(np.asarray(x)[tok].astype(acc) @ W_gu[e].astype(acc).T, acc=acc,
+                              round_h=round_h)
         h[e * ms.capacity:e * ms.capacity + m] = he
         z = he @ W_down[e].astype(acc).T
         np.add.at(y, tok, ms.slot_weight[e, :m].astype(acc)[:, None] * z)
@@ -584,7 +602,8 @@ def moe_forward_fp8_rows(xq, x_scale, Wq, w_scale, expert_ids, topk_weights, tok
 # ----------------------------------------------------------------------------
 # Sampled evaluation for full-size parity checks
 # ----------------------------------------------------------------------------
-def gated_intermediate_rows(x, W_gu, expert_ids, E: int, rows, *, acc=np.float64) -> np.ndarray:
+def gated_intermediate_rows(x, W_gu, expert_ids, E: int, rows, *, acc=np.float64,
+                            round_h=False) -> np.ndarray:
     """Rows of h [R, F] for the listed schedule rows only: row r is the r-th
     assignment s in (expert, s) order, h[r] = silu(W_gate[e] x[t]) * (W_up[e] x[t])."""
     sch = routing_schedule(expert_ids, None, E)
@@ -594,11 +613,13 @@ def gated_intermediate_rows(x, W_gu, expert_ids, E: int, rows, *, acc=np.float64
     for i, r in enumerate(rows):
         s = int(sch.perm[r])
         gu = W_gu[int(ids[s])].astype(acc) @ np.asarray(x)[int(sch.row_to_token[r])].astype(acc)
-        out[i] = (silu(gu[:F]) * gu[F:]).astype(acc)
+        h = silu(gu[:F]) * gu[F:]
+        out[i] = (round_bf16(h) if round_h else h).astype(acc)
     return out
 
 
-def gated_ffn_rows(x, W_gu, W_down, expert_ids, topk_weights, tokens, *, acc=np.float64):
+def gated_ffn_rows(x, W_gu, W_down, expert_ids, topk_weights, tokens, *, acc=np.float64,
+                   round_h=False):
     """y[t, :] of the gated FFN for the listed tokens only, from the definition
     y[t] = sum_j w[t, j] * W_down[e] (silu(W_gate[e] x[t]) * (W_up[e] x[t]))."""
     expert_ids = np.asarray(expert_ids)
@@ -610,7 +631,8 @@ def gated_ffn_rows(x, W_gu, W_down, expert_ids, topk_weights, tokens, *, acc=np.
             e = int(expert_ids[t, j])
             w = 1.0 if topk_weights is None else float(topk_weights[t, j])
             gu = W_gu[e].astype(acc) @ xt
-            h = (silu(gu[:F]) * gu[F:]).astype(acc)
+            h = silu(gu[:F]) * gu[F:]
+            h = (round_bf16(h) if round_h else h).astype(acc)
             out[i] += acc(w) * (W_down[e].astype(acc) @ h)
     return out
 

@@ -87,25 +87,28 @@ def _bwd_dw_transposed_sum(dY, x, W, expert_ids, topk_weights, E, *, acc=np.floa
     return dX2, dW, d_w2                       # dW without the routing weight
 
 
-def _gated_swapped(gu, *, acc=np.float64):
+def _gated_swapped(gu, *, acc=np.float64, round_h=False):
     F = gu.shape[1] // 2
-    return _ORIG["gated_activation"](np.concatenate([gu[:, F:], gu[:, :F]], axis=1), acc=acc)
+    return _ORIG["gated_activation"](np.concatenate([gu[:, F:], gu[:, :F]], axis=1), acc=acc,
+                                     round_h=round_h)
 
 
-def _gated_sigmoid(gu, *, acc=np.float64):
+def _gated_sigmoid(gu, *, acc=np.float64, round_h=False):
     F = gu.shape[1] // 2
     g = np.asarray(gu[:, :F], dtype=np.float64)
     return (1.0 / (1.0 + np.exp(-g)) * gu[:, F:]).astype(acc)   # sigmoid instead of silu
 
 
-def _gated_down_untransposed(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+def _gated_down_untransposed(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64,
+                             round_h=False):
     Wd = np.swapaxes(np.asarray(W_down), 1, 2)
     if Wd.shape[2] != W_gu.shape[1] // 2:
         raise ValueError("shape")
     return _ORIG["gated_ffn_forward"](x, W_gu, Wd, expert_ids, topk_weights, E, acc=acc)
 
 
-def _gated_no_weight(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+def _gated_no_weight(x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64,
+                     round_h=False):
     return _ORIG["gated_ffn_forward"](x, W_gu, W_down, expert_ids, None, E, acc=acc)
 
 
@@ -131,7 +134,8 @@ def _fp8_channel_scale_on_rows(xq, x_scale, Wq, w_scale, expert_ids, topk_weight
                                     topk_weights, E, acc=acc)      # one scale per expert only
 
 
-def _gated_bwd_sigmoid_derivative(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+def _gated_bwd_sigmoid_derivative(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64,
+                                  round_h=False):
     """silu' taken as the logistic function alone (the g s (1 - s) term dropped)."""
     saved = np.exp
     dX, dWgu, dWd, d_w = _ORIG["gated_ffn_backward"](dY, x, W_gu, W_down, expert_ids, topk_weights, E,
@@ -156,7 +160,8 @@ def _gated_bwd_sigmoid_derivative(dY, x, W_gu, W_down, expert_ids, topk_weights,
     return dX2, dWgu, dWd, d_w
 
 
-def _gated_bwd_weighted_dw(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64):
+def _gated_bwd_weighted_dw(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, acc=np.float64,
+                           round_h=False):
     dX, dWgu, dWd, d_w = _ORIG["gated_ffn_backward"](dY, x, W_gu, W_down, expert_ids, topk_weights, E,
                                                       acc=acc)
     return dX, dWgu, dWd, d_w * np.asarray(topk_weights)

@@ -740,3 +740,15 @@ def test_gated_backward_sampled_forms_agree():
     eg, ed = O.gated_weight_grad_entries(dY, x, Wgu, Wd, ids, w, E, ge, de)
     assert np.allclose(eg, [dWgu[i] for i in ge], rtol=1e-12, atol=1e-12)
     assert np.allclose(ed, [dWd[i] for i in de], rtol=1e-12, atol=1e-12)
+
+
+def test_round_bf16_against_torch():
+    """The oracle's bf16 rounding equals torch's float32 -> bfloat16 conversion
+    (round to nearest, ties to even) on random values, ties and extremes."""
+    import torch
+    rng = np.random.default_rng(95)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 6, 4000),
+                        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -1.0 - 2.0 ** -8, 0.0, 448.0])])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(O.round_bf16(v), ref)
+    assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0 and O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
