@@ -206,13 +206,47 @@ int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
  *   schedule row order (kept for a backward pass); rows of empty masked slots
  *   and rows at or past offsets[E-1] are left untouched.  h is rounded to bf16
  *   before the down projection.
+ *   gu [sched->R, 2F] float or NULL: when given, the gate values g (columns
+ *   0..F-1) and up values u (F..2F-1) of every valid row as accumulated (fp32),
+ *   which moe_gated_ffn_bwd needs; same rows as h.  16-byte aligned.
  *   y [T, N] float, OVERWRITTEN (zeroed by the call, then accumulated).
  * Three launches on `stream`: the gated up-projection, the zeroing of y and
  * the down projection.
  */
 int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
-                      const moe_schedule *sched, void *h, float *y, int64_t K, int64_t F,
-                      int64_t N, int32_t dtype, void *stream);
+                      const moe_schedule *sched, void *h, void *gu, float *y, int64_t K,
+                      int64_t F, int64_t N, int32_t dtype, void *stream);
+
+/* Bytes of device workspace moe_gated_ffn_bwd needs (its [R, 2F] bf16
+ * gradient of the gate/up values); 0 for invalid arguments. */
+size_t moe_gated_ffn_bwd_workspace_bytes(const moe_schedule *sched, int64_t F);
+
+/*
+ * Gated expert FFN backward for L = sum(dY * y) with y from moe_gated_ffn_fwd
+ * (the chain rule through the down projection, the SiLU gate and the doubled
+ * up-projection; [GG] "The backward pass" for the grouped products):
+ *   dh[r]      = w_r * dY[t_r] W_down[e_r]                       (per row)
+ *   dgu[r]     = (dh * u * silu'(g) | dh * silu(g)),  silu'(g) = s (1 + g (1 - s)),
+ *                s = 1 / (1 + exp(-g)), with g, u the saved gate / up values
+ *   dX[t]      = sum over the token's rows of dgu[r] W_gu[e_r]
+ *   dW_gu[e]   = sum over rows of e of dgu[r]^T x[t_r]
+ *   dW_down[e] = sum over rows of e of (w_r dY[t_r])^T h[r]   (0 for empty experts)
+ *   d_topk[t, j] = dY[t] . (h[r] W_down[e]^T), the unweighted down output.
+ *   dY [T, N], x [T, K], W_gu [E, 2F, K], W_down [E, N, F] and h [R, F]
+ *   bf16, gu [R, 2F] float (h and gu saved by the forward with the same
+ *   schedule); all 16-byte aligned.  dX [T, K] float, dW_gu [E, 2F, K] and dW_down [E, N, F] bf16,
+ *   d_topk [T, k] float: each OVERWRITTEN, or NULL to skip.
+ *   workspace: moe_gated_ffn_bwd_workspace_bytes(sched, F) bytes, 256-byte
+ *   aligned (required when dX or dW_gu is asked for).
+ * Up to four launches on `stream`: dW_down (which zeroes dX and d_topk on the
+ * side; a fill launch when dW_down is NULL), the per-row dh / dgu / d_topk
+ * kernel, dX, dW_gu.  The routing weight enters through dh, so dX and dW_gu
+ * take dgu unweighted.
+ */
+int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const void *W_down,
+                      const moe_schedule *sched, const void *gu, const void *h, float *dX,
+                      void *dW_gu, void *dW_down, float *d_topk, int64_t K, int64_t F, int64_t N,
+                      int32_t dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace moe_fused_bwd needs for these sizes (may be 0). */
 size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64_t N,

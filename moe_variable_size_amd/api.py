@@ -209,12 +209,13 @@ def moe_fused_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, W_q: torch.Tenso
 
 def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor, sched: Schedule, *,
                       h: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
-                      stream=None):
+                      gu: Optional[torch.Tensor] = None, save_gu: bool = False, stream=None):
     """Gated expert FFN forward: h = silu(x W_gate^T) * (x W_up^T) per schedule
     row from one grouped GEMM over W_gu [E, 2F, K] (gate rows, then up rows),
     then y = the weighted scatter-combine of h W_down^T, W_down [E, N, F]
     ([GG] "Choosing an implementation").  Returns (y [T, N] float32,
-    h [R, F] bfloat16)."""
+    h [R, F] bfloat16) and, with ``save_gu`` (or ``gu`` given), also the saved
+    gate/up values gu [R, 2F] float32 the backward needs."""
     lib = _lib.load()
     _require(x, "x", torch.bfloat16, 2)
     _require(W_gu, "W_gu", torch.bfloat16, 3)
@@ -232,10 +233,48 @@ def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor,
     _require(y, "y", torch.float32, 2)
     if tuple(h.shape) != (sched.c.R, F) or tuple(y.shape) != (T, N):
         raise ValueError("h must be [R, F] and y [T, N]")
+    if gu is None and save_gu:
+        gu = torch.empty((sched.c.R, 2 * F), dtype=torch.float32, device=x.device)
+    if gu is not None:
+        _require(gu, "gu", torch.float32, 2)
+        if tuple(gu.shape) != (sched.c.R, 2 * F):
+            raise ValueError("gu must be [R, 2F]")
     st = lib.moe_gated_ffn_fwd(_ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c), _ptr(h),
-                               _ptr(y), K, F, N, MOE_BF16, _stream(stream))
+                               _ptr(gu), _ptr(y), K, F, N, MOE_BF16, _stream(stream))
     _lib.check("moe_gated_ffn_fwd", st)
-    return y, h
+    return (y, h, gu) if gu is not None else (y, h)
+
+
+def moe_gated_ffn_bwd(dY: torch.Tensor, x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor,
+                      sched: Schedule, gu: torch.Tensor, h: torch.Tensor, *, dx: bool = True,
+                      dw_gu: bool = True, dw_down: bool = True, dtopk: bool = True, stream=None):
+    """Gated expert FFN backward from the saved gu and h.  Returns (dX [T, K]
+    float32 | None, dW_gu [E, 2F, K] bf16 | None, dW_down [E, N, F] bf16 |
+    None, d_topk [T, k] float32 | None)."""
+    lib = _lib.load()
+    for t, name, nd in ((dY, "dY", 2), (x, "x", 2), (W_gu, "W_gu", 3), (W_down, "W_down", 3),
+                        (h, "h", 2)):
+        _require(t, name, torch.bfloat16, nd)
+    _require(gu, "gu", torch.float32, 2)
+    T, K = x.shape
+    E, F2, _ = W_gu.shape
+    F = F2 // 2
+    N = W_down.shape[1]
+    if tuple(W_down.shape) != (E, N, F) or tuple(dY.shape) != (T, N) or T != sched.c.T \
+            or tuple(gu.shape) != (sched.c.R, 2 * F) or tuple(h.shape) != (sched.c.R, F):
+        raise ValueError("shape mismatch among dY, x, W_gu, W_down, gu, h and the schedule")
+    dev = x.device
+    dX = torch.empty((T, K), dtype=torch.float32, device=dev) if dx else None
+    dWgu = torch.empty((E, 2 * F, K), dtype=torch.bfloat16, device=dev) if dw_gu else None
+    dWd = torch.empty((E, N, F), dtype=torch.bfloat16, device=dev) if dw_down else None
+    dT = torch.empty((T, sched.c.k), dtype=torch.float32, device=dev) if dtopk else None
+    ws_bytes = int(lib.moe_gated_ffn_bwd_workspace_bytes(ctypes.byref(sched.c), F))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    st = lib.moe_gated_ffn_bwd(_ptr(dY), _ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c),
+                               _ptr(gu), _ptr(h), _ptr(dX), _ptr(dWgu), _ptr(dWd), _ptr(dT), K, F, N,
+                               MOE_BF16, _ptr(ws), ws_bytes, _stream(stream))
+    _lib.check("moe_gated_ffn_bwd", st)
+    return dX, dWgu, dWd, dT
 
 
 def moe_fused_bwd_workspace_bytes(sched: Schedule, K: int, N: int, dtype) -> int:

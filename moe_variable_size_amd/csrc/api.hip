@@ -282,7 +282,7 @@ int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
 }
 
 int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
-                      const moe_schedule *sched, void *h, float *y, int64_t K, int64_t F,
+                      const moe_schedule *sched, void *h, void *gu, float *y, int64_t K, int64_t F,
                       int64_t N, int32_t dtype, void *stream) {
   int rc = check_sched(sched);
   if (rc) return rc;
@@ -298,12 +298,13 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
   if (!fits(s.T, K, dtype) || !fits(2 * F, K, dtype) || !fits(N, F, dtype) ||
       !fits(s.R, F, dtype) || !fits(s.T, N, MOE_F32))
     return MOE_ERR_LIMIT;
+  if (gu && !fits(s.R, 2 * F, MOE_F32)) return MOE_ERR_LIMIT;
   if (!aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) || !aligned(h, 16) ||
-      !aligned(y, 4))
+      (gu && !aligned(gu, 16)) || !aligned(y, 4))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(F_GATED_UP, st, [&] {
-    return mfma_gated_up(x, W_gu, s, h, (int)K, (int)F, st);
+    return mfma_gated_up(x, W_gu, s, h, gu, (int)K, (int)F, st);
   });
   if (e == hipSuccess)
     e = timed(F_FILL, st, [&] {
@@ -312,6 +313,68 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
   if (e == hipSuccess)
     e = timed(F_GATED_DOWN, st, [&] {
       return mfma_fused_fwd(h, W_down, s, y, (int)F, (int)N, true, st);
+    });
+  return hip_status(e);
+}
+
+size_t moe_gated_ffn_bwd_workspace_bytes(const moe_schedule *sched, int64_t F) {
+  if (!sched || F < 1 || F >= kMax32) return 0;
+  return align256((size_t)sched->R * 2 * (size_t)F * 2);  // dgu [R, 2F] bf16
+}
+
+int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const void *W_down,
+                      const moe_schedule *sched, const void *gu, const void *h, float *dX,
+                      void *dW_gu, void *dW_down, float *d_topk, int64_t K, int64_t F, int64_t N,
+                      int32_t dtype, void *workspace, size_t workspace_bytes, void *stream) {
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  rc = check_dtype_dims(dtype, K, N);
+  if (rc) return rc;
+  if (F < 1) return MOE_ERR_SHAPE;
+  if (F >= kMax32) return MOE_ERR_LIMIT;
+  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
+  if (!dY || !x || !W_gu || !W_down || !gu || !h) return MOE_ERR_NULL;
+  const moe_schedule &s = *sched;
+  const bool need_dgu = dX || dW_gu;
+  if (!mfma_supported((int)K, (int)(2 * F)) || !mfma_supported((int)F, (int)N))
+    return MOE_ERR_SHAPE;
+  if (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(2 * F, K, dtype) ||
+      !fits(N, F, dtype) || !fits(s.R, 2 * F, MOE_F32) || !fits(s.T, K, MOE_F32))
+    return MOE_ERR_LIMIT;
+  const size_t ws_need = moe_gated_ffn_bwd_workspace_bytes(sched, F);
+  if (need_dgu && (!workspace || workspace_bytes < ws_need)) return MOE_ERR_WORKSPACE;
+  if (!aligned(dY, 16) || !aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) ||
+      !aligned(gu, 16) || !aligned(h, 16) || (dX && !aligned(dX, 4)) ||
+      (dW_gu && !aligned(dW_gu, 2)) || (dW_down && !aligned(dW_down, 2)) ||
+      (d_topk && !aligned(d_topk, 4)) || (workspace && !aligned(workspace, 256)))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  void *dgu = workspace;
+  const size_t dx_bytes = dX ? (size_t)s.T * K * sizeof(float) : 0;
+  const size_t dt_bytes = d_topk ? (size_t)s.S * sizeof(float) : 0;
+  hipError_t e = hipSuccess;
+  // 1. dW_down = sum (w dY)^T h (zeroes dX and d_topk on the side), or one fill
+  if (dW_down)
+    e = timed(F_DW, st, [&] {
+      return mfma_bwd_dw_rows(dY, false, h, true, s, dW_down, (int)F, (int)N, true, dX, dx_bytes,
+                              d_topk, dt_bytes, st);
+    });
+  else if (dX || d_topk)
+    e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, dx_bytes, d_topk, dt_bytes, st); });
+  // 2. G = dY W_down per row; d_topk += <G, h>; dgu from the saved gate / up
+  if (e == hipSuccess && (need_dgu || d_topk))
+    e = timed(F_DX, st, [&] {
+      return mfma_gated_bwd_dh(dY, h, W_down, s, d_topk, (int)F, (int)N, gu,
+                               need_dgu ? dgu : nullptr, st);
+    });
+  // 3. dX[t] += dgu[r] W_gu[e]
+  if (e == hipSuccess && dX)
+    e = timed(F_DX, st, [&] { return mfma_gated_bwd_dx(dgu, W_gu, s, dX, (int)K, (int)F, st); });
+  // 4. dW_gu = sum dgu^T x
+  if (e == hipSuccess && dW_gu)
+    e = timed(F_DW, st, [&] {
+      return mfma_bwd_dw_rows(dgu, true, x, false, s, dW_gu, (int)K, (int)(2 * F), false,
+                              nullptr, 0, nullptr, 0, st);
     });
   return hip_status(e);
 }

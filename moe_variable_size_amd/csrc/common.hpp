@@ -104,14 +104,29 @@ hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *
                               const float *w_scale, const moe_schedule &s, float *y, int K, int N,
                               hipStream_t st);
 // h [R, F] bf16 = silu(x W_gate^T) * (x W_up^T) per schedule row; W_gu [E, 2F, K]
-hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, int K,
-                         int F, hipStream_t st);
+// gu (optional, NULL to skip): [R, 2F] fp32 gate and up values kept for a backward
+hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,
+                         int K, int F, hipStream_t st);
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, hipStream_t st);
 // zero0 / zero1: byte ranges the kernel zeroes on the side (NULL / 0 when unused)
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
                        int N, float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
                        hipStream_t st);
+// dW[e] = sum over rows r of e of (w_r? dY[.])^T x[.], each operand read by token
+// or, with *_by_row, by schedule row (an operand already in schedule order)
+hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool x_by_row,
+                            const moe_schedule &s, void *dW, int K, int N, bool weighted,
+                            float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
+                            hipStream_t st);
+// gated FFN backward, first step: G = dY W_down (dY by token), d_w += <G, h>
+// (h [R, F] by row), dgu [R, 2F] = (dh u silu'(g) | dh silu(g)), dh = w G
+hipError_t mfma_gated_bwd_dh(const void *dY, const void *h, const void *W_down,
+                             const moe_schedule &s, float *d_w, int F, int N, const void *gu,
+                             void *dgu, hipStream_t st);
+// gated FFN backward: dX[t] += dgu[r] W_gu[e] (dgu by row, unweighted scatter)
+hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedule &s, float *dX,
+                             int K, int F, hipStream_t st);
 }  // namespace moe
 
 namespace moe {

@@ -730,6 +730,7 @@ struct FwdArgs {
   int tile_rows;     // routed, BM = 256: 0 = picked on the device, 128 / 256 = forced
   const float *x_scale;  // 8-bit operands: per-token scale [T]
   const float *w_scale;  // 8-bit operands: per-expert output-channel scale [E, N]
+  float *gu_out;         // gated: [R, 2F] gate and up values (fp32) kept for a backward, or NULL
 };
 
 // What a forward-shaped kernel writes:
@@ -940,6 +941,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         // tile's schedule row r for live rows and f < F
         constexpr int NH = NIc / 2;
         bf16_t *const hb = (bf16_t *)p.C;
+        float *const gub = p.gu_out;
         const int cl0 = wn * 32 + (lane & 31);
 #pragma unroll
         for (int mi = 0; mi < MIc; ++mi) {
@@ -958,6 +960,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
                 if (cl >= ncols) continue;
                 const float g = acc[mi][ni][4 * j + q], u = acc[mi][ni + NH][4 * j + q];
                 hrow[cl] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
+                if (gub) {
+                  float *const gr = gub + (size_t)(c.row0 + rq + q) * (2 * N) + n0 + cl;
+                  gr[0] = g;
+                  gr[N] = u;
+                }
               }
             }
           }
@@ -1105,6 +1112,12 @@ struct DxArgs {
   int stream_k;
   int tail_split;  // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int tile_rows;   // 0 = picked on the device, 128 / 256 = forced
+  int a_by_row;    // 1: A row of schedule row r is row r of dY (already in schedule order)
+  int unweighted;  // 1: scatter G itself (the routing weight is already in the operand)
+  // gated FFN backward (GB kernels): x is h [R, K] read by schedule row, gu the
+  // saved gate/up values [R, 2K] (fp32), dgu the output [R, 2K] (bf16; K here is F)
+  const float *gu;
+  bf16_t *dgu;
 };
 
 template <int NW>
@@ -1152,8 +1165,12 @@ struct DxOp {
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
 };
 
-// NW waves in a 2 x NW/2 grid
-template <int NW>
+// NW waves in a 2 x NW/2 grid.  GB (gated FFN backward): the output columns
+// run over F; instead of scattering w * G into dX, each element makes
+// dh = w * G, reads the saved gate g and up u of its row, and stores
+// dg = dh * u * silu'(g) and du = dh * silu(g) into dgu; the routing-weight
+// gradient takes h (read by schedule row) where the plain kernel takes x.
+template <int NW, bool GB = false>
 __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = NW / 2, NTH = NW * 64;
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
@@ -1208,9 +1225,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       const int r = c.row0 + tid;
       const int t = ok ? p.row_to_token[r] : -1;
       tok[tid] = t;
-      wgt[tid] = ok ? p.row_weight[r] : 0.f;
+      wgt[tid] = ok ? (p.unweighted ? 1.f : p.row_weight[r]) : 0.f;
       asg[tid] = ok ? p.row_to_assign[r] : -1;
-      rowoff_a[tid] = t >= 0 ? t * N * 2 : -1;
+      rowoff_a[tid] = t >= 0 ? (p.a_by_row ? r : t) * N * 2 : -1;
     }
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
@@ -1243,7 +1260,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
           for (int i = 0; i < XPW; ++i) {
             const int row = (wid * XPW + i) * 8 + (lane >> 3);
             const int cch = (lane & 7) ^ ((row >> 1) & 7);
-            const int t = tok[row];
+            const int t = GB ? (tok[row] >= 0 ? c.row0 + row : -1) : tok[row];
             const int col = kc0 + q * 64 + cch * 8;
             const uint32_t off =
                 (t >= 0 && col < K) ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u : kOobOffset;
@@ -1297,8 +1314,18 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float g = cok ? acc[mi][ni][4 * j + q] : 0.f;  // dead columns may hold stale values
-              if (has_dx && t4[q] >= 0 && cok)
+              if constexpr (GB) {
+                if (p.dgu && t4[q] >= 0 && cok) {
+                  const size_t gi = (size_t)(c.row0 + rq + q) * (2 * K) + kc0 + cl;
+                  const float gv = p.gu[gi], uv = p.gu[gi + K];
+                  const float sg = 1.f / (1.f + __expf(-gv));
+                  const float dh = w4[q] * g;
+                  p.dgu[gi] = f32_to_bf16(dh * uv * sg * (1.f + gv * (1.f - sg)));
+                  p.dgu[gi + K] = f32_to_bf16(dh * gv * sg);
+                }
+              } else if (has_dx && t4[q] >= 0 && cok) {
                 unsafeAtomicAdd((float *)(xb + (ro[q] + cb[ni])), w4[q] * g);
+              }
               if (has_dw) {
                 const float xv = __builtin_bit_cast(float, (uint32_t)(uint16_t)xq[ni][q] << 16);
                 dwp[q] = fmaf(g, xv, dwp[q]);  // masked rows / columns hold zeros
@@ -1370,6 +1397,7 @@ struct DwArgs {
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes, rw_bytes;
   int weighted;
+  int dy_by_row, x_by_row;  // 1: that operand is already in schedule row order (row r, not token)
   // zeroed by the kernel on the side (the accumulation targets of the input
   // gradient kernel that runs after it): byte ranges, NULL / 0 when unused
   float *zero0;
@@ -1414,7 +1442,7 @@ struct DwOp {
   __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
   uint32_t lds0;
   const char *lds;
-  int r0, m, wid, lane, K, N, weighted;
+  int r0, m, wid, lane, K, N, weighted, dy_by_row, x_by_row;
   uint32_t ncol[PW], kcol[PW];  // byte offsets of this lane's column chunk (dY / x), or OOB
   i32x4 tq[PW / 2];             // tokens of this wave's 2*PW rows of the stage being issued
 
@@ -1451,13 +1479,15 @@ struct DwOp {
       int tok = (lane >> 5) ? to : te;
       if (q >= m) tok = -1;
       if (j < PW) {
+        const int ry = dy_by_row ? r0 + q : tok;  // row of dY (valid when tok >= 0)
         const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
-                                  ? (uint32_t)tok * (uint32_t)N * 2u + ncol[i]
+                                  ? (uint32_t)ry * (uint32_t)N * 2u + ncol[i]
                                   : kOobOffset;
         dma16(rsY, offy, t + Map::lds_of(wid, i));
       } else {
+        const int rx = x_by_row ? r0 + q : tok;
         const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
-                                  ? (uint32_t)tok * (uint32_t)K * 2u + kcol[i]
+                                  ? (uint32_t)rx * (uint32_t)K * 2u + kcol[i]
                                   : kOobOffset;
         dma16(rsX, offx, t + OPND + Map::lds_of(wid, i));
       }
@@ -1517,6 +1547,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   op.K = K;
   op.N = N;
   op.weighted = p.weighted;
+  op.dy_by_row = p.dy_by_row;
+  op.x_by_row = p.x_by_row;
 
   for (int round = 0;; ++round) {
     const int base = round * G;
@@ -1724,13 +1756,16 @@ hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *
   return launch_routed<FWD_SCATTER, true>(a, s, st);
 }
 
-hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, int K,
-                         int F, hipStream_t st) {
+hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,
+                         int K, int F, hipStream_t st) {
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W_gu, h, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, F,
             (uint32_t)((size_t)s.T * K * 2), 0, tail_split(), (int)s.T};
+  a.gu_out = (float *)gu;
   return launch_routed<FWD_GATED>(a, s, st);
 }
+
+static hipError_t launch_dx(const DxArgs &a, hipStream_t st);
 
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, hipStream_t st) {
@@ -1738,6 +1773,37 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
            (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split(), forced_bm()};
+  return launch_dx(a, st);
+}
+
+hipError_t mfma_gated_bwd_dh(const void *dY, const void *h, const void *W_down,
+                             const moe_schedule &s, float *d_w, int F, int N, const void *gu,
+                             void *dgu, hipStream_t st) {
+  DxArgs a{(const bf16_t *)dY, (const bf16_t *)h, (const bf16_t *)W_down, nullptr, d_w, s.offsets,
+           s.counts, s.block_start, s.row_to_assign, s.row_to_token,
+           s.row_weight, s.E, s.layout, s.capacity, F, N, (uint32_t)((size_t)s.T * N * 2),
+           (uint32_t)((size_t)s.R * F * 2), 0, tail_split(), forced_bm()};
+  a.gu = (const float *)gu;
+  a.dgu = (bf16_t *)dgu;
+  const dim3 grid(device_cu_count());
+  hipError_t e = set_smem<mfma_dx_kernel<4, true>>(kStageLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_dx_kernel<4, true>), grid, dim3(256), kStageLds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedule &s, float *dX,
+                             int K, int F, hipStream_t st) {
+  DxArgs a{(const bf16_t *)dgu, nullptr, (const bf16_t *)W_gu, dX, nullptr, s.offsets,
+           s.counts, s.block_start, s.row_to_assign, s.row_to_token,
+           s.row_weight, s.E, s.layout, s.capacity, K, 2 * F,
+           (uint32_t)((size_t)s.R * 2 * F * 2), 0u, 0, tail_split(), forced_bm()};
+  a.a_by_row = 1;
+  a.unweighted = 1;
+  return launch_dx(a, st);
+}
+
+static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
   if (dx_waves() == 4) {
     hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);
@@ -1754,10 +1820,38 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
                        int N, float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
                        hipStream_t st) {
-  DwArgs a{(const bf16_t *)dY, (const bf16_t *)x, dW, s.offsets, s.counts, s.expert_order,
-           s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-           (uint32_t)((size_t)s.T * N * 2), (uint32_t)((size_t)s.T * K * 2),
-           (uint32_t)((size_t)s.R * 4), 1, zero0, zero0_bytes, zero1, zero1_bytes};
+  return mfma_bwd_dw_rows(dY, false, x, false, s, dW, K, N, true, zero0, zero0_bytes, zero1,
+                          zero1_bytes, st);
+}
+
+hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool x_by_row,
+                            const moe_schedule &s, void *dW, int K, int N, bool weighted,
+                            float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
+                            hipStream_t st) {
+  DwArgs a{};
+  a.dY = (const bf16_t *)dY;
+  a.x = (const bf16_t *)x;
+  a.dW = dW;
+  a.offsets = s.offsets;
+  a.counts = s.counts;
+  a.expert_order = s.expert_order;
+  a.row_to_token = s.row_to_token;
+  a.row_weight = s.row_weight;
+  a.E = s.E;
+  a.layout = s.layout;
+  a.capacity = s.capacity;
+  a.K = K;
+  a.N = N;
+  a.dy_bytes = (uint32_t)((size_t)(dy_by_row ? s.R : s.T) * N * 2);
+  a.x_bytes = (uint32_t)((size_t)(x_by_row ? s.R : s.T) * K * 2);
+  a.rw_bytes = (uint32_t)((size_t)s.R * 4);
+  a.weighted = weighted ? 1 : 0;
+  a.dy_by_row = dy_by_row ? 1 : 0;
+  a.x_by_row = x_by_row ? 1 : 0;
+  a.zero0 = zero0;
+  a.zero0_bytes = zero0_bytes;
+  a.zero1 = zero1;
+  a.zero1_bytes = zero1_bytes;
   if (dw_waves() == 4) {
     constexpr size_t lds = DwOp<4>::LDS_BYTES;
     hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 4>>(lds);

@@ -106,14 +106,14 @@ def test_gated_ffn_rejects_before_launch(lib):
               "row_weight", "status"):
         setattr(s, f, 1 << 20)
     r = ctypes.byref(s)
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 16, 16, 16, 0, None) == 3      # fp32: bf16 only
-    assert lib.moe_gated_ffn_fwd(P, P, None, r, P, P, 16, 16, 16, 1, None) == 1   # no W_down
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, None, P, 16, 16, 16, 1, None) == 1   # no h
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 16, 0, 16, 1, None) == 2      # F = 0
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 16, 12, 16, 1, None) == 2     # F % 8 != 0
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, ctypes.c_void_p((1 << 20) + 2), P, 16, 16, 16, 1,
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 16, 16, 0, None) == 3      # fp32: bf16 only
+    assert lib.moe_gated_ffn_fwd(P, P, None, r, P, None, P, 16, 16, 16, 1, None) == 1   # no W_down
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, None, None, P, 16, 16, 16, 1, None) == 1   # no h
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 0, 16, 1, None) == 2      # F = 0
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 12, 16, 1, None) == 2     # F % 8 != 0
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, ctypes.c_void_p((1 << 20) + 2), None, P, 16, 16, 16, 1,
                                  None) == 4                                       # h misaligned
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, P, 1 << 16, 1 << 15, 16, 1, None) == 7  # W_gu > 2^31 B
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 1 << 16, 1 << 15, 16, 1, None) == 7  # W_gu > 2^31 B
 
 
 def test_fp8_rejects_before_launch(lib):
@@ -128,3 +128,20 @@ def test_fp8_rejects_before_launch(lib):
     assert lib.moe_fused_fwd_fp8(P, None, P, P, r, P, 32, 8, None) == 1   # no x_scale
     assert lib.moe_fused_fwd_fp8(ctypes.c_void_p((1 << 20) + 8), P, P, P, r, P, 32, 8, None) == 4
     assert lib.moe_fused_fwd_fp8(P, P, P, P, r, P, 1 << 16, 1 << 15, None) == 7   # W_q >= 2^31 B
+
+
+def test_gated_backward_rejects_before_launch(lib):
+    P = FAKE
+    s = _lib.MoeSchedule()
+    s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
+    for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
+              "row_weight", "status"):
+        setattr(s, f, 1 << 20)
+    r = ctypes.byref(s)
+    assert lib.moe_gated_ffn_bwd_workspace_bytes(r, 16) >= 8 * 32 * 2
+    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, None, P, P, P, P, P, 16, 16, 16, 1, P, 1 << 20,
+                                 None) == 1                                          # no gu
+    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 16, 16, 1, None, 0,
+                                 None) == 5                                          # no workspace
+    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 16, 16, 0, P, 1 << 20,
+                                 None) == 3                                          # fp32
