@@ -14,8 +14,8 @@ gradient) / step time, S = T*top_k; padding is never counted.
 
 More objects ride on the same line: "decode" (masked decode forward, HBM
 GB/s), "fp8" (the 8-bit forward on the config-2 shape and the masked decode)
-and "gated_ffn" (gated expert FFN forward on the balanced step of the page's
-worked example, TFLOP/s).
+and "gated_ffn" (gated expert FFN forward and backward on the balanced step
+of the page's worked example, TFLOP/s).
 
 Prints ONE JSON line.  --gpus above 1 is not supported (one GPU per process,
 single-GPU machine) and exits with a message.
@@ -151,11 +151,13 @@ def decode_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
 
 
 def gated_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
-    """Gated expert FFN forward on the balanced step of the page's worked
-    example (T=8192, hidden 4096, F=2048, E=64 with 256 rows each, top-2):
-    gate+up as one grouped GEMM with silu(gate)*up in its epilogue, then the
-    down projection with the weighted scatter-combine.  Useful FLOPs:
-    2*S*K*2F + 2*S*F*N."""
+    """Gated expert FFN forward and backward on the balanced step of the page's
+    worked example (T=8192, hidden 4096, F=2048, E=64 with 256 rows each,
+    top-2): gate+up as one grouped GEMM with silu(gate)*up in its epilogue,
+    the down projection with the weighted scatter-combine, and the backward
+    (dW_down, dh/dgu/d routing weight, dX, dW_gu).  Useful FLOPs: forward
+    2*S*K*2F + 2*S*F*N, backward twice that.  Kernel times per launch (the
+    backward's two dX-kernel launches and two dW launches average together)."""
     g = WL.gated_page_example()
 
     def to_dev(t):
@@ -169,9 +171,14 @@ def gated_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
     h = torch.empty((S, g.F), dtype=torch.bfloat16, device=dev)
     y = torch.empty((g.T, g.N), dtype=torch.float32, device=dev)
 
+    gu = torch.empty((S, 2 * g.F), dtype=torch.float32, device=dev)
+    rng = np.random.default_rng(g.seed + 1)
+    dY = torch.from_numpy(rng.standard_normal((g.T, g.N), dtype=np.float32)).to(torch.bfloat16).to(dev)
+
     def step():
         sch = api.moe_build_schedule(ids, w, g.E, workspace=ws)
-        api.moe_gated_ffn_fwd(x, Wgu, Wd, sch, h=h, y=y)
+        api.moe_gated_ffn_fwd(x, Wgu, Wd, sch, h=h, y=y, gu=gu)
+        api.moe_gated_ffn_bwd(dY, x, Wgu, Wd, sch, gu, h)
 
     for _ in range(warmup):
         step()
@@ -187,17 +194,20 @@ def gated_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     api.moe_timing_enable(False)
     kt = {}
-    for f in ("build_schedule", "gated_up", "fill_zero", "gated_down"):
+    for f in ("build_schedule", "gated_up", "fill_zero", "gated_down", "bwd_dx", "bwd_dw"):
         tot, n = api.moe_timing_read(f)
         kt[f] = round(tot * 1e3 / max(n, 1), 3)
     fl_up = 2.0 * S * g.K * 2 * g.F
     fl_dn = 2.0 * S * g.F * g.N
+    # backward: dh and dW_down (2 S N F each), dX and dW_gu (2 S 2F K each)
+    fl_bwd = 2 * fl_dn + 2 * fl_up
     up_tf = fl_up / (kt["gated_up"] * 1e-6) / 1e12
-    del x, Wgu, Wd, h, y
-    return {"workload": f"{g.name} forward (schedule + gated up + zero y + down)",
+    del x, Wgu, Wd, h, y, gu, dY
+    return {"workload": f"{g.name} forward + backward (schedule, gated up saving gate/up, zero y, "
+                        "down; dW_down, dh/dgu/d_topk, dX, dW_gu)",
             "T": g.T, "K": g.K, "F": g.F, "N": g.N, "E": g.E, "top_k": g.k,
             "step_ms": round(ms_step, 4),
-            "tflops": round((fl_up + fl_dn) / (ms_step * 1e-3) / 1e12, 2),
+            "tflops": round((fl_up + fl_dn + fl_bwd) / (ms_step * 1e-3) / 1e12, 2),
             "kernels_us": kt,
             "gated_up_tflops": round(up_tf, 2),
             "gated_down_tflops": round(fl_dn / (kt["gated_down"] * 1e-6) / 1e12, 2),
