@@ -194,7 +194,8 @@ def gated_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     api.moe_timing_enable(False)
     kt = {}
-    for f in ("build_schedule", "gated_up", "fill_zero", "gated_down", "bwd_dx", "bwd_dw"):
+    for f in ("build_schedule", "gated_up", "fill_zero", "gated_down", "gated_bwd_dw_down",
+              "gated_bwd_dh", "gated_bwd_dx", "gated_bwd_dw_gu"):
         tot, n = api.moe_timing_read(f)
         kt[f] = round(tot * 1e3 / max(n, 1), 3)
     fl_up = 2.0 * S * g.K * 2 * g.F

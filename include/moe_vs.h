@@ -297,7 +297,8 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
  * kernel it launches with a pair of HIP events recorded on that launch's own
  * stream and keeps them per kernel family.  Families: "build_schedule",
  * "fill_zero", "grouped_gemm", "fused_fwd", "bwd_dx", "bwd_dw", "tile_map",
- * "gated_up", "gated_down", "fused_fwd_fp8".
+ * "gated_up", "gated_down", "fused_fwd_fp8", "gated_bwd_dw_down",
+ * "gated_bwd_dh", "gated_bwd_dx", "gated_bwd_dw_gu".
  *   moe_timing_enable(1) clears earlier records and starts recording;
  *   moe_timing_enable(0) stops recording (records are kept).
  *   moe_timing_read waits for the recorded events of `family` and returns the

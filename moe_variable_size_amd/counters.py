@@ -32,6 +32,9 @@ COPY_BYTES = 256 << 20   # bench.py --calib-copy: 64 Mi float32 copied device to
 # forward-shaped kernels: mfma_fwd_kernel<BM, BN, WGM, WGN, MODE, Tout, F8>
 _FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+), (true|false)>")
 FWD_MODES = {0: "grouped_gemm", 1: "fused_fwd", 2: "gated_up", 3: "gated_down"}
+# input-gradient kernels: mfma_dx_kernel<NW, GB, ROWS>; weight gradient: mfma_dw_kernel<Tout, NW, RM>
+_DX = re.compile(r"mfma_dx_kernel<(\d+), (true|false), (true|false)>")
+_DW = re.compile(r"mfma_dw_kernel<[^,<>]+, (\d+), (\d+)>")
 
 
 def source_digest() -> str:
@@ -56,10 +59,13 @@ def _family(name: str):
         if fam == "fused_fwd" and bm == 64:
             fam = "decode_fwd"
         return fam + "_fp8" if f8 else fam
-    if "mfma_dx_kernel" in name:
-        return "bwd_dx"
-    if "mfma_dw_kernel" in name:
-        return "bwd_dw"
+    m = _DX.search(name)
+    if m:
+        gb, rows = m.group(2) == "true", m.group(3) == "true"
+        return "gated_bwd_dh" if gb else "gated_bwd_dx" if rows else "bwd_dx"
+    m = _DW.search(name)
+    if m:
+        return {0: "bwd_dw", 1: "gated_bwd_dw_down", 2: "gated_bwd_dw_gu"}.get(int(m.group(2)))
     return None
 
 

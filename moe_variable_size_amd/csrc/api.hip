@@ -106,7 +106,8 @@ bool fits(int64_t rows, int64_t cols, int32_t dtype) {
 // ---- kernel timing (benchmarks only) ---------------------------------------
 const char *const kFamilies[] = {"build_schedule", "fill_zero", "grouped_gemm", "fused_fwd",
                                  "bwd_dx", "bwd_dw", "tile_map", "gated_up", "gated_down",
-                                 "fused_fwd_fp8"};
+                                 "fused_fwd_fp8", "gated_bwd_dw_down", "gated_bwd_dh",
+                                 "gated_bwd_dx", "gated_bwd_dw_gu"};
 constexpr int kNumFamilies = sizeof(kFamilies) / sizeof(kFamilies[0]);
 
 struct Timing {
@@ -141,7 +142,7 @@ hipError_t timed(int fam, hipStream_t st, F &&f) {
 }
 
 enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP, F_GATED_UP, F_GATED_DOWN,
-       F_FWD_FP8 };
+       F_FWD_FP8, F_GB_DWD, F_GB_DH, F_GB_DX, F_GB_DWGU };
 
 }  // namespace
 }  // namespace moe
@@ -355,7 +356,7 @@ int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const voi
   hipError_t e = hipSuccess;
   // 1. dW_down = sum (w dY)^T h (zeroes dX and d_topk on the side), or one fill
   if (dW_down)
-    e = timed(F_DW, st, [&] {
+    e = timed(F_GB_DWD, st, [&] {
       return mfma_bwd_dw_rows(dY, false, h, true, s, dW_down, (int)F, (int)N, true, dX, dx_bytes,
                               d_topk, dt_bytes, st);
     });
@@ -363,16 +364,16 @@ int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const voi
     e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, dx_bytes, d_topk, dt_bytes, st); });
   // 2. G = dY W_down per row; d_topk += <G, h>; dgu from the saved gate / up
   if (e == hipSuccess && (need_dgu || d_topk))
-    e = timed(F_DX, st, [&] {
+    e = timed(F_GB_DH, st, [&] {
       return mfma_gated_bwd_dh(dY, h, W_down, s, d_topk, (int)F, (int)N, gu,
                                need_dgu ? dgu : nullptr, st);
     });
   // 3. dX[t] += dgu[r] W_gu[e]
   if (e == hipSuccess && dX)
-    e = timed(F_DX, st, [&] { return mfma_gated_bwd_dx(dgu, W_gu, s, dX, (int)K, (int)F, st); });
+    e = timed(F_GB_DX, st, [&] { return mfma_gated_bwd_dx(dgu, W_gu, s, dX, (int)K, (int)F, st); });
   // 4. dW_gu = sum dgu^T x
   if (e == hipSuccess && dW_gu)
-    e = timed(F_DW, st, [&] {
+    e = timed(F_GB_DWGU, st, [&] {
       return mfma_bwd_dw_rows(dgu, true, x, false, s, dW_gu, (int)K, (int)(2 * F), false,
                               nullptr, 0, nullptr, 0, st);
     });

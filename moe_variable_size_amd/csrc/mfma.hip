@@ -1112,8 +1112,6 @@ struct DxArgs {
   int stream_k;
   int tail_split;  // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int tile_rows;   // 0 = picked on the device, 128 / 256 = forced
-  int a_by_row;    // 1: A row of schedule row r is row r of dY (already in schedule order)
-  int unweighted;  // 1: scatter G itself (the routing weight is already in the operand)
   // gated FFN backward (GB kernels): x is h [R, K] read by schedule row, gu the
   // saved gate/up values [R, 2K] (fp32), dgu the output [R, 2K] (bf16; K here is F)
   const float *gu;
@@ -1170,7 +1168,9 @@ struct DxOp {
 // dh = w * G, reads the saved gate g and up u of its row, and stores
 // dg = dh * u * silu'(g) and du = dh * silu(g) into dgu; the routing-weight
 // gradient takes h (read by schedule row) where the plain kernel takes x.
-template <int NW, bool GB = false>
+// ROWS: A (dY's place) is already in schedule row order and carries the routing
+// weight (the gated FFN's dgu): read by row, scattered unweighted.
+template <int NW, bool GB = false, bool ROWS = false>
 __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = NW / 2, NTH = NW * 64;
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
@@ -1225,9 +1225,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       const int r = c.row0 + tid;
       const int t = ok ? p.row_to_token[r] : -1;
       tok[tid] = t;
-      wgt[tid] = ok ? (p.unweighted ? 1.f : p.row_weight[r]) : 0.f;
+      wgt[tid] = ok ? (ROWS ? 1.f : p.row_weight[r]) : 0.f;
       asg[tid] = ok ? p.row_to_assign[r] : -1;
-      rowoff_a[tid] = t >= 0 ? (p.a_by_row ? r : t) * N * 2 : -1;
+      rowoff_a[tid] = t >= 0 ? (ROWS ? r : t) * N * 2 : -1;
     }
     __syncthreads();
     op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
@@ -1397,7 +1397,6 @@ struct DwArgs {
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes, rw_bytes;
   int weighted;
-  int dy_by_row, x_by_row;  // 1: that operand is already in schedule row order (row r, not token)
   // zeroed by the kernel on the side (the accumulation targets of the input
   // gradient kernel that runs after it): byte ranges, NULL / 0 when unused
   float *zero0;
@@ -1422,7 +1421,10 @@ MOE_DEV void zero_share(float *p, size_t bytes, int Lb, int G) {
   if (Lb == 0 && threadIdx.x < tail / 4) p[n16 * 4 + threadIdx.x] = 0.f;
 }
 
-template <int NW>
+// RM: operands read by schedule row instead of by token (an operand already in
+// schedule order): 0 none, DW_X_ROWS x, DW_DY_ROWS dY
+enum { DW_GATHER = 0, DW_X_ROWS = 1, DW_DY_ROWS = 2 };
+template <int NW, int RM = DW_GATHER>
 struct DwOp {
   using Map = MnmajMapT<NW>;
   static constexpr int PW = Map::PER_WAVE;  // dY (and x) instructions per wave per stage
@@ -1442,7 +1444,7 @@ struct DwOp {
   __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
   uint32_t lds0;
   const char *lds;
-  int r0, m, wid, lane, K, N, weighted, dy_by_row, x_by_row;
+  int r0, m, wid, lane, K, N, weighted;
   uint32_t ncol[PW], kcol[PW];  // byte offsets of this lane's column chunk (dY / x), or OOB
   i32x4 tq[PW / 2];             // tokens of this wave's 2*PW rows of the stage being issued
 
@@ -1479,13 +1481,13 @@ struct DwOp {
       int tok = (lane >> 5) ? to : te;
       if (q >= m) tok = -1;
       if (j < PW) {
-        const int ry = dy_by_row ? r0 + q : tok;  // row of dY (valid when tok >= 0)
+        const int ry = RM == DW_DY_ROWS ? r0 + q : tok;  // row of dY (valid when tok >= 0)
         const uint32_t offy = (tok >= 0 && ncol[i] != kOobOffset)
                                   ? (uint32_t)ry * (uint32_t)N * 2u + ncol[i]
                                   : kOobOffset;
         dma16(rsY, offy, t + Map::lds_of(wid, i));
       } else {
-        const int rx = x_by_row ? r0 + q : tok;
+        const int rx = RM == DW_X_ROWS ? r0 + q : tok;
         const uint32_t offx = (tok >= 0 && kcol[i] != kOobOffset)
                                   ? (uint32_t)rx * (uint32_t)K * 2u + kcol[i]
                                   : kOobOffset;
@@ -1519,7 +1521,7 @@ struct DwOp {
 
 // NW waves: 4 (2 x 2 grid, 128 x 128 per wave) or 8 (4 x 2, 64 x 128 per wave:
 // two waves per SIMD, half the LDS reads per wave per MFMA step)
-template <typename Tout, int NW>
+template <typename Tout, int NW, int RM = DW_GATHER>
 __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   constexpr int BM = 256, BN = 256, WGM = NW == 8 ? 4 : 2, WGN = 2;
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
@@ -1535,7 +1537,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   // the next kernel's accumulation targets, zeroed while this one runs
   zero_share<NW * 64>(p.zero0, p.zero0_bytes, L, G);
   zero_share<NW * 64>(p.zero1, p.zero1_bytes, L, G);
-  DwOp<NW> op;
+  DwOp<NW, RM> op;
   op.rsY = uniform_rsrc(p.dY, p.dy_bytes);
   op.rsX = uniform_rsrc(p.x, p.x_bytes);
   op.rsW = uniform_rsrc(p.row_weight, p.rw_bytes);
@@ -1547,8 +1549,6 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   op.K = K;
   op.N = N;
   op.weighted = p.weighted;
-  op.dy_by_row = p.dy_by_row;
-  op.x_by_row = p.x_by_row;
 
   for (int round = 0;; ++round) {
     const int base = round * G;
@@ -1798,9 +1798,11 @@ hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedu
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, 2 * F,
            (uint32_t)((size_t)s.R * 2 * F * 2), 0u, 0, tail_split(), forced_bm()};
-  a.a_by_row = 1;
-  a.unweighted = 1;
-  return launch_dx(a, st);
+  const dim3 grid(device_cu_count());
+  hipError_t e = set_smem<mfma_dx_kernel<4, false, true>>(kStageLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_dx_kernel<4, false, true>), grid, dim3(256), kStageLds, st, a);
+  return hipGetLastError();
 }
 
 static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
@@ -1813,6 +1815,24 @@ static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
     hipError_t e = set_smem<mfma_dx_kernel<8>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(mfma_dx_kernel<8>, grid, dim3(512), kStageLds, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int RM>
+static hipError_t launch_dw(const DwArgs &a, hipStream_t st) {
+  if (dw_waves() == 4) {
+    constexpr size_t lds = DwOp<4, RM>::LDS_BYTES;
+    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 4, RM>>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 4, RM>), dim3(device_cu_count()), dim3(256), lds,
+                       st, a);
+  } else {
+    constexpr size_t lds = DwOp<8, RM>::LDS_BYTES;
+    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM>>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM>), dim3(device_cu_count()), dim3(512), lds,
+                       st, a);
   }
   return hipGetLastError();
 }
@@ -1846,24 +1866,14 @@ hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool 
   a.x_bytes = (uint32_t)((size_t)(x_by_row ? s.R : s.T) * K * 2);
   a.rw_bytes = (uint32_t)((size_t)s.R * 4);
   a.weighted = weighted ? 1 : 0;
-  a.dy_by_row = dy_by_row ? 1 : 0;
-  a.x_by_row = x_by_row ? 1 : 0;
   a.zero0 = zero0;
   a.zero0_bytes = zero0_bytes;
   a.zero1 = zero1;
   a.zero1_bytes = zero1_bytes;
-  if (dw_waves() == 4) {
-    constexpr size_t lds = DwOp<4>::LDS_BYTES;
-    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 4>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 4>), dim3(device_cu_count()), dim3(256), lds, st, a);
-  } else {
-    constexpr size_t lds = DwOp<8>::LDS_BYTES;
-    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8>), dim3(device_cu_count()), dim3(512), lds, st, a);
-  }
-  return hipGetLastError();
+  if (dy_by_row && x_by_row) return hipErrorInvalidValue;
+  if (dy_by_row) return launch_dw<DW_DY_ROWS>(a, st);
+  if (x_by_row) return launch_dw<DW_X_ROWS>(a, st);
+  return launch_dw<DW_GATHER>(a, st);
 }
 
 }  // namespace moe

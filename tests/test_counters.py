@@ -12,7 +12,11 @@ def test_families_of_demangled_names():
     assert f("mfma_fwd_kernel<256, 256, 2, 4, 2, float, false>") == "gated_up"
     assert f("mfma_fwd_kernel<256, 256, 2, 4, 3, float, false>") == "gated_down"
     assert f("mfma_fwd_kernel<256, 256, 2, 4, 0, unsigned short, false>") == "grouped_gemm"
-    assert C._family(ns + "mfma_dx_kernel<4>(moe::(anonymous namespace)::DxArgs)") == "bwd_dx"
-    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8>(DwArgs)") == "bwd_dw"
+    assert C._family(ns + "mfma_dx_kernel<4, false, false>(moe::(anonymous namespace)::DxArgs)") == "bwd_dx"
+    assert C._family(ns + "mfma_dx_kernel<4, true, false>(DxArgs)") == "gated_bwd_dh"
+    assert C._family(ns + "mfma_dx_kernel<4, false, true>(DxArgs)") == "gated_bwd_dx"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0>(DwArgs)") == "bwd_dw"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 1>(DwArgs)") == "gated_bwd_dw_down"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 2>(DwArgs)") == "gated_bwd_dw_gu"
     assert C._family("__amd_rocclr_copyBuffer") == "copy"
     assert C._family(ns + "sched_hist_kernel(int const*)") is None
