@@ -1307,6 +1307,25 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
           uint32_t ro[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) ro[q] = (uint32_t)t4[q] * (uint32_t)K * 4u;
+          // GB: the saved gate / up values of this lane's 4 rows x NIc columns,
+          // all loads issued together (dead elements read element 0, a valid
+          // address, and are not used)
+          float gvs[GB ? NIc : 1][4], uvs[GB ? NIc : 1][4];
+          if constexpr (GB) {
+            if (p.dgu) {
+#pragma unroll
+              for (int ni = 0; ni < NIc; ++ni) {
+                const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const bool live = t4[q] >= 0 && cl < ncols;
+                  const size_t gi = live ? (size_t)(c.row0 + rq + q) * (2 * K) + kc0 + cl : 0;
+                  gvs[ni][q] = p.gu[gi];
+                  uvs[ni][q] = p.gu[gi + (live ? K : 0)];
+                }
+              }
+            }
+          }
 #pragma unroll
           for (int ni = 0; ni < NIc; ++ni) {
             const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);  // column inside the tile
@@ -1317,7 +1336,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
               if constexpr (GB) {
                 if (p.dgu && t4[q] >= 0 && cok) {
                   const size_t gi = (size_t)(c.row0 + rq + q) * (2 * K) + kc0 + cl;
-                  const float gv = p.gu[gi], uv = p.gu[gi + K];
+                  const float gv = gvs[ni][q], uv = uvs[ni][q];
                   const float sg = 1.f / (1.f + __expf(-gv));
                   const float dh = w4[q] * g;
                   p.dgu[gi] = f32_to_bf16(dh * uv * sg * (1.f + gv * (1.f - sg)));
