@@ -584,6 +584,36 @@ def masked_forward_fp8(xq, x_scale, Wq, w_scale, ms: MaskedSchedule, T: int, *,
     return masked_forward(x, W, ms, T, acc=acc)
 
 
+# Per-block scales (the other reading of "per-group or per-block"): every run of
+# 32 consecutive reduction elements of a token row and of an expert's weight
+# row carries its own power-of-two scale, an 8-bit exponent code E8M0 (value
+# 2^(c - 127), code 255 = NaN).  The operand value is the E4M3 value times its
+# block's scale.
+MX_BLOCK = 32
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """2^(c - 127) for each E8M0 code (NaN for 255), float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.float64)
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def mx_values(q, scales) -> np.ndarray:
+    """Values of E4M3 codes q [..., K] with per-32-element scales [..., K/32]."""
+    s = np.repeat(decode_e8m0(scales), MX_BLOCK, axis=-1)
+    return decode_e4m3(q) * s
+
+
+def moe_forward_mx(xq, x_bs, Wq, w_bs, expert_ids, topk_weights, E: int, *, acc=np.float64):
+    """Fused forward of 8-bit operands with per-32-element block scales."""
+    return moe_forward(mx_values(xq, x_bs), mx_values(Wq, w_bs), expert_ids, topk_weights, E,
+                       acc=acc)
+
+
+def masked_forward_mx(xq, x_bs, Wq, w_bs, ms: MaskedSchedule, T: int, *, acc=np.float64):
+    return masked_forward(mx_values(xq, x_bs), mx_values(Wq, w_bs), ms, T, acc=acc)
+
+
 def moe_forward_fp8_rows(xq, x_scale, Wq, w_scale, expert_ids, topk_weights, tokens, *,
                          acc=np.float64) -> np.ndarray:
     """y[t, :] of the 8-bit forward for the listed tokens only."""

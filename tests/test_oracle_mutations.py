@@ -167,7 +167,12 @@ def _gated_bwd_weighted_dw(dY, x, W_gu, W_down, expert_ids, topk_weights, E, *, 
     return dX, dWgu, dWd, d_w * np.asarray(topk_weights)
 
 
-_ORIG = {n: getattr(O, n) for n in ["routing_schedule", "tile_owner", "tile_coords", "moe_forward",
+def _mx_first_block_scale(q, scales):
+    sc = np.asarray(scales)
+    return _ORIG["mx_values"](q, np.repeat(sc[..., :1], sc.shape[-1], axis=-1))   # one scale per row
+
+
+_ORIG = {n: getattr(O, n) for n in ["mx_values", "routing_schedule", "tile_owner", "tile_coords", "moe_forward",
                                      "grouped_gemm", "moe_backward", "gated_activation",
                                      "gated_ffn_forward", "decode_e4m3", "moe_forward_fp8",
                                      "gated_ffn_backward"]}
@@ -212,6 +217,8 @@ CASES = [
     ("gated routing-weight gradient from the weighted product", "gated_ffn_backward",
      lambda: _gated_bwd_weighted_dw,
      [P.test_gated_backward_finite_differences, P.test_gated_backward_identities]),
+    ("block scales collapsed to one per row", "mx_values", lambda: _mx_first_block_scale,
+     [P.test_mx_forward_brute_force_and_block_structure]),
     ("fp8 channel scale collapsed to one per expert", "moe_forward_fp8",
      lambda: _fp8_channel_scale_on_rows,
      [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),

@@ -752,3 +752,43 @@ def test_round_bf16_against_torch():
     ref = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(O.round_bf16(v), ref)
     assert O.round_bf16(1.0 + 2.0 ** -8) == 1.0 and O.round_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+
+
+def test_e8m0_decode_closed_form():
+    c = np.arange(256, dtype=np.uint8)
+    v = O.decode_e8m0(c)
+    assert np.isnan(v[255]) and v[127] == 1.0 and v[128] == 2.0 and v[0] == 2.0 ** -127
+    assert np.array_equal(v[:255], [math.ldexp(1.0, int(i) - 127) for i in range(255)])
+
+
+def test_mx_forward_brute_force_and_block_structure():
+    """Each 32-element block of x and W takes its own scale: brute force over
+    blocks, and a scale change in one block moves only that block's terms."""
+    import torch
+    rng, xq, Wq, ids, w = _tiny_fp8(84, T=6, K=64, N=5, E=3, k=2)
+    T, K = xq.shape
+    E, N, _ = Wq.shape
+    xs = rng.integers(120, 134, size=(T, K // 32)).astype(np.uint8)
+    ws = rng.integers(120, 134, size=(E, N, K // 32)).astype(np.uint8)
+    dec = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xv, Wv = dec(xq), dec(Wq)
+    ref = np.zeros((T, N))
+    for t in range(T):
+        for j in range(2):
+            e = ids[t, j]
+            for n in range(N):
+                tot = 0.0
+                for b in range(K // 32):
+                    sc = 2.0 ** (int(xs[t, b]) - 127) * 2.0 ** (int(ws[e, n, b]) - 127)
+                    tot += sc * sum(float(xv[t, c]) * float(Wv[e, n, c]) for c in range(32 * b, 32 * b + 32))
+                ref[t, n] += w[t, j] * tot
+    y = O.moe_forward_mx(xq, xs, Wq, ws, ids, w, E)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+    # raising block 1's scale of every x row by 2^3 multiplies exactly that block's part by 8
+    xs2 = xs.copy()
+    xs2[:, 1] += 3
+    y2 = O.moe_forward_mx(xq, xs2, Wq, ws, ids, w, E)
+    only0 = xs.copy()
+    only0[:, 1] = 0                     # 2^-127: block 1 contributes nothing measurable
+    y0 = O.moe_forward_mx(xq, only0, Wq, ws, ids, w, E)
+    assert np.allclose(y2 - y0, 8 * (y - y0), rtol=1e-12, atol=1e-12)
