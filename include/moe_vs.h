@@ -189,6 +189,23 @@ int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
                       int64_t N, void *stream);
 
 /*
+ * Fused MoE forward on 8-bit operands with per-block scales ([GG] "Choosing
+ * an implementation": FP8 brings per-group or per-block scale factors; this
+ * is the per-block form the gfx950 matrix cores apply themselves): every run
+ * of 32 consecutive reduction elements of a token row and of an expert weight
+ * row carries a power-of-two scale, an E8M0 code c with value 2^(c - 127):
+ *     y[t, n] = sum_j w[t, j] * sum_b 2^(x_bs[t, b] - 127) * 2^(w_bs[e, n, b] - 127)
+ *               * sum_{k in block b} q(x_q[t, k]) * q(W_q[e, n, k]),  e = ids[t, j],
+ * with q(.) the E4M3 value as in moe_fused_fwd_fp8.
+ *   x_q [T, K], W_q [E, N, K] uint8 codes (16-byte aligned); x_bs [T, K/32],
+ *   w_bs [E, N, K/32] uint8 E8M0 codes (4-byte aligned); K a multiple of 128
+ *   (MOE_ERR_SHAPE otherwise).  sched from moe_build_schedule (either
+ *   layout); y [T, N] float, OVERWRITTEN.
+ */
+int moe_fused_fwd_mx(const void *x_q, const uint8_t *x_bs, const void *W_q, const uint8_t *w_bs,
+                     const moe_schedule *sched, float *y, int64_t K, int64_t N, void *stream);
+
+/*
  * Gated expert FFN forward ([GG] "Choosing an implementation": the gate and up
  * projections run as one grouped GEMM over a weight with twice the output
  * rows, with the activation in that GEMM's epilogue; the down projection is
@@ -298,7 +315,7 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
  * stream and keeps them per kernel family.  Families: "build_schedule",
  * "fill_zero", "grouped_gemm", "fused_fwd", "bwd_dx", "bwd_dw", "tile_map",
  * "gated_up", "gated_down", "fused_fwd_fp8", "gated_bwd_dw_down",
- * "gated_bwd_dh", "gated_bwd_dx", "gated_bwd_dw_gu".
+ * "gated_bwd_dh", "gated_bwd_dx", "gated_bwd_dw_gu", "fused_fwd_mx".
  *   moe_timing_enable(1) clears earlier records and starts recording;
  *   moe_timing_enable(0) stops recording (records are kept).
  *   moe_timing_read waits for the recorded events of `family` and returns the

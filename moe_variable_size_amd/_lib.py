@@ -55,6 +55,7 @@ SIGNATURES = {
     "grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "moe_fused_fwd": (ctypes.c_int, [_P, _P, _SCHED_P, _P, _I64, _I64, _I32, _P]),
     "moe_fused_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _SCHED_P, _P, _I64, _I64, _P]),
+    "moe_fused_fwd_mx": (ctypes.c_int, [_P, _P, _P, _P, _SCHED_P, _P, _I64, _I64, _P]),
     "moe_gated_ffn_fwd": (ctypes.c_int, [_P, _P, _P, _SCHED_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "moe_gated_ffn_bwd_workspace_bytes": (_SZ, [_SCHED_P, _I64]),
     "moe_gated_ffn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _SCHED_P, _P, _P, _P, _P, _P, _P, _I64,

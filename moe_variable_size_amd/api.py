@@ -207,6 +207,30 @@ def moe_fused_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, W_q: torch.Tenso
     return y
 
 
+def moe_fused_fwd_mx(x_q: torch.Tensor, x_bs: torch.Tensor, W_q: torch.Tensor, w_bs: torch.Tensor,
+                     sched: Schedule, *, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Fused MoE forward on 8-bit E4M3 operands with a power-of-two (E8M0,
+    uint8) scale per 32 reduction elements: x_bs [T, K/32], w_bs [E, N, K/32];
+    y [T, N] float32."""
+    lib = _lib.load()
+    _require(x_q, "x_q", None, 2)
+    _require(W_q, "W_q", None, 3)
+    _require(x_bs, "x_bs", torch.uint8, 2)
+    _require(w_bs, "w_bs", torch.uint8, 3)
+    T, K = x_q.shape
+    E, N, K2 = W_q.shape
+    if K2 != K or T != sched.c.T or E != sched.c.E or tuple(x_bs.shape) != (T, K // 32) \
+            or tuple(w_bs.shape) != (E, N, K // 32):
+        raise ValueError("shape mismatch between x_q, W_q, their block scales and the schedule")
+    if y is None:
+        y = torch.empty((T, N), dtype=torch.float32, device=x_q.device)
+    _require(y, "y", torch.float32, 2)
+    st = lib.moe_fused_fwd_mx(_ptr(x_q), _ptr(x_bs), _ptr(W_q), _ptr(w_bs), ctypes.byref(sched.c),
+                              _ptr(y), K, N, _stream(stream))
+    _lib.check("moe_fused_fwd_mx", st)
+    return y
+
+
 def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor, sched: Schedule, *,
                       h: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                       gu: Optional[torch.Tensor] = None, save_gu: bool = False, stream=None):

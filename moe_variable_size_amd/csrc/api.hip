@@ -107,7 +107,7 @@ bool fits(int64_t rows, int64_t cols, int32_t dtype) {
 const char *const kFamilies[] = {"build_schedule", "fill_zero", "grouped_gemm", "fused_fwd",
                                  "bwd_dx", "bwd_dw", "tile_map", "gated_up", "gated_down",
                                  "fused_fwd_fp8", "gated_bwd_dw_down", "gated_bwd_dh",
-                                 "gated_bwd_dx", "gated_bwd_dw_gu"};
+                                 "gated_bwd_dx", "gated_bwd_dw_gu", "fused_fwd_mx"};
 constexpr int kNumFamilies = sizeof(kFamilies) / sizeof(kFamilies[0]);
 
 struct Timing {
@@ -142,7 +142,7 @@ hipError_t timed(int fam, hipStream_t st, F &&f) {
 }
 
 enum { F_SCHED = 0, F_FILL, F_BARE, F_FWD, F_DX, F_DW, F_TILEMAP, F_GATED_UP, F_GATED_DOWN,
-       F_FWD_FP8, F_GB_DWD, F_GB_DH, F_GB_DX, F_GB_DWGU };
+       F_FWD_FP8, F_GB_DWD, F_GB_DH, F_GB_DX, F_GB_DWGU, F_FWD_MX };
 
 }  // namespace
 }  // namespace moe
@@ -279,6 +279,30 @@ int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(timed(F_FWD_FP8, st, [&] {
     return mfma_fused_fwd_fp8(x_q, x_scale, W_q, w_scale, s, y, (int)K, (int)N, st);
+  }));
+}
+
+int moe_fused_fwd_mx(const void *x_q, const uint8_t *x_bs, const void *W_q, const uint8_t *w_bs,
+                     const moe_schedule *sched, float *y, int64_t K, int64_t N, void *stream) {
+  int rc = check_sched(sched);
+  if (rc) return rc;
+  if (K < 128 || N < 1 || K % 128 != 0) return MOE_ERR_SHAPE;
+  if (K >= kMax32 || N >= kMax32) return MOE_ERR_LIMIT;
+  if (!x_q || !x_bs || !W_q || !w_bs || !y) return MOE_ERR_NULL;
+  const moe_schedule &s = *sched;
+  if ((double)s.T * K >= (double)kMax32 || (double)N * K >= (double)kMax32 ||
+      !fits(s.T, N, MOE_F32))
+    return MOE_ERR_LIMIT;
+  if (!aligned(x_q, 16) || !aligned(W_q, 16) || !aligned(x_bs, 4) || !aligned(w_bs, 4) ||
+      !aligned(y, 4))
+    return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e =
+      timed(F_FILL, st,
+            [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st); });
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(timed(F_FWD_MX, st, [&] {
+    return mfma_fused_fwd_mx(x_q, x_bs, W_q, w_bs, s, y, (int)K, (int)N, st);
   }));
 }
 

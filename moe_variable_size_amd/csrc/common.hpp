@@ -103,6 +103,11 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
 hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *Wq,
                               const float *w_scale, const moe_schedule &s, float *y, int K, int N,
                               hipStream_t st);
+// 8-bit (E4M3) operands with E8M0 block scales per 32 reduction elements:
+// x_bs [T, K/32], w_bs [E, N, K/32]; K a multiple of 128
+hipError_t mfma_fused_fwd_mx(const void *xq, const uint8_t *x_bs, const void *Wq,
+                             const uint8_t *w_bs, const moe_schedule &s, float *y, int K, int N,
+                             hipStream_t st);
 // h [R, F] bf16 = silu(x W_gate^T) * (x W_up^T) per schedule row; W_gu [E, 2F, K]
 // gu (optional, NULL to skip): [R, 2F] fp32 gate and up values kept for a backward
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,

@@ -115,6 +115,14 @@ MOE_DEV void dma4(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
                : "s"(m0v), "v"(voff), "s"(rsrc)
                : "memory", "m0");
 }
+// As dma4, with the wave-uniform byte offset `soff` added (cf. dma16_so).
+MOE_DEV void dma4_so(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
 template <int N>
 MOE_DEV void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -296,14 +304,18 @@ MOE_DEV bf16x8_t frag_kmaj(const char *tile, int row, int step, int lane) {
   return *(const bf16x8_t *)(tile + kmaj_off(row, 2 * step + (lane >> 5)));
 }
 
-// 8-bit operands: a step is 64 reduction elements (64 bytes of the row); lane
-// half h takes the 32 bytes 32h .. 32h+31 (chunks 4 step + 2h, + 1).  A and B
-// fragments are read with the same pattern, so the products pair the same
-// reduction index whatever order the matrix core assigns inside a lane.
+// 8-bit operands: a step is 64 reduction elements (64 bytes of the row, 16-byte
+// chunks 4 step + 0..3).  The matrix core takes bytes 0-15 of both lane halves
+// as its first 32-element block (scaled by the half-0 lane's block scale) and
+// bytes 16-31 as its second (half-1 lane's scale) -- measured with one-hot
+// operands on gfx950.  So lane half h loads chunk h (elements 16h .. 16h+15)
+// into bytes 0-15 and chunk 2 + h (32 + 16h ..) into bytes 16-31: the first
+// block is elements 0-31 of the step, the second 32-63, as the block scales
+// count them.  A and B fragments use the same pattern.
 MOE_DEV i32x8 frag_kmaj8(const char *tile, int row, int step, int lane) {
-  const int c = 4 * step + 2 * (lane >> 5);
+  const int c = 4 * step + (lane >> 5);
   const i32x4 lo = *(const i32x4 *)(tile + kmaj_off(row, c));
-  const i32x4 hi = *(const i32x4 *)(tile + kmaj_off(row, c + 1));
+  const i32x4 hi = *(const i32x4 *)(tile + kmaj_off(row, c + 2));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -389,6 +401,8 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   using frag_t = std::conditional_t<F8, i32x8, bf16x8_t>;
   frag_t fa[2][MI], fb[2][NI];
   float sc[2][8];
+  constexpr bool MXS = Op::MX;  // block scales ride with each fragment
+  uint32_t fsa[2][MXS ? MI : 1], fsb[2][MXS ? NI : 1];
 
   // read item f, in order of first use by the next step's MFMAs (mi outer,
   // ni inner): [scale factors], A0, B0 .. B(NI-1), A1 .. A(MI-1)
@@ -403,10 +417,14 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
     if constexpr (F8) {
       if (g == 0 || g > NI) {
         const int mi = g == 0 ? 0 : g - NI;
-        fa[slot][mi] = frag_kmaj8(As, wm * 32 + mi * 32 * WGM + (lane & 31), step, lane);
+        const int row = wm * 32 + mi * 32 * WGM + (lane & 31);
+        fa[slot][mi] = frag_kmaj8(As, row, step, lane);
+        if constexpr (MXS) fsa[slot][mi] = op.scale_of(buf, false, row, step, lane);
       } else {
         const int ni = g - 1;
-        fb[slot][ni] = frag_kmaj8(Bs, wn * 32 + ni * 32 * WGN + (lane & 31), step, lane);
+        const int row = wn * 32 + ni * 32 * WGN + (lane & 31);
+        fb[slot][ni] = frag_kmaj8(Bs, row, step, lane);
+        if constexpr (MXS) fsb[slot][ni] = op.scale_of(buf, true, row, step, lane);
       }
       return;
     } else {
@@ -428,7 +446,10 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   auto mfma = [&](int slot, int i) __attribute__((always_inline)) {
     const int mi = i / NI, ni = i % NI;
     if (SKIP && (mi >= live_mi || ni >= live_ni)) return;  // wave-uniform
-    if constexpr (F8)
+    if constexpr (MXS)
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fa[slot][mi], fb[slot][ni], acc[mi][ni], 0, 0, 0, fsa[slot][mi], 0, fsb[slot][ni]);
+    else if constexpr (F8)
       acc[mi][ni] = mfma_f8(fa[slot][mi], fb[slot][ni], acc[mi][ni]);
     else
       acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][mi], fb[slot][ni],
@@ -731,6 +752,8 @@ struct FwdArgs {
   const float *x_scale;  // 8-bit operands: per-token scale [T]
   const float *w_scale;  // 8-bit operands: per-expert output-channel scale [E, N]
   float *gu_out;         // gated: [R, 2F] gate and up values (fp32) kept for a backward, or NULL
+  const uint8_t *x_bs;   // 8-bit with block scales: E8M0 codes [T, K/32]
+  const uint8_t *w_bs;   // 8-bit with block scales: E8M0 codes [E, N, K/32]
 };
 
 // What a forward-shaped kernel writes:
@@ -746,26 +769,50 @@ struct FwdArgs {
 enum { FWD_BARE = 0, FWD_SCATTER = 1, FWD_GATED = 2, FWD_SCATTER_ROWS = 3 };
 
 // F8: 8-bit operands (a stage is 128 reduction elements; K below is the
-// reduction length in 2-byte units, i.e. row bytes / 2, for the bounds checks)
-template <int BM, int BN, int NW, bool F8_ = false>
+// reduction length in 2-byte units, i.e. row bytes / 2, for the bounds checks).
+// MX: 8-bit operands with a power-of-two (E8M0) scale per 32 reduction
+// elements of every A and B row, applied by the matrix cores.
+template <int BM, int BN, int NW, bool F8_ = false, bool MX_ = false>
 struct FwdOp {
   static constexpr bool A_KMAJ = true, B_KMAJ = true, A_SCALED = false, PREFETCH = false;
-  static constexpr bool F8 = F8_;
+  static constexpr bool F8 = F8_, MX = MX_;
   static constexpr bool CHECKED_TAIL = true;
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
-  static constexpr int DMA_PER_STAGE = DA + DB;
+  // MX: the block scales of a stage, one 4-byte word (4 blocks of 32) per A
+  // row and per B row, after the stages in LDS (A rows, then B rows)
+  static constexpr int SCG = (BM + BN) / 64;           // 64-row scale groups per stage
+  static constexpr int DS = MX ? SCG / NW : 0;          // scale loads per wave per stage
+  static_assert(!MX || (SCG % NW == 0 && BM % 64 == 0), "scale groups per wave");
+  static constexpr int SC_STAGE = (BM + BN) * 4;
+  static constexpr int SC_OFF = NSTAGE * STAGE;
+  static constexpr int DMA_PER_STAGE = DA + DB + DS;
   KmajDma<BM, NW> da;
   KmajDma<BN, NW> db;
-  __amdgpu_buffer_rsrc_t rsA, rsW;
+  __amdgpu_buffer_rsrc_t rsA, rsW, rsAS, rsWS;
   uint32_t lds0;
+  const char *ldsp;
+  uint32_t soff[DS > 0 ? DS : 1];  // MX: per-lane byte offset of the row's scales, or OOB
   int K, wid;
   template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
-    if (j < DA)
+    if (j < DA) {
       da.template issue_one<SKIP, CHECKED>(rsA, kt, K, t, wid, j);
-    else
+    } else if (j < DA + DB) {
       db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + OPND, wid, j - DA);
+    } else if constexpr (MX) {
+      const int i = j - DA - DB, grp = wid * DS + i;  // 64-row group of A rows, then B rows
+      dma4_so(grp < BM / 64 ? rsAS : rsWS, soff[i], (uint32_t)kt * 4u,
+              lds0 + (uint32_t)(SC_OFF + buf * SC_STAGE + grp * 256));
+    }
+  }
+  // E8M0 scale of row `row` (A or B) for step `step`: the lane in half h
+  // supplies block 2 step + h of the stage (elements 32h .. 32h+31 of the
+  // step, spread over both halves' fragments), in byte 0
+  MOE_DEV uint32_t scale_of(int buf, bool b_side, int row, int step, int lane) const {
+    const uint32_t w = *(const uint32_t *)(ldsp + SC_OFF + buf * SC_STAGE + (b_side ? BM * 4 : 0) +
+                                           row * 4);
+    return (w >> (8 * (2 * step + (lane >> 5)))) & 0xffu;
   }
   MOE_DEV void prefetch(int) {}
   MOE_DEV void row_scale(int, int, int, float (&)[8]) {}
@@ -774,7 +821,7 @@ struct FwdOp {
 // A (BM rows) and B (BN rows) K-major for the deep pipeline of small tiles.
 template <int BM, int BN, int NW, bool F8_ = false>
 struct FwdDeepOp {
-  static constexpr bool F8 = F8_;  // as FwdOp
+  static constexpr bool F8 = F8_, MX = false;  // as FwdOp
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
   static_assert(DA >= 1 && DB >= 1, "at least one DMA row group per wave");
   static constexpr int DMA_PER_STAGE = DA + DB;
@@ -805,7 +852,8 @@ struct FwdDeepOp {
   }
 };
 
-template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout, bool F8 = false>
+template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout, bool F8 = false,
+          bool MX = false>
 __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr bool FUSED = MODE != FWD_BARE;       // rows come from a routing schedule
   constexpr bool GATED = MODE == FWD_GATED;
@@ -814,6 +862,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   static_assert(!GATED || NI % 2 == 0, "gate and up blocks pair up inside a wave");
   static_assert(!F8 || MODE == FWD_SCATTER, "8-bit operands: the routed scatter forward");
+  static_assert(!MX || (F8 && BM == 256), "block scales: 8-bit operands, 256-row kernel");
   constexpr int NW = WGM * WGN, NTH = NW * 64;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int ESZ = F8 ? 1 : 2;                 // bytes per operand element
@@ -846,9 +895,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   else
     group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
   const int total = bs[E] * tiles_n;
-  FwdOp<BM, BN, NW, F8> op;
+  FwdOp<BM, BN, NW, F8, MX> op;
   op.rsA = uniform_rsrc(p.A, p.a_bytes);
   op.lds0 = lds_addr(lds);
+  op.ldsp = lds;
+  const uint32_t kblk = (uint32_t)K / 32;  // MX: scale bytes per row
+  if constexpr (MX) op.rsAS = uniform_rsrc(p.x_bs, (uint32_t)p.M * kblk);
   op.K = K * ESZ / 2;  // reduction length in 2-byte units (the bounds checks' unit)
   op.wid = wid;
   const int wrows = GATED ? 2 * N : N;  // rows of one expert's weight
@@ -886,16 +938,33 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       const int t = ok ? (FUSED ? p.row_to_token[r] : (r < p.M ? r : -1)) : -1;
       tok[tid] = t;
       // 8-bit: the token's scale rides on its routing weight
-      wgt[tid] = (FUSED && ok) ? p.row_weight[r] * (F8 && t >= 0 ? p.x_scale[t] : 1.f) : 0.f;
+      wgt[tid] = (FUSED && ok) ? p.row_weight[r] * (F8 && !MX && t >= 0 ? p.x_scale[t] : 1.f) : 0.f;
       rowoff_a[tid] = t >= 0 ? (A_BY_ROW ? r : t) * (int)rowbytes : -1;
     }
     for (int j = tid; j < BN; j += NTH) {
       const int jj = GATED ? j % BNO : j;  // gated: gate rows, then the up rows
       rowoff_b[j] = jj < ncols ? (n0 + jj + (GATED && j >= BNO ? N : 0)) * (int)rowbytes : -1;
-      if (F8) cscale[j] = jj < ncols ? p.w_scale[(size_t)c.g * N + n0 + jj] : 0.f;
+      if (F8 && !MX) cscale[j] = jj < ncols ? p.w_scale[(size_t)c.g * N + n0 + jj] : 0.f;
     }
     __syncthreads();
     op.rsW = uniform_rsrc((const char *)p.W + (size_t)c.g * wrows * rowbytes, wbytes);
+    if constexpr (MX) {
+      // per-lane offsets of the scale rows: group grp of 64 rows (A rows, then
+      // B rows), lane = row inside the group; dead rows read out of range
+      op.rsWS = uniform_rsrc(p.w_bs + (size_t)c.g * N * kblk, (uint32_t)N * kblk);
+#pragma unroll
+      for (int i = 0; i < op.DS; ++i) {
+        const int grp = wid * op.DS + i;
+        const int ra = grp * 64 + lane;  // tile row (A) or column (B)
+        if (grp < BM / 64) {
+          const int t = tok[ra];
+          op.soff[i] = t >= 0 ? (uint32_t)t * kblk : kOobOffset;
+        } else {
+          const int jb = ra - BM;
+          op.soff[i] = jb < ncols ? (uint32_t)(n0 + jb) * kblk : kOobOffset;
+        }
+      }
+    }
     const bool part = BM <= 64 || ws.nS > 1 || BMr < BM;  // rows / columns partly dead
     // (gated: the live B rows are two runs, not a prefix; nothing is skipped)
     const int live_b = GATED ? BN : ncols;
@@ -930,8 +999,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi,
                                                dop.parts(), acc);
       } else {
-        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8>, DSK>(op, lds, kb, ke, wm, wn,
-                                                                           lane, live_mi, NIc, acc);
+        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8, MX>, DSK>(
+            op, lds, kb, ke, wm, wn, lane, live_mi, NIc, acc);
       }
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
@@ -985,7 +1054,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         const int cl0 = wn * 32 + (lane & 31);
         float cs[NIc];  // 8-bit: output-channel scale of each column block
 #pragma unroll
-        for (int ni = 0; ni < NIc; ++ni) cs[ni] = F8 ? cscale[cl0 + ni * 32 * WGN] : 1.f;
+        for (int ni = 0; ni < NIc; ++ni) cs[ni] = F8 && !MX ? cscale[cl0 + ni * 32 * WGN] : 1.f;
 #pragma unroll
         for (int mi = 0; mi < MIc; ++mi) {
           if (mi >= live_mi) continue;
@@ -1001,8 +1070,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
 #pragma unroll
               for (int ni = 0; ni < NIc; ++ni) {
                 if (!all_cols && cl0 + ni * 32 * WGN >= ncols) continue;
-                const float v = F8 ? w4[q] * cs[ni] * acc[mi][ni][4 * j + q]
-                                   : w4[q] * acc[mi][ni][4 * j + q];
+                const float v = F8 && !MX ? w4[q] * cs[ni] * acc[mi][ni][4 * j + q]
+                                          : w4[q] * acc[mi][ni][4 * j + q];
                 unsafeAtomicAdd((float *)(yb + (ro + cb[ni])), v);
               }
             }
@@ -1122,7 +1191,7 @@ template <int NW>
 struct DxOp {
   using Map = MnmajMapT<NW>;
   static constexpr bool A_KMAJ = true, B_KMAJ = false, A_SCALED = false, PREFETCH = false;
-  static constexpr bool CHECKED_TAIL = true, F8 = false;
+  static constexpr bool CHECKED_TAIL = true, F8 = false, MX = false;
   static constexpr int DA = 256 / (8 * NW), PW = Map::PER_WAVE;
   static constexpr int DMA_PER_STAGE = DA + PW;
   KmajDma<256, NW> da;
@@ -1449,7 +1518,7 @@ struct DwOp {
   static constexpr int PW = Map::PER_WAVE;  // dY (and x) instructions per wave per stage
   static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
   static constexpr bool CHECKED_TAIL = false;  // offsets are data dependent every stage
-  static constexpr bool F8 = false;
+  static constexpr bool F8 = false, MX = false;
   // per stage: PW dY + PW x instructions, the stage's routing weights, the
   // tokens of the stage two ahead
   static constexpr int DMA_PER_STAGE = 2 * PW + 1 + 1;
@@ -1711,19 +1780,21 @@ bool mfma_supported(int K, int N) { return K % 8 == 0 && N % 8 == 0; }
 
 namespace {
 // Launch a 256 x 256 forward-shaped kernel with 4 (2 x 2) or 8 (2 x 4) waves.
-template <int MODE, typename Tout, bool F8 = false>
+template <int MODE, typename Tout, bool F8 = false, bool MX = false>
 hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
+  // block scales: two stages of (256 + 256) 4-byte scale words after the operands
+  constexpr size_t lds = kStageLds + (MX ? 2 * (256 + 256) * 4 : 0);
   if ((F8 ? f8_waves() : gemm_waves()) == 4) {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8, MX>>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8>), grid, dim3(256),
-                       kStageLds, st, a);
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8, MX>), grid, dim3(256), lds,
+                       st, a);
   } else {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8>), grid, dim3(512),
-                       kStageLds, st, a);
+    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>), grid, dim3(512), lds,
+                       st, a);
   }
   return hipGetLastError();
 }
@@ -1773,6 +1844,20 @@ hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *
   a.x_scale = x_scale;
   a.w_scale = w_scale;
   return launch_routed<FWD_SCATTER, true>(a, s, st);
+}
+
+hipError_t mfma_fused_fwd_mx(const void *xq, const uint8_t *x_bs, const void *Wq,
+                             const uint8_t *w_bs, const moe_schedule &s, float *y, int K, int N,
+                             hipStream_t st) {
+  FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
+            s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
+            (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T};
+  a.x_bs = x_bs;
+  a.w_bs = w_bs;
+  a.bstart = s.block_start;
+  // one kernel for both layouts (128-row tiles; a masked expert's slots are
+  // its rows)
+  return launch_fwd256<FWD_SCATTER, float, true, true>(a, st);
 }
 
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,

@@ -385,6 +385,50 @@ def fp8_routed(r: Routed) -> Fp8Routed:
                      r.topk_weights, capacity=r.capacity)
 
 
+@dataclass
+class MxRouted:
+    """Inputs of the 8-bit routed forward with per-32-element block scales."""
+
+    name: str
+    T: int
+    K: int
+    N: int
+    E: int
+    k: int
+    xq: np.ndarray                 # [T, K] uint8 E4M3 codes
+    x_bs: np.ndarray               # [T, K/32] uint8 E8M0 codes
+    Wq: np.ndarray                 # [E, N, K] uint8 E4M3 codes
+    w_bs: np.ndarray               # [E, N, K/32] uint8 E8M0 codes
+    expert_ids: np.ndarray
+    topk_weights: Optional[np.ndarray]
+    capacity: int = 0
+
+
+def quantize_mx_blocks(a: np.ndarray, block: int = 32) -> tuple[np.ndarray, np.ndarray]:
+    """Quantize the last axis of ``a`` in blocks of ``block`` elements: a
+    power-of-two scale 2^e per block, e the smallest exponent with
+    max|block| / 2^e <= 448 (e = -127 for an all-zero block), stored as the
+    E8M0 code 127 + e; codes by torch's float8_e4m3fn conversion of a / 2^e."""
+    import torch
+    a = np.asarray(a, dtype=np.float32)
+    shp = a.shape
+    blk = a.reshape(shp[:-1] + (shp[-1] // block, block))
+    amax = np.abs(blk).max(axis=-1).astype(np.float64)
+    e = np.where(amax > 0, np.ceil(np.log2(np.maximum(amax, 1e-300) / E4M3_MAX)), -127.0)
+    e = np.clip(e, -127, 127)
+    q = torch.from_numpy(np.ascontiguousarray((blk / np.exp2(e)[..., None]).astype(np.float32)))
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(shp)
+    return codes, (e + 127).astype(np.uint8)
+
+
+def mx_routed(r: Routed) -> MxRouted:
+    """Block-scaled 8-bit version of a routed workload (x and W from its values)."""
+    xq, xs = quantize_mx_blocks(r.x.values)
+    Wq, ws = quantize_mx_blocks(r.W.values)
+    return MxRouted(r.name + "_mxfp8", r.T, r.K, r.N, r.E, r.k, xq, xs, Wq, ws, r.expert_ids,
+                    r.topk_weights, capacity=r.capacity)
+
+
 def grouped_as_routed(g: Grouped) -> Routed:
     """The weight-gradient stress case seen as a routed layer with k=1 and rows
     already in expert order (token r belongs to group g(r)), routing weight 1."""

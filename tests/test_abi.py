@@ -145,3 +145,16 @@ def test_gated_backward_rejects_before_launch(lib):
                                  None) == 5                                          # no workspace
     assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 16, 16, 0, P, 1 << 20,
                                  None) == 3                                          # fp32
+
+
+def test_mx_rejects_before_launch(lib):
+    P = FAKE
+    s = _lib.MoeSchedule()
+    s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
+    for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
+              "row_weight", "status"):
+        setattr(s, f, 1 << 20)
+    r = ctypes.byref(s)
+    assert lib.moe_fused_fwd_mx(P, P, P, P, r, P, 64, 8, None) == 2        # K % 128 != 0
+    assert lib.moe_fused_fwd_mx(P, None, P, P, r, P, 128, 8, None) == 1    # no x block scales
+    assert lib.moe_fused_fwd_mx(P, ctypes.c_void_p((1 << 20) + 2), P, P, r, P, 128, 8, None) == 4

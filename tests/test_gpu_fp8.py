@@ -83,3 +83,52 @@ def test_fp8_config5_decode():
     ms = O.masked_schedule(f.expert_ids, f.topk_weights, f.E, r.capacity)
     ref = O.masked_forward_fp8(f.xq, f.x_scale, f.Wq, f.w_scale, ms, f.T)
     assert_close(y, ref, "f32", "config5 fp8 y")
+
+
+# ----------------------------------------------------------------------------
+# per-block (E8M0, 32 elements) scales
+# ----------------------------------------------------------------------------
+def _run_mx(f, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
+    sch = api.moe_build_schedule(dev(f.expert_ids), dev(f.topk_weights), f.E, layout=layout,
+                                 capacity=cap)
+    y = api.moe_fused_fwd_mx(_u8(f.xq), _u8(f.x_bs), _u8(f.Wq), _u8(f.w_bs), sch)
+    torch.cuda.synchronize()
+    return sch, host(y)
+
+
+@pytest.mark.parametrize("T,K,N,E,k,empty", [
+    (333, 256, 200, 7, 2, (3,)),
+    (1030, 512, 768, 8, 2, ()),
+    (4000, 128, 520, 8, 2, ()),
+])
+def test_mx_contiguous(T, K, N, E, k, empty):
+    r = WL.routed("small_mx", T, K, N, E, k, seed=T + 5 * K)
+    if empty:
+        live = [e for e in range(E) if e not in empty]
+        rng = np.random.default_rng(T)
+        r.expert_ids = np.array([rng.choice(live, size=k, replace=False) for _ in range(T)],
+                                dtype=np.int32)
+    f = WL.mx_routed(r)
+    log(f"mx fwd T={T} K={K} N={N} E={E} k={k} empty={empty}")
+    _, y = _run_mx(f)
+    ref = O.moe_forward_mx(f.xq, f.x_bs, f.Wq, f.w_bs, f.expert_ids, f.topk_weights, E)
+    assert_close(y, ref, "f32", "y")
+
+
+@pytest.mark.parametrize("T,K,N,E,k,cap", [(128, 512, 384, 16, 4, 64), (97, 128, 136, 11, 4, 3)])
+def test_mx_masked(T, K, N, E, k, cap):
+    r = WL.routed("small_mx", T, K, N, E, k, seed=T + cap, capacity=cap)
+    f = WL.mx_routed(r)
+    log(f"mx masked T={T} K={K} N={N} E={E} k={k} cap={cap}")
+    sch, y = _run_mx(f, api.MOE_LAYOUT_MASKED, cap)
+    ms = O.masked_schedule(f.expert_ids, f.topk_weights, E, cap)
+    ref = O.masked_forward_mx(f.xq, f.x_bs, f.Wq, f.w_bs, ms, T)
+    assert_close(y, ref, "f32", "masked y")
+
+
+def test_mx_config2():
+    f = WL.mx_routed(WL.config2(with_dy=False))
+    log(f"mx fwd {f.name}")
+    _, y = _run_mx(f)
+    ref = O.moe_forward_mx(f.xq, f.x_bs, f.Wq, f.w_bs, f.expert_ids, f.topk_weights, f.E)
+    assert_close(y, ref, "f32", "config2 mx y")

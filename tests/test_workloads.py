@@ -98,3 +98,20 @@ def test_e4m3_quantization_bounds():
     assert np.allclose(np.abs(v).max(axis=1)[[0, 1, 3, 4]], 448.0)
     rel = np.abs(v * s[:, None] - a) / np.maximum(np.abs(a), 2.0 ** -6 * s[:, None])
     assert rel.max() <= 2.0 ** -4 + 1e-6
+
+
+def test_mx_quantization_bounds():
+    """Block scales are powers of two bounding each block by 448; the codes
+    times their scale stay within one E4M3 step of the values."""
+    import torch
+    rng = np.random.default_rng(6)
+    a = rng.standard_normal((4, 96)).astype(np.float32) * 10.0 ** rng.integers(-3, 3, (4, 1))
+    a[1, 32:64] = 0.0
+    q, s = W.quantize_mx_blocks(a)
+    assert q.shape == a.shape and s.shape == (4, 3) and s.dtype == np.uint8 and s[1, 1] == 0
+    v = torch.from_numpy(q).view(torch.float8_e4m3fn).float().numpy().reshape(4, 3, 32)
+    sc = np.exp2(s.astype(np.float64) - 127.0)
+    assert (np.abs(v) <= 448.0).all() and np.isfinite(v).all()
+    back = (v * sc[..., None]).reshape(4, 96)
+    blk_max = np.repeat(np.abs(a.reshape(4, 3, 32)).max(-1), 32, axis=1)
+    assert (np.abs(back - a) <= blk_max * 2.0 ** -3 + 1e-30).all()
