@@ -271,6 +271,48 @@ def fp8_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
                          "hbm_GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
                          "step_ms": round(ms_step, 4)}
         del xq, Wq, y
+    # per-32-element block scales (E8M0), same shapes
+    for name, r, lay in (("fwd_mx", WL.config2(with_dy=False), api.MOE_LAYOUT_CONTIGUOUS),
+                         ("decode_mx", WL.config5(), api.MOE_LAYOUT_MASKED)):
+        f = WL.mx_routed(r)
+
+        def u8(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        xq, xs, Wq, wsc = u8(f.xq), u8(f.x_bs), u8(f.Wq), u8(f.w_bs)
+        ids, w = u8(f.expert_ids), u8(f.topk_weights)
+        ws = torch.empty(api.moe_schedule_workspace_bytes(f.T, f.k, f.E, lay, r.capacity),
+                         dtype=torch.uint8, device=dev)
+        y = torch.empty((f.T, f.N), dtype=torch.float32, device=dev)
+
+        def step_mx():
+            sch = api.moe_build_schedule(ids, w, f.E, layout=lay, capacity=r.capacity, workspace=ws)
+            api.moe_fused_fwd_mx(xq, xs, Wq, wsc, sch, y=y)
+
+        for _ in range(warmup):
+            step_mx()
+        torch.cuda.synchronize()
+        api.moe_timing_enable(True)
+        for _ in range(steps):
+            step_mx()
+        torch.cuda.synchronize()
+        api.moe_timing_enable(False)
+        tot, n = api.moe_timing_read("fused_fwd_mx")
+        us = tot * 1e3 / max(n, 1)
+        S = f.T * f.k
+        if name == "fwd_mx":
+            tf = 2.0 * S * f.K * f.N / (us * 1e-6) / 1e12
+            out[name] = {"workload": f"{f.name} forward (block scales per 32 elements)",
+                         "fwd_us": round(us, 3), "tflops": round(tf, 2),
+                         "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4)}
+        else:
+            active = int(np.count_nonzero(np.bincount(f.expert_ids.ravel(), minlength=f.E)))
+            nbytes = active * f.N * (f.K + f.K // 32) + f.T * (f.K + f.K // 32) + f.T * f.N * 4
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[name] = {"workload": f"{f.name} forward (masked layout, block scales)",
+                         "bytes_per_launch": nbytes, "fwd_us": round(us, 3),
+                         "hbm_GBps": round(gbs, 1), "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        del xq, Wq, y
     return out
 
 
