@@ -695,6 +695,7 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
     for (int step = 0; step < (F8 ? 2 : KS); ++step) {
       using frag_t = std::conditional_t<F8, i32x8, bf16x8_t>;
       frag_t fa[MI], fb[NI];
+      uint32_t sa[Op::MX ? MI : 1], sb[Op::MX ? NI : 1];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         const int row = wm * 32 + mi * 32 * WGM + (lane & 31);
@@ -702,6 +703,7 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
           fa[mi] = frag_kmaj8(As, row, step, lane);
         else
           fa[mi] = frag_kmaj(As, row, step, lane);
+        if constexpr (Op::MX) sa[mi] = op.scale_of(buf, false, row, step, lane);
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
@@ -710,13 +712,17 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
           fb[ni] = frag_kmaj8(Bs, row, step, lane);
         else
           fb[ni] = frag_kmaj(Bs, row, step, lane);
+        if constexpr (Op::MX) sb[ni] = op.scale_of(buf, true, row, step, lane);
       }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
         if (mi >= live_mi) continue;  // wave-uniform
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
-          if constexpr (F8)
+          if constexpr (Op::MX)
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa[mi], fb[ni], acc[mi][ni], 0, 0, 0, sa[mi], 0, sb[ni]);
+          else if constexpr (F8)
             acc[mi][ni] = mfma_f8(fa[mi], fb[ni], acc[mi][ni]);
           else
             acc[mi][ni] =
@@ -781,8 +787,8 @@ struct FwdOp {
   // MX: the block scales of a stage, one 4-byte word (4 blocks of 32) per A
   // row and per B row, after the stages in LDS (A rows, then B rows)
   static constexpr int SCG = (BM + BN) / 64;           // 64-row scale groups per stage
-  static constexpr int DS = MX ? SCG / NW : 0;          // scale loads per wave per stage
-  static_assert(!MX || (SCG % NW == 0 && BM % 64 == 0), "scale groups per wave");
+  static constexpr int DS = MX ? (SCG + NW - 1) / NW : 0;  // scale loads per wave (at most)
+  static_assert(!MX || BM % 64 == 0, "whole scale groups");
   static constexpr int SC_STAGE = (BM + BN) * 4;
   static constexpr int SC_OFF = NSTAGE * STAGE;
   static constexpr int DMA_PER_STAGE = DA + DB + DS;
@@ -801,9 +807,11 @@ struct FwdOp {
     } else if (j < DA + DB) {
       db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + OPND, wid, j - DA);
     } else if constexpr (MX) {
-      const int i = j - DA - DB, grp = wid * DS + i;  // 64-row group of A rows, then B rows
-      dma4_so(grp < BM / 64 ? rsAS : rsWS, soff[i], (uint32_t)kt * 4u,
-              lds0 + (uint32_t)(SC_OFF + buf * SC_STAGE + grp * 256));
+      // 64-row group of A rows, then B rows, dealt to the waves round robin
+      const int i = j - DA - DB, grp = wid + i * NW;
+      if (grp < SCG)
+        dma4_so(grp < BM / 64 ? rsAS : rsWS, soff[i], (uint32_t)kt * 4u,
+                lds0 + (uint32_t)(SC_OFF + buf * SC_STAGE + grp * 256));
     }
   }
   // E8M0 scale of row `row` (A or B) for step `step`: the lane in half h
@@ -819,27 +827,42 @@ struct FwdOp {
 };
 
 // A (BM rows) and B (BN rows) K-major for the deep pipeline of small tiles.
-template <int BM, int BN, int NW, bool F8_ = false>
+template <int BM, int BN, int NW, bool F8_ = false, bool MX_ = false>
 struct FwdDeepOp {
-  static constexpr bool F8 = F8_, MX = false;  // as FwdOp
+  static constexpr bool F8 = F8_, MX = MX_;  // as FwdOp
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
   static_assert(DA >= 1 && DB >= 1, "at least one DMA row group per wave");
-  static constexpr int DMA_PER_STAGE = DA + DB;
-  static constexpr int A_BYTES = BM * KROW, STAGE_BYTES = (BM + BN) * KROW;
+  // MX: a stage also holds one 4-byte scale word per A row and per B row
+  // (after the B rows); the (BM + BN) / 64 groups of 64 words are dealt to the
+  // waves round robin, so a wave issues DSMAX or fewer scale loads
+  static constexpr int SCG = MX ? (BM + BN) / 64 : 0;
+  static constexpr int DSMAX = (SCG + NW - 1) / NW;
+  static_assert(!MX || (BM + BN) % 64 == 0, "whole scale groups");
+  static constexpr int DMA_PER_STAGE = DA + DB + DSMAX;
+  static constexpr int A_BYTES = BM * KROW, SC_OFF = (BM + BN) * KROW;
+  static constexpr int STAGE_BYTES = SC_OFF + (MX ? (BM + BN) * 4 : 0);
   static constexpr int NSTAGES = NSTAGE * STAGE / STAGE_BYTES > 6 ? 6 : NSTAGE * STAGE / STAGE_BYTES;
   static_assert(NSTAGES >= 2, "two stages at least");
   KmajDma<BM, NW> da;
   KmajDma<BN, NW> db;
-  __amdgpu_buffer_rsrc_t rsA, rsW;
+  __amdgpu_buffer_rsrc_t rsA, rsW, rsAS, rsWS;
   uint32_t lds0;
+  const char *ldsp;
+  uint32_t soff[DSMAX > 0 ? DSMAX : 1];  // MX: per-lane byte offset of the row's scales, or OOB
   int K, wid;
   template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)(buf * STAGE_BYTES);
-    if (j < DA)
+    if (j < DA) {
       da.template issue_one<SKIP, CHECKED>(rsA, kt, K, t, wid, j);
-    else
+    } else if (j < DA + DB) {
       db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + A_BYTES, wid, j - DA);
+    } else if constexpr (MX) {
+      const int i = j - DA - DB, grp = wid + i * NW;
+      if (grp < SCG)
+        dma4_so(grp < BM / 64 ? rsAS : rsWS, soff[i], (uint32_t)kt * 4u,
+                t + (uint32_t)(SC_OFF + grp * 256));
+    }
   }
   // DMA instructions this wave issues per stage (the others cover dead rows)
   MOE_DEV int parts() const {
@@ -848,7 +871,15 @@ struct FwdDeepOp {
     for (int i = 0; i < DA; ++i) n += (wid * DA + i) * 8 < da.live_rows ? 1 : 0;
 #pragma unroll
     for (int i = 0; i < DB; ++i) n += (wid * DB + i) * 8 < db.live_rows ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < DSMAX; ++i) n += wid + i * NW < SCG ? 1 : 0;
     return n;
+  }
+  // as FwdOp::scale_of, for the stage at `buf`
+  MOE_DEV uint32_t scale_of(int buf, bool b_side, int row, int step, int lane) const {
+    const uint32_t w = *(const uint32_t *)(ldsp + buf * STAGE_BYTES + SC_OFF +
+                                           (b_side ? BM * 4 : 0) + row * 4);
+    return (w >> (8 * (2 * step + (lane >> 5)))) & 0xffu;
   }
 };
 
@@ -862,7 +893,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   static_assert(!GATED || NI % 2 == 0, "gate and up blocks pair up inside a wave");
   static_assert(!F8 || MODE == FWD_SCATTER, "8-bit operands: the routed scatter forward");
-  static_assert(!MX || (F8 && BM == 256), "block scales: 8-bit operands, 256-row kernel");
+  static_assert(!MX || F8, "block scales: 8-bit operands");
   constexpr int NW = WGM * WGN, NTH = NW * 64;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   constexpr int ESZ = F8 ? 1 : 2;                 // bytes per operand element
@@ -954,15 +985,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       op.rsWS = uniform_rsrc(p.w_bs + (size_t)c.g * N * kblk, (uint32_t)N * kblk);
 #pragma unroll
       for (int i = 0; i < op.DS; ++i) {
-        const int grp = wid * op.DS + i;
+        const int grp = wid + i * NW;
         const int ra = grp * 64 + lane;  // tile row (A) or column (B)
+        uint32_t o = kOobOffset;
         if (grp < BM / 64) {
           const int t = tok[ra];
-          op.soff[i] = t >= 0 ? (uint32_t)t * kblk : kOobOffset;
-        } else {
+          if (t >= 0) o = (uint32_t)t * kblk;
+        } else if (grp < op.SCG) {
           const int jb = ra - BM;
-          op.soff[i] = jb < ncols ? (uint32_t)(n0 + jb) * kblk : kOobOffset;
+          if (jb < ncols) o = (uint32_t)(n0 + jb) * kblk;
         }
+        op.soff[i] = o;
       }
     }
     const bool part = BM <= 64 || ws.nS > 1 || BMr < BM;  // rows / columns partly dead
@@ -988,14 +1021,32 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         for (int ni = 0; ni < NIc; ++ni) acc[mi][ni] = f32x16{};
       if constexpr (decltype(DEEP_)::value) {
         constexpr int BMs = MIc * 32 * WGM, BNs = NIc * 32 * WGN;  // rows of A and of B
-        FwdDeepOp<BMs, BNs, NW, F8> dop;
+        FwdDeepOp<BMs, BNs, NW, F8, MX> dop;
         dop.rsA = op.rsA;
         dop.rsW = op.rsW;
         dop.lds0 = op.lds0;
+        dop.ldsp = lds;
         dop.K = K * ESZ / 2;
         dop.wid = wid;
         dop.da.setup(wid, lane, rowoff_a, c.rows);
         dop.db.setup(wid, lane, rowoff_b, GATED ? BNs : ncols);
+        if constexpr (MX) {
+          dop.rsAS = op.rsAS;
+          dop.rsWS = op.rsWS;
+#pragma unroll
+          for (int i = 0; i < dop.DSMAX; ++i) {
+            const int grp = wid + i * NW, ra = grp * 64 + lane;
+            uint32_t o = kOobOffset;
+            if (grp < BMs / 64) {
+              const int t = tok[ra];
+              if (t >= 0) o = (uint32_t)t * kblk;
+            } else if (grp < dop.SCG) {
+              const int jb = ra - BMs;
+              if (jb < ncols) o = (uint32_t)(n0 + jb) * kblk;
+            }
+            dop.soff[i] = o;
+          }
+        }
         tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi,
                                                dop.parts(), acc);
       } else {
@@ -1801,19 +1852,19 @@ hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
 
 // Routed forward-shaped launch: masked schedules of capacity <= 64 take 64-row
 // tiles (one row block per expert), everything else 256 x 256 tiles.
-template <int MODE, bool F8 = false>
+template <int MODE, bool F8 = false, bool MX = false>
 hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
   a.bstart = s.block_start;
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
-    auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8>>(kStageLds);
+    auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8, MX>;
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8, MX>>(kStageLds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
     return hipGetLastError();
   }
   a.tile_rows = forced_bm();
-  return launch_fwd256<MODE, float, F8>(a, st);
+  return launch_fwd256<MODE, float, F8, MX>(a, st);
 }
 }  // namespace
 
@@ -1854,10 +1905,7 @@ hipError_t mfma_fused_fwd_mx(const void *xq, const uint8_t *x_bs, const void *Wq
             (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T};
   a.x_bs = x_bs;
   a.w_bs = w_bs;
-  a.bstart = s.block_start;
-  // one kernel for both layouts (128-row tiles; a masked expert's slots are
-  // its rows)
-  return launch_fwd256<FWD_SCATTER, float, true, true>(a, st);
+  return launch_routed<FWD_SCATTER, true, true>(a, s, st);
 }
 
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,

@@ -132,3 +132,13 @@ def test_mx_config2():
     _, y = _run_mx(f)
     ref = O.moe_forward_mx(f.xq, f.x_bs, f.Wq, f.w_bs, f.expert_ids, f.topk_weights, f.E)
     assert_close(y, ref, "f32", "config2 mx y")
+
+
+def test_mx_config5_decode():
+    r = WL.config5()
+    f = WL.mx_routed(r)
+    log(f"mx decode {f.name}")
+    _, y = _run_mx(f, api.MOE_LAYOUT_MASKED, r.capacity)
+    ms = O.masked_schedule(f.expert_ids, f.topk_weights, f.E, r.capacity)
+    ref = O.masked_forward_mx(f.xq, f.x_bs, f.Wq, f.w_bs, ms, f.T)
+    assert_close(y, ref, "f32", "config5 mx y")
