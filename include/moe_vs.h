@@ -251,7 +251,7 @@ size_t moe_gated_ffn_bwd_workspace_bytes(const moe_schedule *sched, int64_t F);
  *   d_topk[t, j] = dY[t] . (h[r] W_down[e]^T), the unweighted down output.
  *   dY [T, N], x [T, K], W_gu [E, 2F, K], W_down [E, N, F] and h [R, F]
  *   bf16, gu [R, 2F] float (h and gu saved by the forward with the same
- *   schedule); all 16-byte aligned.  dX [T, K] float, dW_gu [E, 2F, K] and dW_down [E, N, F] bf16,
+ *   schedule); all 16-byte aligned, as are dW_gu and dW_down.  dX [T, K] float, dW_gu [E, 2F, K] and dW_down [E, N, F] bf16,
  *   d_topk [T, k] float: each OVERWRITTEN, or NULL to skip.
  *   workspace: moe_gated_ffn_bwd_workspace_bytes(sched, F) bytes, 256-byte
  *   aligned (required when dX or dW_gu is asked for).
@@ -283,7 +283,8 @@ size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64
  *                  unweighted per-assignment product.
  *   dY [T, N], x [T, K], W [E, N, K] in `dtype`.
  *   dX [T, K] float or NULL (skip); OVERWRITTEN.
- *   dW [E, N, K] in `dtype` or NULL (skip); OVERWRITTEN.
+ *   dW [E, N, K] in `dtype` or NULL (skip); OVERWRITTEN; 16-byte aligned for
+ *   bf16 (4-byte for fp32).
  *   d_topk [T, k] float or NULL (skip); OVERWRITTEN.  Rows of empty masked
  *   slots contribute nothing; dropped assignments get 0.
  *   W may be NULL only when dX and d_topk are both NULL.

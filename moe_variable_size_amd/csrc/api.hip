@@ -370,7 +370,7 @@ int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const voi
   if (need_dgu && (!workspace || workspace_bytes < ws_need)) return MOE_ERR_WORKSPACE;
   if (!aligned(dY, 16) || !aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) ||
       !aligned(gu, 16) || !aligned(h, 16) || (dX && !aligned(dX, 4)) ||
-      (dW_gu && !aligned(dW_gu, 2)) || (dW_down && !aligned(dW_down, 2)) ||
+      (dW_gu && !aligned(dW_gu, 16)) || (dW_down && !aligned(dW_down, 16)) ||
       (d_topk && !aligned(d_topk, 4)) || (workspace && !aligned(workspace, 256)))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
@@ -429,7 +429,7 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
     return MOE_ERR_LIMIT;
   const size_t al = dtype == MOE_BF16 ? 16 : 4;
   if (!aligned(dY, al) || !aligned(x, al) || (W && !aligned(W, al)) || (dX && !aligned(dX, 4)) ||
-      (dW && !aligned(dW, esize(dtype))) || (d_topk && !aligned(d_topk, 4)))
+      (dW && !aligned(dW, dtype == MOE_BF16 ? 16 : 4)) || (d_topk && !aligned(d_topk, 4)))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   const bool mfma = dtype == MOE_BF16 && mfma_supported((int)K, (int)N);

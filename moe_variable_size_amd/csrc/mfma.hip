@@ -1713,25 +1713,32 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
       op.fill_ring(p.row_to_token, 0, KI < 2 ? KI : 2);
       tile_multiply<MI, NI, WGM, WGN, false>(op, lds, 0, KI, wm, wn, lane, MI, NI, acc);
     }
-    // store (exact zeros for an empty expert)
-    Tout *out = (Tout *)p.dW + (size_t)e * N * K;
+    // store (exact zeros for an empty expert): the bf16 tile goes through the
+    // (now idle) LDS stages, 256 x 256 row-major, and out with 16-byte row-
+    // contiguous stores (a 16-byte chunk is 8 columns; K is a multiple of 8)
+    static_assert(sizeof(Tout) == 2, "bf16 weight gradient");
+    __syncthreads();  // every wave done reading the last stage
+    __bf16 *const stile = (__bf16 *)lds;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int col = kc0 + wn * 32 + ni * 32 * WGN + (lane & 31);
-        if (col >= K) continue;
+        const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int n = n0 + wm * 32 + mi * 32 * WGM + acc_row(i, lane);
-          if (n >= N) continue;
-          if (sizeof(Tout) == 4)
-            ((float *)out)[(size_t)n * K + col] = acc[mi][ni][i];
-          else
-            ((__bf16 *)out)[(size_t)n * K + col] = (__bf16)acc[mi][ni][i];
+          const int rl = wm * 32 + mi * 32 * WGM + acc_row(i, lane);
+          stile[rl * BN + cl] = (__bf16)acc[mi][ni][i];
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    Tout *const out = (Tout *)p.dW + (size_t)e * N * K;
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    for (int c = tid; c < BM * (BN / 8); c += NW * 64) {
+      const int rl = c / (BN / 8), cc = (c % (BN / 8)) * 8;
+      const int n = n0 + rl, col = kc0 + cc;
+      if (n < N && col < K)
+        *(u32x4_t *)(out + (size_t)n * K + col) = *(const u32x4_t *)(stile + rl * BN + cc);
     }
   }
 }
