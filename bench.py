@@ -17,8 +17,8 @@ GB/s), "fp8" (the 8-bit forward on the config-2 shape and the masked decode)
 and "gated_ffn" (gated expert FFN forward and backward on the balanced step
 of the page's worked example, TFLOP/s).
 
-Prints ONE JSON line.  --gpus above 1 is not supported (one GPU per process,
-single-GPU machine) and exits with a message.
+Prints ONE JSON line.  --gpus above 1 is not supported (this path runs on one
+GPU) and exits with a message.
 """
 from __future__ import annotations
 
