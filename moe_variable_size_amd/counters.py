@@ -29,8 +29,8 @@ KERNEL_SOURCES = ("moe_variable_size_amd/csrc/mfma.hip", "moe_variable_size_amd/
                   "moe_variable_size_amd/csrc/api.hip")
 COPY_BYTES = 256 << 20   # bench.py --calib-copy: 64 Mi float32 copied device to device
 
-# forward-shaped kernels: mfma_fwd_kernel<BM, BN, WGM, WGN, MODE, Tout, F8>
-_FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+), (true|false)>")
+# forward-shaped kernels: mfma_fwd_kernel<BM, BN, WGM, WGN, MODE, Tout, F8, MX>
+_FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+), (true|false), (true|false)>")
 FWD_MODES = {0: "grouped_gemm", 1: "fused_fwd", 2: "gated_up", 3: "gated_down"}
 # input-gradient kernels: mfma_dx_kernel<NW, GB, ROWS>; weight gradient: mfma_dw_kernel<Tout, NW, RM>
 _DX = re.compile(r"mfma_dx_kernel<(\d+), (true|false), (true|false)>")
@@ -52,13 +52,14 @@ def _family(name: str):
         return "copy"
     m = _FWD.search(name)
     if m:
-        bm, mode, f8 = int(m.group(1)), int(m.group(5)), m.group(7) == "true"
+        bm, mode = int(m.group(1)), int(m.group(5))
+        f8, mx = m.group(7) == "true", m.group(8) == "true"
         fam = FWD_MODES.get(mode)
         if fam is None:
             return None
         if fam == "fused_fwd" and bm == 64:
             fam = "decode_fwd"
-        return fam + "_fp8" if f8 else fam
+        return fam + "_mx" if mx else fam + "_fp8" if f8 else fam
     m = _DX.search(name)
     if m:
         gb, rows = m.group(2) == "true", m.group(3) == "true"

@@ -5,13 +5,15 @@ from moe_variable_size_amd import counters as C
 def test_families_of_demangled_names():
     ns = "moe::(anonymous namespace)::"
     f = lambda t: C._family(ns + t + "(moe::(anonymous namespace)::FwdArgs)")
-    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, false>") == "fused_fwd"
-    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, false>") == "decode_fwd"
-    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, true>") == "fused_fwd_fp8"
-    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, true>") == "decode_fwd_fp8"
-    assert f("mfma_fwd_kernel<256, 256, 2, 4, 2, float, false>") == "gated_up"
-    assert f("mfma_fwd_kernel<256, 256, 2, 4, 3, float, false>") == "gated_down"
-    assert f("mfma_fwd_kernel<256, 256, 2, 4, 0, unsigned short, false>") == "grouped_gemm"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, false, false>") == "fused_fwd"
+    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, false, false>") == "decode_fwd"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, true, false>") == "fused_fwd_fp8"
+    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, true, false>") == "decode_fwd_fp8"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 2, float, false, false>") == "gated_up"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 3, float, false, false>") == "gated_down"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 0, unsigned short, false, false>") == "grouped_gemm"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, true, true>") == "fused_fwd_mx"
+    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, true, true>") == "decode_fwd_mx"
     assert C._family(ns + "mfma_dx_kernel<4, false, false>(moe::(anonymous namespace)::DxArgs)") == "bwd_dx"
     assert C._family(ns + "mfma_dx_kernel<4, true, false>(DxArgs)") == "gated_bwd_dh"
     assert C._family(ns + "mfma_dx_kernel<4, false, true>(DxArgs)") == "gated_bwd_dx"
