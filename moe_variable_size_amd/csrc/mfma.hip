@@ -47,6 +47,7 @@
 #include "common.hpp"
 
 #include <type_traits>
+#include <utility>
 
 namespace moe {
 namespace {
@@ -145,6 +146,18 @@ MOE_DEV void barrier() {
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
+}
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in sequence:
+// a loop that is unrolled whatever its body's size, so that register arrays
+// indexed by its counter stay in registers
+template <class F, int... I>
+MOE_DEV void unroll_seq(F &&f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+template <int N, class F>
+MOE_DEV void unroll(F &&f) {
+  unroll_seq(f, std::make_integer_sequence<int, N>());
 }
 
 // Buffer resource built from wave-uniform values (scalar registers), as the
@@ -1399,14 +1412,24 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       // dX scatter: atomics with 32-bit byte offsets from the base of dX, on
       // live rows and columns only
       char *const xb = (char *)p.dX;
+      // GB: gate / up and dgu addressed by 32-bit byte offsets from the tile's
+      // first row; an offset past the tile's rows reads zero and drops the store
+      const __amdgpu_buffer_rsrc_t rsG =
+          uniform_rsrc(GB ? p.gu + (size_t)c.row0 * 2 * K : nullptr, GB ? (uint32_t)c.rows * (uint32_t)K * 8u : 0u);
+      const __amdgpu_buffer_rsrc_t rsD =
+          uniform_rsrc(GB ? p.dgu + (size_t)c.row0 * 2 * K : nullptr, GB ? (uint32_t)c.rows * (uint32_t)K * 4u : 0u);
+      const uint32_t gcol = (uint32_t)(kc0 + wn * 32 + (lane & 31));
       uint32_t cb[NIc];
 #pragma unroll
       for (int ni = 0; ni < NIc; ++ni)
         cb[ni] = (uint32_t)(kc0 + wn * 32 + ni * 32 * WGN + (lane & 31)) * 4u;
-#pragma unroll
-      for (int mi = 0; mi < MIc; ++mi) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      // mi and j unrolled by construction: with the gated arithmetic the body
+      // is past the compiler's unrolling limit, and a rolled loop would index
+      // the accumulators at run time, which moves them to scratch memory
+      unroll<MIc>([&](auto mi_) __attribute__((always_inline)) {
+        constexpr int mi = decltype(mi_)::value;
+        unroll<4>([&](auto j_) __attribute__((always_inline)) {
+          constexpr int j = decltype(j_)::value;
           const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
           const i32x4 t4 = *(const i32x4 *)(tok + rq);
           const f32x4 w4 = *(const f32x4 *)(wgt + rq);
@@ -1428,20 +1451,27 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) ro[q] = (uint32_t)t4[q] * (uint32_t)K * 4u;
           // GB: the saved gate / up values of this lane's 4 rows x NIc columns,
-          // all loads issued together (dead elements read element 0, a valid
-          // address, and are not used)
+          // all loads issued together; per row one offset, the columns of
+          // the NIc blocks in the instruction's immediate offset and the up
+          // half in its scalar offset (dead columns read a neighbour, unused)
           float gvs[GB ? NIc : 1][4], uvs[GB ? NIc : 1][4];
+          uint32_t go[4], gd[4];
           if constexpr (GB) {
             if (p.dgu) {
 #pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const uint32_t r = (uint32_t)(rq + q) * (uint32_t)K * 2u + gcol;
+                go[q] = t4[q] >= 0 ? r * 4u : kOobOffset;
+                gd[q] = t4[q] >= 0 ? r * 2u : kOobOffset;
+              }
+#pragma unroll
               for (int ni = 0; ni < NIc; ++ni) {
-                const int cl = wn * 32 + ni * 32 * WGN + (lane & 31);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                  const bool live = t4[q] >= 0 && cl < ncols;
-                  const size_t gi = live ? (size_t)(c.row0 + rq + q) * (2 * K) + kc0 + cl : 0;
-                  gvs[ni][q] = p.gu[gi];
-                  uvs[ni][q] = p.gu[gi + (live ? K : 0)];
+                  gvs[ni][q] = __builtin_bit_cast(
+                      float, __builtin_amdgcn_raw_buffer_load_b32(rsG, go[q] + ni * 128 * WGN, 0, 0));
+                  uvs[ni][q] = __builtin_bit_cast(
+                      float, __builtin_amdgcn_raw_buffer_load_b32(rsG, go[q] + ni * 128 * WGN, K * 4, 0));
                 }
               }
             }
@@ -1454,13 +1484,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
             for (int q = 0; q < 4; ++q) {
               const float g = cok ? acc[mi][ni][4 * j + q] : 0.f;  // dead columns may hold stale values
               if constexpr (GB) {
-                if (p.dgu && t4[q] >= 0 && cok) {
-                  const size_t gi = (size_t)(c.row0 + rq + q) * (2 * K) + kc0 + cl;
+                if (p.dgu) {  // dead rows and columns store out of range
+                  const uint32_t so = cok ? gd[q] + ni * 64 * WGN : kOobOffset;
                   const float gv = gvs[ni][q], uv = uvs[ni][q];
                   const float sg = 1.f / (1.f + __expf(-gv));
                   const float dh = w4[q] * g;
-                  p.dgu[gi] = f32_to_bf16(dh * uv * sg * (1.f + gv * (1.f - sg)));
-                  p.dgu[gi + K] = f32_to_bf16(dh * gv * sg);
+                  __builtin_amdgcn_raw_buffer_store_b16(
+                      f32_to_bf16(dh * uv * sg * (1.f + gv * (1.f - sg))), rsD, so, 0, 0);
+                  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dh * gv * sg), rsD, so, K * 2, 0);
                 }
               } else if (has_dx && t4[q] >= 0 && cok) {
                 unsafeAtomicAdd((float *)(xb + (ro[q] + cb[ni])), w4[q] * g);
@@ -1484,9 +1515,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
                 if (t4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], dwp[q]);
             }
           }
-        }
+        });
         __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     };
     using std::integral_constant;
     // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
