@@ -1413,11 +1413,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       // live rows and columns only
       char *const xb = (char *)p.dX;
       // GB: gate / up and dgu addressed by 32-bit byte offsets from the tile's
-      // first row; an offset past the tile's rows reads zero and drops the store
+      // first row
+      const uint32_t grows = GB ? (uint32_t)c.rows * (uint32_t)K : 0u;
       const __amdgpu_buffer_rsrc_t rsG =
-          uniform_rsrc(GB ? p.gu + (size_t)c.row0 * 2 * K : nullptr, GB ? (uint32_t)c.rows * (uint32_t)K * 8u : 0u);
+          uniform_rsrc(GB ? p.gu + (size_t)c.row0 * 2 * K : nullptr, grows * 8u);
       const __amdgpu_buffer_rsrc_t rsD =
-          uniform_rsrc(GB ? p.dgu + (size_t)c.row0 * 2 * K : nullptr, GB ? (uint32_t)c.rows * (uint32_t)K * 4u : 0u);
+          uniform_rsrc(GB ? p.dgu + (size_t)c.row0 * 2 * K : nullptr, grows * 4u);
       const uint32_t gcol = (uint32_t)(kc0 + wn * 32 + (lane & 31));
       uint32_t cb[NIc];
 #pragma unroll
@@ -1451,9 +1452,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) ro[q] = (uint32_t)t4[q] * (uint32_t)K * 4u;
           // GB: the saved gate / up values of this lane's 4 rows x NIc columns,
-          // all loads issued together; per row one offset, the columns of
-          // the NIc blocks in the instruction's immediate offset and the up
-          // half in its scalar offset (dead columns read a neighbour, unused)
+          // all loads issued together; per row one gate and one up offset (both
+          // range-checked: a dead row reads zero, a dead column a neighbour or
+          // zero, and neither is used), the column blocks in the immediate
           float gvs[GB ? NIc : 1][4], uvs[GB ? NIc : 1][4];
           uint32_t go[4], gd[4];
           if constexpr (GB) {
@@ -1462,7 +1463,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
               for (int q = 0; q < 4; ++q) {
                 const uint32_t r = (uint32_t)(rq + q) * (uint32_t)K * 2u + gcol;
                 go[q] = t4[q] >= 0 ? r * 4u : kOobOffset;
-                gd[q] = t4[q] >= 0 ? r * 2u : kOobOffset;
+                gd[q] = r * 2u;
               }
 #pragma unroll
               for (int ni = 0; ni < NIc; ++ni) {
@@ -1471,7 +1472,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
                   gvs[ni][q] = __builtin_bit_cast(
                       float, __builtin_amdgcn_raw_buffer_load_b32(rsG, go[q] + ni * 128 * WGN, 0, 0));
                   uvs[ni][q] = __builtin_bit_cast(
-                      float, __builtin_amdgcn_raw_buffer_load_b32(rsG, go[q] + ni * 128 * WGN, K * 4, 0));
+                      float, __builtin_amdgcn_raw_buffer_load_b32(
+                                 rsG, go[q] + (uint32_t)K * 4u + ni * 128 * WGN, 0, 0));
                 }
               }
             }
@@ -1484,8 +1486,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
             for (int q = 0; q < 4; ++q) {
               const float g = cok ? acc[mi][ni][4 * j + q] : 0.f;  // dead columns may hold stale values
               if constexpr (GB) {
-                if (p.dgu) {  // dead rows and columns store out of range
-                  const uint32_t so = cok ? gd[q] + ni * 64 * WGN : kOobOffset;
+                if (p.dgu && t4[q] >= 0 && cok) {
+                  const uint32_t so = gd[q] + ni * 64 * WGN;
                   const float gv = gvs[ni][q], uv = uvs[ni][q];
                   const float sg = 1.f / (1.f + __expf(-gv));
                   const float dh = w4[q] * g;
