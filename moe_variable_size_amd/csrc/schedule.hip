@@ -4,24 +4,26 @@
 // [CARD] = "grouped-gemm-moe" model card
 // [NOTE] = "Grouped GEMM" study notes (scholia-log)
 //
-// Three launches, no host readback ([GG] "Problem descriptors and the tile
+// Two launches, no host readback ([GG] "Problem descriptors and the tile
 // scheduler": group sizes stay on the device; "Failure modes": no host sync).
 // The assignments s = 0 .. S-1 are cut into nblk blocks of B consecutive ids.
 //   1. hist  (nblk workgroups): per-block count of each expert id
 //      (bincount, [GG] "Data layout, offsets and alignment") and of ids
 //      outside [0, E);
-//   2. scan  (one workgroup): the block x expert table is brought into LDS and
-//      each expert's column turned into exclusive block bases; per-expert
-//      counts, int32 END offsets (inclusive prefix), the row-block prefix for
-//      each tile height (tile counts and their exclusive prefix, [GG] "Problem
-//      descriptors and the tile scheduler"), experts ordered by load, status,
-//      and the rows no assignment fills;
-//   3. place (nblk workgroups): a stable counting sort inside each block: every
-//      wave counts its range per expert, takes its base from the block base
-//      and the waves before it, then walks its range in order and places each
-//      assignment at (base + rank among equal ids earlier in the same 64-wide
-//      chunk), giving row -> assignment, row -> token and the per-row routing
-//      weight ([CARD] "How it works"; [NOTE] 4.1).
+//   2. place (nblk workgroups): every workgroup sums the block x expert table
+//      itself: its own block's base inside each expert (the counts of the
+//      blocks before it) and each expert's total, whose exclusive prefix gives
+//      the expert's first row.  Four workgroups also write, one job each, the
+//      per-expert counts with the int32 END offsets (inclusive prefix) and the
+//      status; the row-block prefix for each tile height (tile counts and their
+//      exclusive prefix, [GG] "Problem descriptors and the tile scheduler");
+//      the experts ordered by load; the rows no assignment fills.  Then a
+//      stable counting sort inside
+//      each block: every wave counts its range per expert, takes its base from
+//      the block base and the waves before it, then walks its range in order
+//      and places each assignment at (base + rank among equal ids earlier in
+//      the same 64-wide chunk), giving row -> assignment, row -> token and the
+//      per-row routing weight ([CARD] "How it works"; [NOTE] 4.1).
 // Equal ids inside a chunk are matched with one ballot per id bit, so ranks do
 // not depend on the order in which hardware executes atomics: the result is
 // deterministic and equals a stable argsort by expert.
@@ -31,17 +33,16 @@ namespace moe {
 
 namespace {
 
-constexpr int kScanThreads = 1024;
 constexpr int kBlkThreads = 256;  // hist / place workgroups: 4 waves
 constexpr int kBlkWaves = kBlkThreads / kWave;
-constexpr int kTableInts = 16384;  // block x expert table held in LDS by the scan
+constexpr int kTableInts = 16384;  // bound on the block x expert table
 
 MOE_DEV uint64_t ballot(bool p) { return __ballot(p); }
 
-// Exclusive prefix sum over a 1024-thread block of one int per thread.
-// `scratch` holds kScanThreads/64 + 1 ints.  Returns the prefix; *total gets the sum.
+// Exclusive prefix sum over the workgroup's kBlkThreads threads, one int each.
+// `scratch` holds kBlkWaves + 1 ints.  Returns the prefix; *total gets the sum.
 MOE_DEV int block_exclusive_scan(int v, int *scratch, int *total) {
-  constexpr int kWaves = kScanThreads / kWave;
+  constexpr int kWaves = kBlkWaves;
   const int lane = threadIdx.x & (kWave - 1);
   const int wid = threadIdx.x / kWave;
   int inc = v;
@@ -116,79 +117,109 @@ __global__ __launch_bounds__(kBlkThreads) void sched_hist_kernel(
   if (tid == 0) invalid_per_block[b] = hist[E];
 }
 
-// ---- 2. scan ------------------------------------------------------------------
-__global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(
-    int32_t *__restrict__ table, const int32_t *__restrict__ invalid_per_block, int nblk, int E,
-    int layout, int capacity, int R, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ block_start, int32_t *__restrict__ expert_order,
-    int32_t *__restrict__ rowbase_out, int32_t *__restrict__ row_to_assign,
+// Exclusive prefix over experts of val[0 .. E-1] (LDS) into out[] (LDS), each
+// thread summing a run of consecutive experts; returns the total.
+MOE_DEV int scan_experts(const int *val, int *out, int E, int *scratch) {
+  const int chunk = (E + kBlkThreads - 1) / kBlkThreads;
+  const int e0 = min(E, (int)threadIdx.x * chunk), e1 = min(E, e0 + chunk);
+  int sum = 0;
+  for (int e = e0; e < e1; ++e) sum += val[e];
+  int total;
+  int pre = block_exclusive_scan(sum, scratch, &total);
+  for (int e = e0; e < e1; ++e) {
+    out[e] = pre;
+    pre += val[e];
+  }
+  __syncthreads();
+  return total;
+}
+
+// ---- 2. bases, per-expert outputs, stable placement ----------------------------
+__global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
+    const int32_t *__restrict__ ids, const float *__restrict__ w, int S, int k, int E, int B,
+    int nblk, int layout, int capacity, int R, const int32_t *__restrict__ table,
+    const int32_t *__restrict__ invalid_per_block, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ block_start,
+    int32_t *__restrict__ expert_order, int32_t *__restrict__ row_to_assign,
     int32_t *__restrict__ row_to_token, float *__restrict__ row_weight,
     int32_t *__restrict__ status) {
   extern __shared__ int smem[];
-  int *tab = smem;                      // [nblk * E]
-  int *cnt = tab + nblk * E;            // [E]: valid rows per expert
-  int *scratch = cnt + E;               // [kScanThreads / 64 + 1]
-  int *tally = scratch + kScanThreads / kWave + 1;  // [2]
-  const int tid = threadIdx.x;
-  const int n = nblk * E;
-  for (int i = tid; i < n; i += kScanThreads) tab[i] = table[i];
+  int *hist = smem;                     // [kBlkWaves][E]: per-wave counts, then running bases
+  int *base = hist + kBlkWaves * E;     // [E] this block's base inside each expert
+  int *cnt = base + E;                  // [E] valid rows per expert
+  int *rowbase = cnt + E;               // [E] first row of each expert
+  int *tmp = rowbase + E;               // [2][E] workgroup 0: tile counts and their prefix
+  int *scratch = tmp + 2 * E;           // [kBlkWaves + 1]
+  int *tally = scratch + kBlkWaves + 1; // [2] invalid ids, assignments over capacity
+  const int tid = threadIdx.x, b = blockIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const bool masked = layout == MOE_LAYOUT_MASKED;
+  for (int i = tid; i < kBlkWaves * E; i += kBlkThreads) hist[i] = 0;
   if (tid < 2) tally[tid] = 0;
   __syncthreads();
-  int inv = 0;
-  for (int i = tid; i < nblk; i += kScanThreads) inv += invalid_per_block[i];
-  if (inv) atomicAdd(&tally[0], inv);
-
-  const bool masked = layout == MOE_LAYOUT_MASKED;
-  static_assert(kMaxExperts <= kScanThreads, "one expert per scan thread");
-  {
-    const int e = tid;
-    int m_e = 0;
-    if (e < E) {
-      for (int b = 0; b < nblk; ++b) {  // exclusive block bases inside the expert
-        const int c = tab[b * E + e];
-        tab[b * E + e] = m_e;
-        m_e += c;
-      }
+  // the table's column sums: this block's base and each expert's total
+  for (int e = tid; e < E; e += kBlkThreads) {
+    int before = 0, m_e = 0;
+    for (int bb = 0; bb < nblk; ++bb) {
+      const int c = table[(size_t)bb * E + e];
+      before += bb < b ? c : 0;
+      m_e += c;
     }
-    const int valid_rows = (e < E) ? (masked ? min(m_e, capacity) : m_e) : 0;
-    if (masked && e < E && m_e > capacity) atomicAdd(&tally[1], m_e - capacity);
-    int total;
-    const int start = block_exclusive_scan(valid_rows, scratch, &total);
-    if (e < E) {
-      counts[e] = valid_rows;
-      offsets[e] = start + valid_rows;
-      rowbase_out[e] = masked ? e * capacity : start;
-      cnt[e] = valid_rows;
+    base[e] = before;
+    cnt[e] = masked ? min(m_e, capacity) : m_e;
+    if (b == 0 && masked && m_e > capacity) atomicAdd(&tally[1], m_e - capacity);
+  }
+  __syncthreads();
+  // packed prefix of the valid counts: END offsets in both layouts, first rows
+  // in the contiguous one (the masked layout starts expert e at e * capacity)
+  const int total = scan_experts(cnt, rowbase, E, scratch);
+  for (int e = tid; e < E; e += kBlkThreads) {
+    if (b == 0) {
+      counts[e] = cnt[e];
+      offsets[e] = rowbase[e] + cnt[e];
     }
+    if (masked) rowbase[e] = e * capacity;
+  }
+  // the per-expert outputs, one job per workgroup (workgroup j % nblk takes
+  // job j), each on the counts every workgroup has summed
+  if (b == 1 % nblk) {
 #pragma unroll
     for (int i = 0; i < MOE_NUM_BM; ++i) {
       const int bm = 32 << i;
-      const int nb = (e < E) ? (masked ? (capacity + bm - 1) / bm : (valid_rows + bm - 1) / bm) : 0;
-      int tot;
-      const int pre = block_exclusive_scan(nb, scratch, &tot);
-      if (e < E) block_start[i * (E + 1) + e] = pre;
+      for (int e = tid; e < E; e += kBlkThreads)
+        tmp[e] = masked ? (capacity + bm - 1) / bm : (cnt[e] + bm - 1) / bm;
+      __syncthreads();
+      const int tot = scan_experts(tmp, tmp + E, E, scratch);
+      for (int e = tid; e < E; e += kBlkThreads) block_start[i * (E + 1) + e] = tmp[E + e];
       if (tid == 0) block_start[i * (E + 1) + E] = tot;
+      __syncthreads();
     }
-    __syncthreads();  // cnt[] and tab[] complete
+  }
+  if (b == 2 % nblk) {
     // experts by descending row count, ties by id
-    if (e < E) {
+    for (int e = tid; e < E; e += kBlkThreads) {
+      const int c = cnt[e];
       int rank = 0;
       for (int o = 0; o < E; ++o) {
-        const int c = cnt[o];
-        rank += (c > valid_rows || (c == valid_rows && o < e)) ? 1 : 0;
+        const int co = cnt[o];
+        rank += (co > c || (co == c && o < e)) ? 1 : 0;
       }
       expert_order[rank] = e;
     }
+  }
+  if (b == 3 % nblk) {
     // rows no assignment fills: past the last valid row (contiguous) or past
     // each expert's valid prefix (masked)
     if (!masked) {
-      for (int r = total + tid; r < R; r += kScanThreads) {
+      for (int r = total + tid; r < R; r += kBlkThreads) {
         row_to_assign[r] = -1;
         row_to_token[r] = -1;
         row_weight[r] = 0.f;
       }
     } else {
-      for (int r = tid; r < R; r += kScanThreads) {
+      for (int r = tid; r < R; r += kBlkThreads) {
         const int ex = r / capacity;
         if (r - ex * capacity >= cnt[ex]) {
           row_to_assign[r] = -1;
@@ -198,28 +229,16 @@ __global__ __launch_bounds__(kScanThreads) void sched_scan_kernel(
       }
     }
   }
-  for (int i = tid; i < n; i += kScanThreads) table[i] = tab[i];
-  __syncthreads();
-  if (tid == 0) {
-    status[0] = tally[0];
-    status[1] = tally[1];
+  if (b == 0) {
+    int inv = 0;
+    for (int i = tid; i < nblk; i += kBlkThreads) inv += invalid_per_block[i];
+    if (inv) atomicAdd(&tally[0], inv);
+    __syncthreads();
+    if (tid == 0) {
+      status[0] = tally[0];
+      status[1] = tally[1];
+    }
   }
-}
-
-// ---- 3. stable placement inside each block -------------------------------------
-__global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
-    const int32_t *__restrict__ ids, const float *__restrict__ w, int S, int k, int E, int B,
-    int layout, int capacity, const int32_t *__restrict__ table,
-    const int32_t *__restrict__ rowbase, int32_t *__restrict__ row_to_assign,
-    int32_t *__restrict__ row_to_token, float *__restrict__ row_weight) {
-  extern __shared__ int hist[];  // [kBlkWaves][E]: per-wave counts, then running bases
-  const int tid = threadIdx.x, b = blockIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  const bool masked = layout == MOE_LAYOUT_MASKED;
-  for (int i = tid; i < kBlkWaves * E; i += kBlkThreads) hist[i] = 0;
-  __syncthreads();
   const BlockRange rg = wave_range(b, B, S, wid);
   for (int s = rg.begin + lane; s < rg.end; s += kWave) {
     const int id = ids[s];
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
   __syncthreads();
   // per-wave base = rank base of this block inside the expert + earlier waves
   for (int e = tid; e < E; e += kBlkThreads) {
-    int run = table[(size_t)b * E + e];
+    int run = base[e];
     for (int v = 0; v < kBlkWaves; ++v) {
       const int c = hist[v * E + e];
       hist[v * E + e] = run;
@@ -326,29 +345,19 @@ hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_s
   const int B = schedule_block(S, E), nblk = schedule_blocks(S, E);
   int32_t *table = scratch;                          // [nblk * E]
   int32_t *inv = table + (size_t)nblk * E;           // [nblk]
-  int32_t *rowbase = inv + nblk;                     // [E]
   hipLaunchKernelGGL(sched_hist_kernel, dim3(nblk), dim3(kBlkThreads), sizeof(int) * (E + 1), st,
                      ids, S, E, B, table, inv);
-  const size_t scan_smem =
-      sizeof(int) * ((size_t)nblk * E + E + kScanThreads / kWave + 1 + 2);
-  if (scan_smem > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void *)sched_scan_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)scan_smem);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(sched_scan_kernel, dim3(1), dim3(kScanThreads), scan_smem, st, table, inv,
-                     nblk, E, s.layout, s.capacity, (int)s.R, s.counts, s.offsets, s.block_start,
-                     s.expert_order, rowbase, s.row_to_assign, s.row_to_token, s.row_weight,
-                     s.status);
-  hipLaunchKernelGGL(sched_place_kernel, dim3(nblk), dim3(kBlkThreads),
-                     sizeof(int) * kBlkWaves * E, st, ids, w, S, s.k, E, B, s.layout, s.capacity,
-                     table, rowbase, s.row_to_assign, s.row_to_token, s.row_weight);
+  const size_t place_smem = sizeof(int) * ((size_t)(kBlkWaves + 5) * E + kBlkWaves + 1 + 2);
+  hipLaunchKernelGGL(sched_place_kernel, dim3(nblk), dim3(kBlkThreads), place_smem, st, ids, w, S,
+                     s.k, E, B, nblk, s.layout, s.capacity, (int)s.R, table, inv, s.counts,
+                     s.offsets, s.block_start, s.expert_order, s.row_to_assign, s.row_to_token,
+                     s.row_weight, s.status);
   return hipGetLastError();
 }
 
 size_t schedule_scratch_bytes(int64_t S, int E) {
   const int nblk = schedule_blocks(S, E);
-  return sizeof(int32_t) * ((size_t)nblk * E + nblk + E);
+  return sizeof(int32_t) * ((size_t)nblk * E + nblk);
 }
 
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,
