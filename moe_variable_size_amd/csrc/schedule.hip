@@ -156,16 +156,36 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
   const bool masked = layout == MOE_LAYOUT_MASKED;
+  // this wave's first kBatch x 64 ids and weights, loaded before anything
+  // else so their latency overlaps the table sums (with B = 1024 that is the
+  // wave's whole range)
+  constexpr int kBatch = 4;
+  const BlockRange rg = wave_range(b, B, S, wid);
+  int idv0[kBatch];
+  float wv0[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int s = rg.begin + u * kWave + lane;
+    idv0[u] = s < rg.end ? ids[s] : -1;
+    wv0[u] = (s < rg.end && w) ? w[s] : 1.f;
+  }
+  const bool one_batch = rg.end - rg.begin <= kBatch * kWave;  // wave-uniform
   for (int i = tid; i < kBlkWaves * E; i += kBlkThreads) hist[i] = 0;
   if (tid < 2) tally[tid] = 0;
   __syncthreads();
   // the table's column sums: this block's base and each expert's total
   for (int e = tid; e < E; e += kBlkThreads) {
     int before = 0, m_e = 0;
-    for (int bb = 0; bb < nblk; ++bb) {
-      const int c = table[(size_t)bb * E + e];
-      before += bb < b ? c : 0;
-      m_e += c;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)  // eight loads in flight, then the sums
+        c[u] = b0 + u < nblk ? table[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        before += b0 + u < b ? c[u] : 0;
+        m_e += c[u];
+      }
     }
     base[e] = before;
     cnt[e] = masked ? min(m_e, capacity) : m_e;
@@ -239,10 +259,15 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
       status[1] = tally[1];
     }
   }
-  const BlockRange rg = wave_range(b, B, S, wid);
-  for (int s = rg.begin + lane; s < rg.end; s += kWave) {
-    const int id = ids[s];
-    if (id >= 0 && id < E) atomicAdd(&hist[wid * E + id], 1);
+  if (one_batch) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u)
+      if (idv0[u] >= 0 && idv0[u] < E) atomicAdd(&hist[wid * E + idv0[u]], 1);
+  } else {
+    for (int s = rg.begin + lane; s < rg.end; s += kWave) {
+      const int id = ids[s];
+      if (id >= 0 && id < E) atomicAdd(&hist[wid * E + id], 1);
+    }
   }
   __syncthreads();
   // per-wave base = rank base of this block inside the expert + earlier waves
@@ -258,15 +283,22 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
 
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
-  constexpr int kBatch = 4;
   for (int b0 = rg.begin; b0 < rg.end; b0 += kBatch * kWave) {
     int idv[kBatch];
     float wv[kBatch];
+    if (b0 == rg.begin) {  // wave-uniform: the preloaded batch
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {  // all loads of the batch before any use
-      const int s = b0 + u * kWave + lane;
-      idv[u] = s < rg.end ? ids[s] : -1;
-      wv[u] = (s < rg.end && w) ? w[s] : 1.f;
+      for (int u = 0; u < kBatch; ++u) {
+        idv[u] = idv0[u];
+        wv[u] = wv0[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {  // all loads of the batch before any use
+        const int s = b0 + u * kWave + lane;
+        idv[u] = s < rg.end ? ids[s] : -1;
+        wv[u] = (s < rg.end && w) ? w[s] : 1.f;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
