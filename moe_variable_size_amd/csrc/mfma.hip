@@ -148,6 +148,26 @@ MOE_DEV void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Data-parallel-primitive moves inside rows of 16 lanes (gfx9 DPP controls).
+template <int CTRL>
+MOE_DEV float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                            0xF, false));
+}
+// Sum of v over each 32-lane half of the wave, by DPP adds instead of LDS
+// permutes: quad_perm [1,0,3,2] and [2,3,0,1] (quads), row_half_mirror (8
+// lanes), row_mirror (16 lanes), then row_bcast15 into rows 1 and 3 only.
+// The half's sum is valid in lanes 16..31 (first half) and 48..63 (second).
+MOE_DEV float half_wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);
+  v += dpp_mov<0x4E>(v);
+  v += dpp_mov<0x141>(v);
+  v += dpp_mov<0x140>(v);
+  v += __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  return v;
+}
+
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>) in sequence:
 // a loop that is unrolled whatever its body's size, so that register arrays
 // indexed by its counter stay in registers
@@ -1505,13 +1525,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
             }
           }
           if (has_dw) {
-            // sum each row over the 32 lanes of its half-wave
+            // sum each row over the 32 lanes of its half-wave (the sums land
+            // in lanes 16..31 and 48..63)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-              for (int d = 16; d >= 1; d >>= 1) dwp[q] += __shfl_xor(dwp[q], d, 32);
-            }
-            if ((lane & 31) == 0) {
+            for (int q = 0; q < 4; ++q) dwp[q] = half_wave_sum(dwp[q]);
+            if ((lane & 31) == 16) {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
                 if (t4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], dwp[q]);
