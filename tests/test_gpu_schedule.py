@@ -48,8 +48,12 @@ def test_schedule_page_example():
     assert sch.offsets.cpu().numpy().tolist() == [3, 3, 8]
 
 
+# the builder cuts the assignments into blocks of 1024 (more when T*k*E is
+# large); (700, 2) and (1000, 3) give two and three blocks, where workgroups
+# take more than one of the per-expert output jobs
 @pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (37, 3, 6, 1), (5, 2, 64, 2), (1000, 4, 7, 3),
-                                        (4099, 2, 130, 4), (5000, 8, 1000, 5), (333, 1, 1024, 6)])
+                                        (4099, 2, 130, 4), (5000, 8, 1000, 5), (333, 1, 1024, 6),
+                                        (700, 2, 5, 7), (1000, 3, 9, 8)])
 def test_schedule_random(T, k, E, seed):
     rng = np.random.default_rng(seed)
     ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
