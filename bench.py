@@ -319,8 +319,9 @@ def fp8_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
 def main():
     a = _args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported by this build "
-              "(single-GPU path; see DESIGN.md for how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {a.gpus} is not supported (the library "
+              "runs the single-GPU path; expert shards across GPUs are not built)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
