@@ -335,8 +335,10 @@ __global__ void tile_map_kernel(const int32_t *__restrict__ bstart, int E, int t
   }
 }
 
-// Zero up to two byte ranges in one launch: 16-byte nontemporal stores over the
-// aligned part of each, then the bytes of each tail.
+// Zero up to two byte ranges in one launch: 16-byte stores over the aligned part
+// of each, then the bytes of each tail.  Plain stores rather than nontemporal
+// ones: 134 MB took 22 instead of 29 us, and the zeros the next kernel's
+// atomics update partly stay in the caches.
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 struct FillRange {
   u32x4_t *p;
@@ -349,9 +351,9 @@ __global__ void fill_zero_kernel(FillRange a, FillRange b) {
   const u32x4_t z = {0u, 0u, 0u, 0u};
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.n16 + b.n16; i += stride) {
     if (i < a.n16)
-      __builtin_nontemporal_store(z, a.p + i);
+      a.p[i] = z;
     else
-      __builtin_nontemporal_store(z, b.p + (i - a.n16));
+      b.p[i - a.n16] = z;
   }
   if (blockIdx.x == 0 && (int)threadIdx.x < a.ntail) a.tail[threadIdx.x] = 0;
   if (blockIdx.x == 0 && (int)threadIdx.x < b.ntail) b.tail[threadIdx.x] = 0;
