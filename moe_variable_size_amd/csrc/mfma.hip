@@ -1635,6 +1635,17 @@ struct DwOp {
   uint32_t lds0;
   const char *lds;
   int r0, m, wid, lane, K, N, weighted;
+  // the next kernel's zero range, cleared on the side: one 16-byte chunk per
+  // lane with each stage's token load (this lane's next chunk zi, step zstep)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t *zp;
+  size_t zn16, zi, zstep;
+  MOE_DEV void zero_chunk() {
+    if (zi < zn16) {
+      __builtin_nontemporal_store(u32x4_t{0u, 0u, 0u, 0u}, zp + zi);
+      zi += zstep;
+    }
+  }
   uint32_t ncol[PW], kcol[PW];  // byte offsets of this lane's column chunk (dY / x), or OOB
   i32x4 tq[PW / 2];             // tokens of this wave's 2*PW rows of the stage being issued
 
@@ -1694,6 +1705,9 @@ struct DwOp {
       const int qt = (kt + 2) * BK + lane;
       const uint32_t offt = qt < m ? (uint32_t)(r0 + qt) * 4u : kOobOffset;
       dma4(rsT, offt, lds0 + (uint32_t)ring_off(kt + 2));
+      // at most one more vector-memory operation per stage: the waits of the
+      // pipeline stay valid (they drain, or leave at most one stage's count)
+      zero_chunk();
     }
   }
   // factors of the 8 reduction rows this lane holds in step `step`
@@ -1725,9 +1739,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   const int units = E * per_e;
   const int G = gridDim.x, L = logical_block();
   // the next kernel's accumulation targets, zeroed while this one runs
-  zero_share<NW * 64>(p.zero0, p.zero0_bytes, L, G);
+  // the next kernel's accumulation targets: the small one now, the large one
+  // (dX) a chunk per stage on the side and the rest at the end
   zero_share<NW * 64>(p.zero1, p.zero1_bytes, L, G);
   DwOp<NW, RM> op;
+  op.zp = (typename DwOp<NW, RM>::u32x4_t *)p.zero0;
+  op.zn16 = p.zero0 ? p.zero0_bytes / 16 : 0;
+  op.zi = (size_t)L * (NW * 64) + tid;
+  op.zstep = (size_t)G * (NW * 64);
   op.rsY = uniform_rsrc(p.dY, p.dy_bytes);
   op.rsX = uniform_rsrc(p.x, p.x_bytes);
   op.rsW = uniform_rsrc(p.row_weight, p.rw_bytes);
@@ -1792,6 +1811,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
         *(u32x4_t *)(out + (size_t)n * K + col) = *(const u32x4_t *)(stile + rl * BN + cc);
     }
   }
+  // the part of the zero range the stages did not reach, and its trailing bytes
+  while (op.zi < op.zn16) op.zero_chunk();
+  if (p.zero0 && L == 0 && tid < (p.zero0_bytes - op.zn16 * 16) / 4)
+    p.zero0[op.zn16 * 4 + tid] = 0.f;
 }
 
 // dynamic LDS of the forward and input-gradient kernels: NSTAGE stages of
