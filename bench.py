@@ -50,6 +50,8 @@ def _args():
                    help="untimed steps first (also brings the GPU clocks to their loaded state)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-config3", action="store_true", help="skip the Zipf-skewed fwd+bwd line")
+    p.add_argument("--no-config4", action="store_true", help="skip the dW stress line")
     p.add_argument("--no-fp8", action="store_true", help="skip the 8-bit forward lines")
     p.add_argument("--no-gated", action="store_true",
                    help="skip the gated expert FFN line (its inputs take ~10 s to draw)")
@@ -101,6 +103,132 @@ def _traffic(kernel_family: str):
         return None
     k = rec.get("kernels", {}).get(kernel_family)
     return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def _timed_steps(torch, api, step, steps: int, warmup: int, families) -> tuple:
+    """Wall time per step over `steps` steps after `warmup`, then the library's
+    per-launch HIP-event durations (us) of each kernel family over as many
+    steps again."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    api.moe_timing_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    api.moe_timing_enable(False)
+    kt = {}
+    for f in families:
+        tot, n = api.moe_timing_read(f)
+        kt[f] = round(tot * 1e3 / max(n, 1), 3) if n else None
+    return ms_step, kt
+
+
+def useful_rows(counts) -> dict:
+    """Fraction of the computed tile rows that are real rows, per tile height
+    ("Grouped GEMM for MoE, in depth" -- "Worked example: tile counts under
+    skew")."""
+    c = np.asarray(counts, dtype=np.int64)
+    out = {}
+    for bm in (64, 128, 256):
+        blocks = int((-(-c // bm)).sum())
+        out[f"bm{bm}"] = round(float(c.sum()) / (blocks * bm), 4) if blocks else None
+    return out
+
+
+def config3_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
+    """Zipf-skewed fused layer, forward + backward (T=8192, E=64, top-4,
+    K=4096, N=1408; 4 empty experts): useful TFLOP/s of each grouped kernel
+    against the bf16 matrix-core peak."""
+    r = WL.config3()
+    T, K, N, E, k = r.T, r.K, r.N, r.E, r.k
+    S = T * k
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, W, dY = to_dev(r.x), to_dev(r.W), to_dev(r.dY)
+    ids = torch.from_numpy(r.expert_ids).to(dev)
+    w = torch.from_numpy(r.topk_weights).to(dev)
+    ws = torch.empty(api.moe_schedule_workspace_bytes(T, k, E), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    dX = torch.empty((T, K), dtype=torch.float32, device=dev)
+    dW = torch.empty((E, N, K), dtype=torch.bfloat16, device=dev)
+    dT = torch.empty((T, k), dtype=torch.float32, device=dev)
+
+    def step():
+        sch = api.moe_build_schedule(ids, w, E, workspace=ws)
+        api.moe_fused_fwd(x, W, sch, y=y)
+        api.moe_fused_bwd(dY, x, W, sch, out_dX=dX, out_dW=dW, out_dtopk=dT)
+
+    ms_step, kt = _timed_steps(torch, api, step, steps, warmup,
+                               ("build_schedule", "fill_zero", "fused_fwd", "bwd_dx", "bwd_dw"))
+    gemm = 2.0 * S * K * N
+    tf = {f: round((gemm + (2.0 * S * N if f == "bwd_dx" else 0.0)) / (kt[f] * 1e-6) / 1e12, 2)
+          for f in ("fused_fwd", "bwd_dx", "bwd_dw")}
+    step_tf = (3 * gemm + 2.0 * S * N) / (ms_step * 1e-3) / 1e12
+    dom = max(("fused_fwd", "bwd_dx", "bwd_dw"), key=lambda f: kt[f])
+    counts = np.bincount(r.expert_ids.ravel(), minlength=E)
+    del x, W, dY, dX, dW, y
+    return {"workload": f"{r.name} fwd+bwd step (schedule + fused fwd + dX/d_topk + dW)",
+            "T": T, "K": K, "N": N, "E": E, "top_k": k, "S": S,
+            "max_expert_rows": int(counts.max()), "empty_experts": int((counts == 0).sum()),
+            "step_ms": round(ms_step, 4), "tflops": round(step_tf, 2),
+            "pct_bf16_peak": round(100.0 * step_tf / PEAK_BF16_TFLOPS, 2),
+            "kernels_us": kt, "kernels_tflops": tf,
+            "schedule_share": round(kt["build_schedule"] * 1e-3 / ms_step, 4),
+            "useful_rows": useful_rows(counts),
+            "roofline": {"bound": "mfma", "kernel": dom, "achieved": tf[dom],
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf[dom] / PEAK_BF16_TFLOPS, 4)}}
+
+
+def config4_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
+    """Weight-gradient stress (E=128, K=2048, N=768, 65536 grouped rows,
+    Dirichlet(0.3) group sizes): dW = per-group dY^T X, useful TFLOP/s and
+    HBM GB/s of the algorithmic bytes (X, dY read once, dW written once)
+    against both rooflines."""
+    g = WL.config4()
+    r = WL.grouped_as_routed(g)
+
+    def to_dev(t):
+        return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X, dY = to_dev(r.x), to_dev(r.dY)
+    ids = torch.from_numpy(r.expert_ids).to(dev)
+    ws = torch.empty(api.moe_schedule_workspace_bytes(r.T, 1, g.E), dtype=torch.uint8, device=dev)
+    dW = torch.empty((g.E, g.N, g.K), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        sch = api.moe_build_schedule(ids, None, g.E, workspace=ws)
+        api.moe_fused_bwd(dY, X, None, sch, dx=False, dtopk=False, N=g.N, out_dW=dW)
+
+    ms_step, kt = _timed_steps(torch, api, step, steps, warmup, ("build_schedule", "bwd_dw"))
+    flops = 2.0 * g.M * g.K * g.N
+    nbytes = g.M * g.K * 2 + g.M * g.N * 2 + g.E * g.N * g.K * 2
+    us = kt["bwd_dw"]
+    tf = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    bound_us = max(flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e6
+    sizes = np.asarray(g.group_sizes)
+    del X, dY, dW
+    return {"workload": f"{g.name} weight gradient (schedule + dW)",
+            "S": g.M, "K": g.K, "N": g.N, "E": g.E, "seed": g.seed,
+            "max_group_rows": int(sizes.max()), "empty_groups": int((sizes == 0).sum()),
+            "groups_over_4096": int((sizes > 4096).sum()),
+            "step_ms": round(ms_step, 4), "kernels_us": kt,
+            "dw_tflops": round(tf, 2), "dw_hbm_GBps": round(gbs, 1), "bytes_per_launch": nbytes,
+            "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "roofline": {"bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
+                         else "mfma", "bound_us": round(bound_us, 2),
+                         "frac": round(bound_us / us, 4)},
+            "schedule_share": round(kt["build_schedule"] * 1e-3 / ms_step, 4)}
 
 
 def decode_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
@@ -419,6 +547,13 @@ def main():
     tr = _traffic(dom)
     if tr is not None:
         out["roofline"]["traffic"] = tr
+    out["schedule_share"] = round(kt["build_schedule"]["avg_us"] * 1e-3 / ms_step, 4)
+    out["useful_rows"] = useful_rows(np.bincount(r.expert_ids.ravel(), minlength=E))
+    del x, W, dY, y, dX, dW, dT
+    if not a.no_config3:
+        out["config3"] = config3_line(torch, api, WL, dev, min(a.steps, 50), min(a.warmup, 20))
+    if not a.no_config4:
+        out["config4"] = config4_line(torch, api, WL, dev, min(a.steps, 100), min(a.warmup, 20))
     if not a.no_decode:
         out["decode"] = decode_line(torch, api, WL, dev, a.steps, a.warmup)
     if not a.no_fp8:

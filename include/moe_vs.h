@@ -279,8 +279,8 @@ size_t moe_fused_bwd_workspace_bytes(const moe_schedule *sched, int64_t K, int64
  *                  w_s * dY[t_s, n] * x[t_s, k]   (a per-expert A^T B reduction
  *                  whose reduction length m_e varies; written for EVERY expert,
  *                  exactly 0 for an expert with no rows);
- *   d_topk[t, j] = sum_n dY[t, n] * Z[s, n], Z[s] = x[t] W[ids[t,j]]^T, the
- *                  unweighted per-assignment product.
+ *   d_topk[t, j] = sum_n dY[t, n] * Z[s, n], Z[s] = x[t] W[ids[t,j]]^T (the
+ *                  product of assignment s before its weight is applied).
  *   dY [T, N], x [T, K], W [E, N, K] in `dtype`.
  *   dX [T, K] float or NULL (skip); OVERWRITTEN.
  *   dW [E, N, K] in `dtype` or NULL (skip); OVERWRITTEN; 16-byte aligned for
@@ -309,6 +309,19 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
 int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
                  int32_t *tile_start, int32_t *total, int32_t *owner, int64_t owner_capacity,
                  void *stream);
+
+/*
+ * Tile height of the routed kernels (the fused forward, the gated FFN and the
+ * input gradient), a process-wide setting read at each launch ([GG] "Worked
+ * example: tile counts under skew": shorter tiles waste fewer rows of small
+ * groups, taller ones reuse each weight tile more).
+ *   rows  0   = chosen on the device at each launch from the schedule's
+ *               row-block totals (the default; no host read-back);
+ *         128 or 256 = that height for every routed launch until changed.
+ * Returns MOE_ERR_SHAPE (and changes nothing) for any other value.  Results
+ * do not depend on the setting beyond floating-point summation order.
+ */
+int moe_set_tile_rows(int32_t rows);
 
 /*
  * Kernel timing for benchmarks.  While enabled, the library brackets every

@@ -63,6 +63,7 @@ SIGNATURES = {
     "moe_fused_bwd_workspace_bytes": (_SZ, [_SCHED_P, _I64, _I64, _I32]),
     "moe_fused_bwd": (ctypes.c_int, [_P, _P, _P, _SCHED_P, _P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
     "moe_tile_map": (ctypes.c_int, [_SCHED_P, _I64, _I32, _I32, _P, _P, _P, _I64, _P]),
+    "moe_set_tile_rows": (ctypes.c_int, [_I32]),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64)]),

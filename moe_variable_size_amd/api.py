@@ -11,6 +11,7 @@ Pages the operations follow:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 from dataclasses import dataclass
 from typing import Optional
@@ -43,6 +44,30 @@ def _require(t: torch.Tensor, name: str, dtype=None, ndim=None, contiguous=True)
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
     if contiguous and not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _require_out(t, name: str, dtype, shape, device) -> None:
+    """A caller-supplied output: exactly the dtype, shape and device the call
+    writes, dense.  The kernels write every byte of that shape from the
+    pointer, so anything smaller would be written past."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on(stream):
+    """Allocation context: buffers the binding allocates for a launch on a
+    stream other than the current one come from that stream's pool, so the
+    caching allocator never hands them to other work while the launch may
+    still use them."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -127,7 +152,12 @@ def moe_build_schedule(expert_ids: torch.Tensor, topk_weights: Optional[torch.Te
     if nbytes == 0:
         raise ValueError(f"invalid schedule sizes T={T} k={k} E={E} layout={layout} capacity={capacity}")
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=expert_ids.device)
+        with _on(stream):
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=expert_ids.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1)
+        if workspace.numel() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel()} bytes, the schedule needs {nbytes}")
     c = _lib.MoeSchedule()
     st = lib.moe_build_schedule(_ptr(expert_ids), _ptr(topk_weights), T, k, E, layout, capacity,
                                 _ptr(workspace), workspace.numel(), ctypes.byref(c), _stream(stream))
@@ -150,8 +180,9 @@ def grouped_gemm(A: torch.Tensor, W: torch.Tensor, offsets: torch.Tensor, *,
     if out_dtype is None:
         out_dtype = A.dtype
     if out is None:
-        out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
-    _require(out, "out", out_dtype, 2)
+        with _on(stream):
+            out = torch.zeros((M, N), dtype=out_dtype, device=A.device)
+    _require_out(out, "out", out_dtype, (M, N), A.device)
     st = lib.grouped_gemm(_ptr(A), _ptr(W), _ptr(offsets), _ptr(out), M, K, N, E, _dtype_code(A),
                           _DTYPES[out_dtype], _stream(stream))
     _lib.check("grouped_gemm", st)
@@ -170,8 +201,9 @@ def moe_fused_fwd(x: torch.Tensor, W: torch.Tensor, sched: Schedule, *,
     if K2 != K or T != sched.c.T or E != sched.c.E:
         raise ValueError("shape mismatch between x [T,K], W [E,N,K] and the schedule")
     if y is None:
-        y = torch.empty((T, N), dtype=torch.float32, device=x.device)
-    _require(y, "y", torch.float32, 2)
+        with _on(stream):
+            y = torch.empty((T, N), dtype=torch.float32, device=x.device)
+    _require_out(y, "y", torch.float32, (T, N), x.device)
     st = lib.moe_fused_fwd(_ptr(x), _ptr(W), ctypes.byref(sched.c), _ptr(y), K, N, _dtype_code(x),
                            _stream(stream))
     _lib.check("moe_fused_fwd", st)
@@ -199,8 +231,9 @@ def moe_fused_fwd_fp8(x_q: torch.Tensor, x_scale: torch.Tensor, W_q: torch.Tenso
             or tuple(w_scale.shape) != (E, N):
         raise ValueError("shape mismatch between x_q [T,K], W_q [E,N,K], the scales and the schedule")
     if y is None:
-        y = torch.empty((T, N), dtype=torch.float32, device=x_q.device)
-    _require(y, "y", torch.float32, 2)
+        with _on(stream):
+            y = torch.empty((T, N), dtype=torch.float32, device=x_q.device)
+    _require_out(y, "y", torch.float32, (T, N), x_q.device)
     st = lib.moe_fused_fwd_fp8(_ptr(x_q), _ptr(x_scale), _ptr(W_q), _ptr(w_scale),
                                ctypes.byref(sched.c), _ptr(y), K, N, _stream(stream))
     _lib.check("moe_fused_fwd_fp8", st)
@@ -223,8 +256,9 @@ def moe_fused_fwd_mx(x_q: torch.Tensor, x_bs: torch.Tensor, W_q: torch.Tensor, w
             or tuple(w_bs.shape) != (E, N, K // 32):
         raise ValueError("shape mismatch between x_q, W_q, their block scales and the schedule")
     if y is None:
-        y = torch.empty((T, N), dtype=torch.float32, device=x_q.device)
-    _require(y, "y", torch.float32, 2)
+        with _on(stream):
+            y = torch.empty((T, N), dtype=torch.float32, device=x_q.device)
+    _require_out(y, "y", torch.float32, (T, N), x_q.device)
     st = lib.moe_fused_fwd_mx(_ptr(x_q), _ptr(x_bs), _ptr(W_q), _ptr(w_bs), ctypes.byref(sched.c),
                               _ptr(y), K, N, _stream(stream))
     _lib.check("moe_fused_fwd_mx", st)
@@ -249,20 +283,17 @@ def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor,
     E2, N, F = W_down.shape
     if K2 != K or F2 != 2 * F or E2 != E or T != sched.c.T or E != sched.c.E:
         raise ValueError("shape mismatch between x [T,K], W_gu [E,2F,K], W_down [E,N,F] and the schedule")
-    if h is None:
-        h = torch.empty((sched.c.R, F), dtype=torch.bfloat16, device=x.device)
-    if y is None:
-        y = torch.empty((T, N), dtype=torch.float32, device=x.device)
-    _require(h, "h", torch.bfloat16, 2)
-    _require(y, "y", torch.float32, 2)
-    if tuple(h.shape) != (sched.c.R, F) or tuple(y.shape) != (T, N):
-        raise ValueError("h must be [R, F] and y [T, N]")
-    if gu is None and save_gu:
-        gu = torch.empty((sched.c.R, 2 * F), dtype=torch.float32, device=x.device)
+    with _on(stream):
+        if h is None:
+            h = torch.empty((sched.c.R, F), dtype=torch.bfloat16, device=x.device)
+        if y is None:
+            y = torch.empty((T, N), dtype=torch.float32, device=x.device)
+        if gu is None and save_gu:
+            gu = torch.empty((sched.c.R, 2 * F), dtype=torch.float32, device=x.device)
+    _require_out(h, "h", torch.bfloat16, (sched.c.R, F), x.device)
+    _require_out(y, "y", torch.float32, (T, N), x.device)
     if gu is not None:
-        _require(gu, "gu", torch.float32, 2)
-        if tuple(gu.shape) != (sched.c.R, 2 * F):
-            raise ValueError("gu must be [R, 2F]")
+        _require_out(gu, "gu", torch.float32, (sched.c.R, 2 * F), x.device)
     st = lib.moe_gated_ffn_fwd(_ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c), _ptr(h),
                                _ptr(gu), _ptr(y), K, F, N, MOE_BF16, _stream(stream))
     _lib.check("moe_gated_ffn_fwd", st)
@@ -288,12 +319,15 @@ def moe_gated_ffn_bwd(dY: torch.Tensor, x: torch.Tensor, W_gu: torch.Tensor, W_d
             or tuple(gu.shape) != (sched.c.R, 2 * F) or tuple(h.shape) != (sched.c.R, F):
         raise ValueError("shape mismatch among dY, x, W_gu, W_down, gu, h and the schedule")
     dev = x.device
-    dX = torch.empty((T, K), dtype=torch.float32, device=dev) if dx else None
-    dWgu = torch.empty((E, 2 * F, K), dtype=torch.bfloat16, device=dev) if dw_gu else None
-    dWd = torch.empty((E, N, F), dtype=torch.bfloat16, device=dev) if dw_down else None
-    dT = torch.empty((T, sched.c.k), dtype=torch.float32, device=dev) if dtopk else None
     ws_bytes = int(lib.moe_gated_ffn_bwd_workspace_bytes(ctypes.byref(sched.c), F))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    with _on(stream):
+        dX = torch.empty((T, K), dtype=torch.float32, device=dev) if dx else None
+        dWgu = torch.empty((E, 2 * F, K), dtype=torch.bfloat16, device=dev) if dw_gu else None
+        dWd = torch.empty((E, N, F), dtype=torch.bfloat16, device=dev) if dw_down else None
+        dT = torch.empty((T, sched.c.k), dtype=torch.float32, device=dev) if dtopk else None
+        # dgu workspace: freed into this stream's pool when the call returns, so
+        # it is not reused before the launches queued here have run
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     st = lib.moe_gated_ffn_bwd(_ptr(dY), _ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c),
                                _ptr(gu), _ptr(h), _ptr(dX), _ptr(dWgu), _ptr(dWd), _ptr(dT), K, F, N,
                                MOE_BF16, _ptr(ws), ws_bytes, _stream(stream))
@@ -323,12 +357,20 @@ def moe_fused_bwd(dY: torch.Tensor, x: torch.Tensor, W: Optional[torch.Tensor], 
     if dY.shape[0] != T or T != sched.c.T:
         raise ValueError("dY, x and the schedule disagree on T")
     dev = x.device
-    dX = (out_dX if out_dX is not None else torch.empty((T, K), dtype=torch.float32, device=dev)) if dx else None
-    dW = (out_dW if out_dW is not None else torch.empty((E, N, K), dtype=x.dtype, device=dev)) if dw else None
-    dT = (out_dtopk if out_dtopk is not None else torch.empty((T, sched.c.k), dtype=torch.float32, device=dev)) if dtopk else None
     code = _dtype_code(x)
-    ws_bytes = int(lib.moe_fused_bwd_workspace_bytes(ctypes.byref(sched.c), K, N, code))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    k = sched.c.k
+    with _on(stream):
+        dX = (out_dX if out_dX is not None else torch.empty((T, K), dtype=torch.float32, device=dev)) if dx else None
+        dW = (out_dW if out_dW is not None else torch.empty((E, N, K), dtype=x.dtype, device=dev)) if dw else None
+        dT = (out_dtopk if out_dtopk is not None else torch.empty((T, k), dtype=torch.float32, device=dev)) if dtopk else None
+        ws_bytes = int(lib.moe_fused_bwd_workspace_bytes(ctypes.byref(sched.c), K, N, code))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    if dX is not None:
+        _require_out(dX, "out_dX", torch.float32, (T, K), dev)
+    if dW is not None:
+        _require_out(dW, "out_dW", x.dtype, (E, N, K), dev)
+    if dT is not None:
+        _require_out(dT, "out_dtopk", torch.float32, (T, k), dev)
     st = lib.moe_fused_bwd(_ptr(dY), _ptr(x), _ptr(W), ctypes.byref(sched.c), _ptr(dX), _ptr(dW),
                            _ptr(dT), K, N, code, _ptr(ws), ws_bytes, _stream(stream))
     _lib.check("moe_fused_bwd", st)
@@ -346,13 +388,20 @@ def moe_tile_map(sched: Schedule, N: int, BM: int, BN: int, owner_capacity: Opti
     if owner_capacity is None:
         owner_capacity = (sched.c.R // BM + E) * tiles_n + 1
     dev = sched.workspace.device
-    tile_start = torch.empty(E, dtype=torch.int32, device=dev)
-    total = torch.empty(1, dtype=torch.int32, device=dev)
-    owner = torch.full((owner_capacity,), -1, dtype=torch.int32, device=dev)
+    with _on(stream):
+        tile_start = torch.empty(E, dtype=torch.int32, device=dev)
+        total = torch.empty(1, dtype=torch.int32, device=dev)
+        owner = torch.full((owner_capacity,), -1, dtype=torch.int32, device=dev)
     st = lib.moe_tile_map(ctypes.byref(sched.c), N, BM, BN, _ptr(tile_start), _ptr(total), _ptr(owner),
                           owner_capacity, _stream(stream))
     _lib.check("moe_tile_map", st)
     return tile_start, total, owner
+
+
+def moe_set_tile_rows(rows: int) -> None:
+    """Tile height of the routed kernels: 0 = chosen on the device per launch
+    (default), 128 or 256 = forced for every later launch of this process."""
+    _lib.check("moe_set_tile_rows", _lib.load().moe_set_tile_rows(int(rows)))
 
 
 def moe_timing_enable(enable: bool = True) -> None:

@@ -468,6 +468,8 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN, i
   }));
 }
 
+int moe_set_tile_rows(int32_t rows) { return set_tile_rows(rows); }
+
 int moe_timing_enable(int enable) {
   Timing &t = timing();
   std::lock_guard<std::mutex> g(t.mu);

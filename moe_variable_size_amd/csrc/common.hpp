@@ -92,6 +92,8 @@ hipError_t simt_bwd_dw(const void *dY, const void *x, const moe_schedule &s, voi
 
 // bf16 MFMA path
 bool mfma_supported(int K, int N);
+// process-wide tile height of the routed kernels: 0 (device pick), 128 or 256
+int set_tile_rows(int rows);
 hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C,
                              int M, int K, int N, int E, int out_dtype, hipStream_t st);
 // a_by_row: the A operand is already in schedule row order ([R, K]) instead of

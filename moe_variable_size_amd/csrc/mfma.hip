@@ -46,6 +46,7 @@
 //    all workgroups (stream-K), which evens out the tail.
 #include "common.hpp"
 
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -201,96 +202,57 @@ MOE_DEV int logical_block() {
   return (G & 7) ? b : (b & 7) * (G >> 3) + (b >> 3);
 }
 
-// Work split of `total` tiles of KI stages over G workgroups.  Whole tiles go
-// out in rounds of G (workgroup Lb takes tiles Lb, Lb + G, ...).  The tiles of
-// the last partial round are either
-//   * cut into S sub-tiles each (S = 4 or 8, rows and columns split, at most
-//     one sub-tile per workgroup), so no workgroup idles for a whole tile time
-//     and every output element is still produced by exactly one workgroup; a
-//     workgroup runs its sub-tile BEFORE its whole tiles, so the sub-tile's
-//     scatter drains while the whole tiles multiply (run after them, it would
-//     wait behind the whole tiles' atomics, which retire in order); or
-//   * (stream_k) split along the reduction over all G workgroups.
+// Work split of `total` tiles over G workgroups.  Whole tiles go out in
+// rounds of G (workgroup Lb takes tiles Lb, Lb + G, ...).  The tiles of the
+// last partial round are cut into S sub-tiles each (S = 8, 4 or 2 with rows
+// and columns split, at most one sub-tile per workgroup; S = 1 when even the
+// 2-way split leaves more pieces than workgroups), so no workgroup idles for a
+// whole tile time and every output element is still produced by exactly one
+// workgroup.  A workgroup runs its sub-tile BEFORE its whole tiles, so the
+// sub-tile's scatter drains while the whole tiles multiply (run after them, it
+// would wait behind the whole tiles' atomics, which retire in order).
 struct WorkSplit {
-  int64_t it, it_end, tail0, tot;
-  int KI, G, Lb;
-  bool sk;
+  int G, Lb;
   int next_tile, full, pieces, S;
   bool piece_done;
   int s, nS;  // sub-tile of the current piece (0 of 1 for a whole tile)
-  enum { WHOLE = 0, SUBTILE_TAIL = 1, STREAM_K = 2 };
-  MOE_DEV void init(int total, int KI_, int G_, int Lb_, int mode, int max_split = 8) {
-    KI = KI_;
+  enum { WHOLE = 0, SUBTILE_TAIL = 1 };
+  MOE_DEV void init(int total, int G_, int Lb_, int mode, int max_split = 8) {
     G = G_;
     Lb = Lb_;
-    sk = mode == STREAM_K;
     s = 0;
     nS = 1;
-    if (!sk) {
-      full = (total / G) * G;
-      const int rem = total - full;
-      S = 1;
-      if (mode == SUBTILE_TAIL && rem > 0)
-        S = (max_split >= 8 && rem * 8 <= G) ? 8
-            : (max_split >= 4 && rem * 4 <= G) ? 4
-            : (max_split >= 2 && rem * 2 <= G) ? 2 : 1;
-      pieces = rem * S;
-      next_tile = Lb;
-      piece_done = false;
-      return;
-    }
-    tot = (int64_t)total * KI;
-    const int fullr = (total / G) * G;
-    tail0 = (int64_t)fullr * KI;
-    if (Lb < fullr) {
-      it = (int64_t)Lb * KI;
-      it_end = it + KI;
-    } else {
-      it = tail0 + (tot - tail0) * Lb / G;
-      it_end = tail0 + (tot - tail0) * (Lb + 1) / G;
-    }
+    full = (total / G) * G;
+    const int rem = total - full;
+    S = 1;
+    if (mode == SUBTILE_TAIL && rem > 0)
+      S = (max_split >= 8 && rem * 8 <= G) ? 8
+          : (max_split >= 4 && rem * 4 <= G) ? 4
+          : (max_split >= 2 && rem * 2 <= G) ? 2 : 1;
+    pieces = rem * S;
+    next_tile = Lb;
+    piece_done = false;
   }
-  // next piece (tile, kb, ke; sub-tile s of nS); false when done
-  MOE_DEV bool next(int &tau, int &kb, int &ke) {
-    if (!sk) {
-      kb = 0;
-      ke = KI;
-      // a workgroup's piece of the last round comes first: its few atomics
-      // drain while the whole tiles multiply, instead of queueing behind them
-      if (!piece_done && Lb < pieces) {
-        piece_done = true;
-        tau = full + Lb / S;
-        s = Lb % S;
-        nS = S;
-        return true;
-      }
+  // next piece (tile tau; sub-tile s of nS); false when done
+  MOE_DEV bool next(int &tau) {
+    // a workgroup's piece of the last round comes first: its few atomics
+    // drain while the whole tiles multiply, instead of queueing behind them
+    if (!piece_done && Lb < pieces) {
       piece_done = true;
-      if (next_tile < full) {
-        tau = next_tile;
-        next_tile += G;
-        s = 0;
-        nS = 1;
-        return true;
-      }
-      return false;
+      tau = full + Lb / S;
+      s = Lb % S;
+      nS = S;
+      return true;
     }
-    while (it >= it_end) {
-      if (it_end <= tail0 && it_end + (int64_t)(G - 1) * KI < tail0) {
-        it = it_end + (int64_t)(G - 1) * KI;  // next whole tile of this workgroup
-        it_end = it + KI;
-      } else if (it_end <= tail0) {
-        it = tail0 + (tot - tail0) * Lb / G;  // whole tiles done: tail slice
-        it_end = tail0 + (tot - tail0) * (Lb + 1) / G;
-        if (it >= it_end) return false;
-      } else {
-        return false;
-      }
+    piece_done = true;
+    if (next_tile < full) {
+      tau = next_tile;
+      next_tile += G;
+      s = 0;
+      nS = 1;
+      return true;
     }
-    tau = (int)(it / KI);
-    kb = (int)(it - (int64_t)tau * KI);
-    ke = (int)min((int64_t)KI, kb + (it_end - it));
-    it += ke - kb;
-    return true;
+    return false;
   }
 };
 
@@ -784,8 +746,6 @@ struct FwdArgs {
   const float *row_weight;
   int E, layout, capacity, K, N;
   uint32_t a_bytes;  // bytes of A (x or the bare A)
-  int stream_k;      // 1: split the last partial wave of tiles along K
-  int tail_split;    // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int M;             // bare: rows of A and C (rows at or past M are never touched)
   int tile_rows;     // routed, BM = 256: 0 = picked on the device, 128 / 256 = forced
   const float *x_scale;  // 8-bit operands: per-token scale [T]
@@ -975,14 +935,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   WorkSplit ws;
   // gated tiles split along rows only (a column split would part gate from up);
   // 128-row tiles split at most 4 ways (64 x 128)
-  ws.init(total, KI, gridDim.x, Lb,
-          p.stream_k && !GATED && BMr == BM
-              ? WorkSplit::STREAM_K
-              : (BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE),
-          GATED ? (BMr == BM ? min(p.tail_split, 2) : 1)
-                : (BMr == BM ? p.tail_split : min(p.tail_split, 4)));
-  int tau, kb, ke;
-  while (ws.next(tau, kb, ke)) {
+  ws.init(total, gridDim.x, Lb, BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE,
+          GATED ? (BMr == BM ? 2 : 1) : (BMr == BM ? 8 : 4));
+  int tau;
+  const int kb = 0, ke = KI;
+  while (ws.next(tau)) {
     TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BMr);
     int n0 = c.nb * BNO, ncols = min(BNO, N - n0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
@@ -1262,8 +1219,6 @@ struct DxArgs {
   const float *row_weight;
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes;
-  int stream_k;
-  int tail_split;  // largest split of a tile of the last partial round (8, 4, 2 or 1)
   int tile_rows;   // 0 = picked on the device, 128 / 256 = forced
   // gated FFN backward (GB kernels): x is h [R, K] read by schedule row, gu the
   // saved gate/up values [R, 2K] (fp32), dgu the output [R, 2K] (bf16; K here is F)
@@ -1357,11 +1312,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   const int Lb = logical_block();
   WorkSplit ws;
   // 128-row tiles split at most 4 ways (64 x 128)
-  ws.init(total, KI, gridDim.x, Lb,
-          p.stream_k && BMr == BM ? WorkSplit::STREAM_K : WorkSplit::SUBTILE_TAIL,
-          BMr == BM ? p.tail_split : min(p.tail_split, 4));
-  int tau, kb, ke;
-  while (ws.next(tau, kb, ke)) {
+  ws.init(total, gridDim.x, Lb, WorkSplit::SUBTILE_TAIL, BMr == BM ? 8 : 4);
+  int tau;
+  const int kb = 0, ke = KI;
+  while (ws.next(tau)) {
     TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BMr);
     int kc0 = c.nb * BN, ncols = min(BN, K - kc0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
@@ -1836,98 +1790,25 @@ hipError_t set_smem(size_t bytes) {
   return e;
 }
 
-// MOE_VS_STREAM_K=1: split the last partial round of atomic-output kernels
-// along the reduction instead of into sub-tiles (read once per process)
-int stream_k_mode() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_STREAM_K");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
-}
-
-// MOE_VS_TAIL_SPLIT=n: largest split (8, 4, 2, 1) of a tile of the last
-// partial round of the forward and input-gradient kernels (read once)
-int tail_split() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_TAIL_SPLIT");
-    const int n = e ? atoi(e) : 8;
-    return (n == 1 || n == 2 || n == 4 || n == 8) ? n : 8;
-  }();
-  return v;
-}
-
-// MOE_VS_BM=128 / 256: routed forward and input-gradient kernels with 128- or
-// 256-row tiles instead of the device-side pick (read once)
-int forced_bm() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_BM");
-    const int n = e ? atoi(e) : 0;
-    return n == 128 || n == 256 ? n : 0;
-  }();
-  return v;
-}
-
-// MOE_VS_F8_WAVES=4: 8-bit forward with 4 waves (256 x 256 tiles) instead of 8
-// (128 x 256 tiles) (read once)
-int f8_waves() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_F8_WAVES");
-    return e && atoi(e) == 4 ? 4 : 8;
-  }();
-  return v;
-}
-
-// MOE_VS_DX_WAVES=8: input-gradient kernel with 8 waves per workgroup instead of
-// 4 (its routing-weight epilogue runs short of registers with 8)
-int dx_waves() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_DX_WAVES");
-    return e && atoi(e) == 8 ? 8 : 4;
-  }();
-  return v;
-}
-
-// MOE_VS_GEMM_WAVES=4: forward kernels with 4 waves per workgroup instead of 8
-int gemm_waves() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_GEMM_WAVES");
-    return e && atoi(e) == 4 ? 4 : 8;
-  }();
-  return v;
-}
-
-// MOE_VS_DW_WAVES=4: weight gradient with 4 waves per workgroup instead of 8
-int dw_waves() {
-  static const int v = [] {
-    const char *e = getenv("MOE_VS_DW_WAVES");
-    return e && atoi(e) == 4 ? 4 : 8;
-  }();
-  return v;
-}
+// Tile height of the routed forward-shaped and input-gradient kernels: 0 =
+// picked on the device per launch, 128 / 256 = forced (moe_set_tile_rows).
+std::atomic<int> g_tile_rows{0};
 
 }  // namespace
 
 bool mfma_supported(int K, int N) { return K % 8 == 0 && N % 8 == 0; }
 
 namespace {
-// Launch a 256 x 256 forward-shaped kernel with 4 (2 x 2) or 8 (2 x 4) waves.
+// Launch a 256 x 256 forward-shaped kernel with 8 waves (2 x 4).
 template <int MODE, typename Tout, bool F8 = false, bool MX = false>
 hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
   // block scales: two stages of (256 + 256) 4-byte scale words after the operands
   constexpr size_t lds = kStageLds + (MX ? 2 * (256 + 256) * 4 : 0);
-  if ((F8 ? f8_waves() : gemm_waves()) == 4) {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8, MX>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 2, MODE, Tout, F8, MX>), grid, dim3(256), lds,
-                       st, a);
-  } else {
-    hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>), grid, dim3(512), lds,
-                       st, a);
-  }
+  hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>), grid, dim3(512), lds,
+                     st, a);
   return hipGetLastError();
 }
 
@@ -1944,7 +1825,7 @@ hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
     hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
     return hipGetLastError();
   }
-  a.tile_rows = forced_bm();
+  a.tile_rows = g_tile_rows.load(std::memory_order_relaxed);
   return launch_fwd256<MODE, float, F8, MX>(a, st);
 }
 }  // namespace
@@ -1952,7 +1833,7 @@ hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
 hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int M,
                              int K, int N, int E, int out_dtype, hipStream_t st) {
   FwdArgs a{(const bf16_t *)A, (const bf16_t *)W, C, offsets, nullptr, nullptr, nullptr, nullptr,
-            E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), 0, tail_split(), M};
+            E, 0, 0, K, N, (uint32_t)((size_t)M * K * 2), M};
   if (out_dtype == MOE_F32) return launch_fwd256<FWD_BARE, float>(a, st);
   return launch_fwd256<FWD_BARE, bf16_t>(a, st);
 }
@@ -1962,7 +1843,7 @@ hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, f
   const size_t arows = a_by_row ? (size_t)s.R : (size_t)s.T;
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)(arows * K * 2), stream_k_mode(), tail_split(), (int)s.T};
+            (uint32_t)(arows * K * 2), (int)s.T};
   if (a_by_row) return launch_routed<FWD_SCATTER_ROWS>(a, s, st);
   return launch_routed<FWD_SCATTER>(a, s, st);
 }
@@ -1972,7 +1853,7 @@ hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *
                               hipStream_t st) {
   FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T};
+            (uint32_t)((size_t)s.T * K), (int)s.T};
   a.x_scale = x_scale;
   a.w_scale = w_scale;
   return launch_routed<FWD_SCATTER, true>(a, s, st);
@@ -1983,7 +1864,7 @@ hipError_t mfma_fused_fwd_mx(const void *xq, const uint8_t *x_bs, const void *Wq
                              hipStream_t st) {
   FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
-            (uint32_t)((size_t)s.T * K), 0, tail_split(), (int)s.T};
+            (uint32_t)((size_t)s.T * K), (int)s.T};
   a.x_bs = x_bs;
   a.w_bs = w_bs;
   return launch_routed<FWD_SCATTER, true, true>(a, s, st);
@@ -1993,7 +1874,7 @@ hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s,
                          int K, int F, hipStream_t st) {
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W_gu, h, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, F,
-            (uint32_t)((size_t)s.T * K * 2), 0, tail_split(), (int)s.T};
+            (uint32_t)((size_t)s.T * K * 2), (int)s.T};
   a.gu_out = (float *)gu;
   return launch_routed<FWD_GATED>(a, s, st);
 }
@@ -2005,7 +1886,7 @@ hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
-           (uint32_t)((size_t)s.T * K * 2), stream_k_mode(), tail_split(), forced_bm()};
+           (uint32_t)((size_t)s.T * K * 2), g_tile_rows.load(std::memory_order_relaxed)};
   return launch_dx(a, st);
 }
 
@@ -2015,7 +1896,7 @@ hipError_t mfma_gated_bwd_dh(const void *dY, const void *h, const void *W_down,
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)h, (const bf16_t *)W_down, nullptr, d_w, s.offsets,
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, F, N, (uint32_t)((size_t)s.T * N * 2),
-           (uint32_t)((size_t)s.R * F * 2), 0, tail_split(), forced_bm()};
+           (uint32_t)((size_t)s.R * F * 2), g_tile_rows.load(std::memory_order_relaxed)};
   a.gu = (const float *)gu;
   a.dgu = (bf16_t *)dgu;
   const dim3 grid(device_cu_count());
@@ -2030,7 +1911,7 @@ hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedu
   DxArgs a{(const bf16_t *)dgu, nullptr, (const bf16_t *)W_gu, dX, nullptr, s.offsets,
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, 2 * F,
-           (uint32_t)((size_t)s.R * 2 * F * 2), 0u, 0, tail_split(), forced_bm()};
+           (uint32_t)((size_t)s.R * 2 * F * 2), 0u, g_tile_rows.load(std::memory_order_relaxed)};
   const dim3 grid(device_cu_count());
   hipError_t e = set_smem<mfma_dx_kernel<4, false, true>>(kStageLds);
   if (e != hipSuccess) return e;
@@ -2040,33 +1921,19 @@ hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedu
 
 static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
-  if (dx_waves() == 4) {
-    hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mfma_dx_kernel<4>, grid, dim3(256), kStageLds, st, a);
-  } else {
-    hipError_t e = set_smem<mfma_dx_kernel<8>>(kStageLds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(mfma_dx_kernel<8>, grid, dim3(512), kStageLds, st, a);
-  }
+  hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mfma_dx_kernel<4>, grid, dim3(256), kStageLds, st, a);
   return hipGetLastError();
 }
 
 template <int RM>
 static hipError_t launch_dw(const DwArgs &a, hipStream_t st) {
-  if (dw_waves() == 4) {
-    constexpr size_t lds = DwOp<4, RM>::LDS_BYTES;
-    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 4, RM>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 4, RM>), dim3(device_cu_count()), dim3(256), lds,
-                       st, a);
-  } else {
-    constexpr size_t lds = DwOp<8, RM>::LDS_BYTES;
-    hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM>), dim3(device_cu_count()), dim3(512), lds,
-                       st, a);
-  }
+  constexpr size_t lds = DwOp<8, RM>::LDS_BYTES;
+  hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM>>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM>), dim3(device_cu_count()), dim3(512), lds, st,
+                     a);
   return hipGetLastError();
 }
 
@@ -2109,4 +1976,12 @@ hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool 
   return launch_dw<DW_GATHER>(a, st);
 }
 
+}  // namespace moe
+
+namespace moe {
+int set_tile_rows(int rows) {
+  if (rows != 0 && rows != 128 && rows != 256) return MOE_ERR_SHAPE;
+  g_tile_rows.store(rows, std::memory_order_relaxed);
+  return MOE_OK;
+}
 }  // namespace moe

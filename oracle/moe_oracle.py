@@ -62,8 +62,8 @@ def routing_schedule(expert_ids: np.ndarray, topk_weights: Optional[np.ndarray],
     [GG] "Data layout, offsets and alignment": a stable argsort of the per-copy
     expert index groups the rows by expert; bincount gives the per-expert
     counts and an int32 cumulative sum gives the end offsets.
-    [CARD] "How it works": the sorted order gives a row -> token map, a per-row
-    routing weight and the per-expert group sizes.
+    [CARD] "How it works": from the sorted order come the token of each row,
+    the weight of each row and the size of each expert's group.
     Ids outside [0, E) belong to no expert: they are excluded and counted.
     """
     expert_ids = np.asarray(expert_ids)
@@ -252,7 +252,7 @@ def moe_forward(x, W, expert_ids, topk_weights, E: int, *, acc=np.float64) -> np
     return y
 
 
-def moe_backward(dY, x, W, expert_ids, topk_weights, E: int, *, acc=np.float64):
+def moe_backward(dY, x, W, expert_ids, topk_weights, E: int, *, acc=np.float64, dw_experts=None):
     """Gradients of L = sum(dY * y) for the fused layer.
 
     [GG] "The backward pass": with Y_g = X_g W_g, the input gradient is
@@ -261,10 +261,12 @@ def moe_backward(dY, x, W, expert_ids, topk_weights, E: int, *, acc=np.float64):
     expert with no rows gets an exact zero gradient.  In (E, N, K) storage the
     weight gradient of expert e is sum over its rows of (w * dY[t])^T x[t].
     [CARD] "How it works": the token gradient is scattered with the routing
-    weight like the forward; the routing-weight gradient is the inner product
-    of the incoming gradient with the unweighted per-assignment product.
+    weight like the forward; for assignment s of token t to expert e,
+    d_w[s] = <dY[t], x[t] W[e]^T> (the product before the weight multiplies it).
 
-    Returns dX [T, K], dW [E, N, K], d_w [T, k].
+    Returns dX [T, K], dW [E, N, K], d_w [T, k].  With ``dw_experts`` (a list
+    of expert ids) dW is instead a dict holding dW[e] for those experts only
+    (the full [E, N, K] array is not formed).
     """
     expert_ids = np.asarray(expert_ids)
     T, k = expert_ids.shape
@@ -273,7 +275,10 @@ def moe_backward(dY, x, W, expert_ids, topk_weights, E: int, *, acc=np.float64):
     K = x.shape[1]
     N = W.shape[1]
     dX = np.zeros((T, K), dtype=acc)
-    dW = np.zeros((E, N, K), dtype=acc)
+    if dw_experts is None:
+        dW = np.zeros((E, N, K), dtype=acc)
+    else:
+        dW = {int(e): np.zeros((N, K), dtype=acc) for e in dw_experts}
     d_w = np.zeros(T * k, dtype=acc)
     xa = np.asarray(x)
     dYa = np.asarray(dY)
@@ -288,7 +293,8 @@ def moe_backward(dY, x, W, expert_ids, topk_weights, E: int, *, acc=np.float64):
         x_rows = xa[tok].astype(acc)     # [m_e, K]
         G = g_rows @ We                  # unweighted input gradient per assignment
         np.add.at(dX, tok, we[:, None] * G)
-        dW[e] = (we[:, None] * g_rows).T @ x_rows
+        if dw_experts is None or e in dW:
+            dW[e] = (we[:, None] * g_rows).T @ x_rows
         Z = x_rows @ We.T                # unweighted forward product per assignment
         d_w[s_e] = np.sum(g_rows * Z, axis=1)
     return dX, dW, d_w.reshape(T, k)

@@ -158,3 +158,10 @@ def test_mx_rejects_before_launch(lib):
     assert lib.moe_fused_fwd_mx(P, P, P, P, r, P, 64, 8, None) == 2        # K % 128 != 0
     assert lib.moe_fused_fwd_mx(P, None, P, P, r, P, 128, 8, None) == 1    # no x block scales
     assert lib.moe_fused_fwd_mx(P, ctypes.c_void_p((1 << 20) + 2), P, P, r, P, 128, 8, None) == 4
+
+
+def test_tile_rows_setting(lib):
+    assert lib.moe_set_tile_rows(100) == 2
+    assert lib.moe_set_tile_rows(64 + 1) == 2
+    for rows in (128, 256, 0):
+        assert lib.moe_set_tile_rows(rows) == 0

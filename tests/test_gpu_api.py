@@ -1,0 +1,150 @@
+"""GPU checks of the Python binding's own paths against the oracle: the
+differentiable layer (autograd), backward calls that skip outputs, launches on
+a side stream, forced tile heights, and caller-supplied outputs of the wrong
+shape (rejected before any launch)."""
+import numpy as np
+import pytest
+import torch
+
+from moe_variable_size_amd import api
+from moe_variable_size_amd import workloads as WL
+from oracle import moe_oracle as O
+from tests.gpu_util import assert_close, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(T=700, K=256, N=320, E=6, k=2, seed=41):
+    return WL.routed("api_small", T, K, N, E, k, seed=seed)
+
+
+@pytest.mark.parametrize("frozen_w", [False, True])
+def test_autograd_layer_matches_oracle(frozen_w):
+    """y = api.moe(x, W, ids, w); y.backward(dY) reaches x, W (unless frozen)
+    and the routing weights ("grouped-gemm-moe" card, "Usage")."""
+    r = _small()
+    log(f"autograd frozen_w={frozen_w}")
+    x = dev(r.x).requires_grad_(True)
+    W = dev(r.W).requires_grad_(not frozen_w)
+    w = dev(r.topk_weights).requires_grad_(True)
+    y = api.moe(x, W, dev(r.expert_ids), w)
+    y.backward(dev(r.dY).float())
+    torch.cuda.synchronize()
+    ry = O.moe_forward(r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+    rx, rW, rt = O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+    assert_close(host(y.detach()), ry, "bf16", "y")
+    assert_close(host(x.grad), rx, "bf16", "dX")
+    assert_close(host(w.grad), rt, "bf16", "d_topk")
+    if frozen_w:
+        assert W.grad is None
+    else:
+        assert_close(host(W.grad), rW, "bf16", "dW")
+
+
+def test_backward_without_weight_grad_overwrites_outputs():
+    """dw=False takes the zero-fill launch and the input-gradient kernel alone;
+    NaN-filled output buffers must come back fully written."""
+    r = _small(seed=42)
+    sch = api.moe_build_schedule(dev(r.expert_ids), dev(r.topk_weights), r.E)
+    dX0 = torch.full((r.T, r.K), float("nan"), dtype=torch.float32, device="cuda")
+    dT0 = torch.full((r.T, r.k), float("nan"), dtype=torch.float32, device="cuda")
+    dX, dW, dT = api.moe_fused_bwd(dev(r.dY), dev(r.x), dev(r.W), sch, dw=False,
+                                   out_dX=dX0, out_dtopk=dT0)
+    torch.cuda.synchronize()
+    assert dW is None
+    rx, _, rt = O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights,
+                               r.E, dw_experts=())
+    assert_close(host(dX), rx, "bf16", "dX")
+    assert_close(host(dT), rt, "bf16", "d_topk")
+
+
+def test_gated_backward_without_down_weight_grad():
+    """dw_down=False: the fill launch zeroes dX / d_topk instead of the
+    dW_down kernel; results match the oracle, NaN buffers are overwritten."""
+    g = WL.gated("api_gated", 333, 136, 200, 72, 7, 2, seed=43)
+    rng = np.random.default_rng(43)
+    dY = WL._make(rng.standard_normal((g.T, g.N), dtype=np.float32), True)
+    sch = api.moe_build_schedule(dev(g.expert_ids), dev(g.topk_weights), g.E)
+    y, h, gu = api.moe_gated_ffn_fwd(dev(g.x), dev(g.W_gu), dev(g.W_down), sch, save_gu=True)
+    dX, dWgu, dWd, dT = api.moe_gated_ffn_bwd(dev(dY), dev(g.x), dev(g.W_gu), dev(g.W_down), sch,
+                                              gu, h, dw_down=False)
+    torch.cuda.synchronize()
+    assert dWd is None
+    rx, rgu, _, rt = O.gated_ffn_backward(dY.values, g.x.values, g.W_gu.values, g.W_down.values,
+                                          g.expert_ids, g.topk_weights, g.E, round_h=True)
+    assert_close(host(dX), rx, "bf16", "dX")
+    assert_close(host(dWgu), rgu, "bf16", "dW_gu")
+    assert_close(host(dT), rt, "bf16", "d_topk")
+
+
+def test_gated_backward_on_a_side_stream_with_allocation_churn():
+    """The backward on a side stream while the current stream allocates and
+    frees memory: the binding's own buffers (the dgu workspace, outputs) come
+    from the side stream's pool, so the churn cannot reuse them early."""
+    g = WL.gated("api_stream", 1030, 256, 384, 256, 8, 2, seed=44)
+    rng = np.random.default_rng(44)
+    dY = WL._make(rng.standard_normal((g.T, g.N), dtype=np.float32), True)
+    args = [dev(dY), dev(g.x), dev(g.W_gu), dev(g.W_down)]
+    sch = api.moe_build_schedule(dev(g.expert_ids), dev(g.topk_weights), g.E)
+    y, h, gu = api.moe_gated_ffn_fwd(dev(g.x), dev(g.W_gu), dev(g.W_down), sch, save_gu=True)
+    ref = [host(t).copy() for t in api.moe_gated_ffn_bwd(*args, sch, gu, h)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        res = api.moe_gated_ffn_bwd(*args, sch, gu, h, stream=side)
+        for _ in range(8):   # churn on the current stream
+            t = torch.empty(int(40e6), dtype=torch.uint8, device="cuda")
+            t.fill_(rep + 1)
+            del t
+        side.synchronize()
+        outs.append([host(t) for t in res])
+    torch.cuda.synchronize()
+    for rep, got in enumerate(outs):
+        for a, b, name in zip(got, ref, ("dX", "dW_gu", "dW_down", "d_topk")):
+            assert_close(a, b.astype(np.float64), "bf16", f"side stream rep {rep} {name}")
+
+
+@pytest.mark.parametrize("rows", [128, 256])
+def test_forced_tile_rows(rows):
+    """moe_set_tile_rows forces the tile height of the routed kernels; both
+    heights give the oracle's results (forward, backward, gated FFN)."""
+    r = _small(T=2100, K=384, N=640, E=8, k=2, seed=45)
+    g = WL.gated("api_tiles", 1030, 256, 384, 256, 8, 2, seed=46)
+    log(f"forced tile rows {rows}")
+    api.moe_set_tile_rows(rows)
+    try:
+        sch = api.moe_build_schedule(dev(r.expert_ids), dev(r.topk_weights), r.E)
+        y = api.moe_fused_fwd(dev(r.x), dev(r.W), sch)
+        dX, dW, dT = api.moe_fused_bwd(dev(r.dY), dev(r.x), dev(r.W), sch)
+        gs = api.moe_build_schedule(dev(g.expert_ids), dev(g.topk_weights), g.E)
+        gy, gh = api.moe_gated_ffn_fwd(dev(g.x), dev(g.W_gu), dev(g.W_down), gs)
+        torch.cuda.synchronize()
+    finally:
+        api.moe_set_tile_rows(0)
+    assert_close(host(y), O.moe_forward(r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E),
+                 "bf16", "y")
+    rx, rW, rt = O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+    assert_close(host(dX), rx, "bf16", "dX")
+    assert_close(host(dW), rW, "bf16", "dW")
+    assert_close(host(dT), rt, "bf16", "d_topk")
+    assert_close(host(gy), O.gated_ffn_forward(g.x.values, g.W_gu.values, g.W_down.values,
+                                               g.expert_ids, g.topk_weights, g.E), "bf16", "gated y")
+
+
+def test_wrong_outputs_are_rejected_before_launch():
+    r = _small(seed=47)
+    sch = api.moe_build_schedule(dev(r.expert_ids), dev(r.topk_weights), r.E)
+    x, W, dY = dev(r.x), dev(r.W), dev(r.dY)
+    with pytest.raises(ValueError):
+        api.moe_fused_fwd(x, W, sch, y=torch.empty((r.T, r.N - 1), device="cuda"))
+    with pytest.raises(ValueError):
+        api.moe_fused_bwd(dY, x, W, sch, out_dX=torch.empty((r.T - 1, r.K), device="cuda"))
+    with pytest.raises(TypeError):
+        api.moe_fused_bwd(dY, x, W, sch, out_dW=torch.empty((r.E, r.N, r.K), device="cuda"))
+    with pytest.raises(ValueError):
+        api.moe_fused_bwd(dY, x, W, sch, out_dtopk=torch.empty((r.T, r.k + 1), device="cuda"))
+    with pytest.raises(ValueError):
+        api.grouped_gemm(x, W, torch.tensor([r.T] * r.E, dtype=torch.int32, device="cuda"),
+                         out=torch.empty((r.T, 3), dtype=torch.bfloat16, device="cuda"))

@@ -172,7 +172,11 @@ def _mx_first_block_scale(q, scales):
     return _ORIG["mx_values"](q, np.repeat(sc[..., :1], sc.shape[-1], axis=-1))   # one scale per row
 
 
-_ORIG = {n: getattr(O, n) for n in ["mx_values", "routing_schedule", "tile_owner", "tile_coords", "moe_forward",
+def _mx_masked_no_weight_scales(xq, x_bs, Wq, w_bs, ms, T, *, acc=np.float64):
+    return O.masked_forward(O.mx_values(xq, x_bs), O.decode_e4m3(Wq), ms, T, acc=acc)
+
+
+_ORIG = {n: getattr(O, n) for n in ["masked_forward_mx", "mx_values", "routing_schedule", "tile_owner", "tile_coords", "moe_forward",
                                      "grouped_gemm", "moe_backward", "gated_activation",
                                      "gated_ffn_forward", "decode_e4m3", "moe_forward_fp8",
                                      "gated_ffn_backward"]}
@@ -219,6 +223,9 @@ CASES = [
      [P.test_gated_backward_finite_differences, P.test_gated_backward_identities]),
     ("block scales collapsed to one per row", "mx_values", lambda: _mx_first_block_scale,
      [P.test_mx_forward_brute_force_and_block_structure]),
+    ("masked block-scaled forward without the weight block scales", "masked_forward_mx",
+     lambda: _mx_masked_no_weight_scales,
+     [P.test_mx_masked_equals_contiguous, P.test_mx_masked_overflow_brute_force]),
     ("fp8 channel scale collapsed to one per expert", "moe_forward_fp8",
      lambda: _fp8_channel_scale_on_rows,
      [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),

@@ -792,3 +792,70 @@ def test_mx_forward_brute_force_and_block_structure():
     only0[:, 1] = 0                     # 2^-127: block 1 contributes nothing measurable
     y0 = O.moe_forward_mx(xq, only0, Wq, ws, ids, w, E)
     assert np.allclose(y2 - y0, 8 * (y - y0), rtol=1e-12, atol=1e-12)
+
+
+def test_mx_masked_equals_contiguous():
+    """Masked layout with room for every assignment: the block-scaled decode
+    forward equals the contiguous block-scaled forward ("Grouped GEMM" notes,
+    section 5: the two layouts hold the same rows)."""
+    rng, xq, Wq, ids, w = _tiny_fp8(85, T=20, K=64, N=7, E=5, k=3)
+    T, K = xq.shape
+    E, N, _ = Wq.shape
+    xs = rng.integers(118, 136, size=(T, K // 32)).astype(np.uint8)
+    ws = rng.integers(118, 136, size=(E, N, K // 32)).astype(np.uint8)
+    ms = O.masked_schedule(ids, w, E, capacity=T)
+    a = O.masked_forward_mx(xq, xs, Wq, ws, ms, T)
+    b = O.moe_forward_mx(xq, xs, Wq, ws, ids, w, E)
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-13)
+
+
+def test_mx_masked_overflow_brute_force():
+    """Masked block-scaled forward with a capacity below the busiest expert's
+    load, against plain loops: per expert, the assignments taken in ascending
+    s = t*k + j keep a slot while fewer than `capacity` came before them; each
+    kept one adds w * sum over 32-element blocks of (block scales) x (decoded
+    code products) to its token's row; dropped ones add nothing."""
+    import torch
+    rng, xq, Wq, ids, w = _tiny_fp8(86, T=14, K=64, N=4, E=3, k=2)
+    T, K = xq.shape
+    E, N, _ = Wq.shape
+    cap = 5
+    xs = rng.integers(120, 134, size=(T, K // 32)).astype(np.uint8)
+    ws = rng.integers(120, 134, size=(E, N, K // 32)).astype(np.uint8)
+    dec = lambda a: torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    xv, Wv = dec(xq), dec(Wq)
+    seen = [0] * E
+    ref = np.zeros((T, N))
+    dropped = 0
+    for t in range(T):
+        for j in range(2):
+            e = int(ids[t, j])
+            if seen[e] >= cap:
+                dropped += 1
+                continue
+            seen[e] += 1
+            for n in range(N):
+                tot = 0.0
+                for b in range(K // 32):
+                    sc = 2.0 ** (int(xs[t, b]) - 127) * 2.0 ** (int(ws[e, n, b]) - 127)
+                    tot += sc * sum(float(xv[t, c]) * float(Wv[e, n, c]) for c in range(32 * b, 32 * b + 32))
+                ref[t, n] += w[t, j] * tot
+    assert dropped > 0, "the case must overflow"
+    ms = O.masked_schedule(ids, w, E, capacity=cap)
+    y = O.masked_forward_mx(xq, xs, Wq, ws, ms, T)
+    assert np.abs(y - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_backward_selected_experts_match_full():
+    """The per-expert weight gradients of moe_backward's dw_experts form are
+    the same numbers as its full form (the same loop, dW kept for the listed
+    experts only); an expert with no rows gives exact zeros."""
+    rng = np.random.default_rng(97)
+    T, K, N, E, k = 13, 7, 5, 4, 2
+    ids = np.array([rng.choice([0, 1, 3], size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    x, W, dY = rng.standard_normal((T, K)), rng.standard_normal((E, N, K)), rng.standard_normal((T, N))
+    w = rng.random((T, k))
+    dX, dW, dw = O.moe_backward(dY, x, W, ids, w, E)
+    dX2, dWs, dw2 = O.moe_backward(dY, x, W, ids, w, E, dw_experts=[3, 2])
+    assert np.array_equal(dX, dX2) and np.array_equal(dw, dw2)
+    assert set(dWs) == {2, 3} and np.array_equal(dWs[3], dW[3]) and np.all(dWs[2] == 0)
