@@ -103,6 +103,29 @@ typedef struct moe_schedule {
                              were given), 0 for an empty row                    */
   int32_t *status;        /* [2]  {#assignments with expert id outside [0, E),
                                    #assignments dropped over capacity}          */
+  /* Rank-ordered view (contiguous layout, k <= 8 and k*E <= 1024; otherwise
+   * phases = 0 and the pointers are NULL).  The rank of an assignment is the
+   * number of valid assignments of the same token in earlier slots; the rows
+   * are sorted stably by (rank, expert), so for each rank p the rows of rank p
+   * form E consecutive groups (group p*E + e: rank p routed to expert e) and
+   * every token has at most one row of each rank.  A token with no valid
+   * assignment has one row of rank 0 in expert 0's group, with weight 0 and
+   * assignment -1, so every token has exactly one rank-0 row.  The fused
+   * kernels use it to combine the k contributions to an output row without
+   * atomics: rank 0 stores, rank p > 0 adds to what ranks < p wrote. */
+  int32_t phases;              /* k when built, else 0                           */
+  int32_t *phase_counts;       /* [k*E] rows of each (rank, expert) group        */
+  int32_t *phase_offsets;      /* [k*E] END offsets of those groups              */
+  int32_t *phase_block_start;  /* [MOE_NUM_BM][k*E+1] their row-block prefixes  */
+  int32_t *phase_row_to_assign;/* [S]  assignment of each row, or -1            */
+  int32_t *phase_row_to_token; /* [S]  token of each row, or -1 past the end    */
+  float *phase_row_weight;     /* [S]  routing weight (1 without weights; 0 for
+                                  the row of a token with no valid assignment)  */
+  int32_t *phase_sync;         /* [8*64 + 2] completion counters of the ranked
+                                  combine (zeroed by the build, left zeroed by
+                                  each ranked launch); word 8*64 + 1 counts
+                                  waits that gave up (0 unless a ranked launch
+                                  did not get every compute unit)               */
 } moe_schedule;
 
 /* Bytes of device workspace moe_build_schedule needs (256-byte aligned
@@ -322,6 +345,35 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN,
  * do not depend on the setting beyond floating-point summation order.
  */
 int moe_set_tile_rows(int32_t rows);
+
+/*
+ * How the fused forward and the input gradient combine the k contributions to
+ * a token's output row (a process-wide setting read at each call):
+ *   MOE_COMBINE_AUTO   (default) chosen per call from the sizes alone;
+ *   MOE_COMBINE_ATOMIC the output is zeroed, then one launch adds every
+ *                      routing-weighted product into it atomically ([CARD]
+ *                      "How it works": scatter-combine on store);
+ *   MOE_COMBINE_RANKED one launch over the schedule's rank-ordered view (see
+ *                      moe_schedule), tiles in rank order: rank 0 stores
+ *                      w * product, rank p adds w * product to what ranks < p
+ *                      stored, with plain loads and stores (a rank holds at
+ *                      most one row per token); no zero fill and no atomics.
+ *                      Used only where the schedule has the view (phases > 0)
+ *                      and the matrix-core path runs; otherwise atomic.
+ * The ranked combine is one launch over all ranks: a tile of rank p > 0 waits
+ * (in the device) until every rank p-1 tile of its output column block has
+ * stored, so launches that use the same schedule's rank-ordered view must not
+ * run concurrently (its completion counters live in the schedule).  It needs
+ * every compute unit for its persistent workgroups; a wait that does not end
+ * within about half a second gives up and is counted in phase_sync (results
+ * are then wrong, the call still returns).  Output column blocks (256 wide)
+ * at most 64.  The fp32 sum for a token follows rank order (deterministic).
+ * Returns MOE_ERR_SHAPE for an unknown mode.
+ */
+#define MOE_COMBINE_AUTO 0
+#define MOE_COMBINE_ATOMIC 1
+#define MOE_COMBINE_RANKED 2
+int moe_set_combine(int32_t mode);
 
 /*
  * Kernel timing for benchmarks.  While enabled, the library brackets every

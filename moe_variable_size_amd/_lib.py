@@ -19,6 +19,9 @@ MOE_LAYOUT_CONTIGUOUS = 0
 MOE_LAYOUT_MASKED = 1
 MOE_NUM_BM = 4
 BM_VALUES = (32, 64, 128, 256)
+MOE_COMBINE_AUTO = 0
+MOE_COMBINE_ATOMIC = 1
+MOE_COMBINE_RANKED = 2
 
 
 class MoeSchedule(ctypes.Structure):
@@ -40,6 +43,14 @@ class MoeSchedule(ctypes.Structure):
         ("row_to_token", ctypes.c_void_p),
         ("row_weight", ctypes.c_void_p),
         ("status", ctypes.c_void_p),
+        ("phases", ctypes.c_int32),
+        ("phase_counts", ctypes.c_void_p),
+        ("phase_offsets", ctypes.c_void_p),
+        ("phase_block_start", ctypes.c_void_p),
+        ("phase_row_to_assign", ctypes.c_void_p),
+        ("phase_row_to_token", ctypes.c_void_p),
+        ("phase_row_weight", ctypes.c_void_p),
+        ("phase_sync", ctypes.c_void_p),
     ]
 
 
@@ -64,6 +75,7 @@ SIGNATURES = {
     "moe_fused_bwd": (ctypes.c_int, [_P, _P, _P, _SCHED_P, _P, _P, _P, _I64, _I64, _I32, _P, _SZ, _P]),
     "moe_tile_map": (ctypes.c_int, [_SCHED_P, _I64, _I32, _I32, _P, _P, _P, _I64, _P]),
     "moe_set_tile_rows": (ctypes.c_int, [_I32]),
+    "moe_set_combine": (ctypes.c_int, [_I32]),
     "moe_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "moe_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_int64)]),

@@ -20,6 +20,7 @@ import torch
 
 from . import _lib
 from ._lib import MOE_BF16, MOE_F32, MOE_LAYOUT_CONTIGUOUS, MOE_LAYOUT_MASKED, BM_VALUES
+from ._lib import MOE_COMBINE_AUTO, MOE_COMBINE_ATOMIC, MOE_COMBINE_RANKED
 
 _DTYPES = {torch.float32: MOE_F32, torch.bfloat16: MOE_BF16}
 
@@ -129,6 +130,44 @@ class Schedule:
     @property
     def status(self) -> torch.Tensor:
         return self._view(self.c.status, 2, torch.int32)
+
+    # rank-ordered view (None when the schedule has none)
+    @property
+    def phases(self) -> int:
+        return self.c.phases
+
+    @property
+    def phase_counts(self) -> Optional[torch.Tensor]:
+        return self._view(self.c.phase_counts, self.c.k * self.c.E, torch.int32) if self.c.phases else None
+
+    @property
+    def phase_offsets(self) -> Optional[torch.Tensor]:
+        return self._view(self.c.phase_offsets, self.c.k * self.c.E, torch.int32) if self.c.phases else None
+
+    def phase_block_start(self, BM: int) -> Optional[torch.Tensor]:
+        if not self.c.phases:
+            return None
+        i = BM_VALUES.index(BM)
+        n = self.c.k * self.c.E + 1
+        return self._view(self.c.phase_block_start, 4 * n, torch.int32)[i * n:(i + 1) * n]
+
+    @property
+    def phase_row_to_assign(self) -> Optional[torch.Tensor]:
+        return self._view(self.c.phase_row_to_assign, self.c.S, torch.int32) if self.c.phases else None
+
+    @property
+    def phase_row_to_token(self) -> Optional[torch.Tensor]:
+        return self._view(self.c.phase_row_to_token, self.c.S, torch.int32) if self.c.phases else None
+
+    @property
+    def phase_row_weight(self) -> Optional[torch.Tensor]:
+        return self._view(self.c.phase_row_weight, self.c.S, torch.float32) if self.c.phases else None
+
+    @property
+    def phase_sync(self) -> Optional[torch.Tensor]:
+        """Completion counters of the ranked combine ([8, 64] words, then the
+        finished-workgroup count and the count of waits that gave up)."""
+        return self._view(self.c.phase_sync, 8 * 64 + 2, torch.int32) if self.c.phases else None
 
 
 def moe_schedule_workspace_bytes(T: int, k: int, E: int, layout: int = MOE_LAYOUT_CONTIGUOUS,
@@ -402,6 +441,12 @@ def moe_set_tile_rows(rows: int) -> None:
     """Tile height of the routed kernels: 0 = chosen on the device per launch
     (default), 128 or 256 = forced for every later launch of this process."""
     _lib.check("moe_set_tile_rows", _lib.load().moe_set_tile_rows(int(rows)))
+
+
+def moe_set_combine(mode: int) -> None:
+    """How the fused forward / input gradient combine a token's k contributions:
+    MOE_COMBINE_AUTO (default), MOE_COMBINE_ATOMIC or MOE_COMBINE_RANKED."""
+    _lib.check("moe_set_combine", _lib.load().moe_set_combine(int(mode)))
 
 
 def moe_timing_enable(enable: bool = True) -> None:

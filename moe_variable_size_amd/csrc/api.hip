@@ -8,6 +8,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -41,11 +42,17 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 struct WsLayout {
-  size_t counts, offsets, bstart, order, status, r2a, r2t, rw, scratch, total;
+  size_t counts, offsets, bstart, order, status, r2a, r2t, rw;
+  size_t pcounts, poffsets, pbstart, pr2a, pr2t, prw, psync;  // rank-ordered view (0 sizes if absent)
+  size_t scratch, total;
+  bool ranked;
 };
 
-WsLayout ws_layout(int64_t S, int64_t R, int E) {
+WsLayout ws_layout(int64_t S, int64_t R, int E, int k, int layout) {
   WsLayout l;
+  l.ranked = rank_order_supported(layout, k, E);
+  const int64_t kE = l.ranked ? (int64_t)k * E : 0;
+  const int64_t PR = l.ranked ? S + kRowPad : 0;
   size_t o = 0;
   l.counts = o;  o = align256(o + sizeof(int32_t) * E);
   l.offsets = o; o = align256(o + sizeof(int32_t) * E);
@@ -57,7 +64,14 @@ WsLayout ws_layout(int64_t S, int64_t R, int E) {
   l.r2a = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
   l.r2t = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
   l.rw = o;      o = align256(o + sizeof(float) * (R + kRowPad));
-  l.scratch = o; o = align256(o + schedule_scratch_bytes(S, E));  // builder's block table
+  l.pcounts = o;  o = align256(o + sizeof(int32_t) * kE);
+  l.poffsets = o; o = align256(o + sizeof(int32_t) * kE);
+  l.pbstart = o;  o = align256(o + sizeof(int32_t) * (l.ranked ? MOE_NUM_BM * (kE + 1) : 0));
+  l.pr2a = o;     o = align256(o + sizeof(int32_t) * PR);
+  l.pr2t = o;     o = align256(o + sizeof(int32_t) * PR);
+  l.prw = o;      o = align256(o + sizeof(float) * PR);
+  l.psync = o;    o = align256(o + sizeof(int32_t) * (l.ranked ? kRankSyncInts : 0));
+  l.scratch = o;  o = align256(o + schedule_scratch_bytes(S, E, k, l.ranked));  // block tables
   l.total = o;
   return l;
 }
@@ -86,6 +100,13 @@ int check_sched(const moe_schedule *s) {
   int rc = check_sizes(s->T, s->k, s->E, s->layout, s->capacity, &R);
   if (rc) return rc;
   if (R != s->R || s->S != s->T * s->k) return MOE_ERR_SHAPE;
+  if (s->phases != 0) {
+    if (s->phases != s->k || !rank_order_supported(s->layout, s->k, s->E)) return MOE_ERR_SHAPE;
+    if (!s->phase_counts || !s->phase_offsets || !s->phase_block_start ||
+        !s->phase_row_to_assign || !s->phase_row_to_token || !s->phase_row_weight ||
+        !s->phase_sync)
+      return MOE_ERR_NULL;
+  }
   return MOE_OK;
 }
 
@@ -101,6 +122,25 @@ size_t esize(int32_t dtype) { return dtype == MOE_F32 ? 4 : 2; }
 // byte size of an [rows, cols] tensor must stay below 2^31 (32-bit offsets)
 bool fits(int64_t rows, int64_t cols, int32_t dtype) {
   return (double)rows * (double)cols * (double)esize(dtype) < (double)kMax32;
+}
+
+// ---- combine of the k contributions to an output row -----------------------
+std::atomic<int> g_combine{MOE_COMBINE_AUTO};
+
+// Whether a scattering launch over this schedule uses the ranked combine (one
+// launch over the rank-ordered view: rank 0 stores, later ranks wait for the
+// earlier ones and add; no atomics, no zero fill) rather than atomic adds into
+// a zeroed output.  The automatic choice is the atomic combine except for a
+// forward with one slot per token (k = 1: a single rank, only stores, no
+// waits): measured on MI355X, the waits and read-backs of later ranks cost
+// more than the atomic adds they replace (config 2 forward 105-109 against
+// 104-107 us, input gradient 229-236 against 125-129 us).
+bool use_ranked(const moe_schedule &s, int64_t out_cols, bool input_grad) {
+  if (s.phases == 0 || (out_cols + 255) / 256 > kRankSyncCols) return false;
+  const int mode = g_combine.load(std::memory_order_relaxed);
+  if (mode == MOE_COMBINE_ATOMIC) return false;
+  if (mode == MOE_COMBINE_RANKED) return true;
+  return !input_grad && s.k == 1;
 }
 
 // ---- kernel timing (benchmarks only) ---------------------------------------
@@ -171,7 +211,7 @@ size_t moe_schedule_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t lay
                                     int32_t capacity) {
   int64_t R = 0;
   if (check_sizes(T, k, E, layout, capacity, &R)) return 0;
-  return ws_layout(T * k, R, E).total;
+  return ws_layout(T * k, R, E, k, layout).total;
 }
 
 int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T, int32_t k,
@@ -182,7 +222,7 @@ int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int
   int rc = check_sizes(T, k, E, layout, capacity, &R);
   if (rc) return rc;
   if (!aligned(expert_ids, 4) || (topk_weights && !aligned(topk_weights, 4))) return MOE_ERR_ALIGN;
-  const WsLayout l = ws_layout(T * k, R, E);
+  const WsLayout l = ws_layout(T * k, R, E, k, layout);
   if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
   char *w = (char *)workspace;
@@ -203,6 +243,16 @@ int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int
   s.row_to_assign = (int32_t *)(w + l.r2a);
   s.row_to_token = (int32_t *)(w + l.r2t);
   s.row_weight = (float *)(w + l.rw);
+  if (l.ranked) {
+    s.phases = k;
+    s.phase_counts = (int32_t *)(w + l.pcounts);
+    s.phase_offsets = (int32_t *)(w + l.poffsets);
+    s.phase_block_start = (int32_t *)(w + l.pbstart);
+    s.phase_row_to_assign = (int32_t *)(w + l.pr2a);
+    s.phase_row_to_token = (int32_t *)(w + l.pr2t);
+    s.phase_row_weight = (float *)(w + l.prw);
+    s.phase_sync = (int32_t *)(w + l.psync);
+  }
   *sched = s;
   hipStream_t st = (hipStream_t)stream;
   return hip_status(
@@ -246,13 +296,16 @@ int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float
   const size_t al = dtype == MOE_BF16 ? 16 : 4;
   if (!aligned(x, al) || !aligned(W, al) || !aligned(y, 4)) return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e =
-      timed(F_FILL, st,
-            [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  const bool mfma = dtype == MOE_BF16 && mfma_supported((int)K, (int)N);
+  const bool ranked = mfma && use_ranked(s, N, false);
+  if (!ranked) {
+    hipError_t e = timed(F_FILL, st, [&] {
+      return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   return hip_status(timed(F_FWD, st, [&] {
-    if (dtype == MOE_BF16 && mfma_supported((int)K, (int)N))
-      return mfma_fused_fwd(x, W, s, y, (int)K, (int)N, false, st);
+    if (mfma) return mfma_fused_fwd(x, W, s, y, (int)K, (int)N, false, ranked, st);
     return simt_fused_fwd(x, W, s, y, (int)K, (int)N, dtype, st);
   }));
 }
@@ -273,12 +326,15 @@ int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
       !aligned(y, 4))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e =
-      timed(F_FILL, st,
-            [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  const bool ranked = use_ranked(s, N, false);
+  if (!ranked) {
+    hipError_t e = timed(F_FILL, st, [&] {
+      return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   return hip_status(timed(F_FWD_FP8, st, [&] {
-    return mfma_fused_fwd_fp8(x_q, x_scale, W_q, w_scale, s, y, (int)K, (int)N, st);
+    return mfma_fused_fwd_fp8(x_q, x_scale, W_q, w_scale, s, y, (int)K, (int)N, ranked, st);
   }));
 }
 
@@ -297,12 +353,15 @@ int moe_fused_fwd_mx(const void *x_q, const uint8_t *x_bs, const void *W_q, cons
       !aligned(y, 4))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e =
-      timed(F_FILL, st,
-            [&] { return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st); });
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  const bool ranked = use_ranked(s, N, false);
+  if (!ranked) {
+    hipError_t e = timed(F_FILL, st, [&] {
+      return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
+    });
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   return hip_status(timed(F_FWD_MX, st, [&] {
-    return mfma_fused_fwd_mx(x_q, x_bs, W_q, w_bs, s, y, (int)K, (int)N, st);
+    return mfma_fused_fwd_mx(x_q, x_bs, W_q, w_bs, s, y, (int)K, (int)N, ranked, st);
   }));
 }
 
@@ -337,7 +396,7 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
     });
   if (e == hipSuccess)
     e = timed(F_GATED_DOWN, st, [&] {
-      return mfma_fused_fwd(h, W_down, s, y, (int)F, (int)N, true, st);
+      return mfma_fused_fwd(h, W_down, s, y, (int)F, (int)N, true, false, st);
     });
   return hip_status(e);
 }
@@ -436,19 +495,26 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
   hipError_t e = hipSuccess;
   const size_t dx_bytes = dX ? (size_t)s.T * K * sizeof(float) : 0;
   const size_t dt_bytes = d_topk ? (size_t)s.S * sizeof(float) : 0;
-  // On the matrix-core path the weight gradient runs first and zeroes dX and
-  // d_topk on the side (it reads neither); the kernel boundary orders those
-  // stores before the input-gradient kernel's atomics.  Otherwise one fill.
+  // With the ranked combine the input-gradient launches store dX (rank 0) and
+  // add to it (later ranks), so only d_topk (atomic partial sums over column
+  // blocks) needs zeros.  On the matrix-core path the weight gradient runs
+  // first and writes those zeros on the side (it reads neither); the kernel
+  // boundary orders them before the input-gradient kernel.  Otherwise one fill.
+  const bool ranked = mfma && (dX || d_topk) && use_ranked(s, K, true);
+  const size_t dxz_bytes = ranked ? 0 : dx_bytes;
   const bool dw_first = mfma && dW != nullptr;
   if (dw_first)
     e = timed(F_DW, st, [&] {
-      return mfma_bwd_dw(dY, x, s, dW, (int)K, (int)N, dX, dx_bytes, d_topk, dt_bytes, st);
+      return mfma_bwd_dw(dY, x, s, dW, (int)K, (int)N, dxz_bytes ? dX : nullptr, dxz_bytes,
+                         d_topk, dt_bytes, st);
     });
-  else if (dX || d_topk)
-    e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, dx_bytes, d_topk, dt_bytes, st); });
+  else if (dxz_bytes || dt_bytes)
+    e = timed(F_FILL, st, [&] {
+      return launch_fill_zero(dxz_bytes ? dX : nullptr, dxz_bytes, d_topk, dt_bytes, st);
+    });
   if (e == hipSuccess && (dX || d_topk))
     e = timed(F_DX, st, [&] {
-      return mfma ? mfma_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, st)
+      return mfma ? mfma_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, ranked, st)
                   : simt_bwd_dx(dY, x, W, s, dX, d_topk, (int)K, (int)N, dtype, st);
     });
   if (e == hipSuccess && dW && !dw_first)
@@ -469,6 +535,13 @@ int moe_tile_map(const moe_schedule *sched, int64_t N, int32_t BM, int32_t BN, i
 }
 
 int moe_set_tile_rows(int32_t rows) { return set_tile_rows(rows); }
+
+int moe_set_combine(int32_t mode) {
+  if (mode != MOE_COMBINE_AUTO && mode != MOE_COMBINE_ATOMIC && mode != MOE_COMBINE_RANKED)
+    return MOE_ERR_SHAPE;
+  g_combine.store(mode, std::memory_order_relaxed);
+  return MOE_OK;
+}
 
 int moe_timing_enable(int enable) {
   Timing &t = timing();

@@ -15,6 +15,12 @@ typedef uint16_t bf16_t;  // raw bfloat16 bit pattern
 constexpr int kWave = 64;            // CDNA wavefront width
 constexpr int kMaxExperts = 1024;    // E limit (LDS-resident per-expert tables)
 constexpr int kRowPad = 64;          // spare entries after each schedule row array
+constexpr int kMaxRankK = 8;         // rank-ordered view: at most this many slots per token
+constexpr int kMaxRankKeys = 1024;   // ... and k * E groups
+// completion counters of the ranked combine: [kMaxRankK][kRankSyncCols] words,
+// then a finished-workgroup count and a count of waits that gave up
+constexpr int kRankSyncCols = 64;    // at most 64 output column blocks of 256
+constexpr int kRankSyncInts = kMaxRankK * kRankSyncCols + 2;
 constexpr int kBmValues[MOE_NUM_BM] = {32, 64, 128, 256};
 
 MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
@@ -67,11 +73,13 @@ struct LaunchCtx {
 };
 int device_cu_count();
 
-// scratch: schedule_scratch_bytes(S, E) bytes of device memory (part of the
-// caller's schedule workspace)
+// scratch: schedule_scratch_bytes(S, E, k, s.phases > 0) bytes of device
+// memory (part of the caller's schedule workspace)
 hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_schedule &s,
                                  int32_t *scratch, hipStream_t st);
-size_t schedule_scratch_bytes(int64_t S, int E);
+size_t schedule_scratch_bytes(int64_t S, int E, int k, bool ranked);
+// whether the schedule also gets the rank-ordered row view (one phase per rank)
+bool rank_order_supported(int layout, int k, int E);
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,
                            int32_t *total, int32_t *owner, int64_t owner_cap, hipStream_t st);
 // zero [p, p + bytes) and [p2, p2 + bytes2) in one launch (either pointer may be
@@ -98,24 +106,28 @@ hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offset
                              int M, int K, int N, int E, int out_dtype, hipStream_t st);
 // a_by_row: the A operand is already in schedule row order ([R, K]) instead of
 // being gathered from x [T, K] by token
+// ranked: one launch over the schedule's rank-ordered view whose rank-0 tiles
+// store and whose later ranks add in rank order (no atomics, y need not be
+// zeroed); otherwise one launch adding atomically into a zeroed y
 hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
-                          int N, bool a_by_row, hipStream_t st);
+                          int N, bool a_by_row, bool ranked, hipStream_t st);
 // 8-bit (E4M3) operands: y[t] += w * x_scale[t] * w_scale[e, n] * (xq[t] . Wq[e, n]);
 // K a multiple of 16 (16-byte rows)
 hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *Wq,
                               const float *w_scale, const moe_schedule &s, float *y, int K, int N,
-                              hipStream_t st);
+                              bool ranked, hipStream_t st);
 // 8-bit (E4M3) operands with E8M0 block scales per 32 reduction elements:
 // x_bs [T, K/32], w_bs [E, N, K/32]; K a multiple of 128
 hipError_t mfma_fused_fwd_mx(const void *xq, const uint8_t *x_bs, const void *Wq,
                              const uint8_t *w_bs, const moe_schedule &s, float *y, int K, int N,
-                             hipStream_t st);
+                             bool ranked, hipStream_t st);
 // h [R, F] bf16 = silu(x W_gate^T) * (x W_up^T) per schedule row; W_gu [E, 2F, K]
 // gu (optional, NULL to skip): [R, 2F] fp32 gate and up values kept for a backward
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,
                          int K, int F, hipStream_t st);
+// ranked: as for mfma_fused_fwd (dX need not be zeroed; d_w must be)
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
-                       float *dX, float *d_w, int K, int N, hipStream_t st);
+                       float *dX, float *d_w, int K, int N, bool ranked, hipStream_t st);
 // zero0 / zero1: byte ranges the kernel zeroes on the side (NULL / 0 when unused)
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
                        int N, float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
@@ -208,8 +220,11 @@ MOE_DEV void group_tables_from_schedule(const int32_t *__restrict__ counts,
                                         const int32_t *__restrict__ offsets,
                                         const int32_t *__restrict__ bstart, int E, int layout,
                                         int capacity, int *bs, int *rstart, int *rcnt) {
+  // bstart may be a window of a longer prefix (one rank's groups of the
+  // rank-ordered view): entries are taken relative to its first
+  const int b0 = bstart[0];
   for (int e = threadIdx.x; e <= E; e += NT) {
-    bs[e] = bstart[e];
+    bs[e] = bstart[e] - b0;
     if (e < E) {
       const int c = counts[e];
       rcnt[e] = c;
@@ -239,6 +254,12 @@ MOE_DEV TileCoord tile_coord(const int *bs, const int *rstart, const int *rcnt, 
   c.mb = local - c.nb * mblocks;
   c.row0 = rstart[c.g] + c.mb * BM;
   c.rows = min(BM, rcnt[c.g] - c.mb * BM);
+  // the same for every lane (tau is): keep the coordinates in scalar registers
+  c.g = __builtin_amdgcn_readfirstlane(c.g);
+  c.mb = __builtin_amdgcn_readfirstlane(c.mb);
+  c.nb = __builtin_amdgcn_readfirstlane(c.nb);
+  c.row0 = __builtin_amdgcn_readfirstlane(c.row0);
+  c.rows = __builtin_amdgcn_readfirstlane(c.rows);
   return c;
 }
 

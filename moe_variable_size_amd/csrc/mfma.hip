@@ -217,9 +217,12 @@ struct WorkSplit {
   bool piece_done;
   int s, nS;  // sub-tile of the current piece (0 of 1 for a whole tile)
   enum { WHOLE = 0, SUBTILE_TAIL = 1 };
-  MOE_DEV void init(int total, int G_, int Lb_, int mode, int max_split = 8) {
+  bool pieces_last;  // the piece after the whole tiles (tiles in increasing order)
+  MOE_DEV void init(int total, int G_, int Lb_, int mode, int max_split = 8,
+                    bool pieces_last_ = false) {
     G = G_;
     Lb = Lb_;
+    pieces_last = pieces_last_;
     s = 0;
     nS = 1;
     full = (total / G) * G;
@@ -237,14 +240,15 @@ struct WorkSplit {
   MOE_DEV bool next(int &tau) {
     // a workgroup's piece of the last round comes first: its few atomics
     // drain while the whole tiles multiply, instead of queueing behind them
-    if (!piece_done && Lb < pieces) {
+    // (with pieces_last, after them: tiles then run in increasing index order)
+    if (!piece_done && Lb < pieces && (!pieces_last || next_tile >= full)) {
       piece_done = true;
       tau = full + Lb / S;
       s = Lb % S;
       nS = S;
       return true;
     }
-    piece_done = true;
+    if (!pieces_last) piece_done = true;
     if (next_tile < full) {
       tau = next_tile;
       next_tile += G;
@@ -277,10 +281,16 @@ MOE_DEV SubTile sub_tile(int s, int nS) {
 // closer than 0.75 the 256-row tiles still won (their last round splits
 // better).  Every workgroup reads the same totals and takes the same decision.
 // forced = 128 or 256 overrides the estimate.
-MOE_DEV int pick_tile_rows(const int32_t *bstart_all, int E, int tiles_n, int G, int forced) {
+// bstart_all: the prefixes of the launch's E groups for each tile height,
+// `stride` ints apart (a window of the rank-ordered view's longer prefixes is
+// read relative to its first entry).
+MOE_DEV int pick_tile_rows(const int32_t *bstart_all, int stride, int E, int tiles_n, int G,
+                           int forced) {
   if (forced == 128 || forced == 256) return forced;
-  const float r256 = (float)bstart_all[bm_index(256) * (E + 1) + E] * tiles_n / G;
-  const float r128 = (float)bstart_all[bm_index(128) * (E + 1) + E] * tiles_n / G;
+  const int32_t *b256 = bstart_all + bm_index(256) * stride;
+  const int32_t *b128 = bstart_all + bm_index(128) * stride;
+  const float r256 = (float)(b256[E] - b256[0]) * tiles_n / G;
+  const float r128 = (float)(b128[E] - b128[0]) * tiles_n / G;
   return __builtin_amdgcn_readfirstlane(0.75f * fmaxf(r128, 1.f) < fmaxf(r256, 1.f) ? 128 : 256);
 }
 
@@ -748,6 +758,10 @@ struct FwdArgs {
   uint32_t a_bytes;  // bytes of A (x or the bare A)
   int M;             // bare: rows of A and C (rows at or past M are never touched)
   int tile_rows;     // routed, BM = 256: 0 = picked on the device, 128 / 256 = forced
+  int bstride;       // routed: ints between the row-block prefixes of two tile heights
+  int combine;       // routed scatter: COMBINE_ATOMIC or COMBINE_RANKED
+  int nranks;        // COMBINE_RANKED: ranks of the view (the launch has nranks * E groups)
+  int32_t *sync;     // COMBINE_RANKED: completion counters
   const float *x_scale;  // 8-bit operands: per-token scale [T]
   const float *w_scale;  // 8-bit operands: per-expert output-channel scale [E, N]
   float *gu_out;         // gated: [R, 2F] gate and up values (fp32) kept for a backward, or NULL
@@ -766,6 +780,80 @@ struct FwdArgs {
 //   FWD_SCATTER_ROWS  as FWD_SCATTER with A already in schedule row order (A row
 //               r is row r: the gated FFN's intermediate), nothing gathered
 enum { FWD_BARE = 0, FWD_SCATTER = 1, FWD_GATED = 2, FWD_SCATTER_ROWS = 3 };
+
+// How a scattering kernel combines its results into the output rows:
+//   COMBINE_ATOMIC  atomic adds into a zeroed output (canonical schedule);
+//   COMBINE_RANKED  one launch over the k*E groups of the rank-ordered view,
+//                   tiles in rank order: rank 0 stores, a tile of rank p > 0
+//                   waits until every rank p-1 tile of its column block has
+//                   stored, then reads, adds and stores (each rank holds a
+//                   token at most once, so no element has two writers at once).
+enum { COMBINE_ATOMIC = 0, COMBINE_RANKED = 1 };
+
+// ---- rank-ordered combine: completion counters --------------------------------
+// sync (the schedule's phase_sync words): [kMaxRankK][kSyncCols] completed work
+// per (rank, column block) in eighths of a tile, then the number of finished
+// workgroups of the launch, then the number of waits that gave up.  Zero
+// before a launch; the launch's last workgroup zeroes the counters again.
+constexpr int kSyncCols = kRankSyncCols;
+constexpr int kSyncFin = kMaxRankK * kSyncCols;
+constexpr int kSyncFlag = kSyncFin + 1;
+static_assert(kSyncFlag + 1 == kRankSyncInts, "counter layout");
+// a wait gives up (and counts itself in the flag word) after this many sleeps
+// of ~256 clocks, ~0.5 s: every workgroup is resident (one per compute unit),
+// so a wait that long means the launch did not get the whole device
+constexpr int kSpinLimit = 1 << 21;
+
+// Stores and loads that other XCDs see within the launch: device scope, which
+// on gfx950 writes through / reads past the XCD's own L2.
+MOE_DEV void store_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// As dma16, device-scope (coherent) read.
+MOE_DEV void dma16_coherent(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen sc1 lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// Whole workgroup: wait until *ctr >= need (thread 0 polls, then a barrier).
+MOE_DEV void wait_count(int32_t *sync, int idx, int need) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(sync + idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+      __builtin_amdgcn_s_sleep(4);
+      if (++spins > kSpinLimit) {
+        __hip_atomic_fetch_add(sync + kSyncFlag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+// Whole workgroup, after its coherent stores of a tile: every wave waits for
+// them to complete, then thread 0 adds `amount` to the tile's counter.
+MOE_DEV void count_done(int32_t *sync, int idx, int amount) {
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sync + idx, amount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Whole workgroup, at the end of a ranked launch: the last workgroup to get
+// here (every other one is past all its waits) zeroes the counters.
+MOE_DEV void finish_ranked(int32_t *sync, int nranks) {
+  __syncthreads();
+  __shared__ int last;
+  if (threadIdx.x == 0)
+    last = __hip_atomic_fetch_add(sync + kSyncFin, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+           (int)gridDim.x - 1;
+  __syncthreads();
+  if (last) {
+    for (int i = threadIdx.x; i < nranks * kSyncCols; i += blockDim.x)
+      __hip_atomic_store(sync + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(sync + kSyncFin, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
 
 // F8: 8-bit operands (a stage is 128 reduction elements; K below is the
 // reduction length in 2-byte units, i.e. row bytes / 2, for the bounds checks).
@@ -877,7 +965,7 @@ struct FwdDeepOp {
 };
 
 template <int BM, int BN, int WGM, int WGN, int MODE, typename Tout, bool F8 = false,
-          bool MX = false>
+          bool MX = false, int COMB = COMBINE_ATOMIC>
 __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   constexpr bool FUSED = MODE != FWD_BARE;       // rows come from a routing schedule
   constexpr bool GATED = MODE == FWD_GATED;
@@ -910,15 +998,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   // double-buffered 32-byte fragments does not fit the registers of 8 waves
   // per compute unit (4 waves, one per SIMD, have twice the registers).
   constexpr bool F8_HALF = F8 && NW == 8;
+  // COMBINE_RANKED: the launch's groups are the nranks * E (rank, expert)
+  // groups of the rank-ordered view, group g using expert g % E's weights
+  constexpr bool RK = COMB == COMBINE_RANKED;
+  const int GE = RK ? p.nranks * E : E;
   const int BMr = (FUSED && BM == 256)
-                      ? (F8_HALF ? 128 : pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows))
+                      ? (F8_HALF ? 128
+                                 : pick_tile_rows(p.bstart, p.bstride, GE, tiles_n, gridDim.x,
+                                                  p.tile_rows))
                       : BM;
   if (FUSED)
-    group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * (E + 1), E,
+    group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * p.bstride, GE,
                                     p.layout, p.capacity, bs, rstart, rcnt);
   else
     group_tables_from_offsets<NTH>(p.offsets, E, BM, bs, rstart, rcnt, scratch);
-  const int total = bs[E] * tiles_n;
+  const int total = bs[GE] * tiles_n;
   FwdOp<BM, BN, NW, F8, MX> op;
   op.rsA = uniform_rsrc(p.A, p.a_bytes);
   op.lds0 = lds_addr(lds);
@@ -935,12 +1029,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
   WorkSplit ws;
   // gated tiles split along rows only (a column split would part gate from up);
   // 128-row tiles split at most 4 ways (64 x 128)
+  // (ranked: tiles in increasing order, so a workgroup finishes its rank p
+  // work before it waits in a rank p+1 tile)
   ws.init(total, gridDim.x, Lb, BM == 256 ? WorkSplit::SUBTILE_TAIL : WorkSplit::WHOLE,
-          GATED ? (BMr == BM ? 2 : 1) : (BMr == BM ? 8 : 4));
+          GATED ? (BMr == BM ? 2 : 1) : (BMr == BM ? 8 : 4), RK);
   int tau;
   const int kb = 0, ke = KI;
   while (ws.next(tau)) {
-    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BMr);
+    TileCoord c = tile_coord(bs, rstart, rcnt, GE, tau, tiles_n, BMr);
+    const int ge = RK ? c.g % E : c.g;   // the expert whose weights the tile uses
+    const int rank = RK ? c.g / E : 0;
     int n0 = c.nb * BNO, ncols = min(BNO, N - n0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
       const SubTile st = BMr == 128 ? sub_tile128(ws.s, ws.nS) : sub_tile(ws.s, ws.nS);
@@ -951,7 +1049,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         ncols = min(st.cols, N - n0);
       }
     }
-    if (c.rows <= 0 || ncols <= 0) continue;
+    if (c.rows <= 0 || ncols <= 0) {
+      // an empty piece still counts as done for the ranks after it
+      if constexpr (RK) count_done(p.sync, rank * kSyncCols + c.nb, 8 / ws.nS);
+      continue;
+    }
     __syncthreads();  // LDS stages and row tables free
     if (tid < BM) {
       const bool ok = tid < c.rows;
@@ -965,14 +1067,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     for (int j = tid; j < BN; j += NTH) {
       const int jj = GATED ? j % BNO : j;  // gated: gate rows, then the up rows
       rowoff_b[j] = jj < ncols ? (n0 + jj + (GATED && j >= BNO ? N : 0)) * (int)rowbytes : -1;
-      if (F8 && !MX) cscale[j] = jj < ncols ? p.w_scale[(size_t)c.g * N + n0 + jj] : 0.f;
+      if (F8 && !MX) cscale[j] = jj < ncols ? p.w_scale[(size_t)ge * N + n0 + jj] : 0.f;
     }
     __syncthreads();
-    op.rsW = uniform_rsrc((const char *)p.W + (size_t)c.g * wrows * rowbytes, wbytes);
+    op.rsW = uniform_rsrc((const char *)p.W + (size_t)ge * wrows * rowbytes, wbytes);
     if constexpr (MX) {
       // per-lane offsets of the scale rows: group grp of 64 rows (A rows, then
       // B rows), lane = row inside the group; dead rows read out of range
-      op.rsWS = uniform_rsrc(p.w_bs + (size_t)c.g * N * kblk, (uint32_t)N * kblk);
+      op.rsWS = uniform_rsrc(p.w_bs + (size_t)ge * N * kblk, (uint32_t)N * kblk);
 #pragma unroll
       for (int i = 0; i < op.DS; ++i) {
         const int grp = wid + i * NW;
@@ -1083,9 +1185,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         return;
       }
       if (FUSED) {
-        // weighted scatter-combine: atomics on y with 32-bit byte offsets from
-        // its base; only live rows and columns are touched (the column test is
-        // left out when every column of the accumulator is live)
+        // weighted scatter-combine on y with 32-bit byte offsets from its
+        // base; only live rows and columns are touched (the column test is
+        // left out when every column of the accumulator is live).
+        //   COMBINE_ATOMIC: atomic adds (any number of rows per token);
+        //   COMBINE_RANKED: the tile's rank holds each token at most once, so
+        //   no other workgroup writes its elements now: rank 0 stores w * acc;
+        //   rank p > 0 waits for rank p-1 of this column block, then stores
+        //   the old value plus w * acc (device-coherent stores and reads).
         char *const yb = (char *)p.C;
         const bool all_cols = ncols >= NIc * 32 * WGN;  // wave-uniform
         uint32_t cb[NIc];
@@ -1096,9 +1203,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         float cs[NIc];  // 8-bit: output-channel scale of each column block
 #pragma unroll
         for (int ni = 0; ni < NIc; ++ni) cs[ni] = F8 && !MX ? cscale[cl0 + ni * 32 * WGN] : 1.f;
-#pragma unroll
-        for (int mi = 0; mi < MIc; ++mi) {
-          if (mi >= live_mi) continue;
+        // one row band (64 rows: 32 per row of waves) of the scatter; ranked:
+        // oldb holds the band's old values in LDS (1 KB per tile row), or is
+        // NULL for rank 0
+        auto band = [&](int mi, const char *oldb) __attribute__((always_inline)) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
@@ -1110,16 +1218,66 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
               const uint32_t ro = (uint32_t)t4[q] * (uint32_t)N * 4u;
 #pragma unroll
               for (int ni = 0; ni < NIc; ++ni) {
-                if (!all_cols && cl0 + ni * 32 * WGN >= ncols) continue;
+                const int cl = cl0 + ni * 32 * WGN;
+                if (!all_cols && cl >= ncols) continue;
                 const float v = F8 && !MX ? w4[q] * cs[ni] * acc[mi][ni][4 * j + q]
                                           : w4[q] * acc[mi][ni][4 * j + q];
-                unsafeAtomicAdd((float *)(yb + (ro + cb[ni])), v);
+                float *const dst = (float *)(yb + (ro + cb[ni]));
+                if constexpr (!RK) {
+                  unsafeAtomicAdd(dst, v);
+                } else {
+                  const int rb = rq + q - mi * 32 * WGM;  // row inside the band
+                  const float o = oldb ? *(const float *)(oldb + rb * 1024 + cl * 4) : 0.f;
+                  store_coherent(dst, __fadd_rn(o, v));
+                }
               }
             }
           }
           __builtin_amdgcn_sched_barrier(0);
+        };
+        if constexpr (!RK || !(BM == 256 && WGM == 2)) {  // (ranked launches use 256-row tiles)
+          unroll<MIc>([&](auto mi_) __attribute__((always_inline)) {
+            if (decltype(mi_)::value < live_mi) band(decltype(mi_)::value, nullptr);
+          });
+          return;
+        } else {
+          // rank p > 0: wait for rank p-1 of this column block (in eighths of
+          // a tile: its row blocks x 8), then its values of two bands at a
+          // time (128 tile rows x 256 columns, 128 KB) go by coherent
+          // global -> LDS DMA into the idle stages, one row (1 KB, 16 bytes
+          // per lane) per instruction; dead rows and columns read out of range
+          if (rank > 0)
+            wait_count(p.sync, (rank - 1) * kSyncCols + c.nb, 8 * (bs[rank * E] - bs[(rank - 1) * E]));
+          const __amdgpu_buffer_rsrc_t rsY =
+              uniform_rsrc(p.C, (uint32_t)((size_t)p.M * (size_t)N * 4u));
+          const uint32_t l0 = lds_addr(lds);
+          constexpr int RPW = 128 / NW;  // rows per wave per half
+          const bool cok = lane * 4 < ncols;
+          unroll<(MIc + 1) / 2>([&](auto h_) __attribute__((always_inline)) {
+            constexpr int h = decltype(h_)::value;
+            if (rank > 0) {
+              barrier();  // every wave done with the LDS (stages or previous half)
+#pragma unroll
+              for (int i = 0; i < RPW; ++i) {
+                const int row = h * 128 + wid * RPW + i;
+                const int t = tok[row];
+                const uint32_t off =
+                    (t >= 0 && cok) ? ((uint32_t)t * (uint32_t)N + (uint32_t)(n0 + lane * 4)) * 4u
+                                    : kOobOffset;
+                dma16_coherent(rsY, off, l0 + (uint32_t)((wid * RPW + i) * 1024));
+              }
+              wait_vmcnt<0>();
+              barrier();
+            }
+            unroll<2>([&](auto m_) __attribute__((always_inline)) {
+              constexpr int m = decltype(m_)::value;
+              if (2 * h + m < MIc && 2 * h + m < live_mi)
+                band(2 * h + m, rank > 0 ? lds + m * 64 * 1024 : nullptr);
+            });
+          });
+          count_done(p.sync, rank * kSyncCols + c.nb, 8 / ws.nS);
+          return;
         }
-        return;
       }
 #pragma unroll
       for (int mi = 0; mi < MIc; ++mi) {
@@ -1153,6 +1311,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     using std::integral_constant;
     using std::false_type;
     using std::true_type;
+    const int nsub = ws.nS;  // row / column pieces of a tail tile
     if constexpr (BM <= 64) {
       tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(), true_type(),
            true_type());
@@ -1160,30 +1319,30 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
       constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
       if constexpr (GATED) {  // whole tiles and 128 x 256 halves only
-        if (ws.nS == 2 || BMr == 128)
+        if (nsub == 2 || BMr == 128)
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
         else
           tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
                false_type(), false_type());
       } else if (BMr == 128) {  // 128 x 256 tiles, split 2 (128 x 128) or 4 (64 x 128)
-        if (ws.nS == 4)
+        if (nsub == 4)
           tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
                true_type(), false_type());
-        else if (ws.nS == 2)
+        else if (nsub == 2)
           tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(),
                true_type(), false_type());
         else
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
       } else if constexpr (!F8_HALF) {
-        if (ws.nS == 8)
+        if (nsub == 8)
           tile(integral_constant<int, R8>(), integral_constant<int, C>(), false_type(),
                true_type(), false_type());
-        else if (ws.nS == 4)
+        else if (nsub == 4)
           tile(integral_constant<int, R4>(), integral_constant<int, C>(), false_type(),
                true_type(), false_type());
-        else if (ws.nS == 2)
+        else if (nsub == 2)
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
         else
@@ -1192,6 +1351,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       }
     }
   }
+  if constexpr (RK) finish_ranked(p.sync, p.nranks);
 }
 
 // ============================================================================
@@ -1220,6 +1380,11 @@ struct DxArgs {
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes;
   int tile_rows;   // 0 = picked on the device, 128 / 256 = forced
+  int bstride;     // ints between the row-block prefixes of two tile heights
+  int combine;     // dX scatter: COMBINE_ATOMIC or COMBINE_RANKED
+  uint32_t dx_bytes;  // bytes of dX (COMBINE_RANKED reads it back)
+  int nranks;         // COMBINE_RANKED: ranks of the view
+  int32_t *sync;      // COMBINE_RANKED: completion counters
   // gated FFN backward (GB kernels): x is h [R, K] read by schedule row, gu the
   // saved gate/up values [R, 2K] (fp32), dgu the output [R, 2K] (bf16; K here is F)
   const float *gu;
@@ -1278,12 +1443,13 @@ struct DxOp {
 // gradient takes h (read by schedule row) where the plain kernel takes x.
 // ROWS: A (dY's place) is already in schedule row order and carries the routing
 // weight (the gated FFN's dgu): read by row, scattered unweighted.
-template <int NW, bool GB = false, bool ROWS = false>
+template <int NW, bool GB = false, bool ROWS = false, int COMB = COMBINE_ATOMIC>
 __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   constexpr int BM = 256, BN = 256, WGM = 2, WGN = NW / 2, NTH = NW * 64;
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
+  __shared__ int scratch[NTH / kWave + 1];
   __shared__ __attribute__((aligned(16))) int tok[BM];
   __shared__ __attribute__((aligned(16))) float wgt[BM];
   __shared__ __attribute__((aligned(16))) int asg[BM];
@@ -1295,10 +1461,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   const int E = p.E, K = p.K, N = p.N;
   const int tiles_n = (K + BN - 1) / BN;  // output columns run over K
   const int KI = (N + BK - 1) / BK;       // reduction runs over N
-  const int BMr = pick_tile_rows(p.bstart, E, tiles_n, gridDim.x, p.tile_rows);
-  group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * (E + 1), E,
+  // COMBINE_RANKED: the nranks * E groups of the rank-ordered view (group g
+  // uses expert g % E's weights)
+  constexpr bool RK = COMB == COMBINE_RANKED;
+  const int GE = RK ? p.nranks * E : E;
+  const int BMr = pick_tile_rows(p.bstart, p.bstride, GE, tiles_n, gridDim.x, p.tile_rows);
+  group_tables_from_schedule<NTH>(p.counts, p.offsets, p.bstart + bm_index(BMr) * p.bstride, GE,
                                   p.layout, p.capacity, bs, rstart, rcnt);
-  const int total = bs[E] * tiles_n;
+  const int total = bs[GE] * tiles_n;
   DxOp<NW> op;
   op.rsA = uniform_rsrc(p.dY, p.dy_bytes);
   op.lds0 = lds_addr(lds);
@@ -1312,11 +1482,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
   const int Lb = logical_block();
   WorkSplit ws;
   // 128-row tiles split at most 4 ways (64 x 128)
-  ws.init(total, gridDim.x, Lb, WorkSplit::SUBTILE_TAIL, BMr == BM ? 8 : 4);
+  ws.init(total, gridDim.x, Lb, WorkSplit::SUBTILE_TAIL, BMr == BM ? 8 : 4, RK);
   int tau;
   const int kb = 0, ke = KI;
   while (ws.next(tau)) {
-    TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BMr);
+    TileCoord c = tile_coord(bs, rstart, rcnt, GE, tau, tiles_n, BMr);
+    const int ge = RK ? c.g % E : c.g;   // the expert whose weights the tile uses
+    const int rank = RK ? c.g / E : 0;
     int kc0 = c.nb * BN, ncols = min(BN, K - kc0);
     if (ws.nS > 1) {  // a sub-tile of a tile of the last round
       const SubTile st = BMr == 128 ? sub_tile128(ws.s, ws.nS) : sub_tile(ws.s, ws.nS);
@@ -1325,7 +1497,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       kc0 += st.c0;
       ncols = min(st.cols, K - kc0);
     }
-    if (c.rows <= 0 || ncols <= 0) continue;
+    if (c.rows <= 0 || ncols <= 0) {
+      // an empty piece still counts as done for the ranks after it
+      if constexpr (RK) {
+        if (p.dX) count_done(p.sync, rank * kSyncCols + c.nb, 8 / ws.nS);
+      }
+      continue;
+    }
     __syncthreads();
     if (tid < BM) {
       const bool ok = tid < c.rows;
@@ -1337,7 +1515,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       rowoff_a[tid] = t >= 0 ? (ROWS ? r : t) * N * 2 : -1;
     }
     __syncthreads();
-    op.rsW = uniform_rsrc(p.W + (size_t)c.g * N * K, wbytes);
+    op.rsW = uniform_rsrc(p.W + (size_t)ge * N * K, wbytes);
     const bool part = ws.nS > 1 || BMr < BM;  // rows / columns partly dead
     op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
     op.setup_b(kc0, kc0 + ncols);
@@ -1355,9 +1533,17 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       tile_multiply<MIc, NIc, WGM, WGN, false, DxOp<NW>, DSK>(op, lds, kb, ke, wm, wn, lane, MIc,
                                                               NIc, acc);
 
+      // COMBINE_RANKED works band by band (64 tile rows): the x rows of the
+      // band (for the routing-weight gradient) and, for rank p > 0 once rank
+      // p-1 of this column block is done, the dX values the earlier ranks left
+      // go into the idle LDS stages first (coherent reads), then the band is
+      // stored (device-coherent stores).  The atomic combine loads the x tile
+      // of all rows at once.
+      constexpr bool CAN_ADD = !GB && !ROWS;
+      constexpr bool add = CAN_ADD && RK;
       // x[tok(r), kc0 .. kc0+255] for the routing-weight gradient: four
       // 64-column K-major sub-tiles into the (now idle) LDS stages
-      if (p.d_w) {
+      if (p.d_w && !add) {
         barrier();
         const uint32_t l0 = lds_addr(lds);
         constexpr int XPW = 32 / NW;  // instructions per wave per 64-column sub-tile
@@ -1398,11 +1584,61 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 #pragma unroll
       for (int ni = 0; ni < NIc; ++ni)
         cb[ni] = (uint32_t)(kc0 + wn * 32 + ni * 32 * WGN + (lane & 31)) * 4u;
+      // LDS of a band (ranked): x sub-tiles of 64 rows (8 KB each) from
+      // offset 0, the old dX rows (1 KB each) from XB_OLD
+      constexpr int XB_SUB = 64 * KROW, XB_OLD = 4 * XB_SUB;
+      const __amdgpu_buffer_rsrc_t rsO =
+          uniform_rsrc(CAN_ADD ? (const void *)p.dX : nullptr, CAN_ADD && p.dX ? p.dx_bytes : 0u);
       // mi and j unrolled by construction: with the gated arithmetic the body
       // is past the compiler's unrolling limit, and a rolled loop would index
       // the accumulators at run time, which moves them to scratch memory
+      if constexpr (add) {
+        if (rank > 0 && has_dx)
+          wait_count(p.sync, (rank - 1) * kSyncCols + c.nb, 8 * (bs[rank * E] - bs[(rank - 1) * E]));
+      }
       unroll<MIc>([&](auto mi_) __attribute__((always_inline)) {
         constexpr int mi = decltype(mi_)::value;
+        if constexpr (add) {
+          // the band's rows mi*64 .. mi*64+63: x chunks (two 8-row groups per
+          // wave and sub-tile) and old dX rows (16 per wave), dead rows and
+          // columns out of range
+          barrier();
+          const uint32_t l0 = lds_addr(lds);
+          constexpr int RG = 64 / (8 * NW), RO = 64 / NW;
+          if (has_dw) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+              for (int i = 0; i < RG; ++i) {
+                const int rl = (wid * RG + i) * 8 + (lane >> 3);  // row inside the band
+                const int row = mi * 64 + rl;
+                const int cch = (lane & 7) ^ ((row >> 1) & 7);
+                const int t = tok[row];
+                const int col = kc0 + q * 64 + cch * 8;
+                const uint32_t off = (t >= 0 && col < K)
+                                         ? (uint32_t)t * (uint32_t)K * 2u + (uint32_t)col * 2u
+                                         : kOobOffset;
+                dma16(rsX, off, l0 + (uint32_t)(q * XB_SUB + (wid * RG + i) * 1024));
+              }
+            }
+          }
+          // (rank 0 reads nothing: its offsets are all out of range, so the
+          // band's old values are zeros and one code path serves every rank)
+          if (has_dx) {
+            const bool cok = lane * 4 < ncols && rank > 0;
+#pragma unroll
+            for (int i = 0; i < RO; ++i) {
+              const int rl = wid * RO + i;
+              const int t = tok[mi * 64 + rl];
+              const uint32_t off =
+                  (t >= 0 && cok) ? ((uint32_t)t * (uint32_t)K + (uint32_t)(kc0 + lane * 4)) * 4u
+                                  : kOobOffset;
+              dma16_coherent(rsO, off, l0 + (uint32_t)(XB_OLD + rl * 1024));
+            }
+          }
+          wait_vmcnt<0>();
+          barrier();
+        }
         unroll<4>([&](auto j_) __attribute__((always_inline)) {
           constexpr int j = decltype(j_)::value;
           const int rq = wm * 32 + mi * 32 * WGM + 8 * j + 4 * (lane >> 5);
@@ -1416,7 +1652,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 #pragma unroll
             for (int ni = 0; ni < NIc; ++ni) {
               const int cs = wn * 32 + ni * 32 * WGN + 16 * ((lane >> 4) & 1) + 4 * (jl & 3);
-              const char *a = lds + (cs >> 6) * OPND + kmaj_off(row, (cs >> 3) & 7) + (cs & 7) * 2;
+              // (a band's sub-tiles hold 64 rows; the swizzle of row - mi*64
+              // equals that of row)
+              const char *a = add ? lds + (cs >> 6) * XB_SUB + kmaj_off(row - mi * 64, (cs >> 3) & 7) +
+                                        (cs & 7) * 2
+                                  : lds + (cs >> 6) * OPND + kmaj_off(row, (cs >> 3) & 7) + (cs & 7) * 2;
               xq[ni] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                   (LDS_AS i16x4 *)(LDS_AS char *)a);
             }
@@ -1470,7 +1710,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
                   __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dh * gv * sg), rsD, so, K * 2, 0);
                 }
               } else if (has_dx && t4[q] >= 0 && cok) {
-                unsafeAtomicAdd((float *)(xb + (ro[q] + cb[ni])), w4[q] * g);
+                float *const dst = (float *)(xb + (ro[q] + cb[ni]));
+                const float v = w4[q] * g;
+                if constexpr (!add) {
+                  unsafeAtomicAdd(dst, v);
+                } else {
+                  const float o = *(const float *)(lds + XB_OLD + (rq + q - mi * 64) * 1024 + cl * 4);
+                  store_coherent(dst, __fadd_rn(o, v));
+                }
               }
               if (has_dw) {
                 const float xv = __builtin_bit_cast(float, (uint32_t)(uint16_t)xq[ni][q] << 16);
@@ -1486,32 +1733,37 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
             if ((lane & 31) == 16) {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
-                if (t4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], dwp[q]);
+                if (a4[q] >= 0) unsafeAtomicAdd(p.d_w + a4[q], dwp[q]);
             }
           }
         });
         __builtin_amdgcn_sched_barrier(0);
       });
+      if constexpr (add) {
+        if (has_dx) count_done(p.sync, rank * kSyncCols + c.nb, 8 / ws.nS);
+      }
     };
     using std::integral_constant;
     // sub-tiles 64 x 128 (8 per tile) and 128 x 128 (4 per tile)
+    const int nsub = ws.nS;
     constexpr int R8 = 64 / (32 * WGM), R4 = 128 / (32 * WGM), C = 128 / (32 * WGN);
     if (BMr == 128) {  // 128 x 256 tiles, split 2 (128 x 128) or 4 (64 x 128)
-      if (ws.nS == 4)
+      if (nsub == 4)
         tile(integral_constant<int, R8>(), integral_constant<int, C>(), std::true_type());
-      else if (ws.nS == 2)
+      else if (nsub == 2)
         tile(integral_constant<int, R4>(), integral_constant<int, C>(), std::true_type());
       else
         tile(integral_constant<int, R4>(), integral_constant<int, NI>(), std::true_type());
-    } else if (ws.nS == 8)
+    } else if (nsub == 8)
       tile(integral_constant<int, R8>(), integral_constant<int, C>(), std::true_type());
-    else if (ws.nS == 4)
+    else if (nsub == 4)
       tile(integral_constant<int, R4>(), integral_constant<int, C>(), std::true_type());
-    else if (ws.nS == 2)
+    else if (nsub == 2)
       tile(integral_constant<int, R4>(), integral_constant<int, NI>(), std::true_type());
     else
       tile(integral_constant<int, MI>(), integral_constant<int, NI>(), std::false_type());
   }
+  if constexpr (RK) finish_ranked(p.sync, p.nranks);
 }
 
 // ============================================================================
@@ -1800,23 +2052,36 @@ bool mfma_supported(int K, int N) { return K % 8 == 0 && N % 8 == 0; }
 
 namespace {
 // Launch a 256 x 256 forward-shaped kernel with 8 waves (2 x 4).
-template <int MODE, typename Tout, bool F8 = false, bool MX = false>
-hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
+template <int MODE, typename Tout, bool F8, bool MX, int COMB>
+hipError_t launch_fwd256_c(const FwdArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
   // block scales: two stages of (256 + 256) 4-byte scale words after the operands
   constexpr size_t lds = kStageLds + (MX ? 2 * (256 + 256) * 4 : 0);
-  hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>>(lds);
+  hipError_t e = set_smem<mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX, COMB>>(lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX>), grid, dim3(512), lds,
-                     st, a);
+  hipLaunchKernelGGL((mfma_fwd_kernel<256, 256, 2, 4, MODE, Tout, F8, MX, COMB>), grid, dim3(512),
+                     lds, st, a);
   return hipGetLastError();
+}
+// The combine is a kernel template argument (each variant carries only its own
+// epilogue); the rank-ordered modes exist for the routed scatter forward.
+template <int MODE, typename Tout, bool F8 = false, bool MX = false>
+hipError_t launch_fwd256(const FwdArgs &a, hipStream_t st) {
+  if constexpr (MODE == FWD_SCATTER) {
+    if (a.combine == COMBINE_RANKED)
+      return launch_fwd256_c<MODE, Tout, F8, MX, COMBINE_RANKED>(a, st);
+  }
+  return launch_fwd256_c<MODE, Tout, F8, MX, COMBINE_ATOMIC>(a, st);
 }
 
 // Routed forward-shaped launch: masked schedules of capacity <= 64 take 64-row
 // tiles (one row block per expert), everything else 256 x 256 tiles.
 template <int MODE, bool F8 = false, bool MX = false>
 hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
-  a.bstart = s.block_start;
+  if (!a.bstart) {  // the canonical schedule (a rank launch has set its window)
+    a.bstart = s.block_start;
+    a.bstride = s.E + 1;
+  }
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
     auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8, MX>;
@@ -1838,36 +2103,63 @@ hipError_t mfma_grouped_gemm(const void *A, const void *W, const int32_t *offset
   return launch_fwd256<FWD_BARE, bf16_t>(a, st);
 }
 
+namespace {
+// The launch's groups: the k*E (rank, expert) groups of the rank-ordered view.
+template <typename Args>
+void use_ranks(Args &a, const moe_schedule &s) {
+  a.counts = s.phase_counts;
+  a.offsets = s.phase_offsets;
+  a.bstart = s.phase_block_start;
+  a.bstride = s.k * s.E + 1;
+  a.row_to_token = s.phase_row_to_token;
+  a.row_weight = s.phase_row_weight;
+  a.layout = MOE_LAYOUT_CONTIGUOUS;
+  a.capacity = 0;
+  a.combine = COMBINE_RANKED;
+  a.nranks = s.k;
+  a.sync = s.phase_sync;
+}
+
+// A routed scatter forward: atomic adds over the canonical schedule, or one
+// ranked launch over the rank-ordered view.
+template <bool F8, bool MX>
+hipError_t launch_scatter(FwdArgs &a, const moe_schedule &s, bool ranked, hipStream_t st) {
+  a.combine = COMBINE_ATOMIC;
+  if (ranked) use_ranks(a, s);
+  return launch_routed<FWD_SCATTER, F8, MX>(a, s, st);
+}
+}  // namespace
+
 hipError_t mfma_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
-                          int N, bool a_by_row, hipStream_t st) {
+                          int N, bool a_by_row, bool ranked, hipStream_t st) {
   const size_t arows = a_by_row ? (size_t)s.R : (size_t)s.T;
   FwdArgs a{(const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
             (uint32_t)(arows * K * 2), (int)s.T};
   if (a_by_row) return launch_routed<FWD_SCATTER_ROWS>(a, s, st);
-  return launch_routed<FWD_SCATTER>(a, s, st);
+  return launch_scatter<false, false>(a, s, ranked, st);
 }
 
 hipError_t mfma_fused_fwd_fp8(const void *xq, const float *x_scale, const void *Wq,
                               const float *w_scale, const moe_schedule &s, float *y, int K, int N,
-                              hipStream_t st) {
+                              bool ranked, hipStream_t st) {
   FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
             (uint32_t)((size_t)s.T * K), (int)s.T};
   a.x_scale = x_scale;
   a.w_scale = w_scale;
-  return launch_routed<FWD_SCATTER, true>(a, s, st);
+  return launch_scatter<true, false>(a, s, ranked, st);
 }
 
 hipError_t mfma_fused_fwd_mx(const void *xq, const uint8_t *x_bs, const void *Wq,
                              const uint8_t *w_bs, const moe_schedule &s, float *y, int K, int N,
-                             hipStream_t st) {
+                             bool ranked, hipStream_t st) {
   FwdArgs a{(const bf16_t *)xq, (const bf16_t *)Wq, y, s.offsets, s.counts, nullptr,
             s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N,
             (uint32_t)((size_t)s.T * K), (int)s.T};
   a.x_bs = x_bs;
   a.w_bs = w_bs;
-  return launch_routed<FWD_SCATTER, true, true>(a, s, st);
+  return launch_scatter<true, true>(a, s, ranked, st);
 }
 
 hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h, void *gu,
@@ -1882,11 +2174,18 @@ hipError_t mfma_gated_up(const void *x, const void *W_gu, const moe_schedule &s,
 static hipError_t launch_dx(const DxArgs &a, hipStream_t st);
 
 hipError_t mfma_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
-                       float *dX, float *d_w, int K, int N, hipStream_t st) {
+                       float *dX, float *d_w, int K, int N, bool ranked, hipStream_t st) {
   DxArgs a{(const bf16_t *)dY, (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets,
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, N, (uint32_t)((size_t)s.T * N * 2),
            (uint32_t)((size_t)s.T * K * 2), g_tile_rows.load(std::memory_order_relaxed)};
+  a.bstride = s.E + 1;
+  a.combine = COMBINE_ATOMIC;
+  a.dx_bytes = (uint32_t)((size_t)s.T * K * 4);
+  if (ranked) {
+    use_ranks(a, s);
+    a.row_to_assign = s.phase_row_to_assign;
+  }
   return launch_dx(a, st);
 }
 
@@ -1897,6 +2196,8 @@ hipError_t mfma_gated_bwd_dh(const void *dY, const void *h, const void *W_down,
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, F, N, (uint32_t)((size_t)s.T * N * 2),
            (uint32_t)((size_t)s.R * F * 2), g_tile_rows.load(std::memory_order_relaxed)};
+  a.bstride = s.E + 1;
+  a.combine = COMBINE_ATOMIC;
   a.gu = (const float *)gu;
   a.dgu = (bf16_t *)dgu;
   const dim3 grid(device_cu_count());
@@ -1912,6 +2213,8 @@ hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedu
            s.counts, s.block_start, s.row_to_assign, s.row_to_token,
            s.row_weight, s.E, s.layout, s.capacity, K, 2 * F,
            (uint32_t)((size_t)s.R * 2 * F * 2), 0u, g_tile_rows.load(std::memory_order_relaxed)};
+  a.bstride = s.E + 1;
+  a.combine = COMBINE_ATOMIC;
   const dim3 grid(device_cu_count());
   hipError_t e = set_smem<mfma_dx_kernel<4, false, true>>(kStageLds);
   if (e != hipSuccess) return e;
@@ -1919,12 +2222,17 @@ hipError_t mfma_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedu
   return hipGetLastError();
 }
 
-static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
+template <int COMB>
+static hipError_t launch_dx_c(const DxArgs &a, hipStream_t st) {
   const dim3 grid(device_cu_count());
-  hipError_t e = set_smem<mfma_dx_kernel<4>>(kStageLds);
+  hipError_t e = set_smem<mfma_dx_kernel<4, false, false, COMB>>(kStageLds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mfma_dx_kernel<4>, grid, dim3(256), kStageLds, st, a);
+  hipLaunchKernelGGL((mfma_dx_kernel<4, false, false, COMB>), grid, dim3(256), kStageLds, st, a);
   return hipGetLastError();
+}
+static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
+  if (a.combine == COMBINE_RANKED) return launch_dx_c<COMBINE_RANKED>(a, st);
+  return launch_dx_c<COMBINE_ATOMIC>(a, st);
 }
 
 template <int RM>

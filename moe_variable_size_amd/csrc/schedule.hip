@@ -27,6 +27,8 @@
 // Equal ids inside a chunk are matched with one ballot per id bit, so ranks do
 // not depend on the order in which hardware executes atomics: the result is
 // deterministic and equals a stable argsort by expert.
+#include <string.h>
+
 #include "common.hpp"
 
 namespace moe {
@@ -92,36 +94,82 @@ MOE_DEV BlockRange wave_range(int b, int B, int S, int w) {
   return BlockRange{s0, min(S, s0 + q)};
 }
 
+// One counting sort of the assignments by a key, with everything it writes.
+//   by_rank 0: key = the expert id (the canonical schedule);
+//   by_rank 1: key = p * E + e, p = the assignment's rank among the valid
+//              assignments of its token (0 for the first valid slot, ...):
+//              rows ordered by (rank, expert, s).  A token with no valid
+//              assignment gets one row of key 0 (rank 0, expert 0) with weight
+//              0 and assignment -1, placed at its last slot's s, so that every
+//              token has exactly one rank-0 row.
+struct SortJob {
+  int nkeys;        // E, or k * E
+  int by_rank;
+  int32_t *table;   // [nblk][nkeys] per-block counts
+  int32_t *inv;     // [nblk] excluded assignments per block (by_rank 0), else NULL
+  int32_t *counts, *offsets;  // [nkeys]
+  int32_t *block_start;       // [MOE_NUM_BM][nkeys + 1]
+  int32_t *expert_order;      // [nkeys] (by_rank 0), else NULL
+  int32_t *row_to_assign, *row_to_token;
+  float *row_weight;
+  int32_t *status;            // (by_rank 0), else NULL
+  int32_t *sync;              // (by_rank 1) ranked-combine counters, zeroed here
+};
+struct SortJobs {
+  SortJob j[2];
+};
+
+// Key of assignment s (id = ids[s]) for a sort, or -1 when s is in no group.
+MOE_DEV int sort_key(const SortJob &job, const int32_t *__restrict__ ids, int s, int id, int k,
+                     int E) {
+  const bool valid = id >= 0 && id < E;
+  if (!job.by_rank) return valid ? id : -1;
+  const int t = s / k, j = s - t * k;
+  int before = 0, others = 0;
+  for (int jj = 0; jj < k; ++jj) {
+    if (jj == j) continue;
+    const int o = ids[t * k + jj];
+    const int v = (o >= 0 && o < E) ? 1 : 0;
+    before += jj < j ? v : 0;
+    others += v;
+  }
+  if (valid) return before * E + id;
+  return (j == k - 1 && others == 0) ? 0 : -1;
+}
+
 // ---- 1. per-block histogram ---------------------------------------------------
+// Workgroup (job, b) counts the keys of block b's assignments for sort `job`.
 __global__ __launch_bounds__(kBlkThreads) void sched_hist_kernel(
-    const int32_t *__restrict__ ids, int S, int E, int B, int32_t *__restrict__ table,
-    int32_t *__restrict__ invalid_per_block) {
-  extern __shared__ int hist[];  // [E]
-  const int tid = threadIdx.x, b = blockIdx.x;
-  for (int e = tid; e <= E; e += kBlkThreads) hist[e] = 0;
+    const int32_t *__restrict__ ids, int S, int k, int E, int B, int nblk, SortJobs jobs) {
+  extern __shared__ int hist[];  // [nkeys + 1]
+  const int tid = threadIdx.x;
+  const int jb = blockIdx.x / nblk, b = blockIdx.x - jb * nblk;
+  const SortJob &job = jobs.j[jb];
+  const int nk = job.nkeys;
+  for (int e = tid; e <= nk; e += kBlkThreads) hist[e] = 0;
   __syncthreads();
   int invalid = 0;
   const int s0 = b * B, s1 = min(S, s0 + B);
   for (int s = s0 + tid; s < s1; s += kBlkThreads) {
     const int id = ids[s];
-    if (id >= 0 && id < E)
-      atomicAdd(&hist[id], 1);
-    else
-      ++invalid;
+    const int key = sort_key(job, ids, s, id, k, E);
+    if (key >= 0)
+      atomicAdd(&hist[key], 1);
+    if (id < 0 || id >= E) ++invalid;
   }
   for (int d = kWave / 2; d >= 1; d >>= 1) invalid += __shfl_xor(invalid, d, kWave);
   __syncthreads();
-  if ((tid & (kWave - 1)) == 0 && invalid) atomicAdd(&hist[E], invalid);  // hist has E+1 ints
+  if ((tid & (kWave - 1)) == 0 && invalid) atomicAdd(&hist[nk], invalid);  // hist has nk+1 ints
   __syncthreads();
-  for (int e = tid; e < E; e += kBlkThreads) table[(size_t)b * E + e] = hist[e];
-  if (tid == 0) invalid_per_block[b] = hist[E];
+  for (int e = tid; e < nk; e += kBlkThreads) job.table[(size_t)b * nk + e] = hist[e];
+  if (tid == 0 && job.inv) job.inv[b] = hist[nk];
 }
 
-// Exclusive prefix over experts of val[0 .. E-1] (LDS) into out[] (LDS), each
-// thread summing a run of consecutive experts; returns the total.
-MOE_DEV int scan_experts(const int *val, int *out, int E, int *scratch) {
-  const int chunk = (E + kBlkThreads - 1) / kBlkThreads;
-  const int e0 = min(E, (int)threadIdx.x * chunk), e1 = min(E, e0 + chunk);
+// Exclusive prefix over keys of val[0 .. n-1] (LDS) into out[] (LDS), each
+// thread summing a run of consecutive keys; returns the total.
+MOE_DEV int scan_experts(const int *val, int *out, int n, int *scratch) {
+  const int chunk = (n + kBlkThreads - 1) / kBlkThreads;
+  const int e0 = min(n, (int)threadIdx.x * chunk), e1 = min(n, e0 + chunk);
   int sum = 0;
   for (int e = e0; e < e1; ++e) sum += val[e];
   int total;
@@ -134,28 +182,27 @@ MOE_DEV int scan_experts(const int *val, int *out, int E, int *scratch) {
   return total;
 }
 
-// ---- 2. bases, per-expert outputs, stable placement ----------------------------
+// ---- 2. bases, per-key outputs, stable placement ------------------------------
+// Workgroup (job, b): block b's placement for sort `job`.
 __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
     const int32_t *__restrict__ ids, const float *__restrict__ w, int S, int k, int E, int B,
-    int nblk, int layout, int capacity, int R, const int32_t *__restrict__ table,
-    const int32_t *__restrict__ invalid_per_block, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ block_start,
-    int32_t *__restrict__ expert_order, int32_t *__restrict__ row_to_assign,
-    int32_t *__restrict__ row_to_token, float *__restrict__ row_weight,
-    int32_t *__restrict__ status) {
+    int nblk, int layout, int capacity, int R, SortJobs jobs) {
   extern __shared__ int smem[];
-  int *hist = smem;                     // [kBlkWaves][E]: per-wave counts, then running bases
-  int *base = hist + kBlkWaves * E;     // [E] this block's base inside each expert
-  int *cnt = base + E;                  // [E] valid rows per expert
-  int *rowbase = cnt + E;               // [E] first row of each expert
-  int *tmp = rowbase + E;               // [2][E] workgroup 0: tile counts and their prefix
-  int *scratch = tmp + 2 * E;           // [kBlkWaves + 1]
-  int *tally = scratch + kBlkWaves + 1; // [2] invalid ids, assignments over capacity
-  const int tid = threadIdx.x, b = blockIdx.x;
+  const int jb = blockIdx.x / nblk, b = blockIdx.x - jb * nblk;
+  const SortJob &job = jobs.j[jb];
+  const int nk = job.nkeys;
+  int *hist = smem;                      // [kBlkWaves][nk]: per-wave counts, then running bases
+  int *base = hist + kBlkWaves * nk;     // [nk] this block's base inside each key
+  int *cnt = base + nk;                  // [nk] rows per key
+  int *rowbase = cnt + nk;               // [nk] first row of each key
+  int *tmp = rowbase + nk;               // [2][nk] tile counts and their prefix
+  int *scratch = tmp + 2 * nk;           // [kBlkWaves + 1]
+  int *tally = scratch + kBlkWaves + 1;  // [2] invalid ids, assignments over capacity
+  const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);  // wave-uniform
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-  const bool masked = layout == MOE_LAYOUT_MASKED;
+  const bool masked = !job.by_rank && layout == MOE_LAYOUT_MASKED;
   // this wave's first kBatch x 64 ids and weights, loaded before anything
   // else so their latency overlaps the table sums (with B = 1024 that is the
   // wave's whole range)
@@ -170,17 +217,17 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
     wv0[u] = (s < rg.end && w) ? w[s] : 1.f;
   }
   const bool one_batch = rg.end - rg.begin <= kBatch * kWave;  // wave-uniform
-  for (int i = tid; i < kBlkWaves * E; i += kBlkThreads) hist[i] = 0;
+  for (int i = tid; i < kBlkWaves * nk; i += kBlkThreads) hist[i] = 0;
   if (tid < 2) tally[tid] = 0;
   __syncthreads();
-  // the table's column sums: this block's base and each expert's total
-  for (int e = tid; e < E; e += kBlkThreads) {
+  // the table's column sums: this block's base and each key's total
+  for (int e = tid; e < nk; e += kBlkThreads) {
     int before = 0, m_e = 0;
     for (int b0 = 0; b0 < nblk; b0 += 8) {
       int c[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)  // eight loads in flight, then the sums
-        c[u] = b0 + u < nblk ? table[(size_t)(b0 + u) * E + e] : 0;
+        c[u] = b0 + u < nblk ? job.table[(size_t)(b0 + u) * nk + e] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         before += b0 + u < b ? c[u] : 0;
@@ -192,129 +239,148 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
     if (b == 0 && masked && m_e > capacity) atomicAdd(&tally[1], m_e - capacity);
   }
   __syncthreads();
-  // packed prefix of the valid counts: END offsets in both layouts, first rows
-  // in the contiguous one (the masked layout starts expert e at e * capacity)
-  const int total = scan_experts(cnt, rowbase, E, scratch);
-  for (int e = tid; e < E; e += kBlkThreads) {
+  // packed prefix of the counts: END offsets in both layouts, first rows in the
+  // contiguous one (the masked layout starts expert e at e * capacity)
+  const int total = scan_experts(cnt, rowbase, nk, scratch);
+  for (int e = tid; e < nk; e += kBlkThreads) {
     if (b == 0) {
-      counts[e] = cnt[e];
-      offsets[e] = rowbase[e] + cnt[e];
+      job.counts[e] = cnt[e];
+      job.offsets[e] = rowbase[e] + cnt[e];
     }
     if (masked) rowbase[e] = e * capacity;
   }
-  // the per-expert outputs, one job per workgroup (workgroup j % nblk takes
+  // the per-key outputs, one job per workgroup (workgroup j % nblk takes
   // job j), each on the counts every workgroup has summed
   if (b == 1 % nblk) {
 #pragma unroll
     for (int i = 0; i < MOE_NUM_BM; ++i) {
       const int bm = 32 << i;
-      for (int e = tid; e < E; e += kBlkThreads)
+      for (int e = tid; e < nk; e += kBlkThreads)
         tmp[e] = masked ? (capacity + bm - 1) / bm : (cnt[e] + bm - 1) / bm;
       __syncthreads();
-      const int tot = scan_experts(tmp, tmp + E, E, scratch);
-      for (int e = tid; e < E; e += kBlkThreads) block_start[i * (E + 1) + e] = tmp[E + e];
-      if (tid == 0) block_start[i * (E + 1) + E] = tot;
+      const int tot = scan_experts(tmp, tmp + nk, nk, scratch);
+      for (int e = tid; e < nk; e += kBlkThreads) job.block_start[i * (nk + 1) + e] = tmp[nk + e];
+      if (tid == 0) job.block_start[i * (nk + 1) + nk] = tot;
       __syncthreads();
     }
   }
-  if (b == 2 % nblk) {
+  if (b == 2 % nblk && job.expert_order) {
     // experts by descending row count, ties by id
-    for (int e = tid; e < E; e += kBlkThreads) {
+    for (int e = tid; e < nk; e += kBlkThreads) {
       const int c = cnt[e];
       int rank = 0;
-      for (int o = 0; o < E; ++o) {
+      for (int o = 0; o < nk; ++o) {
         const int co = cnt[o];
         rank += (co > c || (co == c && o < e)) ? 1 : 0;
       }
-      expert_order[rank] = e;
+      job.expert_order[rank] = e;
     }
   }
+  if (b == 2 % nblk && job.sync) {
+    for (int i = tid; i < kRankSyncInts; i += kBlkThreads) job.sync[i] = 0;
+  }
   if (b == 3 % nblk) {
-    // rows no assignment fills: past the last valid row (contiguous) or past
+    // rows no assignment fills: past the last filled row (contiguous) or past
     // each expert's valid prefix (masked)
     if (!masked) {
       for (int r = total + tid; r < R; r += kBlkThreads) {
-        row_to_assign[r] = -1;
-        row_to_token[r] = -1;
-        row_weight[r] = 0.f;
+        job.row_to_assign[r] = -1;
+        job.row_to_token[r] = -1;
+        job.row_weight[r] = 0.f;
       }
     } else {
       for (int r = tid; r < R; r += kBlkThreads) {
         const int ex = r / capacity;
         if (r - ex * capacity >= cnt[ex]) {
-          row_to_assign[r] = -1;
-          row_to_token[r] = -1;
-          row_weight[r] = 0.f;
+          job.row_to_assign[r] = -1;
+          job.row_to_token[r] = -1;
+          job.row_weight[r] = 0.f;
         }
       }
     }
   }
-  if (b == 0) {
+  if (b == 0 && job.status) {
     int inv = 0;
-    for (int i = tid; i < nblk; i += kBlkThreads) inv += invalid_per_block[i];
+    for (int i = tid; i < nblk; i += kBlkThreads) inv += job.inv[i];
     if (inv) atomicAdd(&tally[0], inv);
     __syncthreads();
     if (tid == 0) {
-      status[0] = tally[0];
-      status[1] = tally[1];
+      job.status[0] = tally[0];
+      job.status[1] = tally[1];
     }
+  }
+  // keys of this wave's assignments (the preloaded batch)
+  int kv0[kBatch];
+#pragma unroll
+  for (int u = 0; u < kBatch; ++u) {
+    const int s = rg.begin + u * kWave + lane;
+    kv0[u] = s < rg.end ? sort_key(job, ids, s, idv0[u], k, E) : -1;
   }
   if (one_batch) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u)
-      if (idv0[u] >= 0 && idv0[u] < E) atomicAdd(&hist[wid * E + idv0[u]], 1);
+      if (kv0[u] >= 0) atomicAdd(&hist[wid * nk + kv0[u]], 1);
   } else {
     for (int s = rg.begin + lane; s < rg.end; s += kWave) {
-      const int id = ids[s];
-      if (id >= 0 && id < E) atomicAdd(&hist[wid * E + id], 1);
+      const int key = sort_key(job, ids, s, ids[s], k, E);
+      if (key >= 0) atomicAdd(&hist[wid * nk + key], 1);
     }
   }
   __syncthreads();
-  // per-wave base = rank base of this block inside the expert + earlier waves
-  for (int e = tid; e < E; e += kBlkThreads) {
+  // per-wave base = rank base of this block inside the key + earlier waves
+  for (int e = tid; e < nk; e += kBlkThreads) {
     int run = base[e];
     for (int v = 0; v < kBlkWaves; ++v) {
-      const int c = hist[v * E + e];
-      hist[v * E + e] = run;
+      const int c = hist[v * nk + e];
+      hist[v * nk + e] = run;
       run += c;
     }
   }
   __syncthreads();
 
   int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
+  while ((1 << nbits) < nk) ++nbits;
   for (int b0 = rg.begin; b0 < rg.end; b0 += kBatch * kWave) {
-    int idv[kBatch];
+    int kv[kBatch];
     float wv[kBatch];
     if (b0 == rg.begin) {  // wave-uniform: the preloaded batch
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
-        idv[u] = idv0[u];
+        kv[u] = kv0[u];
         wv[u] = wv0[u];
       }
     } else {
+      int idv[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {  // all loads of the batch before any use
         const int s = b0 + u * kWave + lane;
         idv[u] = s < rg.end ? ids[s] : -1;
         wv[u] = (s < rg.end && w) ? w[s] : 1.f;
       }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int s = b0 + u * kWave + lane;
+        kv[u] = s < rg.end ? sort_key(job, ids, s, idv[u], k, E) : -1;
+      }
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       if (b0 + u * kWave >= rg.end) break;  // wave-uniform
       const int s = b0 + u * kWave + lane;
-      const int id = idv[u];
-      const bool valid = s < rg.end && id >= 0 && id < E;
-      const uint64_t m = peers(id, valid, nbits);
+      const int key = kv[u];
+      const bool valid = s < rg.end && key >= 0;
+      const uint64_t m = peers(key, valid, nbits);
       int rank = 0;
-      if (valid) rank = hist[wid * E + id] + __popcll(m & below);
-      if (valid && (m & below) == 0) hist[wid * E + id] += __popcll(m);
+      if (valid) rank = hist[wid * nk + key] + __popcll(m & below);
+      if (valid && (m & below) == 0) hist[wid * nk + key] += __popcll(m);
       if (valid && (!masked || rank < capacity)) {
-        const int r = rowbase[id] + rank;
-        row_to_assign[r] = s;
-        row_to_token[r] = s / k;
-        row_weight[r] = wv[u];
+        const int r = rowbase[key] + rank;
+        // a token's row with no valid assignment (rank order only): weight 0
+        const int id = ids[s];
+        const bool real = id >= 0 && id < E;
+        job.row_to_assign[r] = real ? s : -1;
+        job.row_to_token[r] = s / k;
+        job.row_weight[r] = real ? wv[u] : 0.f;
       }
     }
   }
@@ -362,36 +428,70 @@ __global__ void fill_zero_kernel(FillRange a, FillRange b) {
 }  // namespace
 
 // Block size of the build: a multiple of 256 ids, at least 1024, large enough
-// that the block x expert table fits the scan's LDS.
-int schedule_block(int64_t S, int E) {
+// that the block x key table of the larger sort fits the scan's LDS.
+int schedule_block(int64_t S, int nkeys) {
   int64_t B = 1024;
-  while (((S + B - 1) / B) * E > kTableInts) B *= 2;
+  while (((S + B - 1) / B) * nkeys > kTableInts) B *= 2;
   return (int)B;
 }
-int schedule_blocks(int64_t S, int E) {
-  const int B = schedule_block(S, E);
+int schedule_blocks(int64_t S, int nkeys) {
+  const int B = schedule_block(S, nkeys);
   return (int)((S + B - 1) / B);
+}
+
+bool rank_order_supported(int layout, int k, int E) {
+  return layout == MOE_LAYOUT_CONTIGUOUS && k <= kMaxRankK && k * E <= kMaxRankKeys;
 }
 
 hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_schedule &s,
                                  int32_t *scratch, hipStream_t st) {
-  const int S = (int)s.S, E = s.E;
-  const int B = schedule_block(S, E), nblk = schedule_blocks(S, E);
-  int32_t *table = scratch;                          // [nblk * E]
-  int32_t *inv = table + (size_t)nblk * E;           // [nblk]
-  hipLaunchKernelGGL(sched_hist_kernel, dim3(nblk), dim3(kBlkThreads), sizeof(int) * (E + 1), st,
-                     ids, S, E, B, table, inv);
-  const size_t place_smem = sizeof(int) * ((size_t)(kBlkWaves + 5) * E + kBlkWaves + 1 + 2);
-  hipLaunchKernelGGL(sched_place_kernel, dim3(nblk), dim3(kBlkThreads), place_smem, st, ids, w, S,
-                     s.k, E, B, nblk, s.layout, s.capacity, (int)s.R, table, inv, s.counts,
-                     s.offsets, s.block_start, s.expert_order, s.row_to_assign, s.row_to_token,
-                     s.row_weight, s.status);
+  const int S = (int)s.S, E = s.E, k = s.k;
+  const bool ranked = s.phases > 0;
+  const int nk1 = ranked ? k * E : 0;
+  const int nkmax = nk1 > E ? nk1 : E;
+  const int B = schedule_block(S, nkmax), nblk = schedule_blocks(S, nkmax);
+  SortJobs jobs;
+  memset(&jobs, 0, sizeof(jobs));
+  SortJob &c = jobs.j[0];
+  c.nkeys = E;
+  c.by_rank = 0;
+  c.table = scratch;                         // [nblk * E]
+  c.inv = c.table + (size_t)nblk * E;        // [nblk]
+  c.counts = s.counts;
+  c.offsets = s.offsets;
+  c.block_start = s.block_start;
+  c.expert_order = s.expert_order;
+  c.row_to_assign = s.row_to_assign;
+  c.row_to_token = s.row_to_token;
+  c.row_weight = s.row_weight;
+  c.status = s.status;
+  if (ranked) {
+    SortJob &p = jobs.j[1];
+    p.nkeys = nk1;
+    p.by_rank = 1;
+    p.table = c.inv + nblk;                  // [nblk * k * E]
+    p.counts = s.phase_counts;
+    p.offsets = s.phase_offsets;
+    p.block_start = s.phase_block_start;
+    p.row_to_assign = s.phase_row_to_assign;
+    p.row_to_token = s.phase_row_to_token;
+    p.row_weight = s.phase_row_weight;
+    p.sync = s.phase_sync;
+  }
+  const int grid = nblk * (ranked ? 2 : 1);
+  hipLaunchKernelGGL(sched_hist_kernel, dim3(grid), dim3(kBlkThreads), sizeof(int) * (nkmax + 1),
+                     st, ids, S, k, E, B, nblk, jobs);
+  const size_t place_smem = sizeof(int) * ((size_t)(kBlkWaves + 5) * nkmax + kBlkWaves + 1 + 2);
+  hipLaunchKernelGGL(sched_place_kernel, dim3(grid), dim3(kBlkThreads), place_smem, st, ids, w, S,
+                     k, E, B, nblk, s.layout, s.capacity, (int)s.R, jobs);
   return hipGetLastError();
 }
 
-size_t schedule_scratch_bytes(int64_t S, int E) {
-  const int nblk = schedule_blocks(S, E);
-  return sizeof(int32_t) * ((size_t)nblk * E + nblk);
+size_t schedule_scratch_bytes(int64_t S, int E, int k, bool ranked) {
+  const int nk1 = ranked ? k * E : 0;
+  const int nkmax = nk1 > E ? nk1 : E;
+  const int nblk = schedule_blocks(S, nkmax);
+  return sizeof(int32_t) * ((size_t)nblk * (E + nk1) + nblk);
 }
 
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,

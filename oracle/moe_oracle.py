@@ -84,6 +84,48 @@ def routing_schedule(expert_ids: np.ndarray, topk_weights: Optional[np.ndarray],
                     int((~valid).sum()))
 
 
+@dataclass
+class RankSchedule:
+    """Rows of the assignments ordered by (rank, expert, s), where the rank of
+    an assignment is the number of valid assignments of its token in earlier
+    slots.  Group p*E + e holds the rank-p assignments routed to expert e.  A
+    token with no valid assignment has one row in group 0 (rank 0, expert 0)
+    at its last slot's s, with weight 0 and assignment -1."""
+    E: int
+    k: int
+    counts: np.ndarray        # [k*E] int64 rows per (rank, expert) group
+    offsets: np.ndarray       # [k*E] int32 END offsets
+    row_to_assign: np.ndarray  # [rows] int64, -1 for a token's row with no valid assignment
+    row_to_token: np.ndarray   # [rows] int64
+    row_weight: np.ndarray     # [rows] float32
+
+
+def rank_schedule(expert_ids: np.ndarray, topk_weights: Optional[np.ndarray], E: int) -> RankSchedule:
+    """The rank-ordered view of the assignments (a layout of this library, not
+    of the pages): each token's contributions numbered by slot among its valid
+    ones, so that the rows of one rank hold every token at most once and the
+    rank-0 rows hold every token exactly once."""
+    expert_ids = np.asarray(expert_ids)
+    T, k = expert_ids.shape
+    ids = expert_ids.astype(np.int64)
+    valid = (ids >= 0) & (ids < E)
+    rank = np.cumsum(valid, axis=1) - valid            # valid slots before each one
+    dead = ~valid.any(axis=1)                           # tokens with no valid assignment
+    key = np.where(valid, rank * E + ids, -1)
+    key[dead, k - 1] = 0
+    flat = key.reshape(-1)
+    s_in = np.nonzero(flat >= 0)[0]
+    order = s_in[np.argsort(flat[s_in], kind="stable")]
+    counts = np.bincount(flat[s_in], minlength=k * E).astype(np.int64)
+    offsets = np.cumsum(counts).astype(np.int32)
+    vflat = valid.reshape(-1)
+    assign = np.where(vflat[order], order, -1)
+    w = np.ones(T * k, dtype=np.float32) if topk_weights is None else \
+        np.asarray(topk_weights, dtype=np.float32).reshape(-1)
+    weight = np.where(vflat[order], w[order], np.float32(0)).astype(np.float32)
+    return RankSchedule(E, k, counts, offsets, assign, order // k, weight)
+
+
 def group_rows(offsets: np.ndarray) -> list:
     """Row ranges of each group from END offsets ([GG] "Data layout, offsets and
     alignment"): group e owns rows [offs[e-1], offs[e]), with offs[-1] := 0."""

@@ -39,7 +39,31 @@ def _check_contiguous(ids, w, E, name):
     order = np.argsort(-ref.counts, kind="stable")
     assert sch.expert_order.cpu().numpy().tolist() == order.tolist()
     assert sch.status.cpu().numpy().tolist() == [ref.n_invalid, 0]
+    _check_rank_view(sch, ids, w, E)
     return sch, ref
+
+
+def _check_rank_view(sch, ids, w, E):
+    """The rank-ordered view: built exactly when k <= 8 and k*E <= 1024 (the
+    library's limits), and then bit-exact against the oracle's definition."""
+    T, k = ids.shape
+    if k > 8 or k * E > 1024:
+        assert sch.phases == 0
+        return
+    assert sch.phases == k
+    rs = O.rank_schedule(ids, w, E)
+    n = int(rs.counts.sum())
+    assert sch.phase_counts.cpu().numpy().tolist() == rs.counts.tolist()
+    assert sch.phase_offsets.cpu().numpy().tolist() == rs.offsets.tolist()
+    for BM in BMS:
+        assert sch.phase_block_start(BM).cpu().numpy().tolist() == _excl_blocks(rs.counts, BM).tolist()
+    a = sch.phase_row_to_assign.cpu().numpy()
+    t = sch.phase_row_to_token.cpu().numpy()
+    wt = sch.phase_row_weight.cpu().numpy()
+    assert a[:n].tolist() == rs.row_to_assign.tolist()
+    assert t[:n].tolist() == rs.row_to_token.tolist()
+    assert np.array_equal(wt[:n].view(np.uint32), rs.row_weight.view(np.uint32))
+    assert (a[n:] == -1).all() and (t[n:] == -1).all() and (wt[n:] == 0).all()
 
 
 def test_schedule_page_example():
@@ -106,6 +130,7 @@ def test_schedule_masked(cap, seed, T):
         expect = (np.arange(E + 1) * -(-cap // BM)).tolist()
         assert sch.block_start(BM).cpu().numpy().tolist() == expect
     assert sch.status.cpu().numpy().tolist() == [ref.n_invalid, ref.n_dropped]
+    assert sch.phases == 0   # no rank-ordered view for the masked layout
 
 
 @pytest.mark.parametrize("N,BM,BN", [(2048, 128, 128), (1408, 256, 256), (7, 32, 16), (130, 64, 64)])

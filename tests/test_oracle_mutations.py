@@ -176,7 +176,16 @@ def _mx_masked_no_weight_scales(xq, x_bs, Wq, w_bs, ms, T, *, acc=np.float64):
     return O.masked_forward(O.mx_values(xq, x_bs), O.decode_e4m3(Wq), ms, T, acc=acc)
 
 
-_ORIG = {n: getattr(O, n) for n in ["masked_forward_mx", "mx_values", "routing_schedule", "tile_owner", "tile_coords", "moe_forward",
+def _rank_counts_invalid_slots(expert_ids, topk_weights, E):
+    # ranks counted over all earlier slots, valid or not
+    ids = np.asarray(expert_ids)
+    T, k = ids.shape
+    shifted = np.where((ids >= 0) & (ids < E), ids, 0)   # every slot looks valid to the rank
+    rs = _ORIG["rank_schedule"](shifted, topk_weights, E)
+    return rs
+
+
+_ORIG = {n: getattr(O, n) for n in ["rank_schedule", "masked_forward_mx", "mx_values", "routing_schedule", "tile_owner", "tile_coords", "moe_forward",
                                      "grouped_gemm", "moe_backward", "gated_activation",
                                      "gated_ffn_forward", "decode_e4m3", "moe_forward_fp8",
                                      "gated_ffn_backward"]}
@@ -226,6 +235,8 @@ CASES = [
     ("masked block-scaled forward without the weight block scales", "masked_forward_mx",
      lambda: _mx_masked_no_weight_scales,
      [P.test_mx_masked_equals_contiguous, P.test_mx_masked_overflow_brute_force]),
+    ("rank counted over invalid slots too", "rank_schedule", lambda: _rank_counts_invalid_slots,
+     [lambda: P.test_rank_schedule_brute_force(2, 31, 3, 4, 0.2)]),
     ("fp8 channel scale collapsed to one per expert", "moe_forward_fp8",
      lambda: _fp8_channel_scale_on_rows,
      [P.test_fp8_forward_brute_force, P.test_fp8_power_of_two_scales_are_exact]),

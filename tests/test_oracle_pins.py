@@ -859,3 +859,62 @@ def test_backward_selected_experts_match_full():
     dX2, dWs, dw2 = O.moe_backward(dY, x, W, ids, w, E, dw_experts=[3, 2])
     assert np.array_equal(dX, dX2) and np.array_equal(dw, dw2)
     assert set(dWs) == {2, 3} and np.array_equal(dWs[3], dW[3]) and np.all(dWs[2] == 0)
+
+
+# ----------------------------------------------------------------------------
+# Rank-ordered view (the layout the rank-by-rank combine runs on)
+# ----------------------------------------------------------------------------
+def _rank_brute(ids, w, E):
+    """Plain loops: rank = valid slots of the token before this one; rows sorted
+    by (rank * E + expert, s); a token with no valid slot contributes one row
+    (rank 0, expert 0) at its last slot."""
+    T, k = ids.shape
+    rows = []
+    for t in range(T):
+        nvalid = 0
+        for j in range(k):
+            e = int(ids[t, j])
+            if 0 <= e < E:
+                rows.append((nvalid * E + e, t * k + j, t * k + j, float(w[t, j])))
+                nvalid += 1
+        if nvalid == 0:
+            rows.append((0, t * k + k - 1, -1, 0.0))
+    rows.sort(key=lambda r: (r[0], r[1]))
+    counts = [0] * (k * E)
+    for key, *_ in rows:
+        counts[key] += 1
+    return counts, [r[2] for r in rows], [r[1] // k for r in rows], [r[3] for r in rows]
+
+
+@pytest.mark.parametrize("seed,T,k,E,bad", [(1, 40, 2, 5, 0.0), (2, 31, 3, 4, 0.2), (3, 17, 1, 6, 0.3),
+                                            (4, 25, 4, 3, 0.5)])
+def test_rank_schedule_brute_force(seed, T, k, E, bad):
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[rng.random((T, k)) < bad] = -3          # excluded ids, some tokens left with none
+    w = rng.random((T, k)).astype(np.float32)
+    rs = O.rank_schedule(ids, w, E)
+    counts, assign, tok, wt = _rank_brute(ids, w, E)
+    assert list(rs.counts) == counts
+    assert list(rs.offsets) == list(np.cumsum(counts))
+    assert list(rs.row_to_assign) == assign and list(rs.row_to_token) == tok
+    assert np.array_equal(rs.row_weight, np.array(wt, dtype=np.float32))
+
+
+def test_rank_schedule_rank_groups_hold_each_token_once():
+    """Rank 0 rows hold every token exactly once; any rank holds a token at
+    most once; the valid rows are the canonical schedule's rows."""
+    rng = np.random.default_rng(5)
+    T, k, E = 200, 3, 7
+    ids = np.array([rng.choice(E, size=k, replace=True) for _ in range(T)], dtype=np.int32)
+    ids[rng.random((T, k)) < 0.15] = E + 4
+    rs = O.rank_schedule(ids, None, E)
+    starts = np.concatenate([[0], rs.offsets])
+    for p in range(k):
+        toks = rs.row_to_token[starts[p * E]:starts[(p + 1) * E]]
+        assert len(set(toks.tolist())) == len(toks)
+        if p == 0:
+            assert sorted(toks.tolist()) == list(range(T))
+    sch = O.routing_schedule(ids, None, E)
+    real = rs.row_to_assign[rs.row_to_assign >= 0]
+    assert sorted(real.tolist()) == sorted(sch.perm.tolist())
