@@ -160,6 +160,31 @@ int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int
                        void *stream);
 
 /*
+ * moe_build_schedule for callers that cannot allocate device memory at all
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  It builds the same schedule, bit for bit, into `workspace`,
+ * but the per-block count tables the build needs on the way are kept in a
+ * static device array of the library (192 KiB per GPU, held until the process
+ * ends) instead of at the end of the workspace.  Nothing is allocated or freed.
+ *   Arguments and results as for moe_build_schedule, except workspace_bytes:
+ *   moe_schedule_workspace_bytes(...) always suffices; the call needs that
+ *   size less the tables' share (256-byte aligned), and returns
+ *   MOE_ERR_WORKSPACE below it.
+ *   Returns MOE_ERR_LIMIT if the tables would not fit the static array (not
+ *   reachable within the size limits above: the tables hold at most 3 * 16384
+ *   ints) and MOE_ERR_HIP if the array's device address cannot be obtained.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on the same GPU (on different streams, or from several host threads without
+ * ordering) race and may build wrong schedules; calls ordered on one stream
+ * are safe.  The array needs no clearing: each build writes every entry it
+ * reads.
+ */
+int moe_build_schedule_noalloc(const int32_t *expert_ids, const float *topk_weights, int64_t T,
+                               int32_t k, int32_t E, int32_t layout, int32_t capacity,
+                               void *workspace, size_t workspace_bytes, moe_schedule *sched,
+                               void *stream);
+
+/*
  * Bare variable-size grouped GEMM, rows already grouped by expert ([GG] "Problem
  * descriptors and the tile scheduler"; [CARD] "How it works", the kernel with
  * the permutation maps omitted):

@@ -63,6 +63,7 @@ _SCHED_P = ctypes.POINTER(MoeSchedule)
 SIGNATURES = {
     "moe_schedule_workspace_bytes": (_SZ, [_I64, _I32, _I32, _I32, _I32]),
     "moe_build_schedule": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _SCHED_P, _P]),
+    "moe_build_schedule_noalloc": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _SZ, _SCHED_P, _P]),
     "grouped_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "moe_fused_fwd": (ctypes.c_int, [_P, _P, _SCHED_P, _P, _I64, _I64, _I32, _P]),
     "moe_fused_fwd_fp8": (ctypes.c_int, [_P, _P, _P, _P, _SCHED_P, _P, _I64, _I64, _P]),

@@ -204,6 +204,29 @@ def moe_build_schedule(expert_ids: torch.Tensor, topk_weights: Optional[torch.Te
     return Schedule(c, workspace)
 
 
+def moe_build_schedule_noalloc(expert_ids: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                               E: int, workspace: torch.Tensor, *,
+                               layout: int = MOE_LAYOUT_CONTIGUOUS, capacity: int = 0,
+                               stream=None) -> Schedule:
+    """moe_build_schedule into a caller-given workspace with the build's block
+    tables in the library's static per-GPU array: allocates nothing.  Calls
+    that overlap in time on one GPU race (they share that array)."""
+    lib = _lib.load()
+    _require(expert_ids, "expert_ids", torch.int32, 2)
+    T, k = expert_ids.shape
+    if topk_weights is not None:
+        _require(topk_weights, "topk_weights", torch.float32, 2)
+        if tuple(topk_weights.shape) != (T, k):
+            raise ValueError("topk_weights must have the shape of expert_ids")
+    _require(workspace, "workspace", torch.uint8, 1)
+    c = _lib.MoeSchedule()
+    st = lib.moe_build_schedule_noalloc(_ptr(expert_ids), _ptr(topk_weights), T, k, E, layout,
+                                        capacity, _ptr(workspace), workspace.numel(),
+                                        ctypes.byref(c), _stream(stream))
+    _lib.check("moe_build_schedule_noalloc", st)
+    return Schedule(c, workspace)
+
+
 def grouped_gemm(A: torch.Tensor, W: torch.Tensor, offsets: torch.Tensor, *,
                  out: Optional[torch.Tensor] = None, out_dtype=None, stream=None) -> torch.Tensor:
     """Bare grouped GEMM: C[r] = A[r] @ W[e(r)]^T for rows grouped by END offsets

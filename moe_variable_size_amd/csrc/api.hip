@@ -214,18 +214,32 @@ size_t moe_schedule_workspace_bytes(int64_t T, int32_t k, int32_t E, int32_t lay
   return ws_layout(T * k, R, E, k, layout).total;
 }
 
-int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T, int32_t k,
-                       int32_t E, int32_t layout, int32_t capacity, void *workspace,
-                       size_t workspace_bytes, moe_schedule *sched, void *stream) {
+}  // extern "C"
+
+namespace moe {
+namespace {
+// The schedule build of both entry points: the schedule's arrays go into
+// `workspace`; the block tables into `tables` (static_tables) or behind the
+// arrays in the workspace.
+int build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T, int32_t k,
+                   int32_t E, int32_t layout, int32_t capacity, void *workspace,
+                   size_t workspace_bytes, moe_schedule *sched, void *stream, bool static_tables) {
   if (!expert_ids || !sched) return MOE_ERR_NULL;
   int64_t R = 0;
   int rc = check_sizes(T, k, E, layout, capacity, &R);
   if (rc) return rc;
   if (!aligned(expert_ids, 4) || (topk_weights && !aligned(topk_weights, 4))) return MOE_ERR_ALIGN;
   const WsLayout l = ws_layout(T * k, R, E, k, layout);
-  if (!workspace || workspace_bytes < l.total) return MOE_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < (static_tables ? l.scratch : l.total))
+    return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, 256)) return MOE_ERR_ALIGN;
   char *w = (char *)workspace;
+  int32_t *tables = (int32_t *)(w + l.scratch);
+  if (static_tables) {
+    size_t cap = 0;
+    if (static_schedule_scratch(&tables, &cap) != hipSuccess) return MOE_ERR_HIP;
+    if (schedule_scratch_bytes(T * k, E, k, l.ranked) > cap) return MOE_ERR_LIMIT;
+  }
   moe_schedule s;
   memset(&s, 0, sizeof(s));
   s.T = T;
@@ -257,8 +271,27 @@ int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int
   hipStream_t st = (hipStream_t)stream;
   return hip_status(
       timed(F_SCHED, st, [&] {
-        return launch_build_schedule(expert_ids, topk_weights, s, (int32_t *)(w + l.scratch), st);
+        return launch_build_schedule(expert_ids, topk_weights, s, tables, st);
       }));
+}
+}  // namespace
+}  // namespace moe
+
+extern "C" {
+
+int moe_build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t T, int32_t k,
+                       int32_t E, int32_t layout, int32_t capacity, void *workspace,
+                       size_t workspace_bytes, moe_schedule *sched, void *stream) {
+  return moe::build_schedule(expert_ids, topk_weights, T, k, E, layout, capacity, workspace,
+                             workspace_bytes, sched, stream, false);
+}
+
+int moe_build_schedule_noalloc(const int32_t *expert_ids, const float *topk_weights, int64_t T,
+                               int32_t k, int32_t E, int32_t layout, int32_t capacity,
+                               void *workspace, size_t workspace_bytes, moe_schedule *sched,
+                               void *stream) {
+  return moe::build_schedule(expert_ids, topk_weights, T, k, E, layout, capacity, workspace,
+                             workspace_bytes, sched, stream, true);
 }
 
 int grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int64_t M,

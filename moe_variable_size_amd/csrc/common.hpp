@@ -78,6 +78,9 @@ int device_cu_count();
 hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_schedule &s,
                                  int32_t *scratch, hipStream_t st);
 size_t schedule_scratch_bytes(int64_t S, int E, int k, bool ranked);
+// the current device's static block tables for the build (address and size);
+// shared by every call on that device
+hipError_t static_schedule_scratch(int32_t **tables, size_t *bytes);
 // whether the schedule also gets the rank-ordered row view (one phase per rank)
 bool rank_order_supported(int layout, int k, int E);
 hipError_t launch_tile_map(const moe_schedule &s, int N, int BM, int BN, int32_t *tile_start,

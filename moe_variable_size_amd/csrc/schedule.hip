@@ -29,6 +29,8 @@
 // deterministic and equals a stable argsort by expert.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -485,6 +487,34 @@ hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_s
   hipLaunchKernelGGL(sched_place_kernel, dim3(grid), dim3(kBlkThreads), place_smem, st, ids, w, S,
                      k, E, B, nblk, s.layout, s.capacity, (int)s.R, jobs);
   return hipGetLastError();
+}
+
+// Block tables of the build for callers that cannot allocate device memory:
+// one array per device, as large as any build needs (each of the two sort jobs
+// keeps at most kTableInts block x key counts, and one word per block), held
+// until the process ends.  Its device address is taken once per device with
+// hipGetSymbolAddress (in host code the name stands for a host-side shadow).
+constexpr size_t kStaticTableInts = 3 * (size_t)kTableInts;
+static __device__ __align__(256) int32_t sched_scratch[kStaticTableInts];
+
+hipError_t static_schedule_scratch(int32_t **tables, size_t *bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int32_t *addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(sched_scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = (int32_t *)p;
+  }
+  *tables = addr[dev];
+  *bytes = sizeof(int32_t) * kStaticTableInts;
+  return hipSuccess;
 }
 
 size_t schedule_scratch_bytes(int64_t S, int E, int k, bool ranked) {
