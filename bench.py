@@ -59,7 +59,20 @@ def _args():
                    help="minimum host time spent on the oracle sample")
     p.add_argument("--calib-copy", action="store_true",
                    help="also run a plain 256 MiB device copy (calibrates HBM byte counters)")
+    p.add_argument("--only", choices=("config3", "config4", "decode", "fp8", "gated"),
+                   help="run only this line, with --steps / --warmup as given (for profiling "
+                        "one workload's kernels); prints {\"only\": name, name: object}")
     return p.parse_args()
+
+
+def _calib_copy(torch, dev) -> None:
+    """A plain device copy of known size (256 MiB) for the HBM byte counters."""
+    src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(r, flops_step: float, min_seconds: float) -> dict:
@@ -89,10 +102,11 @@ def cpu_baseline(r, flops_step: float, min_seconds: float) -> dict:
             "blas": blas}
 
 
-def _traffic(kernel_family: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy's reading),
-    or None when there is none or the kernels changed since it was taken."""
+def _traffic(kernel_family: str, workload: str = "config2"):
+    """HBM bytes per launch of a kernel family on a workload from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE runs, scaled by a plain copy's
+    reading), or None when there is none or the kernels changed since it was
+    taken."""
     path = os.path.join(ROOT, "profiles", "traffic_counters.json")
     if not os.path.exists(path):
         return None
@@ -101,7 +115,7 @@ def _traffic(kernel_family: str):
     from moe_variable_size_amd.counters import source_digest
     if rec.get("source_sha256") != source_digest():
         return None
-    k = rec.get("kernels", {}).get(kernel_family)
+    k = rec.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel_family)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
@@ -185,7 +199,8 @@ def config3_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
             "useful_rows": useful_rows(counts),
             "roofline": {"bound": "mfma", "kernel": dom, "achieved": tf[dom],
                          "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf[dom] / PEAK_BF16_TFLOPS, 4)}}
+                         "frac": round(tf[dom] / PEAK_BF16_TFLOPS, 4),
+                         "traffic": _traffic(dom, "config3")}}
 
 
 def config4_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
@@ -227,7 +242,7 @@ def config4_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "roofline": {"bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
                          else "mfma", "bound_us": round(bound_us, 2),
-                         "frac": round(bound_us / us, 4)},
+                         "frac": round(bound_us / us, 4), "traffic": _traffic("bwd_dw", "config4")},
             "schedule_share": round(kt["build_schedule"] * 1e-3 / ms_step, 4)}
 
 
@@ -456,10 +471,19 @@ def main():
     from moe_variable_size_amd import api
     from moe_variable_size_amd import workloads as WL
 
+    dev = torch.device("cuda:0")
+    if a.only:
+        lines = {"config3": config3_line, "config4": config4_line, "decode": decode_line,
+                 "fp8": fp8_line, "gated": gated_line}
+        obj = lines[a.only](torch, api, WL, dev, a.steps, a.warmup)
+        if a.calib_copy:
+            _calib_copy(torch, dev)
+        print(json.dumps({"only": a.only, a.only: obj}), flush=True)
+        return
+
     r = WL.config2()
     T, K, N, E, k = r.T, r.K, r.N, r.E, r.k
     S = T * k
-    dev = torch.device("cuda:0")
 
     def to_dev(t):
         return torch.from_numpy(t.bits.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -502,13 +526,7 @@ def main():
         kt[f] = {"avg_us": round(tot * 1e3 / max(n, 1), 3), "launches": n}
 
     if a.calib_copy:
-        # a plain copy of known size for the HBM byte counters
-        src = torch.empty(64 << 20, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        _calib_copy(torch, dev)
 
     gemm = 2.0 * S * K * N
     flops_step = 3 * gemm + 2.0 * S * N

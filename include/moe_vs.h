@@ -126,6 +126,9 @@ typedef struct moe_schedule {
                                   each ranked launch); word 8*64 + 1 counts
                                   waits that gave up (0 unless a ranked launch
                                   did not get every compute unit)               */
+  int32_t weighted;            /* 1 when the build was given topk_weights; 0
+                                  when every row weight is 1 (the kernels then
+                                  skip the multiplications by the weight)      */
 } moe_schedule;
 
 /* Bytes of device workspace moe_build_schedule needs (256-byte aligned

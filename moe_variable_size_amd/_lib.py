@@ -51,6 +51,7 @@ class MoeSchedule(ctypes.Structure):
         ("phase_row_to_token", ctypes.c_void_p),
         ("phase_row_weight", ctypes.c_void_p),
         ("phase_sync", ctypes.c_void_p),
+        ("weighted", ctypes.c_int32),
     ]
 
 

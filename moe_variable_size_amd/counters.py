@@ -1,17 +1,24 @@
-"""HBM traffic per kernel launch from rocprofv3 counter runs.
+"""HBM traffic and matrix-core activity per kernel launch from rocprofv3
+counter runs.
 
-Two runs of the benchmark under ``rocprofv3 --pmc`` (one with FETCH_SIZE, one
-with WRITE_SIZE; both in KiB per dispatch) are reduced to the average per
-launch of each GEMM kernel family.  Each counter is scaled by what it reads for
-a plain device copy of known size (``bench.py --calib-copy`` copies 256 MiB),
-so the figures are bytes, whatever the counter's own unit or coverage.
+Two runs of one benchmark workload under ``rocprofv3 --pmc`` (one with
+FETCH_SIZE, one with WRITE_SIZE; both in KiB per dispatch) are reduced to the
+average per launch of each GEMM kernel family.  Each counter is scaled by what
+it reads for a plain device copy of known size (``bench.py --calib-copy``
+copies 256 MiB), so the figures are bytes, whatever the counter's own unit or
+coverage.  Optional runs add the matrix-core counters: one with
+SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA work in units of 512 flops),
+SQ_VALU_MFMA_BUSY_CYCLES, SQ_BUSY_CYCLES and GRBM_GUI_ACTIVE, and one with the
+derived MfmaUtil (percent of SIMD cycles with the MFMA unit busy).
 
-    python -m moe_variable_size_amd.counters --fetch DIR --write DIR \\
+    python -m moe_variable_size_amd.counters --workload config2 \\
+        --fetch DIR --write DIR [--mfma DIR] [--util DIR] \\
         --out profiles/traffic_counters.json
 
-DIR is the ``-d`` directory of a run made with ``--output-format csv``.
-The record carries the sha256 of the kernel sources; ``bench.py`` reports the
-traffic only while the sources still match.
+DIR is the ``-d`` directory of a run made with ``--output-format csv``.  The
+output file keeps one record per workload (others already in it are kept while
+the kernel sources match).  The file carries the sha256 of the kernel sources;
+``bench.py`` reports the traffic only while the sources still match.
 """
 from __future__ import annotations
 
@@ -29,11 +36,13 @@ KERNEL_SOURCES = ("moe_variable_size_amd/csrc/mfma.hip", "moe_variable_size_amd/
                   "moe_variable_size_amd/csrc/api.hip")
 COPY_BYTES = 256 << 20   # bench.py --calib-copy: 64 Mi float32 copied device to device
 
-# forward-shaped kernels: mfma_fwd_kernel<BM, BN, WGM, WGN, MODE, Tout, F8, MX>
-_FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+), (true|false), (true|false)>")
+# forward-shaped kernels: mfma_fwd_kernel<BM, BN, WGM, WGN, MODE, Tout, F8, MX, COMB>
+_FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+), (true|false), "
+                  r"(true|false)(?:, (\d+))?>")
 FWD_MODES = {0: "grouped_gemm", 1: "fused_fwd", 2: "gated_up", 3: "gated_down"}
-# input-gradient kernels: mfma_dx_kernel<NW, GB, ROWS>; weight gradient: mfma_dw_kernel<Tout, NW, RM>
-_DX = re.compile(r"mfma_dx_kernel<(\d+), (true|false), (true|false)>")
+# input-gradient kernels: mfma_dx_kernel<NW, GB, ROWS, COMB>; weight gradient:
+# mfma_dw_kernel<Tout, NW, RM>.  COMB 1 = the ranked combine ("_ranked" families).
+_DX = re.compile(r"mfma_dx_kernel<(\d+), (true|false), (true|false)(?:, (\d+))?>")
 _DW = re.compile(r"mfma_dw_kernel<[^,<>]+, (\d+), (\d+)>")
 
 
@@ -59,11 +68,13 @@ def _family(name: str):
             return None
         if fam == "fused_fwd" and bm == 64:
             fam = "decode_fwd"
-        return fam + "_mx" if mx else fam + "_fp8" if f8 else fam
+        fam = fam + "_mx" if mx else fam + "_fp8" if f8 else fam
+        return fam + "_ranked" if m.group(9) == "1" else fam
     m = _DX.search(name)
     if m:
         gb, rows = m.group(2) == "true", m.group(3) == "true"
-        return "gated_bwd_dh" if gb else "gated_bwd_dx" if rows else "bwd_dx"
+        fam = "gated_bwd_dh" if gb else "gated_bwd_dx" if rows else "bwd_dx"
+        return fam + "_ranked" if m.group(4) == "1" else fam
     m = _DW.search(name)
     if m:
         return {0: "bwd_dw", 1: "gated_bwd_dw_down", 2: "gated_bwd_dw_gu"}.get(int(m.group(2)))
@@ -71,9 +82,10 @@ def _family(name: str):
 
 
 def per_launch_kib(run_dir: str, counter: str) -> dict:
-    """Average counter value per dispatch, per kernel family.  The calibration
-    ("copy") family keeps only the copy dispatches with the largest grid: the
-    256 MiB calibration copy, not the small copies of results to the host."""
+    """Average counter value per dispatch, per kernel family ("kib" is the
+    counter's value, whatever its unit).  The calibration ("copy") family keeps
+    only the copy dispatches with the largest grid: the 256 MiB calibration
+    copy, not the small copies of results to the host."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
@@ -106,10 +118,37 @@ def per_launch_kib(run_dir: str, counter: str) -> dict:
     return {fam: {"kib": sums[fam] / counts[fam], "dispatches": counts[fam]} for fam in sums}
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+
+
+def mfma_summary(mfma_dir, util_dir) -> dict:
+    """Per kernel family: bf16 MFMA flops executed per launch (MOPS x 512),
+    the raw busy-cycle counters and the derived MfmaUtil (percent)."""
+    out = defaultdict(dict)
+    if mfma_dir:
+        for c in MFMA_COUNTERS:
+            for fam, v in per_launch_kib(mfma_dir, c).items():
+                if fam == "copy":
+                    continue
+                out[fam][c] = round(v["kib"], 1)
+                if c == "SQ_INSTS_VALU_MFMA_MOPS_BF16":
+                    out[fam]["mfma_bf16_flops"] = int(v["kib"] * 512)
+    if util_dir:
+        for fam, v in per_launch_kib(util_dir, "MfmaUtil").items():
+            if fam != "copy":
+                out[fam]["MfmaUtil_pct"] = round(v["kib"], 2)
+    return dict(out)
+
+
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--workload", required=True,
+                    help="name of the benchmark line the runs profiled (config2, config3, ...)")
     ap.add_argument("--fetch", required=True, help="rocprofv3 -d directory of the FETCH_SIZE run")
     ap.add_argument("--write", required=True, help="rocprofv3 -d directory of the WRITE_SIZE run")
+    ap.add_argument("--mfma", help="rocprofv3 -d directory of the raw matrix-core counter run")
+    ap.add_argument("--util", help="rocprofv3 -d directory of the MfmaUtil run")
     ap.add_argument("--out", required=True)
     ap.add_argument("--command", action="append", default=[],
                     help="the profiling commands, recorded in the output")
@@ -131,16 +170,26 @@ def main(argv=None) -> None:
                         "fetch_bytes": int(fb), "write_bytes": int(wb),
                         "hbm_bytes_per_launch": int(fb + wb),
                         "dispatches": [fetch[fam]["dispatches"], write[fam]["dispatches"]]}
-    rec = {"source_sha256": source_digest(),
-           "calibration": {"copy_bytes": COPY_BYTES,
-                           "fetch_kib_raw": round(fetch["copy"]["kib"], 1),
-                           "write_kib_raw": round(write["copy"]["kib"], 1),
-                           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
-           "kernels": kernels, "commands": a.command}
+    for fam, m in mfma_summary(a.mfma, a.util).items():
+        if fam in kernels:
+            kernels[fam]["mfma"] = m
+    wl = {"calibration": {"copy_bytes": COPY_BYTES,
+                          "fetch_kib_raw": round(fetch["copy"]["kib"], 1),
+                          "write_kib_raw": round(write["copy"]["kib"], 1),
+                          "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)},
+          "kernels": kernels, "commands": a.command}
+    digest = source_digest()
+    rec = {"source_sha256": digest, "workloads": {}}
+    if os.path.exists(a.out):
+        with open(a.out) as fh:
+            old = json.load(fh)
+        if old.get("source_sha256") == digest:
+            rec["workloads"] = old.get("workloads", {})
+    rec["workloads"][a.workload] = wl
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out, "w") as fh:
         json.dump(rec, fh, indent=1)
-    print(json.dumps(rec, indent=1))
+    print(json.dumps(wl, indent=1))
 
 
 if __name__ == "__main__":

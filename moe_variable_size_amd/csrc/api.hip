@@ -249,6 +249,7 @@ int build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t
   s.E = E;
   s.layout = layout;
   s.capacity = layout == MOE_LAYOUT_MASKED ? capacity : 0;
+  s.weighted = topk_weights ? 1 : 0;
   s.counts = (int32_t *)(w + l.counts);
   s.offsets = (int32_t *)(w + l.offsets);
   s.block_start = (int32_t *)(w + l.bstart);

@@ -1775,9 +1775,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 // and the per-workgroup sums even out ([NOTE] 4.2: hot experts get more work
 // units and the persistent workgroups absorb the imbalance).
 // Both operands are MN-major tiles of 32 gathered token rows, loaded by DMA.
-// The routing weights of a stage are DMA'd next to it; each dY fragment is
-// multiplied by its rows' weights in fp32 and rounded to bf16 before the MFMA
-// (one bf16 rounding per product).  The tokens that address a stage's rows are
+// With routing weights (SC), a stage's weights are DMA'd next to it and each dY
+// fragment is multiplied by its rows' weights in fp32 and rounded to bf16
+// before the MFMA (one bf16 rounding per product); a schedule built without
+// weights (all 1) takes the instantiation without that vector-ALU work.  The tokens that address a stage's rows are
 // themselves DMA'd into a small LDS ring four stages ahead, so issuing a stage
 // never waits on a global load outside the DMA accounting.
 // ============================================================================
@@ -1792,7 +1793,6 @@ struct DwArgs {
   const float *row_weight;
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes, rw_bytes;
-  int weighted;
   // zeroed by the kernel on the side (the accumulation targets of the input
   // gradient kernel that runs after it): byte ranges, NULL / 0 when unused
   float *zero0;
@@ -1820,16 +1820,16 @@ MOE_DEV void zero_share(float *p, size_t bytes, int Lb, int G) {
 // RM: operands read by schedule row instead of by token (an operand already in
 // schedule order): 0 none, DW_X_ROWS x, DW_DY_ROWS dY
 enum { DW_GATHER = 0, DW_X_ROWS = 1, DW_DY_ROWS = 2 };
-template <int NW, int RM = DW_GATHER>
+template <int NW, int RM = DW_GATHER, bool SC = true>
 struct DwOp {
   using Map = MnmajMapT<NW>;
   static constexpr int PW = Map::PER_WAVE;  // dY (and x) instructions per wave per stage
-  static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = true, PREFETCH = true;
+  static constexpr bool A_KMAJ = false, B_KMAJ = false, A_SCALED = SC, PREFETCH = true;
   static constexpr bool CHECKED_TAIL = false;  // offsets are data dependent every stage
   static constexpr bool F8 = false, MX = false;
-  // per stage: PW dY + PW x instructions, the stage's routing weights, the
-  // tokens of the stage two ahead
-  static constexpr int DMA_PER_STAGE = 2 * PW + 1 + 1;
+  // per stage: PW dY + PW x instructions, the stage's routing weights (SC),
+  // the tokens of the stage two ahead
+  static constexpr int DMA_PER_STAGE = 2 * PW + (SC ? 1 : 0) + 1;
   // LDS after the stages: per stage one 64-float weight strip per wave, then a
   // ring of TOKSLOTS slots holding one 64-token copy per wave
   static constexpr int WSTRIPS = NSTAGE * STAGE;
@@ -1840,7 +1840,7 @@ struct DwOp {
   __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
   uint32_t lds0;
   const char *lds;
-  int r0, m, wid, lane, K, N, weighted;
+  int r0, m, wid, lane, K, N;
   // the next kernel's zero range, cleared on the side: one 16-byte chunk per
   // lane with each stage's token load (this lane's next chunk zi, step zstep)
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -1900,7 +1900,7 @@ struct DwOp {
                                   : kOobOffset;
         dma16(rsX, offx, t + OPND + Map::lds_of(wid, i));
       }
-    } else if (j == 2 * PW) {
+    } else if (SC && j == 2 * PW) {
       // routing weights of the stage's 64 rows into this wave's strip
       const int qw = kt * BK + lane;
       const uint32_t offw = qw < m ? (uint32_t)(r0 + qw) * 4u : kOobOffset;
@@ -1916,22 +1916,22 @@ struct DwOp {
       zero_chunk();
     }
   }
-  // factors of the 8 reduction rows this lane holds in step `step`
+  // routing weights of the 8 reduction rows this lane holds in step `step`
   MOE_DEV void row_scale(int buf, int step, int ln, float (&w)[8]) {
     const float *src = (const float *)(lds + WSTRIPS + buf * WB + wid * 256) + step * 16 +
                        8 * (ln >> 5);
     const f32x4 a = *(const f32x4 *)src, b = *(const f32x4 *)(src + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      w[i] = weighted ? a[i] : 1.f;
-      w[4 + i] = weighted ? b[i] : 1.f;
+      w[i] = a[i];
+      w[4 + i] = b[i];
     }
   }
 };
 
 // NW waves: 4 (2 x 2 grid, 128 x 128 per wave) or 8 (4 x 2, 64 x 128 per wave:
 // two waves per SIMD, half the LDS reads per wave per MFMA step)
-template <typename Tout, int NW, int RM = DW_GATHER>
+template <typename Tout, int NW, int RM = DW_GATHER, bool SC = true>
 __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   constexpr int BM = 256, BN = 256, WGM = NW == 8 ? 4 : 2, WGN = 2;
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
@@ -1948,8 +1948,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   // the next kernel's accumulation targets: the small one now, the large one
   // (dX) a chunk per stage on the side and the rest at the end
   zero_share<NW * 64>(p.zero1, p.zero1_bytes, L, G);
-  DwOp<NW, RM> op;
-  op.zp = (typename DwOp<NW, RM>::u32x4_t *)p.zero0;
+  DwOp<NW, RM, SC> op;
+  op.zp = (typename DwOp<NW, RM, SC>::u32x4_t *)p.zero0;
   op.zn16 = p.zero0 ? p.zero0_bytes / 16 : 0;
   op.zi = (size_t)L * (NW * 64) + tid;
   op.zstep = (size_t)G * (NW * 64);
@@ -1963,7 +1963,6 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   op.lane = lane;
   op.K = K;
   op.N = N;
-  op.weighted = p.weighted;
 
   for (int round = 0;; ++round) {
     const int base = round * G;
@@ -2235,21 +2234,21 @@ static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
   return launch_dx_c<COMBINE_ATOMIC>(a, st);
 }
 
-template <int RM>
+template <int RM, bool SC>
 static hipError_t launch_dw(const DwArgs &a, hipStream_t st) {
-  constexpr size_t lds = DwOp<8, RM>::LDS_BYTES;
-  hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM>>(lds);
+  constexpr size_t lds = DwOp<8, RM, SC>::LDS_BYTES;
+  hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM, SC>>(lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM>), dim3(device_cu_count()), dim3(512), lds, st,
-                     a);
+  hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM, SC>), dim3(device_cu_count()), dim3(512), lds,
+                     st, a);
   return hipGetLastError();
 }
 
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
                        int N, float *zero0, size_t zero0_bytes, float *zero1, size_t zero1_bytes,
                        hipStream_t st) {
-  return mfma_bwd_dw_rows(dY, false, x, false, s, dW, K, N, true, zero0, zero0_bytes, zero1,
-                          zero1_bytes, st);
+  return mfma_bwd_dw_rows(dY, false, x, false, s, dW, K, N, s.weighted != 0, zero0, zero0_bytes,
+                          zero1, zero1_bytes, st);
 }
 
 hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool x_by_row,
@@ -2273,15 +2272,17 @@ hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool 
   a.dy_bytes = (uint32_t)((size_t)(dy_by_row ? s.R : s.T) * N * 2);
   a.x_bytes = (uint32_t)((size_t)(x_by_row ? s.R : s.T) * K * 2);
   a.rw_bytes = (uint32_t)((size_t)s.R * 4);
-  a.weighted = weighted ? 1 : 0;
   a.zero0 = zero0;
   a.zero0_bytes = zero0_bytes;
   a.zero1 = zero1;
   a.zero1_bytes = zero1_bytes;
+  // the instantiations the callers use: gathered operands with or without
+  // weights; x by row (the gated dW_down) weighted; dY by row (dW_gu, whose
+  // dgu already holds the weight) unweighted
   if (dy_by_row && x_by_row) return hipErrorInvalidValue;
-  if (dy_by_row) return launch_dw<DW_DY_ROWS>(a, st);
-  if (x_by_row) return launch_dw<DW_X_ROWS>(a, st);
-  return launch_dw<DW_GATHER>(a, st);
+  if (dy_by_row) return weighted ? hipErrorInvalidValue : launch_dw<DW_DY_ROWS, false>(a, st);
+  if (x_by_row) return weighted ? launch_dw<DW_X_ROWS, true>(a, st) : hipErrorInvalidValue;
+  return weighted ? launch_dw<DW_GATHER, true>(a, st) : launch_dw<DW_GATHER, false>(a, st);
 }
 
 }  // namespace moe

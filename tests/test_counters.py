@@ -20,5 +20,12 @@ def test_families_of_demangled_names():
     assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0>(DwArgs)") == "bwd_dw"
     assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 1>(DwArgs)") == "gated_bwd_dw_down"
     assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 2>(DwArgs)") == "gated_bwd_dw_gu"
+    # with the combine-mode parameter the kernels carry now (1 = ranked)
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, false, false, 0>") == "fused_fwd"
+    assert f("mfma_fwd_kernel<256, 256, 2, 4, 1, float, false, false, 1>") == "fused_fwd_ranked"
+    assert f("mfma_fwd_kernel<64, 256, 1, 4, 1, float, true, true, 0>") == "decode_fwd_mx"
+    assert C._family(ns + "mfma_dx_kernel<4, false, false, 0>(DxArgs)") == "bwd_dx"
+    assert C._family(ns + "mfma_dx_kernel<4, false, false, 1>(DxArgs)") == "bwd_dx_ranked"
+    assert C._family(ns + "mfma_dx_kernel<4, true, false, 0>(DxArgs)") == "gated_bwd_dh"
     assert C._family("__amd_rocclr_copyBuffer") == "copy"
     assert C._family(ns + "sched_hist_kernel(int const*)") is None

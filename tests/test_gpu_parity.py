@@ -241,6 +241,26 @@ def test_backward_config3():
     assert all((dW[e] == 0).all() for e in zero)
 
 
+def test_unweighted_schedule_equals_unit_weights():
+    """A schedule built without routing weights takes the weight gradient's
+    instantiation without the per-row multiplications; with every weight 1 the
+    products are the same bits, so dW equals, bit for bit, the result of a
+    schedule built with explicit unit weights (and dX too: two contributions
+    per element add in either order to the same sum)."""
+    r = _routed_small(900, 256, 320, 6, 2, seed=77, bf16=True, empty=(2,))
+    ids, x, W, dY = dev(r.expert_ids), dev(r.x), dev(r.W), dev(r.dY)
+    ones = torch.ones(r.expert_ids.shape, dtype=torch.float32, device="cuda")
+    s0 = api.moe_build_schedule(ids, None, r.E)
+    s1 = api.moe_build_schedule(ids, ones, r.E)
+    assert s0.c.weighted == 0 and s1.c.weighted == 1
+    dX0, dW0, dT0 = api.moe_fused_bwd(dY, x, W, s0)
+    dX1, dW1, dT1 = api.moe_fused_bwd(dY, x, W, s1)
+    torch.cuda.synchronize()
+    assert torch.equal(dW0.view(torch.int16), dW1.view(torch.int16)), "dW differs"
+    assert torch.equal(dX0, dX1), "dX differs"
+    assert_close(host(dT0), host(dT1).astype(np.float64), "f32", "d_topk")
+
+
 def test_weight_grad_config4():
     g = WL.config4()
     r = WL.grouped_as_routed(g)
