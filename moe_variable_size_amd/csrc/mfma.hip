@@ -100,9 +100,14 @@ MOE_DEV void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t lds) {
                : "memory", "m0");
 }
 // As dma16, with a wave-uniform byte offset `soff` added to the address (the
-// per-stage advance of a tile whose per-lane offsets stay fixed).  Only used
-// where voff + soff stays inside the lane's row; rows masked with an
-// out-of-range voff stay masked.
+// per-stage advance of a tile whose per-lane offsets stay fixed).  The
+// buffer's range check looks at voff (and an immediate offset) only; soff is
+// added after it, so a lane whose voff passes the check is not stopped at the
+// buffer's end.  Callers therefore use it only for stages that lie wholly
+// inside every row (each stage of a reduction range but the last, which takes
+// per-lane checked offsets), where voff + soff + 16 stays inside the lane's
+// row; a lane masked with voff = kOobOffset stays out of range whatever soff
+// is (buffers are smaller than 2^31 bytes).
 MOE_DEV void dma16_so(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
   const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
