@@ -1095,15 +1095,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         op.soff[i] = o;
       }
     }
-    const bool part = BM <= 64 || ws.nS > 1 || BMr < BM;  // rows / columns partly dead
+    const bool part = BM <= 64 || ws.nS > 1 || BMr < BM ||
+                      (!GATED && (ncols < BNO || c.rows < BMr));  // rows / columns partly dead
     // (gated: the live B rows are two runs, not a prefix; nothing is skipped)
     const int live_b = GATED ? BN : ncols;
     op.da.setup(wid, lane, rowoff_a, part ? c.rows : BM);
     op.db.setup(wid, lane, rowoff_b, part ? live_b : BN);
     // The tile body, instantiated per accumulator shape: MIc x NIc blocks per
     // wave (a whole tile, or a 128 x 128 / 64 x 128 sub-tile), each with its own
-    // accumulators.  SKM: MFMAs of row blocks past the last live row are left
-    // out (wave-uniform, masked decode); DSK: DMA of dead rows is left out;
+    // accumulators.  SKM: MFMAs of row blocks past the last live row and of
+    // column blocks past the last live column are left out (wave-uniform:
+    // masked decode, and whole tiles that end past a group's rows or past N,
+    // e.g. the last 256-column block of N = 1408); DSK: DMA of dead rows is left out;
     // DEEP: the streaming pipeline with more stages in flight (masked decode).
     auto tile = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_, auto DEEP_)
                     __attribute__((always_inline)) {
@@ -1111,6 +1114,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
       constexpr bool SKM = decltype(SKM_)::value, DSK = decltype(DSK_)::value;
       const int live_mi =
           SKM ? min(MIc, max(0, (c.rows - wm * 32 + 32 * WGM - 1) / (32 * WGM))) : MIc;
+      const int live_ni =
+          SKM ? min(NIc, max(0, (ncols - wn * 32 + 32 * WGN - 1) / (32 * WGN))) : NIc;
       f32x16 acc[MIc][NIc];
 #pragma unroll
       for (int mi = 0; mi < MIc; ++mi)
@@ -1148,7 +1153,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
                                                dop.parts(), acc);
       } else {
         tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8, MX>, DSK>(
-            op, lds, kb, ke, wm, wn, lane, live_mi, NIc, acc);
+            op, lds, kb, ke, wm, wn, lane, live_mi, live_ni, acc);
       }
 
       // epilogue: 4 consecutive accumulator rows share one 16-byte read of the
@@ -1349,6 +1354,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
                true_type(), false_type());
         else if (nsub == 2)
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
+               true_type(), false_type());
+        else if (ncols < BNO || c.rows < BMr)
+          tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(),
                true_type(), false_type());
         else
           tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
