@@ -5,20 +5,30 @@ One step = the whole hot path on one batch: build the routing schedule on the
 device, the fused forward (gather on load, weighted atomic scatter-combine),
 and the fused backward (dX with the routing-weight gradient, and dW).
 
-Workload (seeded, synthetic, resident in HBM before timing): T=4096 tokens,
-K=N=2048, E=8 experts, top-2 routing drawn uniformly, routing weights U[0,1),
-x, dY ~ N(0,1), W ~ N(0,1/K), bf16 storage with fp32 accumulation.
+Workload of the headline line (seeded, synthetic, resident in HBM before
+timing): T=4096 tokens, K=N=2048, E=8 experts, top-2 routing drawn uniformly,
+routing weights U[0,1), x, dY ~ N(0,1), W ~ N(0,1/K), bf16 storage with fp32
+accumulation.
 
 Metric: useful TFLOP/s = (2SKN forward + 4SKN backward + 2SN routing-weight
-gradient) / step time, S = T*top_k; padding is never counted.
+gradient) / step time, S = T*top_k; padding is never counted.  The roofline
+object is the dominant kernel's useful TFLOP/s (from HIP events on the
+kernels' own stream) against the bf16 matrix-core peak, with its measured HBM
+bytes per launch (profiles/traffic_counters.json) while the kernel sources
+match the counters.
 
-More objects ride on the same line: "decode" (masked decode forward, HBM
-GB/s), "fp8" (the 8-bit forward on the config-2 shape and the masked decode)
-and "gated_ffn" (gated expert FFN forward and backward on the balanced step
-of the page's worked example, TFLOP/s).
+More objects ride on the same line: "config3" (Zipf-skewed T=8192 K=4096
+N=1408 E=64 top-4 step, with its own roofline), "config4" (the weight
+gradient alone on S=65536 Dirichlet-sized groups, against the larger of its
+matrix-core and HBM bounds), "decode" (masked decode forward, HBM GB/s),
+"fp8" (the 8-bit forwards on the headline shape and on the masked decode),
+"gated_ffn" (gated expert FFN forward and backward on the balanced step of the
+page's worked example) and "cpu_baseline" (the float64 oracle on the host's
+cores, a bounded number of steps).
 
-Prints ONE JSON line.  --gpus above 1 is not supported (this path runs on one
-GPU) and exits with a message.
+--only LINE runs one of the extra lines by itself (for profiling one
+workload's kernels).  Prints ONE JSON line.  --gpus above 1 is not supported
+(this path runs on one GPU) and exits with a message.
 """
 from __future__ import annotations
 
@@ -242,7 +252,8 @@ def config4_line(torch, api, WL, dev, steps: int, warmup: int) -> dict:
             "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
             "roofline": {"bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (PEAK_BF16_TFLOPS * 1e12)
                          else "mfma", "bound_us": round(bound_us, 2),
-                         "frac": round(bound_us / us, 4), "traffic": _traffic("bwd_dw", "config4")},
+                         "frac": round(bound_us / us, 4),
+                         "traffic": _traffic("bwd_dw_unweighted", "config4")},
             "schedule_share": round(kt["build_schedule"] * 1e-3 / ms_step, 4)}
 
 

@@ -41,9 +41,10 @@ _FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+)
                   r"(true|false)(?:, (\d+))?>")
 FWD_MODES = {0: "grouped_gemm", 1: "fused_fwd", 2: "gated_up", 3: "gated_down"}
 # input-gradient kernels: mfma_dx_kernel<NW, GB, ROWS, COMB>; weight gradient:
-# mfma_dw_kernel<Tout, NW, RM>.  COMB 1 = the ranked combine ("_ranked" families).
+# mfma_dw_kernel<Tout, NW, RM, SC>.  COMB 1 = the ranked combine ("_ranked"
+# families); SC false = no routing weights ("_unweighted" for the plain dW).
 _DX = re.compile(r"mfma_dx_kernel<(\d+), (true|false), (true|false)(?:, (\d+))?>")
-_DW = re.compile(r"mfma_dw_kernel<[^,<>]+, (\d+), (\d+)>")
+_DW = re.compile(r"mfma_dw_kernel<[^,<>]+, (\d+), (\d+)(?:, (true|false))?>")
 
 
 def source_digest() -> str:
@@ -77,7 +78,8 @@ def _family(name: str):
         return fam + "_ranked" if m.group(4) == "1" else fam
     m = _DW.search(name)
     if m:
-        return {0: "bwd_dw", 1: "gated_bwd_dw_down", 2: "gated_bwd_dw_gu"}.get(int(m.group(2)))
+        fam = {0: "bwd_dw", 1: "gated_bwd_dw_down", 2: "gated_bwd_dw_gu"}.get(int(m.group(2)))
+        return fam + "_unweighted" if fam == "bwd_dw" and m.group(3) == "false" else fam
     return None
 
 

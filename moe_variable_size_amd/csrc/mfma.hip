@@ -4,46 +4,56 @@
 // [CARD] = "grouped-gemm-moe" model card
 // [NOTE] = "Grouped GEMM" study notes (scholia-log)
 //
-// All kernels share one tile core.
-//  * A workgroup of 4 waves (WGM x WGN) owns a BM x BN output tile made of
-//    32 x 32 blocks, each one v_mfma_f32_32x32x16_bf16 accumulator (16 fp32 per
-//    lane).  Wave (wm, wn) owns row blocks wm, wm + WGM, ... and column blocks
-//    wn, wn + WGN, ... (interleaved so a wave's LDS addresses differ by
-//    constants).
-//  * The reduction advances 32 elements per stage.  An operand tile sits in LDS
-//    in one of two layouts:
-//      K-major : [tile row][32 reduction elements], 64 B per row -- token rows
+// All kernels share one tile core (tile_multiply).
+//  * A persistent workgroup per compute unit owns a 256 x 256 fp32 output tile
+//    made of 32 x 32 blocks, each one v_mfma_f32_32x32x16_bf16 accumulator
+//    (16 fp32 per lane).  Wave grids: forward 8 waves, 2 x 4 (128 x 64 per
+//    wave, two waves per SIMD); input gradient 4 waves, 2 x 2 (128 x 128 per
+//    wave, one per SIMD: its routing-weight epilogue needs the registers);
+//    weight gradient 8 waves, 4 x 2.  Wave (wm, wn) owns row blocks wm,
+//    wm + WGM, ... and column blocks wn, wn + WGN, ...
+//  * The reduction advances 64 elements (128 bytes of a bf16 row) per stage.
+//    An operand tile sits in LDS in one of two layouts:
+//      K-major : [tile row][64 reduction elements], 128 B per row -- token rows
 //                and weight rows whose reduction index is contiguous in memory
 //                (both operands of the forward, dY in the input gradient);
-//      MN-major: [32 reduction rows][256 tile columns], 512 B per row -- operands
-//                whose reduction index is strided in memory (the weights in the
-//                input gradient, both operands of the weight gradient).
+//      MN-major: [64 reduction rows][256 tile columns], 512 B per row --
+//                operands whose reduction index is strided in memory (the
+//                weights in the input gradient, both weight-gradient operands).
 //    16-byte chunks are XOR-swizzled by the row so that the operand reads and
 //    the DMA writes are free of bank conflicts.
 //  * Tiles are loaded by direct global->LDS DMA (buffer_load ... lds, 16 bytes
 //    per lane, any global address per lane): gathered token rows land in LDS
 //    without passing through registers ([CARD] "How it works": rows gathered
-//    on load).  Out-of-range offsets of a raw buffer load return zeros, which
-//    masks rows past a group's end, columns past N and chunks past K
-//    ([GG] "Problem descriptors and the tile scheduler").
+//    on load).  A per-lane offset past the buffer returns zeros, which masks
+//    rows past a group's end and columns past N ([GG] "Problem descriptors and
+//    the tile scheduler").  Every stage but the last of a reduction range keeps
+//    fixed per-lane offsets and passes the stage's advance as the scalar
+//    offset (outside the range check, so only stages wholly inside every row
+//    take it); the last stage is checked per lane.
 //  * MFMA operands come from K-major tiles with one 16-byte read per lane and
-//    from MN-major tiles with two ds_read_b64_tr_b16 (4 x 16 transposing reads).
-//  * Four LDS stages: while stage i multiplies, stages i+1 .. i+3 are in
-//    flight ([CARD] "How it works": the next K chunk streams while the current
-//    one computes).  Each stage is two 16-deep MFMA steps; the fragments of
-//    step 1 are read while step 0 multiplies; then the waves meet at one
-//    barrier, the DMA of stage i+4 goes into the buffer just released, and the
-//    first fragments of stage i+1 are read while step 1 multiplies.  The DMA is
-//    issued from inline assembly with explicit vmcnt accounting, so the
-//    compiler's conservative waits on LDS DMA do not serialise the pipeline.
-//  * One persistent workgroup per compute unit.  Workgroup ids are remapped so
-//    that each of the 8 XCDs (one L2 each) takes a contiguous slice of the
-//    flat tile space; inside a group tiles are walked column-block-major, so the
-//    workgroups of one XCD share weight column blocks in L2 ([GG] "Problem
-//    descriptors and the tile scheduler").  Whole tiles go out in waves of one
-//    tile per workgroup (all workgroups advance through K together, which keeps
-//    the shared blocks in L2); only the last partial wave is split along K over
-//    all workgroups (stream-K), which evens out the tail.
+//    from MN-major tiles with two ds_read_b64_tr_b16 (transposing reads).
+//  * Two LDS stages of 64 KB (A then B).  A stage is four 16-deep MFMA steps
+//    (two 64-deep steps for 8-bit operands); each step's MFMAs have the next
+//    step's fragment reads placed between them; one vector-memory wait and one
+//    barrier per stage, then the last step issues the DMA of the stage two
+//    ahead into the buffer just released.  The DMA is issued from inline
+//    assembly with explicit wait accounting, so the compiler's conservative
+//    waits on LDS DMA do not serialise the pipeline.  The masked decode's
+//    64-row tiles take a streaming loop instead (tile_multiply_deep: compact
+//    stages, several in flight).
+//  * Workgroup ids are remapped so that each of the 8 XCDs (one L2 each) takes
+//    a contiguous slice of the flat tile space; inside a group tiles are
+//    walked column-block-major ([GG] "Problem descriptors and the tile
+//    scheduler": consecutive tiles share a weight column block in L2).  Whole
+//    tiles go out in rounds of one tile per workgroup; the tiles of a last
+//    partial round are cut into 8, 4 or 2 sub-tiles, each run before its
+//    workgroup's whole tiles.  Forward tiles that end past a group's rows or
+//    past N leave out the MFMAs of their dead 32-row and 32-column blocks.
+//  * Outputs of the routed forward and of the input gradient are combined by
+//    fp32 atomic adds (the default), or by plain stores and read-add-stores in
+//    rank order over the schedule's rank-ordered view (COMBINE_RANKED).  The
+//    weight gradient stores bf16 tiles through LDS.
 #include "common.hpp"
 
 #include <atomic>

@@ -27,5 +27,8 @@ def test_families_of_demangled_names():
     assert C._family(ns + "mfma_dx_kernel<4, false, false, 0>(DxArgs)") == "bwd_dx"
     assert C._family(ns + "mfma_dx_kernel<4, false, false, 1>(DxArgs)") == "bwd_dx_ranked"
     assert C._family(ns + "mfma_dx_kernel<4, true, false, 0>(DxArgs)") == "gated_bwd_dh"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, true>(DwArgs)") == "bwd_dw"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, false>(DwArgs)") == "bwd_dw_unweighted"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 2, false>(DwArgs)") == "gated_bwd_dw_gu"
     assert C._family("__amd_rocclr_copyBuffer") == "copy"
     assert C._family(ns + "sched_hist_kernel(int const*)") is None
