@@ -103,8 +103,10 @@ typedef struct moe_schedule {
                              were given), 0 for an empty row                    */
   int32_t *status;        /* [2]  {#assignments with expert id outside [0, E),
                                    #assignments dropped over capacity}          */
-  /* Rank-ordered view (contiguous layout, k <= 8 and k*E <= 1024; otherwise
-   * phases = 0 and the pointers are NULL).  The rank of an assignment is the
+  /* Rank-ordered view (contiguous layout, k <= 8 and k*E <= 1024, and built
+   * only when the combine setting in force at build time can use it:
+   * MOE_COMBINE_RANKED, or MOE_COMBINE_AUTO with k = 1; otherwise phases = 0
+   * and the pointers are NULL; the workspace size does not depend on it).  The rank of an assignment is the
    * number of valid assignments of the same token in earlier slots; the rows
    * are sorted stably by (rank, expert), so for each rank p the rows of rank p
    * form E consecutive groups (group p*E + e: rank p routed to expert e) and
@@ -396,6 +398,9 @@ int moe_set_tile_rows(int32_t rows);
  * within about half a second gives up and is counted in phase_sync (results
  * are then wrong, the call still returns).  Output column blocks (256 wide)
  * at most 64.  The fp32 sum for a token follows rank order (deterministic).
+ * The setting in force when a schedule is built also decides whether the
+ * schedule carries the rank-ordered view (see moe_schedule): set
+ * MOE_COMBINE_RANKED before building a schedule meant for ranked launches.
  * Returns MOE_ERR_SHAPE for an unknown mode.
  */
 #define MOE_COMBINE_AUTO 0

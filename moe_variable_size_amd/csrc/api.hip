@@ -135,6 +135,14 @@ std::atomic<int> g_combine{MOE_COMBINE_AUTO};
 // waits): measured on MI355X, the waits and read-backs of later ranks cost
 // more than the atomic adds they replace (config 2 forward 105-109 against
 // 104-107 us, input gradient 229-236 against 125-129 us).
+// Whether a schedule built now gets the rank-ordered view: only when a launch
+// under the present combine setting can use it (the second sort job costs
+// about a fifth of the build).
+bool rank_view_wanted(int k) {
+  const int mode = g_combine.load(std::memory_order_relaxed);
+  return mode == MOE_COMBINE_RANKED || (mode == MOE_COMBINE_AUTO && k == 1);
+}
+
 bool use_ranked(const moe_schedule &s, int64_t out_cols, bool input_grad) {
   if (s.phases == 0 || (out_cols + 255) / 256 > kRankSyncCols) return false;
   const int mode = g_combine.load(std::memory_order_relaxed);
@@ -258,7 +266,7 @@ int build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t
   s.row_to_assign = (int32_t *)(w + l.r2a);
   s.row_to_token = (int32_t *)(w + l.r2t);
   s.row_weight = (float *)(w + l.rw);
-  if (l.ranked) {
+  if (l.ranked && rank_view_wanted(k)) {
     s.phases = k;
     s.phase_counts = (int32_t *)(w + l.pcounts);
     s.phase_offsets = (int32_t *)(w + l.poffsets);

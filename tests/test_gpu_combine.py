@@ -42,9 +42,13 @@ def _run(r, mode):
         torch.cuda.synchronize()
     finally:
         api.moe_set_combine(api.MOE_COMBINE_AUTO)
-    assert sch.phases == r.k
-    sync = sch.phase_sync.cpu().numpy()
-    assert (sync == 0).all(), f"ranked counters not reset / waits gave up: {np.nonzero(sync)[0][:8]}"
+    # the view is built only when the mode at build time can use it
+    if mode == "ranked":
+        assert sch.phases == r.k
+        sync = sch.phase_sync.cpu().numpy()
+        assert (sync == 0).all(), f"ranked counters not reset / waits gave up: {np.nonzero(sync)[0][:8]}"
+    else:
+        assert sch.phases == 0
     return host(y), host(dX), host(dW), host(dT)
 
 

@@ -20,7 +20,11 @@ def _excl_blocks(counts, BM):
 
 def _check_contiguous(ids, w, E, name):
     log(f"schedule contiguous: {name} T={ids.shape[0]} k={ids.shape[1]} E={E}")
-    sch = api.moe_build_schedule(dev(ids), None if w is None else dev(w), E)
+    api.moe_set_combine(api.MOE_COMBINE_RANKED)   # so the build also makes the rank-ordered view
+    try:
+        sch = api.moe_build_schedule(dev(ids), None if w is None else dev(w), E)
+    finally:
+        api.moe_set_combine(api.MOE_COMBINE_AUTO)
     torch.cuda.synchronize()
     ref = O.routing_schedule(ids, w, E)
     R = ids.size

@@ -71,6 +71,15 @@ def _build(fn, ids, w, E, layout, cap, ws):
 ])
 def test_noalloc_schedule_matches(layout, cases):
     lib = _lib.load()
+    # the ranked setting makes the contiguous builds carry the rank-ordered view too
+    lib.moe_set_combine(2)
+    try:
+        _cases(lib, layout, cases)
+    finally:
+        lib.moe_set_combine(0)
+
+
+def _cases(lib, layout, cases):
     for i, (T, k, E, cap, bad) in enumerate(cases):
         log(f"no-alloc schedule layout={layout} call {i}: T={T} k={k} E={E} cap={cap} bad={bad}")
         ids, w = _routing(T, k, E, seed=T + 7 * E + i, bad=bad)
