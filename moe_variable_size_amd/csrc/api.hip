@@ -179,11 +179,21 @@ template <typename F>
 hipError_t timed(int fam, hipStream_t st, F &&f) {
   Timing &t = timing();
   if (!t.on) return f();
+  // an event failure only drops this launch's record; the launch still runs
   hipEvent_t a = nullptr, b = nullptr;
-  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return f();
-  hipEventRecord(a, st);
-  hipError_t e = f();
-  hipEventRecord(b, st);
+  if (hipEventCreate(&a) != hipSuccess) return f();
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return f();
+  }
+  const bool ra = hipEventRecord(a, st) == hipSuccess;
+  const hipError_t e = f();
+  const bool rb = ra && hipEventRecord(b, st) == hipSuccess;
+  if (!rb) {
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    return e;
+  }
   std::lock_guard<std::mutex> g(t.mu);
   t.ev[fam].emplace_back(a, b);
   return e;
@@ -591,8 +601,8 @@ int moe_timing_enable(int enable) {
   if (enable) {
     for (auto &v : t.ev) {
       for (auto &pr : v) {
-        hipEventDestroy(pr.first);
-        hipEventDestroy(pr.second);
+        (void)hipEventDestroy(pr.first);
+        (void)hipEventDestroy(pr.second);
       }
       v.clear();
     }
