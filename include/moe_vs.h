@@ -131,6 +131,11 @@ typedef struct moe_schedule {
   int32_t weighted;            /* 1 when the build was given topk_weights; 0
                                   when every row weight is 1 (the kernels then
                                   skip the multiplications by the weight)      */
+  int32_t *dw_queue;           /* [2] work-queue counters of the weight
+                                  gradient: zeroed by the build, left zeroed by
+                                  each launch.  Weight-gradient launches that
+                                  use the same schedule must not overlap in
+                                  time (they share these counters)             */
 } moe_schedule;
 
 /* Bytes of device workspace moe_build_schedule needs (256-byte aligned

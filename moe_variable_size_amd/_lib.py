@@ -52,6 +52,7 @@ class MoeSchedule(ctypes.Structure):
         ("phase_row_weight", ctypes.c_void_p),
         ("phase_sync", ctypes.c_void_p),
         ("weighted", ctypes.c_int32),
+        ("dw_queue", ctypes.c_void_p),
     ]
 
 

@@ -131,6 +131,11 @@ class Schedule:
     def status(self) -> torch.Tensor:
         return self._view(self.c.status, 2, torch.int32)
 
+    @property
+    def dw_queue(self) -> torch.Tensor:
+        """The weight-gradient work-queue counters (zero between launches)."""
+        return self._view(self.c.dw_queue, 2, torch.int32)
+
     # rank-ordered view (None when the schedule has none)
     @property
     def phases(self) -> int:

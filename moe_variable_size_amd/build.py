@@ -29,6 +29,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# per source: mfma.hip's weight gradient claims its next unit with an atomic
+# whose result it reads only when the current unit ends; the atomic optimizer
+# (one atomic per wave plus a broadcast of the result) would wait for the
+# result at once
+FILE_FLAGS = {"mfma.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def sources():
@@ -55,7 +60,8 @@ def build(verbose: bool = False, extra=()) -> str:
     inc = ["-I", os.path.join(ROOT, "include")]
     with tempfile.TemporaryDirectory(prefix="moe_vs_build_") as tmpd:
         objs = [os.path.join(tmpd, os.path.basename(s) + ".o") for s in srcs]
-        jobs = [[HIPCC, *FLAGS, *extra, *inc, "-c", "-o", o, s] for s, o in zip(srcs, objs)]
+        jobs = [[HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(s), ()), *extra, *inc, "-c", "-o", o, s]
+                for s, o in zip(srcs, objs)]
         with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
             list(ex.map(lambda c: _run(c, verbose), jobs))
         tmp = LIB + ".tmp"

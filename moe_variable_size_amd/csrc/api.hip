@@ -42,7 +42,7 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 struct WsLayout {
-  size_t counts, offsets, bstart, order, status, r2a, r2t, rw;
+  size_t counts, offsets, bstart, order, status, queue, r2a, r2t, rw;
   size_t pcounts, poffsets, pbstart, pr2a, pr2t, prw, psync;  // rank-ordered view (0 sizes if absent)
   size_t scratch, total;
   bool ranked;
@@ -59,6 +59,7 @@ WsLayout ws_layout(int64_t S, int64_t R, int E, int k, int layout) {
   l.bstart = o;  o = align256(o + sizeof(int32_t) * MOE_NUM_BM * (E + 1));
   l.order = o;   o = align256(o + sizeof(int32_t) * E);
   l.status = o;  o = align256(o + sizeof(int32_t) * 2);
+  l.queue = o;   o = align256(o + sizeof(int32_t) * 2);
   // row arrays carry kRowPad spare entries: kernels read row data a stage
   // (32 rows) at a time and may read past the last row (values ignored)
   l.r2a = o;     o = align256(o + sizeof(int32_t) * (R + kRowPad));
@@ -94,7 +95,7 @@ int check_sizes(int64_t T, int32_t k, int32_t E, int32_t layout, int32_t capacit
 
 int check_sched(const moe_schedule *s) {
   if (!s || !s->counts || !s->offsets || !s->block_start || !s->expert_order ||
-      !s->row_to_assign || !s->row_to_token || !s->row_weight || !s->status)
+      !s->row_to_assign || !s->row_to_token || !s->row_weight || !s->status || !s->dw_queue)
     return MOE_ERR_NULL;
   int64_t R = 0;
   int rc = check_sizes(s->T, s->k, s->E, s->layout, s->capacity, &R);
@@ -273,6 +274,7 @@ int build_schedule(const int32_t *expert_ids, const float *topk_weights, int64_t
   s.block_start = (int32_t *)(w + l.bstart);
   s.expert_order = (int32_t *)(w + l.order);
   s.status = (int32_t *)(w + l.status);
+  s.dw_queue = (int32_t *)(w + l.queue);
   s.row_to_assign = (int32_t *)(w + l.r2a);
   s.row_to_token = (int32_t *)(w + l.r2t);
   s.row_weight = (float *)(w + l.rw);

@@ -1793,10 +1793,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
 // Weight gradient: dW[e, n, kc] = sum over rows r of e of (w_r dY[tok(r), n]) x[tok(r), kc].
 // [GG] "The backward pass": a grouped GEMM whose reduction length (the group's
 // rows) varies; every expert's output is written, zeros for an empty one.  Work
-// units (expert, 256 x 256 output tile) are taken in descending expert load and
-// dealt to workgroups in a snake order, so the longest reductions start first
-// and the per-workgroup sums even out ([NOTE] 4.2: hot experts get more work
-// units and the persistent workgroups absorb the imbalance).
+// units (expert, 256 x 256 output tile) are ordered by descending expert load
+// and each workgroup takes the next one from a counter in the schedule as soon
+// as it is free, so the longest reductions start first and the short ones fill
+// in behind them ([NOTE] 4.2: hot experts get more work units and the
+// persistent workgroups absorb the imbalance; [GG] "The backward pass": the
+// hot expert's long reductions form the tail).  The last workgroup to finish
+// resets the counter.
 // Both operands are MN-major tiles of 32 gathered token rows, loaded by DMA.
 // With routing weights (SC), a stage's weights are DMA'd next to it and each dY
 // fragment is multiplied by its rows' weights in fp32 and rounded to bf16
@@ -1816,6 +1819,7 @@ struct DwArgs {
   const float *row_weight;
   int E, layout, capacity, K, N;
   uint32_t dy_bytes, x_bytes, rw_bytes;
+  int32_t *queue;  // [2]: next unit, finished workgroups (zero at launch; left zero)
   // zeroed by the kernel on the side (the accumulation targets of the input
   // gradient kernel that runs after it): byte ranges, NULL / 0 when unused
   float *zero0;
@@ -1860,6 +1864,8 @@ struct DwOp {
   static constexpr int TOKS = WSTRIPS + NSTAGE * WB;
   static constexpr int TSLOT = NW * 256;
   static constexpr size_t LDS_BYTES = (size_t)TOKS + TOKSLOTS * TSLOT;
+  // and last the indices of the units the workgroup holds (from the work queue)
+  static constexpr size_t LDS_TOTAL = LDS_BYTES + 16;  // two int slots, padded
   __amdgpu_buffer_rsrc_t rsY, rsX, rsW, rsT;
   uint32_t lds0;
   const char *lds;
@@ -1967,7 +1973,6 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   const int per_e = tn * tk;
   const int units = E * per_e;
   const int G = gridDim.x, L = logical_block();
-  // the next kernel's accumulation targets, zeroed while this one runs
   // the next kernel's accumulation targets: the small one now, the large one
   // (dX) a chunk per stage on the side and the rest at the end
   zero_share<NW * 64>(p.zero1, p.zero1_bytes, L, G);
@@ -1987,11 +1992,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   op.K = K;
   op.N = N;
 
-  for (int round = 0;; ++round) {
-    const int base = round * G;
-    if (base >= units) break;
-    const int u = base + ((round & 1) ? (G - 1 - L) : L);
-    if (u >= units) continue;
+  // Units come from the queue in order (heaviest experts first): a workgroup
+  // claims its next unit while the current one runs, so the claim's latency
+  // hides behind it.  The claimed index passes to all waves through an LDS
+  // slot (two slots: the unit being worked on and the one claimed).
+  int *const slot = (int *)(lds + DwOp<NW, RM, SC>::LDS_BYTES);
+  if (tid == 0) slot[0] = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  for (int it = 0;; ++it) {
+    const int u = slot[it & 1];
+    if ((unsigned)u >= (unsigned)units) break;  // (a counter not from a build stops too)
     const int e = p.expert_order[u / per_e];
     const int t = u - (u / per_e) * per_e;
     const int n0 = (t / tk) * BM, kc0 = (t % tk) * BN;
@@ -2000,6 +2010,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
     op.m = m;
     op.setup(n0, kc0);
     const int KI = (m + BK - 1) / BK;
+    // the claim, issued after this unit's own loads of the schedule (memory
+    // operations complete in order: issued before them, it would hold them up)
+    int claim = 0;
+    if (tid == 0) claim = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     f32x16 acc[MI][NI];
 #pragma unroll
@@ -2038,6 +2052,14 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
       if (n < N && col < K)
         *(u32x4_t *)(out + (size_t)n * K + col) = *(const u32x4_t *)(stile + rl * BN + cc);
     }
+    if (tid == 0) slot[(it + 1) & 1] = claim;
+    __syncthreads();  // the claim is visible; slot[it & 1] is free again
+  }
+  // the last workgroup out resets the queue for the next launch
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(p.queue + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1) {
+    __hip_atomic_store(p.queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.queue + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   // the part of the zero range the stages did not reach, and its trailing bytes
   while (op.zi < op.zn16) op.zero_chunk();
@@ -2259,7 +2281,7 @@ static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
 
 template <int RM, bool SC>
 static hipError_t launch_dw(const DwArgs &a, hipStream_t st) {
-  constexpr size_t lds = DwOp<8, RM, SC>::LDS_BYTES;
+  constexpr size_t lds = DwOp<8, RM, SC>::LDS_TOTAL;
   hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM, SC>>(lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM, SC>), dim3(device_cu_count()), dim3(512), lds,
@@ -2295,6 +2317,7 @@ hipError_t mfma_bwd_dw_rows(const void *dY, bool dy_by_row, const void *x, bool 
   a.dy_bytes = (uint32_t)((size_t)(dy_by_row ? s.R : s.T) * N * 2);
   a.x_bytes = (uint32_t)((size_t)(x_by_row ? s.R : s.T) * K * 2);
   a.rw_bytes = (uint32_t)((size_t)s.R * 4);
+  a.queue = s.dw_queue;
   a.zero0 = zero0;
   a.zero0_bytes = zero0_bytes;
   a.zero1 = zero1;

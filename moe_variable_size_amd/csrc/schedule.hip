@@ -116,6 +116,7 @@ struct SortJob {
   float *row_weight;
   int32_t *status;            // (by_rank 0), else NULL
   int32_t *sync;              // (by_rank 1) ranked-combine counters, zeroed here
+  int32_t *queue;             // (by_rank 0) the weight gradient's work-queue counters, zeroed here
 };
 struct SortJobs {
   SortJob j[2];
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(kBlkThreads) void sched_place_kernel(
   if (b == 2 % nblk && job.sync) {
     for (int i = tid; i < kRankSyncInts; i += kBlkThreads) job.sync[i] = 0;
   }
+  if (b == 2 % nblk && job.queue && tid < 2) job.queue[tid] = 0;
   if (b == 3 % nblk) {
     // rows no assignment fills: past the last filled row (contiguous) or past
     // each expert's valid prefix (masked)
@@ -472,6 +474,7 @@ hipError_t launch_build_schedule(const int32_t *ids, const float *w, const moe_s
   c.row_to_token = s.row_to_token;
   c.row_weight = s.row_weight;
   c.status = s.status;
+  c.queue = s.dw_queue;
   if (ranked) {
     SortJob &p = jobs.j[1];
     p.nkeys = nk1;

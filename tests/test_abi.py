@@ -86,7 +86,7 @@ def test_gemm_entry_points_reject_before_launch(lib):
     assert lib.moe_fused_fwd(P, P, ctypes.byref(s), P, 8, 8, 1, None) == 1      # empty descriptor
     s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
     for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
-              "row_weight", "status"):
+              "row_weight", "status", "dw_queue"):
         setattr(s, f, 1 << 20)
     assert lib.moe_fused_fwd(P, P, ctypes.byref(s), P, 8, 8, 9, None) == 3
     assert lib.moe_fused_fwd(None, P, ctypes.byref(s), P, 8, 8, 1, None) == 1
@@ -103,7 +103,7 @@ def test_gated_ffn_rejects_before_launch(lib):
     s = _lib.MoeSchedule()
     s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
     for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
-              "row_weight", "status"):
+              "row_weight", "status", "dw_queue"):
         setattr(s, f, 1 << 20)
     r = ctypes.byref(s)
     assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 16, 16, 0, None) == 3      # fp32: bf16 only
@@ -121,7 +121,7 @@ def test_fp8_rejects_before_launch(lib):
     s = _lib.MoeSchedule()
     s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
     for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
-              "row_weight", "status"):
+              "row_weight", "status", "dw_queue"):
         setattr(s, f, 1 << 20)
     r = ctypes.byref(s)
     assert lib.moe_fused_fwd_fp8(P, P, P, P, r, P, 24, 8, None) == 2      # K % 16 != 0
@@ -135,7 +135,7 @@ def test_gated_backward_rejects_before_launch(lib):
     s = _lib.MoeSchedule()
     s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
     for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
-              "row_weight", "status"):
+              "row_weight", "status", "dw_queue"):
         setattr(s, f, 1 << 20)
     r = ctypes.byref(s)
     assert lib.moe_gated_ffn_bwd_workspace_bytes(r, 16) >= 8 * 32 * 2
@@ -152,7 +152,7 @@ def test_mx_rejects_before_launch(lib):
     s = _lib.MoeSchedule()
     s.T, s.S, s.R, s.k, s.E = 4, 8, 8, 2, 3
     for f in ("counts", "offsets", "block_start", "expert_order", "row_to_assign", "row_to_token",
-              "row_weight", "status"):
+              "row_weight", "status", "dw_queue"):
         setattr(s, f, 1 << 20)
     r = ctypes.byref(s)
     assert lib.moe_fused_fwd_mx(P, P, P, P, r, P, 64, 8, None) == 2        # K % 128 != 0

@@ -261,6 +261,28 @@ def test_unweighted_schedule_equals_unit_weights():
     assert_close(host(dT0), host(dT1).astype(np.float64), "f32", "d_topk")
 
 
+def test_weight_grad_queue_resets():
+    """The weight gradient hands out its tiles from a counter pair in the
+    schedule workspace, which the last workgroup of each launch sets back to
+    zero: launches in a row on one schedule each see a fresh queue and give
+    the same bits; every
+    tile is reduced whole by one workgroup, so the order they are taken in
+    does not change a result."""
+    r = _routed_small(1500, 384, 520, 9, 2, seed=78, bf16=True, empty=(4,))
+    ids, x, W, dY, tw = dev(r.expert_ids), dev(r.x), dev(r.W), dev(r.dY), dev(r.topk_weights)
+    sch = api.moe_build_schedule(ids, tw, r.E)
+    assert sch.dw_queue.tolist() == [0, 0]
+    outs = []
+    for _ in range(3):
+        _, dW, _ = api.moe_fused_bwd(dY, x, W, sch, dx=False, dtopk=False)
+        torch.cuda.synchronize()
+        assert sch.dw_queue.tolist() == [0, 0]
+        outs.append(dW)
+    assert all(torch.equal(o.view(torch.int16), outs[0].view(torch.int16)) for o in outs[1:])
+    _, rw, _ = O.moe_backward(r.dY.values, r.x.values, r.W.values, r.expert_ids, r.topk_weights, r.E)
+    assert_close(host(outs[0]), rw, "bf16", "dW")
+
+
 def test_weight_grad_config4():
     g = WL.config4()
     r = WL.grouped_as_routed(g)
