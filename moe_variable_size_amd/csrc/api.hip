@@ -134,8 +134,8 @@ std::atomic<int> g_combine{MOE_COMBINE_AUTO};
 // a zeroed output.  The automatic choice is the atomic combine except for a
 // forward with one slot per token (k = 1: a single rank, only stores, no
 // waits): measured on MI355X, the waits and read-backs of later ranks cost
-// more than the atomic adds they replace (config 2 forward 105-109 against
-// 104-107 us, input gradient 229-236 against 125-129 us).
+// more than the atomic adds they replace (T = 4096, K = N = 2048, E = 8 top-2:
+// forward 105-109 against 104-107 us, input gradient 229-236 against 125-129 us).
 // Whether a schedule built now gets the rank-ordered view: only when a launch
 // under the present combine setting can use it (the second sort job costs
 // about a fifth of the build).

@@ -1193,9 +1193,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
                 const float g = acc[mi][ni][4 * j + q], u = acc[mi][ni + NH][4 * j + q];
                 hrow[cl] = f32_to_bf16(g / (1.f + __expf(-g)) * u);
                 if (gub) {
+                  // kept for the backward only: nontemporal, so the lines do
+                  // not take L2 from the weight rows (623 against 643 us for
+                  // T = 8192, K = 4096, F = 2048, E = 64 top-2)
                   float *const gr = gub + (size_t)(c.row0 + rq + q) * (2 * N) + n0 + cl;
-                  gr[0] = g;
-                  gr[N] = u;
+                  __builtin_nontemporal_store(g, gr);
+                  __builtin_nontemporal_store(u, gr + N);
                 }
               }
             }
@@ -2027,7 +2030,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
     }
     // store (exact zeros for an empty expert): the bf16 tile goes through the
     // (now idle) LDS stages, 256 x 256 row-major, and out with 16-byte row-
-    // contiguous stores (a 16-byte chunk is 8 columns; K is a multiple of 8)
+    // contiguous stores (a 16-byte chunk is 8 columns; K is a multiple of 8).
+    // The stores are nontemporal: nothing reads dW soon, and output lines
+    // kept in L2 would push out the operand rows the other units re-read
+    // (measured: 581 -> 548 us for the Zipf-routed T = 8192, E = 64 top-4 dW,
+    // 1117 -> 986 us for the gated FFN's gate/up weight gradient)
     static_assert(sizeof(Tout) == 2, "bf16 weight gradient");
     __syncthreads();  // every wave done reading the last stage
     __bf16 *const stile = (__bf16 *)lds;
@@ -2050,7 +2057,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
       const int rl = c / (BN / 8), cc = (c % (BN / 8)) * 8;
       const int n = n0 + rl, col = kc0 + cc;
       if (n < N && col < K)
-        *(u32x4_t *)(out + (size_t)n * K + col) = *(const u32x4_t *)(stile + rl * BN + cc);
+        __builtin_nontemporal_store(*(const u32x4_t *)(stile + rl * BN + cc),
+                                    (u32x4_t *)(out + (size_t)n * K + col));
     }
     if (tid == 0) slot[(it + 1) & 1] = claim;
     __syncthreads();  // the claim is visible; slot[it & 1] is free again
