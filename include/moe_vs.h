@@ -33,9 +33,14 @@
  *   - dtype codes: MOE_F32 (float) or MOE_BF16 (bfloat16 bit patterns).  The
  *     bf16 path multiplies on the matrix cores with fp32 accumulation; the fp32
  *     path is exact fp32 (no reduced-precision products) ([CARD] "How it works").
- *   - Sizes: every tensor handed to a call must be smaller than 2^31 bytes
- *     (x, dY and each expert's weight slice are addressed with 32-bit offsets);
- *     E <= 1024; 1 <= k <= 64.
+ *   - Sizes: every input tensor handed to a call must be smaller than 2^31
+ *     bytes (x, dY, each expert's weight slice and the saved gate/up values
+ *     are addressed with 32-bit offsets); E <= 1024; 1 <= k <= 64.  The
+ *     outputs y, dX, dW and a grouped GEMM's out take 64-bit addresses and
+ *     may be larger, except under the ranked combine (moe_set_combine), which
+ *     reads y / dX back with 32-bit offsets: a launch that would use it on an
+ *     output of 2^31 bytes or more returns MOE_ERR_LIMIT when the ranked
+ *     combine is forced and takes the atomic combine otherwise.
  */
 #ifndef MOE_VS_H
 #define MOE_VS_H

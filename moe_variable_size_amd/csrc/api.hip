@@ -144,12 +144,16 @@ bool rank_view_wanted(int k) {
   return mode == MOE_COMBINE_RANKED || (mode == MOE_COMBINE_AUTO && k == 1);
 }
 
+// The ranked combine reads earlier ranks' values back through 32-bit buffer
+// offsets, so its output must stay below 2^31 bytes: the automatic choice
+// takes the atomic combine (64-bit addresses, any size) for a larger output,
+// and a launch with the ranked combine forced refuses it (MOE_ERR_LIMIT).
 bool use_ranked(const moe_schedule &s, int64_t out_cols, bool input_grad) {
   if (s.phases == 0 || (out_cols + 255) / 256 > kRankSyncCols) return false;
   const int mode = g_combine.load(std::memory_order_relaxed);
   if (mode == MOE_COMBINE_ATOMIC) return false;
   if (mode == MOE_COMBINE_RANKED) return true;
-  return !input_grad && s.k == 1;
+  return !input_grad && s.k == 1 && fits(s.T, out_cols, MOE_F32);
 }
 
 // ---- kernel timing (benchmarks only) ---------------------------------------
@@ -326,7 +330,7 @@ int grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, 
   if (out_dtype != MOE_F32 && out_dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (M == 0) return MOE_OK;
   if (!A || !W || !offsets || !C) return MOE_ERR_NULL;
-  if (!fits(M, K, dtype) || !fits(N, K, dtype) || !fits(M, N, out_dtype)) return MOE_ERR_LIMIT;
+  if (!fits(M, K, dtype) || !fits(N, K, dtype)) return MOE_ERR_LIMIT;  // (C: 64-bit addresses)
   const size_t al = dtype == MOE_BF16 ? 16 : 4;
   if (!aligned(A, al) || !aligned(W, al) || !aligned(offsets, 4) || !aligned(C, esize(out_dtype)))
     return MOE_ERR_ALIGN;
@@ -346,12 +350,13 @@ int moe_fused_fwd(const void *x, const void *W, const moe_schedule *sched, float
   if (rc) return rc;
   if (!x || !W || !y) return MOE_ERR_NULL;
   const moe_schedule &s = *sched;
-  if (!fits(s.T, K, dtype) || !fits(N, K, dtype) || !fits(s.T, N, MOE_F32)) return MOE_ERR_LIMIT;
+  if (!fits(s.T, K, dtype) || !fits(N, K, dtype)) return MOE_ERR_LIMIT;
   const size_t al = dtype == MOE_BF16 ? 16 : 4;
   if (!aligned(x, al) || !aligned(W, al) || !aligned(y, 4)) return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   const bool mfma = dtype == MOE_BF16 && mfma_supported((int)K, (int)N);
   const bool ranked = mfma && use_ranked(s, N, false);
+  if (ranked && !fits(s.T, N, MOE_F32)) return MOE_ERR_LIMIT;
   if (!ranked) {
     hipError_t e = timed(F_FILL, st, [&] {
       return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
@@ -373,14 +378,14 @@ int moe_fused_fwd_fp8(const void *x_q, const float *x_scale, const void *W_q,
   if (K >= kMax32 || N >= kMax32) return MOE_ERR_LIMIT;
   if (!x_q || !x_scale || !W_q || !w_scale || !y) return MOE_ERR_NULL;
   const moe_schedule &s = *sched;
-  if ((double)s.T * K >= (double)kMax32 || (double)N * K >= (double)kMax32 ||
-      !fits(s.T, N, MOE_F32))
+  if ((double)s.T * K >= (double)kMax32 || (double)N * K >= (double)kMax32)
     return MOE_ERR_LIMIT;
   if (!aligned(x_q, 16) || !aligned(W_q, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
       !aligned(y, 4))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   const bool ranked = use_ranked(s, N, false);
+  if (ranked && !fits(s.T, N, MOE_F32)) return MOE_ERR_LIMIT;
   if (!ranked) {
     hipError_t e = timed(F_FILL, st, [&] {
       return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
@@ -400,14 +405,14 @@ int moe_fused_fwd_mx(const void *x_q, const uint8_t *x_bs, const void *W_q, cons
   if (K >= kMax32 || N >= kMax32) return MOE_ERR_LIMIT;
   if (!x_q || !x_bs || !W_q || !w_bs || !y) return MOE_ERR_NULL;
   const moe_schedule &s = *sched;
-  if ((double)s.T * K >= (double)kMax32 || (double)N * K >= (double)kMax32 ||
-      !fits(s.T, N, MOE_F32))
+  if ((double)s.T * K >= (double)kMax32 || (double)N * K >= (double)kMax32)
     return MOE_ERR_LIMIT;
   if (!aligned(x_q, 16) || !aligned(W_q, 16) || !aligned(x_bs, 4) || !aligned(w_bs, 4) ||
       !aligned(y, 4))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   const bool ranked = use_ranked(s, N, false);
+  if (ranked && !fits(s.T, N, MOE_F32)) return MOE_ERR_LIMIT;
   if (!ranked) {
     hipError_t e = timed(F_FILL, st, [&] {
       return launch_fill_zero(y, (size_t)s.T * N * sizeof(float), nullptr, 0, st);
@@ -434,7 +439,7 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
   if (!mfma_supported((int)K, (int)(2 * F)) || !mfma_supported((int)F, (int)N))
     return MOE_ERR_SHAPE;
   if (!fits(s.T, K, dtype) || !fits(2 * F, K, dtype) || !fits(N, F, dtype) ||
-      !fits(s.R, F, dtype) || !fits(s.T, N, MOE_F32))
+      !fits(s.R, F, dtype))
     return MOE_ERR_LIMIT;
   if (gu && !fits(s.R, 2 * F, MOE_F32)) return MOE_ERR_LIMIT;
   if (!aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) || !aligned(h, 16) ||
@@ -477,7 +482,7 @@ int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const voi
   if (!mfma_supported((int)K, (int)(2 * F)) || !mfma_supported((int)F, (int)N))
     return MOE_ERR_SHAPE;
   if (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(2 * F, K, dtype) ||
-      !fits(N, F, dtype) || !fits(s.R, 2 * F, MOE_F32) || !fits(s.T, K, MOE_F32))
+      !fits(N, F, dtype) || !fits(s.R, 2 * F, MOE_F32))
     return MOE_ERR_LIMIT;
   const size_t ws_need = moe_gated_ffn_bwd_workspace_bytes(sched, F);
   if (need_dgu && (!workspace || workspace_bytes < ws_need)) return MOE_ERR_WORKSPACE;
@@ -538,8 +543,7 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
   if (!dY || !x) return MOE_ERR_NULL;
   if ((dX || d_topk) && !W) return MOE_ERR_NULL;
   const moe_schedule &s = *sched;
-  if (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(N, K, dtype) || !fits(s.T, K, MOE_F32))
-    return MOE_ERR_LIMIT;
+  if (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(N, K, dtype)) return MOE_ERR_LIMIT;
   const size_t al = dtype == MOE_BF16 ? 16 : 4;
   if (!aligned(dY, al) || !aligned(x, al) || (W && !aligned(W, al)) || (dX && !aligned(dX, 4)) ||
       (dW && !aligned(dW, dtype == MOE_BF16 ? 16 : 4)) || (d_topk && !aligned(d_topk, 4)))
@@ -555,6 +559,7 @@ int moe_fused_bwd(const void *dY, const void *x, const void *W, const moe_schedu
   // first and writes those zeros on the side (it reads neither); the kernel
   // boundary orders them before the input-gradient kernel.  Otherwise one fill.
   const bool ranked = mfma && (dX || d_topk) && use_ranked(s, K, true);
+  if (ranked && !fits(s.T, K, MOE_F32)) return MOE_ERR_LIMIT;
   const size_t dxz_bytes = ranked ? 0 : dx_bytes;
   const bool dw_first = mfma && dW != nullptr;
   if (dw_first)

@@ -1208,7 +1208,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         return;
       }
       if (FUSED) {
-        // weighted scatter-combine on y with 32-bit byte offsets from its
+        // weighted scatter-combine on y with 64-bit byte offsets from its
         // base; only live rows and columns are touched (the column test is
         // left out when every column of the accumulator is live).
         //   COMBINE_ATOMIC: atomic adds (any number of rows per token);
@@ -1238,14 +1238,14 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               if (t4[q] < 0) continue;
-              const uint32_t ro = (uint32_t)t4[q] * (uint32_t)N * 4u;
+              const size_t ro = (size_t)t4[q] * (size_t)N * 4u;  // y may pass 2^32 bytes
 #pragma unroll
               for (int ni = 0; ni < NIc; ++ni) {
                 const int cl = cl0 + ni * 32 * WGN;
                 if (!all_cols && cl >= ncols) continue;
                 const float v = F8 && !MX ? w4[q] * cs[ni] * acc[mi][ni][4 * j + q]
                                           : w4[q] * acc[mi][ni][4 * j + q];
-                float *const dst = (float *)(yb + (ro + cb[ni]));
+                float *const dst = (float *)(yb + ro + cb[ni]);
                 if constexpr (!RK) {
                   unsafeAtomicAdd(dst, v);
                 } else {
@@ -1595,7 +1595,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
       // rq = wm*32 + mi*64 + 8j + 4*(lane/32); one transposing read of the K-major
       // x tile gives each lane exactly x at rows rq .. rq+3 of its column.
       const bool has_dw = p.d_w != nullptr, has_dx = p.dX != nullptr;
-      // dX scatter: atomics with 32-bit byte offsets from the base of dX, on
+      // dX scatter: atomics with 64-bit byte offsets from the base of dX, on
       // live rows and columns only
       char *const xb = (char *)p.dX;
       // GB: gate / up and dgu addressed by 32-bit byte offsets from the tile's
@@ -1688,9 +1688,9 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
             }
           }
           float dwp[4] = {0.f, 0.f, 0.f, 0.f};
-          uint32_t ro[4];
+          size_t ro[4];  // dX may pass 2^32 bytes
 #pragma unroll
-          for (int q = 0; q < 4; ++q) ro[q] = (uint32_t)t4[q] * (uint32_t)K * 4u;
+          for (int q = 0; q < 4; ++q) ro[q] = (size_t)t4[q] * (size_t)K * 4u;
           // GB: the saved gate / up values of this lane's 4 rows x NIc columns,
           // all loads issued together; per row one gate and one up offset (both
           // range-checked: a dead row reads zero, a dead column a neighbour or
@@ -1736,7 +1736,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_dx_kernel(DxArgs p) {
                   __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(dh * gv * sg), rsD, so, K * 2, 0);
                 }
               } else if (has_dx && t4[q] >= 0 && cok) {
-                float *const dst = (float *)(xb + (ro[q] + cb[ni]));
+                float *const dst = (float *)(xb + ro[q] + cb[ni]);
                 const float v = w4[q] * g;
                 if constexpr (!add) {
                   unsafeAtomicAdd(dst, v);

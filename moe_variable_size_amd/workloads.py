@@ -200,16 +200,18 @@ def config1(seed: int = BASE_SEED + 1) -> Grouped:
 def routed(name: str, T: int, K: int, N: int, E: int, k: int, *, seed: int, bf16: bool = True,
            routing: str = "uniform", zipf_s: float = 1.2, n_zero: int = 0,
            weights: str = "uniform", with_dy: bool = True, capacity: int = 0,
-           dense: bool = True) -> Routed:
+           dense: bool = True, with_x: bool = True) -> Routed:
     """Generic routed workload.  Draw order: x, W, ids, weights, dY, each from its
     own child stream of ``seed``.  ``dense=False`` skips x, W and dY (routing
-    only); the routing drawn is the same either way."""
+    only); ``with_x=False`` skips x alone (for a backward that never reads it);
+    the other draws are the same either way."""
     ss = np.random.SeedSequence(seed)
     s_x, s_w, s_r, s_dy = ss.spawn(4)
     x = Wv = None
     if dense:
-        rng_x = np.random.Generator(np.random.PCG64(s_x))
-        x = rng_x.standard_normal((T, K), dtype=np.float32)
+        if with_x:
+            rng_x = np.random.Generator(np.random.PCG64(s_x))
+            x = rng_x.standard_normal((T, K), dtype=np.float32)
         Wv = _normal_blocks(s_w, E, (N, K), 1.0 / np.sqrt(K))
     rng = np.random.Generator(np.random.PCG64(s_r))
     notes = {}
@@ -236,7 +238,7 @@ def routed(name: str, T: int, K: int, N: int, E: int, k: int, *, seed: int, bf16
     if with_dy and dense:
         rng_dy = np.random.Generator(np.random.PCG64(s_dy))
         dY = _make(rng_dy.standard_normal((T, N), dtype=np.float32), bf16)
-    return Routed(name, T, K, N, E, k, _make(x, bf16) if dense else None,
+    return Routed(name, T, K, N, E, k, _make(x, bf16) if x is not None else None,
                   _make(Wv, bf16) if dense else None, ids, w, dY,
                   capacity=capacity, seed=seed, notes=notes)
 
