@@ -41,10 +41,11 @@ _FWD = re.compile(r"mfma_fwd_kernel<(\d+), (\d+), (\d+), (\d+), (\d+), ([^,<>]+)
                   r"(true|false)(?:, (\d+))?>")
 FWD_MODES = {0: "grouped_gemm", 1: "fused_fwd", 2: "gated_up", 3: "gated_down"}
 # input-gradient kernels: mfma_dx_kernel<NW, GB, ROWS, COMB>; weight gradient:
-# mfma_dw_kernel<Tout, NW, RM, SC>.  COMB 1 = the ranked combine ("_ranked"
-# families); SC false = no routing weights ("_unweighted" for the plain dW).
+# mfma_dw_kernel<Tout, NW, RM, SC, DYN>.  COMB 1 = the ranked combine
+# ("_ranked" families); SC false = no routing weights ("_unweighted" for the
+# plain dW); DYN (work queue or static deal) does not split a family.
 _DX = re.compile(r"mfma_dx_kernel<(\d+), (true|false), (true|false)(?:, (\d+))?>")
-_DW = re.compile(r"mfma_dw_kernel<[^,<>]+, (\d+), (\d+)(?:, (true|false))?>")
+_DW = re.compile(r"mfma_dw_kernel<[^,<>]+, (\d+), (\d+)(?:, (true|false))?(?:, (?:true|false))?>")
 
 
 def source_digest() -> str:

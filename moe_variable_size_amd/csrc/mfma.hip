@@ -1963,7 +1963,9 @@ struct DwOp {
 
 // NW waves: 4 (2 x 2 grid, 128 x 128 per wave) or 8 (4 x 2, 64 x 128 per wave:
 // two waves per SIMD, half the LDS reads per wave per MFMA step)
-template <typename Tout, int NW, int RM = DW_GATHER, bool SC = true>
+// DYN: units from the work queue (chosen by the host when there are more than
+// two rounds of units), else the static deal.
+template <typename Tout, int NW, int RM = DW_GATHER, bool SC = true, bool DYN = true>
 __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   constexpr int BM = 256, BN = 256, WGM = NW == 8 ? 4 : 2, WGN = 2;
   constexpr int MI = BM / WGM / 32, NI = BN / WGN / 32;
@@ -1995,16 +1997,29 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
   op.K = K;
   op.N = N;
 
-  // Units come from the queue in order (heaviest experts first): a workgroup
-  // claims its next unit while the current one runs, so the claim's latency
-  // hides behind it.  The claimed index passes to all waves through an LDS
-  // slot (two slots: the unit being worked on and the one claimed).
+  // Units are ordered heaviest experts first.  With more than two rounds of
+  // them they come from the queue: a workgroup claims its next unit while the
+  // current one runs, so the claim's latency hides behind it, and the claimed
+  // index passes to all waves through an LDS slot (two slots: the unit being
+  // worked on and the one claimed).  With at most two rounds the queue has
+  // nothing to rebalance and its claims only cost: round r deals unit
+  // r G + L (r even) or r G + G - 1 - L (r odd) to logical workgroup L.
+  constexpr bool dyn = DYN;
   int *const slot = (int *)(lds + DwOp<NW, RM, SC>::LDS_BYTES);
-  if (tid == 0) slot[0] = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
+  if constexpr (dyn) {
+    if (tid == 0) slot[0] = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+  }
   for (int it = 0;; ++it) {
-    const int u = slot[it & 1];
-    if ((unsigned)u >= (unsigned)units) break;  // (a counter not from a build stops too)
+    int u;
+    if constexpr (dyn) {
+      u = slot[it & 1];
+      if ((unsigned)u >= (unsigned)units) break;  // (a counter not from a build stops too)
+    } else {
+      if (it * G >= units) break;
+      u = it * G + ((it & 1) ? G - 1 - L : L);
+      if (u >= units) continue;
+    }
     const int e = p.expert_order[u / per_e];
     const int t = u - (u / per_e) * per_e;
     const int n0 = (t / tk) * BM, kc0 = (t % tk) * BN;
@@ -2016,7 +2031,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
     // the claim, issued after this unit's own loads of the schedule (memory
     // operations complete in order: issued before them, it would hold them up)
     int claim = 0;
-    if (tid == 0) claim = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dyn && tid == 0)
+      claim = __hip_atomic_fetch_add(p.queue, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     f32x16 acc[MI][NI];
 #pragma unroll
@@ -2060,8 +2076,10 @@ __global__ __launch_bounds__(NW * 64) void mfma_dw_kernel(DwArgs p) {
         __builtin_nontemporal_store(*(const u32x4_t *)(stile + rl * BN + cc),
                                     (u32x4_t *)(out + (size_t)n * K + col));
     }
-    if (tid == 0) slot[(it + 1) & 1] = claim;
-    __syncthreads();  // the claim is visible; slot[it & 1] is free again
+    if constexpr (dyn) {
+      if (tid == 0) slot[(it + 1) & 1] = claim;
+      __syncthreads();  // the claim is visible; slot[it & 1] is free again
+    }
   }
   // the last workgroup out resets the queue for the next launch
   if (tid == 0 &&
@@ -2287,14 +2305,24 @@ static hipError_t launch_dx(const DxArgs &a, hipStream_t st) {
   return launch_dx_c<COMBINE_ATOMIC>(a, st);
 }
 
+template <int RM, bool SC, bool DYN>
+static hipError_t launch_dw_q(const DwArgs &a, hipStream_t st) {
+  constexpr size_t lds = DwOp<8, RM, SC>::LDS_TOTAL;
+  hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM, SC, DYN>>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM, SC, DYN>), dim3(device_cu_count()), dim3(512),
+                     lds, st, a);
+  return hipGetLastError();
+}
+
+// the work queue only with more than two rounds of units (a round: one unit
+// per workgroup, one workgroup per compute unit)
 template <int RM, bool SC>
 static hipError_t launch_dw(const DwArgs &a, hipStream_t st) {
-  constexpr size_t lds = DwOp<8, RM, SC>::LDS_TOTAL;
-  hipError_t e = set_smem<mfma_dw_kernel<bf16_t, 8, RM, SC>>(lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((mfma_dw_kernel<bf16_t, 8, RM, SC>), dim3(device_cu_count()), dim3(512), lds,
-                     st, a);
-  return hipGetLastError();
+  const long long units =
+      (long long)a.E * ((a.N + 255) / 256) * ((a.K + 255) / 256);
+  return units > 2LL * device_cu_count() ? launch_dw_q<RM, SC, true>(a, st)
+                                         : launch_dw_q<RM, SC, false>(a, st);
 }
 
 hipError_t mfma_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,

@@ -30,5 +30,10 @@ def test_families_of_demangled_names():
     assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, true>(DwArgs)") == "bwd_dw"
     assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, false>(DwArgs)") == "bwd_dw_unweighted"
     assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 2, false>(DwArgs)") == "gated_bwd_dw_gu"
+    # with the work-queue parameter
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, true, true>(DwArgs)") == "bwd_dw"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, true, false>(DwArgs)") == "bwd_dw"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 0, false, true>(DwArgs)") == "bwd_dw_unweighted"
+    assert C._family(ns + "mfma_dw_kernel<unsigned short, 8, 1, true, false>(DwArgs)") == "gated_bwd_dw_down"
     assert C._family("__amd_rocclr_copyBuffer") == "copy"
     assert C._family(ns + "sched_hist_kernel(int const*)") is None

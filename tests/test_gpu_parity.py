@@ -261,14 +261,17 @@ def test_unweighted_schedule_equals_unit_weights():
     assert_close(host(dT0), host(dT1).astype(np.float64), "f32", "d_topk")
 
 
-def test_weight_grad_queue_resets():
-    """The weight gradient hands out its tiles from a counter pair in the
-    schedule workspace, which the last workgroup of each launch sets back to
-    zero: launches in a row on one schedule each see a fresh queue and give
-    the same bits; every
-    tile is reduced whole by one workgroup, so the order they are taken in
-    does not change a result."""
-    r = _routed_small(1500, 384, 520, 9, 2, seed=78, bf16=True, empty=(4,))
+@pytest.mark.parametrize("K,N,E", [
+    (384, 520, 9),      # 54 units (expert x 256 x 256 tile): two rounds or fewer, dealt statically
+    (1024, 2048, 20),   # 640 units: more than two rounds on 256 compute units, from the queue
+])
+def test_weight_grad_queue_resets(K, N, E):
+    """With more than two rounds of units the weight gradient hands them out
+    from a counter pair in the schedule workspace, which the last workgroup of
+    each launch sets back to zero: launches in a row on one schedule each see a
+    fresh queue and give the same bits; every tile is reduced whole by one
+    workgroup, so the order the tiles are taken in does not change a result."""
+    r = _routed_small(1500, K, N, E, 2, seed=78, bf16=True, empty=(4,))
     ids, x, W, dY, tw = dev(r.expert_ids), dev(r.x), dev(r.W), dev(r.dY), dev(r.topk_weights)
     sch = api.moe_build_schedule(ids, tw, r.E)
     assert sch.dw_queue.tolist() == [0, 0]
