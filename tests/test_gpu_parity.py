@@ -303,11 +303,17 @@ def test_weight_grad_config4():
 # ----------------------------------------------------------------------------
 # graph capture: no host sync anywhere in schedule + forward + backward
 # ----------------------------------------------------------------------------
-def test_graph_capture_layer():
+@pytest.mark.parametrize("T,K,N,E", [
+    (512, 256, 256, 8),
+    (1500, 1024, 2048, 20),   # 640 weight-gradient units: the work-queue instantiation
+])
+def test_graph_capture_layer(T, K, N, E):
     """Build the schedule, run forward and backward inside one captured HIP
     graph ([GG] "What to do next": no device-to-host sync, capture the layer);
-    every replay, with eager work in between, equals the eager result."""
-    r = _routed_small(512, 256, 256, 8, 2, seed=12, bf16=True, empty=(5,))
+    every replay, with eager work in between, equals the eager result (the
+    weight gradient's queue counters are reset by the kernel itself, so a
+    replay finds them zero)."""
+    r = _routed_small(T, K, N, E, 2, seed=12, bf16=True, empty=(5,))
     ids, w, x, W, dY = dev(r.expert_ids), dev(r.topk_weights), dev(r.x), dev(r.W), dev(r.dY)
     E = r.E
 
