@@ -279,16 +279,17 @@ int moe_fused_fwd_mx(const void *x_q, const uint8_t *x_bs, const void *W_q, cons
  * with silu(z) = z / (1 + exp(-z)), r the schedule row of an assignment, t_r,
  * e_r its token and expert.
  *   x [T, K], W_gu [E, 2F, K] (rows 0..F-1 gate, F..2F-1 up) and
- *   W_down [E, N, F]: bf16 only (MOE_ERR_DTYPE otherwise); K, F and N
- *   multiples of 8 (MOE_ERR_SHAPE otherwise); x, W_gu, W_down and h 16-byte
- *   aligned.
- *   h [sched->R, F] bf16, written for every valid row of the schedule in
+ *   W_down [E, N, F] in `dtype` (MOE_BF16 or MOE_F32).  bf16 with K, F and N
+ *   multiples of 8 runs on the matrix cores (x, W_gu, W_down, h and gu then
+ *   16-byte aligned); fp32, or bf16 with other sizes, runs on the vector ALUs
+ *   with exact fp32 products (element alignment only, any sizes).
+ *   h [sched->R, F] in `dtype`, written for every valid row of the schedule in
  *   schedule row order (kept for a backward pass); rows of empty masked slots
- *   and rows at or past offsets[E-1] are left untouched.  h is rounded to bf16
- *   before the down projection.
+ *   and rows at or past offsets[E-1] are left untouched.  h is rounded to
+ *   `dtype` before the down projection.
  *   gu [sched->R, 2F] float or NULL: when given, the gate values g (columns
  *   0..F-1) and up values u (F..2F-1) of every valid row as accumulated (fp32),
- *   which moe_gated_ffn_bwd needs; same rows as h.  16-byte aligned.
+ *   which moe_gated_ffn_bwd needs; same rows as h.
  *   y [T, N] float, OVERWRITTEN (zeroed by the call, then accumulated).
  * Three launches on `stream`: the gated up-projection, the zeroing of y and
  * the down projection.
@@ -297,8 +298,8 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
                       const moe_schedule *sched, void *h, void *gu, float *y, int64_t K,
                       int64_t F, int64_t N, int32_t dtype, void *stream);
 
-/* Bytes of device workspace moe_gated_ffn_bwd needs (its [R, 2F] bf16
- * gradient of the gate/up values); 0 for invalid arguments. */
+/* Bytes of device workspace moe_gated_ffn_bwd needs (its [R, 2F] gradient of
+ * the gate/up values, sized for either dtype); 0 for invalid arguments. */
 size_t moe_gated_ffn_bwd_workspace_bytes(const moe_schedule *sched, int64_t F);
 
 /*
@@ -312,16 +313,19 @@ size_t moe_gated_ffn_bwd_workspace_bytes(const moe_schedule *sched, int64_t F);
  *   dW_gu[e]   = sum over rows of e of dgu[r]^T x[t_r]
  *   dW_down[e] = sum over rows of e of (w_r dY[t_r])^T h[r]   (0 for empty experts)
  *   d_topk[t, j] = dY[t] . (h[r] W_down[e]^T), the unweighted down output.
- *   dY [T, N], x [T, K], W_gu [E, 2F, K], W_down [E, N, F] and h [R, F]
- *   bf16, gu [R, 2F] float (h and gu saved by the forward with the same
- *   schedule); all 16-byte aligned, as are dW_gu and dW_down.  dX [T, K] float, dW_gu [E, 2F, K] and dW_down [E, N, F] bf16,
+ *   dY [T, N], x [T, K], W_gu [E, 2F, K], W_down [E, N, F] and h [R, F] in
+ *   `dtype`, gu [R, 2F] float (h and gu saved by the forward with the same
+ *   schedule); on the matrix-core path (bf16, K, F, N multiples of 8) all
+ *   16-byte aligned, as are dW_gu and dW_down; else element alignment.
+ *   dX [T, K] float, dW_gu [E, 2F, K] and dW_down [E, N, F] in `dtype`,
  *   d_topk [T, k] float: each OVERWRITTEN, or NULL to skip.
  *   workspace: moe_gated_ffn_bwd_workspace_bytes(sched, F) bytes, 256-byte
  *   aligned (required when dX or dW_gu is asked for).
- * Up to four launches on `stream`: dW_down (which zeroes dX and d_topk on the
- * side; a fill launch when dW_down is NULL), the per-row dh / dgu / d_topk
- * kernel, dX, dW_gu.  The routing weight enters through dh, so dX and dW_gu
- * take dgu unweighted.
+ * Up to four launches on `stream` (matrix cores): dW_down (which zeroes dX and
+ * d_topk on the side; a fill launch when dW_down is NULL), the per-row dh /
+ * dgu / d_topk kernel, dX, dW_gu; the vector-ALU path zeroes with a fill
+ * launch first.  The routing weight enters through dh, so dX and dW_gu take
+ * dgu unweighted.
  */
 int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const void *W_down,
                       const moe_schedule *sched, const void *gu, const void *h, float *dX,

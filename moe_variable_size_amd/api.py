@@ -338,13 +338,17 @@ def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor,
     """Gated expert FFN forward: h = silu(x W_gate^T) * (x W_up^T) per schedule
     row from one grouped GEMM over W_gu [E, 2F, K] (gate rows, then up rows),
     then y = the weighted scatter-combine of h W_down^T, W_down [E, N, F]
-    ([GG] "Choosing an implementation").  Returns (y [T, N] float32,
-    h [R, F] bfloat16) and, with ``save_gu`` (or ``gu`` given), also the saved
-    gate/up values gu [R, 2F] float32 the backward needs."""
+    ([GG] "Choosing an implementation").  Inputs all bfloat16 or all float32.
+    Returns (y [T, N] float32, h [R, F] in the input dtype) and, with
+    ``save_gu`` (or ``gu`` given), also the saved gate/up values gu [R, 2F]
+    float32 the backward needs."""
     lib = _lib.load()
-    _require(x, "x", torch.bfloat16, 2)
-    _require(W_gu, "W_gu", torch.bfloat16, 3)
-    _require(W_down, "W_down", torch.bfloat16, 3)
+    _require(x, "x", None, 2)
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    dt = x.dtype
+    _require(W_gu, "W_gu", dt, 3)
+    _require(W_down, "W_down", dt, 3)
     T, K = x.shape
     E, F2, K2 = W_gu.shape
     E2, N, F = W_down.shape
@@ -352,17 +356,17 @@ def moe_gated_ffn_fwd(x: torch.Tensor, W_gu: torch.Tensor, W_down: torch.Tensor,
         raise ValueError("shape mismatch between x [T,K], W_gu [E,2F,K], W_down [E,N,F] and the schedule")
     with _on(stream):
         if h is None:
-            h = torch.empty((sched.c.R, F), dtype=torch.bfloat16, device=x.device)
+            h = torch.empty((sched.c.R, F), dtype=dt, device=x.device)
         if y is None:
             y = torch.empty((T, N), dtype=torch.float32, device=x.device)
         if gu is None and save_gu:
             gu = torch.empty((sched.c.R, 2 * F), dtype=torch.float32, device=x.device)
-    _require_out(h, "h", torch.bfloat16, (sched.c.R, F), x.device)
+    _require_out(h, "h", dt, (sched.c.R, F), x.device)
     _require_out(y, "y", torch.float32, (T, N), x.device)
     if gu is not None:
         _require_out(gu, "gu", torch.float32, (sched.c.R, 2 * F), x.device)
     st = lib.moe_gated_ffn_fwd(_ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c), _ptr(h),
-                               _ptr(gu), _ptr(y), K, F, N, MOE_BF16, _stream(stream))
+                               _ptr(gu), _ptr(y), K, F, N, _DTYPES[dt], _stream(stream))
     _lib.check("moe_gated_ffn_fwd", st)
     return (y, h, gu) if gu is not None else (y, h)
 
@@ -371,12 +375,15 @@ def moe_gated_ffn_bwd(dY: torch.Tensor, x: torch.Tensor, W_gu: torch.Tensor, W_d
                       sched: Schedule, gu: torch.Tensor, h: torch.Tensor, *, dx: bool = True,
                       dw_gu: bool = True, dw_down: bool = True, dtopk: bool = True, stream=None):
     """Gated expert FFN backward from the saved gu and h.  Returns (dX [T, K]
-    float32 | None, dW_gu [E, 2F, K] bf16 | None, dW_down [E, N, F] bf16 |
-    None, d_topk [T, k] float32 | None)."""
+    float32 | None, dW_gu [E, 2F, K] | None, dW_down [E, N, F] | None (both in
+    the input dtype), d_topk [T, k] float32 | None)."""
     lib = _lib.load()
+    if x.dtype not in _DTYPES:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    dt = x.dtype
     for t, name, nd in ((dY, "dY", 2), (x, "x", 2), (W_gu, "W_gu", 3), (W_down, "W_down", 3),
                         (h, "h", 2)):
-        _require(t, name, torch.bfloat16, nd)
+        _require(t, name, dt, nd)
     _require(gu, "gu", torch.float32, 2)
     T, K = x.shape
     E, F2, _ = W_gu.shape
@@ -389,15 +396,15 @@ def moe_gated_ffn_bwd(dY: torch.Tensor, x: torch.Tensor, W_gu: torch.Tensor, W_d
     ws_bytes = int(lib.moe_gated_ffn_bwd_workspace_bytes(ctypes.byref(sched.c), F))
     with _on(stream):
         dX = torch.empty((T, K), dtype=torch.float32, device=dev) if dx else None
-        dWgu = torch.empty((E, 2 * F, K), dtype=torch.bfloat16, device=dev) if dw_gu else None
-        dWd = torch.empty((E, N, F), dtype=torch.bfloat16, device=dev) if dw_down else None
+        dWgu = torch.empty((E, 2 * F, K), dtype=dt, device=dev) if dw_gu else None
+        dWd = torch.empty((E, N, F), dtype=dt, device=dev) if dw_down else None
         dT = torch.empty((T, sched.c.k), dtype=torch.float32, device=dev) if dtopk else None
         # dgu workspace: freed into this stream's pool when the call returns, so
         # it is not reused before the launches queued here have run
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     st = lib.moe_gated_ffn_bwd(_ptr(dY), _ptr(x), _ptr(W_gu), _ptr(W_down), ctypes.byref(sched.c),
                                _ptr(gu), _ptr(h), _ptr(dX), _ptr(dWgu), _ptr(dWd), _ptr(dT), K, F, N,
-                               MOE_BF16, _ptr(ws), ws_bytes, _stream(stream))
+                               _DTYPES[dt], _ptr(ws), ws_bytes, _stream(stream))
     _lib.check("moe_gated_ffn_bwd", st)
     return dX, dWgu, dWd, dT
 

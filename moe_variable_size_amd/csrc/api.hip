@@ -156,6 +156,13 @@ bool use_ranked(const moe_schedule &s, int64_t out_cols, bool input_grad) {
   return !input_grad && s.k == 1 && fits(s.T, out_cols, MOE_F32);
 }
 
+// The gated FFN's products take the matrix cores for bf16 with K, F and N
+// multiples of 8 (both of its GEMM shapes then fit them).
+bool gated_mfma(int32_t dtype, int64_t K, int64_t F, int64_t N) {
+  return dtype == MOE_BF16 && mfma_supported((int)K, (int)(2 * F)) &&
+         mfma_supported((int)F, (int)N);
+}
+
 // ---- kernel timing (benchmarks only) ---------------------------------------
 const char *const kFamilies[] = {"build_schedule", "fill_zero", "grouped_gemm", "fused_fwd",
                                  "bwd_dx", "bwd_dw", "tile_map", "gated_up", "gated_down",
@@ -433,21 +440,25 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
   if (rc) return rc;
   if (F < 1) return MOE_ERR_SHAPE;
   if (F >= kMax32) return MOE_ERR_LIMIT;
-  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (!x || !W_gu || !W_down || !h || !y) return MOE_ERR_NULL;
   const moe_schedule &s = *sched;
-  if (!mfma_supported((int)K, (int)(2 * F)) || !mfma_supported((int)F, (int)N))
-    return MOE_ERR_SHAPE;
-  if (!fits(s.T, K, dtype) || !fits(2 * F, K, dtype) || !fits(N, F, dtype) ||
-      !fits(s.R, F, dtype))
-    return MOE_ERR_LIMIT;
-  if (gu && !fits(s.R, 2 * F, MOE_F32)) return MOE_ERR_LIMIT;
-  if (!aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) || !aligned(h, 16) ||
-      (gu && !aligned(gu, 16)) || !aligned(y, 4))
+  // matrix cores for bf16 with K, F, N multiples of 8; the vector-ALU kernels
+  // (64-bit addressing, element alignment) otherwise
+  const bool mfma = gated_mfma(dtype, K, F, N);
+  if (mfma) {
+    if (!fits(s.T, K, dtype) || !fits(2 * F, K, dtype) || !fits(N, F, dtype) ||
+        !fits(s.R, F, dtype))
+      return MOE_ERR_LIMIT;
+    if (gu && !fits(s.R, 2 * F, MOE_F32)) return MOE_ERR_LIMIT;
+  }
+  const size_t al = mfma ? 16 : esize(dtype);
+  if (!aligned(x, al) || !aligned(W_gu, al) || !aligned(W_down, al) || !aligned(h, al) ||
+      (gu && !aligned(gu, mfma ? 16 : 4)) || !aligned(y, 4))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = timed(F_GATED_UP, st, [&] {
-    return mfma_gated_up(x, W_gu, s, h, gu, (int)K, (int)F, st);
+    return mfma ? mfma_gated_up(x, W_gu, s, h, gu, (int)K, (int)F, st)
+                : simt_gated_up(x, W_gu, s, h, (float *)gu, (int)K, (int)F, dtype, st);
   });
   if (e == hipSuccess)
     e = timed(F_FILL, st, [&] {
@@ -455,14 +466,15 @@ int moe_gated_ffn_fwd(const void *x, const void *W_gu, const void *W_down,
     });
   if (e == hipSuccess)
     e = timed(F_GATED_DOWN, st, [&] {
-      return mfma_fused_fwd(h, W_down, s, y, (int)F, (int)N, true, false, st);
+      return mfma ? mfma_fused_fwd(h, W_down, s, y, (int)F, (int)N, true, false, st)
+                  : simt_gated_down(h, W_down, s, y, (int)F, (int)N, dtype, st);
     });
   return hip_status(e);
 }
 
 size_t moe_gated_ffn_bwd_workspace_bytes(const moe_schedule *sched, int64_t F) {
   if (!sched || F < 1 || F >= kMax32) return 0;
-  return align256((size_t)sched->R * 2 * (size_t)F * 2);  // dgu [R, 2F] bf16
+  return align256((size_t)sched->R * 2 * (size_t)F * 4);  // dgu [R, 2F], fp32 at most
 }
 
 int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const void *W_down,
@@ -475,20 +487,19 @@ int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const voi
   if (rc) return rc;
   if (F < 1) return MOE_ERR_SHAPE;
   if (F >= kMax32) return MOE_ERR_LIMIT;
-  if (dtype != MOE_BF16) return MOE_ERR_DTYPE;
   if (!dY || !x || !W_gu || !W_down || !gu || !h) return MOE_ERR_NULL;
   const moe_schedule &s = *sched;
   const bool need_dgu = dX || dW_gu;
-  if (!mfma_supported((int)K, (int)(2 * F)) || !mfma_supported((int)F, (int)N))
-    return MOE_ERR_SHAPE;
-  if (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(2 * F, K, dtype) ||
-      !fits(N, F, dtype) || !fits(s.R, 2 * F, MOE_F32))
+  const bool mfma = gated_mfma(dtype, K, F, N);
+  if (mfma && (!fits(s.T, K, dtype) || !fits(s.T, N, dtype) || !fits(2 * F, K, dtype) ||
+               !fits(N, F, dtype) || !fits(s.R, 2 * F, MOE_F32)))
     return MOE_ERR_LIMIT;
   const size_t ws_need = moe_gated_ffn_bwd_workspace_bytes(sched, F);
   if (need_dgu && (!workspace || workspace_bytes < ws_need)) return MOE_ERR_WORKSPACE;
-  if (!aligned(dY, 16) || !aligned(x, 16) || !aligned(W_gu, 16) || !aligned(W_down, 16) ||
-      !aligned(gu, 16) || !aligned(h, 16) || (dX && !aligned(dX, 4)) ||
-      (dW_gu && !aligned(dW_gu, 16)) || (dW_down && !aligned(dW_down, 16)) ||
+  const size_t al = mfma ? 16 : esize(dtype);
+  if (!aligned(dY, al) || !aligned(x, al) || !aligned(W_gu, al) || !aligned(W_down, al) ||
+      !aligned(gu, mfma ? 16 : 4) || !aligned(h, al) || (dX && !aligned(dX, 4)) ||
+      (dW_gu && !aligned(dW_gu, al)) || (dW_down && !aligned(dW_down, al)) ||
       (d_topk && !aligned(d_topk, 4)) || (workspace && !aligned(workspace, 256)))
     return MOE_ERR_ALIGN;
   hipStream_t st = (hipStream_t)stream;
@@ -496,6 +507,29 @@ int moe_gated_ffn_bwd(const void *dY, const void *x, const void *W_gu, const voi
   const size_t dx_bytes = dX ? (size_t)s.T * K * sizeof(float) : 0;
   const size_t dt_bytes = d_topk ? (size_t)s.S * sizeof(float) : 0;
   hipError_t e = hipSuccess;
+  if (!mfma) {
+    // vector-ALU kernels: zero dX / d_topk, dW_down, dh / dgu / d_topk, dX, dW_gu
+    if (dx_bytes || dt_bytes)
+      e = timed(F_FILL, st, [&] { return launch_fill_zero(dX, dx_bytes, d_topk, dt_bytes, st); });
+    if (e == hipSuccess && dW_down)
+      e = timed(F_GB_DWD, st, [&] {
+        return simt_bwd_dw_rows(dY, false, h, true, s, dW_down, (int)F, (int)N, dtype, st);
+      });
+    if (e == hipSuccess && (need_dgu || d_topk))
+      e = timed(F_GB_DH, st, [&] {
+        return simt_gated_bwd_dh(dY, h, W_down, s, d_topk, (int)F, (int)N, (const float *)gu,
+                                 need_dgu ? dgu : nullptr, dtype, st);
+      });
+    if (e == hipSuccess && dX)
+      e = timed(F_GB_DX, st, [&] {
+        return simt_gated_bwd_dx(dgu, W_gu, s, dX, (int)K, (int)F, dtype, st);
+      });
+    if (e == hipSuccess && dW_gu)
+      e = timed(F_GB_DWGU, st, [&] {
+        return simt_bwd_dw_rows(dgu, true, x, false, s, dW_gu, (int)K, (int)(2 * F), dtype, st);
+      });
+    return hip_status(e);
+  }
   // 1. dW_down = sum (w dY)^T h (zeroes dX and d_topk on the side), or one fill
   if (dW_down)
     e = timed(F_GB_DWD, st, [&] {

@@ -100,6 +100,22 @@ hipError_t simt_bwd_dx(const void *dY, const void *x, const void *W, const moe_s
                        float *dX, float *d_w, int K, int N, int dtype, hipStream_t st);
 hipError_t simt_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
                        int N, int dtype, hipStream_t st);
+// gated expert FFN on the vector ALUs (fp32, or bf16 with K, F or N not a
+// multiple of 8): h [R, F] and dgu [R, 2F] in the input dtype, gu [R, 2F] fp32
+hipError_t simt_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h,
+                         float *gu, int K, int F, int dtype, hipStream_t st);
+hipError_t simt_gated_down(const void *h, const void *W_down, const moe_schedule &s, float *y,
+                           int F, int N, int dtype, hipStream_t st);
+hipError_t simt_gated_bwd_dh(const void *dY, const void *h, const void *W_down,
+                             const moe_schedule &s, float *d_w, int F, int N, const float *gu,
+                             void *dgu, int dtype, hipStream_t st);
+hipError_t simt_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedule &s, float *dX,
+                             int K, int F, int dtype, hipStream_t st);
+// dW[e] = sum over rows of a^T b with a (N columns) and b (K columns) read by
+// schedule row (by_row) or gathered by token (dY with the routing weight)
+hipError_t simt_bwd_dw_rows(const void *A, bool a_by_row, const void *B, bool b_by_row,
+                            const moe_schedule &s, void *dW, int K, int N, int dtype,
+                            hipStream_t st);
 
 // bf16 MFMA path
 bool mfma_supported(int K, int N);

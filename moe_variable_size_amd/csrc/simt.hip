@@ -31,8 +31,6 @@ MOE_DEV float ld(const bf16_t *p, size_t i) { return bf16_to_f32(p[i]); }
 MOE_DEV void st(float *p, size_t i, float v) { p[i] = v; }
 MOE_DEV void st(bf16_t *p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
-enum Mode { kBare = 0, kFused = 1 };
-
 // acc[i][j] += A[kk][8 ty + i] * B[kk][8 tx + j] over the BK reduction indices
 // of one step, each output's FMAs in ascending reduction order.
 MOE_DEV void step_fma(const float (*As)[LDP], const float (*Bs)[LDP], int ty, int tx,
@@ -51,9 +49,21 @@ MOE_DEV void step_fma(const float (*As)[LDP], const float (*Bs)[LDP], int ty, in
   }
 }
 
-// Forward-shaped product: out[r, n] = sum_k A[src(r), k] * W[g, n, k].
-//  kBare : src(r) = r, plain store of C[r, n] (row space = A's rows).
-//  kFused: src(r) = row_to_token[r]; y[src(r), n] += row_weight[r] * acc.
+// Forward-shaped products: out[r, n] = sum_k A[src(r), k] * B[n, k] with B the
+// group's weight rows.
+//  kBare   : src(r) = r, plain store of C[r, n] (row space = A's rows).
+//  kFused  : src(r) = row_to_token[r]; y[src(r), n] += row_weight[r] * acc.
+//  kGatedUp: src(r) = row_to_token[r]; a tile's 128 columns are 64 gate /
+//            up pairs: column c is W_gu row f (c % 8 < 4, gate) or F + f (up)
+//            with f = f0 + 4 (c / 8) + c % 4, so a thread holds the gate and
+//            up values of 4 f for its 8 rows and stores h[r, f] = silu(g) u
+//            (and g, u into gu[r, f], gu[r, F + f] when gu is given).  N = F.
+//  kRowsOut: src(r) = r over the schedule's rows (A = h, one row per
+//            assignment); y[row_to_token[r], n] += row_weight[r] * acc.
+enum Mode { kBare = 0, kFused = 1, kGatedUp = 2, kRowsOut = 3 };
+
+MOE_DEV float silu(float g) { return g / (1.f + __expf(-g)); }
+
 // Operand loads: thread t brings row t / 2, reduction indices 4 (t % 2) .. +3
 // of both the A rows and the W rows of the step.
 template <int MODE, typename Tin, typename Tout>
@@ -61,11 +71,14 @@ __global__ __launch_bounds__(NT) void simt_fwd_kernel(
     const Tin *__restrict__ A, const Tin *__restrict__ W, Tout *__restrict__ C,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ bstart, const int32_t *__restrict__ row_to_token,
-    const float *__restrict__ row_weight, int E, int layout, int capacity, int K, int N, int M) {
+    const float *__restrict__ row_weight, int E, int layout, int capacity, int K, int N, int M,
+    float *__restrict__ gu) {
+  constexpr bool GATED = MODE == kGatedUp;
+  constexpr int TILE_N = GATED ? BN / 2 : BN;  // output columns (f) per tile
   __shared__ __attribute__((aligned(16))) float As[BK][LDP];
   __shared__ __attribute__((aligned(16))) float Bs[BK][LDP];
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
-  __shared__ int src[BM];
+  __shared__ int src[BM], dst[BM];
   __shared__ float wrow[BM];
   __shared__ int scratch[NT / kWave + 1];
 
@@ -76,29 +89,51 @@ __global__ __launch_bounds__(NT) void simt_fwd_kernel(
 
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const int lr = tid / 2, lk = (tid % 2) * 4;  // this thread's load row / reduction offset
-  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_n = (N + TILE_N - 1) / TILE_N;
   const int total = bs[E] * tiles_n;
   for (int tau = blockIdx.x; tau < total; tau += gridDim.x) {
     const TileCoord c = tile_coord(bs, rstart, rcnt, E, tau, tiles_n, BM);
     if (c.rows <= 0) continue;  // masked layout: no valid rows in this block
-    const int n0 = c.nb * BN;
+    const int n0 = c.nb * TILE_N;
     __syncthreads();
     if (tid < BM) {
       const int r = c.row0 + tid;
       const bool ok = tid < c.rows;
-      src[tid] = ok ? (MODE == kBare ? (r < M ? r : -1) : row_to_token[r]) : -1;
-      wrow[tid] = (ok && MODE != kBare) ? row_weight[r] : 0.f;
+      int sa = -1, so = -1;
+      if (ok) {
+        if (MODE == kBare) {
+          sa = r < M ? r : -1;
+          so = sa;
+        } else if (MODE == kRowsOut) {
+          sa = r;
+          so = row_to_token[r];
+        } else {
+          sa = row_to_token[r];
+          so = GATED ? r : sa;
+        }
+      }
+      src[tid] = sa;
+      dst[tid] = so;
+      wrow[tid] = (ok && MODE != kBare && !GATED) ? row_weight[r] : 0.f;
     }
     __syncthreads();
-    const Tin *Wg = W + (size_t)c.g * N * K;
-    const int s_ld = src[lr], n_ld = n0 + lr;
+    const Tin *Wg = W + (size_t)c.g * (GATED ? 2 * (size_t)N : (size_t)N) * K;
+    const int s_ld = src[lr];
+    // the weight row this thread loads for tile column lr, or -1
+    int w_ld;
+    if constexpr (GATED) {
+      const int f = n0 + 4 * (lr / 8) + (lr % 4);
+      w_ld = f < N ? ((lr % 8) < 4 ? f : N + f) : -1;
+    } else {
+      w_ld = n0 + lr < N ? n0 + lr : -1;
+    }
     float ra[4], rb[4];
     auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int kx = k0 + lk + q;
         ra[q] = (s_ld >= 0 && kx < K) ? ld(A, (size_t)s_ld * K + kx) : 0.f;
-        rb[q] = (n_ld < N && kx < K) ? ld(Wg, (size_t)n_ld * K + kx) : 0.f;
+        rb[q] = (w_ld >= 0 && kx < K) ? ld(Wg, (size_t)w_ld * K + kx) : 0.f;
       }
     };
     float acc[TM][TN] = {};
@@ -117,41 +152,66 @@ __global__ __launch_bounds__(NT) void simt_fwd_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rr = 8 * ty + i;
-      const int s = src[rr];
+      const int s = dst[rr];
       if (s < 0) continue;
+      if constexpr (GATED) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int n = n0 + 8 * tx + j;
-        if (n >= N) continue;
-        if (MODE == kBare)
-          st(C, (size_t)s * N + n, acc[i][j]);
-        else
-          atomicAdd((float *)C + (size_t)s * N + n, wrow[rr] * acc[i][j]);
+        for (int j = 0; j < 4; ++j) {
+          const int f = n0 + 4 * tx + j;
+          if (f >= N) continue;
+          const float g = acc[i][j], u = acc[i][j + 4];
+          st(C, (size_t)s * N + f, silu(g) * u);
+          if (gu) {
+            gu[(size_t)s * 2 * N + f] = g;
+            gu[(size_t)s * 2 * N + N + f] = u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int n = n0 + 8 * tx + j;
+          if (n >= N) continue;
+          if (MODE == kBare)
+            st(C, (size_t)s * N + n, acc[i][j]);
+          else
+            atomicAdd((float *)C + (size_t)s * N + n, wrow[rr] * acc[i][j]);
+        }
       }
     }
   }
 }
 
-// Input gradient: G[r, kc] = sum_n dY[tok(r), n] * W[g, n, kc];
-// dX[tok(r), kc] += w_r * G[r, kc];  d_w[assign(r)] += sum_kc G[r, kc] * x[tok(r), kc].
-// Operand loads: the dY rows as the forward's A rows (thread t: row t / 2,
-// n 4 (t % 2) .. +3); W rows n0 + t / 32, columns kc0 + 4 (t % 32) .. +3.
-template <typename Tin>
+// Input-gradient-shaped products: G[r, kc] = sum_n A[src(r), n] * W[g, n, kc]
+// (the weight read transposed).
+//  kDx     : A = dY, src(r) = row_to_token[r]; dX[tok(r), kc] += w_r G[r, kc];
+//            d_w[assign(r)] += sum_kc G[r, kc] * x[tok(r), kc].
+//  kGatedDh: A = dY, src(r) = row_to_token[r], W = W_down (kc runs over F):
+//            dh = w_r G; d_w[assign(r)] += sum_f G[r, f] h[r, f]; from the
+//            saved g = gu[r, f], u = gu[r, F + f]:
+//            dgu[r, f] = dh u s (1 + g (1 - s)), dgu[r, F + f] = dh g s,
+//            s = 1 / (1 + exp(-g)).
+//  kGatedDx: A = dgu, src(r) = r (the schedule's rows), W = W_gu (n runs
+//            over 2F); dX[tok(r), kc] += G[r, kc] (the weight is in dgu).
+// Operand loads: the A rows as the forward's (thread t: row t / 2, n 4 (t % 2)
+// .. +3); W rows n0 + t / 32, columns kc0 + 4 (t % 32) .. +3.
+enum DxMode { kDx = 0, kGatedDh = 1, kGatedDx = 2 };
+template <int MODE, typename Tin>
 __global__ __launch_bounds__(NT) void simt_dx_kernel(
     const Tin *__restrict__ dY, const Tin *__restrict__ x, const Tin *__restrict__ W,
     float *__restrict__ dX, float *__restrict__ d_w, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ counts, const int32_t *__restrict__ bstart,
     const int32_t *__restrict__ row_to_assign, const int32_t *__restrict__ row_to_token,
-    const float *__restrict__ row_weight, int E, int layout, int capacity, int K, int N) {
+    const float *__restrict__ row_weight, int E, int layout, int capacity, int K, int N,
+    const float *__restrict__ gu, Tin *__restrict__ dgu) {
   __shared__ __attribute__((aligned(16))) float As[BK][LDP];
   __shared__ __attribute__((aligned(16))) float Bs[BK][LDP];
   __shared__ int bs[kMaxExperts + 1], rstart[kMaxExperts], rcnt[kMaxExperts];
-  __shared__ int src[BM], asg[BM];
+  __shared__ int src[BM], tokr[BM], asg[BM];
   __shared__ float wrow[BM];
 
   group_tables_from_schedule<NT>(counts, offsets, bstart, E, layout, capacity, bs, rstart, rcnt);
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
-  const int lr = tid / 2, ln = (tid % 2) * 4;   // dY rows
+  const int lr = tid / 2, ln = (tid % 2) * 4;   // A rows
   const int wr = tid / 32, wc = (tid % 32) * 4;  // W rows (reduction) and columns
   const int tiles_n = (K + BN - 1) / BN;  // output columns are the K dimension
   const int total = bs[E] * tiles_n;
@@ -163,7 +223,9 @@ __global__ __launch_bounds__(NT) void simt_dx_kernel(
     if (tid < BM) {
       const int r = c.row0 + tid;
       const bool ok = tid < c.rows;
-      src[tid] = ok ? row_to_token[r] : -1;
+      const int t = ok ? row_to_token[r] : -1;
+      src[tid] = ok ? (MODE == kGatedDx ? r : t) : -1;
+      tokr[tid] = MODE == kGatedDh ? (ok ? r : -1) : t;  // the row the epilogue addresses
       asg[tid] = ok ? row_to_assign[r] : -1;
       wrow[tid] = ok ? row_weight[r] : 0.f;
     }
@@ -196,18 +258,32 @@ __global__ __launch_bounds__(NT) void simt_dx_kernel(
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int rr = 8 * ty + i;
-      const int s = src[rr];
+      const int s = tokr[rr];
       float part = 0.f;
       if (s >= 0) {
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int kc = kc0 + 8 * tx + j;
           if (kc >= K) continue;
-          if (dX) atomicAdd(dX + (size_t)s * K + kc, wrow[rr] * acc[i][j]);
-          if (d_w) part = fmaf(acc[i][j], ld(x, (size_t)s * K + kc), part);
+          const float g = acc[i][j];
+          if (MODE == kDx) {
+            if (dX) atomicAdd(dX + (size_t)s * K + kc, wrow[rr] * g);
+            if (d_w) part = fmaf(g, ld(x, (size_t)s * K + kc), part);
+          } else if (MODE == kGatedDx) {
+            atomicAdd(dX + (size_t)s * K + kc, g);
+          } else {  // kGatedDh: s is the schedule row, K is F
+            if (d_w) part = fmaf(g, ld(x, (size_t)s * K + kc), part);
+            if (dgu) {
+              const float dh = wrow[rr] * g;
+              const float gv = gu[(size_t)s * 2 * K + kc], uv = gu[(size_t)s * 2 * K + K + kc];
+              const float sg = 1.f / (1.f + __expf(-gv));
+              st(dgu, (size_t)s * 2 * K + kc, dh * uv * sg * (1.f + gv * (1.f - sg)));
+              st(dgu, (size_t)s * 2 * K + K + kc, dh * gv * sg);
+            }
+          }
         }
       }
-      if (d_w) {
+      if (MODE != kGatedDx && d_w) {
         // the 16 threads with the same ty are 16 consecutive lanes of one wave
 #pragma unroll
         for (int d = 8; d >= 1; d >>= 1) part += __shfl_xor(part, d, 16);
@@ -217,12 +293,14 @@ __global__ __launch_bounds__(NT) void simt_dx_kernel(
   }
 }
 
-// Weight gradient: dW[e, n, kc] = sum over rows r of e of w_r dY[tok(r), n] x[tok(r), kc].
-// Work units are (expert, output tile) taken in descending expert load and dealt
-// to blocks in a snake order so that long reductions are spread out; every unit
-// of an empty expert stores zeros.  Operand loads: reduction row t / 32 of the
-// step, columns 4 (t % 32) .. +3 of both the weighted dY row and the x row.
-template <typename Tin, typename Tout>
+// Weight gradient: dW[e, n, kc] = sum over rows r of e of a(r, n) b(r, kc) with
+// a(r, n) = w_r dY[tok(r), n] (or A[r, n], unweighted, with A_ROWS) and
+// b(r, kc) = x[tok(r), kc] (or B[r, kc] with B_ROWS).  Work units are (expert,
+// output tile) taken in descending expert load and dealt to blocks in a snake
+// order so that long reductions are spread out; every unit of an empty expert
+// stores zeros.  Operand loads: reduction row t / 32 of the step, columns
+// 4 (t % 32) .. +3 of both rows.
+template <typename Tin, typename Tout, bool A_ROWS = false, bool B_ROWS = false>
 __global__ __launch_bounds__(NT) void simt_dw_kernel(
     const Tin *__restrict__ dY, const Tin *__restrict__ x, Tout *__restrict__ dW,
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ counts,
@@ -249,13 +327,15 @@ __global__ __launch_bounds__(NT) void simt_dw_kernel(
     float ra[4], rb[4];
     auto load = [&](int q0) __attribute__((always_inline)) {
       const bool ok = q0 + lq < m;
-      const int s = ok ? row_to_token[r0 + q0 + lq] : -1;
-      const float wv = ok ? row_weight[r0 + q0 + lq] : 0.f;
+      const int r = r0 + q0 + lq;
+      const int tok = ok ? row_to_token[r] : -1;
+      const int sa = A_ROWS ? (ok ? r : -1) : tok, sb = B_ROWS ? (ok ? r : -1) : tok;
+      const float wv = A_ROWS ? 1.f : (ok ? row_weight[r] : 0.f);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + lc + q, kc = kc0 + lc + q;
-        ra[q] = (s >= 0 && n < N) ? wv * ld(dY, (size_t)s * N + n) : 0.f;
-        rb[q] = (s >= 0 && kc < K) ? ld(x, (size_t)s * K + kc) : 0.f;
+        ra[q] = (sa >= 0 && n < N) ? wv * ld(dY, (size_t)sa * N + n) : 0.f;
+        rb[q] = (sb >= 0 && kc < K) ? ld(x, (size_t)sb * K + kc) : 0.f;
       }
     };
     float acc[TM][TN] = {};
@@ -287,6 +367,9 @@ __global__ __launch_bounds__(NT) void simt_dw_kernel(
 
 int simt_grid(int num_cu) { return num_cu * 4; }
 
+template <typename T>
+const int32_t *bst128(const T &s) { return s.block_start + bm_index(BM) * (s.E + 1); }
+
 }  // namespace
 
 hipError_t simt_grouped_gemm(const void *A, const void *W, const int32_t *offsets, void *C, int M,
@@ -295,64 +378,115 @@ hipError_t simt_grouped_gemm(const void *A, const void *W, const int32_t *offset
   if (dtype == MOE_F32) {
     hipLaunchKernelGGL((simt_fwd_kernel<kBare, float, float>), grid, block, 0, st,
                        (const float *)A, (const float *)W, (float *)C, offsets, nullptr, nullptr,
-                       nullptr, nullptr, E, 0, 0, K, N, M);
+                       nullptr, nullptr, E, 0, 0, K, N, M, nullptr);
   } else if (out_dtype == MOE_F32) {
     hipLaunchKernelGGL((simt_fwd_kernel<kBare, bf16_t, float>), grid, block, 0, st,
                        (const bf16_t *)A, (const bf16_t *)W, (float *)C, offsets, nullptr,
-                       nullptr, nullptr, nullptr, E, 0, 0, K, N, M);
+                       nullptr, nullptr, nullptr, E, 0, 0, K, N, M, nullptr);
   } else {
     hipLaunchKernelGGL((simt_fwd_kernel<kBare, bf16_t, bf16_t>), grid, block, 0, st,
                        (const bf16_t *)A, (const bf16_t *)W, (bf16_t *)C, offsets, nullptr,
-                       nullptr, nullptr, nullptr, E, 0, 0, K, N, M);
+                       nullptr, nullptr, nullptr, E, 0, 0, K, N, M, nullptr);
   }
   return hipGetLastError();
 }
 
+namespace {
+template <int MODE, typename Tin>
+hipError_t launch_fwd(const void *A, const void *W, const moe_schedule &s, void *C, int K, int N,
+                      float *gu, hipStream_t st) {
+  const dim3 grid(simt_grid(device_cu_count())), block(NT);
+  using Tout = std::conditional_t<MODE == kGatedUp, Tin, float>;
+  hipLaunchKernelGGL((simt_fwd_kernel<MODE, Tin, Tout>), grid, block, 0, st, (const Tin *)A,
+                     (const Tin *)W, (Tout *)C, s.offsets, s.counts, bst128(s), s.row_to_token,
+                     s.row_weight, s.E, s.layout, s.capacity, K, N, (int)s.T, gu);
+  return hipGetLastError();
+}
+
+template <int MODE, typename Tin>
+hipError_t launch_dx(const void *A, const void *x, const void *W, const moe_schedule &s,
+                     float *dX, float *d_w, int K, int N, const float *gu, void *dgu,
+                     hipStream_t st) {
+  const dim3 grid(simt_grid(device_cu_count())), block(NT);
+  hipLaunchKernelGGL((simt_dx_kernel<MODE, Tin>), grid, block, 0, st, (const Tin *)A,
+                     (const Tin *)x, (const Tin *)W, dX, d_w, s.offsets, s.counts, bst128(s),
+                     s.row_to_assign, s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K,
+                     N, gu, (Tin *)dgu);
+  return hipGetLastError();
+}
+
+template <typename Tin, bool A_ROWS, bool B_ROWS>
+hipError_t launch_dw(const void *A, const void *B, const moe_schedule &s, void *dW, int K, int N,
+                     hipStream_t st) {
+  const dim3 grid(simt_grid(device_cu_count())), block(NT);
+  hipLaunchKernelGGL((simt_dw_kernel<Tin, Tin, A_ROWS, B_ROWS>), grid, block, 0, st,
+                     (const Tin *)A, (const Tin *)B, (Tin *)dW, s.offsets, s.counts,
+                     s.expert_order, s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K,
+                     N);
+  return hipGetLastError();
+}
+}  // namespace
+
 hipError_t simt_fused_fwd(const void *x, const void *W, const moe_schedule &s, float *y, int K,
                           int N, int dtype, hipStream_t st) {
-  const dim3 grid(simt_grid(device_cu_count())), block(NT);
-  const int32_t *bst = s.block_start + bm_index(BM) * (s.E + 1);
-  if (dtype == MOE_F32)
-    hipLaunchKernelGGL((simt_fwd_kernel<kFused, float, float>), grid, block, 0, st,
-                       (const float *)x, (const float *)W, y, s.offsets, s.counts, bst,
-                       s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N, (int)s.T);
-  else
-    hipLaunchKernelGGL((simt_fwd_kernel<kFused, bf16_t, float>), grid, block, 0, st,
-                       (const bf16_t *)x, (const bf16_t *)W, y, s.offsets, s.counts, bst,
-                       s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N, (int)s.T);
-  return hipGetLastError();
+  return dtype == MOE_F32 ? launch_fwd<kFused, float>(x, W, s, y, K, N, nullptr, st)
+                          : launch_fwd<kFused, bf16_t>(x, W, s, y, K, N, nullptr, st);
 }
 
 hipError_t simt_bwd_dx(const void *dY, const void *x, const void *W, const moe_schedule &s,
                        float *dX, float *d_w, int K, int N, int dtype, hipStream_t st) {
-  const dim3 grid(simt_grid(device_cu_count())), block(NT);
-  const int32_t *bst = s.block_start + bm_index(BM) * (s.E + 1);
-  if (dtype == MOE_F32)
-    hipLaunchKernelGGL((simt_dx_kernel<float>), grid, block, 0, st, (const float *)dY,
-                       (const float *)x, (const float *)W, dX, d_w, s.offsets, s.counts, bst,
-                       s.row_to_assign, s.row_to_token, s.row_weight, s.E, s.layout, s.capacity,
-                       K, N);
-  else
-    hipLaunchKernelGGL((simt_dx_kernel<bf16_t>), grid, block, 0, st, (const bf16_t *)dY,
-                       (const bf16_t *)x, (const bf16_t *)W, dX, d_w, s.offsets, s.counts, bst,
-                       s.row_to_assign, s.row_to_token, s.row_weight, s.E, s.layout, s.capacity,
-                       K, N);
-  return hipGetLastError();
+  return dtype == MOE_F32
+             ? launch_dx<kDx, float>(dY, x, W, s, dX, d_w, K, N, nullptr, nullptr, st)
+             : launch_dx<kDx, bf16_t>(dY, x, W, s, dX, d_w, K, N, nullptr, nullptr, st);
 }
 
 hipError_t simt_bwd_dw(const void *dY, const void *x, const moe_schedule &s, void *dW, int K,
                        int N, int dtype, hipStream_t st) {
-  const dim3 grid(simt_grid(device_cu_count())), block(NT);
-  if (dtype == MOE_F32)
-    hipLaunchKernelGGL((simt_dw_kernel<float, float>), grid, block, 0, st, (const float *)dY,
-                       (const float *)x, (float *)dW, s.offsets, s.counts, s.expert_order,
-                       s.row_to_token, s.row_weight, s.E, s.layout, s.capacity, K, N);
-  else
-    hipLaunchKernelGGL((simt_dw_kernel<bf16_t, bf16_t>), grid, block, 0, st,
-                       (const bf16_t *)dY, (const bf16_t *)x, (bf16_t *)dW, s.offsets, s.counts,
-                       s.expert_order, s.row_to_token, s.row_weight, s.E, s.layout, s.capacity,
-                       K, N);
-  return hipGetLastError();
+  return dtype == MOE_F32 ? launch_dw<float, false, false>(dY, x, s, dW, K, N, st)
+                          : launch_dw<bf16_t, false, false>(dY, x, s, dW, K, N, st);
+}
+
+hipError_t simt_gated_up(const void *x, const void *W_gu, const moe_schedule &s, void *h,
+                         float *gu, int K, int F, int dtype, hipStream_t st) {
+  return dtype == MOE_F32 ? launch_fwd<kGatedUp, float>(x, W_gu, s, h, K, F, gu, st)
+                          : launch_fwd<kGatedUp, bf16_t>(x, W_gu, s, h, K, F, gu, st);
+}
+
+hipError_t simt_gated_down(const void *h, const void *W_down, const moe_schedule &s, float *y,
+                           int F, int N, int dtype, hipStream_t st) {
+  return dtype == MOE_F32 ? launch_fwd<kRowsOut, float>(h, W_down, s, y, F, N, nullptr, st)
+                          : launch_fwd<kRowsOut, bf16_t>(h, W_down, s, y, F, N, nullptr, st);
+}
+
+hipError_t simt_gated_bwd_dh(const void *dY, const void *h, const void *W_down,
+                             const moe_schedule &s, float *d_w, int F, int N, const float *gu,
+                             void *dgu, int dtype, hipStream_t st) {
+  return dtype == MOE_F32
+             ? launch_dx<kGatedDh, float>(dY, h, W_down, s, nullptr, d_w, F, N, gu, dgu, st)
+             : launch_dx<kGatedDh, bf16_t>(dY, h, W_down, s, nullptr, d_w, F, N, gu, dgu, st);
+}
+
+hipError_t simt_gated_bwd_dx(const void *dgu, const void *W_gu, const moe_schedule &s, float *dX,
+                             int K, int F, int dtype, hipStream_t st) {
+  return dtype == MOE_F32
+             ? launch_dx<kGatedDx, float>(dgu, nullptr, W_gu, s, dX, nullptr, K, 2 * F, nullptr,
+                                          nullptr, st)
+             : launch_dx<kGatedDx, bf16_t>(dgu, nullptr, W_gu, s, dX, nullptr, K, 2 * F,
+                                           nullptr, nullptr, st);
+}
+
+hipError_t simt_bwd_dw_rows(const void *A, bool a_by_row, const void *B, bool b_by_row,
+                            const moe_schedule &s, void *dW, int K, int N, int dtype,
+                            hipStream_t st) {
+  if (a_by_row && b_by_row) return hipErrorInvalidValue;
+  if (dtype == MOE_F32) {
+    if (a_by_row) return launch_dw<float, true, false>(A, B, s, dW, K, N, st);
+    if (b_by_row) return launch_dw<float, false, true>(A, B, s, dW, K, N, st);
+    return launch_dw<float, false, false>(A, B, s, dW, K, N, st);
+  }
+  if (a_by_row) return launch_dw<bf16_t, true, false>(A, B, s, dW, K, N, st);
+  if (b_by_row) return launch_dw<bf16_t, false, true>(A, B, s, dW, K, N, st);
+  return launch_dw<bf16_t, false, false>(A, B, s, dW, K, N, st);
 }
 
 }  // namespace moe

@@ -319,15 +319,16 @@ class Gated:
 
 def gated(name: str, T: int, K: int, F: int, N: int, E: int, k: int, *, seed: int,
           routing: str = "uniform", weights: str = "uniform", capacity: int = 0,
-          dense: bool = True) -> Gated:
+          dense: bool = True, bf16: bool = True) -> Gated:
     """Gated FFN workload: routing as in ``routed`` (same draws for the same
-    seed), x ~ N(0, 1), W_gu ~ N(0, 1/K), W_down ~ N(0, 1/F), all bf16."""
+    seed), x ~ N(0, 1), W_gu ~ N(0, 1/K), W_down ~ N(0, 1/F); bf16 (or fp32
+    with ``bf16=False``)."""
     r = routed(name, T, K, 2 * F, E, k, seed=seed, routing=routing, weights=weights,
-               with_dy=False, capacity=capacity, dense=dense)
+               with_dy=False, capacity=capacity, dense=dense, bf16=bf16)
     Wd = None
     if dense:
         s_d = np.random.SeedSequence(seed).spawn(5)[4]
-        Wd = _make(_normal_blocks(s_d, E, (N, F), 1.0 / np.sqrt(F)), True)
+        Wd = _make(_normal_blocks(s_d, E, (N, F), 1.0 / np.sqrt(F)), bf16)
     return Gated(name, T, K, F, N, E, k, r.x, r.W, Wd, r.expert_ids, r.topk_weights,
                  capacity=capacity, seed=seed)
 

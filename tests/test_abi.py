@@ -106,13 +106,17 @@ def test_gated_ffn_rejects_before_launch(lib):
               "row_weight", "status", "dw_queue"):
         setattr(s, f, 1 << 20)
     r = ctypes.byref(s)
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 16, 16, 0, None) == 3      # fp32: bf16 only
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 16, 16, 5, None) == 3      # dtype code
     assert lib.moe_gated_ffn_fwd(P, P, None, r, P, None, P, 16, 16, 16, 1, None) == 1   # no W_down
     assert lib.moe_gated_ffn_fwd(P, P, P, r, None, None, P, 16, 16, 16, 1, None) == 1   # no h
     assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 0, 16, 1, None) == 2      # F = 0
-    assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 16, 12, 16, 1, None) == 2     # F % 8 != 0
     assert lib.moe_gated_ffn_fwd(P, P, P, r, ctypes.c_void_p((1 << 20) + 2), None, P, 16, 16, 16, 1,
-                                 None) == 4                                       # h misaligned
+                                 None) == 4                                       # h misaligned (16 B)
+    # F % 8 != 0 takes the vector-ALU kernels, which need element alignment only
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, ctypes.c_void_p((1 << 20) + 1), None, P, 16, 12, 16, 1,
+                                 None) == 4                                       # h misaligned (2 B)
+    assert lib.moe_gated_ffn_fwd(P, P, P, r, ctypes.c_void_p((1 << 20) + 2), None, P, 16, 12, 16, 0,
+                                 None) == 4                                       # fp32 h misaligned (4 B)
     assert lib.moe_gated_ffn_fwd(P, P, P, r, P, None, P, 1 << 16, 1 << 15, 16, 1, None) == 7  # W_gu > 2^31 B
 
 
@@ -143,8 +147,12 @@ def test_gated_backward_rejects_before_launch(lib):
                                  None) == 1                                          # no gu
     assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 16, 16, 1, None, 0,
                                  None) == 5                                          # no workspace
-    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 16, 16, 0, P, 1 << 20,
-                                 None) == 3                                          # fp32
+    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 16, 16, 5, P, 1 << 20,
+                                 None) == 3                                          # dtype code
+    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, P, P, P, P, P, 16, 12, 16, 0, P, 100,
+                                 None) == 5                                          # fp32 dgu workspace
+    assert lib.moe_gated_ffn_bwd(P, P, P, P, r, P, ctypes.c_void_p((1 << 20) + 2), P, P, P, P, 16, 12,
+                                 16, 0, P, 1 << 20, None) == 4                       # fp32 h misaligned
 
 
 def test_mx_rejects_before_launch(lib):
