@@ -525,3 +525,36 @@ class MoEFunction(torch.autograd.Function):
 
 def moe(x, W, expert_ids, topk_weights):
     return MoEFunction.apply(x, W, expert_ids, topk_weights)
+
+
+class GatedMoEFunction(torch.autograd.Function):
+    """Differentiable gated expert FFN y = gated_moe(x, W_gu, W_down, expert_ids,
+    topk_weights) over the C ABI: the forward keeps h and the fp32 gate/up
+    values, the backward returns the gradients of x, both weights and the
+    routing weights ([GG] "Choosing an implementation", "The backward pass")."""
+
+    @staticmethod
+    def forward(ctx, x, W_gu, W_down, expert_ids, topk_weights):
+        sched = moe_build_schedule(expert_ids, topk_weights.detach().float().contiguous(),
+                                   W_gu.shape[0])
+        y, h, gu = moe_gated_ffn_fwd(x.detach().contiguous(), W_gu.detach().contiguous(),
+                                     W_down.detach().contiguous(), sched, save_gu=True)
+        ctx.save_for_backward(x, W_gu, W_down, h, gu)
+        ctx.sched = sched
+        ctx.w_dtype = topk_weights.dtype
+        return y
+
+    @staticmethod
+    def backward(ctx, gy):
+        x, W_gu, W_down, h, gu = ctx.saved_tensors
+        dY = gy.to(x.dtype).contiguous()
+        dX, dWgu, dWd, dT = moe_gated_ffn_bwd(
+            dY, x.detach().contiguous(), W_gu.detach().contiguous(), W_down.detach().contiguous(),
+            ctx.sched, gu, h, dx=ctx.needs_input_grad[0], dw_gu=ctx.needs_input_grad[1],
+            dw_down=ctx.needs_input_grad[2], dtopk=ctx.needs_input_grad[4])
+        return (dX.to(x.dtype) if dX is not None else None, dWgu, dWd, None,
+                dT.to(ctx.w_dtype) if dT is not None else None)
+
+
+def gated_moe(x, W_gu, W_down, expert_ids, topk_weights):
+    return GatedMoEFunction.apply(x, W_gu, W_down, expert_ids, topk_weights)

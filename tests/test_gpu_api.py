@@ -41,6 +41,37 @@ def test_autograd_layer_matches_oracle(frozen_w):
         assert_close(host(W.grad), rW, "bf16", "dW")
 
 
+@pytest.mark.parametrize("bf16,K,F,N", [(True, 136, 200, 72), (False, 37, 13, 29)])
+def test_autograd_gated_layer_matches_oracle(bf16, K, F, N):
+    """y = api.gated_moe(x, W_gu, W_down, ids, w); y.backward(dY) reaches x,
+    both weights and the routing weights (matrix-core path for bf16 with
+    multiples of 8, vector-ALU path for fp32 with odd sizes)."""
+    T, E, k = 300, 5, 2
+    g = WL.gated("api_gated", T, K, F, N, E, k, seed=43, bf16=bf16)
+    rng = np.random.default_rng(44)
+    dYv = WL._make(rng.standard_normal((T, N), dtype=np.float32), bf16)
+    log(f"gated autograd bf16={bf16} K={K} F={F} N={N}")
+    x = dev(g.x, bf16).requires_grad_(True)
+    Wgu = dev(g.W_gu, bf16).requires_grad_(True)
+    Wd = dev(g.W_down, bf16).requires_grad_(True)
+    w = dev(g.topk_weights).requires_grad_(True)
+    y = api.gated_moe(x, Wgu, Wd, dev(g.expert_ids), w)
+    y.backward(dev(dYv, bf16).float())
+    torch.cuda.synchronize()
+    tol = "bf16" if bf16 else "f32"
+    ry = O.gated_ffn_forward(g.x.values, g.W_gu.values, g.W_down.values, g.expert_ids,
+                             g.topk_weights, E)
+    ex = O.gated_ffn_backward(dYv.values, g.x.values, g.W_gu.values, g.W_down.values,
+                              g.expert_ids, g.topk_weights, E)
+    rd = O.gated_ffn_backward(dYv.values, g.x.values, g.W_gu.values, g.W_down.values,
+                              g.expert_ids, g.topk_weights, E, round_h=True)[2] if bf16 else ex[2]
+    assert_close(host(y.detach()), ry, tol, "y")
+    assert_close(host(x.grad), ex[0], tol, "dX")
+    assert_close(host(Wgu.grad), ex[1], tol, "dW_gu")
+    assert_close(host(Wd.grad), rd, tol, "dW_down")
+    assert_close(host(w.grad), ex[3], tol, "d_topk")
+
+
 def test_backward_without_weight_grad_overwrites_outputs():
     """dw=False takes the zero-fill launch and the input-gradient kernel alone;
     NaN-filled output buffers must come back fully written."""
