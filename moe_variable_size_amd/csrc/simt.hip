@@ -29,6 +29,18 @@ constexpr int LDP = BM + 4;  // LDS row pitch (floats): 16-byte aligned, rows of
 MOE_DEV float ld(const float *p, size_t i) { return p[i]; }
 MOE_DEV float ld(const bf16_t *p, size_t i) { return bf16_to_f32(p[i]); }
 MOE_DEV void st(float *p, size_t i, float v) { p[i] = v; }
+// elements i .. i+3 (i a multiple of 4, the row 4-element aligned), or zeros
+MOE_DEV void ld4(const float *p, size_t i, bool ok, float (&v)[4]) {
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 a = ok ? *(const f4 *)(p + i) : f4{0.f, 0.f, 0.f, 0.f};
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+}
+MOE_DEV void ld4(const bf16_t *p, size_t i, bool ok, float (&v)[4]) {
+  typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+  const u2 a = ok ? *(const u2 *)(p + i) : u2{0u, 0u};
+  v[0] = __uint_as_float(a[0] << 16); v[1] = __uint_as_float(a[0] & 0xffff0000u);
+  v[2] = __uint_as_float(a[1] << 16); v[3] = __uint_as_float(a[1] & 0xffff0000u);
+}
 MOE_DEV void st(bf16_t *p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 
 // acc[i][j] += A[kk][8 ty + i] * B[kk][8 tx + j] over the BK reduction indices
@@ -118,6 +130,10 @@ __global__ __launch_bounds__(NT) void simt_fwd_kernel(
     }
     __syncthreads();
     const Tin *Wg = W + (size_t)c.g * (GATED ? 2 * (size_t)N : (size_t)N) * K;
+    // 4 consecutive reduction elements per operand row in one load when every
+    // row starts on a 4-element boundary
+    const bool vec4 = K % 4 == 0 && (uintptr_t)A % (4 * sizeof(Tin)) == 0 &&
+                      (uintptr_t)W % (4 * sizeof(Tin)) == 0;
     const int s_ld = src[lr];
     // the weight row this thread loads for tile column lr, or -1
     int w_ld;
@@ -129,6 +145,12 @@ __global__ __launch_bounds__(NT) void simt_fwd_kernel(
     }
     float ra[4], rb[4];
     auto load = [&](int k0) __attribute__((always_inline)) {
+      if (vec4) {  // one 4-element load per operand (K % 4 == 0: in range or not as a whole)
+        const int kx = k0 + lk;
+        ld4(A, (size_t)s_ld * K + kx, s_ld >= 0 && kx < K, ra);
+        ld4(Wg, (size_t)w_ld * K + kx, w_ld >= 0 && kx < K, rb);
+        return;
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int kx = k0 + lk + q;
@@ -232,14 +254,29 @@ __global__ __launch_bounds__(NT) void simt_dx_kernel(
     __syncthreads();
     const Tin *Wg = W + (size_t)c.g * N * K;
     const int s_ld = src[lr];
+    // 4-element loads where every row starts on a 4-element boundary
+    const bool va = N % 4 == 0 && (uintptr_t)dY % (4 * sizeof(Tin)) == 0;
+    const bool vb = K % 4 == 0 && (uintptr_t)W % (4 * sizeof(Tin)) == 0;
     float ra[4], rb[4];
     auto load = [&](int n0) __attribute__((always_inline)) {
+      const int nw = n0 + wr;
+      if (va) {
+        ld4(dY, (size_t)s_ld * N + n0 + ln, s_ld >= 0 && n0 + ln < N, ra);
+      } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int nx = n0 + ln + q;
-        ra[q] = (s_ld >= 0 && nx < N) ? ld(dY, (size_t)s_ld * N + nx) : 0.f;
-        const int kx = kc0 + wc + q, nw = n0 + wr;
-        rb[q] = (nw < N && kx < K) ? ld(Wg, (size_t)nw * K + kx) : 0.f;
+        for (int q = 0; q < 4; ++q) {
+          const int nx = n0 + ln + q;
+          ra[q] = (s_ld >= 0 && nx < N) ? ld(dY, (size_t)s_ld * N + nx) : 0.f;
+        }
+      }
+      if (vb) {
+        ld4(Wg, (size_t)nw * K + kc0 + wc, nw < N && kc0 + wc < K, rb);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kx = kc0 + wc + q;
+          rb[q] = (nw < N && kx < K) ? ld(Wg, (size_t)nw * K + kx) : 0.f;
+        }
       }
     };
     float acc[TM][TN] = {};
@@ -310,6 +347,9 @@ __global__ __launch_bounds__(NT) void simt_dw_kernel(
   __shared__ __attribute__((aligned(16))) float Bs[BK][LDP];
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const int lq = tid / 32, lc = (tid % 32) * 4;
+  // 4-element loads where every row starts on a 4-element boundary
+  const bool va = N % 4 == 0 && (uintptr_t)dY % (4 * sizeof(Tin)) == 0;
+  const bool vb = K % 4 == 0 && (uintptr_t)x % (4 * sizeof(Tin)) == 0;
   const int tn = (N + BM - 1) / BM, tk = (K + BN - 1) / BN;
   const int per_e = tn * tk;
   const int units = E * per_e;
@@ -331,11 +371,25 @@ __global__ __launch_bounds__(NT) void simt_dw_kernel(
       const int tok = ok ? row_to_token[r] : -1;
       const int sa = A_ROWS ? (ok ? r : -1) : tok, sb = B_ROWS ? (ok ? r : -1) : tok;
       const float wv = A_ROWS ? 1.f : (ok ? row_weight[r] : 0.f);
+      if (va) {
+        ld4(dY, (size_t)sa * N + n0 + lc, sa >= 0 && n0 + lc < N, ra);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + lc + q, kc = kc0 + lc + q;
-        ra[q] = (sa >= 0 && n < N) ? wv * ld(dY, (size_t)sa * N + n) : 0.f;
-        rb[q] = (sb >= 0 && kc < K) ? ld(x, (size_t)sb * K + kc) : 0.f;
+        for (int q = 0; q < 4; ++q) ra[q] *= wv;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + lc + q;
+          ra[q] = (sa >= 0 && n < N) ? wv * ld(dY, (size_t)sa * N + n) : 0.f;
+        }
+      }
+      if (vb) {
+        ld4(x, (size_t)sb * K + kc0 + lc, sb >= 0 && kc0 + lc < K, rb);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int kc = kc0 + lc + q;
+          rb[q] = (sb >= 0 && kc < K) ? ld(x, (size_t)sb * K + kc) : 0.f;
+        }
       }
     };
     float acc[TM][TN] = {};
