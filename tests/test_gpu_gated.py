@@ -38,7 +38,8 @@ def _run(g, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     sch = api.moe_build_schedule(dev(g.expert_ids), dev(g.topk_weights), g.E, layout=layout,
                                  capacity=cap)
     h0 = torch.full((sch.c.R, g.F), SENTINEL, dtype=torch.bfloat16, device="cuda")
-    y, h = api.moe_gated_ffn_fwd(dev(g.x), dev(g.W_gu), dev(g.W_down), sch, h=h0)
+    y0 = torch.full((g.T, g.N), float("nan"), dtype=torch.float32, device="cuda")  # y is overwritten
+    y, h = api.moe_gated_ffn_fwd(dev(g.x), dev(g.W_gu), dev(g.W_down), sch, h=h0, y=y0)
     torch.cuda.synchronize()
     return host(y), host(h)
 

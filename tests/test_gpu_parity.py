@@ -286,6 +286,40 @@ def test_weight_grad_queue_resets(K, N, E):
     assert_close(host(outs[0]), rw, "bf16", "dW")
 
 
+@pytest.mark.parametrize("T,K,N,E,k,masked", [
+    (1500, 256, 520, 9, 2, False),
+    (333, 128, 264, 5, 1, False),   # k = 1 with the atomic combine forced (the automatic one is ranked)
+    (128, 512, 384, 16, 4, True),   # masked, 64-row tiles
+])
+def test_forward_overwrites_y(T, K, N, E, k, masked):
+    """With the atomic combine the library zeroes y before the scattering
+    forward adds into it, so a y full of NaN comes back right, and repeated
+    launches agree bit for bit (at most two adds per element, which commute)."""
+    r = _routed_small(T, K, N, E, k, seed=T + k, bf16=True)
+    cap = 64 if masked else 0
+    layout = api.MOE_LAYOUT_MASKED if masked else api.MOE_LAYOUT_CONTIGUOUS
+    try:
+        api.moe_set_combine(api.MOE_COMBINE_ATOMIC)
+        sch = api.moe_build_schedule(dev(r.expert_ids), dev(r.topk_weights), E, layout=layout,
+                                     capacity=cap)
+        outs = []
+        for _ in range(3):
+            y0 = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+            y = api.moe_fused_fwd(dev(r.x), dev(r.W), sch, y=y0)
+            torch.cuda.synchronize()
+            outs.append(host(y))
+    finally:
+        api.moe_set_combine(api.MOE_COMBINE_AUTO)
+    if masked:
+        ms = O.masked_schedule(r.expert_ids, r.topk_weights, E, cap)
+        ref = O.masked_forward(r.x.values, r.W.values, ms, T)
+    else:
+        ref = O.moe_forward(r.x.values, r.W.values, r.expert_ids, r.topk_weights, E)
+    assert_close(outs[0], ref, "bf16", "y")
+    if k <= 2:
+        assert all(np.array_equal(o.view(np.uint32), outs[0].view(np.uint32)) for o in outs[1:])
+
+
 def test_weight_grad_config4():
     g = WL.config4()
     r = WL.grouped_as_routed(g)
