@@ -92,7 +92,8 @@ def test_fp8_config5_decode():
 def _run_mx(f, layout=api.MOE_LAYOUT_CONTIGUOUS, cap=0):
     sch = api.moe_build_schedule(dev(f.expert_ids), dev(f.topk_weights), f.E, layout=layout,
                                  capacity=cap)
-    y = api.moe_fused_fwd_mx(_u8(f.xq), _u8(f.x_bs), _u8(f.Wq), _u8(f.w_bs), sch)
+    y0 = torch.full((f.T, f.N), float("nan"), dtype=torch.float32, device="cuda")  # overwritten
+    y = api.moe_fused_fwd_mx(_u8(f.xq), _u8(f.x_bs), _u8(f.Wq), _u8(f.w_bs), sch, y=y0)
     torch.cuda.synchronize()
     return sch, host(y)
 
