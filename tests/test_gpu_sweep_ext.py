@@ -1,4 +1,5 @@
-"""Seeded sweeps of ragged shapes through the 8-bit forwards and the gated FFN.
+"""Seeded sweeps of ragged shapes through the 8-bit forwards, the gated FFN,
+the bare grouped GEMM and the fp32 step.
 
 Each case draws its sizes, expert count, top-k, experts left without rows and
 the layout (contiguous, or masked with a capacity that may drop assignments)
@@ -146,3 +147,59 @@ def test_sweep_gated(seed):
     got_gu, got_d = host(dWgu), host(dWd)
     for e in np.nonzero(counts == 0)[0]:
         assert (got_gu[e] == 0).all() and (got_d[e] == 0).all(), f"dW of expert {e} without rows"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_sweep_grouped_gemm(seed):
+    """Bare grouped GEMM over drawn group sizes (empty groups included) and
+    input / output dtypes; sizes not a multiple of 8 take the vector ALUs.
+    Rows past the last offset keep what the caller left there."""
+    rng = np.random.default_rng(15000 + seed)
+    E = int(rng.integers(1, 24))
+    counts = [int(c) if rng.random() > 0.25 else 0 for c in rng.integers(0, 300, size=E)]
+    odd = bool(rng.random() < 0.3)
+    K = int(rng.integers(1, 400)) if odd else 8 * int(rng.integers(1, 50))
+    N = int(rng.integers(1, 400)) if odd else 8 * int(rng.integers(1, 50))
+    bf16 = bool(rng.random() < 0.7)
+    out = "bf16" if bf16 and rng.random() < 0.4 else "f32"
+    M = sum(counts) + 5
+    A = WL._make(rng.standard_normal((M, K), dtype=np.float32), bf16)
+    W = WL._make(rng.standard_normal((E, N, K), dtype=np.float32) / np.sqrt(K), bf16)
+    offs = np.cumsum(counts).astype(np.int32)
+    log(f"grouped_gemm sweep seed={seed}: counts={counts} K={K} N={N} bf16={bf16} out={out}")
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    C0 = torch.full((M, N), 7.0, dtype=od, device="cuda")
+    C = api.grouped_gemm(dev(A), dev(W), dev(offs), out=C0, out_dtype=od)
+    torch.cuda.synchronize()
+    got = host(C)
+    nv = int(offs[-1])
+    ref = O.grouped_gemm(A.values, W.values, offs)
+    assert_close(got[:nv], ref[:nv], "bf16" if (bf16 or out == "bf16") else "f32", "C")
+    assert (got[nv:] == 7.0).all()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sweep_fp32_step(seed):
+    """fp32 inputs (exact fp32 products on the vector ALUs) at any sizes:
+    forward and backward against the oracle at the fp32 bar."""
+    rng = np.random.default_rng(16000 + seed)
+    T = int(rng.integers(1, 300))
+    K = int(rng.integers(1, 200))
+    N = int(rng.integers(1, 200))
+    E = int(rng.integers(1, 16))
+    k = int(rng.integers(1, min(E, 4) + 1))
+    ids, empty, masked, cap = _routing(rng, T, E, k)
+    r = WL.routed(f"sweep_f32_{seed}", T, K, N, E, k, seed=16500 + seed, bf16=False)
+    r.expert_ids = ids
+    log(f"fp32 sweep seed={seed}: T={T} K={K} N={N} E={E} k={k} empty={empty} masked={masked} cap={cap}")
+    sch = _schedule(ids, r.topk_weights, E, masked, cap)
+    y = api.moe_fused_fwd(dev(r.x), dev(r.W), sch, y=_nan((T, N)))
+    dX, dW, dT = api.moe_fused_bwd(dev(r.dY), dev(r.x), dev(r.W), sch)
+    torch.cuda.synchronize()
+    ref_ids = _kept(ids, r.topk_weights, E, cap)[1] if masked else ids
+    ry = O.moe_forward(r.x.values, r.W.values, ref_ids, r.topk_weights, E)
+    rx, rw, rt = O.moe_backward(r.dY.values, r.x.values, r.W.values, ref_ids, r.topk_weights, E)
+    assert_close(host(y), ry, "f32", "y")
+    assert_close(host(dX), rx, "f32", "dX")
+    assert_close(host(dW), rw, "f32", "dW")
+    assert_close(host(dT), rt, "f32", "d_topk")
