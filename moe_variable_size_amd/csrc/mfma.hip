@@ -687,7 +687,7 @@ MOE_DEV void wait_vmcnt_upto(int n) {
 // as the rows it skips are).  Only the range's last stage is bounds-checked.
 template <int MI, int NI, int WGM, int WGN, class Op>
 MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
-                                int live_mi, int parts, f32x16 (&acc)[MI][NI]) {
+                                int live_mi, f32x16 (&acc)[MI][NI]) {
   constexpr int NS = Op::NSTAGES, D = Op::DMA_PER_STAGE;
   auto issue = [&](int kt) __attribute__((always_inline)) {
     const int buf = (kt - kb) % NS;
@@ -704,7 +704,9 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
   for (int kt = kb; kt < ke; ++kt) {
     const int buf = (kt - kb) % NS;
     // stages issued after kt: kt+1 .. min(kt+NS-2, ke-1)
-    wait_vmcnt_upto(min(NS - 2, ke - 1 - kt) * parts);
+    int after = 0;
+    for (int s2 = kt + 1; s2 <= min(kt + NS - 2, ke - 1); ++s2) after += op.parts_at(s2);
+    wait_vmcnt_upto(after);
     wait_lgkm0();
     barrier();  // stage kt in LDS for every wave; the buffer of stage kt-1 is free
     if (kt + NS - 1 < ke) issue(kt + NS - 1);
@@ -723,7 +725,7 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
           fa[mi] = frag_kmaj8(As, row, step, lane);
         else
           fa[mi] = frag_kmaj(As, row, step, lane);
-        if constexpr (Op::MX) sa[mi] = op.scale_of(buf, false, row, step, lane);
+        if constexpr (Op::MX) sa[mi] = op.scale_of(kt, false, row, step, lane);
       }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
@@ -732,7 +734,7 @@ MOE_DEV void tile_multiply_deep(Op &op, char *lds, int kb, int ke, int wm, int w
           fb[ni] = frag_kmaj8(Bs, row, step, lane);
         else
           fb[ni] = frag_kmaj(Bs, row, step, lane);
-        if constexpr (Op::MX) sb[ni] = op.scale_of(buf, true, row, step, lane);
+        if constexpr (Op::MX) sb[ni] = op.scale_of(kt, true, row, step, lane);
       }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
@@ -928,17 +930,26 @@ struct FwdDeepOp {
   static constexpr bool F8 = F8_, MX = MX_;  // as FwdOp
   static constexpr int DA = BM / (8 * NW), DB = BN / (8 * NW);
   static_assert(DA >= 1 && DB >= 1, "at least one DMA row group per wave");
-  // MX: a stage also holds one 4-byte scale word per A row and per B row
-  // (after the B rows); the (BM + BN) / 64 groups of 64 words are dealt to the
-  // waves round robin, so a wave issues DSMAX or fewer scale loads
+  // MX: each stage needs one 4-byte scale word per A row and per B row.  They
+  // sit in a ring of two slots after the stages, a slot holding the words of
+  // four consecutive stages: with K a multiple of 512 (sc16) every row's four
+  // words are one 16-byte load issued with the first stage of the four (slot
+  // layout [row][4 words]); otherwise each stage loads its 4-byte words (slot
+  // layout [stage of the four][row]).  The (BM + BN) / 64 groups of 64 rows are
+  // dealt to the waves round robin, so a wave issues DSMAX or fewer scale loads
+  // (measured for the masked decode, E = 64, K = 7168, N = 2048: one 4-byte
+  // load per row and stage cost 22 us of its 186, the scales' lines being
+  // requested as often as the operand rows themselves)
   static constexpr int SCG = MX ? (BM + BN) / 64 : 0;
   static constexpr int DSMAX = (SCG + NW - 1) / NW;
   static_assert(!MX || (BM + BN) % 64 == 0, "whole scale groups");
   static constexpr int DMA_PER_STAGE = DA + DB + DSMAX;
-  static constexpr int A_BYTES = BM * KROW, SC_OFF = (BM + BN) * KROW;
-  static constexpr int STAGE_BYTES = SC_OFF + (MX ? (BM + BN) * 4 : 0);
+  static constexpr int A_BYTES = BM * KROW, STAGE_BYTES = (BM + BN) * KROW;
   static constexpr int NSTAGES = NSTAGE * STAGE / STAGE_BYTES > 6 ? 6 : NSTAGE * STAGE / STAGE_BYTES;
   static_assert(NSTAGES >= 2, "two stages at least");
+  static constexpr int RSLOT = MX ? (BM + BN) * 16 : 0;  // one slot of the scale ring
+  static constexpr int RING_OFF = NSTAGES * STAGE_BYTES;
+  static constexpr size_t LDS_BYTES = (size_t)RING_OFF + 2 * RSLOT;
   KmajDma<BM, NW> da;
   KmajDma<BN, NW> db;
   __amdgpu_buffer_rsrc_t rsA, rsW, rsAS, rsWS;
@@ -946,6 +957,8 @@ struct FwdDeepOp {
   const char *ldsp;
   uint32_t soff[DSMAX > 0 ? DSMAX : 1];  // MX: per-lane byte offset of the row's scales, or OOB
   int K, wid;
+  bool sc16 = false;                     // MX: four stages' scale words per 16-byte load
+  int pbase = 0, pscale = 0;             // DMA instructions of this wave per stage (count_parts)
   template <bool SKIP, bool CHECKED>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)(buf * STAGE_BYTES);
@@ -955,26 +968,40 @@ struct FwdDeepOp {
       db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + A_BYTES, wid, j - DA);
     } else if constexpr (MX) {
       const int i = j - DA - DB, grp = wid + i * NW;
-      if (grp < SCG)
-        dma4_so(grp < BM / 64 ? rsAS : rsWS, soff[i], (uint32_t)kt * 4u,
-                t + (uint32_t)(SC_OFF + grp * 256));
+      const uint32_t slot = lds0 + (uint32_t)(RING_OFF + ((kt >> 2) & 1) * RSLOT);
+      if (grp < SCG) {
+        const __amdgpu_buffer_rsrc_t rs = grp < BM / 64 ? rsAS : rsWS;
+        if (sc16) {
+          if ((kt & 3) == 0)
+            dma16_so(rs, soff[i], (uint32_t)(kt >> 2) * 16u, slot + (uint32_t)(grp * 1024));
+        } else {
+          dma4_so(rs, soff[i], (uint32_t)kt * 4u,
+                  slot + (uint32_t)((kt & 3) * (BM + BN) * 4 + grp * 256));
+        }
+      }
     }
   }
-  // DMA instructions this wave issues per stage (the others cover dead rows)
-  MOE_DEV int parts() const {
-    int n = 0;
+  // DMA instructions this wave issues for a stage (the others cover dead rows;
+  // with sc16 the scale loads come with every fourth stage only)
+  MOE_DEV void count_parts() {
+    pbase = 0;
+    pscale = 0;
 #pragma unroll
-    for (int i = 0; i < DA; ++i) n += (wid * DA + i) * 8 < da.live_rows ? 1 : 0;
+    for (int i = 0; i < DA; ++i) pbase += (wid * DA + i) * 8 < da.live_rows ? 1 : 0;
 #pragma unroll
-    for (int i = 0; i < DB; ++i) n += (wid * DB + i) * 8 < db.live_rows ? 1 : 0;
+    for (int i = 0; i < DB; ++i) pbase += (wid * DB + i) * 8 < db.live_rows ? 1 : 0;
 #pragma unroll
-    for (int i = 0; i < DSMAX; ++i) n += wid + i * NW < SCG ? 1 : 0;
-    return n;
+    for (int i = 0; i < DSMAX; ++i) pscale += wid + i * NW < SCG ? 1 : 0;
   }
-  // as FwdOp::scale_of, for the stage at `buf`
-  MOE_DEV uint32_t scale_of(int buf, bool b_side, int row, int step, int lane) const {
-    const uint32_t w = *(const uint32_t *)(ldsp + buf * STAGE_BYTES + SC_OFF +
-                                           (b_side ? BM * 4 : 0) + row * 4);
+  MOE_DEV int parts_at(int kt) const {
+    return pbase + ((!sc16 || (kt & 3) == 0) ? pscale : 0);
+  }
+  // as FwdOp::scale_of, for stage kt (its words in the ring)
+  MOE_DEV uint32_t scale_of(int kt, bool b_side, int row, int step, int lane) const {
+    const int rr = (b_side ? BM : 0) + row;
+    const char *slot = ldsp + RING_OFF + ((kt >> 2) & 1) * RSLOT;
+    const uint32_t w = *(const uint32_t *)(slot + (sc16 ? rr * 16 + (kt & 3) * 4
+                                                        : (kt & 3) * (BM + BN) * 4 + rr * 4));
     return (w >> (8 * (2 * step + (lane >> 5)))) & 0xffu;
   }
 };
@@ -1145,6 +1172,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         if constexpr (MX) {
           dop.rsAS = op.rsAS;
           dop.rsWS = op.rsWS;
+          dop.sc16 = K % 512 == 0;
 #pragma unroll
           for (int i = 0; i < dop.DSMAX; ++i) {
             const int grp = wid + i * NW, ra = grp * 64 + lane;
@@ -1159,8 +1187,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
             dop.soff[i] = o;
           }
         }
-        tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi,
-                                               dop.parts(), acc);
+        dop.count_parts();
+        tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi, acc);
       } else {
         tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8, MX>, DSK>(
             op, lds, kb, ke, wm, wn, lane, live_mi, live_ni, acc);
@@ -2154,10 +2182,13 @@ hipError_t launch_routed(FwdArgs &a, const moe_schedule &s, hipStream_t st) {
   }
   if (s.layout == MOE_LAYOUT_MASKED && s.capacity <= 64) {
     constexpr int BM = 64, BN = 256;
+    // (block scales: the scale ring after the stages)
+    constexpr size_t ring_lds = FwdDeepOp<BM, BN, 4, F8, MX>::LDS_BYTES;
+    constexpr size_t lds = ring_lds > kStageLds ? ring_lds : kStageLds;
     auto k = mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8, MX>;
-    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8, MX>>(kStageLds);
+    hipError_t e = set_smem<mfma_fwd_kernel<BM, BN, 1, 4, MODE, float, F8, MX>>(lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), kStageLds, st, a);
+    hipLaunchKernelGGL(k, dim3(device_cu_count()), dim3(256), lds, st, a);
     return hipGetLastError();
   }
   a.tile_rows = g_tile_rows.load(std::memory_order_relaxed);

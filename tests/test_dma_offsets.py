@@ -108,6 +108,26 @@ def test_block_scale_words(rows, K):
         _check_lane(OOB, 4 * kt, 4, nrec)
 
 
+@pytest.mark.parametrize("rows,K", [(1, 512), (9, 1024), (4096, 2048), (3, 7168), (64, 7168)])
+def test_block_scale_groups_of_four_stages(rows, K):
+    """The masked decode's scale ring with K a multiple of 512: a row's 16
+    bytes of four stages (512 elements) at row * K/32 + 16 g, the row offset
+    per lane and 16 g as the scalar offset for every group g, the last one
+    included (K/32 is a multiple of 16, so a group never crosses a row end);
+    without that multiple, 4 kt per stage for every stage, the last included."""
+    assert K % 512 == 0
+    kblk = K // 32
+    nrec = rows * kblk
+    for row in {0, rows - 1}:
+        assert (row * kblk) % 16 == 0
+        for g in range(K // 512):
+            _check_lane(row * kblk, 16 * g, 16, nrec)
+        for kt in range(K // 128):
+            _check_lane(row * kblk, 4 * kt, 4, nrec)
+    for g in range(K // 512):
+        _check_lane(OOB, 16 * g, 16, nrec)
+
+
 def test_size_limit_keeps_masked_lanes_masked():
     """With every buffer below 2^31 bytes, kOobOffset is out of range of all
     of them, and adding any in-buffer advance to it cannot wrap to a small
