@@ -423,7 +423,8 @@ MOE_DEV int acc_row(int i, int lane) { return ((i >> 2) << 3) + ((lane >> 5) << 
 // SKIP: wave-uniform live_mi / live_ni bound the row / column blocks this wave
 // multiplies, and the Op may leave out DMA instructions of dead rows.
 // DSKIP: the Op leaves out DMA instructions whose rows are all dead.
-template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op, bool DSKIP = SKIP>
+template <int MI, int NI, int WGM, int WGN, bool SKIP, class Op, bool DSKIP = SKIP,
+          bool NTW = false>
 MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, int lane,
                            int live_mi, int live_ni, f32x16 (&acc)[MI][NI]) {
   constexpr int D = Op::DMA_PER_STAGE;
@@ -534,7 +535,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
         if (j * SLOTS / NR == i) read_item(nbuf, 0, 0, j);
 #pragma unroll
       for (int j = 0; j < DD; ++j)
-        if (j * SLOTS / DD == i) op.template issue_part<DSKIP, decltype(CHK)::value>(dma, buf, j);
+        if (j * SLOTS / DD == i) op.template issue_part<DSKIP, decltype(CHK)::value, NTW>(dma, buf, j);
       if constexpr (NS > 0) {
         if (i >= NM - NS) fa[0][i - (NM - NS)] = scale_frag(fa[0][i - (NM - NS)], sc[0]);
       }
@@ -550,7 +551,7 @@ MOE_DEV void tile_multiply(Op &op, char *lds, int kb, int ke, int wm, int wn, in
   auto issue_stage = [&](int kt, int buf) __attribute__((always_inline)) {
     if (Op::PREFETCH) op.prefetch(kt);
 #pragma unroll
-    for (int j = 0; j < D; ++j) op.template issue_part<DSKIP, true>(kt, buf, j);
+    for (int j = 0; j < D; ++j) op.template issue_part<DSKIP, true, NTW>(kt, buf, j);
   };
 
   // prologue: the first two stages in flight; wait for the first
@@ -918,13 +919,14 @@ struct FwdOp {
   const char *ldsp;
   uint32_t soff[DS > 0 ? DS : 1];  // MX: per-lane byte offset of the row's scales, or OOB
   int K, wid;
-  template <bool SKIP, bool CHECKED>
+  // NTW: the tile's weight block is read by no other tile (non-temporal loads)
+  template <bool SKIP, bool CHECKED, bool NTW = false>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < DA) {
       da.template issue_one<SKIP, CHECKED>(rsA, kt, K, t, wid, j);
     } else if (j < DA + DB) {
-      db.template issue_one<SKIP, CHECKED>(rsW, kt, K, t + OPND, wid, j - DA);
+      db.template issue_one<SKIP, CHECKED, NTW>(rsW, kt, K, t + OPND, wid, j - DA);
     } else if constexpr (MX) {
       // 64-row group of A rows, then B rows, dealt to the waves round robin
       const int i = j - DA - DB, grp = wid + i * NW;
@@ -980,7 +982,7 @@ struct FwdDeepOp {
   int K, wid;
   bool sc16 = false;                     // MX: four stages' scale words per 16-byte load
   int pbase = 0, pscale = 0;             // DMA instructions of this wave per stage (count_parts)
-  template <bool SKIP, bool CHECKED>
+  template <bool SKIP, bool CHECKED, bool NTW = false>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)(buf * STAGE_BYTES);
     if (j < DA) {
@@ -1135,6 +1137,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     }
     __syncthreads();
     op.rsW = uniform_rsrc((const char *)p.W + (size_t)ge * wrows * rowbytes, wbytes);
+    // a whole tile of a group with a single row block is the only reader of
+    // its weight block in this launch: those weights stream past with
+    // non-temporal loads and leave L2 to the token rows the group's other
+    // column blocks read again (gated FFN, 256 rows per expert: up-projection
+    // 627 -> 588 us, down projection 460 -> 433; the hint on every weight
+    // load instead slows the forward of groups of several row blocks, whose
+    // tiles share each weight block: config-2 forward 103 -> 106, Zipf
+    // T = 8192 E = 64 top-4 forward 436 -> 468).  Only the gated FFN's two
+    // kernels carry the second tile body for it: in the routed forward it cost
+    // about 1 % (config-2 forward 106.0 -> 106.9 us, Zipf 439 -> 443) and in
+    // the input gradient more (Zipf dX 688 -> 698), from the larger code alone
+    constexpr bool NT_OK = GATED || MODE == FWD_SCATTER_ROWS;
+    const bool ntw = NT_OK && !RK && ws.nS == 1 && bs[c.g + 1] - bs[c.g] <= 1;
     if constexpr (MX) {
       // per-lane offsets of the scale rows: group grp of 64 rows (A rows, then
       // B rows), lane = row inside the group; dead rows read out of range
@@ -1167,8 +1182,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     // masked decode, and whole tiles that end past a group's rows or past N,
     // e.g. the last 256-column block of N = 1408); DSK: DMA of dead rows is left out;
     // DEEP: the streaming pipeline with more stages in flight (masked decode).
-    auto tile = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_, auto DEEP_)
-                    __attribute__((always_inline)) {
+    auto tile_nt = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_, auto DEEP_, auto NTW_)
+                       __attribute__((always_inline)) {
+      constexpr bool NTW = decltype(NTW_)::value;
       constexpr int MIc = decltype(MIc_)::value, NIc = decltype(NIc_)::value;
       constexpr bool SKM = decltype(SKM_)::value, DSK = decltype(DSK_)::value;
       const int live_mi =
@@ -1212,7 +1228,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         dop.count_parts();
         tile_multiply_deep<MIc, NIc, WGM, WGN>(dop, lds, kb, ke, wm, wn, lane, live_mi, acc);
       } else {
-        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8, MX>, DSK>(
+        tile_multiply<MIc, NIc, WGM, WGN, SKM, FwdOp<BM, BN, NW, F8, MX>, DSK, NTW>(
             op, lds, kb, ke, wm, wn, lane, live_mi, live_ni, acc);
       }
 
@@ -1381,6 +1397,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    // (whole tiles of single-row-block groups take tile_nt with NTW set)
+    auto tile = [&](auto MIc_, auto NIc_, auto SKM_, auto DSK_, auto DEEP_)
+                    __attribute__((always_inline)) {
+      tile_nt(MIc_, NIc_, SKM_, DSK_, DEEP_, std::false_type());
+    };
     using std::integral_constant;
     using std::false_type;
     using std::true_type;
@@ -1395,6 +1416,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         if (nsub == 2 || BMr == 128)
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
+        else if (ntw)
+          tile_nt(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
+                  false_type(), false_type(), true_type());
         else
           tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
                false_type(), false_type());
@@ -1418,12 +1442,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
         else if (nsub == 2)
           tile(integral_constant<int, R4>(), integral_constant<int, NI>(), false_type(),
                true_type(), false_type());
-        else if (ncols < BNO || c.rows < BMr)
+        else if (ncols < BNO || c.rows < BMr) {
+          if constexpr (NT_OK) {
+            if (ntw) {
+              tile_nt(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(),
+                      true_type(), false_type(), true_type());
+              continue;
+            }
+          }
           tile(integral_constant<int, MI>(), integral_constant<int, NI>(), true_type(),
                true_type(), false_type());
-        else
+        } else {
+          if constexpr (NT_OK) {
+            if (ntw) {
+              tile_nt(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
+                      false_type(), false_type(), true_type());
+              continue;
+            }
+          }
           tile(integral_constant<int, MI>(), integral_constant<int, NI>(), false_type(),
                false_type(), false_type());
+        }
       }
     }
   }
@@ -1490,7 +1529,7 @@ struct DxOp {
                           : kOobOffset;
     }
   }
-  template <bool SKIP, bool CHECKED>
+  template <bool SKIP, bool CHECKED, bool NTW = false>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < DA) {
@@ -1959,7 +1998,7 @@ struct DwOp {
     for (int i = 0; i < PW / 2; ++i)
       tq[i] = *(const i32x4 *)(lds + ring_off(kt) + wid * (8 * PW) + 16 * i);
   }
-  template <bool SKIP, bool CHECKED>
+  template <bool SKIP, bool CHECKED, bool NTW = false>
   MOE_DEV void issue_part(int kt, int buf, int j) {
     const uint32_t t = lds0 + (uint32_t)buf * STAGE;
     if (j < 2 * PW) {
