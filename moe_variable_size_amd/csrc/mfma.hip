@@ -1140,14 +1140,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void mfma_fwd_kernel(FwdArgs p) {
     // a whole tile of a group with a single row block is the only reader of
     // its weight block in this launch: those weights stream past with
     // non-temporal loads and leave L2 to the token rows the group's other
-    // column blocks read again (gated FFN, 256 rows per expert: up-projection
-    // 627 -> 588 us, down projection 460 -> 433; the hint on every weight
-    // load instead slows the forward of groups of several row blocks, whose
-    // tiles share each weight block: config-2 forward 103 -> 106, Zipf
-    // T = 8192 E = 64 top-4 forward 436 -> 468).  Only the gated FFN's two
-    // kernels carry the second tile body for it: in the routed forward it cost
-    // about 1 % (config-2 forward 106.0 -> 106.9 us, Zipf 439 -> 443) and in
-    // the input gradient more (Zipf dX 688 -> 698), from the larger code alone
+    // column blocks read again (gated FFN, T = 8192, K = 4096, F = 2048,
+    // N = 4096, 64 experts of 256 rows: up-projection 627 -> 588 us, down
+    // projection 460 -> 433; the hint on every weight load instead slows the
+    // forward of groups of several row blocks, whose tiles share each weight
+    // block: T = 4096, K = N = 2048, E = 8 top-2 forward 103 -> 106, Zipf-routed
+    // T = 8192, K = 4096, N = 1408, E = 64 top-4 forward 436 -> 468).  Only the
+    // gated FFN's two kernels carry the second tile body for it: in the routed
+    // forward it cost about 1 % from the larger code alone (the same two
+    // shapes: 106.0 -> 106.9 us, 439 -> 443), and in the input gradient more
+    // (the Zipf-routed dX 688 -> 698)
     constexpr bool NT_OK = GATED || MODE == FWD_SCATTER_ROWS;
     const bool ntw = NT_OK && !RK && ws.nS == 1 && bs[c.g + 1] - bs[c.g] <= 1;
     if constexpr (MX) {
